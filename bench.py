@@ -1,0 +1,263 @@
+"""Benchmark of the fused residual-add + RMSNorm + per-group quantization on
+one MI355X.
+
+A step is one fused launch over one batch: the prefill chunk of 8192 tokens x
+7168 hidden (bf16), residual add written back, bf16 side-output, FP8 e4m3fn
+codes with fp32 scales per 1x128 group. Inputs are synthetic and already
+resident in HBM; buffer sets rotate so that no step finds its data in the
+256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value         algorithmic HBM GB/s of the whole step (bytes: x and residual
+                read, residual, codes, scales and bf16 written; gamma excluded)
+  roofline      the fused kernel against the 8 TB/s HBM peak, timed with HIP
+                events around each launch on the launch stream
+  cpu_baseline  the double-precision CPU oracle on the machine's host cores
+  configs       the other workloads (decode, prefill at 512 rows, the two MLA
+                latent norms in one launch, MXFP4 in both scale layouts)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ work --
+def algorithmic_bytes(M, N, fmt, residual, keep_bf16):
+    """x read + residual read + residual/codes/scales written (+ bf16 written)."""
+    b = M * N * 2
+    if residual:
+        b += 2 * M * N * 2
+    b += M * N if fmt == 0 else M * N // 2
+    b += M * (N // 128) * 4 if fmt == 0 else M * (N // 32)
+    if keep_bf16:
+        b += M * N * 2
+    return b
+
+
+class Workload:
+    """Rotating sets of device buffers for one or more problems launched together."""
+
+    def __init__(self, name, specs, fmt, layout=0):
+        import torch
+        import fp4_quant_amd as fq
+        from fp4_quant_amd import inputs
+        self.name, self.fmt, self.layout = name, fmt, layout
+        self.bytes = sum(algorithmic_bytes(s["M"], s["N"], fmt, s["residual"], s["keep_bf16"]) for s in specs)
+        self.rows = sum(s["M"] for s in specs)
+        nsets = max(2, min(512, -(-3 * MALL_BYTES // max(self.bytes, 1))))
+        self.sets = []
+        host = []
+        for s in specs:
+            p = inputs.make_problem(s["M"], s["N"], seed_x=s.get("seed", 0), residual=s["residual"],
+                                    outliers=s.get("outliers", True))
+            host.append(p)
+        for k in range(nsets):
+            probs, keep = [], []
+            for s, p in zip(specs, host):
+                M, N = s["M"], s["N"]
+                x = torch.from_numpy(p["x"].view("int16")).view(torch.bfloat16).cuda()
+                g = torch.from_numpy(p["gamma"].view("int16")).view(torch.bfloat16).cuda()
+                r = ro = None
+                if s["residual"]:
+                    r = torch.from_numpy(p["residual"].view("int16")).view(torch.bfloat16).cuda()
+                    ro = torch.empty_like(r)
+                q, sc, yb = fq.alloc_outputs(M, N, fmt, layout, s["keep_bf16"])
+                keep += [x, g, r, ro, q, sc, yb]
+                probs.append(fq.make_problem(x, g, p["eps"], q, sc, residual_in=r, residual_out=ro,
+                                             out_bf16=yb, fmt=fmt, scale_layout=layout))
+            self.sets.append((probs, keep))
+        self.host = host
+
+    def launch(self, i):
+        import fp4_quant_amd as fq
+        fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0])
+
+
+def time_workload(w, steps, warmup):
+    """Per-launch time from HIP events bracketing each launch on the launch
+    stream, and the step time from one event pair around all steps."""
+    import torch
+    for i in range(warmup):
+        w.launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        w.launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    per_launch_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        w.launch(i)
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    return per_launch_ms, step_ms
+
+
+def copy_ceiling_gbps():
+    """A plain device copy (torch's copy kernel) of 2 GiB: read + write bytes
+    over its time, the box's achievable streaming bandwidth."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(10):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / 10
+    del a, b
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(w, budget_s):
+    """The CPU oracle as it stands on this host, over the workload's rows,
+    repeated until budget_s has passed (at least once)."""
+    import oracle
+    p = w.host[0]
+    M, N = p["x"].shape
+    keep = True
+    t_total, reps = 0.0, 0
+    while True:
+        t0 = time.perf_counter()
+        oracle.rmsnorm_quant_group(p["x"], p["gamma"], p["eps"], residual=p.get("residual"),
+                                   group=128, fmt=0, keep_bf16=keep)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if t_total >= budget_s:
+            break
+    sec = t_total / reps
+    return {"value": round(w.bytes / sec / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "mtok_per_s": round(M / sec / 1e6, 4),
+            "sample": f"the full {M}x{N} workload, {reps} run(s), {sec:.3f} s each (median not taken: mean)"}
+
+
+SPECS = {
+    "decode": ([dict(M=64, N=7168, residual=True, keep_bf16=False)], 0, 0),
+    "prefill": ([dict(M=8192, N=7168, residual=True, keep_bf16=True)], 0, 0),
+    "prefill512": ([dict(M=512, N=7168, residual=True, keep_bf16=True)], 0, 0),
+    "mla": ([dict(M=4096, N=1536, residual=False, keep_bf16=False, seed=10, outliers=False),
+             dict(M=4096, N=512, residual=False, keep_bf16=False, seed=20, outliers=False)], 0, 0),
+    "mxfp4_row": ([dict(M=16384, N=7168, residual=True, keep_bf16=False)], 1, 0),
+    "mxfp4_tiled32": ([dict(M=16384, N=7168, residual=True, keep_bf16=False)], 1, 1),
+}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="prefill", choices=sorted(SPECS))
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline budget (0 skips it)")
+    ap.add_argument("--only-kernel", action="store_true",
+                    help="launch only the headline workload (for profiler runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this library runs on one GPU; rows are independent, so several GPUs would "
+              "each run the same kernel on their own rows. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp4_quant_amd as fq
+    assert torch.cuda.is_available() and fq.rmsq_device_supported(0), "needs a gfx950 GPU"
+    torch.cuda.set_device(0)
+
+    specs, fmt, layout = SPECS[args.config]
+    log(f"bench: building workload {args.config}")
+    w = Workload(args.config, specs, fmt, layout)
+    log(f"bench: {len(w.sets)} rotating buffer sets, {w.bytes / 1e6:.1f} MB per step")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    per_launch_ms, step_ms = time_workload(w, args.steps, args.warmup)
+    wall = time.perf_counter() - t_wall
+    gbps = w.bytes / (step_ms * 1e-3) / 1e9
+    kern_gbps = w.bytes / (per_launch_ms * 1e-3) / 1e9
+    log(f"bench: {args.config}: step {step_ms * 1e3:.2f} us, per launch (events) {per_launch_ms * 1e3:.2f} us, "
+        f"{gbps:.0f} GB/s")
+    if args.only_kernel:
+        return
+
+    configs = {}
+    if not args.no_configs:
+        for name, (sp, f, lay) in SPECS.items():
+            if name == args.config:
+                continue
+            log(f"bench: workload {name}")
+            wk = Workload(name, sp, f, lay)
+            pl, st = time_workload(wk, max(20, args.steps // 2), 10)
+            configs[name] = {"us_per_launch": round(pl * 1e3, 2), "GBps": round(wk.bytes / (pl * 1e-3) / 1e9, 1),
+                             "frac_of_peak": round(wk.bytes / (pl * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                             "Mtok_per_s": round(wk.rows / (pl * 1e-3) / 1e6, 2), "bytes": wk.bytes}
+            del wk
+            torch.cuda.empty_cache()
+    ceiling = copy_ceiling_gbps()
+    log(f"bench: device copy ceiling {ceiling:.0f} GB/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("bench: CPU oracle baseline")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    M, N = specs[0]["M"], specs[0]["N"]
+    out = {
+        "metric": "achieved HBM GB/s (% of MI355X peak) and Mtokens/s at N=7168, group=128",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill chunk 8192x7168 bf16: residual add + RMSNorm + bf16 side-output + "
+                               "FP8 e4m3fn 1x128 group quant" if args.config == "prefill" else args.config,
+                   "M": M, "N": N, "group": 128 if fmt == 0 else 32,
+                   "fmt": "fp8_e4m3fn" if fmt == 0 else "mxfp4_e2m1", "residual": specs[0]["residual"],
+                   "keep_bf16": specs[0]["keep_bf16"], "parallelism": "none (one GPU)"},
+        "mtok_per_s": round(w.rows / (step_ms * 1e-3) / 1e6, 2),
+        "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "rmsq_fused_kernel<0,14>", "bytes_per_launch": w.bytes,
+                     "us_per_launch": round(per_launch_ms * 1e3, 2)},
+        "copy_ceiling_GBps": round(ceiling, 1),
+        "cpu_baseline": cpu,
+        "configs": configs,
+        "timed_wall_s": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

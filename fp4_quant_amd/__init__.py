@@ -1,0 +1,184 @@
+"""fp4_quant_amd: fused residual-add + RMSNorm + per-group FP8 / MXFP4
+quantization for AMD Instinct MI355X (gfx950).
+
+Every step of the operation runs in the HIP kernels of ``librmsq.so``; this
+module only marshals arguments over its C ABI (``include/rmsq.h``), with torch
+providing device memory and streams. There is no CPU fallback: if the
+library is not built, or the GPU is not a gfx950, calls raise.
+
+The raw entry points keep the C names and argument order:
+
+* ``rmsnorm_quant_group(x, residual_in, gamma, eps, M, N, group, fmt, out_q,
+  out_scale, residual_out, out_bf16_or_null, stream=None)``
+* ``rmsnorm_quant_group_multi(problems, stream=None)``
+
+``fused_rmsnorm_quant`` allocates the outputs and returns them in the tuple
+shape of the pull request "[AMD] Add fused all-reduce RMSNorm per-group quant
+for Qwen3.5 FP8" (Modifications): ``((q, scale), residual)`` or, with the bf16
+side-output, ``((bf16, q, scale), residual)``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librmsq.so")
+
+RMSQ_OK, RMSQ_ERR_INVALID_ARG, RMSQ_ERR_UNSUPPORTED, RMSQ_ERR_HIP = 0, 1, 2, 3
+FMT_FP8_E4M3FN, FMT_MXFP4_E2M1 = 0, 1
+SCALE_ROW_MAJOR, SCALE_TILED32 = 0, 1
+MAX_PROBLEMS = 4
+N_MAX = 32768
+_FMT = {"fp8": FMT_FP8_E4M3FN, "mxfp4": FMT_MXFP4_E2M1}
+_GROUP = {FMT_FP8_E4M3FN: 128, FMT_MXFP4_E2M1: 32}
+_LAYOUT = {"row": SCALE_ROW_MAJOR, "tiled32": SCALE_TILED32}
+
+
+class RmsqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_STATUS = {0: "RMSQ_OK", 1: "RMSQ_ERR_INVALID_ARG", 2: "RMSQ_ERR_UNSUPPORTED", 3: "RMSQ_ERR_HIP"}
+
+
+class rmsq_problem(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("ldx", C.c_int64),
+                ("residual_in", C.c_void_p), ("residual_out", C.c_void_p), ("ldr", C.c_int64),
+                ("gamma", C.c_void_p), ("eps", C.c_float),
+                ("M", C.c_int64), ("N", C.c_int64), ("group", C.c_int32), ("fmt", C.c_int32),
+                ("scale_layout", C.c_int32),
+                ("out_q", C.c_void_p), ("out_scale", C.c_void_p), ("out_bf16", C.c_void_p),
+                ("ldb", C.c_int64)]
+
+
+EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "rmsq_device_supported",
+           "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape")
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load librmsq.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(the HIP library is required; there is no CPU fallback)")
+        L = C.CDLL(LIB_PATH)
+        p, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
+        L.rmsnorm_quant_group.restype = i32
+        L.rmsnorm_quant_group.argtypes = [p, p, p, C.c_float, i64, i64, i32, i32, p, p, p, p, p]
+        L.rmsnorm_quant_group_multi.restype = i32
+        L.rmsnorm_quant_group_multi.argtypes = [C.POINTER(rmsq_problem), i32, p]
+        L.rmsq_device_supported.restype = i32
+        L.rmsq_device_supported.argtypes = [i32]
+        L.rmsq_scale_bytes.restype = C.c_size_t
+        L.rmsq_scale_bytes.argtypes = [i64, i64, i32, i32, i32]
+        L.rmsq_status_string.restype = C.c_char_p
+        L.rmsq_status_string.argtypes = [i32]
+        L.rmsq_last_error.restype = C.c_char_p
+        L.rmsq_last_error.argtypes = []
+        L.rmsq_set_shape.restype = None
+        L.rmsq_set_shape.argtypes = [i32, i32]
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != RMSQ_OK:
+        raise RmsqError(status, lib().rmsq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device=None):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream(device).cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ------------------------------------------------------------- raw ABI --
+def rmsnorm_quant_group(x, residual_in, gamma, eps, M, N, group, fmt, out_q, out_scale,
+                        residual_out, out_bf16_or_null, stream=None) -> None:
+    """The C entry point with torch tensors (or None) for the buffers."""
+    _check(lib().rmsnorm_quant_group(
+        _ptr(x), _ptr(residual_in), _ptr(gamma), float(eps), int(M), int(N), int(group), int(fmt),
+        _ptr(out_q), _ptr(out_scale), _ptr(residual_out), _ptr(out_bf16_or_null),
+        _stream(stream, x.device if x is not None else None)))
+
+
+def _ld(t):
+    return 0 if t is None else int(t.stride(0))
+
+
+def make_problem(x, gamma, eps, out_q, out_scale, *, residual_in=None, residual_out=None,
+                 out_bf16=None, fmt=FMT_FP8_E4M3FN, scale_layout=SCALE_ROW_MAJOR) -> rmsq_problem:
+    M, N = x.shape
+    return rmsq_problem(x=_ptr(x), ldx=_ld(x), residual_in=_ptr(residual_in),
+                        residual_out=_ptr(residual_out), ldr=_ld(residual_in), gamma=_ptr(gamma),
+                        eps=float(eps), M=M, N=N, group=_GROUP.get(fmt, 0), fmt=fmt,
+                        scale_layout=scale_layout, out_q=_ptr(out_q), out_scale=_ptr(out_scale),
+                        out_bf16=_ptr(out_bf16), ldb=_ld(out_bf16))
+
+
+def rmsnorm_quant_group_multi(problems, stream=None) -> None:
+    """Up to four independent problems (``rmsq_problem`` structs from
+    ``make_problem``) in one kernel launch."""
+    arr = (rmsq_problem * len(problems))(*problems)
+    _check(lib().rmsnorm_quant_group_multi(arr, len(problems), _stream(stream)))
+
+
+def rmsq_device_supported(device: int = 0) -> bool:
+    return bool(lib().rmsq_device_supported(int(device)))
+
+
+def rmsq_scale_bytes(M, N, group, fmt, scale_layout=SCALE_ROW_MAJOR) -> int:
+    return int(lib().rmsq_scale_bytes(int(M), int(N), int(group), int(fmt), int(scale_layout)))
+
+
+def rmsq_set_shape(J: int = 0, W: int = 0) -> None:
+    lib().rmsq_set_shape(int(J), int(W))
+
+
+# -------------------------------------------------------- convenience --
+def alloc_outputs(M, N, fmt, scale_layout=SCALE_ROW_MAJOR, keep_bf16=False, device="cuda"):
+    import torch
+    q = torch.empty((M, N if fmt == FMT_FP8_E4M3FN else N // 2), dtype=torch.uint8, device=device)
+    G = N // _GROUP[fmt]
+    if fmt == FMT_FP8_E4M3FN:
+        scale = torch.empty((M, G), dtype=torch.float32, device=device)
+    elif scale_layout == SCALE_TILED32:
+        scale = torch.empty((((M + 31) // 32) * 32 * G,), dtype=torch.uint8, device=device)
+    else:
+        scale = torch.empty((M, G), dtype=torch.uint8, device=device)
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=device) if keep_bf16 else None
+    return q, scale, yb
+
+
+def fused_rmsnorm_quant(x, gamma, eps=1e-6, residual=None, fmt="fp8", keep_bf16=False,
+                        scale_layout="row", inplace_residual=False, stream=None):
+    """Allocate outputs and run one fused call.
+
+    Returns ``((q, scale), residual_out)`` or ``((bf16, q, scale), residual_out)``
+    (``residual_out`` is None without a residual; it is ``residual`` itself
+    when ``inplace_residual``). FP8 codes are returned as ``uint8`` (view them
+    with ``.view(torch.float8_e4m3fn)``), MXFP4 codes as packed ``uint8``.
+    """
+    import torch
+    f = _FMT[fmt] if isinstance(fmt, str) else int(fmt)
+    lay = _LAYOUT[scale_layout] if isinstance(scale_layout, str) else int(scale_layout)
+    M, N = x.shape
+    q, scale, yb = alloc_outputs(M, N, f, lay, keep_bf16, x.device)
+    res_out = None
+    if residual is not None:
+        res_out = residual if inplace_residual else torch.empty_like(residual)
+    p = make_problem(x, gamma, eps, q, scale, residual_in=residual, residual_out=res_out,
+                     out_bf16=yb, fmt=f, scale_layout=lay)
+    rmsnorm_quant_group_multi([p], stream)
+    return ((yb, q, scale) if keep_bf16 else (q, scale)), res_out

@@ -1,0 +1,295 @@
+// rmsq_abi.hip - C ABI of librmsq: argument validation, device check, launch
+// configuration and kernel dispatch. Declarations and the contract are in
+// include/rmsq.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "rmsq.h"
+#include "rmsq_kernel.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+rmsq_status fail(rmsq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool output;
+  int problem;
+  int kind;          // 0 x, 1 residual_in, 2 residual_out, 3 gamma, 4 q, 5 scale, 6 bf16
+};
+
+size_t scale_bytes(int64_t M, int64_t N, int32_t group, int32_t fmt, int32_t layout) {
+  if (M < 0 || N <= 0 || group <= 0 || N % group) return 0;
+  const int64_t G = N / group;
+  if (fmt == RMSQ_FMT_FP8_E4M3FN && group == 128 && layout == RMSQ_SCALE_ROW_MAJOR) return (size_t)(M * G * 4);
+  if (fmt == RMSQ_FMT_MXFP4_E2M1 && group == 32) {
+    if (layout == RMSQ_SCALE_ROW_MAJOR) return (size_t)(M * G);
+    if (layout == RMSQ_SCALE_TILED32) return (size_t)(((M + 31) / 32) * 32 * G);
+  }
+  return 0;
+}
+
+// Validate one problem and append its buffers' byte ranges.
+rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Range* rs, int* nr) {
+  if (p.fmt != RMSQ_FMT_FP8_E4M3FN && p.fmt != RMSQ_FMT_MXFP4_E2M1)
+    return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: unknown fmt %d", idx, p.fmt);
+  if (p.fmt != fmt0) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: all problems must share fmt", idx);
+  const int32_t want_group = p.fmt == RMSQ_FMT_FP8_E4M3FN ? 128 : 32;
+  if (p.group != want_group)
+    return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: group %d unsupported for fmt %d (need %d)", idx, p.group, p.fmt,
+                want_group);
+  if (p.scale_layout != RMSQ_SCALE_ROW_MAJOR && p.scale_layout != RMSQ_SCALE_TILED32)
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: unknown scale layout %d", idx, p.scale_layout);
+  if (p.scale_layout == RMSQ_SCALE_TILED32 && p.fmt != RMSQ_FMT_MXFP4_E2M1)
+    return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: the tiled scale layout is for MXFP4 only", idx);
+  if (p.M < 0) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: M = %lld < 0", idx, (long long)p.M);
+  if (p.N <= 0 || p.N % p.group) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: N = %lld not a positive multiple of %d", idx, (long long)p.N, p.group);
+  if (p.N > RMSQ_N_MAX) return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: N = %lld > %d", idx, (long long)p.N, RMSQ_N_MAX);
+  if (p.M > INT32_MAX) return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: M = %lld too large", idx, (long long)p.M);
+  if (!std::isfinite(p.eps) || p.eps < 0.0f) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: eps must be finite and >= 0", idx);
+  if ((p.residual_in == nullptr) != (p.residual_out == nullptr))
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: residual_in and residual_out must both be set or both be NULL", idx);
+  const int64_t ldx = p.ldx ? p.ldx : p.N, ldr = p.ldr ? p.ldr : p.N, ldb = p.ldb ? p.ldb : p.N;
+  if (ldx < p.N || ldx % 8 || (p.residual_in && (ldr < p.N || ldr % 8)) || (p.out_bf16 && (ldb < p.N || ldb % 8)))
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: row strides must be multiples of 8 and >= N", idx);
+  if (p.M == 0) return RMSQ_OK;
+  if (!p.x || !p.gamma || !p.out_q || !p.out_scale)
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: x, gamma, out_q and out_scale must be non-NULL", idx);
+  if (!aligned(p.x, 16) || !aligned(p.gamma, 16) || (p.residual_in && !aligned(p.residual_in, 16)) ||
+      (p.residual_out && !aligned(p.residual_out, 16)) || (p.out_bf16 && !aligned(p.out_bf16, 16)))
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: bf16 pointers must be 16-byte aligned", idx);
+  if (!aligned(p.out_q, p.fmt == RMSQ_FMT_FP8_E4M3FN ? 8 : 4))
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: out_q misaligned", idx);
+  if (p.fmt == RMSQ_FMT_FP8_E4M3FN && !aligned(p.out_scale, 4))
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: out_scale must be 4-byte aligned", idx);
+
+  auto add = [&](const void* ptr, int64_t bytes, bool out, int kind) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(ptr);
+    rs[(*nr)++] = Range{a, a + (uintptr_t)bytes, out, idx, kind};
+  };
+  const int64_t M = p.M, N = p.N;
+  add(p.x, ((M - 1) * ldx + N) * 2, false, 0);
+  if (p.residual_in) {
+    add(p.residual_in, ((M - 1) * ldr + N) * 2, false, 1);
+    add(p.residual_out, ((M - 1) * ldr + N) * 2, true, 2);
+  }
+  add(p.gamma, N * 2, false, 3);
+  add(p.out_q, M * (p.fmt == RMSQ_FMT_FP8_E4M3FN ? N : N / 2), true, 4);
+  add(p.out_scale, (int64_t)scale_bytes(M, N, p.group, p.fmt, p.scale_layout), true, 5);
+  if (p.out_bf16) add(p.out_bf16, ((M - 1) * ldb + N) * 2, true, 6);
+  return RMSQ_OK;
+}
+
+rmsq_status check_overlaps(const Range* rs, int nr) {
+  for (int i = 0; i < nr; ++i) {
+    if (!rs[i].output) continue;
+    for (int k = 0; k < nr; ++k) {
+      if (k == i || (k < i && rs[k].output)) continue;
+      const Range &a = rs[i], &b = rs[k];
+      if (a.lo >= b.hi || b.lo >= a.hi) continue;
+      // in-place residual: residual_out is exactly residual_in of the same problem
+      if (a.problem == b.problem && a.kind == 2 && b.kind == 1 && a.lo == b.lo && a.hi == b.hi) continue;
+      return fail(RMSQ_ERR_INVALID_ARG, "output buffer %d of problem %d overlaps buffer %d of problem %d", a.kind,
+                  a.problem, b.kind, b.problem);
+    }
+  }
+  return RMSQ_OK;
+}
+
+// gfx950 check, cached per device.
+std::atomic<int8_t> g_arch_ok[64];
+
+bool device_is_gfx950(int dev) {
+  if (dev < 0) return false;
+  if (dev < 64) {
+    const int8_t c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c) return c > 0;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  return ok;
+}
+
+// Launch shape: chunk-steps per lane J (compiled set) and waves per row W.
+// Many rows: long per-lane work, one wave per row when it fits, so more rows
+// are in flight per CU. Few rows: spread each row over more waves.
+constexpr int kJs[] = {14, 8, 7, 4, 3, 2, 1};
+
+void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
+  for (int J : kJs) {
+    const int64_t W = (C + 64 * J - 1) / (64 * J);
+    if (W > rmsq::max_waves(J)) continue;
+    const int64_t slots = W * 64 * J;
+    if (J > 1 && (slots - C) * 5 > slots) continue;      // more than 20% idle lanes
+    if (J > 1 && rows * W < 2048) continue;               // too few waves for 256 CUs
+    *J_out = J;
+    *W_out = (int)W;
+    return;
+  }
+  *J_out = 1;
+  *W_out = (int)((C + 63) / 64);
+}
+
+template <int FMT>
+rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, hipStream_t stream) {
+  const dim3 grid((unsigned)L.rows), block((unsigned)(64 * W));
+  switch (J) {
+    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14>), grid, block, 0, stream, L); break;
+    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8>), grid, block, 0, stream, L); break;
+    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7>), grid, block, 0, stream, L); break;
+    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4>), grid, block, 0, stream, L); break;
+    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3>), grid, block, 0, stream, L); break;
+    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2>), grid, block, 0, stream, L); break;
+    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1>), grid, block, 0, stream, L); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return RMSQ_OK;
+}
+
+// Launch-shape override for measurement sweeps, set by rmsq_set_shape
+// (0, 0 = automatic choice).
+std::atomic<int> g_force_J{0}, g_force_W{0};
+
+bool compiled_J(int J) {
+  for (int k : kJs)
+    if (k == J) return true;
+  return false;
+}
+
+rmsq_status run(const rmsq_problem* ps, int32_t count, void* stream) {
+  g_err[0] = 0;
+  if (!ps) return fail(RMSQ_ERR_INVALID_ARG, "problems is NULL");
+  if (count < 1 || count > RMSQ_MAX_PROBLEMS)
+    return fail(RMSQ_ERR_INVALID_ARG, "count = %d outside 1..%d", count, RMSQ_MAX_PROBLEMS);
+  Range rs[RMSQ_MAX_PROBLEMS * 7];
+  int nr = 0;
+  for (int i = 0; i < count; ++i) {
+    const rmsq_status s = check_problem(ps[i], i, ps[0].fmt, rs, &nr);
+    if (s != RMSQ_OK) return s;
+  }
+  if (const rmsq_status s = check_overlaps(rs, nr); s != RMSQ_OK) return s;
+
+  rmsq::Launch L;
+  std::memset(&L, 0, sizeof L);
+  int64_t rows = 0, Cmax = 0;
+  int n = 0;
+  for (int i = 0; i < count; ++i) {
+    const rmsq_problem& p = ps[i];
+    if (p.M == 0) continue;
+    rmsq::Problem& d = L.p[n++];
+    d.x = static_cast<const uint16_t*>(p.x);
+    d.r = static_cast<const uint16_t*>(p.residual_in);
+    d.h = static_cast<uint16_t*>(p.residual_out);
+    d.gamma = static_cast<const uint16_t*>(p.gamma);
+    d.q = static_cast<uint8_t*>(p.out_q);
+    d.scale = p.out_scale;
+    d.yb = static_cast<uint16_t*>(p.out_bf16);
+    d.ldx = p.ldx ? p.ldx : p.N;
+    d.ldr = p.ldr ? p.ldr : p.N;
+    d.ldb = p.ldb ? p.ldb : p.N;
+    d.M = (int32_t)p.M;
+    d.N = (int32_t)p.N;
+    d.row_begin = (int32_t)rows;
+    d.layout = p.scale_layout;
+    d.eps = p.eps;
+    rows += p.M;
+    if (p.N / 8 > Cmax) Cmax = p.N / 8;
+  }
+  if (n == 0) return RMSQ_OK;
+  if (rows > INT32_MAX) return fail(RMSQ_ERR_UNSUPPORTED, "total rows %lld exceed the grid limit", (long long)rows);
+  L.count = n;
+  L.rows = (int32_t)rows;
+
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
+    return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");
+
+  int J, W;
+  pick_shape(Cmax, rows, &J, &W);
+  const int fJ = g_force_J.load(), fW = g_force_W.load();
+  if (compiled_J(fJ) && fW > 0 && fW <= rmsq::max_waves(fJ) && (int64_t)fJ * fW * 64 >= Cmax) {
+    J = fJ;
+    W = fW;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(L, J, W, s) : launch_fmt<1>(L, J, W, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+rmsq_status rmsnorm_quant_group(const void* x, const void* residual_in, const void* gamma, float eps, int64_t M,
+                                int64_t N, int32_t group, int32_t fmt, void* out_q, void* out_scale,
+                                void* residual_out, void* out_bf16_or_null, void* stream) {
+  rmsq_problem p;
+  std::memset(&p, 0, sizeof p);
+  p.x = x;
+  p.residual_in = residual_in;
+  p.residual_out = residual_out;
+  p.gamma = gamma;
+  p.eps = eps;
+  p.M = M;
+  p.N = N;
+  p.group = group;
+  p.fmt = fmt;
+  p.scale_layout = RMSQ_SCALE_ROW_MAJOR;
+  p.out_q = out_q;
+  p.out_scale = out_scale;
+  p.out_bf16 = out_bf16_or_null;
+  return run(&p, 1, stream);
+}
+
+rmsq_status rmsnorm_quant_group_multi(const rmsq_problem* problems, int32_t count, void* stream) {
+  return run(problems, count, stream);
+}
+
+int32_t rmsq_device_supported(int32_t device) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return 0;
+  return device_is_gfx950(device) ? 1 : 0;
+}
+
+size_t rmsq_scale_bytes(int64_t M, int64_t N, int32_t group, int32_t fmt, int32_t scale_layout) {
+  return scale_bytes(M, N, group, fmt, scale_layout);
+}
+
+const char* rmsq_status_string(rmsq_status s) {
+  switch (s) {
+    case RMSQ_OK: return "RMSQ_OK";
+    case RMSQ_ERR_INVALID_ARG: return "RMSQ_ERR_INVALID_ARG";
+    case RMSQ_ERR_UNSUPPORTED: return "RMSQ_ERR_UNSUPPORTED";
+    case RMSQ_ERR_HIP: return "RMSQ_ERR_HIP";
+    default: return "RMSQ_UNKNOWN_STATUS";
+  }
+}
+
+const char* rmsq_last_error(void) { return g_err; }
+
+// Measurement hook: force the launch shape (chunk-steps per lane J, waves per
+// row W) of later calls in this process; 0, 0 restores the automatic choice.
+// Shapes that cannot cover a row are ignored.
+void rmsq_set_shape(int32_t J, int32_t W) {
+  g_force_J.store(J);
+  g_force_W.store(W);
+}
+
+}  // extern "C"

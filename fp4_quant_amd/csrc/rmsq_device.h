@@ -1,0 +1,224 @@
+// rmsq_device.h - device-side number formats and cross-lane helpers for gfx950.
+//
+// Conversions go through the CDNA4 hardware convert instructions
+// (v_cvt_pk_bf16_f32, v_cvt_pk_fp8_f32, v_cvt_scalef32_pk_fp4_f32), all
+// round-to-nearest-even. Where an fp32 intermediate could double-round, the
+// value is first rounded to odd in fp32 (f64_to_f32_odd): rounding to odd
+// with at least two extra bits and then to nearest even equals a single
+// rounding to nearest even (Boldo & Melquiond, "When double rounding is odd").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmsq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16 halves of a packed dword, widened to fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// double -> float rounded to odd: the float neighbour of v with an odd last
+// bit when v is not a float, v itself otherwise. Overflow gives the largest
+// finite float, underflow the least subnormal (both odd), sign kept.
+__device__ __forceinline__ float f64_to_f32_odd(double v) {
+  float t = (float)v;                       // nearest even
+  uint32_t b = __float_as_uint(t);
+  double back = (double)t;
+  if (back != v && (b & 1u) == 0u) b += (__builtin_fabs(v) > __builtin_fabs(back)) ? 1u : 0xFFFFFFFFu;
+  return __uint_as_float(b);
+}
+
+// bf16 nearest-even of a double (one rounding): round to odd in fp32, then
+// the hardware nearest-even bf16 convert. Returns the 16-bit pattern.
+__device__ __forceinline__ uint32_t bf16_from_f64(double v) {
+  return pack_bf16(f64_to_f32_odd(v), 0.0f) & 0xFFFFu;
+}
+
+// Two fp32 -> two e4m3fn bytes (a in the lower byte), nearest even, written
+// into the low (HI_WORD false) or high 16 bits of `old` (v_cvt_pk_fp8_f32;
+// gfx950 uses the OCP e4m3fn encoding). The caller keeps |v| < 464 so
+// nothing saturates.
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI_WORD);
+}
+
+// Two fp32 -> two e2m1 nibbles (a low, b high) in byte `sel` of `old`, nearest
+// even with saturation at 6 (v_cvt_scalef32_pk_fp4_f32 with scale 1).
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2(float a, float b, uint32_t old) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// e4m3fn byte of the exact quotient v / s for the rare cases the fast path
+// cannot decide: the quotient in double is within 2^-53 relative of the
+// exact one, and a non-tie quotient of a bf16 value by an fp32 value sits at
+// least 2^-29 relative away from every e4m3fn rounding midpoint, so rounding
+// the double (to odd in fp32, then to nearest even in hardware) decides as
+// the exact quotient would.
+__device__ __forceinline__ uint32_t fp8_exact(float v, float s) {
+  float t = f64_to_f32_odd((double)v / (double)s);
+  return cvt_fp8x2<false>(t, t, 0u) & 0xFFu;
+}
+
+// ------------------------------------------------------- element blocks --
+// The per-chunk arithmetic of the fused kernel, on 8 consecutive elements.
+
+__device__ __forceinline__ bool near_bf16_midpoint(float y) {
+  return ((__float_as_uint(y) & 0xFFFFu) - 0x7FFCu) <= 8u;
+}
+
+// p within 8 ulp of an e4m3fn rounding midpoint (normal range), or
+// 0 < |p| < 2^-6 (the e4m3fn subnormal range, where the midpoints sit at a
+// fixed spacing the bit test does not see).
+__device__ __forceinline__ bool fp8_undecided(float p) {
+  const uint32_t u = __float_as_uint(p);
+  return ((u & 0x7FFFFFFFu) - 1u) < 0x3C7FFFFFu || ((u & 0xFFFFFu) - 0x7FFF8u) <= 16u;
+}
+
+// bf16(hg * inv) for 8 elements, hg = h * gamma (exact in fp32), inv the fp64
+// inverse norm and inv32 = fl32(inv). The fp32 product is within 2 ulp of the
+// fp64 one, so its bf16 rounding is final unless it lies within 4 ulp of a
+// bf16 midpoint; those elements (all of them when row_exact) are redone from
+// the fp64 product with a single rounding.
+__device__ __forceinline__ u32x4 norm_bf16x8(const float hg[8], float inv32, double inv, bool row_exact) {
+  u32x4 yw;
+  bool need = row_exact;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float y0 = hg[2 * i] * inv32, y1 = hg[2 * i + 1] * inv32;
+    need = need || near_bf16_midpoint(y0) || near_bf16_midpoint(y1);
+    yw[i] = pack_bf16(y0, y1);
+  }
+  if (need) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (row_exact || near_bf16_midpoint(hg[e] * inv32)) {
+        const uint32_t b = bf16_from_f64((double)hg[e] * inv);
+        const int sh = (e & 1) * 16;
+        yw[e >> 1] = (yw[e >> 1] & ~(0xFFFFu << sh)) | (b << sh);
+      }
+    }
+  }
+  return yw;
+}
+
+// FP8 scale of a group from its amax (a bf16 magnitude pattern): amax / 448
+// as an IEEE fp32 division (the compiler's correctly rounded sequence, fp32
+// denormals kept), 1.0 for an all-zero group.
+__device__ __forceinline__ float fp8_scale(uint32_t amax_bits) {
+  return amax_bits ? __uint_as_float(amax_bits << 16) / 448.0f : 1.0f;
+}
+
+// e4m3fn codes of v[e] / s for 8 bf16 values v (as fp32) of one group, bytes
+// in element order. p = v * rcp(s) is within 3 ulp of the exact quotient
+// (v_rcp_f32 is within 1 ulp); a code is final unless p is undecided, or s is
+// so small that rcp(s) leaves the normal range, and then the exact path
+// decides.
+__device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
+  const float rs = __builtin_amdgcn_rcpf(s);
+  const bool tiny = s < 0x1p-100f;
+  float p[8];
+  bool need = tiny;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = v[e] * rs;
+    need = need || fp8_undecided(p[e]);
+  }
+  u32x2 qw;
+  qw[0] = cvt_fp8x2<true>(p[2], p[3], cvt_fp8x2<false>(p[0], p[1], 0u));
+  qw[1] = cvt_fp8x2<true>(p[6], p[7], cvt_fp8x2<false>(p[4], p[5], 0u));
+  if (need) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (tiny || fp8_undecided(p[e])) {
+        const uint32_t b = fp8_exact(v[e], s);
+        const int sh = (e & 3) * 8;
+        qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
+      }
+    }
+  }
+  return qw;
+}
+
+// MXFP4 e8m0 scale byte of a group from its amax (bf16 magnitude pattern):
+// e = floor(log2 amax) - 2 clamped to [-127, 127], byte = e + 127, which is
+// the bf16 exponent field of amax minus 2 (0 for subnormal amax), and 127
+// (scale 1) for an all-zero group.
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
+  const uint32_t E = amax_bits >> 7;
+  return amax_bits == 0 ? 127u : (E >= 2u ? E - 2u : 0u);
+}
+
+// e2m1 codes of v[e] * 2^-(byte-127) for 8 values, packed two per byte with
+// the even element in the low nibble. byte <= 252 (bf16 exponents stop at
+// 254), so 2^-e = 2^(127-byte) is a normal fp32 and every product is exact.
+__device__ __forceinline__ uint32_t fp4_codes8(const float v[8], uint32_t byte) {
+  const float f = __uint_as_float((254u - byte) << 23);
+  uint32_t w = cvt_fp4x2<0>(v[0] * f, v[1] * f, 0u);
+  w = cvt_fp4x2<1>(v[2] * f, v[3] * f, w);
+  w = cvt_fp4x2<2>(v[4] * f, v[5] * f, w);
+  w = cvt_fp4x2<3>(v[6] * f, v[7] * f, w);
+  return w;
+}
+
+// ---------------------------------------------------------------- lanes --
+// Rotate within each row of 16 lanes (DPP row_ror).
+template <int N>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xF, 0xF, false);
+}
+// Swap within quads: lane i reads lane i^1 (quad_perm [1,0,3,2]) or i^2 ([2,3,0,1]).
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+
+// max over the 16 lanes of a DPP row; every lane of the row gets the result.
+__device__ __forceinline__ uint32_t max16(uint32_t v) {
+  v = max(v, row_ror<8>(v));
+  v = max(v, row_ror<4>(v));
+  v = max(v, row_ror<2>(v));
+  v = max(v, row_ror<1>(v));
+  return v;
+}
+// max over a quad of lanes.
+__device__ __forceinline__ uint32_t max4(uint32_t v) {
+  v = max(v, quad_xor1(v));
+  v = max(v, quad_xor2(v));
+  return v;
+}
+
+// Sum over the 64 lanes of a wave in a fixed tree order; all lanes get it.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Largest |value| of eight packed bf16 (four dwords), as a bf16 magnitude
+// pattern: integer max of (bits & 0x7FFF) orders bf16 magnitudes exactly.
+__device__ __forceinline__ uint32_t amax8(u32x4 w) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a = w[i] & 0x7FFF7FFFu;
+    m = max(m, max(a & 0xFFFFu, a >> 16));
+  }
+  return m;
+}
+
+}  // namespace rmsq

@@ -1,0 +1,196 @@
+// rmsq_kernel.h - the fused residual-add + RMSNorm + per-group quantization
+// kernel for gfx950.
+//
+// Sources, cited by title:
+//   [FRQ] "fused rmsnorm quant fp8 work"
+//   [ARQ] "[AMD] Add fused all-reduce RMSNorm per-group quant for Qwen3.5 FP8"
+//   [ATF] "[Feat] Support input_rmsnorm_quant & qknorm_quant fused for Atom
+//          dpsk v2 model"
+//   [ATT] "[Triton] DS FP4/FP8 Triton fusion and GEMM optimization"
+//
+// Mapping. One workgroup per token row, 64*W threads (W waves, runtime),
+// each lane owning J chunks of 8 bf16 (16 bytes): chunk c = j*64*W + lane.
+// Loads and stores are 16-byte and coalesced across the wave. A 128-element
+// FP8 group is 16 consecutive chunks, i.e. one 16-lane DPP row, so its amax
+// is four DPP row rotations; a 32-element MXFP4 group is one lane quad.
+//
+// Numerics (results equal the double-precision definition bit for bit):
+//  * h = bf16(x + r): the fp32 sum rounds to the same bf16 as the exact sum.
+//  * sum of h^2 in fp64 (each square exact), wave tree + LDS across waves,
+//    inv = 1/sqrt(ss/N + eps) in fp64 with correctly rounded divide / sqrt.
+//  * y = (h*g) * inv: h*g is exact in fp32; the product is first taken in
+//    fp32 with fl32(inv) (within 2 ulp of the fp64 product); only when it
+//    lands within 4 ulp of a bf16 rounding midpoint is the element redone as
+//    fp64 (h*g)*inv rounded once to bf16.
+//  * FP8 scale s = amax/448 as an IEEE fp32 division; codes from
+//    p = yb * rcp(s) (within 3 ulp of yb/s) through the hardware convert;
+//    elements whose p is within 8 ulp of an e4m3fn midpoint, in the e4m3fn
+//    subnormal range, or in a group with a tiny scale take the exact path.
+//  * MXFP4 scale byte from the bf16 exponent of amax; codes from the exact
+//    product yb * 2^-e through the hardware e2m1 convert.
+#pragma once
+
+#include "rmsq_device.h"
+
+namespace rmsq {
+
+struct Problem {
+  const uint16_t* x;
+  const uint16_t* r;      // residual in, or null
+  uint16_t* h;            // residual out (null exactly when r is null)
+  const uint16_t* gamma;
+  uint8_t* q;
+  void* scale;
+  uint16_t* yb;           // bf16 side-output, or null
+  int64_t ldx, ldr, ldb;  // row strides in elements
+  int32_t M, N;
+  int32_t row_begin;      // first launch row of this problem
+  int32_t layout;         // MXFP4 scale layout: 0 row-major, 1 32-row tiles
+  float eps;
+};
+
+constexpr int kMaxProblems = 4;
+constexpr int kMaxWaves = 16;
+// Long per-lane rows (J >= 7 chunks) keep up to ~120 VGPRs of row data live;
+// they are launched with at most 4 waves per row so the register budget is
+// not cut to 128 by a 1024-thread bound.
+constexpr int max_waves(int J) { return J >= 7 ? 4 : kMaxWaves; }
+
+struct Launch {
+  Problem p[kMaxProblems];
+  int32_t count;
+  int32_t rows;           // grid size: one workgroup per row over all problems
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2). Give XCD x a contiguous run of rows so that scale lines shared by
+// neighbouring rows (and the rows of a 32-row scale tile) stay in one L2.
+__device__ __forceinline__ int32_t xcd_row(int32_t b, int32_t rows) {
+  const int32_t x = b & 7, k = b >> 3, q = rows >> 3, rem = rows & 7;
+  return x < rem ? x * (q + 1) + k : rem * (q + 1) + (x - rem) * q + k;
+}
+
+template <int FMT, int J>
+__global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Launch L) {
+  __shared__ double red[kMaxWaves];
+
+  const int32_t row = xcd_row((int32_t)blockIdx.x, L.rows);
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProblems; ++i)
+    if (i < L.count && row >= L.p[i].row_begin) pi = i;
+  const Problem& P = L.p[pi];
+
+  const int64_t m = row - P.row_begin;
+  const int T = blockDim.x;
+  const int tid = threadIdx.x;
+  const int C = P.N >> 3;
+  const bool has_res = P.r != nullptr;
+
+  // ---- phase 1: h = x (+ r), write h, sum of squares ---------------------
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(P.x + m * P.ldx);
+  u32x4 h[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = j * T + tid;
+    if (c < C) h[j] = __builtin_nontemporal_load(xrow + c);
+  }
+  if (has_res) {
+    const u32x4* rrow = reinterpret_cast<const u32x4*>(P.r + m * P.ldr);
+    u32x4* hrow = reinterpret_cast<u32x4*>(P.h + m * P.ldr);
+    u32x4 rv[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = j * T + tid;
+      if (c < C) rv[j] = __builtin_nontemporal_load(rrow + c);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = j * T + tid;
+      if (c < C) {
+        u32x4 s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[i] = pack_bf16(bf16_lo(h[j][i]) + bf16_lo(rv[j][i]), bf16_hi(h[j][i]) + bf16_hi(rv[j][i]));
+        h[j] = s;
+        __builtin_nontemporal_store(s, hrow + c);
+      }
+    }
+  }
+
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = j * T + tid;
+    if (c < C) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double a = bf16_lo(h[j][i]), b = bf16_hi(h[j][i]);
+        ss = __builtin_fma(a, a, ss);
+        ss = __builtin_fma(b, b, ss);
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  const int nw = T >> 6;
+  if (nw > 1) {
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    ss = 0.0;
+    for (int w = 0; w < nw; ++w) ss += red[w];
+  }
+  const double denom = ss / (double)P.N + (double)P.eps;
+  const double inv = denom > 0.0 ? 1.0 / __builtin_sqrt(denom) : 0.0;
+  const float inv32 = (float)inv;
+  // rows whose inverse norm leaves the comfortable fp32 range take the exact
+  // path for every element
+  const bool row_exact = inv > 0x1p100 || (inv != 0.0 && inv < 0x1p-100);
+
+  // ---- phase 2: normalize, bf16, group scale, codes -----------------------
+  const u32x4* grow = reinterpret_cast<const u32x4*>(P.gamma);
+  u32x4* ybrow = P.yb ? reinterpret_cast<u32x4*>(P.yb + m * P.ldb) : nullptr;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = j * T + tid;
+    if (c >= C) continue;
+    const u32x4 g = grow[c];
+    float hg[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hg[2 * i] = bf16_lo(h[j][i]) * bf16_lo(g[i]);
+      hg[2 * i + 1] = bf16_hi(h[j][i]) * bf16_hi(g[i]);
+    }
+    const u32x4 yw = norm_bf16x8(hg, inv32, inv, row_exact);
+    if (ybrow) __builtin_nontemporal_store(yw, ybrow + c);
+
+    const uint32_t am = amax8(yw);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(yw[i]);
+      v[2 * i + 1] = bf16_hi(yw[i]);
+    }
+
+    if constexpr (FMT == 0) {
+      // FP8 e4m3fn, group 128 = one 16-lane DPP row
+      const float sc = fp8_scale(max16(am));
+      const u32x2 qw = fp8_codes8(v, sc);
+      u32x2* qrow = reinterpret_cast<u32x2*>(P.q + m * (int64_t)P.N);
+      __builtin_nontemporal_store(qw, qrow + c);
+      if ((tid & 15) == 0) reinterpret_cast<float*>(P.scale)[m * (P.N >> 7) + (c >> 4)] = sc;
+    } else {
+      // MXFP4 e2m1, group 32 = one lane quad
+      const uint32_t byte = mx_scale_byte(max4(am));
+      const uint32_t w = fp4_codes8(v, byte);
+      uint32_t* qrow = reinterpret_cast<uint32_t*>(P.q + m * (int64_t)(P.N >> 1));
+      __builtin_nontemporal_store(w, qrow + c);
+      if ((tid & 3) == 0) {
+        const int64_t gcount = P.N >> 5, gi = c >> 2;
+        const int64_t off = P.layout == 0 ? m * gcount + gi : (m >> 5) * (32 * gcount) + gi * 32 + (m & 31);
+        reinterpret_cast<uint8_t*>(P.scale)[off] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
+}  // namespace rmsq

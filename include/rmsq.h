@@ -1,0 +1,159 @@
+/*
+ * rmsq.h - C ABI of the fused residual-add + RMSNorm + per-group dynamic
+ * quantization library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation follows four pull-request pages, cited by title:
+ *   [FRQ]  "fused rmsnorm quant fp8 work"
+ *   [ARQ]  "[AMD] Add fused all-reduce RMSNorm per-group quant for Qwen3.5 FP8"
+ *   [ATF]  "[Feat] Support input_rmsnorm_quant & qknorm_quant fused for Atom
+ *           dpsk v2 model"
+ *   [ATT]  "[Triton] DS FP4/FP8 Triton fusion and GEMM optimization"
+ *
+ * Per token row (all arithmetic on the device, one kernel launch per call):
+ *   h  = bf16(x + residual_in)            (h = x without a residual)
+ *   y  = h * gamma / sqrt(mean(h^2) + eps)
+ *   yb = bf16(y)                          (optional side-output)
+ *   per group of G columns: scale from max |yb|, codes = quantize(yb / scale)
+ *     FP8:   G = 128, scale = amax / 448 in fp32, codes are OCP e4m3fn bytes
+ *     MXFP4: G = 32, scale = 2^(floor(log2 amax) - 2) stored as an e8m0 byte,
+ *            codes are e2m1 nibbles, two per byte, element 2k in the low nibble
+ * Every rounding is to nearest, ties to even; all-zero groups get scale 1.0
+ * (FP8) or byte 127 (MXFP4). Results are bit-for-bit those of the double
+ * precision definition above.
+ *
+ * Conventions shared by every entry point:
+ *  - Data pointers are DEVICE pointers owned by the caller. The library
+ *    allocates no device memory, keeps no per-call state, and never
+ *    synchronizes the host: work is enqueued on `stream` (a hipStream_t;
+ *    NULL is the default stream) and the call returns.
+ *  - bf16 tensors are row-major with a row stride (ld, in elements) that is a
+ *    multiple of 8 and >= N; bf16 pointers are 16-byte aligned. Codes and
+ *    scales are dense: codes [M, N] bytes (FP8) or [M, N/2] (MXFP4); scales
+ *    [M, N/128] fp32 (FP8, 4-byte aligned) or e8m0 bytes (MXFP4, see the
+ *    layouts below). FP8 code pointers are 8-byte aligned, MXFP4 ones 4-byte.
+ *  - Outputs must not overlap each other or the inputs, except that
+ *    residual_out may be the very same buffer as residual_in (in place).
+ *  - Validation happens before any HIP call; a status other than RMSQ_OK
+ *    means nothing was enqueued. M == 0 is a no-op returning RMSQ_OK.
+ *  - Non-finite inputs are outside the contract (no fault, undefined values).
+ *  - Thread safety: calls are re-entrant; calls on different streams may run
+ *    concurrently.
+ */
+#ifndef RMSQ_H
+#define RMSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t rmsq_status;
+#define RMSQ_OK 0
+#define RMSQ_ERR_INVALID_ARG 1 /* bad pointer, alignment, stride, shape or overlap */
+#define RMSQ_ERR_UNSUPPORTED 2 /* not a gfx950 device, or format/group/N outside what is built */
+#define RMSQ_ERR_HIP 3         /* the HIP runtime reported an error at launch */
+
+#define RMSQ_FMT_FP8_E4M3FN 0  /* group 128, fp32 scales            */
+#define RMSQ_FMT_MXFP4_E2M1 1  /* group 32, e8m0 scales, packed e2m1 */
+
+/* Scale layouts. FP8 scales are always row-major. MXFP4 e8m0 scales are either
+ * row-major [M, N/32], or tiled in blocks of 32 rows: byte offset of (m, g) is
+ * (m/32)*(32*N/32) + g*32 + m%32, so the 32 rows' scales of one group are
+ * adjacent; the buffer holds ceil(M/32)*32*(N/32) bytes and the bytes of the
+ * padding rows of the last tile are left untouched. [ATT, review thread]
+ * views the byte scales in tiles of the MXFP4 block size in rows when the
+ * row count reaches it; [ATF, Technical Details] selects the activation scale
+ * layout that the consuming GEMM expects. */
+#define RMSQ_SCALE_ROW_MAJOR 0
+#define RMSQ_SCALE_TILED32 1
+
+#define RMSQ_MAX_PROBLEMS 4
+#define RMSQ_N_MAX 32768
+
+/*
+ * Fused residual add + RMSNorm + per-group dynamic quantization of M rows of
+ * N bf16 values, contiguous rows (ld = N), row-major scales.
+ * [FRQ, Motivation]: RMSNorm and FP8 group quantization with group size 128
+ * in one kernel. [ARQ, Modifications]: results ((codes, scale), residual) or,
+ * with the bf16 side-output, ((bf16, codes, scale), residual).
+ * [ARQ, kernel count table]: replaces the add + RMSNorm kernel and the
+ * dynamic per-group quant kernel (and the extra quant of the bf16 path).
+ * [ATF, Technical Details]: the MXFP4 variant.
+ *
+ *  x            [M, N] bf16, read only.
+ *  residual_in  [M, N] bf16 or NULL (no residual add; then residual_out must
+ *               be NULL too, else RMSQ_ERR_INVALID_ARG).
+ *  gamma        [N] bf16 RMSNorm weight.
+ *  eps          finite, >= 0; added to mean(h^2) inside the square root.
+ *  group, fmt   128 with RMSQ_FMT_FP8_E4M3FN, 32 with RMSQ_FMT_MXFP4_E2M1;
+ *               other pairs give RMSQ_ERR_UNSUPPORTED.
+ *  out_q        codes; out_scale: scales (row-major).
+ *  residual_out [M, N] bf16: the bf16 sum h, or NULL.
+ *  out_bf16_or_null [M, N] bf16 normalized rows, or NULL to skip them.
+ *  stream       hipStream_t to enqueue on.
+ * N must be a multiple of the group and at most RMSQ_N_MAX.
+ */
+rmsq_status rmsnorm_quant_group(const void* x, const void* residual_in, const void* gamma,
+                                float eps, int64_t M, int64_t N, int32_t group, int32_t fmt,
+                                void* out_q, void* out_scale, void* residual_out,
+                                void* out_bf16_or_null, void* stream);
+
+/* One independent row problem for rmsnorm_quant_group_multi. ld values are in
+ * elements; 0 means N. ldr is the stride of both residual_in and residual_out. */
+typedef struct rmsq_problem {
+    const void* x;
+    int64_t ldx;
+    const void* residual_in;
+    void* residual_out;
+    int64_t ldr;
+    const void* gamma;
+    float eps;
+    int64_t M;
+    int64_t N;
+    int32_t group;
+    int32_t fmt;
+    int32_t scale_layout;
+    void* out_q;
+    void* out_scale;
+    void* out_bf16;
+    int64_t ldb;
+} rmsq_problem;
+
+/*
+ * 1 to RMSQ_MAX_PROBLEMS independent problems in ONE kernel launch, e.g. the
+ * two latent norms of multi-head latent attention (q and kv), which
+ * [FRQ, Modifications] fuses at the attention module and [ATF, Technical
+ * Details] fuses as "qknorm quant". Each problem is the operation of
+ * rmsnorm_quant_group with its own shapes, strides, residual, side-output
+ * and scale layout; all problems use the same fmt. The problem array is read
+ * on the host during the call and may be freed when it returns.
+ */
+rmsq_status rmsnorm_quant_group_multi(const rmsq_problem* problems, int32_t count, void* stream);
+
+/* 1 if HIP device `device` is a gfx950 (MI355X-class) GPU, else 0.
+ * [ARQ, Motivation]: the single-kernel path is gated to gfx95x devices and
+ * callers fall back otherwise; this library's entry points return
+ * RMSQ_ERR_UNSUPPORTED on other devices. */
+int32_t rmsq_device_supported(int32_t device);
+
+/* Bytes of the scale buffer for a problem (0 for an invalid combination). */
+size_t rmsq_scale_bytes(int64_t M, int64_t N, int32_t group, int32_t fmt, int32_t scale_layout);
+
+/* Static, human-readable name of a status code. */
+const char* rmsq_status_string(rmsq_status s);
+
+/* Message of the last validation or HIP error on the calling thread, or "". */
+const char* rmsq_last_error(void);
+
+/* Measurement hook: force the launch shape of later calls in this process:
+ * J 16-byte chunks per lane (one of 1, 2, 3, 4, 7, 8, 14) and W waves (1..16)
+ * per row. Shapes that cannot cover a row, and (0, 0), restore the automatic
+ * choice. Results do not depend on the shape. */
+void rmsq_set_shape(int32_t J, int32_t W);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

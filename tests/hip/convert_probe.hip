@@ -1,0 +1,138 @@
+// convert_probe.hip - test-only library: runs the fused kernel's per-element
+// number helpers (fp4_quant_amd/csrc/rmsq_device.h) and the raw gfx950
+// convert instructions on arrays, so that tests can compare them with the CPU
+// oracle over exhaustive and adversarial inputs. Every kernel is a bounds-
+// checked grid-stride loop over n items.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rmsq_device.h"
+
+using namespace rmsq;
+
+#define GRID_LOOP(i, n) \
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < (n); i += (int64_t)gridDim.x * blockDim.x)
+
+__global__ void k_norm_bf16(const float* hg, const double* inv, const uint8_t* row_exact, uint16_t* out, int64_t n) {
+  GRID_LOOP(k, n) {
+    float h[8];
+    for (int e = 0; e < 8; ++e) h[e] = hg[8 * k + e];
+    const u32x4 w = norm_bf16x8(h, (float)inv[k], inv[k], row_exact[k] != 0);
+    for (int e = 0; e < 8; ++e) out[8 * k + e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+  }
+}
+
+__global__ void k_fp8_scale(const uint16_t* amax, float* s, int64_t n) {
+  GRID_LOOP(i, n) s[i] = fp8_scale(amax[i]);
+}
+
+__global__ void k_fp8_codes(const float* v, const float* s, uint8_t* out, int64_t n) {
+  GRID_LOOP(k, n) {
+    float x[8];
+    for (int e = 0; e < 8; ++e) x[e] = v[8 * k + e];
+    const u32x2 q = fp8_codes8(x, s[k]);
+    for (int e = 0; e < 8; ++e) out[8 * k + e] = (uint8_t)(q[e >> 2] >> ((e & 3) * 8));
+  }
+}
+
+__global__ void k_mx_byte(const uint16_t* amax, uint8_t* out, int64_t n) {
+  GRID_LOOP(i, n) out[i] = (uint8_t)mx_scale_byte(amax[i]);
+}
+
+__global__ void k_fp4_codes(const float* v, const uint8_t* byte, uint32_t* out, int64_t n) {
+  GRID_LOOP(k, n) {
+    float x[8];
+    for (int e = 0; e < 8; ++e) x[e] = v[8 * k + e];
+    out[k] = fp4_codes8(x, byte[k]);
+  }
+}
+
+__global__ void k_cvt_bf16(const float* in, uint16_t* out, int64_t n) {
+  GRID_LOOP(i, n) out[i] = (uint16_t)(pack_bf16(in[i], 0.0f) & 0xFFFFu);
+}
+
+__global__ void k_cvt_fp8(const float* in, uint8_t* out, int64_t n) {  // n pairs
+  GRID_LOOP(k, n) {
+    const uint32_t w = cvt_fp8x2<true>(in[2 * k], in[2 * k + 1], cvt_fp8x2<false>(in[2 * k + 1], in[2 * k], 0u));
+    out[4 * k + 0] = (uint8_t)w;          // low word: (b, a)
+    out[4 * k + 1] = (uint8_t)(w >> 8);
+    out[4 * k + 2] = (uint8_t)(w >> 16);  // high word: (a, b)
+    out[4 * k + 3] = (uint8_t)(w >> 24);
+  }
+}
+
+__global__ void k_cvt_fp4(const float* in, uint8_t* out, int64_t n) {  // n groups of 8
+  GRID_LOOP(k, n) {
+    const float* a = in + 8 * k;
+    uint32_t w = cvt_fp4x2<0>(a[0], a[1], 0u);
+    w = cvt_fp4x2<1>(a[2], a[3], w);
+    w = cvt_fp4x2<2>(a[4], a[5], w);
+    w = cvt_fp4x2<3>(a[6], a[7], w);
+    for (int b = 0; b < 4; ++b) out[4 * k + b] = (uint8_t)(w >> (8 * b));
+  }
+}
+
+__global__ void k_f64_to_bf16(const double* in, uint16_t* out, int64_t n) {
+  GRID_LOOP(i, n) out[i] = (uint16_t)bf16_from_f64(in[i]);
+}
+
+__global__ void k_fp8_exact(const float* v, const float* s, uint8_t* out, int64_t n) {
+  GRID_LOOP(i, n) out[i] = (uint8_t)fp8_exact(v[i], s[i]);
+}
+
+static int launch_status() { return hipGetLastError() == hipSuccess ? 0 : 3; }
+
+#define GRID(n) dim3((unsigned)(((n) + 255) / 256 < 65536 ? ((n) + 255) / 256 : 65536)), dim3(256), 0, (hipStream_t)stream
+
+extern "C" {
+int probe_norm_bf16(const float* hg, const double* inv, const uint8_t* ex, uint16_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_norm_bf16, GRID(n), hg, inv, ex, out, n);
+  return launch_status();
+}
+int probe_fp8_scale(const uint16_t* a, float* s, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_fp8_scale, GRID(n), a, s, n);
+  return launch_status();
+}
+int probe_fp8_codes(const float* v, const float* s, uint8_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_fp8_codes, GRID(n), v, s, out, n);
+  return launch_status();
+}
+int probe_mx_byte(const uint16_t* a, uint8_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_mx_byte, GRID(n), a, out, n);
+  return launch_status();
+}
+int probe_fp4_codes(const float* v, const uint8_t* b, uint32_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_fp4_codes, GRID(n), v, b, out, n);
+  return launch_status();
+}
+int probe_cvt_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_cvt_bf16, GRID(n), in, out, n);
+  return launch_status();
+}
+int probe_cvt_fp8(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_cvt_fp8, GRID(n), in, out, n);
+  return launch_status();
+}
+int probe_cvt_fp4(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_cvt_fp4, GRID(n), in, out, n);
+  return launch_status();
+}
+int probe_f64_to_bf16(const double* in, uint16_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_f64_to_bf16, GRID(n), in, out, n);
+  return launch_status();
+}
+int probe_fp8_exact(const float* v, const float* s, uint8_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_fp8_exact, GRID(n), v, s, out, n);
+  return launch_status();
+}
+}

@@ -1,0 +1,166 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and validates arguments before touching the GPU. Pointers
+here are fake addresses that are never dereferenced: validation needs only
+their values."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp4_quant_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+A = 0x7F0000000000          # fake, 256-byte aligned device addresses
+MB = 1 << 20
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"rmsnorm_quant_group", "rmsnorm_quant_group_multi", "rmsq_device_supported"} <= set(names)
+    L = fq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(fq.EXPORTS) <= set(names)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of rmsq_problem has the C compiler's layout."""
+    fields = [f for f, _ in fq.rmsq_problem._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join(f'printf("%zu\\n", offsetof(rmsq_problem, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "rmsq.h"\n'
+                   f'int main(void){{printf("%zu\\n", sizeof(rmsq_problem));{body}return 0;}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == C.sizeof(fq.rmsq_problem)
+    assert got[1:] == [getattr(fq.rmsq_problem, f).offset for f in fields]
+
+
+def test_status_strings():
+    L = fq.lib()
+    assert L.rmsq_status_string(0) == b"RMSQ_OK"
+    assert L.rmsq_status_string(1) == b"RMSQ_ERR_INVALID_ARG"
+    assert L.rmsq_status_string(2) == b"RMSQ_ERR_UNSUPPORTED"
+    assert L.rmsq_status_string(3) == b"RMSQ_ERR_HIP"
+    assert L.rmsq_status_string(99) == b"RMSQ_UNKNOWN_STATUS"
+
+
+def test_scale_bytes():
+    assert fq.rmsq_scale_bytes(8192, 7168, 128, 0) == 8192 * 56 * 4
+    assert fq.rmsq_scale_bytes(16384, 7168, 32, 1, 0) == 16384 * 224
+    assert fq.rmsq_scale_bytes(33, 7168, 32, 1, 1) == 64 * 224
+    assert fq.rmsq_scale_bytes(0, 7168, 32, 1, 1) == 0
+    assert fq.rmsq_scale_bytes(8, 7168, 32, 0, 0) == 0          # FP8 needs group 128
+    assert fq.rmsq_scale_bytes(8, 7168, 128, 0, 1) == 0         # tiled is MXFP4 only
+    assert fq.rmsq_scale_bytes(8, 100, 32, 1, 0) == 0
+
+
+def _call(x=A, r=None, g=A + 100 * MB, eps=1e-6, M=4, N=256, group=128, fmt=0,
+          q=A + 200 * MB, s=A + 300 * MB, ro=None, yb=None):
+    L = fq.lib()
+    return L.rmsnorm_quant_group(x, r, g, eps, M, N, group, fmt, q, s, ro, yb, None)
+
+
+def _multi(**kw):
+    base = dict(x=A, ldx=0, residual_in=None, residual_out=None, ldr=0, gamma=A + 100 * MB, eps=1e-6,
+                M=4, N=256, group=128, fmt=0, scale_layout=0, out_q=A + 200 * MB, out_scale=A + 300 * MB,
+                out_bf16=None, ldb=0)
+    probs = kw.pop("probs", None)
+    if probs is None:
+        base.update(kw)
+        probs = [base]
+    arr = (fq.rmsq_problem * len(probs))(*[fq.rmsq_problem(**p) for p in probs])
+    return fq.lib().rmsnorm_quant_group_multi(arr, len(probs), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(group=64), fq.RMSQ_ERR_UNSUPPORTED),
+    (dict(fmt=1, group=128), fq.RMSQ_ERR_UNSUPPORTED),
+    (dict(fmt=7), fq.RMSQ_ERR_UNSUPPORTED),
+    (dict(N=65536), fq.RMSQ_ERR_UNSUPPORTED),
+    (dict(N=200), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(N=0), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(M=-1), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(eps=-1.0), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(r=A + 400 * MB), fq.RMSQ_ERR_INVALID_ARG),            # residual_in without residual_out
+    (dict(ro=A + 400 * MB), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(x=None), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(q=None), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(s=None), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(g=None), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(x=A + 8), fq.RMSQ_ERR_INVALID_ARG),                   # bf16 pointers 16-byte aligned
+    (dict(g=A + 100 * MB + 2), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(yb=A + 500 * MB + 4), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(q=A + 200 * MB + 4), fq.RMSQ_ERR_INVALID_ARG),        # FP8 codes 8-byte aligned
+    (dict(s=A + 300 * MB + 2), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(q=A + 100), fq.RMSQ_ERR_INVALID_ARG),                  # codes overlap x
+    (dict(yb=A + 200 * MB), fq.RMSQ_ERR_INVALID_ARG),           # bf16 overlaps codes
+    (dict(s=A + 200 * MB + 512), fq.RMSQ_ERR_INVALID_ARG),      # scales inside the 1 KiB of codes
+    (dict(r=A + 400 * MB, ro=A + 400 * MB + 16), fq.RMSQ_ERR_INVALID_ARG),  # partial in-place
+    (dict(r=A + 400 * MB, ro=A), fq.RMSQ_ERR_INVALID_ARG),      # residual_out over x
+])
+def test_validation_errors(kw, status):
+    assert _call(**kw) == status
+    assert fq.lib().rmsq_last_error()
+
+
+def test_m_zero_is_a_noop_without_device():
+    assert _call(M=0) == fq.RMSQ_OK
+    assert _call(M=0, x=None, q=None, s=None, g=None) == fq.RMSQ_OK
+
+
+def test_valid_call_without_a_gfx950_device_is_unsupported():
+    if fq.rmsq_device_supported(0):
+        pytest.skip("a gfx950 device is present")
+    assert _call() == fq.RMSQ_ERR_UNSUPPORTED
+    assert _call(r=A + 400 * MB, ro=A + 400 * MB) == fq.RMSQ_ERR_UNSUPPORTED   # in place is valid
+    assert b"gfx950" in fq.lib().rmsq_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ldx=100), fq.RMSQ_ERR_INVALID_ARG),                   # stride not a multiple of 8
+    (dict(ldx=128), fq.RMSQ_ERR_INVALID_ARG),                   # stride < N
+    (dict(out_bf16=A + 500 * MB, ldb=260), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(scale_layout=1), fq.RMSQ_ERR_UNSUPPORTED),            # tiled scales with FP8
+    (dict(scale_layout=2), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(fmt=1, group=32, scale_layout=1, out_q=A + 200 * MB + 4, out_scale=A + 300 * MB + 1),
+     fq.RMSQ_ERR_UNSUPPORTED),                                 # valid MXFP4 tiled: no device here
+])
+def test_multi_validation(kw, status):
+    if status == fq.RMSQ_ERR_UNSUPPORTED and fq.rmsq_device_supported(0) and kw.get("fmt") == 1:
+        pytest.skip("a gfx950 device is present")
+    assert _multi(**kw) == status
+
+
+def test_multi_count_and_shared_fmt():
+    L = fq.lib()
+    assert L.rmsnorm_quant_group_multi(None, 1, None) == fq.RMSQ_ERR_INVALID_ARG
+    p = dict(x=A, ldx=0, residual_in=None, residual_out=None, ldr=0, gamma=A + 100 * MB, eps=1e-6,
+             M=4, N=256, group=128, fmt=0, scale_layout=0, out_q=A + 200 * MB, out_scale=A + 300 * MB,
+             out_bf16=None, ldb=0)
+    p2 = dict(p, x=A + 600 * MB, out_q=A + 700 * MB, out_scale=A + 800 * MB, fmt=1, group=32)
+    assert _multi(probs=[p] * 5) == fq.RMSQ_ERR_INVALID_ARG
+    assert _multi(probs=[p, p2]) == fq.RMSQ_ERR_INVALID_ARG
+    # two problems whose outputs collide
+    p3 = dict(p, x=A + 600 * MB)
+    assert _multi(probs=[p, p3]) == fq.RMSQ_ERR_INVALID_ARG
+
+
+def test_set_shape_is_callable():
+    fq.rmsq_set_shape(14, 1)
+    fq.rmsq_set_shape(0, 0)

@@ -1,0 +1,193 @@
+"""The kernel's per-element number helpers and the raw gfx950 converts,
+checked on the GPU against the CPU oracle over exhaustive and adversarial
+inputs (test-only probe library, tests/hip/convert_probe.hip)."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import bf16_f64, call_probe, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+ALL16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+FIN16 = ALL16[((ALL16 >> 7) & 0xFF) != 0xFF]
+MAG16 = FIN16[FIN16 < 0x8000]                 # +0 and every positive finite bf16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import fp4_quant_amd as fq
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert fq.rmsq_device_supported(0), "GPU tests need a gfx950 device"
+
+
+def _f32(bits16):
+    return (bits16.astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------ raw converts --
+def test_hw_bf16_convert_is_round_to_nearest_even():
+    say("raw v_cvt_pk_bf16_f32")
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2 ** 32, 4_000_000, dtype=np.uint64).astype(np.uint32)
+    mids = (FIN16.astype(np.uint32) << 16) | 0x8000
+    bits = np.concatenate([bits, mids, mids + 1, mids - 1, FIN16.astype(np.uint32) << 16])
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    out = torch.empty(f.size, dtype=torch.int16, device="cuda")
+    call_probe("probe_cvt_bf16", dev(f), out, n=f.size)
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(host(out), want)
+
+
+def test_hw_fp8_convert_matches_oracle(orc):
+    say("raw v_cvt_pk_fp8_f32")
+    rng = np.random.default_rng(2)
+    v = np.concatenate([_f32(FIN16), rng.uniform(-463.9, 463.9, 2_000_000).astype(np.float32),
+                        (rng.standard_normal(1_000_000) * 2.0 ** -8).astype(np.float32)])
+    # every e4m3fn rounding midpoint and its fp32 neighbours
+    t = orc.e4m3fn_table()
+    mags = np.unique(np.abs(t[~np.isnan(t)]))
+    mids = ((mags[1:] + mags[:-1]) / 2).astype(np.float32)
+    mb = mids.view(np.uint32)
+    v = np.concatenate([v, mids, (mb + 1).view(np.float32), (mb - 1).view(np.float32), -mids, np.float32([0.0, -0.0])])
+    v = v[np.abs(v) < 464]
+    if v.size % 2:
+        v = v[:-1]
+    out = torch.empty(v.size * 2, dtype=torch.uint8, device="cuda")
+    call_probe("probe_cvt_fp8", dev(v), out, n=v.size // 2)
+    o = host(out).reshape(-1, 4)
+    want = orc.e4m3fn_encode(v.astype(np.float64)).reshape(-1, 2)
+    # low word holds (b, a), high word (a, b): the first operand lands in the lower byte
+    assert np.array_equal(o[:, 0], want[:, 1]) and np.array_equal(o[:, 1], want[:, 0])
+    assert np.array_equal(o[:, 2], want[:, 0]) and np.array_equal(o[:, 3], want[:, 1])
+
+
+def test_hw_fp4_convert_matches_oracle(orc):
+    say("raw v_cvt_scalef32_pk_fp4_f32")
+    rng = np.random.default_rng(3)
+    small = _f32(FIN16)
+    small = small[np.abs(small) < 8]
+    v = np.concatenate([small, rng.uniform(-7.999, 7.999, 1_000_000).astype(np.float32),
+                        np.float32(np.arange(-32, 32) / 4.0)])
+    v = v[: v.size // 8 * 8]
+    out = torch.empty(v.size // 2, dtype=torch.uint8, device="cuda")
+    call_probe("probe_cvt_fp4", dev(v), out, n=v.size // 8)
+    o = host(out)
+    got = np.stack([o & 0xF, o >> 4], -1).reshape(-1)
+    want = orc.e2m1_encode(v.astype(np.float64))
+    tab = orc.e2m1_table()
+    assert np.array_equal(tab[got], tab[want])                  # as values (+-0 equal)
+    nz = tab[want] != 0
+    assert np.array_equal(got[nz], want[nz])                      # and as codes when nonzero
+
+
+def test_f64_to_bf16_single_rounding(orc):
+    say("bf16_from_f64")
+    rng = np.random.default_rng(4)
+    base = bf16_f64(FIN16[(FIN16 & 0x7FFF) < 0x7F7F])
+    nxt = bf16_f64(FIN16[(FIN16 & 0x7FFF) < 0x7F7F] + 1)
+    mid = (base + nxt) / 2
+    d = np.concatenate([mid, mid * (1 + 2.0 ** -40), mid * (1 - 2.0 ** -40), mid * (1 + 2.0 ** -52),
+                        mid * (1 - 2.0 ** -52), rng.standard_normal(1_000_000) * 10.0 ** rng.integers(-40, 38, 1_000_000),
+                        np.array([3.4e38, -3.4e38, 1e-45, -1e-46, 0.0, -0.0, 2.0 ** -134, 3 * 2.0 ** -134])])
+    d = d[np.isfinite(d)]
+    out = torch.empty(d.size, dtype=torch.int16, device="cuda")
+    call_probe("probe_f64_to_bf16", dev(d), out, n=d.size)
+    assert np.array_equal(host(out).view(np.uint16), orc.bf16_from_double(d))
+
+
+# ------------------------------------------------------- kernel helpers --
+def test_norm_bf16x8_matches_fp64_rounding(orc):
+    say("norm_bf16x8")
+    rng = np.random.default_rng(5)
+    n = 400_000 * 8
+    h = _f32(rng.choice(FIN16[(FIN16 & 0x7FFF) < 0x4700], n)).astype(np.float64)      # |h| < 32768
+    g = _f32(rng.choice(FIN16[((FIN16 & 0x7FFF) > 0x3E00) & ((FIN16 & 0x7FFF) < 0x4000)], n)).astype(np.float64)
+    hg = (h * g).astype(np.float32)                 # exact: 8 x 8 significant bits
+    assert np.array_equal(hg.astype(np.float64), h * g)
+    inv = 10.0 ** rng.uniform(-3, 2, n // 8)
+    # one chunk in four aims its first product at a bf16 midpoint
+    k = np.arange(0, n // 8, 4)
+    target = hg[8 * k].astype(np.float64)
+    tb = (target.astype(np.float32).view(np.uint32) & 0xFFFF0000) | 0x8000
+    tmid = tb.view(np.float32).astype(np.float64)
+    nz = target != 0
+    inv[k[nz]] = tmid[nz] / target[nz]
+    inv[k[nz]] *= 1 + rng.choice([-1, 0, 1], nz.sum()) * 2.0 ** -52
+    ex = (rng.random(n // 8) < 0.05).astype(np.uint8)
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    call_probe("probe_norm_bf16", dev(hg), dev(inv), dev(ex), out, n=n // 8)
+    want = orc.bf16_from_double(hg.astype(np.float64) * np.repeat(inv, 8))
+    assert np.array_equal(host(out).view(np.uint16), want)
+
+
+def test_fp8_scale_every_amax():
+    say("fp8_scale")
+    out = torch.empty(MAG16.size, dtype=torch.float32, device="cuda")
+    call_probe("probe_fp8_scale", dev(MAG16.view(np.int16).copy()), out, n=MAG16.size)
+    want = _f32(MAG16) / np.float32(448.0)
+    want[0] = 1.0
+    assert np.array_equal(host(out).view(np.uint32), want.view(np.uint32))
+
+
+def _amax_cases(rng):
+    special = np.uint16([0x3F80, 0x4060, 0x40E0, 0x0001, 0x0080, 0x0100, 0x1000, 0x2000, 0x7F7F, 0x4360,
+                         0x43E0, 0x3C00, 0x0C00])
+    return np.concatenate([special, rng.choice(MAG16[MAG16 > 0], 40)])
+
+
+def test_fp8_codes8_every_value_below_amax(orc):
+    """For each group amax, every bf16 value v with |v| <= amax: code =
+    e4m3fn(v / s) exactly, s the group scale."""
+    say("fp8_codes8")
+    rng = np.random.default_rng(6)
+    for amax in _amax_cases(rng):
+        vals = FIN16[(FIN16 & 0x7FFF) <= amax]
+        vals = vals[: vals.size // 8 * 8]
+        s = np.float32(_f32(np.uint16([amax]))[0] / np.float32(448.0))
+        out = torch.empty(vals.size, dtype=torch.uint8, device="cuda")
+        sv = np.full(vals.size // 8, s, np.float32)
+        call_probe("probe_fp8_codes", dev(_f32(vals)), dev(sv), out, n=vals.size // 8)
+        want = orc.e4m3fn_encode(bf16_f64(vals) / np.float64(s))
+        got = host(out)
+        assert np.array_equal(got, want), f"amax 0x{amax:04x}: {np.count_nonzero(got != want)} codes differ"
+
+
+def test_fp8_exact_path(orc):
+    say("fp8_exact")
+    rng = np.random.default_rng(7)
+    v = _f32(rng.choice(FIN16, 1_000_000))
+    s = (np.abs(v.astype(np.float64)) / rng.uniform(1e-3, 448, v.size)).astype(np.float32)
+    s[s == 0] = np.float32(1e-45)
+    s[: 1000] = np.float32(2.0 ** -140)                        # subnormal scales
+    keep = np.abs(v.astype(np.float64) / s.astype(np.float64)) < 448
+    v, s = v[keep], s[keep]
+    out = torch.empty(v.size, dtype=torch.uint8, device="cuda")
+    call_probe("probe_fp8_exact", dev(v), dev(s), out, n=v.size)
+    assert np.array_equal(host(out), orc.e4m3fn_encode(v.astype(np.float64) / s.astype(np.float64)))
+
+
+def test_mx_scale_byte_every_amax(orc):
+    say("mx_scale_byte")
+    out = torch.empty(MAG16.size, dtype=torch.uint8, device="cuda")
+    call_probe("probe_mx_byte", dev(MAG16.view(np.int16).copy()), out, n=MAG16.size)
+    want = np.array([127] + [orc.mx_scale_exponent(a) + 127 for a in bf16_f64(MAG16[1:])], np.uint8)
+    assert np.array_equal(host(out), want)
+
+
+def test_fp4_codes8_every_value_below_amax(orc):
+    say("fp4_codes8")
+    rng = np.random.default_rng(8)
+    tab = orc.e2m1_table()
+    for amax in _amax_cases(rng):
+        vals = FIN16[(FIN16 & 0x7FFF) <= amax]
+        vals = vals[: vals.size // 8 * 8]
+        e = 0 if amax == 0 else orc.mx_scale_exponent(bf16_f64(np.uint16([amax]))[0])
+        byte = np.full(vals.size // 8, e + 127, np.uint8)
+        out = torch.empty(vals.size // 8, dtype=torch.int32, device="cuda")
+        call_probe("probe_fp4_codes", dev(_f32(vals)), dev(byte), out, n=vals.size // 8)
+        w = host(out).view(np.uint32)
+        got = np.stack([(w >> (4 * i)) & 0xF for i in range(8)], -1).reshape(-1)
+        want = orc.e2m1_encode(np.ldexp(bf16_f64(vals), -e))
+        assert np.array_equal(tab[got], tab[want]), f"amax 0x{amax:04x}"

@@ -1,0 +1,331 @@
+"""End-to-end parity of the HIP path (through the C ABI) with the CPU oracle,
+element by element on the same seeded inputs: the workloads at full size,
+shape sweeps with ragged tails, forced launch shapes, and edge cases. Every
+output buffer is surrounded by guard bands that must stay untouched."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_quant_amd as fq
+from fp4_quant_amd import inputs
+from tests.gpu_util import compare, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+SENT = 0xA5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert fq.rmsq_device_supported(0), "GPU tests need a gfx950 device"
+
+
+class Guarded:
+    """A device output buffer with sentinel bytes before and after it."""
+
+    def __init__(self, nbytes, dtype, shape):
+        self.buf = torch.full((GUARD + nbytes + GUARD,), SENT, dtype=torch.uint8, device="cuda")
+        self.n = nbytes
+        self.t = self.buf[GUARD:GUARD + nbytes].view(dtype).view(shape)
+
+    def check(self, name):
+        b = host(self.buf)
+        assert np.all(b[:GUARD] == SENT) and np.all(b[GUARD + self.n:] == SENT), f"{name}: guard band written"
+
+
+def _strided_dev(a, ld):
+    """Device bf16 [M, N] with row stride ld (padding filled with sentinel)."""
+    M, N = a.shape
+    full = np.full((M, ld), 0x7FC1, np.uint16)
+    full[:, :N] = a
+    return dev(full)[:, :N]
+
+
+def run_gpu(problems, single_entry=False):
+    """problems: dicts with numpy x, gamma, eps and optional residual,
+    fmt, scale_layout, keep_bf16, inplace, ldx, ldr, ldb. Returns a list of
+    dicts of numpy outputs, after checking every guard band."""
+    structs, keep, outs = [], [], []
+    for p in problems:
+        M, N = p["x"].shape
+        fmt = p.get("fmt", 0)
+        lay = p.get("scale_layout", 0)
+        x = _strided_dev(p["x"], p.get("ldx", N))
+        g = dev(p["gamma"])
+        o = {"q": Guarded(M * (N if fmt == 0 else N // 2), torch.uint8, (M, -1) if M else (0,)),
+             "scale": Guarded(fq.rmsq_scale_bytes(M, N, 128 if fmt == 0 else 32, fmt, lay),
+                              torch.float32 if fmt == 0 else torch.uint8, (-1,))}
+        r = ro = yb = None
+        if "residual" in p:
+            r = _strided_dev(p["residual"], p.get("ldr", N))
+            if p.get("inplace"):
+                ro = r
+            else:
+                ld = p.get("ldr", N)
+                o["residual_out"] = Guarded(max(M * ld * 2, 2), torch.bfloat16, (M, ld) if M else (-1,))
+                ro = o["residual_out"].t[:, :N] if M else o["residual_out"].t
+        if p.get("keep_bf16"):
+            ld = p.get("ldb", N)
+            o["bf16"] = Guarded(max(M * ld * 2, 2), torch.bfloat16, (M, ld) if M else (-1,))
+            yb = o["bf16"].t[:, :N] if M else o["bf16"].t
+        keep += [x, g, r]
+        outs.append((o, ro, yb, r, p))
+        if single_entry:
+            fq.rmsnorm_quant_group(x, r, g, p["eps"], M, N, 128 if fmt == 0 else 32, fmt, o["q"].t,
+                                   o["scale"].t, ro, yb)
+        else:
+            structs.append(fq.make_problem(x, g, p["eps"], o["q"].t, o["scale"].t, residual_in=r,
+                                           residual_out=ro, out_bf16=yb, fmt=fmt, scale_layout=lay))
+    if not single_entry:
+        fq.rmsnorm_quant_group_multi(structs)
+    torch.cuda.synchronize()
+    res = []
+    for o, ro, yb, r, p in outs:
+        d = {}
+        for k, gb in o.items():
+            gb.check(k)
+        N = p["x"].shape[1]
+        for k in ("residual_out", "bf16"):
+            if k in o and o[k].t.dim() == 2 and o[k].t.shape[1] > N:
+                pad = host(o[k].t)[:, N:]
+                assert np.all(pad == 0xA5A5), f"{k}: row padding written"
+        d["q"] = host(o["q"].t)
+        d["scale"] = host(o["scale"].t)
+        if ro is not None:
+            d["residual_out"] = host(ro)
+        if yb is not None:
+            d["bf16"] = host(yb)
+        if p.get("fmt", 0) == 0 and p["x"].shape[0]:
+            d["scale"] = d["scale"].reshape(p["x"].shape[0], -1)
+        elif p.get("scale_layout", 0) == 0 and p["x"].shape[0]:
+            d["scale"] = d["scale"].reshape(p["x"].shape[0], -1)
+        res.append(d)
+    return res
+
+
+def run_oracle(orc, p):
+    M, N = p["x"].shape
+    fmt = p.get("fmt", 0)
+    return orc.rmsnorm_quant_group(p["x"], p["gamma"], p["eps"], residual=p.get("residual"),
+                                   group=128 if fmt == 0 else 32, fmt=fmt,
+                                   scale_layout=p.get("scale_layout", 0),
+                                   keep_bf16=True, scale_fill=SENT if fmt == 1 else 0)
+
+
+def check(orc, problems, single_entry=False, strict=True):
+    got = run_gpu(problems, single_entry)
+    reps = []
+    for g, p in zip(got, problems):
+        want = run_oracle(orc, p)
+        if p.get("fmt", 0) == 1 and p.get("scale_layout", 0) == 1:
+            M, G = p["x"].shape[0], p["x"].shape[1] // 32
+            owned = np.array([(m // 32) * 32 * G + gi * 32 + m % 32 for m in range(M) for gi in range(G)], np.int64)
+            g = dict(g, scale=g["scale"][owned])
+            want = dict(want, scale=want["scale"][owned])
+        reps.append(compare(g, want, p.get("fmt", 0), (orc.e4m3fn_table(), orc.e2m1_table()), strict,
+                            yb_ref=want["bf16"]))
+    return reps
+
+
+def _cfg(name, M=None):
+    c = inputs.make_config(name, M)
+    p = {"x": c["x"], "gamma": c["gamma"], "eps": c["eps"], "fmt": c["fmt"], "keep_bf16": c["keep_bf16"]}
+    if "residual" in c:
+        p["residual"] = c["residual"]
+    return p
+
+
+# ----------------------------------------------------------- workloads --
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill512", "prefill"])
+def test_fp8_workloads_full_size(orc, name):
+    say(f"workload {name}")
+    p = _cfg(name)
+    rep = check(orc, [p])[0]
+    say(f"{name}: {rep}")
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_mxfp4_workload_full_size(orc, layout):
+    say(f"workload mxfp4 layout {layout}")
+    p = dict(_cfg("mxfp4"), scale_layout=layout)
+    check(orc, [p])
+
+
+def test_mla_two_problems_one_launch_from_one_projection_buffer(orc):
+    """q (N=1536) and kv (N=512) latents as strided column slices of one
+    [4096, 2112] projection output, normalized and quantized in one launch."""
+    say("workload mla")
+    c = inputs.make_config("mla")
+    pq, pk = c["problems"]
+    probs = [{"x": pq["x"], "gamma": pq["gamma"], "eps": 1e-6, "ldx": 2112},
+             {"x": pk["x"], "gamma": pk["gamma"], "eps": 1e-6, "ldx": 2112}]
+    check(orc, probs)
+
+
+def test_single_entry_point(orc):
+    say("single entry point, decode")
+    check(orc, [_cfg("decode")], single_entry=True)
+    check(orc, [dict(_cfg("tiny"), keep_bf16=True)], single_entry=True)
+    check(orc, [dict(_cfg("mxfp4", M=96))], single_entry=True)
+
+
+# --------------------------------------------------------- shape sweeps --
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_shape_sweep_ragged(orc, fmt):
+    Ns = [128, 256, 384, 512, 640, 896, 1024, 1536, 2048, 2176, 4096, 7168, 8192, 16384, 32768]
+    if fmt == 1:
+        Ns = [32, 96, 160] + Ns
+    for i, N in enumerate(Ns):
+        M = [1, 3, 37][i % 3]
+        say(f"sweep fmt {fmt} M {M} N {N}")
+        p = inputs.make_problem(M, N, seed_x=1000 + N, residual=(i % 2 == 0), outliers=True)
+        p.update(fmt=fmt, keep_bf16=True)
+        check(orc, [p])
+
+
+@pytest.mark.parametrize("N", [7168, 1536, 512])
+def test_every_launch_shape_gives_the_same_result(orc, N):
+    p = inputs.make_problem(40, N, seed_x=77, residual=True, outliers=True)
+    p.update(fmt=0, keep_bf16=True)
+    want = None
+    C = N // 8
+    try:
+        for J in (1, 2, 3, 4, 7, 8, 14):
+            for W in range(1, 17):
+                if J * W * 64 < C or (J >= 7 and W > 4) or (J * (W - 1) * 64 >= C and W > 1):
+                    continue
+                say(f"shape J={J} W={W} N={N}")
+                fq.rmsq_set_shape(J, W)
+                check(orc, [p])
+                got = run_gpu([p])[0]
+                if want is None:
+                    want = got
+                for k in got:
+                    assert np.array_equal(got[k], want[k]), (J, W, k)
+    finally:
+        fq.rmsq_set_shape(0, 0)
+
+
+# ------------------------------------------------------------ edge cases --
+def test_zero_rows_zero_groups_and_signed_zeros(orc):
+    say("edge: zeros")
+    N = 512
+    x = inputs.normal_rows(6, N, 5, False)
+    x[0] = 0.0                              # zero row
+    x[1, 128:256] = 0.0                     # zero group (FP8) / four zero groups (MXFP4)
+    x[2, :] = -0.0                          # negative zero row
+    x[3, ::2] = -0.0
+    g = inputs.gamma_vec(N, 7)
+    for fmt in (0, 1):
+        for eps in (0.0, 1e-6):
+            p = {"x": inputs.to_bf16_bits(x), "gamma": g, "eps": eps, "fmt": fmt, "keep_bf16": True}
+            check(orc, [p])
+
+
+def test_tiny_and_huge_rows_take_the_exact_path(orc):
+    say("edge: extreme magnitudes")
+    N = 1024
+    x = inputs.normal_rows(8, N, 6, True)
+    x[0] *= np.float32(1e-30)               # inv ~ 1e30 with eps = 0
+    x[1] *= np.float32(1e30)                # inv ~ 1e-30
+    x[2] *= np.float32(1e-38)               # bf16 subnormal inputs
+    x[3, :128] *= np.float32(1e-35)         # a group whose scale is an fp32 subnormal
+    x[4, 128:256] = np.float32(2.0 ** -130) # tiny constant group
+    g = inputs.gamma_vec(N, 8)
+    for fmt in (0, 1):
+        for eps in (0.0, 1e-6):
+            p = {"x": inputs.to_bf16_bits(x), "gamma": g, "eps": eps, "fmt": fmt, "keep_bf16": True}
+            check(orc, [p])
+
+
+def test_tie_heavy_rows_exact_codes(orc):
+    """gamma = 1, eps = 0 and sum(h^2) = N: y = h, group amax 3.5 gives
+    s = 2^-7, so yb/s is exact and lands on e4m3fn ties."""
+    say("edge: ties")
+    N = 1024
+    rng = np.random.default_rng(9)
+    ties = np.float32([2.625, 2.875, 3.25, 3.75, 1.0625, 0.5625, 2.0 ** -10 * 128, 3 * 2.0 ** -10 * 128]) / 128
+    rows = []
+    for m in range(16):
+        h = np.zeros(N, np.float32)
+        for gi in range(N // 128):
+            h[gi * 128] = 3.5 * (-1) ** (m + gi)
+            h[gi * 128 + 1: gi * 128 + 1 + ties.size] = ties * rng.choice([-1, 1], ties.size)
+        ss = float((h.astype(np.float64) ** 2).sum())
+        fill = np.flatnonzero(h == 0)
+        k = int(round((N - ss) / 1.0))
+        assert 0 < k <= fill.size
+        h[fill[:k]] = rng.choice([-1.0, 1.0], k)
+        rest = N - float((h.astype(np.float64) ** 2).sum())
+        assert rest >= 0
+        if rest:
+            q = int(round(rest / 0.25))
+            f2 = np.flatnonzero(h == 0)[:q]
+            h[f2] = 0.5
+        assert (h.astype(np.float64) ** 2).sum() == N
+        rows.append(h)
+    x = inputs.to_bf16_bits(np.array(rows))
+    g = inputs.to_bf16_bits(np.ones(N, np.float32))
+    check(orc, [{"x": x, "gamma": g, "eps": 0.0, "fmt": 0, "keep_bf16": True}])
+    check(orc, [{"x": x, "gamma": g, "eps": 0.0, "fmt": 1, "keep_bf16": True}])
+
+
+def test_strides_inplace_and_tiles(orc):
+    say("edge: strides, in place, tiles")
+    p = inputs.make_problem(33, 7168, seed_x=31, residual=True, outliers=True)
+    check(orc, [dict(p, fmt=0, keep_bf16=True, ldx=7168 + 64, ldr=7168 + 8, ldb=7176)])
+    check(orc, [dict(p, fmt=0, keep_bf16=True, inplace=True)])
+    check(orc, [dict(p, fmt=1, scale_layout=1, keep_bf16=True, inplace=True)])
+    check(orc, [dict(p, fmt=1, scale_layout=1, keep_bf16=False)])
+    q = inputs.make_problem(1, 7168, seed_x=32, residual=True, outliers=True)
+    check(orc, [dict(q, fmt=0, keep_bf16=True)])
+    check(orc, [dict(q, fmt=1, scale_layout=1)])
+
+
+def test_four_problems_mixed(orc):
+    say("edge: four problems")
+    ps = []
+    for i, (M, N, res) in enumerate([(5, 7168, True), (64, 1536, False), (1, 512, True), (70, 256, False)]):
+        p = inputs.make_problem(M, N, seed_x=50 + i, residual=res, outliers=True)
+        ps.append(dict(p, fmt=1, scale_layout=i % 2, keep_bf16=bool(i % 2)))
+    check(orc, ps)
+    for p in ps:
+        p["fmt"] = 0
+        p["scale_layout"] = 0
+    check(orc, ps)
+
+
+def test_m_zero_problem_is_skipped(orc):
+    say("edge: M = 0")
+    p0 = inputs.make_problem(0, 512, seed_x=3, residual=True)
+    p1 = inputs.make_problem(3, 512, seed_x=4, residual=True)
+    got = run_gpu([dict(p0, fmt=0), dict(p1, fmt=0, keep_bf16=True)])
+    assert got[0]["q"].size == 0
+    check(orc, [dict(p1, fmt=0, keep_bf16=True)])
+
+
+def test_repeatable(orc):
+    say("repeatability")
+    p = dict(_cfg("decode"), keep_bf16=True)
+    a = run_gpu([p])[0]
+    b = run_gpu([p])[0]
+    for k in a:
+        assert np.array_equal(a[k], b[k])
+
+
+def test_fused_convenience_wrapper_tuples():
+    say("tuple wrapper")
+    p = _cfg("decode")
+    x, r, g = dev(p["x"]), dev(p["residual"]), dev(p["gamma"])
+    (q, s), res = fq.fused_rmsnorm_quant(x, g, 1e-6, residual=r)
+    (yb, q2, s2), res2 = fq.fused_rmsnorm_quant(x, g, 1e-6, residual=r, keep_bf16=True)
+    torch.cuda.synchronize()
+    assert q.shape == (64, 7168) and s.shape == (64, 56) and res.shape == (64, 7168)
+    assert torch.equal(q, q2) and torch.equal(s, s2) and torch.equal(res, res2)
+    (q4, s4), _ = fq.fused_rmsnorm_quant(x, g, 1e-6, fmt="mxfp4", scale_layout="tiled32")
+    torch.cuda.synchronize()
+    assert q4.shape == (64, 3584) and s4.numel() == 64 * 224
+    with pytest.raises(fq.RmsqError):
+        fq.fused_rmsnorm_quant(x[:, :100], g, 1e-6)
