@@ -249,7 +249,8 @@ def main():
         "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "rmsq_fused_kernel<0,14>", "bytes_per_launch": w.bytes,
+                     "kernel": "rmsq_fused_kernel<%d,%d> x %d waves" % ((fmt,) + fq.rmsq_query_shape(N, w.rows)),
+                     "bytes_per_launch": w.bytes,
                      "us_per_launch": round(per_launch_ms * 1e3, 2)},
         "copy_ceiling_GBps": round(ceiling, 1),
         "cpu_baseline": cpu,

@@ -55,7 +55,8 @@ class rmsq_problem(C.Structure):
 
 
 EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "rmsq_device_supported",
-           "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape")
+           "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape",
+           "rmsq_query_shape")
 
 _lib = None
 
@@ -83,6 +84,8 @@ def lib() -> C.CDLL:
         L.rmsq_last_error.argtypes = []
         L.rmsq_set_shape.restype = None
         L.rmsq_set_shape.argtypes = [i32, i32]
+        L.rmsq_query_shape.restype = i32
+        L.rmsq_query_shape.argtypes = [i64, i64, C.POINTER(i32), C.POINTER(i32)]
         _lib = L
     return _lib
 
@@ -144,6 +147,13 @@ def rmsq_scale_bytes(M, N, group, fmt, scale_layout=SCALE_ROW_MAJOR) -> int:
 
 def rmsq_set_shape(J: int = 0, W: int = 0) -> None:
     lib().rmsq_set_shape(int(J), int(W))
+
+
+def rmsq_query_shape(N: int, rows: int):
+    """(J, W): chunks per lane and waves per row the library picks."""
+    j, w = C.c_int32(), C.c_int32()
+    _check(lib().rmsq_query_shape(int(N), int(rows), C.byref(j), C.byref(w)))
+    return j.value, w.value
 
 
 # -------------------------------------------------------- convenience --

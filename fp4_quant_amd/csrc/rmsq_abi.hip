@@ -62,12 +62,12 @@ rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Range* r
   if (p.N > RMSQ_N_MAX) return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: N = %lld > %d", idx, (long long)p.N, RMSQ_N_MAX);
   if (p.M > INT32_MAX) return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: M = %lld too large", idx, (long long)p.M);
   if (!std::isfinite(p.eps) || p.eps < 0.0f) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: eps must be finite and >= 0", idx);
-  if ((p.residual_in == nullptr) != (p.residual_out == nullptr))
-    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: residual_in and residual_out must both be set or both be NULL", idx);
   const int64_t ldx = p.ldx ? p.ldx : p.N, ldr = p.ldr ? p.ldr : p.N, ldb = p.ldb ? p.ldb : p.N;
   if (ldx < p.N || ldx % 8 || (p.residual_in && (ldr < p.N || ldr % 8)) || (p.out_bf16 && (ldb < p.N || ldb % 8)))
     return fail(RMSQ_ERR_INVALID_ARG, "problem %d: row strides must be multiples of 8 and >= N", idx);
-  if (p.M == 0) return RMSQ_OK;
+  if (p.M == 0) return RMSQ_OK;  // nothing is read or written; pointers may be NULL
+  if ((p.residual_in == nullptr) != (p.residual_out == nullptr))
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: residual_in and residual_out must both be set or both be NULL", idx);
   if (!p.x || !p.gamma || !p.out_q || !p.out_scale)
     return fail(RMSQ_ERR_INVALID_ARG, "problem %d: x, gamma, out_q and out_scale must be non-NULL", idx);
   if (!aligned(p.x, 16) || !aligned(p.gamma, 16) || (p.residual_in && !aligned(p.residual_in, 16)) ||
@@ -132,19 +132,24 @@ bool device_is_gfx950(int dev) {
 // are in flight per CU. Few rows: spread each row over more waves.
 constexpr int kJs[] = {14, 8, 7, 4, 3, 2, 1};
 
+// Pass 0 wants at most 20% idle lanes and enough waves to fill the chip;
+// pass 1 drops the wave count; pass 2 takes the first shape that fits. N <=
+// RMSQ_N_MAX (4096 chunks) always fits as J = 4, W = 16.
 void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
-  for (int J : kJs) {
-    const int64_t W = (C + 64 * J - 1) / (64 * J);
-    if (W > rmsq::max_waves(J)) continue;
-    const int64_t slots = W * 64 * J;
-    if (J > 1 && (slots - C) * 5 > slots) continue;      // more than 20% idle lanes
-    if (J > 1 && rows * W < 2048) continue;               // too few waves for 256 CUs
-    *J_out = J;
-    *W_out = (int)W;
-    return;
+  for (int pass = 0; pass < 3; ++pass) {
+    for (int J : kJs) {
+      const int64_t W = (C + 64 * J - 1) / (64 * J);
+      if (W > rmsq::max_waves(J)) continue;
+      const int64_t slots = W * 64 * J;
+      if (pass < 2 && J > 1 && (slots - C) * 5 > slots) continue;
+      if (pass == 0 && J > 1 && rows * W < 2048) continue;
+      *J_out = J;
+      *W_out = (int)W;
+      return;
+    }
   }
-  *J_out = 1;
-  *W_out = (int)((C + 63) / 64);
+  *J_out = 4;
+  *W_out = rmsq::kMaxWaves;
 }
 
 template <int FMT>
@@ -284,12 +289,18 @@ const char* rmsq_status_string(rmsq_status s) {
 
 const char* rmsq_last_error(void) { return g_err; }
 
-// Measurement hook: force the launch shape (chunk-steps per lane J, waves per
-// row W) of later calls in this process; 0, 0 restores the automatic choice.
-// Shapes that cannot cover a row are ignored.
 void rmsq_set_shape(int32_t J, int32_t W) {
   g_force_J.store(J);
   g_force_W.store(W);
+}
+
+int32_t rmsq_query_shape(int64_t N, int64_t rows, int32_t* J, int32_t* W) {
+  if (N <= 0 || N % 8 || N > RMSQ_N_MAX || rows < 0 || !J || !W) return RMSQ_ERR_INVALID_ARG;
+  int j, w;
+  pick_shape(N / 8, rows, &j, &w);
+  *J = j;
+  *W = w;
+  return RMSQ_OK;
 }
 
 }  // extern "C"

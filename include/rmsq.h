@@ -153,6 +153,12 @@ const char* rmsq_last_error(void);
  * choice. Results do not depend on the shape. */
 void rmsq_set_shape(int32_t J, int32_t W);
 
+/* The launch shape the library picks (without an override) for rows of N
+ * elements, the widest problem of a call, and `rows` rows in total: J chunks
+ * of 8 elements per lane and W waves per workgroup (one workgroup per row).
+ * RMSQ_ERR_INVALID_ARG for N outside (0, RMSQ_N_MAX] or not a multiple of 8. */
+rmsq_status rmsq_query_shape(int64_t N, int64_t rows, int32_t* J, int32_t* W);
+
 #ifdef __cplusplus
 }
 #endif

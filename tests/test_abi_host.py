@@ -122,6 +122,7 @@ def test_validation_errors(kw, status):
 def test_m_zero_is_a_noop_without_device():
     assert _call(M=0) == fq.RMSQ_OK
     assert _call(M=0, x=None, q=None, s=None, g=None) == fq.RMSQ_OK
+    assert _call(M=0, r=None, ro=A + 400 * MB) == fq.RMSQ_OK     # empty tensors have NULL data
 
 
 def test_valid_call_without_a_gfx950_device_is_unsupported():
@@ -164,3 +165,17 @@ def test_multi_count_and_shared_fmt():
 def test_set_shape_is_callable():
     fq.rmsq_set_shape(14, 1)
     fq.rmsq_set_shape(0, 0)
+
+
+def test_launch_shape_always_fits():
+    """For every N the library accepts, the chosen shape covers the row with a
+    legal workgroup (long per-lane rows use at most 4 waves)."""
+    for N in range(8, 32768 + 1, 8):
+        for rows in (1, 64, 512, 8192):
+            J, W = fq.rmsq_query_shape(N, rows)
+            C_ = N // 8
+            assert J in (1, 2, 3, 4, 7, 8, 14) and 1 <= W <= (4 if J >= 7 else 16), (N, rows, J, W)
+            assert J * W * 64 >= C_, (N, rows, J, W)
+    assert fq.rmsq_query_shape(7168, 8192) == (14, 1)
+    with pytest.raises(fq.RmsqError):
+        fq.rmsq_query_shape(32776, 1)

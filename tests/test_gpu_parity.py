@@ -240,33 +240,37 @@ def test_tiny_and_huge_rows_take_the_exact_path(orc):
             check(orc, [p])
 
 
+def tie_rows(M, N, seed):
+    """Rows with gamma = 1, eps = 0 and sum(h^2) = 4N exactly, so inv = 1/2 and
+    y = h/2 with no rounding. Every 32-block starts with +-3.5 (group amax
+    1.75 after the norm: FP8 scale 2^-8, MXFP4 scale 2^-2) and holds values
+    whose quotients are exact e4m3fn midpoints (2.125 ... 3.375, 1.0625,
+    1.1875, 0.53125 before the norm) and exact e2m1 midpoints (0.25 ... 5 in
+    units of the MXFP4 scale); the rest is filled so the squares add up."""
+    rng = np.random.default_rng(seed)
+    fp8_ties = [2.125, 2.375, 2.625, 2.875, 3.125, 3.375, 1.0625, 1.1875, 0.53125]
+    e2m1_ties = [0.125, 0.375, 0.625, 0.875, 1.25, 1.75, 2.5]    # y / X = 0.25 ... 5 with X = 2^-2
+    fixed = [3.5] + fp8_ties + e2m1_ties
+    rows = []
+    for m in range(M):
+        h = np.zeros(N, np.float64)
+        for b0 in range(0, N, 32):
+            h[b0:b0 + len(fixed)] = np.array(fixed) * rng.choice([-1, 1], len(fixed))
+        R = 4.0 * N - float((h ** 2).sum())
+        free = list(np.flatnonzero(h == 0))
+        for v in (2.0, 1.0, 0.5, 0.25, 0.125, 0.0625, 0.03125):
+            while R >= v * v and free:
+                h[free.pop()] = v * rng.choice([-1, 1])
+                R -= v * v
+        assert R == 0 and (h ** 2).sum() == 4.0 * N, R
+        rows.append(h)
+    return inputs.to_bf16_bits(np.array(rows, np.float32))
+
+
 def test_tie_heavy_rows_exact_codes(orc):
-    """gamma = 1, eps = 0 and sum(h^2) = N: y = h, group amax 3.5 gives
-    s = 2^-7, so yb/s is exact and lands on e4m3fn ties."""
     say("edge: ties")
     N = 1024
-    rng = np.random.default_rng(9)
-    ties = np.float32([2.625, 2.875, 3.25, 3.75, 1.0625, 0.5625, 2.0 ** -10 * 128, 3 * 2.0 ** -10 * 128]) / 128
-    rows = []
-    for m in range(16):
-        h = np.zeros(N, np.float32)
-        for gi in range(N // 128):
-            h[gi * 128] = 3.5 * (-1) ** (m + gi)
-            h[gi * 128 + 1: gi * 128 + 1 + ties.size] = ties * rng.choice([-1, 1], ties.size)
-        ss = float((h.astype(np.float64) ** 2).sum())
-        fill = np.flatnonzero(h == 0)
-        k = int(round((N - ss) / 1.0))
-        assert 0 < k <= fill.size
-        h[fill[:k]] = rng.choice([-1.0, 1.0], k)
-        rest = N - float((h.astype(np.float64) ** 2).sum())
-        assert rest >= 0
-        if rest:
-            q = int(round(rest / 0.25))
-            f2 = np.flatnonzero(h == 0)[:q]
-            h[f2] = 0.5
-        assert (h.astype(np.float64) ** 2).sum() == N
-        rows.append(h)
-    x = inputs.to_bf16_bits(np.array(rows))
+    x = tie_rows(16, N, 9)
     g = inputs.to_bf16_bits(np.ones(N, np.float32))
     check(orc, [{"x": x, "gamma": g, "eps": 0.0, "fmt": 0, "keep_bf16": True}])
     check(orc, [{"x": x, "gamma": g, "eps": 0.0, "fmt": 1, "keep_bf16": True}])
