@@ -128,21 +128,24 @@ bool device_is_gfx950(int dev) {
 }
 
 // Launch shape: chunk-steps per lane J (compiled set) and waves per row W.
-// Many rows: long per-lane work, one wave per row when it fits, so more rows
-// are in flight per CU. Few rows: spread each row over more waves.
-constexpr int kJs[] = {14, 8, 7, 4, 3, 2, 1};
+// Measured on MI355X (prefill 8192 x 7168): a row spread over 7 waves with 2
+// chunks per lane sustains the traffic far better than long per-lane rows
+// (one wave per row leaves the HBM queues bursty), and the fixed per-wave cost
+// of the norm (reduction, fp64 inverse square root) argues against going to a
+// single chunk per lane when rows are plentiful. So: the smallest J whose W
+// stays <= 8 with at most 20% idle lanes; with few rows (latency-bound
+// calls), the smallest J that fits at all, to spread each row widest.
+constexpr int kJs[] = {1, 2, 3, 4, 7, 8, 14};
 
-// Pass 0 wants at most 20% idle lanes and enough waves to fill the chip;
-// pass 1 drops the wave count; pass 2 takes the first shape that fits. N <=
-// RMSQ_N_MAX (4096 chunks) always fits as J = 4, W = 16.
 void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
+  const bool few_rows = rows < 1024;
   for (int pass = 0; pass < 3; ++pass) {
     for (int J : kJs) {
       const int64_t W = (C + 64 * J - 1) / (64 * J);
       if (W > rmsq::max_waves(J)) continue;
       const int64_t slots = W * 64 * J;
       if (pass < 2 && J > 1 && (slots - C) * 5 > slots) continue;
-      if (pass == 0 && J > 1 && rows * W < 2048) continue;
+      if (pass == 0 && !few_rows && W > 8) continue;
       *J_out = J;
       *W_out = (int)W;
       return;

@@ -79,14 +79,6 @@ __device__ __forceinline__ bool near_bf16_midpoint(float y) {
   return ((__float_as_uint(y) & 0xFFFFu) - 0x7FFCu) <= 8u;
 }
 
-// p within 8 ulp of an e4m3fn rounding midpoint (normal range), or
-// 0 < |p| < 2^-6 (the e4m3fn subnormal range, where the midpoints sit at a
-// fixed spacing the bit test does not see).
-__device__ __forceinline__ bool fp8_undecided(float p) {
-  const uint32_t u = __float_as_uint(p);
-  return ((u & 0x7FFFFFFFu) - 1u) < 0x3C7FFFFFu || ((u & 0xFFFFFu) - 0x7FFF8u) <= 16u;
-}
-
 // bf16(hg * inv) for 8 elements, hg = h * gamma (exact in fp32), inv the fp64
 // inverse norm and inv32 = fl32(inv). The fp32 product is within 2 ulp of the
 // fp64 one, so its bf16 rounding is final unless it lies within 4 ulp of a
@@ -98,13 +90,13 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float hg[8], float inv32, dou
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float y0 = hg[2 * i] * inv32, y1 = hg[2 * i + 1] * inv32;
-    need = need || near_bf16_midpoint(y0) || near_bf16_midpoint(y1);
+    need |= near_bf16_midpoint(y0) | near_bf16_midpoint(y1);   // bitwise: no branches
     yw[i] = pack_bf16(y0, y1);
   }
   if (need) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (row_exact || near_bf16_midpoint(hg[e] * inv32)) {
+      if (row_exact | near_bf16_midpoint(hg[e] * inv32)) {
         const uint32_t b = bf16_from_f64((double)hg[e] * inv);
         const int sh = (e & 1) * 16;
         yw[e >> 1] = (yw[e >> 1] & ~(0xFFFFu << sh)) | (b << sh);
@@ -115,36 +107,52 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float hg[8], float inv32, dou
 }
 
 // FP8 scale of a group from its amax (a bf16 magnitude pattern): amax / 448
-// as an IEEE fp32 division (the compiler's correctly rounded sequence, fp32
-// denormals kept), 1.0 for an all-zero group.
+// rounded once to fp32, 1.0 for an all-zero group. For amax >= 2^-100 the
+// quotient is a normal fp32 and is formed as fl32(amax * fl64(1/448)): amax
+// has 8 significant bits, so amax/448 = (A/7) 2^k, whose bits past any
+// rounding position repeat with period 3 and never come within 2^-27
+// (relative) of an fp32 midpoint unless 7 divides A and the quotient is
+// exact; the fp64 product is within 2^-52 of the quotient, so its fp32
+// rounding is the correctly rounded one. Smaller amax uses the IEEE fp32
+// division (denormals kept).
 __device__ __forceinline__ float fp8_scale(uint32_t amax_bits) {
-  return amax_bits ? __uint_as_float(amax_bits << 16) / 448.0f : 1.0f;
+  if (amax_bits == 0) return 1.0f;
+  const float a = __uint_as_float(amax_bits << 16);
+  if (amax_bits >= 0x0D80u) return (float)((double)a * (1.0 / 448.0));
+  return a / 448.0f;
 }
 
 // e4m3fn codes of v[e] / s for 8 bf16 values v (as fp32) of one group, bytes
-// in element order. p = v * rcp(s) is within 3 ulp of the exact quotient
-// (v_rcp_f32 is within 1 ulp); a code is final unless p is undecided, or s is
-// so small that rcp(s) leaves the normal range, and then the exact path
-// decides.
+// in element order. rs = v_rcp_f32(s) is within 1 ulp of 1/s for every scale
+// this kernel produces (s = fl32(amax/448) for a bf16 amax >= 2^-100; checked
+// exhaustively on the GPU), so r_lo = rs - 4 ulp < 1/s < rs + 4 ulp = r_hi,
+// and the nearest-even products v*r_lo and v*r_hi bracket v/s. Rounding to
+// e4m3fn is monotone, so where both brackets give the same code that code is
+// the rounding of v/s (also across the e4m3fn subnormal range); four codes
+// are compared at once as a packed dword. Elsewhere - quotients within a few
+// ulp of a rounding midpoint, exact ties - and in groups whose scale is too
+// small for a normal reciprocal, the exact path decides.
 __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
-  const float rs = __builtin_amdgcn_rcpf(s);
-  const bool tiny = s < 0x1p-100f;
-  float p[8];
-  bool need = tiny;
+  const uint32_t rb = __float_as_uint(__builtin_amdgcn_rcpf(s));
+  const float r_lo = __uint_as_float(rb - 4u), r_hi = __uint_as_float(rb + 4u);
+  float lo[8], hi[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = v[e] * rs;
-    need = need || fp8_undecided(p[e]);
+    lo[e] = v[e] * r_lo;
+    hi[e] = v[e] * r_hi;
   }
-  u32x2 qw;
-  qw[0] = cvt_fp8x2<true>(p[2], p[3], cvt_fp8x2<false>(p[0], p[1], 0u));
-  qw[1] = cvt_fp8x2<true>(p[6], p[7], cvt_fp8x2<false>(p[4], p[5], 0u));
-  if (need) {
+  u32x2 qw, qh;
+  qw[0] = cvt_fp8x2<true>(lo[2], lo[3], cvt_fp8x2<false>(lo[0], lo[1], 0u));
+  qw[1] = cvt_fp8x2<true>(lo[6], lo[7], cvt_fp8x2<false>(lo[4], lo[5], 0u));
+  qh[0] = cvt_fp8x2<true>(hi[2], hi[3], cvt_fp8x2<false>(hi[0], hi[1], 0u));
+  qh[1] = cvt_fp8x2<true>(hi[6], hi[7], cvt_fp8x2<false>(hi[4], hi[5], 0u));
+  const bool tiny = s < 0x1p-100f;
+  if (tiny | (qw[0] != qh[0]) | (qw[1] != qh[1])) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (tiny || fp8_undecided(p[e])) {
+      const int sh = (e & 3) * 8;
+      if (tiny | (((qw[e >> 2] ^ qh[e >> 2]) >> sh) & 0xFFu) != 0u) {
         const uint32_t b = fp8_exact(v[e], s);
-        const int sh = (e & 3) * 8;
         qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
       }
     }
@@ -202,23 +210,42 @@ __device__ __forceinline__ uint32_t max4(uint32_t v) {
   return v;
 }
 
-// Sum over the 64 lanes of a wave in a fixed tree order; all lanes get it.
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the 64 lanes of a (fully active) wave in a fixed order: DPP
+// rotations within each 16-lane row (addition is commutative, so every lane of
+// a row ends with the same value), then the four row sums in a fixed tree.
+// The result is wave-uniform.
+__device__ __forceinline__ double wave_sum(double v) {
+  v += dpp_f64<0x128>(v);
+  v += dpp_f64<0x124>(v);
+  v += dpp_f64<0x122>(v);
+  v += dpp_f64<0x121>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Largest |value| of eight packed bf16 (four dwords), as a bf16 magnitude
 // pattern: integer max of (bits & 0x7FFF) orders bf16 magnitudes exactly.
 __device__ __forceinline__ uint32_t amax8(u32x4 w) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t a = w[i] & 0x7FFF7FFFu;
-    m = max(m, max(a & 0xFFFFu, a >> 16));
-  }
-  return m;
+  const u16x2 a = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, w[1] & 0x7FFF7FFFu);
+  const u16x2 c = __builtin_bit_cast(u16x2, w[2] & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2, w[3] & 0x7FFF7FFFu);
+  const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max((uint32_t)m[0], (uint32_t)m[1]);
 }
 
 }  // namespace rmsq

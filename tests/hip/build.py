@@ -1,4 +1,5 @@
-"""Build the test-only probe library (tests/hip/libconvert_probe.so) for gfx950."""
+"""Build the test-only probe library (tests/hip/libconvert_probe.so) for gfx950:
+number-format probes and HBM stream probes."""
 import os
 import subprocess
 import sys
@@ -11,7 +12,8 @@ LIB = os.path.join(HERE, "libconvert_probe.so")
 def build(verbose: bool = False) -> str:
     sys.path.insert(0, ROOT)
     from fp4_quant_amd.build import HIPCC, HIP_FLAGS, CSRC
-    cmd = [HIPCC, *HIP_FLAGS, "-I", CSRC, os.path.join(HERE, "convert_probe.hip"), "-o", LIB + ".tmp"]
+    cmd = [HIPCC, *HIP_FLAGS, "-I", CSRC, os.path.join(HERE, "convert_probe.hip"),
+           os.path.join(HERE, "stream_probe.hip"), "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -80,6 +80,10 @@ __global__ void k_fp8_exact(const float* v, const float* s, uint8_t* out, int64_
   GRID_LOOP(i, n) out[i] = (uint8_t)fp8_exact(v[i], s[i]);
 }
 
+__global__ void k_rcp(const float* s, float* out, int64_t n) {
+  GRID_LOOP(i, n) out[i] = __builtin_amdgcn_rcpf(s[i]);
+}
+
 static int launch_status() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 
 #define GRID(n) dim3((unsigned)(((n) + 255) / 256 < 65536 ? ((n) + 255) / 256 : 65536)), dim3(256), 0, (hipStream_t)stream
@@ -128,6 +132,11 @@ int probe_cvt_fp4(const float* in, uint8_t* out, int64_t n, void* stream) {
 int probe_f64_to_bf16(const double* in, uint16_t* out, int64_t n, void* stream) {
   if (n <= 0) return 0;
   hipLaunchKernelGGL(k_f64_to_bf16, GRID(n), in, out, n);
+  return launch_status();
+}
+int probe_rcp(const float* s, float* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_rcp, GRID(n), s, out, n);
   return launch_status();
 }
 int probe_fp8_exact(const float* v, const float* s, uint8_t* out, int64_t n, void* stream) {

@@ -1,0 +1,179 @@
+// stream_probe.hip - test-only bandwidth probes: plain streams (read, write,
+// copy) and the fused kernel's exact traffic pattern with no arithmetic, to
+// measure the achievable HBM ceiling on the box. Grid-stride loops, bounds
+// checked; n16 counts 16-byte elements.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void st(T v, T* p) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+template <bool NT>
+__global__ void k_read(const u32x4* a, int64_t n16, uint32_t* sink) {
+  uint32_t acc = 0;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 v = ld16<NT>(a + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;   // keeps the loads alive; practically never stores
+}
+
+template <bool NT>
+__global__ void k_write(u32x4* a, int64_t n16) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    st<NT>(u32x4{(uint32_t)i, 1u, 2u, 3u}, a + i);
+}
+
+template <bool NT>
+__global__ void k_copy(const u32x4* a, u32x4* b, int64_t n16) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    st<NT>(ld16<NT>(a + i), b + i);
+}
+
+// The fused kernel's traffic per 8-element chunk: read x and r (16 B each),
+// write h and yb (16 B each) and codes (8 B). Grid-stride over chunks.
+template <bool NT>
+__global__ void k_mix(const u32x4* x, const u32x4* r, u32x4* h, u32x4* yb, u32x2* q, int64_t n16) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 a = ld16<NT>(x + i), b = ld16<NT>(r + i);
+    const u32x4 s = a + b;
+    st<NT>(s, h + i);
+    st<NT>(s ^ a, yb + i);
+    st<NT>(u32x2{s[0] ^ s[1], s[2] ^ s[3]}, q + i);
+  }
+}
+
+// Same traffic with the fused kernel's mapping: one workgroup of 64*W lanes
+// per row of C chunks, J chunks per lane (chunk c = j*64*W + lane), all loads
+// of a row issued before any store; SYNC adds the workgroup barrier the norm's
+// cross-wave reduction needs between the two phases.
+template <int J, bool SYNC>
+__global__ void __launch_bounds__(1024) k_mix_rows(const u32x4* x, const u32x4* r, u32x4* h, u32x4* yb, u32x2* q,
+                                                   int32_t M, int32_t C) {
+  const int64_t m = blockIdx.x;
+  if (m >= M) return;
+  const int t = threadIdx.x, T = blockDim.x;
+  u32x4 a[J], b[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = j * T + t;
+    if (c < C) {
+      a[j] = __builtin_nontemporal_load(x + m * C + c);
+      b[j] = __builtin_nontemporal_load(r + m * C + c);
+    }
+  }
+  if (SYNC) __syncthreads();
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = j * T + t;
+    if (c < C) {
+      const u32x4 s = a[j] + b[j];
+      __builtin_nontemporal_store(s, h + m * C + c);
+      __builtin_nontemporal_store(s ^ a[j], yb + m * C + c);
+      __builtin_nontemporal_store(u32x2{s[0] ^ s[1], s[2] ^ s[3]}, q + m * C + c);
+    }
+  }
+}
+
+// Persistent variant: G workgroups loop over rows m = blockIdx.x, +G, ...,
+// with the next row's loads issued before the current row's stores.
+template <int J>
+__global__ void __launch_bounds__(1024) k_mix_rows_persist(const u32x4* x, const u32x4* r, u32x4* h, u32x4* yb,
+                                                           u32x2* q, int32_t M, int32_t C) {
+  const int t = threadIdx.x, T = blockDim.x;
+  u32x4 a[J], b[J], na[J], nb[J];
+  int64_t m = blockIdx.x;
+  if (m >= M) return;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = j * T + t;
+    if (c < C) {
+      a[j] = __builtin_nontemporal_load(x + m * C + c);
+      b[j] = __builtin_nontemporal_load(r + m * C + c);
+    }
+  }
+  for (; m < M; m += gridDim.x) {
+    const int64_t n = m + gridDim.x;
+    if (n < M) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = j * T + t;
+        if (c < C) {
+          na[j] = __builtin_nontemporal_load(x + n * C + c);
+          nb[j] = __builtin_nontemporal_load(r + n * C + c);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = j * T + t;
+      if (c < C) {
+        const u32x4 s = a[j] + b[j];
+        __builtin_nontemporal_store(s, h + m * C + c);
+        __builtin_nontemporal_store(s ^ a[j], yb + m * C + c);
+        __builtin_nontemporal_store(u32x2{s[0] ^ s[1], s[2] ^ s[3]}, q + m * C + c);
+        a[j] = na[j];
+        b[j] = nb[j];
+      }
+    }
+  }
+}
+
+static int st_rc() { return hipGetLastError() == hipSuccess ? 0 : 3; }
+
+extern "C" {
+// kind: 0 read, 1 write, 2 copy, 3 mix; nt: nontemporal hints; blocks/threads: launch shape.
+int stream_probe(int kind, int nt, const void* a, void* b, void* c, void* d, void* e, int64_t n16, int blocks,
+                 int threads, void* stream) {
+  if (n16 <= 0 || blocks <= 0 || threads <= 0 || threads > 1024) return 1;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 g(blocks), t(threads);
+  switch (kind * 2 + (nt ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL(k_read<false>, g, t, 0, s, (const u32x4*)a, n16, (uint32_t*)b); break;
+    case 1: hipLaunchKernelGGL(k_read<true>, g, t, 0, s, (const u32x4*)a, n16, (uint32_t*)b); break;
+    case 2: hipLaunchKernelGGL(k_write<false>, g, t, 0, s, (u32x4*)b, n16); break;
+    case 3: hipLaunchKernelGGL(k_write<true>, g, t, 0, s, (u32x4*)b, n16); break;
+    case 4: hipLaunchKernelGGL(k_copy<false>, g, t, 0, s, (const u32x4*)a, (u32x4*)b, n16); break;
+    case 5: hipLaunchKernelGGL(k_copy<true>, g, t, 0, s, (const u32x4*)a, (u32x4*)b, n16); break;
+    case 6: hipLaunchKernelGGL(k_mix<false>, g, t, 0, s, (const u32x4*)a, (const u32x4*)b, (u32x4*)c, (u32x4*)d, (u32x2*)e, n16); break;
+    case 7: hipLaunchKernelGGL(k_mix<true>, g, t, 0, s, (const u32x4*)a, (const u32x4*)b, (u32x4*)c, (u32x4*)d, (u32x2*)e, n16); break;
+    default: return 1;
+  }
+  return st_rc();
+}
+
+// The row-mapped mix: M rows of C chunks, W waves and J chunks per lane
+// (J*64*W >= C), optional barrier; persist > 0 launches that many persistent
+// workgroups instead of one per row.
+int stream_probe_rows(const void* x, const void* r, void* h, void* yb, void* q, int32_t M, int32_t C, int32_t J,
+                      int32_t W, int32_t sync, int32_t persist, void* stream) {
+  if (M <= 0 || C <= 0 || W < 1 || W > 16 || (int64_t)J * W * 64 < C) return 1;
+  const dim3 g(persist > 0 ? persist : M), t(64 * W);
+  hipStream_t s = (hipStream_t)stream;
+  const u32x4 *X = (const u32x4*)x, *R = (const u32x4*)r;
+  u32x4 *H = (u32x4*)h, *Y = (u32x4*)yb;
+  u32x2* Q = (u32x2*)q;
+#define ROWS(JJ)                                                                         \
+  if (J == JJ) {                                                                          \
+    if (persist > 0) hipLaunchKernelGGL(k_mix_rows_persist<JJ>, g, t, 0, s, X, R, H, Y, Q, M, C); \
+    else if (sync) hipLaunchKernelGGL((k_mix_rows<JJ, true>), g, t, 0, s, X, R, H, Y, Q, M, C); \
+    else hipLaunchKernelGGL((k_mix_rows<JJ, false>), g, t, 0, s, X, R, H, Y, Q, M, C);     \
+    return st_rc();                                                                       \
+  }
+  ROWS(1) ROWS(2) ROWS(4) ROWS(7) ROWS(14)
+#undef ROWS
+  return 1;
+}
+}

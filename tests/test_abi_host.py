@@ -176,6 +176,7 @@ def test_launch_shape_always_fits():
             C_ = N // 8
             assert J in (1, 2, 3, 4, 7, 8, 14) and 1 <= W <= (4 if J >= 7 else 16), (N, rows, J, W)
             assert J * W * 64 >= C_, (N, rows, J, W)
-    assert fq.rmsq_query_shape(7168, 8192) == (14, 1)
+    assert fq.rmsq_query_shape(7168, 8192) == (2, 7)
+    assert fq.rmsq_query_shape(7168, 64) == (1, 14)
     with pytest.raises(fq.RmsqError):
         fq.rmsq_query_shape(32776, 1)

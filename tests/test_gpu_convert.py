@@ -1,6 +1,9 @@
 """The kernel's per-element number helpers and the raw gfx950 converts,
 checked on the GPU against the CPU oracle over exhaustive and adversarial
 inputs (test-only probe library, tests/hip/convert_probe.hip)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -191,3 +194,95 @@ def test_fp4_codes8_every_value_below_amax(orc):
         got = np.stack([(w >> (4 * i)) & 0xF for i in range(8)], -1).reshape(-1)
         want = orc.e2m1_encode(np.ldexp(bf16_f64(vals), -e))
         assert np.array_equal(tab[got], tab[want]), f"amax 0x{amax:04x}"
+
+
+# ------------------------------------------------- exhaustive pair sweeps --
+# Inside a group every value satisfies |v| <= amax, and the group's codes
+# depend only on (v, amax): the sweeps below cover every such pair of bf16
+# values (1.07e9 pairs per format), in batches. RMSQ_EXHAUSTIVE_STRIDE > 1
+# takes every k-th amax instead of all of them.
+STRIDE = int(os.environ.get("RMSQ_EXHAUSTIVE_STRIDE", "1"))
+_BY_MAG = FIN16[np.argsort(FIN16 & 0x7FFF, kind="stable")]
+_MAGS = np.sort(FIN16 & 0x7FFF)
+
+
+def _pair_batches(max_pairs=48_000_000):
+    amaxes = MAG16[1:][::STRIDE]
+    cnt = np.searchsorted(_MAGS, amaxes, side="right")          # values with |v| <= amax
+    cnt8 = (cnt + 7) // 8 * 8
+    i = 0
+    while i < amaxes.size:
+        j = i
+        tot = 0
+        while j < amaxes.size and (tot + cnt8[j] <= max_pairs or j == i):
+            tot += cnt8[j]
+            j += 1
+        v = np.zeros(tot, np.uint16)
+        owner = np.empty(tot // 8, np.int64)
+        o = 0
+        for k in range(i, j):
+            v[o:o + cnt[k]] = _BY_MAG[:cnt[k]]
+            owner[o // 8:(o + cnt8[k]) // 8] = k
+            o += cnt8[k]
+        yield amaxes, owner, v
+        i = j
+
+
+def _threaded(fn, arr, out, nthreads=16):
+    parts = np.array_split(np.arange(arr.size), nthreads)
+    with ThreadPoolExecutor(nthreads) as ex:
+        list(ex.map(lambda ix: out.__setitem__(ix, fn(arr[ix])) if ix.size else None, parts))
+
+
+def test_rcp_within_one_ulp_for_every_scale():
+    """Every scale the kernel forms (fl32(amax/448), amax >= 2^-100) has a
+    v_rcp_f32 within 1 ulp of its exact reciprocal."""
+    from fractions import Fraction
+    say("v_rcp_f32 over all scales")
+    amax = MAG16[MAG16 >= 0x0D80]
+    s = _f32(amax) / np.float32(448.0)
+    out = torch.empty(s.size, dtype=torch.float32, device="cuda")
+    call_probe("probe_rcp", dev(s), out, n=s.size)
+    r = host(out)
+    up = np.nextafter(r, np.float32(np.inf))
+    for sv, rv, uv in zip(s.tolist(), r.tolist(), up.tolist()):
+        exact = 1 / Fraction(sv)
+        assert abs(Fraction(rv) - exact) <= Fraction(uv) - Fraction(rv), sv
+
+
+def test_fp8_codes8_every_value_amax_pair(orc):
+    say(f"fp8_codes8 exhaustive pairs (stride {STRIDE})")
+    total = 0
+    for amaxes, owner, v in _pair_batches():
+        s = (_f32(amaxes.astype(np.uint16)) / np.float32(448.0))[owner]
+        vf = _f32(v)
+        out = torch.empty(v.size, dtype=torch.uint8, device="cuda")
+        call_probe("probe_fp8_codes", dev(vf), dev(s), out, n=v.size // 8)
+        q = vf.astype(np.float64) / np.repeat(s.astype(np.float64), 8)
+        want = np.empty(v.size, np.uint8)
+        _threaded(orc.e4m3fn_encode, q, want)
+        got = host(out)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"{bad.size} codes differ, first v={vf[bad[0]]} s={s[bad[0] // 8]}"
+        total += v.size
+    say(f"fp8 pairs checked: {total}")
+
+
+def test_fp4_codes8_every_value_amax_pair(orc):
+    say(f"fp4_codes8 exhaustive pairs (stride {STRIDE})")
+    tab = orc.e2m1_table()
+    total = 0
+    for amaxes, owner, v in _pair_batches():
+        ex = np.array([orc.mx_scale_exponent(a) for a in bf16_f64(amaxes)], np.int64)
+        byte = (ex + 127).astype(np.uint8)[owner]
+        out = torch.empty(v.size // 8, dtype=torch.int32, device="cuda")
+        call_probe("probe_fp4_codes", dev(_f32(v)), dev(byte), out, n=v.size // 8)
+        w = host(out).view(np.uint32)
+        got = np.stack([(w >> (4 * i)) & 0xF for i in range(8)], -1).reshape(-1)
+        q = np.ldexp(bf16_f64(v), -np.repeat(ex[owner], 8))
+        want = np.empty(v.size, np.uint8)
+        _threaded(orc.e2m1_encode, q, want)
+        bad = np.flatnonzero(tab[got] != tab[want])
+        assert bad.size == 0, f"{bad.size} codes differ"
+        total += v.size
+    say(f"fp4 pairs checked: {total}")
