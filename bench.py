@@ -78,6 +78,9 @@ class Workload:
                     r = torch.from_numpy(p["residual"].view("int16")).view(torch.bfloat16).cuda()
                     ro = torch.empty_like(r)
                 q, sc, yb = fq.alloc_outputs(M, N, fmt, layout, s["keep_bf16"])
+                for t in (ro, q, sc, yb):      # first touch outside the timed region
+                    if t is not None:
+                        t.zero_()
                 keep += [x, g, r, ro, q, sc, yb]
                 probs.append(fq.make_problem(x, g, p["eps"], q, sc, residual_in=r, residual_out=ro,
                                              out_bf16=yb, fmt=fmt, scale_layout=layout))
@@ -109,26 +112,84 @@ def time_workload(w, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
-def copy_ceiling_gbps():
-    """A plain device copy (torch's copy kernel) of 2 GiB: read + write bytes
-    over its time, the box's achievable streaming bandwidth."""
+def _stream_probe():
+    import ctypes as C
+    L = C.CDLL(os.path.join(ROOT, "tests", "hip", "libconvert_probe.so"))
+    L.stream_probe.restype = C.c_int
+    L.stream_probe.argtypes = [C.c_int, C.c_int] + [C.c_void_p] * 5 + [C.c_int64, C.c_int, C.c_int, C.c_void_p]
+    return L
+
+
+def ceilings(reps=30):
+    """Achievable HBM bandwidth on this machine from the no-arithmetic stream
+    probes (tests/hip/stream_probe.hip), nontemporal loads and stores like the
+    fused kernel, three rotating buffer sets so nothing is served from the
+    Infinity Cache: a plain copy, and a stream with the fused FP8 kernel's
+    exact traffic mix (read 2 x 16 B, write 2 x 16 B + 8 B per 8 elements)."""
     import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty(n, dtype=torch.uint8, device="cuda")
-    a.fill_(1)
-    for _ in range(3):
-        b.copy_(a)
+    L = _stream_probe()
+    st = torch.cuda.current_stream().cuda_stream
+    n16 = 8192 * 7168 // 8
+    sets = [[torch.ones(n16 * 16, dtype=torch.uint8, device="cuda") for _ in range(4)] +
+            [torch.zeros(n16 * 8, dtype=torch.uint8, device="cuda")] for _ in range(3)]
+    out = {}
+    for kind, name, nbytes in ((2, "copy", 2 * n16 * 16), (3, "fused_mix", 4 * n16 * 16 + n16 * 8)):
+        def go(i):
+            S = sets[i % 3]
+            assert L.stream_probe(kind, 1, *[t.data_ptr() for t in S], n16, 16384, 256, st) == 0
+        for i in range(50):
+            go(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(reps):
+            go(i)
+        t1.record()
+        torch.cuda.synchronize()
+        out[name] = round(nbytes / (t0.elapsed_time(t1) / reps * 1e-3) / 1e9, 1)
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_probe(launches):
+    """For counter calibration under rocprofv3 --pmc: a nontemporal copy of
+    exactly 1 GiB (1 GiB read, 1 GiB written) per launch."""
+    import torch
+    L = _stream_probe()
+    n16 = (1 << 30) // 16
+    a = torch.ones(n16 * 16, dtype=torch.uint8, device="cuda")
+    b = torch.zeros(n16 * 16, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(launches):
+        assert L.stream_probe(2, 1, a.data_ptr(), b.data_ptr(), None, None, None, n16, 16384, 256, st) == 0
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(10):
-        b.copy_(a)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / 10
-    del a, b
-    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "fp4_quant_amd", "csrc")
+    for fn in sorted(os.listdir(d)):
+        if fn.endswith((".h", ".hip")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(d, fn), "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("{"):
+            rec = json.loads(line)
+            if rec.get("kernel_source_sha256") == kernel_source_hash():
+                return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(w, budget_s):
@@ -167,13 +228,16 @@ SPECS = {
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed launches first; a few hundred let the clocks settle")
     ap.add_argument("--config", default="prefill", choices=sorted(SPECS))
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline budget (0 skips it)")
     ap.add_argument("--only-kernel", action="store_true",
                     help="launch only the headline workload (for profiler runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="LAUNCHES",
+                    help="only launch a 1 GiB nontemporal copy LAUNCHES times (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -185,6 +249,9 @@ def main():
     import fp4_quant_amd as fq
     assert torch.cuda.is_available() and fq.rmsq_device_supported(0), "needs a gfx950 GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     specs, fmt, layout = SPECS[args.config]
     log(f"bench: building workload {args.config}")
@@ -206,14 +273,14 @@ def main():
                 continue
             log(f"bench: workload {name}")
             wk = Workload(name, sp, f, lay)
-            pl = time_workload(wk, max(20, args.steps // 2), 10)
+            pl = time_workload(wk, max(50, args.steps // 2), max(50, args.warmup))
             configs[name] = {"us_per_launch": round(pl * 1e3, 2), "GBps": round(wk.bytes / (pl * 1e-3) / 1e9, 1),
                              "frac_of_peak": round(wk.bytes / (pl * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                              "Mtok_per_s": round(wk.rows / (pl * 1e-3) / 1e6, 2), "bytes": wk.bytes}
             del wk
             torch.cuda.empty_cache()
-    ceiling = copy_ceiling_gbps()
-    log(f"bench: device copy ceiling {ceiling:.0f} GB/s")
+    ceil = ceilings()
+    log(f"bench: stream ceilings (GB/s) {ceil}")
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -242,11 +309,12 @@ def main():
         "mtok_per_s": round(w.rows / (step_ms * 1e-3) / 1e6, 2),
         "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": recorded_traffic(args.config),
                      "kernel": "rmsq_fused_kernel<%d,%d> x %d waves" % ((fmt,) + fq.rmsq_query_shape(N, w.rows)),
                      "bytes_per_launch": w.bytes,
                      "us_per_launch": round(step_ms * 1e3, 2)},
-        "copy_ceiling_GBps": round(ceiling, 1),
+        "stream_ceilings_GBps": ceil,
+        "frac_of_mix_ceiling": round(gbps / ceil["fused_mix"], 4) if args.config == "prefill" else None,
         "cpu_baseline": cpu,
         "configs": configs,
         "timed_wall_s": round(wall, 3),

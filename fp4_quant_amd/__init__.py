@@ -56,7 +56,7 @@ class rmsq_problem(C.Structure):
 
 EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "rmsq_device_supported",
            "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape",
-           "rmsq_query_shape")
+           "rmsq_query_shape", "rmsq_set_row_group")
 
 _lib = None
 
@@ -84,6 +84,8 @@ def lib() -> C.CDLL:
         L.rmsq_last_error.argtypes = []
         L.rmsq_set_shape.restype = None
         L.rmsq_set_shape.argtypes = [i32, i32]
+        L.rmsq_set_row_group.restype = None
+        L.rmsq_set_row_group.argtypes = [i32]
         L.rmsq_query_shape.restype = i32
         L.rmsq_query_shape.argtypes = [i64, i64, C.POINTER(i32), C.POINTER(i32)]
         _lib = L
@@ -147,6 +149,10 @@ def rmsq_scale_bytes(M, N, group, fmt, scale_layout=SCALE_ROW_MAJOR) -> int:
 
 def rmsq_set_shape(J: int = 0, W: int = 0) -> None:
     lib().rmsq_set_shape(int(J), int(W))
+
+
+def rmsq_set_row_group(g: int = 0) -> None:
+    lib().rmsq_set_row_group(int(g))
 
 
 def rmsq_query_shape(N: int, rows: int):

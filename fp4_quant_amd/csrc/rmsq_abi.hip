@@ -128,24 +128,24 @@ bool device_is_gfx950(int dev) {
 }
 
 // Launch shape: chunk-steps per lane J (compiled set) and waves per row W.
-// Measured on MI355X (prefill 8192 x 7168): a row spread over 7 waves with 2
-// chunks per lane sustains the traffic far better than long per-lane rows
-// (one wave per row leaves the HBM queues bursty), and the fixed per-wave cost
-// of the norm (reduction, fp64 inverse square root) argues against going to a
-// single chunk per lane when rows are plentiful. So: the smallest J whose W
-// stays <= 8 with at most 20% idle lanes; with few rows (latency-bound
-// calls), the smallest J that fits at all, to spread each row widest.
-constexpr int kJs[] = {1, 2, 3, 4, 7, 8, 14};
+// Measured on MI355X: spreading a row over several waves with 2-4 chunks per
+// lane sustains the traffic far better than long per-lane rows (one wave per
+// 7168-wide row leaves the HBM queues bursty), while a single chunk per lane
+// pays the per-wave fixed cost of the norm (reduction, fp64 inverse square
+// root) too often. Rule: the first J of 2, 3, 4, 1 whose W stays <= 8 with
+// at most 20% idle lanes (7168 -> J 2 x 7 waves, 1536 -> J 3 x 1 wave);
+// then relax the wave limit, then take anything that fits.
+constexpr int kJs[] = {2, 3, 4, 1, 7, 8, 14};
 
 void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
-  const bool few_rows = rows < 1024;
+  (void)rows;
   for (int pass = 0; pass < 3; ++pass) {
     for (int J : kJs) {
       const int64_t W = (C + 64 * J - 1) / (64 * J);
       if (W > rmsq::max_waves(J)) continue;
       const int64_t slots = W * 64 * J;
-      if (pass < 2 && J > 1 && (slots - C) * 5 > slots) continue;
-      if (pass == 0 && !few_rows && W > 8) continue;
+      if (pass < 2 && (slots - C) * 5 > slots) continue;
+      if (pass == 0 && W > 8) continue;
       *J_out = J;
       *W_out = (int)W;
       return;
@@ -174,7 +174,7 @@ rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, hipStream_t stream) 
 
 // Launch-shape override for measurement sweeps, set by rmsq_set_shape
 // (0, 0 = automatic choice).
-std::atomic<int> g_force_J{0}, g_force_W{0};
+std::atomic<int> g_force_J{0}, g_force_W{0}, g_force_G{0};
 
 bool compiled_J(int J) {
   for (int k : kJs)
@@ -237,6 +237,14 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, void* stream) {
     J = fJ;
     W = fW;
   }
+  // Row grouping per XCD (measured): 16 rows when a problem writes tiled
+  // MXFP4 scales (half a 32-row tile per XCD keeps each tile's scale lines in
+  // few L2s, +1%); plain dispatch order otherwise, which was fastest for
+  // row-major scales.
+  bool tiled = false;
+  for (int i = 0; i < n; ++i) tiled |= L.p[i].layout == RMSQ_SCALE_TILED32;
+  L.row_group = tiled ? 16 : 1;
+  if (const int fG = g_force_G.load(); fG > 0) L.row_group = fG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(L, J, W, s) : launch_fmt<1>(L, J, W, s);
 }
@@ -296,6 +304,8 @@ void rmsq_set_shape(int32_t J, int32_t W) {
   g_force_J.store(J);
   g_force_W.store(W);
 }
+
+void rmsq_set_row_group(int32_t g) { g_force_G.store(g > 0 && g <= 64 ? g : 0); }
 
 int32_t rmsq_query_shape(int64_t N, int64_t rows, int32_t* J, int32_t* W) {
   if (N <= 0 || N % 8 || N > RMSQ_N_MAX || rows < 0 || !J || !W) return RMSQ_ERR_INVALID_ARG;

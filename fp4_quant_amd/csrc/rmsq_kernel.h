@@ -61,7 +61,22 @@ struct Launch {
   Problem p[kMaxProblems];
   int32_t count;
   int32_t rows;           // grid size: one workgroup per row over all problems
+  int32_t row_group;      // rows kept together on one XCD (1 = dispatch order)
 };
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2. With row_group = g > 1, every run of g consecutive rows is processed on
+// one XCD (rows of 8*g consecutive workgroups are interleaved at g-row
+// granularity), so scale bytes of neighbouring rows that share a cache line -
+// a 224-byte scale row, or the 32 rows of a tiled MXFP4 scale block - are
+// written from a single L2 instead of being merged from several. The mapping
+// is a bijection on each block of 8*g rows; a ragged tail keeps dispatch order.
+__device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t g) {
+  const int32_t span = 8 * g;
+  if (g <= 1 || b >= rows / span * span) return b;
+  const int32_t x = b & 7, k = b >> 3;
+  return ((k / g) * 8 + x) * g + (k % g);
+}
 
 template <int FMT, int J>
 __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Launch L) {
@@ -71,11 +86,10 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   constexpr bool kShort = J <= 4;
   __shared__ double red[kMaxWaves];
 
-  // Rows in dispatch order: workgroups go round-robin to the 8 XCDs, so
-  // neighbouring rows run on different XCDs at the same time. (Giving each
-  // XCD a contiguous block of rows instead was measured 12% slower on the
-  // prefill workload.)
-  const int32_t row = (int32_t)blockIdx.x;
+  // Neighbouring row groups run on different XCDs at the same time. (Giving
+  // each XCD one contiguous block of M/8 rows instead was measured 12%
+  // slower on the prefill workload.)
+  const int32_t row = row_of_block((int32_t)blockIdx.x, L.rows, L.row_group);
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < kMaxProblems; ++i)

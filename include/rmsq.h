@@ -153,6 +153,12 @@ const char* rmsq_last_error(void);
  * choice. Results do not depend on the shape. */
 void rmsq_set_shape(int32_t J, int32_t W);
 
+/* Measurement hook: force the number of consecutive rows kept together on one
+ * XCD (1..64; 1 = plain dispatch order) for later calls in this process;
+ * 0 restores the automatic choice (16 when a problem uses the tiled MXFP4
+ * scale layout, else 1). Results do not depend on it. */
+void rmsq_set_row_group(int32_t g);
+
 /* The launch shape the library picks (without an override) for rows of N
  * elements, the widest problem of a call, and `rows` rows in total: J chunks
  * of 8 elements per lane and W waves per workgroup (one workgroup per row).

@@ -131,6 +131,61 @@ __global__ void __launch_bounds__(1024) k_mix_rows_persist(const u32x4* x, const
   }
 }
 
+// Cache-policy variants through buffer instructions (raw buffers, bounds
+// checked by the descriptor: out-of-range lanes read 0 and drop stores).
+// Policy bits: 1 = sc0, 2 = nt, 16 = sc1.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+template <int LP, int SP>
+__global__ void k_mix_pol(const u32x4* x, const u32x4* r, u32x4* h, u32x4* yb, u32x2* q, int64_t n16) {
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, n16 * 16), rr = rsrc(r, n16 * 16), rh = rsrc(h, n16 * 16),
+                               ry = rsrc(yb, n16 * 16), rq = rsrc(q, n16 * 8);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x) {
+    const int off = (int)(i * 16);
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, LP);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, LP);
+    const u32x4 s = a + b;
+    __builtin_amdgcn_raw_buffer_store_b128(s, rh, off, 0, SP);
+    __builtin_amdgcn_raw_buffer_store_b128(s ^ a, ry, off, 0, SP);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{s[0] ^ s[1], s[2] ^ s[3]}, rq, (int)(i * 8), 0, SP);
+  }
+}
+
+// Row-mapped (W waves, 2 chunks per lane, C chunks per row) with the policies.
+template <int LP, int SP>
+__global__ void __launch_bounds__(1024) k_rows_pol(const u32x4* x, const u32x4* r, u32x4* h, u32x4* yb, u32x2* q,
+                                                   int32_t M, int32_t C) {
+  const int64_t m = blockIdx.x;
+  if (m >= M) return;
+  const int t = threadIdx.x, T = blockDim.x;
+  const int64_t rb = m * C * 16;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x + m * C, C * 16), rr = rsrc(r + m * C, C * 16),
+                               rh = rsrc(h + m * C, C * 16), ry = rsrc(yb + m * C, C * 16), rq = rsrc(q + m * C, C * 8);
+  (void)rb;
+  u32x4 a[2], b[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = j * T + t;
+    a[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, c * 16, 0, LP);
+    b[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, c * 16, 0, LP);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = j * T + t;
+    const u32x4 s = a[j] + b[j];
+    __builtin_amdgcn_raw_buffer_store_b128(s, rh, c * 16, 0, SP);
+    __builtin_amdgcn_raw_buffer_store_b128(s ^ a[j], ry, c * 16, 0, SP);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{s[0] ^ s[1], s[2] ^ s[3]}, rq, c * 8, 0, SP);
+  }
+}
+
+__global__ void k_empty(int* p) {
+  if (p && threadIdx.x == 1024) p[0] = 0;   // never true: blocks are at most 1024 threads
+}
+
 static int st_rc() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 
 extern "C" {
@@ -175,5 +230,35 @@ int stream_probe_rows(const void* x, const void* r, void* h, void* yb, void* q, 
   ROWS(1) ROWS(2) ROWS(4) ROWS(7) ROWS(14)
 #undef ROWS
   return 1;
+}
+// Policy probes: lp, sp in {0, 1, 2, 3, 16, 17, 18, 19}; rows > 0 selects the
+// row-mapped kernel with W = threads / 64 waves per row (2 chunks per lane).
+#define POL_CASE(LP, SP)                                                                                  \
+  if (lp == LP && sp == SP) {                                                                             \
+    if (rows > 0)                                                                                         \
+      hipLaunchKernelGGL((k_rows_pol<LP, SP>), dim3(rows), dim3(threads), 0, s, X, R, H, Y, Q, rows, C);  \
+    else                                                                                                  \
+      hipLaunchKernelGGL((k_mix_pol<LP, SP>), dim3(blocks), dim3(threads), 0, s, X, R, H, Y, Q, n16);     \
+    return st_rc();                                                                                       \
+  }
+#define POL_ROW(LP) POL_CASE(LP, 0) POL_CASE(LP, 1) POL_CASE(LP, 2) POL_CASE(LP, 3) POL_CASE(LP, 16) POL_CASE(LP, 17) POL_CASE(LP, 18) POL_CASE(LP, 19)
+int stream_probe_policy(int lp, int sp, const void* x, const void* r, void* h, void* yb, void* q, int64_t n16,
+                        int blocks, int threads, int rows, int C, void* stream) {
+  if (n16 <= 0 || threads <= 0 || threads > 1024 || n16 * 16 > 0x7FFFFFFF) return 1;
+  if (rows > 0 && ((int64_t)rows * C != n16 || 2 * threads < C)) return 1;
+  hipStream_t s = (hipStream_t)stream;
+  const u32x4 *X = (const u32x4*)x, *R = (const u32x4*)r;
+  u32x4 *H = (u32x4*)h, *Y = (u32x4*)yb;
+  u32x2* Q = (u32x2*)q;
+  POL_ROW(0) POL_ROW(1) POL_ROW(2) POL_ROW(3) POL_ROW(16) POL_ROW(17) POL_ROW(18) POL_ROW(19)
+  return 1;
+}
+#undef POL_ROW
+#undef POL_CASE
+// An empty kernel: the launch-overhead floor of back-to-back launches.
+int stream_probe_empty(int blocks, int threads, void* stream) {
+  if (blocks <= 0 || threads <= 0 || threads > 1024) return 1;
+  hipLaunchKernelGGL(k_empty, dim3(blocks), dim3(threads), 0, (hipStream_t)stream, (int*)nullptr);
+  return st_rc();
 }
 }
