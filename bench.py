@@ -92,6 +92,25 @@ class Workload:
         fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0])
 
 
+class UnfusedWorkload(Workload):
+    """The same prefill batch through the two kernels the fusion replaces:
+    add_rmsnorm writes the residual and the bf16 rows, then the standalone
+    per-group quant reads the bf16 rows back (two launches per step)."""
+
+    def __init__(self, name, specs, fmt, layout=0):
+        super().__init__(name, specs, fmt, layout)
+        s = specs[0]
+        self.moved = self.bytes + s["M"] * s["N"] * 2 * (0 if s["keep_bf16"] else 1) + s["M"] * s["N"] * 2
+
+    def launch(self, i):
+        import fp4_quant_amd as fq
+        probs, keep = self.sets[i % len(self.sets)]
+        x, g, r, ro, q, sc, yb = keep[:7]
+        M, N = x.shape
+        fq.add_rmsnorm(x, r, g, 1e-6, M, N, ro, yb)
+        fq.dynamic_per_group_scaled_quant(yb, M, N, 128 if self.fmt == 0 else 32, self.fmt, self.layout, q, sc)
+
+
 def time_workload(w, steps, warmup):
     """Warm up, then time `steps` back-to-back launches between two HIP events
     recorded on the launch stream (torch's current stream, which the binding
@@ -279,6 +298,17 @@ def main():
                              "Mtok_per_s": round(wk.rows / (pl * 1e-3) / 1e6, 2), "bytes": wk.bytes}
             del wk
             torch.cuda.empty_cache()
+    if not args.no_configs and args.config == "prefill":
+        log("bench: unfused pair on the prefill batch")
+        wu = UnfusedWorkload("unfused", specs, fmt, layout)
+        pu = time_workload(wu, max(50, args.steps // 2), max(50, args.warmup))
+        configs["prefill_unfused_pair"] = {
+            "us_per_step": round(pu * 1e3, 2), "launches_per_step": 2,
+            "fused_algorithmic_GBps": round(w.bytes / (pu * 1e-3) / 1e9, 1),
+            "bytes_moved": wu.moved, "moved_GBps": round(wu.moved / (pu * 1e-3) / 1e9, 1),
+            "fused_speedup": round(pu / step_ms, 3)}
+        del wu
+        torch.cuda.empty_cache()
     ceil = ceilings()
     log(f"bench: stream ceilings (GB/s) {ceil}")
 

@@ -54,7 +54,8 @@ class rmsq_problem(C.Structure):
                 ("ldb", C.c_int64)]
 
 
-EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "rmsq_device_supported",
+EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "add_rmsnorm",
+           "dynamic_per_group_scaled_quant", "rmsq_device_supported",
            "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape",
            "rmsq_query_shape", "rmsq_set_row_group")
 
@@ -74,6 +75,10 @@ def lib() -> C.CDLL:
         L.rmsnorm_quant_group.argtypes = [p, p, p, C.c_float, i64, i64, i32, i32, p, p, p, p, p]
         L.rmsnorm_quant_group_multi.restype = i32
         L.rmsnorm_quant_group_multi.argtypes = [C.POINTER(rmsq_problem), i32, p]
+        L.add_rmsnorm.restype = i32
+        L.add_rmsnorm.argtypes = [p, p, p, C.c_float, i64, i64, p, p, p]
+        L.dynamic_per_group_scaled_quant.restype = i32
+        L.dynamic_per_group_scaled_quant.argtypes = [p, i64, i64, i32, i32, i32, p, p, p]
         L.rmsq_device_supported.restype = i32
         L.rmsq_device_supported.argtypes = [i32]
         L.rmsq_scale_bytes.restype = C.c_size_t
@@ -137,6 +142,20 @@ def rmsnorm_quant_group_multi(problems, stream=None) -> None:
     ``make_problem``) in one kernel launch."""
     arr = (rmsq_problem * len(problems))(*problems)
     _check(lib().rmsnorm_quant_group_multi(arr, len(problems), _stream(stream)))
+
+
+def add_rmsnorm(x, residual_in, gamma, eps, M, N, residual_out, out_bf16, stream=None) -> None:
+    """The add + RMSNorm kernel alone (bf16 output), C argument order."""
+    _check(lib().add_rmsnorm(_ptr(x), _ptr(residual_in), _ptr(gamma), float(eps), int(M), int(N),
+                             _ptr(residual_out), _ptr(out_bf16),
+                             _stream(stream, x.device if x is not None else None)))
+
+
+def dynamic_per_group_scaled_quant(x, M, N, group, fmt, scale_layout, out_q, out_scale, stream=None) -> None:
+    """The per-group quantization alone on bf16 rows, C argument order."""
+    _check(lib().dynamic_per_group_scaled_quant(_ptr(x), int(M), int(N), int(group), int(fmt),
+                                                int(scale_layout), _ptr(out_q), _ptr(out_scale),
+                                                _stream(stream, x.device if x is not None else None)))
 
 
 def rmsq_device_supported(device: int = 0) -> bool:

@@ -15,6 +15,8 @@ HIP_FLAGS = [
     # no packed fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
+    # lane flags are combined with bitwise | on purpose: no short-circuit branches
+    "-Wno-bitwise-instead-of-logical",
 ]
 
 

@@ -44,38 +44,52 @@ size_t scale_bytes(int64_t M, int64_t N, int32_t group, int32_t fmt, int32_t lay
   return 0;
 }
 
+// What a problem asks for: the fused operation, the norm alone (bf16
+// output, no quantization), or the quantization alone (x is the bf16 input).
+enum class Mode { kFused, kNormOnly, kQuantOnly };
+
 // Validate one problem and append its buffers' byte ranges.
-rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Range* rs, int* nr) {
-  if (p.fmt != RMSQ_FMT_FP8_E4M3FN && p.fmt != RMSQ_FMT_MXFP4_E2M1)
-    return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: unknown fmt %d", idx, p.fmt);
-  if (p.fmt != fmt0) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: all problems must share fmt", idx);
-  const int32_t want_group = p.fmt == RMSQ_FMT_FP8_E4M3FN ? 128 : 32;
-  if (p.group != want_group)
-    return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: group %d unsupported for fmt %d (need %d)", idx, p.group, p.fmt,
-                want_group);
-  if (p.scale_layout != RMSQ_SCALE_ROW_MAJOR && p.scale_layout != RMSQ_SCALE_TILED32)
-    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: unknown scale layout %d", idx, p.scale_layout);
-  if (p.scale_layout == RMSQ_SCALE_TILED32 && p.fmt != RMSQ_FMT_MXFP4_E2M1)
-    return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: the tiled scale layout is for MXFP4 only", idx);
+rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Mode mode, Range* rs, int* nr) {
+  const bool quant = mode != Mode::kNormOnly, norm = mode != Mode::kQuantOnly;
+  int32_t group = 8;
+  if (quant) {
+    if (p.fmt != RMSQ_FMT_FP8_E4M3FN && p.fmt != RMSQ_FMT_MXFP4_E2M1)
+      return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: unknown fmt %d", idx, p.fmt);
+    if (p.fmt != fmt0) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: all problems must share fmt", idx);
+    group = p.fmt == RMSQ_FMT_FP8_E4M3FN ? 128 : 32;
+    if (p.group != group)
+      return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: group %d unsupported for fmt %d (need %d)", idx, p.group, p.fmt,
+                  group);
+    if (p.scale_layout != RMSQ_SCALE_ROW_MAJOR && p.scale_layout != RMSQ_SCALE_TILED32)
+      return fail(RMSQ_ERR_INVALID_ARG, "problem %d: unknown scale layout %d", idx, p.scale_layout);
+    if (p.scale_layout == RMSQ_SCALE_TILED32 && p.fmt != RMSQ_FMT_MXFP4_E2M1)
+      return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: the tiled scale layout is for MXFP4 only", idx);
+  }
   if (p.M < 0) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: M = %lld < 0", idx, (long long)p.M);
-  if (p.N <= 0 || p.N % p.group) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: N = %lld not a positive multiple of %d", idx, (long long)p.N, p.group);
+  if (p.N <= 0 || p.N % group)
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: N = %lld not a positive multiple of %d", idx, (long long)p.N, group);
   if (p.N > RMSQ_N_MAX) return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: N = %lld > %d", idx, (long long)p.N, RMSQ_N_MAX);
   if (p.M > INT32_MAX) return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: M = %lld too large", idx, (long long)p.M);
-  if (!std::isfinite(p.eps) || p.eps < 0.0f) return fail(RMSQ_ERR_INVALID_ARG, "problem %d: eps must be finite and >= 0", idx);
+  if (norm && (!std::isfinite(p.eps) || p.eps < 0.0f))
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: eps must be finite and >= 0", idx);
   const int64_t ldx = p.ldx ? p.ldx : p.N, ldr = p.ldr ? p.ldr : p.N, ldb = p.ldb ? p.ldb : p.N;
-  if (ldx < p.N || ldx % 8 || (p.residual_in && (ldr < p.N || ldr % 8)) || (p.out_bf16 && (ldb < p.N || ldb % 8)))
+  if (ldx < p.N || ldx % 8 || (norm && p.residual_in && (ldr < p.N || ldr % 8)) ||
+      (norm && p.out_bf16 && (ldb < p.N || ldb % 8)))
     return fail(RMSQ_ERR_INVALID_ARG, "problem %d: row strides must be multiples of 8 and >= N", idx);
   if (p.M == 0) return RMSQ_OK;  // nothing is read or written; pointers may be NULL
-  if ((p.residual_in == nullptr) != (p.residual_out == nullptr))
+  if (norm && (p.residual_in == nullptr) != (p.residual_out == nullptr))
     return fail(RMSQ_ERR_INVALID_ARG, "problem %d: residual_in and residual_out must both be set or both be NULL", idx);
-  if (!p.x || !p.gamma || !p.out_q || !p.out_scale)
+  if (!p.x || (norm && !p.gamma) || (quant && (!p.out_q || !p.out_scale)))
     return fail(RMSQ_ERR_INVALID_ARG, "problem %d: x, gamma, out_q and out_scale must be non-NULL", idx);
-  if (!aligned(p.x, 16) || !aligned(p.gamma, 16) || (p.residual_in && !aligned(p.residual_in, 16)) ||
-      (p.residual_out && !aligned(p.residual_out, 16)) || (p.out_bf16 && !aligned(p.out_bf16, 16)))
+  if (mode == Mode::kNormOnly && !p.out_bf16)
+    return fail(RMSQ_ERR_INVALID_ARG, "problem %d: the norm alone needs out_bf16", idx);
+  if (!aligned(p.x, 16) || (norm && (!aligned(p.gamma, 16) || (p.residual_in && !aligned(p.residual_in, 16)) ||
+                                     (p.residual_out && !aligned(p.residual_out, 16)) ||
+                                     (p.out_bf16 && !aligned(p.out_bf16, 16)))))
     return fail(RMSQ_ERR_INVALID_ARG, "problem %d: bf16 pointers must be 16-byte aligned", idx);
-  if (!aligned(p.out_q, p.fmt == RMSQ_FMT_FP8_E4M3FN ? 8 : 4))
+  if (quant && !aligned(p.out_q, p.fmt == RMSQ_FMT_FP8_E4M3FN ? 8 : 4))
     return fail(RMSQ_ERR_INVALID_ARG, "problem %d: out_q misaligned", idx);
-  if (p.fmt == RMSQ_FMT_FP8_E4M3FN && !aligned(p.out_scale, 4))
+  if (quant && p.fmt == RMSQ_FMT_FP8_E4M3FN && !aligned(p.out_scale, 4))
     return fail(RMSQ_ERR_INVALID_ARG, "problem %d: out_scale must be 4-byte aligned", idx);
 
   auto add = [&](const void* ptr, int64_t bytes, bool out, int kind) {
@@ -84,14 +98,18 @@ rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Range* r
   };
   const int64_t M = p.M, N = p.N;
   add(p.x, ((M - 1) * ldx + N) * 2, false, 0);
-  if (p.residual_in) {
-    add(p.residual_in, ((M - 1) * ldr + N) * 2, false, 1);
-    add(p.residual_out, ((M - 1) * ldr + N) * 2, true, 2);
+  if (norm) {
+    if (p.residual_in) {
+      add(p.residual_in, ((M - 1) * ldr + N) * 2, false, 1);
+      add(p.residual_out, ((M - 1) * ldr + N) * 2, true, 2);
+    }
+    add(p.gamma, N * 2, false, 3);
+    if (p.out_bf16) add(p.out_bf16, ((M - 1) * ldb + N) * 2, true, 6);
   }
-  add(p.gamma, N * 2, false, 3);
-  add(p.out_q, M * (p.fmt == RMSQ_FMT_FP8_E4M3FN ? N : N / 2), true, 4);
-  add(p.out_scale, (int64_t)scale_bytes(M, N, p.group, p.fmt, p.scale_layout), true, 5);
-  if (p.out_bf16) add(p.out_bf16, ((M - 1) * ldb + N) * 2, true, 6);
+  if (quant) {
+    add(p.out_q, M * (p.fmt == RMSQ_FMT_FP8_E4M3FN ? N : N / 2), true, 4);
+    add(p.out_scale, (int64_t)scale_bytes(M, N, p.group, p.fmt, p.scale_layout), true, 5);
+  }
   return RMSQ_OK;
 }
 
@@ -182,7 +200,7 @@ bool compiled_J(int J) {
   return false;
 }
 
-rmsq_status run(const rmsq_problem* ps, int32_t count, void* stream) {
+rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) {
   g_err[0] = 0;
   if (!ps) return fail(RMSQ_ERR_INVALID_ARG, "problems is NULL");
   if (count < 1 || count > RMSQ_MAX_PROBLEMS)
@@ -190,7 +208,7 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, void* stream) {
   Range rs[RMSQ_MAX_PROBLEMS * 7];
   int nr = 0;
   for (int i = 0; i < count; ++i) {
-    const rmsq_status s = check_problem(ps[i], i, ps[0].fmt, rs, &nr);
+    const rmsq_status s = check_problem(ps[i], i, ps[0].fmt, mode, rs, &nr);
     if (s != RMSQ_OK) return s;
   }
   if (const rmsq_status s = check_overlaps(rs, nr); s != RMSQ_OK) return s;
@@ -207,8 +225,8 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, void* stream) {
     d.r = static_cast<const uint16_t*>(p.residual_in);
     d.h = static_cast<uint16_t*>(p.residual_out);
     d.gamma = static_cast<const uint16_t*>(p.gamma);
-    d.q = static_cast<uint8_t*>(p.out_q);
-    d.scale = p.out_scale;
+    d.q = mode == Mode::kNormOnly ? nullptr : static_cast<uint8_t*>(p.out_q);
+    d.scale = mode == Mode::kNormOnly ? nullptr : p.out_scale;
     d.yb = static_cast<uint16_t*>(p.out_bf16);
     d.ldx = p.ldx ? p.ldx : p.N;
     d.ldr = p.ldr ? p.ldr : p.N;
@@ -246,7 +264,40 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, void* stream) {
   L.row_group = tiled ? 16 : 1;
   if (const int fG = g_force_G.load(); fG > 0) L.row_group = fG;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == Mode::kNormOnly) return launch_fmt<2>(L, J, W, s);
   return ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(L, J, W, s) : launch_fmt<1>(L, J, W, s);
+}
+
+// The quantization alone on bf16 rows: grid x = row, y = blocks of 128
+// chunks, one 8-element chunk per lane.
+rmsq_status run_quant(const rmsq_problem& p, void* stream) {
+  g_err[0] = 0;
+  Range rs[4];
+  int nr = 0;
+  if (const rmsq_status st = check_problem(p, 0, p.fmt, Mode::kQuantOnly, rs, &nr); st != RMSQ_OK) return st;
+  if (const rmsq_status st = check_overlaps(rs, nr); st != RMSQ_OK) return st;
+  if (p.M == 0) return RMSQ_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
+    return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");
+  rmsq::QuantArgs A;
+  A.x = static_cast<const uint16_t*>(p.x);
+  A.ldx = p.ldx ? p.ldx : p.N;
+  A.q = static_cast<uint8_t*>(p.out_q);
+  A.scale = p.out_scale;
+  A.M = (int32_t)p.M;
+  A.N = (int32_t)p.N;
+  A.layout = p.scale_layout;
+  const int64_t C = p.N / 8;
+  const dim3 grid((unsigned)p.M, (unsigned)((C + 127) / 128)), block(128);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.fmt == RMSQ_FMT_FP8_E4M3FN)
+    hipLaunchKernelGGL(rmsq::rmsq_group_quant_kernel<0>, grid, block, 0, s, A);
+  else
+    hipLaunchKernelGGL(rmsq::rmsq_group_quant_kernel<1>, grid, block, 0, s, A);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return RMSQ_OK;
 }
 
 }  // namespace
@@ -271,11 +322,41 @@ rmsq_status rmsnorm_quant_group(const void* x, const void* residual_in, const vo
   p.out_q = out_q;
   p.out_scale = out_scale;
   p.out_bf16 = out_bf16_or_null;
-  return run(&p, 1, stream);
+  return run(&p, 1, Mode::kFused, stream);
 }
 
 rmsq_status rmsnorm_quant_group_multi(const rmsq_problem* problems, int32_t count, void* stream) {
-  return run(problems, count, stream);
+  return run(problems, count, Mode::kFused, stream);
+}
+
+rmsq_status add_rmsnorm(const void* x, const void* residual_in, const void* gamma, float eps, int64_t M, int64_t N,
+                        void* residual_out, void* out_bf16, void* stream) {
+  rmsq_problem p;
+  std::memset(&p, 0, sizeof p);
+  p.x = x;
+  p.residual_in = residual_in;
+  p.residual_out = residual_out;
+  p.gamma = gamma;
+  p.eps = eps;
+  p.M = M;
+  p.N = N;
+  p.out_bf16 = out_bf16;
+  return run(&p, 1, Mode::kNormOnly, stream);
+}
+
+rmsq_status dynamic_per_group_scaled_quant(const void* x, int64_t M, int64_t N, int32_t group, int32_t fmt,
+                                           int32_t scale_layout, void* out_q, void* out_scale, void* stream) {
+  rmsq_problem p;
+  std::memset(&p, 0, sizeof p);
+  p.x = x;
+  p.M = M;
+  p.N = N;
+  p.group = group;
+  p.fmt = fmt;
+  p.scale_layout = scale_layout;
+  p.out_q = out_q;
+  p.out_scale = out_scale;
+  return run_quant(p, stream);
 }
 
 int32_t rmsq_device_supported(int32_t device) {

@@ -151,7 +151,7 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int sh = (e & 3) * 8;
-      if (tiny | (((qw[e >> 2] ^ qh[e >> 2]) >> sh) & 0xFFu) != 0u) {
+      if (tiny | ((((qw[e >> 2] ^ qh[e >> 2]) >> sh) & 0xFFu) != 0u)) {
         const uint32_t b = fp8_exact(v[e], s);
         qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
       }

@@ -195,6 +195,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
     if (hrow) __builtin_nontemporal_store(xv[j], hrow + c);
     if (ybrow) __builtin_nontemporal_store(yw, ybrow + c);
 
+    if constexpr (FMT == 2) continue;   // norm only: no quantization
     const uint32_t am = amax8(yw);
     float v[8];
 #pragma unroll
@@ -210,7 +211,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
       u32x2* qrow = reinterpret_cast<u32x2*>(P.q + m * (int64_t)P.N);
       __builtin_nontemporal_store(qw, qrow + c);
       if ((tid & 15) == 0) reinterpret_cast<float*>(P.scale)[m * (P.N >> 7) + (c >> 4)] = sc;
-    } else {
+    } else if constexpr (FMT == 1) {
       // MXFP4 e2m1, group 32 = one lane quad
       const uint32_t byte = mx_scale_byte(max4(am));
       const uint32_t w = fp4_codes8(v, byte);
@@ -221,6 +222,53 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
         const int64_t off = P.layout == 0 ? m * gcount + gi : (m >> 5) * (32 * gcount) + gi * 32 + (m & 31);
         reinterpret_cast<uint8_t*>(P.scale)[off] = (uint8_t)byte;
       }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Standalone dynamic per-group quantization of bf16 rows (the separate quant
+// kernel of the unfused chain: [ARQ, kernel count table] lists it as the
+// dynamic per-group scaled quant kernel, [ARQ, Fallback order] as the
+// separate per-1x128 quant). Same group arithmetic as the fused kernel.
+// Grid: x = row, y = block of 64*W chunks of that row, one chunk per lane.
+
+struct QuantArgs {
+  const uint16_t* x;   // bf16 rows
+  int64_t ldx;
+  uint8_t* q;
+  void* scale;
+  int32_t M, N;
+  int32_t layout;
+};
+
+template <int FMT>
+__global__ void __launch_bounds__(256) rmsq_group_quant_kernel(const QuantArgs A) {
+  const int64_t m = blockIdx.x;
+  const int C = A.N >> 3;
+  const int c = (int)blockIdx.y * (int)blockDim.x + (int)threadIdx.x;
+  if (c >= C) return;   // whole groups exit together: C is a multiple of the group's lanes
+  const u32x4 yw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(A.x + m * A.ldx) + c);
+  const uint32_t am = amax8(yw);
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(yw[i]);
+    v[2 * i + 1] = bf16_hi(yw[i]);
+  }
+  if constexpr (FMT == 0) {
+    const float sc = fp8_scale(max16(am));
+    const u32x2 qw = fp8_codes8(v, sc);
+    __builtin_nontemporal_store(qw, reinterpret_cast<u32x2*>(A.q + m * (int64_t)A.N) + c);
+    if ((threadIdx.x & 15) == 0) reinterpret_cast<float*>(A.scale)[m * (A.N >> 7) + (c >> 4)] = sc;
+  } else {
+    const uint32_t byte = mx_scale_byte(max4(am));
+    const uint32_t w = fp4_codes8(v, byte);
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(A.q + m * (int64_t)(A.N >> 1)) + c);
+    if ((threadIdx.x & 3) == 0) {
+      const int64_t gcount = A.N >> 5, gi = c >> 2;
+      const int64_t off = A.layout == 0 ? m * gcount + gi : (m >> 5) * (32 * gcount) + gi * 32 + (m & 31);
+      reinterpret_cast<uint8_t*>(A.scale)[off] = (uint8_t)byte;
     }
   }
 }

@@ -132,6 +132,30 @@ typedef struct rmsq_problem {
  */
 rmsq_status rmsnorm_quant_group_multi(const rmsq_problem* problems, int32_t count, void* stream);
 
+/*
+ * The two kernels the fused call replaces, for callers that need them apart
+ * (the separate-quant fallback of [ARQ, Fallback order]) and for measuring
+ * what the fusion saves. Their composition equals rmsnorm_quant_group bit
+ * for bit.
+ *
+ * add_rmsnorm: [ARQ, kernel count table] "add_rmsnorm_quant_kernel
+ * (RMSNorm+add)": h = bf16(x + residual_in) written to residual_out (both
+ * NULL: h = x), and the bf16 normalized rows to out_bf16 (required). N must
+ * be a multiple of 8 and at most RMSQ_N_MAX; contiguous rows (ld = N).
+ */
+rmsq_status add_rmsnorm(const void* x, const void* residual_in, const void* gamma, float eps,
+                        int64_t M, int64_t N, void* residual_out, void* out_bf16, void* stream);
+
+/*
+ * dynamic_per_group_scaled_quant: [ARQ, kernel count table] "dynamic per
+ * group scaled quant kernel" / [ARQ, Fallback order] the separate per-1x128
+ * quant: per-group dynamic quantization of M contiguous bf16 rows `x` of N
+ * elements, with the group scales, codes and scale layouts of
+ * rmsnorm_quant_group_multi.
+ */
+rmsq_status dynamic_per_group_scaled_quant(const void* x, int64_t M, int64_t N, int32_t group, int32_t fmt,
+                                           int32_t scale_layout, void* out_q, void* out_scale, void* stream);
+
 /* 1 if HIP device `device` is a gfx950 (MI355X-class) GPU, else 0.
  * [ARQ, Motivation]: the single-kernel path is gated to gfx95x devices and
  * callers fall back otherwise; this library's entry points return

@@ -197,3 +197,25 @@ def test_launch_shape_always_fits():
     assert fq.rmsq_query_shape(1536, 8192) == (3, 1)
     with pytest.raises(fq.RmsqError):
         fq.rmsq_query_shape(32776, 1)
+
+
+def test_unfused_entry_points_validate():
+    L = fq.lib()
+    g, r, ro, yb, q, sc = A + 100 * MB, A + 400 * MB, A + 500 * MB, A + 600 * MB, A + 200 * MB, A + 300 * MB
+    # add_rmsnorm(x, residual_in, gamma, eps, M, N, residual_out, out_bf16, stream)
+    assert L.add_rmsnorm(A, None, g, 1e-6, 4, 100, None, yb, None) == fq.RMSQ_ERR_INVALID_ARG   # N % 8
+    assert L.add_rmsnorm(A, None, g, 1e-6, 4, 256, None, None, None) == fq.RMSQ_ERR_INVALID_ARG  # out_bf16 needed
+    assert L.add_rmsnorm(A, r, g, 1e-6, 4, 256, None, yb, None) == fq.RMSQ_ERR_INVALID_ARG      # pairing
+    assert L.add_rmsnorm(A, None, g, float("inf"), 4, 256, None, yb, None) == fq.RMSQ_ERR_INVALID_ARG
+    assert L.add_rmsnorm(A, None, g, 1e-6, 4, 256, None, A + 16, None) == fq.RMSQ_ERR_INVALID_ARG  # overlap
+    assert L.add_rmsnorm(A, None, g, 1e-6, 0, 256, None, None, None) == fq.RMSQ_OK
+    # dynamic_per_group_scaled_quant(x, M, N, group, fmt, layout, out_q, out_scale, stream)
+    assert L.dynamic_per_group_scaled_quant(A, 4, 256, 64, 0, 0, q, sc, None) == fq.RMSQ_ERR_UNSUPPORTED
+    assert L.dynamic_per_group_scaled_quant(A, 4, 256, 128, 0, 1, q, sc, None) == fq.RMSQ_ERR_UNSUPPORTED
+    assert L.dynamic_per_group_scaled_quant(A, 4, 200, 128, 0, 0, q, sc, None) == fq.RMSQ_ERR_INVALID_ARG
+    assert L.dynamic_per_group_scaled_quant(A, 4, 256, 128, 0, 0, None, sc, None) == fq.RMSQ_ERR_INVALID_ARG
+    assert L.dynamic_per_group_scaled_quant(A, 4, 256, 128, 0, 0, A + 64, sc, None) == fq.RMSQ_ERR_INVALID_ARG
+    assert L.dynamic_per_group_scaled_quant(A, 0, 256, 32, 1, 1, None, None, None) == fq.RMSQ_OK
+    if not fq.rmsq_device_supported(0):
+        assert L.add_rmsnorm(A, r, g, 1e-6, 4, 256, ro, yb, None) == fq.RMSQ_ERR_UNSUPPORTED
+        assert L.dynamic_per_group_scaled_quant(A, 4, 256, 32, 1, 1, q, sc, None) == fq.RMSQ_ERR_UNSUPPORTED
