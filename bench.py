@@ -143,8 +143,9 @@ def ceilings(reps=30):
     """Achievable HBM bandwidth on this machine from the no-arithmetic stream
     probes (tests/hip/stream_probe.hip), nontemporal loads and stores like the
     fused kernel, three rotating buffer sets so nothing is served from the
-    Infinity Cache: a plain copy, and a stream with the fused FP8 kernel's
-    exact traffic mix (read 2 x 16 B, write 2 x 16 B + 8 B per 8 elements)."""
+    Infinity Cache: a plain copy, and streams with the fused kernels' exact
+    traffic mixes per 8 elements: FP8 with bf16 side-output (read 2 x 16 B,
+    write 2 x 16 B + 8 B) and MXFP4 (read 2 x 16 B, write 16 B + 4 B)."""
     import torch
     L = _stream_probe()
     st = torch.cuda.current_stream().cuda_stream
@@ -152,7 +153,8 @@ def ceilings(reps=30):
     sets = [[torch.ones(n16 * 16, dtype=torch.uint8, device="cuda") for _ in range(4)] +
             [torch.zeros(n16 * 8, dtype=torch.uint8, device="cuda")] for _ in range(3)]
     out = {}
-    for kind, name, nbytes in ((2, "copy", 2 * n16 * 16), (3, "fused_mix", 4 * n16 * 16 + n16 * 8)):
+    for kind, name, nbytes in ((2, "copy", 2 * n16 * 16), (3, "fused_mix", 4 * n16 * 16 + n16 * 8),
+                               (4, "fused_mix_mxfp4", 3 * n16 * 16 + n16 * 4)):
         def go(i):
             S = sets[i % 3]
             assert L.stream_probe(kind, 1, *[t.data_ptr() for t in S], n16, 16384, 256, st) == 0
@@ -241,6 +243,7 @@ SPECS = {
              dict(M=4096, N=512, residual=False, keep_bf16=False, seed=20, outliers=False)], 0, 0),
     "mxfp4_row": ([dict(M=16384, N=7168, residual=True, keep_bf16=False)], 1, 0),
     "mxfp4_tiled32": ([dict(M=16384, N=7168, residual=True, keep_bf16=False)], 1, 1),
+    "prefill_colscales": ([dict(M=8192, N=7168, residual=True, keep_bf16=True)], 0, 2),
 }
 
 
@@ -345,6 +348,8 @@ def main():
                      "us_per_launch": round(step_ms * 1e3, 2)},
         "stream_ceilings_GBps": ceil,
         "frac_of_mix_ceiling": round(gbps / ceil["fused_mix"], 4) if args.config == "prefill" else None,
+        "mxfp4_frac_of_mix_ceiling": (round(configs["mxfp4_row"]["GBps"] / ceil["fused_mix_mxfp4"], 4)
+                                      if "mxfp4_row" in configs else None),
         "cpu_baseline": cpu,
         "configs": configs,
         "timed_wall_s": round(wall, 3),

@@ -27,12 +27,12 @@ LIB_PATH = os.path.join(HERE, "librmsq.so")
 
 RMSQ_OK, RMSQ_ERR_INVALID_ARG, RMSQ_ERR_UNSUPPORTED, RMSQ_ERR_HIP = 0, 1, 2, 3
 FMT_FP8_E4M3FN, FMT_MXFP4_E2M1 = 0, 1
-SCALE_ROW_MAJOR, SCALE_TILED32 = 0, 1
+SCALE_ROW_MAJOR, SCALE_TILED32, SCALE_COL_MAJOR = 0, 1, 2
 MAX_PROBLEMS = 4
 N_MAX = 32768
 _FMT = {"fp8": FMT_FP8_E4M3FN, "mxfp4": FMT_MXFP4_E2M1}
 _GROUP = {FMT_FP8_E4M3FN: 128, FMT_MXFP4_E2M1: 32}
-_LAYOUT = {"row": SCALE_ROW_MAJOR, "tiled32": SCALE_TILED32}
+_LAYOUT = {"row": SCALE_ROW_MAJOR, "tiled32": SCALE_TILED32, "col": SCALE_COL_MAJOR}
 
 
 class RmsqError(RuntimeError):
@@ -186,12 +186,13 @@ def alloc_outputs(M, N, fmt, scale_layout=SCALE_ROW_MAJOR, keep_bf16=False, devi
     import torch
     q = torch.empty((M, N if fmt == FMT_FP8_E4M3FN else N // 2), dtype=torch.uint8, device=device)
     G = N // _GROUP[fmt]
-    if fmt == FMT_FP8_E4M3FN:
-        scale = torch.empty((M, G), dtype=torch.float32, device=device)
-    elif scale_layout == SCALE_TILED32:
-        scale = torch.empty((((M + 31) // 32) * 32 * G,), dtype=torch.uint8, device=device)
+    dt = torch.float32 if fmt == FMT_FP8_E4M3FN else torch.uint8
+    if scale_layout == SCALE_TILED32:
+        scale = torch.empty((((M + 31) // 32) * 32 * G,), dtype=dt, device=device)
+    elif scale_layout == SCALE_COL_MAJOR:
+        scale = torch.empty((G, M), dtype=dt, device=device)
     else:
-        scale = torch.empty((M, G), dtype=torch.uint8, device=device)
+        scale = torch.empty((M, G), dtype=dt, device=device)
     yb = torch.empty((M, N), dtype=torch.bfloat16, device=device) if keep_bf16 else None
     return q, scale, yb
 

@@ -36,9 +36,11 @@ struct Range {
 size_t scale_bytes(int64_t M, int64_t N, int32_t group, int32_t fmt, int32_t layout) {
   if (M < 0 || N <= 0 || group <= 0 || N % group) return 0;
   const int64_t G = N / group;
-  if (fmt == RMSQ_FMT_FP8_E4M3FN && group == 128 && layout == RMSQ_SCALE_ROW_MAJOR) return (size_t)(M * G * 4);
+  if (fmt == RMSQ_FMT_FP8_E4M3FN && group == 128 &&
+      (layout == RMSQ_SCALE_ROW_MAJOR || layout == RMSQ_SCALE_COL_MAJOR))
+    return (size_t)(M * G * 4);
   if (fmt == RMSQ_FMT_MXFP4_E2M1 && group == 32) {
-    if (layout == RMSQ_SCALE_ROW_MAJOR) return (size_t)(M * G);
+    if (layout == RMSQ_SCALE_ROW_MAJOR || layout == RMSQ_SCALE_COL_MAJOR) return (size_t)(M * G);
     if (layout == RMSQ_SCALE_TILED32) return (size_t)(((M + 31) / 32) * 32 * G);
   }
   return 0;
@@ -60,7 +62,8 @@ rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Mode mod
     if (p.group != group)
       return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: group %d unsupported for fmt %d (need %d)", idx, p.group, p.fmt,
                   group);
-    if (p.scale_layout != RMSQ_SCALE_ROW_MAJOR && p.scale_layout != RMSQ_SCALE_TILED32)
+    if (p.scale_layout != RMSQ_SCALE_ROW_MAJOR && p.scale_layout != RMSQ_SCALE_TILED32 &&
+        p.scale_layout != RMSQ_SCALE_COL_MAJOR)
       return fail(RMSQ_ERR_INVALID_ARG, "problem %d: unknown scale layout %d", idx, p.scale_layout);
     if (p.scale_layout == RMSQ_SCALE_TILED32 && p.fmt != RMSQ_FMT_MXFP4_E2M1)
       return fail(RMSQ_ERR_UNSUPPORTED, "problem %d: the tiled scale layout is for MXFP4 only", idx);
@@ -255,13 +258,13 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
     J = fJ;
     W = fW;
   }
-  // Row grouping per XCD (measured): 16 rows when a problem writes tiled
-  // MXFP4 scales (half a 32-row tile per XCD keeps each tile's scale lines in
-  // few L2s, +1%); plain dispatch order otherwise, which was fastest for
-  // row-major scales.
-  bool tiled = false;
-  for (int i = 0; i < n; ++i) tiled |= L.p[i].layout == RMSQ_SCALE_TILED32;
-  L.row_group = tiled ? 16 : 1;
+  // Row grouping per XCD (measured): 16 rows when a problem writes tiled or
+  // column-major scales (neighbouring rows' scales share lines there; half a
+  // 32-row tile per XCD keeps each line in few L2s, +1% for tiled); plain
+  // dispatch order otherwise, which was fastest for row-major scales.
+  bool grouped = false;
+  for (int i = 0; i < n; ++i) grouped |= L.p[i].layout != RMSQ_SCALE_ROW_MAJOR;
+  L.row_group = grouped ? 16 : 1;
   if (const int fG = g_force_G.load(); fG > 0) L.row_group = fG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mode == Mode::kNormOnly) return launch_fmt<2>(L, J, W, s);

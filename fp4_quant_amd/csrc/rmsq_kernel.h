@@ -46,7 +46,7 @@ struct Problem {
   int64_t ldx, ldr, ldb;  // row strides in elements
   int32_t M, N;
   int32_t row_begin;      // first launch row of this problem
-  int32_t layout;         // MXFP4 scale layout: 0 row-major, 1 32-row tiles
+  int32_t layout;         // scale layout: 0 row-major, 1 32-row tiles (MXFP4), 2 column-major
   float eps;
 };
 
@@ -210,7 +210,10 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
       const u32x2 qw = fp8_codes8(v, sc);
       u32x2* qrow = reinterpret_cast<u32x2*>(P.q + m * (int64_t)P.N);
       __builtin_nontemporal_store(qw, qrow + c);
-      if ((tid & 15) == 0) reinterpret_cast<float*>(P.scale)[m * (P.N >> 7) + (c >> 4)] = sc;
+      if ((tid & 15) == 0) {
+        const int64_t g = c >> 4;
+        reinterpret_cast<float*>(P.scale)[P.layout == 2 ? g * P.M + m : m * (P.N >> 7) + g] = sc;
+      }
     } else if constexpr (FMT == 1) {
       // MXFP4 e2m1, group 32 = one lane quad
       const uint32_t byte = mx_scale_byte(max4(am));
@@ -219,7 +222,9 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
       __builtin_nontemporal_store(w, qrow + c);
       if ((tid & 3) == 0) {
         const int64_t gcount = P.N >> 5, gi = c >> 2;
-        const int64_t off = P.layout == 0 ? m * gcount + gi : (m >> 5) * (32 * gcount) + gi * 32 + (m & 31);
+        const int64_t off = P.layout == 0   ? m * gcount + gi
+                            : P.layout == 1 ? (m >> 5) * (32 * gcount) + gi * 32 + (m & 31)
+                                            : gi * P.M + m;
         reinterpret_cast<uint8_t*>(P.scale)[off] = (uint8_t)byte;
       }
     }
@@ -260,14 +265,19 @@ __global__ void __launch_bounds__(256) rmsq_group_quant_kernel(const QuantArgs A
     const float sc = fp8_scale(max16(am));
     const u32x2 qw = fp8_codes8(v, sc);
     __builtin_nontemporal_store(qw, reinterpret_cast<u32x2*>(A.q + m * (int64_t)A.N) + c);
-    if ((threadIdx.x & 15) == 0) reinterpret_cast<float*>(A.scale)[m * (A.N >> 7) + (c >> 4)] = sc;
+    if ((threadIdx.x & 15) == 0) {
+      const int64_t g = c >> 4;
+      reinterpret_cast<float*>(A.scale)[A.layout == 2 ? g * A.M + m : m * (A.N >> 7) + g] = sc;
+    }
   } else {
     const uint32_t byte = mx_scale_byte(max4(am));
     const uint32_t w = fp4_codes8(v, byte);
     __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(A.q + m * (int64_t)(A.N >> 1)) + c);
     if ((threadIdx.x & 3) == 0) {
       const int64_t gcount = A.N >> 5, gi = c >> 2;
-      const int64_t off = A.layout == 0 ? m * gcount + gi : (m >> 5) * (32 * gcount) + gi * 32 + (m & 31);
+      const int64_t off = A.layout == 0   ? m * gcount + gi
+                          : A.layout == 1 ? (m >> 5) * (32 * gcount) + gi * 32 + (m & 31)
+                                          : gi * A.M + m;
       reinterpret_cast<uint8_t*>(A.scale)[off] = (uint8_t)byte;
     }
   }

@@ -29,8 +29,8 @@
  *  - bf16 tensors are row-major with a row stride (ld, in elements) that is a
  *    multiple of 8 and >= N; bf16 pointers are 16-byte aligned. Codes and
  *    scales are dense: codes [M, N] bytes (FP8) or [M, N/2] (MXFP4); scales
- *    [M, N/128] fp32 (FP8, 4-byte aligned) or e8m0 bytes (MXFP4, see the
- *    layouts below). FP8 code pointers are 8-byte aligned, MXFP4 ones 4-byte.
+ *    fp32 (FP8, 4-byte aligned) or e8m0 bytes (MXFP4), in one of the layouts
+ *    below (row-major [M, N/group] by default). FP8 code pointers are 8-byte aligned, MXFP4 ones 4-byte.
  *  - Outputs must not overlap each other or the inputs, except that
  *    residual_out may be the very same buffer as residual_in (in place).
  *  - Validation happens before any HIP call; a status other than RMSQ_OK
@@ -58,16 +58,24 @@ typedef int32_t rmsq_status;
 #define RMSQ_FMT_FP8_E4M3FN 0  /* group 128, fp32 scales            */
 #define RMSQ_FMT_MXFP4_E2M1 1  /* group 32, e8m0 scales, packed e2m1 */
 
-/* Scale layouts. FP8 scales are always row-major. MXFP4 e8m0 scales are either
- * row-major [M, N/32], or tiled in blocks of 32 rows: byte offset of (m, g) is
- * (m/32)*(32*N/32) + g*32 + m%32, so the 32 rows' scales of one group are
- * adjacent; the buffer holds ceil(M/32)*32*(N/32) bytes and the bytes of the
- * padding rows of the last tile are left untouched. [ATT, review thread]
- * views the byte scales in tiles of the MXFP4 block size in rows when the
- * row count reaches it; [ATF, Technical Details] selects the activation scale
- * layout that the consuming GEMM expects. */
+/* Scale layouts, G = N/group scales per row:
+ *  RMSQ_SCALE_ROW_MAJOR  [M, G] (both formats).
+ *  RMSQ_SCALE_TILED32    MXFP4 only: tiles of 32 rows, byte offset of (m, g)
+ *                        (m/32)*(32*G) + g*32 + m%32, so the 32 rows' scales of
+ *                        one group are adjacent; the buffer holds
+ *                        ceil(M/32)*32*G bytes and the bytes of the padding rows
+ *                        of the last tile are left untouched. [ATT, review
+ *                        thread] views the byte scales in tiles of the MXFP4
+ *                        block size in rows when the row count reaches it.
+ *  RMSQ_SCALE_COL_MAJOR  [G, M] (both formats): one group column's scales for
+ *                        all rows adjacent, the order a GEMM walking K in
+ *                        group-sized blocks reads them.
+ * [ATF, Technical Details] selects the activation scale layout that the
+ * consuming GEMM expects; the consumers' own permutations are not defined on
+ * the pages, so these three are this library's. */
 #define RMSQ_SCALE_ROW_MAJOR 0
 #define RMSQ_SCALE_TILED32 1
+#define RMSQ_SCALE_COL_MAJOR 2
 
 #define RMSQ_MAX_PROBLEMS 4
 #define RMSQ_N_MAX 32768
@@ -179,8 +187,8 @@ void rmsq_set_shape(int32_t J, int32_t W);
 
 /* Measurement hook: force the number of consecutive rows kept together on one
  * XCD (1..64; 1 = plain dispatch order) for later calls in this process;
- * 0 restores the automatic choice (16 when a problem uses the tiled MXFP4
- * scale layout, else 1). Results do not depend on it. */
+ * 0 restores the automatic choice (16 when a problem uses a tiled or
+ * column-major scale layout, else 1). Results do not depend on it. */
 void rmsq_set_row_group(int32_t g);
 
 /* The launch shape the library picks (without an override) for rows of N

@@ -23,6 +23,7 @@ FMT_FP8 = 0
 FMT_MXFP4 = 1
 LAYOUT_ROW = 0
 LAYOUT_TILED32 = 1
+LAYOUT_COL = 2
 
 _p = C.c_void_p
 _i64 = C.c_int64
@@ -130,11 +131,12 @@ def mx_scale_exponent(amax: float) -> int:
 # --------------------------------------------------------------- pipeline --
 def _scale_shape(M, N, group, fmt, layout):
     G = N // group
-    if fmt == FMT_FP8:
-        return (M, G), np.float32
+    dt = np.float32 if fmt == FMT_FP8 else np.uint8
     if layout == LAYOUT_TILED32:
-        return (((M + 31) // 32) * 32 * G,), np.uint8
-    return (M, G), np.uint8
+        return (((M + 31) // 32) * 32 * G,), dt
+    if layout == LAYOUT_COL:
+        return (G, M), dt
+    return (M, G), dt
 
 
 def rmsnorm_quant_group(x, gamma, eps, residual=None, group=128, fmt=FMT_FP8,

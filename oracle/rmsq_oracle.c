@@ -270,6 +270,21 @@ static int64_t tiled32_offset(int64_t m, int64_t g, int64_t groups_per_row)
     return (m / 32) * (32 * groups_per_row) + g * 32 + (m % 32);
 }
 
+/* Scale offset (in scale elements) of (row m, group g) for M rows and G groups
+ * per row: layout 0 row-major [M][G], 1 the 32-row tiles above, 2 column-major
+ * [G][M] (group-major: one group's scales for all rows adjacent, the order a
+ * GEMM walking K in 128-column blocks reads them). READING: [ARQ, Motivation]
+ * hands (fp8, scale) to a block-scaled FP8 GEMM without fixing how it reads
+ * the scales; the column-major option is this library's, not the pages'. */
+static int64_t scale_offset(int64_t m, int64_t g, int64_t M, int64_t G, int32_t layout)
+{
+    if (layout == 1)
+        return tiled32_offset(m, g, G);
+    if (layout == 2)
+        return g * M + m;
+    return m * G + g;
+}
+
 /*
  * One row of bf16 values, groups of `group` consecutive columns.
  * FP8 [FRQ, Motivation] (group 128) / [ARQ, Fallback order] (1x128 groups):
@@ -283,7 +298,7 @@ static int64_t tiled32_offset(int64_t m, int64_t g, int64_t groups_per_row)
  *   group takes e = 0 (byte 127). Two codes per byte, element 2k in the low
  *   nibble (READING).
  */
-static void group_quant_row(const uint16_t* yb, int64_t m, int64_t N,
+static void group_quant_row(const uint16_t* yb, int64_t m, int64_t M, int64_t N,
                             int32_t group, int32_t fmt, int32_t layout,
                             uint8_t* q_row, void* scale)
 {
@@ -298,15 +313,14 @@ static void group_quant_row(const uint16_t* yb, int64_t m, int64_t N,
         }
         if (fmt == 0) {
             float s = amax == 0.0 ? 1.0f : (float)(amax / 448.0);
-            ((float*)scale)[m * groups + g] = s;
+            ((float*)scale)[scale_offset(m, g, M, groups, layout)] = s;
             for (int32_t i = 0; i < group; ++i)
                 q_row[g * group + i] =
                     oracle_e4m3fn_encode(oracle_bf16_to_double(v[i]) / (double)s);
         } else {
             int e = amax == 0.0 ? 0 : oracle_mx_scale_exponent(amax);
             uint8_t byte = (uint8_t)(e + 127);
-            int64_t off = layout == 1 ? tiled32_offset(m, g, groups) : m * groups + g;
-            ((uint8_t*)scale)[off] = byte;
+            ((uint8_t*)scale)[scale_offset(m, g, M, groups, layout)] = byte;
             for (int32_t i = 0; i < group; i += 2) {
                 uint8_t lo = oracle_e2m1_encode(ldexp(oracle_bf16_to_double(v[i]), -e));
                 uint8_t hi = oracle_e2m1_encode(ldexp(oracle_bf16_to_double(v[i + 1]), -e));
@@ -319,9 +333,9 @@ static void group_quant_row(const uint16_t* yb, int64_t m, int64_t N,
 static int shape_ok(int64_t N, int32_t group, int32_t fmt, int32_t layout)
 {
     if (fmt == 0)
-        return group == 128 && N % 128 == 0 && layout == 0;
+        return group == 128 && N % 128 == 0 && (layout == 0 || layout == 2);
     if (fmt == 1)
-        return group == 32 && N % 32 == 0 && (layout == 0 || layout == 1);
+        return group == 32 && N % 32 == 0 && (layout == 0 || layout == 1 || layout == 2);
     return 0;
 }
 
@@ -334,7 +348,7 @@ void oracle_group_quant(const uint16_t* yb, int64_t ldy, int64_t M, int64_t N,
     int64_t qpitch = fmt == 0 ? N : N / 2;
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m)
-        group_quant_row(yb + m * ldy, m, N, group, fmt, scale_layout,
+        group_quant_row(yb + m * ldy, m, M, N, group, fmt, scale_layout,
                         q + m * qpitch, scale);
 }
 
@@ -365,7 +379,7 @@ int oracle_rmsnorm_quant_group(const uint16_t* x, int64_t ldx,
                             residual_out ? residual_out + m * ldr : NULL, ybuf, hbuf);
             if (out_bf16)
                 memcpy(out_bf16 + m * ldb, ybuf, (size_t)N * sizeof(uint16_t));
-            group_quant_row(ybuf, m, N, group, fmt, scale_layout,
+            group_quant_row(ybuf, m, M, N, group, fmt, scale_layout,
                             out_q + m * qpitch, out_scale);
         }
         free(ybuf);

@@ -44,8 +44,9 @@ void oracle_add_rmsnorm(const uint16_t* x, int64_t ldx,
 /* Stage 2: per-group dynamic quantization of bf16 rows.
  * fmt 0 (FP8 e4m3fn, group 128): q [M, N] bytes, scale fp32 [M, N/group].
  * fmt 1 (MXFP4 e2m1, group 32): q [M, N/2] bytes (element 2k in the low
- * nibble), scale e8m0 bytes, layout 0 = row-major [M, N/32], layout 1 =
- * 32-row tiles: byte (m/32)*(32*N/32) + g*32 + m%32. */
+ * nibble), scale e8m0 bytes. Scale layouts: 0 = row-major [M, N/group];
+ * 1 (MXFP4 only) = 32-row tiles: byte (m/32)*(32*N/32) + g*32 + m%32;
+ * 2 = column-major [N/group, M]. */
 void oracle_group_quant(const uint16_t* yb, int64_t ldy, int64_t M, int64_t N,
                         int32_t group, int32_t fmt, int32_t scale_layout,
                         uint8_t* q, void* scale);

@@ -54,6 +54,17 @@ __global__ void k_mix(const u32x4* x, const u32x4* r, u32x4* h, u32x4* yb, u32x2
   }
 }
 
+// The fused MXFP4 kernel's traffic per 8-element chunk: read x and r (16 B
+// each), write h (16 B) and the packed codes (4 B). Grid-stride over chunks.
+__global__ void k_mix_fp4(const u32x4* x, const u32x4* r, u32x4* h, uint32_t* q, int64_t n16) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 a = __builtin_nontemporal_load(x + i), b = __builtin_nontemporal_load(r + i);
+    const u32x4 s = a + b;
+    __builtin_nontemporal_store(s, h + i);
+    __builtin_nontemporal_store(s[0] ^ s[1] ^ s[2] ^ s[3], q + i);
+  }
+}
+
 // Same traffic with the fused kernel's mapping: one workgroup of 64*W lanes
 // per row of C chunks, J chunks per lane (chunk c = j*64*W + lane), all loads
 // of a row issued before any store; SYNC adds the workgroup barrier the norm's
@@ -189,7 +200,8 @@ __global__ void k_empty(int* p) {
 static int st_rc() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 
 extern "C" {
-// kind: 0 read, 1 write, 2 copy, 3 mix; nt: nontemporal hints; blocks/threads: launch shape.
+// kind: 0 read, 1 write, 2 copy, 3 FP8 mix, 4 MXFP4 mix (nontemporal only); nt: nontemporal
+// hints; blocks/threads: launch shape.
 int stream_probe(int kind, int nt, const void* a, void* b, void* c, void* d, void* e, int64_t n16, int blocks,
                  int threads, void* stream) {
   if (n16 <= 0 || blocks <= 0 || threads <= 0 || threads > 1024) return 1;
@@ -204,6 +216,7 @@ int stream_probe(int kind, int nt, const void* a, void* b, void* c, void* d, voi
     case 5: hipLaunchKernelGGL(k_copy<true>, g, t, 0, s, (const u32x4*)a, (u32x4*)b, n16); break;
     case 6: hipLaunchKernelGGL(k_mix<false>, g, t, 0, s, (const u32x4*)a, (const u32x4*)b, (u32x4*)c, (u32x4*)d, (u32x2*)e, n16); break;
     case 7: hipLaunchKernelGGL(k_mix<true>, g, t, 0, s, (const u32x4*)a, (const u32x4*)b, (u32x4*)c, (u32x4*)d, (u32x2*)e, n16); break;
+    case 9: hipLaunchKernelGGL(k_mix_fp4, g, t, 0, s, (const u32x4*)a, (const u32x4*)b, (u32x4*)c, (uint32_t*)e, n16); break;
     default: return 1;
   }
   return st_rc();

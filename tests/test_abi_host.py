@@ -66,6 +66,8 @@ def test_scale_bytes():
     assert fq.rmsq_scale_bytes(0, 7168, 32, 1, 1) == 0
     assert fq.rmsq_scale_bytes(8, 7168, 32, 0, 0) == 0          # FP8 needs group 128
     assert fq.rmsq_scale_bytes(8, 7168, 128, 0, 1) == 0         # tiled is MXFP4 only
+    assert fq.rmsq_scale_bytes(8, 7168, 128, 0, 2) == 8 * 56 * 4
+    assert fq.rmsq_scale_bytes(9, 7168, 32, 1, 2) == 9 * 224
     assert fq.rmsq_scale_bytes(8, 100, 32, 1, 0) == 0
 
 
@@ -138,7 +140,7 @@ def test_valid_call_without_a_gfx950_device_is_unsupported():
     (dict(ldx=128), fq.RMSQ_ERR_INVALID_ARG),                   # stride < N
     (dict(out_bf16=A + 500 * MB, ldb=260), fq.RMSQ_ERR_INVALID_ARG),
     (dict(scale_layout=1), fq.RMSQ_ERR_UNSUPPORTED),            # tiled scales with FP8
-    (dict(scale_layout=2), fq.RMSQ_ERR_INVALID_ARG),
+    (dict(scale_layout=3), fq.RMSQ_ERR_INVALID_ARG),
     (dict(fmt=1, group=32, scale_layout=1, out_q=A + 200 * MB + 4, out_scale=A + 300 * MB + 1),
      fq.RMSQ_ERR_UNSUPPORTED),                                 # valid MXFP4 tiled: no device here
 ])

@@ -97,10 +97,11 @@ def run_gpu(problems, single_entry=False):
             d["residual_out"] = host(ro)
         if yb is not None:
             d["bf16"] = host(yb)
-        if p.get("fmt", 0) == 0 and p["x"].shape[0]:
+        lay = p.get("scale_layout", 0)
+        if p["x"].shape[0] and lay == 0:
             d["scale"] = d["scale"].reshape(p["x"].shape[0], -1)
-        elif p.get("scale_layout", 0) == 0 and p["x"].shape[0]:
-            d["scale"] = d["scale"].reshape(p["x"].shape[0], -1)
+        elif p["x"].shape[0] and lay == 2:
+            d["scale"] = d["scale"].reshape(-1, p["x"].shape[0])
         res.append(d)
     return res
 
@@ -124,6 +125,10 @@ def check(orc, problems, single_entry=False, strict=True):
             owned = np.array([(m // 32) * 32 * G + gi * 32 + m % 32 for m in range(M) for gi in range(G)], np.int64)
             g = dict(g, scale=g["scale"][owned])
             want = dict(want, scale=want["scale"][owned])
+        if p.get("scale_layout", 0) == 2:
+            assert g["scale"].shape == want["scale"].shape
+            g = dict(g, scale=g["scale"].T.copy())
+            want = dict(want, scale=want["scale"].T.copy())
         reps.append(compare(g, want, p.get("fmt", 0), (orc.e4m3fn_table(), orc.e2m1_table()), strict,
                             yb_ref=want["bf16"]))
     return reps
@@ -151,6 +156,16 @@ def test_mxfp4_workload_full_size(orc, layout):
     say(f"workload mxfp4 layout {layout}")
     p = dict(_cfg("mxfp4"), scale_layout=layout)
     check(orc, [p])
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_column_major_scales(orc, fmt):
+    say(f"column-major scales fmt {fmt}")
+    for M in (1, 37, 512):
+        p = inputs.make_problem(M, 7168, seed_x=60 + M, residual=True, outliers=True)
+        check(orc, [dict(p, fmt=fmt, scale_layout=2, keep_bf16=True)])
+    c = _cfg("prefill" if fmt == 0 else "mxfp4")
+    check(orc, [dict(c, scale_layout=2)])
 
 
 def test_mla_two_problems_one_launch_from_one_projection_buffer(orc):

@@ -49,18 +49,17 @@ def test_add_rmsnorm_matches_oracle_stage(orc, name):
         assert np.array_equal(h, wh)
 
 
-@pytest.mark.parametrize("fmt,layout", [(0, 0), (1, 0), (1, 1)])
+@pytest.mark.parametrize("fmt,layout", [(0, 0), (1, 0), (1, 1), (0, 2), (1, 2)])
 def test_group_quant_matches_oracle_stage(orc, fmt, layout):
     say(f"dynamic_per_group_scaled_quant fmt {fmt} layout {layout}")
     c = inputs.make_config("prefill" if fmt == 0 else "mxfp4")
     _, yb = orc.add_rmsnorm(c["x"], c["gamma"], c["eps"], residual=c.get("residual"))
     q, sc = _quant_gpu(yb, fmt, layout)
     wq, wsc = orc.group_quant(yb, 128 if fmt == 0 else 32, fmt, layout, scale_fill=0xA5)
-    if fmt == 0:
-        sc = sc.reshape(wsc.shape)
-    elif layout == 0:
-        sc = sc.reshape(wsc.shape)
+    sc = sc.reshape(wsc.shape)
     assert np.array_equal(sc.view(np.uint8), wsc.view(np.uint8))
+    if layout == 2:
+        sc, wsc = sc.T.copy(), wsc.T.copy()
     compare({"q": q, "scale": sc}, {"q": wq, "scale": wsc}, fmt, (orc.e4m3fn_table(), orc.e2m1_table()),
             strict=True, yb_ref=yb)
 
@@ -90,7 +89,7 @@ def test_group_quant_ragged_and_edge_rows(orc):
     y[2] *= np.float32(1e-36)
     y[3, ::2] = -0.0
     yb = inputs.to_bf16_bits(y)
-    for fmt, layout in ((0, 0), (1, 0), (1, 1)):
+    for fmt, layout in ((0, 0), (1, 0), (1, 1), (0, 2), (1, 2)):
         q, sc = _quant_gpu(yb, fmt, layout)
         wq, wsc = orc.group_quant(yb, 128 if fmt == 0 else 32, fmt, layout, scale_fill=0xA5)
         assert np.array_equal(sc.view(np.uint8).reshape(-1), wsc.view(np.uint8).reshape(-1))

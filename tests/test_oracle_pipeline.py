@@ -241,6 +241,16 @@ def test_tiled32_is_a_permutation_of_row_major(orc):
     assert np.array_equal(til["q"], row["q"])
 
 
+def test_column_major_scales_are_the_transpose(orc):
+    p = inputs.make_problem(37, 640, seed_x=12, residual=True, outliers=True)
+    for fmt, group in ((0, 128), (1, 32)):
+        row = orc.rmsnorm_quant_group(p["x"], p["gamma"], 1e-6, residual=p["residual"], group=group, fmt=fmt)
+        col = orc.rmsnorm_quant_group(p["x"], p["gamma"], 1e-6, residual=p["residual"], group=group, fmt=fmt,
+                                      scale_layout=2)
+        assert col["scale"].shape == (640 // group, 37)
+        assert np.array_equal(col["scale"], row["scale"].T) and np.array_equal(col["q"], row["q"])
+
+
 def test_row_stride_larger_than_n(orc):
     p = inputs.make_problem(5, 256, seed_x=4, residual=True, outliers=True)
     xs = np.zeros((5, 384), np.uint16)
