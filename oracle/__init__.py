@@ -17,8 +17,6 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "liboracle.so")
-_lib = None
-
 FMT_FP8 = 0
 FMT_MXFP4 = 1
 LAYOUT_ROW = 0
@@ -30,105 +28,41 @@ _i64 = C.c_int64
 _i32 = C.c_int32
 
 
-def lib():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            from . import build as _b
-            _b.build()
-        L = C.CDLL(_LIB_PATH)
-        L.oracle_bf16_from_double.restype = C.c_uint16
-        L.oracle_bf16_from_double.argtypes = [C.c_double]
-        L.oracle_bf16_to_double.restype = C.c_double
-        L.oracle_bf16_to_double.argtypes = [C.c_uint16]
-        L.oracle_e4m3fn_encode.restype = C.c_uint8
-        L.oracle_e4m3fn_encode.argtypes = [C.c_double]
-        L.oracle_e4m3fn_decode.restype = C.c_double
-        L.oracle_e4m3fn_decode.argtypes = [C.c_uint8]
-        L.oracle_e2m1_encode.restype = C.c_uint8
-        L.oracle_e2m1_encode.argtypes = [C.c_double]
-        L.oracle_e2m1_decode.restype = C.c_double
-        L.oracle_e2m1_decode.argtypes = [C.c_uint8]
-        L.oracle_mx_scale_exponent.restype = C.c_int
-        L.oracle_mx_scale_exponent.argtypes = [C.c_double]
-        for name in ("oracle_bf16_from_double_n", "oracle_e4m3fn_encode_n", "oracle_e2m1_encode_n"):
-            f = getattr(L, name)
-            f.restype = None
-            f.argtypes = [_p, _p, _i64]
-        L.oracle_add_rmsnorm.restype = None
-        L.oracle_add_rmsnorm.argtypes = [_p, _i64, _p, _i64, _p, C.c_float, _i64, _i64,
-                                         _p, _i64, _p, _i64]
-        L.oracle_group_quant.restype = None
-        L.oracle_group_quant.argtypes = [_p, _i64, _i64, _i64, _i32, _i32, _i32, _p, _p]
-        L.oracle_rmsnorm_quant_group.restype = C.c_int
-        L.oracle_rmsnorm_quant_group.argtypes = [_p, _i64, _p, _i64, _p, C.c_float, _i64, _i64,
-                                                 _i32, _i32, _i32, _p, _p, _p, _p, _i64]
-        L.oracle_num_threads.restype = C.c_int
-        L.oracle_num_threads.argtypes = []
-        _lib = L
-    return _lib
+def _bind(L):
+    L.oracle_bf16_from_double.restype = C.c_uint16
+    L.oracle_bf16_from_double.argtypes = [C.c_double]
+    L.oracle_bf16_to_double.restype = C.c_double
+    L.oracle_bf16_to_double.argtypes = [C.c_uint16]
+    L.oracle_e4m3fn_encode.restype = C.c_uint8
+    L.oracle_e4m3fn_encode.argtypes = [C.c_double]
+    L.oracle_e4m3fn_decode.restype = C.c_double
+    L.oracle_e4m3fn_decode.argtypes = [C.c_uint8]
+    L.oracle_e2m1_encode.restype = C.c_uint8
+    L.oracle_e2m1_encode.argtypes = [C.c_double]
+    L.oracle_e2m1_decode.restype = C.c_double
+    L.oracle_e2m1_decode.argtypes = [C.c_uint8]
+    L.oracle_mx_scale_exponent.restype = C.c_int
+    L.oracle_mx_scale_exponent.argtypes = [C.c_double]
+    for name in ("oracle_bf16_from_double_n", "oracle_e4m3fn_encode_n", "oracle_e2m1_encode_n"):
+        f = getattr(L, name)
+        f.restype = None
+        f.argtypes = [_p, _p, _i64]
+    L.oracle_add_rmsnorm.restype = None
+    L.oracle_add_rmsnorm.argtypes = [_p, _i64, _p, _i64, _p, C.c_float, _i64, _i64, _p, _i64, _p, _i64]
+    L.oracle_group_quant.restype = None
+    L.oracle_group_quant.argtypes = [_p, _i64, _i64, _i64, _i32, _i32, _i32, _p, _p]
+    L.oracle_rmsnorm_quant_group.restype = C.c_int
+    L.oracle_rmsnorm_quant_group.argtypes = [_p, _i64, _p, _i64, _p, C.c_float, _i64, _i64,
+                                             _i32, _i32, _i32, _p, _p, _p, _p, _i64]
+    L.oracle_num_threads.restype = C.c_int
+    L.oracle_num_threads.argtypes = []
+    return L
 
 
 def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def num_threads() -> int:
-    return lib().oracle_num_threads()
-
-
-# ----------------------------------------------------------------- codecs --
-def bf16_from_double(v) -> np.ndarray:
-    v = np.ascontiguousarray(v, dtype=np.float64)
-    out = np.empty(v.shape, np.uint16)
-    lib().oracle_bf16_from_double_n(_ptr(v), _ptr(out), v.size)
-    return out
-
-
-def bf16_to_double(b) -> np.ndarray:
-    """bf16 bit patterns -> float64 (a widening that numpy does exactly)."""
-    b = np.ascontiguousarray(b, dtype=np.uint16)
-    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def e4m3fn_encode(v) -> np.ndarray:
-    v = np.ascontiguousarray(v, dtype=np.float64)
-    out = np.empty(v.shape, np.uint8)
-    lib().oracle_e4m3fn_encode_n(_ptr(v), _ptr(out), v.size)
-    return out
-
-
-def e2m1_encode(v) -> np.ndarray:
-    v = np.ascontiguousarray(v, dtype=np.float64)
-    out = np.empty(v.shape, np.uint8)
-    lib().oracle_e2m1_encode_n(_ptr(v), _ptr(out), v.size)
-    return out
-
-
-E4M3FN_TABLE = None
-E2M1_TABLE = None
-
-
-def e4m3fn_table() -> np.ndarray:
-    """Decoded value of each of the 256 e4m3fn codes (NaN for 0x7F / 0xFF)."""
-    global E4M3FN_TABLE
-    if E4M3FN_TABLE is None:
-        E4M3FN_TABLE = np.array([lib().oracle_e4m3fn_decode(c) for c in range(256)])
-    return E4M3FN_TABLE
-
-
-def e2m1_table() -> np.ndarray:
-    global E2M1_TABLE
-    if E2M1_TABLE is None:
-        E2M1_TABLE = np.array([lib().oracle_e2m1_decode(c) for c in range(16)])
-    return E2M1_TABLE
-
-
-def mx_scale_exponent(amax: float) -> int:
-    return lib().oracle_mx_scale_exponent(float(amax))
-
-
-# --------------------------------------------------------------- pipeline --
 def _scale_shape(M, N, group, fmt, layout):
     G = N // group
     dt = np.float32 if fmt == FMT_FP8 else np.uint8
@@ -139,57 +73,170 @@ def _scale_shape(M, N, group, fmt, layout):
     return (M, G), dt
 
 
-def rmsnorm_quant_group(x, gamma, eps, residual=None, group=128, fmt=FMT_FP8,
-                        scale_layout=LAYOUT_ROW, keep_bf16=False, scale_fill=0):
-    """Fused oracle. x, residual: [M, N] uint16 (bf16 bits), row stride may
-    exceed N; gamma: [N] uint16. Returns a dict with 'q', 'scale' and, when
-    present, 'residual_out' and 'bf16'. Bytes of the tiled scale buffer that
-    no row owns keep ``scale_fill``."""
-    M, N = x.shape
-    assert x.strides[1] == 2 and gamma.dtype == np.uint16
-    ldx = x.strides[0] // 2
-    gamma = np.ascontiguousarray(gamma)
-    q = np.zeros((M, N if fmt == FMT_FP8 else N // 2), np.uint8)
-    sshape, sdt = _scale_shape(M, N, group, fmt, scale_layout)
-    scale = np.full(sshape, scale_fill, sdt)
-    res_out = None
-    ldr = 0
-    if residual is not None:
-        assert residual.shape == (M, N) and residual.strides[1] == 2
-        ldr = residual.strides[0] // 2
-        res_out = np.zeros((M, ldr), np.uint16)[:, :N]   # same row stride as the input
-    yb = np.zeros((M, N), np.uint16) if keep_bf16 else None
-    rc = lib().oracle_rmsnorm_quant_group(
-        _ptr(x), ldx, _ptr(residual), ldr, _ptr(gamma), float(eps), M, N, group, fmt,
-        scale_layout, _ptr(q), _ptr(scale), _ptr(res_out), _ptr(yb), N)
-    if rc != 0:
-        raise ValueError("oracle: arguments outside the defined operation")
-    out = {"q": q, "scale": scale}
-    if res_out is not None:
-        out["residual_out"] = res_out
-    if yb is not None:
-        out["bf16"] = yb
-    return out
+def bf16_to_double(b) -> np.ndarray:
+    """bf16 bit patterns -> float64 (a widening that numpy does exactly)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def add_rmsnorm(x, gamma, eps, residual=None):
-    """Stage 1 alone: returns (h or None, yb)."""
-    M, N = x.shape
-    x = np.ascontiguousarray(x)
-    h = np.zeros((M, N), np.uint16) if residual is not None else None
-    r = np.ascontiguousarray(residual) if residual is not None else None
-    yb = np.zeros((M, N), np.uint16)
-    lib().oracle_add_rmsnorm(_ptr(x), N, _ptr(r), N, _ptr(np.ascontiguousarray(gamma)), float(eps),
-                             M, N, _ptr(h), N, _ptr(yb), N)
-    return h, yb
+class Oracle:
+    """Binding of one build of the oracle library (the default build, or -
+    in the pin tests' mutation check - a copy with a planted mistake)."""
+
+    def __init__(self, path: str):
+        self._L = _bind(C.CDLL(path))
+        self._e4m3 = None
+        self._e2m1 = None
+
+    def lib(self):
+        return self._L
+
+    def num_threads(self) -> int:
+        return self._L.oracle_num_threads()
+
+    # ------------------------------------------------------------- codecs --
+    def bf16_from_double(self, v) -> np.ndarray:
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, np.uint16)
+        self._L.oracle_bf16_from_double_n(_ptr(v), _ptr(out), v.size)
+        return out
+
+    bf16_to_double = staticmethod(bf16_to_double)
+
+    def e4m3fn_encode(self, v) -> np.ndarray:
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, np.uint8)
+        self._L.oracle_e4m3fn_encode_n(_ptr(v), _ptr(out), v.size)
+        return out
+
+    def e2m1_encode(self, v) -> np.ndarray:
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, np.uint8)
+        self._L.oracle_e2m1_encode_n(_ptr(v), _ptr(out), v.size)
+        return out
+
+    def e4m3fn_table(self) -> np.ndarray:
+        """Decoded value of each of the 256 e4m3fn codes (NaN for 0x7F / 0xFF)."""
+        if self._e4m3 is None:
+            self._e4m3 = np.array([self._L.oracle_e4m3fn_decode(c) for c in range(256)])
+        return self._e4m3
+
+    def e2m1_table(self) -> np.ndarray:
+        if self._e2m1 is None:
+            self._e2m1 = np.array([self._L.oracle_e2m1_decode(c) for c in range(16)])
+        return self._e2m1
+
+    def mx_scale_exponent(self, amax: float) -> int:
+        return self._L.oracle_mx_scale_exponent(float(amax))
+
+    # ----------------------------------------------------------- pipeline --
+    def rmsnorm_quant_group(self, x, gamma, eps, residual=None, group=128, fmt=FMT_FP8,
+                            scale_layout=LAYOUT_ROW, keep_bf16=False, scale_fill=0):
+        """Fused oracle. x, residual: [M, N] uint16 (bf16 bits), row stride may
+        exceed N; gamma: [N] uint16. Returns a dict with 'q', 'scale' and, when
+        present, 'residual_out' and 'bf16'. Bytes of the tiled scale buffer that
+        no row owns keep ``scale_fill``."""
+        M, N = x.shape
+        assert x.strides[1] == 2 and gamma.dtype == np.uint16
+        ldx = x.strides[0] // 2
+        gamma = np.ascontiguousarray(gamma)
+        q = np.zeros((M, N if fmt == FMT_FP8 else N // 2), np.uint8)
+        sshape, sdt = _scale_shape(M, N, group, fmt, scale_layout)
+        scale = np.full(sshape, scale_fill, sdt)
+        res_out = None
+        ldr = 0
+        if residual is not None:
+            assert residual.shape == (M, N) and residual.strides[1] == 2
+            ldr = residual.strides[0] // 2
+            res_out = np.zeros((M, ldr), np.uint16)[:, :N]   # same row stride as the input
+        yb = np.zeros((M, N), np.uint16) if keep_bf16 else None
+        rc = self._L.oracle_rmsnorm_quant_group(
+            _ptr(x), ldx, _ptr(residual), ldr, _ptr(gamma), float(eps), M, N, group, fmt,
+            scale_layout, _ptr(q), _ptr(scale), _ptr(res_out), _ptr(yb), N)
+        if rc != 0:
+            raise ValueError("oracle: arguments outside the defined operation")
+        out = {"q": q, "scale": scale}
+        if res_out is not None:
+            out["residual_out"] = res_out
+        if yb is not None:
+            out["bf16"] = yb
+        return out
+
+    def add_rmsnorm(self, x, gamma, eps, residual=None):
+        """Stage 1 alone: returns (h or None, yb)."""
+        M, N = x.shape
+        x = np.ascontiguousarray(x)
+        h = np.zeros((M, N), np.uint16) if residual is not None else None
+        r = np.ascontiguousarray(residual) if residual is not None else None
+        yb = np.zeros((M, N), np.uint16)
+        self._L.oracle_add_rmsnorm(_ptr(x), N, _ptr(r), N, _ptr(np.ascontiguousarray(gamma)), float(eps),
+                                   M, N, _ptr(h), N, _ptr(yb), N)
+        return h, yb
+
+    def group_quant(self, yb, group=128, fmt=FMT_FP8, scale_layout=LAYOUT_ROW, scale_fill=0):
+        """Stage 2 alone on bf16 rows: returns (q, scale)."""
+        yb = np.ascontiguousarray(yb, dtype=np.uint16)
+        M, N = yb.shape
+        q = np.zeros((M, N if fmt == FMT_FP8 else N // 2), np.uint8)
+        sshape, sdt = _scale_shape(M, N, group, fmt, scale_layout)
+        scale = np.full(sshape, scale_fill, sdt)
+        self._L.oracle_group_quant(_ptr(yb), N, M, N, group, fmt, scale_layout, _ptr(q), _ptr(scale))
+        return q, scale
 
 
-def group_quant(yb, group=128, fmt=FMT_FP8, scale_layout=LAYOUT_ROW, scale_fill=0):
-    """Stage 2 alone on bf16 rows: returns (q, scale)."""
-    yb = np.ascontiguousarray(yb, dtype=np.uint16)
-    M, N = yb.shape
-    q = np.zeros((M, N if fmt == FMT_FP8 else N // 2), np.uint8)
-    sshape, sdt = _scale_shape(M, N, group, fmt, scale_layout)
-    scale = np.full(sshape, scale_fill, sdt)
-    lib().oracle_group_quant(_ptr(yb), N, M, N, group, fmt, scale_layout, _ptr(q), _ptr(scale))
-    return q, scale
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        _default = Oracle(_LIB_PATH)
+    return _default
+
+
+# Module-level API: the default build.
+def lib():
+    return default().lib()
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def bf16_from_double(v):
+    return default().bf16_from_double(v)
+
+
+def e4m3fn_encode(v):
+    return default().e4m3fn_encode(v)
+
+
+def e2m1_encode(v):
+    return default().e2m1_encode(v)
+
+
+def e4m3fn_table():
+    return default().e4m3fn_table()
+
+
+def e2m1_table():
+    return default().e2m1_table()
+
+
+def mx_scale_exponent(amax):
+    return default().mx_scale_exponent(amax)
+
+
+def rmsnorm_quant_group(*a, **k):
+    return default().rmsnorm_quant_group(*a, **k)
+
+
+def add_rmsnorm(*a, **k):
+    return default().add_rmsnorm(*a, **k)
+
+
+def group_quant(*a, **k):
+    return default().group_quant(*a, **k)
