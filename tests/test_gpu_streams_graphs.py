@@ -1,0 +1,129 @@
+"""The fused call on non-default streams, from several host threads at once,
+and captured in a HIP graph: every result equals the eager, default-stream
+result bit for bit. (The library allocates nothing and issues no memsets, so
+a captured launch is a single kernel node.)"""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_quant_amd as fq
+from fp4_quant_amd import inputs
+from tests.gpu_util import dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert fq.rmsq_device_supported(0), "GPU tests need a gfx950 device"
+
+
+def _buffers(p, fmt=0):
+    M, N = p["x"].shape
+    x, g, r = dev(p["x"]), dev(p["gamma"]), dev(p["residual"])
+    ro = torch.zeros_like(r)
+    q, sc, yb = fq.alloc_outputs(M, N, fmt, 0, True)
+    for t in (q, sc, yb):
+        t.zero_()
+    prob = fq.make_problem(x, g, p["eps"], q, sc, residual_in=r, residual_out=ro, out_bf16=yb, fmt=fmt)
+    return prob, (x, g, r, ro, q, sc, yb)
+
+
+def _snapshot(bufs):
+    return [host(t).copy() for t in bufs[3:]]
+
+
+def test_non_default_stream_matches_default():
+    say("non-default stream")
+    p = inputs.make_problem(256, 7168, seed_x=71, residual=True, outliers=True)
+    prob, bufs = _buffers(p)
+    fq.rmsnorm_quant_group_multi([prob])
+    torch.cuda.synchronize()
+    want = _snapshot(bufs)
+    for t in bufs[3:]:
+        t.zero_()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fq.rmsnorm_quant_group_multi([prob])          # picks up the current (side) stream
+    s.synchronize()
+    for a, b in zip(_snapshot(bufs), want):
+        assert np.array_equal(a, b)
+
+
+def test_concurrent_host_threads_on_their_own_streams():
+    say("4 host threads, 4 streams")
+    probs = [inputs.make_problem(128, 7168, seed_x=80 + i, residual=True, outliers=True) for i in range(4)]
+    sets = [_buffers(p, fmt=i % 2) for i, p in enumerate(probs)]
+    for prob, _ in sets:
+        fq.rmsnorm_quant_group_multi([prob])
+    torch.cuda.synchronize()
+    want = [_snapshot(b) for _, b in sets]
+    for _, b in sets:
+        for t in b[3:]:
+            t.zero_()
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    fq.rmsnorm_quant_group_multi([sets[i][0]])
+            s.synchronize()
+        except Exception as e:   # reported below
+            errors.append(e)
+
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (_, b), w in zip(sets, want):
+        for a, c in zip(_snapshot(b), w):
+            assert np.array_equal(a, c)
+
+
+def test_graph_capture_and_replay():
+    say("HIP graph capture / replay")
+    pa = inputs.make_problem(512, 7168, seed_x=90, residual=True, outliers=True)
+    pb = inputs.make_problem(512, 7168, seed_x=91, residual=True, outliers=True)
+    prob, bufs = _buffers(pa)
+    x, g, r = bufs[0], bufs[1], bufs[2]
+    xa, ra = x.clone(), r.clone()
+    xb, rb = dev(pb["x"]), dev(pb["residual"])
+
+    def eager(xs, rs):
+        x.copy_(xs)
+        r.copy_(rs)
+        fq.rmsnorm_quant_group_multi([prob])
+        torch.cuda.synchronize()
+        return _snapshot(bufs)
+
+    want_a, want_b = eager(xa, ra), eager(xb, rb)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fq.rmsnorm_quant_group_multi([prob])          # warm-up on the capture stream
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        fq.rmsnorm_quant_group_multi([prob])
+    for k in range(6):
+        xs, rs, want = (xa, ra, want_a) if k % 2 == 0 else (xb, rb, want_b)
+        x.copy_(xs)
+        r.copy_(rs)
+        for t in bufs[3:]:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, c in zip(_snapshot(bufs), want):
+            assert np.array_equal(a, c), f"replay {k}"
+        _ = (x.float() * 2).sum().item()              # eager work between replays
