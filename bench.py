@@ -84,12 +84,14 @@ class Workload:
                 keep += [x, g, r, ro, q, sc, yb]
                 probs.append(fq.make_problem(x, g, p["eps"], q, sc, residual_in=r, residual_out=ro,
                                              out_bf16=yb, fmt=fmt, scale_layout=layout))
-            self.sets.append((probs, keep))
+            self.sets.append((fq.problem_array(probs), keep))
         self.host = host
+        # launches go to torch's current stream, whose handle is taken once
+        self.stream = torch.cuda.current_stream().cuda_stream
 
-    def launch(self, i):
+    def launch(self, i, stream=None):
         import fp4_quant_amd as fq
-        fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0])
+        fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0], stream or self.stream)
 
 
 class UnfusedWorkload(Workload):
@@ -107,8 +109,9 @@ class UnfusedWorkload(Workload):
         probs, keep = self.sets[i % len(self.sets)]
         x, g, r, ro, q, sc, yb = keep[:7]
         M, N = x.shape
-        fq.add_rmsnorm(x, r, g, 1e-6, M, N, ro, yb)
-        fq.dynamic_per_group_scaled_quant(yb, M, N, 128 if self.fmt == 0 else 32, self.fmt, self.layout, q, sc)
+        fq.add_rmsnorm(x, r, g, 1e-6, M, N, ro, yb, self.stream)
+        fq.dynamic_per_group_scaled_quant(yb, M, N, 128 if self.fmt == 0 else 32, self.fmt, self.layout, q, sc,
+                                          self.stream)
 
 
 def time_workload(w, steps, warmup):
@@ -171,6 +174,35 @@ def ceilings(reps=30):
     del sets
     torch.cuda.empty_cache()
     return out
+
+
+def time_workload_graph(w, steps, replays=20):
+    """Per-launch time of `steps` launches captured in one HIP graph and
+    replayed: what a serving loop that captures its decode step sees, with
+    the host's per-call cost out of the way."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(10):
+            w.launch(i, s.cuda_stream)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(steps):
+            w.launch(i, s.cuda_stream)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / (replays * steps)
+    del g
+    return ms
 
 
 def copy_probe(launches):
@@ -299,6 +331,10 @@ def main():
             configs[name] = {"us_per_launch": round(pl * 1e3, 2), "GBps": round(wk.bytes / (pl * 1e-3) / 1e9, 1),
                              "frac_of_peak": round(wk.bytes / (pl * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                              "Mtok_per_s": round(wk.rows / (pl * 1e-3) / 1e6, 2), "bytes": wk.bytes}
+            if wk.bytes < 64 << 20:       # launch-bound sizes: also replayed from a HIP graph
+                pg = time_workload_graph(wk, 100)
+                configs[name]["us_per_launch_graph"] = round(pg * 1e3, 2)
+                configs[name]["GBps_graph"] = round(wk.bytes / (pg * 1e-3) / 1e9, 1)
             del wk
             torch.cuda.empty_cache()
     if not args.no_configs and args.config == "prefill":

@@ -137,11 +137,19 @@ def make_problem(x, gamma, eps, out_q, out_scale, *, residual_in=None, residual_
                         out_bf16=_ptr(out_bf16), ldb=_ld(out_bf16))
 
 
+def problem_array(problems):
+    """A ctypes array of ``rmsq_problem`` to pass to the multi-problem call
+    repeatedly without rebuilding it."""
+    return (rmsq_problem * len(problems))(*problems)
+
+
 def rmsnorm_quant_group_multi(problems, stream=None) -> None:
     """Up to four independent problems (``rmsq_problem`` structs from
-    ``make_problem``) in one kernel launch."""
-    arr = (rmsq_problem * len(problems))(*problems)
-    _check(lib().rmsnorm_quant_group_multi(arr, len(problems), _stream(stream)))
+    ``make_problem``, or an array from ``problem_array``) in one kernel
+    launch. ``stream``: a torch stream, a raw hipStream_t handle, or None for
+    torch's current stream."""
+    arr = problems if isinstance(problems, C.Array) else problem_array(problems)
+    _check(lib().rmsnorm_quant_group_multi(arr, len(arr), _stream(stream)))
 
 
 def add_rmsnorm(x, residual_in, gamma, eps, M, N, residual_out, out_bf16, stream=None) -> None:

@@ -155,18 +155,24 @@ bool device_is_gfx950(int dev) {
 // pays the per-wave fixed cost of the norm (reduction, fp64 inverse square
 // root) too often. Rule: the first J of 2, 3, 4, 1 whose W stays <= 8 with
 // at most 20% idle lanes (7168 -> J 2 x 7 waves, 1536 -> J 3 x 1 wave);
-// then relax the wave limit, then take anything that fits.
+// then relax the wave limit, then take anything that fits. With no more
+// rows than compute units each row has a CU to itself and only its latency
+// counts: there the most waves win (J 1 x 14 waves for 64 rows of 7168:
+// 6.3 us against 6.8 us for J 2 x 7; at 512 rows J 2 x 7 is faster again).
 constexpr int kJs[] = {2, 3, 4, 1, 7, 8, 14};
+constexpr int kJsFewRows[] = {1, 2, 3, 4, 7, 8, 14};
+constexpr int64_t kComputeUnits = 256;
 
 void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
-  (void)rows;
+  const bool few = rows <= kComputeUnits;
   for (int pass = 0; pass < 3; ++pass) {
-    for (int J : kJs) {
+    for (int k = 0; k < 7; ++k) {
+      const int J = few ? kJsFewRows[k] : kJs[k];
       const int64_t W = (C + 64 * J - 1) / (64 * J);
       if (W > rmsq::max_waves(J)) continue;
       const int64_t slots = W * 64 * J;
       if (pass < 2 && (slots - C) * 5 > slots) continue;
-      if (pass == 0 && W > 8) continue;
+      if (pass == 0 && W > (few ? rmsq::kMaxWaves : 8)) continue;
       *J_out = J;
       *W_out = (int)W;
       return;
@@ -176,18 +182,28 @@ void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
   *W_out = rmsq::kMaxWaves;
 }
 
+template <int FMT, bool RES>
+void launch_res(const rmsq::Launch& L, int J, const dim3 grid, const dim3 block, hipStream_t stream) {
+  switch (J) {
+    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES>), grid, block, 0, stream, L); break;
+    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES>), grid, block, 0, stream, L); break;
+    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES>), grid, block, 0, stream, L); break;
+    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES>), grid, block, 0, stream, L); break;
+    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES>), grid, block, 0, stream, L); break;
+    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES>), grid, block, 0, stream, L); break;
+    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES>), grid, block, 0, stream, L); break;
+  }
+}
+
+// One launch of up to four problems; they either all have a residual or
+// none has (the caller splits a mixed set).
 template <int FMT>
 rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, hipStream_t stream) {
   const dim3 grid((unsigned)L.rows), block((unsigned)(64 * W));
-  switch (J) {
-    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14>), grid, block, 0, stream, L); break;
-    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8>), grid, block, 0, stream, L); break;
-    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7>), grid, block, 0, stream, L); break;
-    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4>), grid, block, 0, stream, L); break;
-    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3>), grid, block, 0, stream, L); break;
-    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2>), grid, block, 0, stream, L); break;
-    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1>), grid, block, 0, stream, L); break;
-  }
+  if (L.p[0].r)
+    launch_res<FMT, true>(L, J, grid, block, stream);
+  else
+    launch_res<FMT, false>(L, J, grid, block, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return RMSQ_OK;
@@ -216,59 +232,72 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
   }
   if (const rmsq_status s = check_overlaps(rs, nr); s != RMSQ_OK) return s;
 
-  rmsq::Launch L;
-  std::memset(&L, 0, sizeof L);
-  int64_t rows = 0, Cmax = 0;
-  int n = 0;
-  for (int i = 0; i < count; ++i) {
-    const rmsq_problem& p = ps[i];
-    if (p.M == 0) continue;
-    rmsq::Problem& d = L.p[n++];
-    d.x = static_cast<const uint16_t*>(p.x);
-    d.r = static_cast<const uint16_t*>(p.residual_in);
-    d.h = static_cast<uint16_t*>(p.residual_out);
-    d.gamma = static_cast<const uint16_t*>(p.gamma);
-    d.q = mode == Mode::kNormOnly ? nullptr : static_cast<uint8_t*>(p.out_q);
-    d.scale = mode == Mode::kNormOnly ? nullptr : p.out_scale;
-    d.yb = static_cast<uint16_t*>(p.out_bf16);
-    d.ldx = p.ldx ? p.ldx : p.N;
-    d.ldr = p.ldr ? p.ldr : p.N;
-    d.ldb = p.ldb ? p.ldb : p.N;
-    d.M = (int32_t)p.M;
-    d.N = (int32_t)p.N;
-    d.row_begin = (int32_t)rows;
-    d.layout = p.scale_layout;
-    d.eps = p.eps;
-    rows += p.M;
-    if (p.N / 8 > Cmax) Cmax = p.N / 8;
-  }
-  if (n == 0) return RMSQ_OK;
-  if (rows > INT32_MAX) return fail(RMSQ_ERR_UNSUPPORTED, "total rows %lld exceed the grid limit", (long long)rows);
-  L.count = n;
-  L.rows = (int32_t)rows;
-
+  bool any = false;
+  for (int i = 0; i < count; ++i) any |= ps[i].M > 0;
+  if (!any) return RMSQ_OK;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
     return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");
 
-  int J, W;
-  pick_shape(Cmax, rows, &J, &W);
-  const int fJ = g_force_J.load(), fW = g_force_W.load();
-  if (compiled_J(fJ) && fW > 0 && fW <= rmsq::max_waves(fJ) && (int64_t)fJ * fW * 64 >= Cmax) {
-    J = fJ;
-    W = fW;
+  // One launch for the problems with a residual and one for those without
+  // (a set that mixes the two takes two launches, in that order).
+  for (int with_res = 1; with_res >= 0; --with_res) {
+    rmsq::Launch L;
+    std::memset(&L, 0, sizeof L);
+    int64_t rows = 0, Cmax = 0;
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+      const rmsq_problem& p = ps[i];
+      if (p.M == 0 || (p.residual_in != nullptr) != (with_res == 1)) continue;
+      rmsq::Problem& d = L.p[n++];
+      d.x = static_cast<const uint16_t*>(p.x);
+      d.r = static_cast<const uint16_t*>(p.residual_in);
+      d.h = static_cast<uint16_t*>(p.residual_out);
+      d.gamma = static_cast<const uint16_t*>(p.gamma);
+      d.q = mode == Mode::kNormOnly ? nullptr : static_cast<uint8_t*>(p.out_q);
+      d.scale = mode == Mode::kNormOnly ? nullptr : p.out_scale;
+      d.yb = static_cast<uint16_t*>(p.out_bf16);
+      d.ldx = p.ldx ? p.ldx : p.N;
+      d.ldr = p.ldr ? p.ldr : p.N;
+      d.ldb = p.ldb ? p.ldb : p.N;
+      d.M = (int32_t)p.M;
+      d.N = (int32_t)p.N;
+      d.row_begin = (int32_t)rows;
+      d.layout = p.scale_layout;
+      d.eps = p.eps;
+      rows += p.M;
+      if (p.N / 8 > Cmax) Cmax = p.N / 8;
+    }
+    if (n == 0) continue;
+    if (rows > INT32_MAX) return fail(RMSQ_ERR_UNSUPPORTED, "total rows %lld exceed the grid limit", (long long)rows);
+    L.count = n;
+    L.rows = (int32_t)rows;
+
+    int J, W;
+    pick_shape(Cmax, rows, &J, &W);
+    const int fJ = g_force_J.load(), fW = g_force_W.load();
+    if (compiled_J(fJ) && fW > 0 && fW <= rmsq::max_waves(fJ) && (int64_t)fJ * fW * 64 >= Cmax) {
+      J = fJ;
+      W = fW;
+    }
+    // Row grouping per XCD (measured): 16 rows when a problem writes tiled or
+    // column-major scales (neighbouring rows' scales share lines there; half a
+    // 32-row tile per XCD keeps each line in few L2s, +1% for tiled); plain
+    // dispatch order otherwise, which was fastest for row-major scales.
+    bool grouped = false;
+    for (int i = 0; i < n; ++i) grouped |= L.p[i].layout != RMSQ_SCALE_ROW_MAJOR;
+    L.row_group_log2 = grouped ? 4 : 0;
+    if (const int fG = g_force_G.load(); fG > 0) {
+      L.row_group_log2 = 0;
+      while ((2 << L.row_group_log2) <= fG) ++L.row_group_log2;   // largest power of two <= fG
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const rmsq_status st = mode == Mode::kNormOnly               ? launch_fmt<2>(L, J, W, s)
+                           : ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(L, J, W, s)
+                                                                : launch_fmt<1>(L, J, W, s);
+    if (st != RMSQ_OK) return st;
   }
-  // Row grouping per XCD (measured): 16 rows when a problem writes tiled or
-  // column-major scales (neighbouring rows' scales share lines there; half a
-  // 32-row tile per XCD keeps each line in few L2s, +1% for tiled); plain
-  // dispatch order otherwise, which was fastest for row-major scales.
-  bool grouped = false;
-  for (int i = 0; i < n; ++i) grouped |= L.p[i].layout != RMSQ_SCALE_ROW_MAJOR;
-  L.row_group = grouped ? 16 : 1;
-  if (const int fG = g_force_G.load(); fG > 0) L.row_group = fG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (mode == Mode::kNormOnly) return launch_fmt<2>(L, J, W, s);
-  return ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(L, J, W, s) : launch_fmt<1>(L, J, W, s);
+  return RMSQ_OK;
 }
 
 // The quantization alone on bf16 rows: grid x = row, y = blocks of 128

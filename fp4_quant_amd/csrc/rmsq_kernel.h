@@ -10,6 +10,8 @@
 //
 // Mapping. One workgroup per token row, 64*W threads (W waves, runtime),
 // each lane owning J chunks of 8 bf16 (16 bytes): chunk c = j*64*W + lane.
+// All of a row's loads are issued before any arithmetic; the row then stays
+// in registers across the one reduction, and every output is stored once.
 // Loads and stores are 16-byte and coalesced across the wave. A 128-element
 // FP8 group is 16 consecutive chunks, i.e. one 16-lane DPP row, so its amax
 // is four DPP row rotations; a 32-element MXFP4 group is one lane quad.
@@ -23,10 +25,11 @@
 //    fp32 with fl32(inv) (within 2 ulp of the fp64 product); only when it
 //    lands within 4 ulp of a bf16 rounding midpoint is the element redone as
 //    fp64 (h*g)*inv rounded once to bf16.
-//  * FP8 scale s = amax/448 as an IEEE fp32 division; codes from
-//    p = yb * rcp(s) (within 3 ulp of yb/s) through the hardware convert;
-//    elements whose p is within 8 ulp of an e4m3fn midpoint, in the e4m3fn
-//    subnormal range, or in a group with a tiny scale take the exact path.
+//  * FP8 scale s = fl32(amax/448), correctly rounded; codes through the
+//    hardware convert of yb * r for two reciprocals r bracketing 1/s: where
+//    both brackets give the same code it is the code of yb/s (rounding is
+//    monotone); elsewhere, and in groups with a tiny scale, the exact path
+//    rounds the double quotient.
 //  * MXFP4 scale byte from the bf16 exponent of amax; codes from the exact
 //    product yb * 2^-e through the hardware e2m1 convert.
 #pragma once
@@ -61,24 +64,25 @@ struct Launch {
   Problem p[kMaxProblems];
   int32_t count;
   int32_t rows;           // grid size: one workgroup per row over all problems
-  int32_t row_group;      // rows kept together on one XCD (1 = dispatch order)
+  int32_t row_group_log2; // 2^k consecutive rows kept together on one XCD (0 = dispatch order)
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
-// L2. With row_group = g > 1, every run of g consecutive rows is processed on
-// one XCD (rows of 8*g consecutive workgroups are interleaved at g-row
+// L2. With g = 2^lg > 1, every run of g consecutive rows is processed on one
+// XCD (rows of 8*g consecutive workgroups are interleaved at g-row
 // granularity), so scale bytes of neighbouring rows that share a cache line -
 // a 224-byte scale row, or the 32 rows of a tiled MXFP4 scale block - are
 // written from a single L2 instead of being merged from several. The mapping
 // is a bijection on each block of 8*g rows; a ragged tail keeps dispatch order.
-__device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t g) {
-  const int32_t span = 8 * g;
-  if (g <= 1 || b >= rows / span * span) return b;
+__device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t lg) {
+  if (lg == 0 || b >= (rows >> (lg + 3)) << (lg + 3)) return b;
   const int32_t x = b & 7, k = b >> 3;
-  return ((k / g) * 8 + x) * g + (k % g);
+  return ((((k >> lg) << 3) + x) << lg) + (k & ((1 << lg) - 1));
 }
 
-template <int FMT, int J>
+// RES: every problem of the launch has a residual (otherwise none has), so
+// the loads of x, r and gamma form one straight block with no branch.
+template <int FMT, int J, bool RES>
 __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Launch L) {
   // Short per-lane rows (the usual shapes) keep h as fp32 and fetch gamma
   // together with x and r; long ones keep h packed and fetch gamma late, to
@@ -89,7 +93,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   // Neighbouring row groups run on different XCDs at the same time. (Giving
   // each XCD one contiguous block of M/8 rows instead was measured 12%
   // slower on the prefill workload.)
-  const int32_t row = row_of_block((int32_t)blockIdx.x, L.rows, L.row_group);
+  const int32_t row = row_of_block((int32_t)blockIdx.x, L.rows, L.row_group_log2);
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < kMaxProblems; ++i)
@@ -100,59 +104,60 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   const int T = blockDim.x;
   const int tid = threadIdx.x;
   const int C = P.N >> 3;
-  const bool has_res = P.r != nullptr;
 
-  // ---- loads: x, r and (short rows) gamma, all issued up front ------------
+  // ---- loads: x, gamma (short rows), then r, all issued before any use ---
+  // (of the issue orders measured, this one was fastest on both the
+  // bandwidth-bound and the latency-bound shapes)
+  // A ragged row clamps its chunk index instead of guarding the loads: lanes
+  // past the row end re-read the last chunk (the address of a live lane of
+  // the same instruction, so no extra traffic) and their h is zeroed before
+  // the sum of squares; their stores are skipped.
   const u32x4* xrow = reinterpret_cast<const u32x4*>(P.x + m * P.ldx);
+  const u32x4* rrow = RES ? reinterpret_cast<const u32x4*>(P.r + m * P.ldr) : nullptr;
   const u32x4* grow = reinterpret_cast<const u32x4*>(P.gamma);
-  u32x4 xv[J], gv[kShort ? J : 1];
+  u32x4 xv[J], rv[RES ? J : 1], gv[kShort ? J : 1];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int c = j * T + tid;
-    if (c < C) {
-      xv[j] = __builtin_nontemporal_load(xrow + c);
-      if constexpr (kShort) gv[j] = grow[c];
-    }
+  for (int j = 0; j < J; ++j) xv[j] = __builtin_nontemporal_load(xrow + min(j * T + tid, C - 1));
+  if constexpr (kShort) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) gv[j] = grow[min(j * T + tid, C - 1)];
   }
+  // keep the r loads in place: the scheduler may otherwise interleave them
+  // with x's, or hoist x's unpacking (and the wait for x) above them
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (RES) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) rv[j] = __builtin_nontemporal_load(rrow + min(j * T + tid, C - 1));
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- phase 1: h = x (+ r), write h, sum of squares ---------------------
-  if (has_res) {
-    const u32x4* rrow = reinterpret_cast<const u32x4*>(P.r + m * P.ldr);
-    u32x4 rv[J];
+  // ---- phase 1: h = x + r (stored after the reduction, with the other outputs)
+  if constexpr (RES) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int c = j * T + tid;
-      if (c < C) rv[j] = __builtin_nontemporal_load(rrow + c);
-    }
+      u32x4 s;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = j * T + tid;
-      if (c < C) {
-        u32x4 s;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s[i] = pack_bf16(bf16_lo(xv[j][i]) + bf16_lo(rv[j][i]), bf16_hi(xv[j][i]) + bf16_hi(rv[j][i]));
-        xv[j] = s;   // stored after the reduction, with the other outputs
-      }
+      for (int i = 0; i < 4; ++i)
+        s[i] = pack_bf16(bf16_lo(xv[j][i]) + bf16_lo(rv[j][i]), bf16_hi(xv[j][i]) + bf16_hi(rv[j][i]));
+      xv[j] = s;
     }
   }
-  // xv now holds h (packed bf16)
+  // xv now holds h (packed bf16); sum of squares over the live chunks
   float hf[kShort ? J : 1][8];
   double ss = 0.0;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int c = j * T + tid;
-    if (c < C) {
+    u32x4 hw = xv[j];
+    if (j * T + tid >= C) hw = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = bf16_lo(xv[j][i]), b = bf16_hi(xv[j][i]);
-        if constexpr (kShort) {
-          hf[j][2 * i] = a;
-          hf[j][2 * i + 1] = b;
-        }
-        ss = __builtin_fma((double)a, (double)a, ss);
-        ss = __builtin_fma((double)b, (double)b, ss);
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_lo(hw[i]), b = bf16_hi(hw[i]);
+      if constexpr (kShort) {
+        hf[j][2 * i] = a;
+        hf[j][2 * i + 1] = b;
       }
+      ss = __builtin_fma((double)a, (double)a, ss);
+      ss = __builtin_fma((double)b, (double)b, ss);
     }
   }
   ss = wave_sum(ss);
@@ -172,7 +177,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
 
   // ---- phase 2: normalize, bf16, group scale, codes -----------------------
   u32x4* ybrow = P.yb ? reinterpret_cast<u32x4*>(P.yb + m * P.ldb) : nullptr;
-  u32x4* hrow = has_res ? reinterpret_cast<u32x4*>(P.h + m * P.ldr) : nullptr;
+  u32x4* hrow = RES ? reinterpret_cast<u32x4*>(P.h + m * P.ldr) : nullptr;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = j * T + tid;
@@ -192,7 +197,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
     // All stores of a row go out after its reduction: keeping the residual
     // write next to the others measured 3% faster than writing it as soon as
     // it is formed.
-    if (hrow) __builtin_nontemporal_store(xv[j], hrow + c);
+    if constexpr (RES) __builtin_nontemporal_store(xv[j], hrow + c);
     if (ybrow) __builtin_nontemporal_store(yw, ybrow + c);
 
     if constexpr (FMT == 2) continue;   // norm only: no quantization

@@ -135,8 +135,10 @@ typedef struct rmsq_problem {
  * [FRQ, Modifications] fuses at the attention module and [ATF, Technical
  * Details] fuses as "qknorm quant". Each problem is the operation of
  * rmsnorm_quant_group with its own shapes, strides, residual, side-output
- * and scale layout; all problems use the same fmt. The problem array is read
- * on the host during the call and may be freed when it returns.
+ * and scale layout; all problems use the same fmt. A set in which some
+ * problems have a residual and others do not takes two launches (those
+ * with a residual first), both on `stream`. The problem array is read on the
+ * host during the call and may be freed when it returns.
  */
 rmsq_status rmsnorm_quant_group_multi(const rmsq_problem* problems, int32_t count, void* stream);
 
@@ -186,7 +188,8 @@ const char* rmsq_last_error(void);
 void rmsq_set_shape(int32_t J, int32_t W);
 
 /* Measurement hook: force the number of consecutive rows kept together on one
- * XCD (1..64; 1 = plain dispatch order) for later calls in this process;
+ * XCD (1..64, rounded down to a power of two; 1 = plain dispatch order) for
+ * later calls in this process;
  * 0 restores the automatic choice (16 when a problem uses a tiled or
  * column-major scale layout, else 1). Results do not depend on it. */
 void rmsq_set_row_group(int32_t g);

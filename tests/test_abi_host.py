@@ -174,13 +174,12 @@ def test_set_shape_is_callable():
 def test_row_grouping_is_a_bijection():
     """The device mapping of workgroups to rows (written out here in Python
     from its definition) permutes the rows for every grid size and group."""
-    def row_of_block(b, rows, g):
-        span = 8 * g
-        if g <= 1 or b >= rows // span * span:
+    def row_of_block(b, rows, lg):
+        if lg == 0 or b >= (rows >> (lg + 3)) << (lg + 3):
             return b
         x, k = b & 7, b >> 3
-        return ((k // g) * 8 + x) * g + (k % g)
-    for g in (1, 2, 4, 32, 64):
+        return ((((k >> lg) << 3) + x) << lg) + (k & ((1 << lg) - 1))
+    for g in (0, 1, 2, 4, 5, 6):
         for rows in list(range(1, 700)) + [8192, 8191, 16384, 16383 + 256]:
             assert sorted(row_of_block(b, rows, g) for b in range(rows)) == list(range(rows)), (g, rows)
 
@@ -195,7 +194,8 @@ def test_launch_shape_always_fits():
             assert J in (1, 2, 3, 4, 7, 8, 14) and 1 <= W <= (4 if J >= 7 else 16), (N, rows, J, W)
             assert J * W * 64 >= C_, (N, rows, J, W)
     assert fq.rmsq_query_shape(7168, 8192) == (2, 7)
-    assert fq.rmsq_query_shape(7168, 64) == (2, 7)
+    assert fq.rmsq_query_shape(7168, 512) == (2, 7)
+    assert fq.rmsq_query_shape(7168, 64) == (1, 14)     # one row per CU: most waves
     assert fq.rmsq_query_shape(1536, 8192) == (3, 1)
     with pytest.raises(fq.RmsqError):
         fq.rmsq_query_shape(32776, 1)
