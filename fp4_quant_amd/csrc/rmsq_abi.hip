@@ -162,6 +162,7 @@ bool device_is_gfx950(int dev) {
 constexpr int kJs[] = {2, 3, 4, 1, 7, 8, 14};
 constexpr int kJsFewRows[] = {1, 2, 3, 4, 7, 8, 14};
 constexpr int64_t kComputeUnits = 256;
+constexpr int kWaveRowsPerBlock = 4;
 
 void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
   const bool few = rows <= kComputeUnits;
@@ -183,27 +184,38 @@ void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
 }
 
 template <int FMT, bool RES>
-void launch_res(const rmsq::Launch& L, int J, const dim3 grid, const dim3 block, hipStream_t stream) {
+void launch_res(const rmsq::Launch& L, int J, int R, const dim3 grid, const dim3 block, hipStream_t stream) {
+  if (R > 1) {   // one row per wave, R rows per workgroup (J <= 4 only)
+    switch (J) {
+      case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, true>), grid, block, 0, stream, L); break;
+      case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, true>), grid, block, 0, stream, L); break;
+      case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, true>), grid, block, 0, stream, L); break;
+      default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, true>), grid, block, 0, stream, L); break;
+    }
+    return;
+  }
   switch (J) {
-    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES>), grid, block, 0, stream, L); break;
-    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES>), grid, block, 0, stream, L); break;
-    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES>), grid, block, 0, stream, L); break;
-    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES>), grid, block, 0, stream, L); break;
-    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES>), grid, block, 0, stream, L); break;
-    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES>), grid, block, 0, stream, L); break;
-    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES>), grid, block, 0, stream, L); break;
+    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES, false>), grid, block, 0, stream, L); break;
+    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES, false>), grid, block, 0, stream, L); break;
+    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES, false>), grid, block, 0, stream, L); break;
+    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, false>), grid, block, 0, stream, L); break;
+    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, false>), grid, block, 0, stream, L); break;
+    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, false>), grid, block, 0, stream, L); break;
+    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, false>), grid, block, 0, stream, L); break;
   }
 }
 
 // One launch of up to four problems; they either all have a residual or
-// none has (the caller splits a mixed set).
+// none has (the caller splits a mixed set). R > 1: W is 1 and R rows share a
+// workgroup, one per wave.
 template <int FMT>
-rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, hipStream_t stream) {
-  const dim3 grid((unsigned)L.rows), block((unsigned)(64 * W));
+rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, int R, hipStream_t stream) {
+  const dim3 grid(R > 1 ? (unsigned)((L.rows + R - 1) / R) : (unsigned)L.rows);
+  const dim3 block((unsigned)(64 * (R > 1 ? R : W)));
   if (L.p[0].r)
-    launch_res<FMT, true>(L, J, grid, block, stream);
+    launch_res<FMT, true>(L, J, R, grid, block, stream);
   else
-    launch_res<FMT, false>(L, J, grid, block, stream);
+    launch_res<FMT, false>(L, J, R, grid, block, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return RMSQ_OK;
@@ -211,7 +223,7 @@ rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, hipStream_t stream) 
 
 // Launch-shape override for measurement sweeps, set by rmsq_set_shape
 // (0, 0 = automatic choice).
-std::atomic<int> g_force_J{0}, g_force_W{0}, g_force_G{0};
+std::atomic<int> g_force_J{0}, g_force_W{0}, g_force_G{0}, g_force_R{0};
 
 bool compiled_J(int J) {
   for (int k : kJs)
@@ -286,15 +298,27 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
     // dispatch order otherwise, which was fastest for row-major scales.
     bool grouped = false;
     for (int i = 0; i < n; ++i) grouped |= L.p[i].layout != RMSQ_SCALE_ROW_MAJOR;
-    L.row_group_log2 = grouped ? 4 : 0;
+    int lg = grouped ? 4 : 0;
     if (const int fG = g_force_G.load(); fG > 0) {
-      L.row_group_log2 = 0;
-      while ((2 << L.row_group_log2) <= fG) ++L.row_group_log2;   // largest power of two <= fG
+      lg = 0;
+      while ((2 << lg) <= fG) ++lg;   // largest power of two <= fG
     }
+    // Rows that fit one wave are packed several per workgroup once there are
+    // enough of them to fill the machine (a CU holds only so many
+    // workgroups, so one-wave workgroups leave wave slots empty).
+    int R = 1;
+    if (W == 1 && J <= 4) {
+      const int fR = g_force_R.load();
+      R = fR > 0 ? fR : (rows >= 4 * kComputeUnits ? kWaveRowsPerBlock : 1);
+      if (R > rmsq::kMaxWaves) R = rmsq::kMaxWaves;
+    }
+    int lgR = 0;
+    while ((2 << lgR) <= R) ++lgR;
+    L.row_group_log2 = R > 1 ? (lg > lgR ? lg - lgR : 0) : lg;   // groups of workgroups when packed
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const rmsq_status st = mode == Mode::kNormOnly               ? launch_fmt<2>(L, J, W, s)
-                           : ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(L, J, W, s)
-                                                                : launch_fmt<1>(L, J, W, s);
+    const rmsq_status st = mode == Mode::kNormOnly               ? launch_fmt<2>(L, J, W, R, s)
+                           : ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(L, J, W, R, s)
+                                                                : launch_fmt<1>(L, J, W, R, s);
     if (st != RMSQ_OK) return st;
   }
   return RMSQ_OK;
@@ -419,6 +443,8 @@ void rmsq_set_shape(int32_t J, int32_t W) {
 }
 
 void rmsq_set_row_group(int32_t g) { g_force_G.store(g > 0 && g <= 64 ? g : 0); }
+
+void rmsq_set_wave_rows(int32_t R) { g_force_R.store(R > 0 && R <= rmsq::kMaxWaves ? R : 0); }
 
 int32_t rmsq_query_shape(int64_t N, int64_t rows, int32_t* J, int32_t* W) {
   if (N <= 0 || N % 8 || N > RMSQ_N_MAX || rows < 0 || !J || !W) return RMSQ_ERR_INVALID_ARG;

@@ -1,7 +1,7 @@
 // rmsq_device.h - device-side number formats and cross-lane helpers for gfx950.
 //
 // Conversions go through the CDNA4 hardware convert instructions
-// (v_cvt_pk_bf16_f32, v_cvt_pk_fp8_f32, v_cvt_scalef32_pk_fp4_f32), all
+// (v_cvt_pk_bf16_f32, v_cvt_pk_fp8_f32, v_cvt_scalef32_pk_fp4_bf16), all
 // round-to-nearest-even. Where an fp32 intermediate could double-round, the
 // value is first rounded to odd in fp32 (f64_to_f32_odd): rounding to odd
 // with at least two extra bits and then to nearest even equals a single
@@ -54,11 +54,17 @@ __device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI_WORD);
 }
 
-// Two fp32 -> two e2m1 nibbles (a low, b high) in byte `sel` of `old`, nearest
-// even with saturation at 6 (v_cvt_scalef32_pk_fp4_f32 with scale 1).
+// A packed pair of bf16 (low half = even element) -> two e2m1 nibbles (even
+// element low) in byte SEL of `old`: v_cvt_scalef32_pk_fp4_bf16, which
+// divides by 2^k, k taken from the exponent field of the fp32 scale operand
+// (scale bits = e8m0 byte << 23, byte 0 meaning 2^-127), then rounds to
+// nearest even and saturates at 6. Checked on the GPU for every e8m0 byte
+// and every bf16 value up to twice the largest magnitude a group with that
+// byte holds.
 template <int SEL>
-__device__ __forceinline__ uint32_t cvt_fp4x2(float a, float b, uint32_t old) {
-  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+__device__ __forceinline__ uint32_t cvt_fp4x2_bf16(uint32_t pair, uint32_t byte, uint32_t old) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(bf16x2, pair), __uint_as_float(byte << 23),
+                                                  SEL);
 }
 
 // e4m3fn byte of the exact quotient v / s for the rare cases the fast path
@@ -79,20 +85,28 @@ __device__ __forceinline__ bool near_bf16_midpoint(float y) {
   return ((__float_as_uint(y) & 0xFFFFu) - 0x7FFCu) <= 8u;
 }
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
 // bf16(hg * inv) for 8 elements, hg = h * gamma (exact in fp32), inv the fp64
 // inverse norm and inv32 = fl32(inv). The fp32 product is within 2 ulp of the
 // fp64 one, so its bf16 rounding is final unless it lies within 4 ulp of a
 // bf16 midpoint; those elements (all of them when row_exact) are redone from
-// the fp64 product with a single rounding.
+// the fp64 product with a single rounding. The window test runs on packed
+// 16-bit lanes: the low halves of two products side by side (v_perm_b32),
+// plus 0x8004 modulo 2^16, fall in [0, 8] exactly for the products whose
+// low 16 bits lie in [0x7FFC, 0x8004]; the minimum over the 8 elements
+// decides whether any of them needs the fp64 path.
 __device__ __forceinline__ u32x4 norm_bf16x8(const float hg[8], float inv32, double inv, bool row_exact) {
   u32x4 yw;
-  bool need = row_exact;
+  u16x2 lo_min = {0xFFFFu, 0xFFFFu};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float y0 = hg[2 * i] * inv32, y1 = hg[2 * i + 1] * inv32;
-    need |= near_bf16_midpoint(y0) | near_bf16_midpoint(y1);   // bitwise: no branches
+    const uint32_t lows = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x05040100u);
+    lo_min = __builtin_elementwise_min(lo_min, __builtin_bit_cast(u16x2, lows) + u16x2{0x8004u, 0x8004u});
     yw[i] = pack_bf16(y0, y1);
   }
+  const bool need = row_exact | (min((uint32_t)lo_min[0], (uint32_t)lo_min[1]) <= 8u);
   if (need) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -169,15 +183,14 @@ __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
   return amax_bits == 0 ? 127u : (E >= 2u ? E - 2u : 0u);
 }
 
-// e2m1 codes of v[e] * 2^-(byte-127) for 8 values, packed two per byte with
-// the even element in the low nibble. byte <= 252 (bf16 exponents stop at
-// 254), so 2^-e = 2^(127-byte) is a normal fp32 and every product is exact.
-__device__ __forceinline__ uint32_t fp4_codes8(const float v[8], uint32_t byte) {
-  const float f = __uint_as_float((254u - byte) << 23);
-  uint32_t w = cvt_fp4x2<0>(v[0] * f, v[1] * f, 0u);
-  w = cvt_fp4x2<1>(v[2] * f, v[3] * f, w);
-  w = cvt_fp4x2<2>(v[4] * f, v[5] * f, w);
-  w = cvt_fp4x2<3>(v[6] * f, v[7] * f, w);
+// e2m1 codes of yb[e] / 2^(byte-127) for 8 bf16 values packed two per dword
+// (the division by a power of two is exact), packed two per byte with the
+// even element in the low nibble.
+__device__ __forceinline__ uint32_t fp4_codes8(const u32x4 yw, uint32_t byte) {
+  uint32_t w = cvt_fp4x2_bf16<0>(yw[0], byte, 0u);
+  w = cvt_fp4x2_bf16<1>(yw[1], byte, w);
+  w = cvt_fp4x2_bf16<2>(yw[2], byte, w);
+  w = cvt_fp4x2_bf16<3>(yw[3], byte, w);
   return w;
 }
 
@@ -236,8 +249,6 @@ __device__ __forceinline__ double wave_sum(double v) {
   v += dpp_f64<0x121>(v);
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
-
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Largest |value| of eight packed bf16 (four dwords), as a bf16 magnitude
 // pattern: integer max of (bits & 0x7FFF) orders bf16 magnitudes exactly.

@@ -30,8 +30,9 @@
 //    both brackets give the same code it is the code of yb/s (rounding is
 //    monotone); elsewhere, and in groups with a tiny scale, the exact path
 //    rounds the double quotient.
-//  * MXFP4 scale byte from the bf16 exponent of amax; codes from the exact
-//    product yb * 2^-e through the hardware e2m1 convert.
+//  * MXFP4 scale byte from the bf16 exponent of amax; codes through the
+//    hardware scaled convert straight from the packed bf16 (exact division
+//    by 2^e, then e2m1 rounding).
 #pragma once
 
 #include "rmsq_device.h"
@@ -82,7 +83,10 @@ __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t
 
 // RES: every problem of the launch has a residual (otherwise none has), so
 // the loads of x, r and gamma form one straight block with no branch.
-template <int FMT, int J, bool RES>
+// WAVE_ROWS: rows short enough for one wave (J*64 chunks) are packed one per
+// wave, blockDim/64 consecutive rows per workgroup, with no LDS and no
+// barrier; otherwise the workgroup's waves share one row.
+template <int FMT, int J, bool RES, bool WAVE_ROWS>
 __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Launch L) {
   // Short per-lane rows (the usual shapes) keep h as fp32 and fetch gamma
   // together with x and r; long ones keep h packed and fetch gamma late, to
@@ -93,7 +97,14 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   // Neighbouring row groups run on different XCDs at the same time. (Giving
   // each XCD one contiguous block of M/8 rows instead was measured 12%
   // slower on the prefill workload.)
-  const int32_t row = row_of_block((int32_t)blockIdx.x, L.rows, L.row_group_log2);
+  int32_t row;
+  if constexpr (WAVE_ROWS) {
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+    row = row_of_block((int32_t)blockIdx.x, (int32_t)gridDim.x, L.row_group_log2) * (int32_t)(blockDim.x >> 6) + wave;
+    if (row >= L.rows) return;   // the whole wave leaves: nothing below synchronizes
+  } else {
+    row = row_of_block((int32_t)blockIdx.x, L.rows, L.row_group_log2);
+  }
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < kMaxProblems; ++i)
@@ -101,8 +112,8 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   const Problem& P = L.p[pi];
 
   const int64_t m = row - P.row_begin;
-  const int T = blockDim.x;
-  const int tid = threadIdx.x;
+  const int T = WAVE_ROWS ? 64 : blockDim.x;
+  const int tid = WAVE_ROWS ? (threadIdx.x & 63) : threadIdx.x;
   const int C = P.N >> 3;
 
   // ---- loads: x, gamma (short rows), then r, all issued before any use ---
@@ -162,7 +173,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   }
   ss = wave_sum(ss);
   const int nw = T >> 6;
-  if (nw > 1) {
+  if (!WAVE_ROWS && nw > 1) {
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     ss = 0.0;
@@ -202,15 +213,15 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
 
     if constexpr (FMT == 2) continue;   // norm only: no quantization
     const uint32_t am = amax8(yw);
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(yw[i]);
-      v[2 * i + 1] = bf16_hi(yw[i]);
-    }
 
     if constexpr (FMT == 0) {
       // FP8 e4m3fn, group 128 = one 16-lane DPP row
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_lo(yw[i]);
+        v[2 * i + 1] = bf16_hi(yw[i]);
+      }
       const float sc = fp8_scale(max16(am));
       const u32x2 qw = fp8_codes8(v, sc);
       u32x2* qrow = reinterpret_cast<u32x2*>(P.q + m * (int64_t)P.N);
@@ -222,7 +233,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
     } else if constexpr (FMT == 1) {
       // MXFP4 e2m1, group 32 = one lane quad
       const uint32_t byte = mx_scale_byte(max4(am));
-      const uint32_t w = fp4_codes8(v, byte);
+      const uint32_t w = fp4_codes8(yw, byte);
       uint32_t* qrow = reinterpret_cast<uint32_t*>(P.q + m * (int64_t)(P.N >> 1));
       __builtin_nontemporal_store(w, qrow + c);
       if ((tid & 3) == 0) {
@@ -260,13 +271,13 @@ __global__ void __launch_bounds__(256) rmsq_group_quant_kernel(const QuantArgs A
   if (c >= C) return;   // whole groups exit together: C is a multiple of the group's lanes
   const u32x4 yw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(A.x + m * A.ldx) + c);
   const uint32_t am = amax8(yw);
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_lo(yw[i]);
-    v[2 * i + 1] = bf16_hi(yw[i]);
-  }
   if constexpr (FMT == 0) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(yw[i]);
+      v[2 * i + 1] = bf16_hi(yw[i]);
+    }
     const float sc = fp8_scale(max16(am));
     const u32x2 qw = fp8_codes8(v, sc);
     __builtin_nontemporal_store(qw, reinterpret_cast<u32x2*>(A.q + m * (int64_t)A.N) + c);
@@ -276,7 +287,7 @@ __global__ void __launch_bounds__(256) rmsq_group_quant_kernel(const QuantArgs A
     }
   } else {
     const uint32_t byte = mx_scale_byte(max4(am));
-    const uint32_t w = fp4_codes8(v, byte);
+    const uint32_t w = fp4_codes8(yw, byte);
     __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(A.q + m * (int64_t)(A.N >> 1)) + c);
     if ((threadIdx.x & 3) == 0) {
       const int64_t gcount = A.N >> 5, gi = c >> 2;

@@ -194,6 +194,13 @@ void rmsq_set_shape(int32_t J, int32_t W);
  * column-major scale layout, else 1). Results do not depend on it. */
 void rmsq_set_row_group(int32_t g);
 
+/* Measurement hook: rows that one wave covers (a shape with W = 1) are packed
+ * R per workgroup, one per wave, for later calls in this process: R in
+ * 2..16, or 1 for one row per workgroup; 0 restores the automatic choice
+ * (R = 4 once a launch has at least 1024 rows, else 1). Results do not
+ * depend on it. */
+void rmsq_set_wave_rows(int32_t R);
+
 /* The launch shape the library picks (without an override) for rows of N
  * elements, the widest problem of a call, and `rows` rows in total: J chunks
  * of 8 elements per lane and W waves per workgroup (one workgroup per row).

@@ -39,11 +39,11 @@ __global__ void k_mx_byte(const uint16_t* amax, uint8_t* out, int64_t n) {
   GRID_LOOP(i, n) out[i] = (uint8_t)mx_scale_byte(amax[i]);
 }
 
-__global__ void k_fp4_codes(const float* v, const uint8_t* byte, uint32_t* out, int64_t n) {
+__global__ void k_fp4_codes(const uint16_t* v, const uint8_t* byte, uint32_t* out, int64_t n) {
   GRID_LOOP(k, n) {
-    float x[8];
-    for (int e = 0; e < 8; ++e) x[e] = v[8 * k + e];
-    out[k] = fp4_codes8(x, byte[k]);
+    u32x4 w;
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)v[8 * k + 2 * i] | ((uint32_t)v[8 * k + 2 * i + 1] << 16);
+    out[k] = fp4_codes8(w, byte[k]);
   }
 }
 
@@ -64,10 +64,11 @@ __global__ void k_cvt_fp8(const float* in, uint8_t* out, int64_t n) {  // n pair
 __global__ void k_cvt_fp4(const float* in, uint8_t* out, int64_t n) {  // n groups of 8
   GRID_LOOP(k, n) {
     const float* a = in + 8 * k;
-    uint32_t w = cvt_fp4x2<0>(a[0], a[1], 0u);
-    w = cvt_fp4x2<1>(a[2], a[3], w);
-    w = cvt_fp4x2<2>(a[4], a[5], w);
-    w = cvt_fp4x2<3>(a[6], a[7], w);
+    // the plain (fp32-input) hardware convert with scale 1
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a[0], a[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[2], a[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[4], a[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[6], a[7], 1.0f, 3);
     for (int b = 0; b < 4; ++b) out[4 * k + b] = (uint8_t)(w >> (8 * b));
   }
 }
@@ -82,6 +83,27 @@ __global__ void k_fp8_exact(const float* v, const float* s, uint8_t* out, int64_
 
 __global__ void k_rcp(const float* s, float* out, int64_t n) {
   GRID_LOOP(i, n) out[i] = __builtin_amdgcn_rcpf(s[i]);
+}
+
+// Raw scaled converts of packed bf16 pairs (v_cvt_scalef32_pk_fp4_bf16 /
+// v_cvt_scalef32_pk_fp8_bf16) with a per-pair fp32 scale operand: the tests
+// pin down how the scale operand enters the result.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+
+__global__ void k_cvt_fp4_bf16_scaled(const uint32_t* pairs, const float* scale, uint8_t* out, int64_t n) {
+  GRID_LOOP(k, n) {
+    const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2_t, pairs[k]), scale[k], 0);
+    out[k] = (uint8_t)w;
+  }
+}
+
+__global__ void k_cvt_fp8_bf16_scaled(const uint32_t* pairs, const float* scale, uint16_t* out, int64_t n) {
+  GRID_LOOP(k, n) {
+    const s16x2_t w = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2_t{0, 0}, __builtin_bit_cast(bf16x2_t, pairs[k]),
+                                                               scale[k], false);
+    out[k] = (uint16_t)w[0];
+  }
 }
 
 static int launch_status() { return hipGetLastError() == hipSuccess ? 0 : 3; }
@@ -109,7 +131,7 @@ int probe_mx_byte(const uint16_t* a, uint8_t* out, int64_t n, void* stream) {
   hipLaunchKernelGGL(k_mx_byte, GRID(n), a, out, n);
   return launch_status();
 }
-int probe_fp4_codes(const float* v, const uint8_t* b, uint32_t* out, int64_t n, void* stream) {
+int probe_fp4_codes(const uint16_t* v, const uint8_t* b, uint32_t* out, int64_t n, void* stream) {
   if (n <= 0) return 0;
   hipLaunchKernelGGL(k_fp4_codes, GRID(n), v, b, out, n);
   return launch_status();
@@ -137,6 +159,16 @@ int probe_f64_to_bf16(const double* in, uint16_t* out, int64_t n, void* stream) 
 int probe_rcp(const float* s, float* out, int64_t n, void* stream) {
   if (n <= 0) return 0;
   hipLaunchKernelGGL(k_rcp, GRID(n), s, out, n);
+  return launch_status();
+}
+int probe_cvt_fp4_bf16_scaled(const uint32_t* pairs, const float* scale, uint8_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_cvt_fp4_bf16_scaled, GRID(n), pairs, scale, out, n);
+  return launch_status();
+}
+int probe_cvt_fp8_bf16_scaled(const uint32_t* pairs, const float* scale, uint16_t* out, int64_t n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_cvt_fp8_bf16_scaled, GRID(n), pairs, scale, out, n);
   return launch_status();
 }
 int probe_fp8_exact(const float* v, const float* s, uint8_t* out, int64_t n, void* stream) {

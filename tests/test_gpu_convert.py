@@ -85,6 +85,32 @@ def test_hw_fp4_convert_matches_oracle(orc):
     assert np.array_equal(got[nz], want[nz])                      # and as codes when nonzero
 
 
+def test_hw_fp4_scaled_bf16_convert_every_scale_byte(orc):
+    """v_cvt_scalef32_pk_fp4_bf16 with scale bits byte << 23 gives the e2m1
+    code of v / 2^(byte - 127) (nearest even, saturating at 6), for every e8m0
+    byte 0..254 and every finite bf16 v below 2^(byte - 127 + 4), i.e. up to
+    twice the largest magnitude a group with that scale byte holds. Both
+    nibbles of the pair are checked."""
+    say("raw v_cvt_scalef32_pk_fp4_bf16, every scale byte")
+    tab = orc.e2m1_table()
+    vals = bf16_f64(FIN16)
+    pairs, scales, want, owner = [], [], [], []
+    for byte in range(255):
+        e = byte - 127
+        sel = np.abs(vals) < 2.0 ** (e + 4)
+        b = FIN16[sel].astype(np.uint32)
+        pairs.append(b | (b << 16))
+        scales.append(np.full(b.size, np.uint32(byte << 23)).view(np.float32))
+        want.append(orc.e2m1_encode(np.ldexp(vals[sel], -e)))
+        owner.append(np.full(b.size, byte))
+    p, sc, w, ow = (np.concatenate(a) for a in (pairs, scales, want, owner))
+    out = torch.empty(p.size, dtype=torch.uint8, device="cuda")
+    call_probe("probe_cvt_fp4_bf16_scaled", dev(p.view(np.int32)), dev(sc), out, n=p.size)
+    o = host(out)
+    bad = (tab[o & 0xF] != tab[w]) | (tab[o >> 4] != tab[w])
+    assert not bad.any(), f"{bad.sum()} of {p.size} differ, first at scale byte {ow[bad][0]}"
+
+
 def test_f64_to_bf16_single_rounding(orc):
     say("bf16_from_f64")
     rng = np.random.default_rng(4)
@@ -189,7 +215,7 @@ def test_fp4_codes8_every_value_below_amax(orc):
         e = 0 if amax == 0 else orc.mx_scale_exponent(bf16_f64(np.uint16([amax]))[0])
         byte = np.full(vals.size // 8, e + 127, np.uint8)
         out = torch.empty(vals.size // 8, dtype=torch.int32, device="cuda")
-        call_probe("probe_fp4_codes", dev(_f32(vals)), dev(byte), out, n=vals.size // 8)
+        call_probe("probe_fp4_codes", dev(vals), dev(byte), out, n=vals.size // 8)
         w = host(out).view(np.uint32)
         got = np.stack([(w >> (4 * i)) & 0xF for i in range(8)], -1).reshape(-1)
         want = orc.e2m1_encode(np.ldexp(bf16_f64(vals), -e))
@@ -276,7 +302,7 @@ def test_fp4_codes8_every_value_amax_pair(orc):
         ex = np.array([orc.mx_scale_exponent(a) for a in bf16_f64(amaxes)], np.int64)
         byte = (ex + 127).astype(np.uint8)[owner]
         out = torch.empty(v.size // 8, dtype=torch.int32, device="cuda")
-        call_probe("probe_fp4_codes", dev(_f32(v)), dev(byte), out, n=v.size // 8)
+        call_probe("probe_fp4_codes", dev(v), dev(byte), out, n=v.size // 8)
         w = host(out).view(np.uint32)
         got = np.stack([(w >> (4 * i)) & 0xF for i in range(8)], -1).reshape(-1)
         q = np.ldexp(bf16_f64(v), -np.repeat(ex[owner], 8))

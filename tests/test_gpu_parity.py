@@ -223,6 +223,28 @@ def test_every_launch_shape_gives_the_same_result(orc, N):
         fq.rmsq_set_shape(0, 0)
 
 
+@pytest.mark.parametrize("R", [2, 3, 4, 8, 16])
+def test_rows_packed_one_per_wave(orc, R):
+    """Short rows packed R per workgroup (one per wave): ragged row counts,
+    both formats, every scale layout, with and without residual, two problems
+    of different widths, and forced XCD row grouping."""
+    try:
+        fq.rmsq_set_wave_rows(R)
+        for k, (M, N, fmt, lay, res) in enumerate([(1030, 1536, 0, 0, False), (37, 512, 1, 1, True),
+                                                     (257, 2048, 0, 2, True), (65, 256, 1, 2, False)]):
+            say(f"packed rows R={R} M={M} N={N} fmt={fmt} layout={lay}")
+            p = inputs.make_problem(M, N, seed_x=600 + k, residual=res, outliers=True)
+            check(orc, [dict(p, fmt=fmt, scale_layout=lay, keep_bf16=(k % 2 == 0))])
+        a = inputs.make_problem(515, 1536, seed_x=610, residual=False, outliers=True)
+        b = inputs.make_problem(299, 512, seed_x=611, residual=False, outliers=True)
+        for g in (0, 16, 64):
+            fq.rmsq_set_row_group(g)
+            check(orc, [dict(a, fmt=0, scale_layout=2), dict(b, fmt=0, scale_layout=0, keep_bf16=True)])
+    finally:
+        fq.rmsq_set_wave_rows(0)
+        fq.rmsq_set_row_group(0)
+
+
 # ------------------------------------------------------------ edge cases --
 def test_zero_rows_zero_groups_and_signed_zeros(orc):
     say("edge: zeros")
