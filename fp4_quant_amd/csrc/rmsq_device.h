@@ -87,31 +87,56 @@ __device__ __forceinline__ bool near_bf16_midpoint(float y) {
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
-// bf16(hg * inv) for 8 elements, hg = h * gamma (exact in fp32), inv the fp64
-// inverse norm and inv32 = fl32(inv). The fp32 product is within 2 ulp of the
-// fp64 one, so its bf16 rounding is final unless it lies within 4 ulp of a
-// bf16 midpoint; those elements (all of them when row_exact) are redone from
-// the fp64 product with a single rounding. The window test runs on packed
-// 16-bit lanes: the low halves of two products side by side (v_perm_b32),
-// plus 0x8004 modulo 2^16, fall in [0, 8] exactly for the products whose
-// low 16 bits lie in [0x7FFC, 0x8004]; the minimum over the 8 elements
-// decides whether any of them needs the fp64 path.
-__device__ __forceinline__ u32x4 norm_bf16x8(const float hg[8], float inv32, double inv, bool row_exact) {
+// Classes of an fp32 product h * gamma that is not exact or not finite:
+// NaN, +-infinity, +-denormal (v_cmp_class_f32 mask). A normal product of two
+// bf16 (8 significant bits each) is exact in fp32.
+constexpr int kInexactProduct = 0x001 | 0x002 | 0x004 | 0x010 | 0x080 | 0x200;
+
+// bf16(h * g * inv) for 8 elements: h bf16 values (as fp32, and packed two
+// per dword in hpk), g the 8 bf16 gammas packed two per dword, inv the fp64
+// inverse norm and inv32 = fl32(inv). hg = h * g is exact in fp32 unless it
+// leaves the normal range; then y = hg * inv32 is within 2 ulp of the fp64
+// product h * g * inv, so its bf16 rounding is final unless y lies within 4
+// ulp of a bf16 midpoint. Those elements, elements whose hg is denormal or
+// infinite, and every element of a row_exact row are redone in fp64 from h
+// and g (their product is exact there) with a single rounding. (A product
+// that underflows to zero is harmless here: the caller flags rows with
+// inv > 2^16, and below that a zero hg keeps the sign of a true result that
+// rounds to zero in bf16 anyway.) The window test runs on packed 16-bit
+// lanes: the low halves of two products side by side (v_perm_b32), plus
+// 0x8004 modulo 2^16, fall in [0, 8] exactly for the products whose low 16
+// bits lie in [0x7FFC, 0x8004]; the minimum over the 8 elements decides
+// whether any of them needs the fp64 path.
+__device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, const u32x4 g, float inv32,
+                                             double inv, bool row_exact) {
   u32x4 yw;
   u16x2 lo_min = {0xFFFFu, 0xFFFFu};
+  bool odd = row_exact;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float y0 = hg[2 * i] * inv32, y1 = hg[2 * i + 1] * inv32;
+    const float hg0 = h[2 * i] * bf16_lo(g[i]), hg1 = h[2 * i + 1] * bf16_hi(g[i]);
+    odd |= __builtin_amdgcn_classf(hg0, kInexactProduct) | __builtin_amdgcn_classf(hg1, kInexactProduct);
+    const float y0 = hg0 * inv32, y1 = hg1 * inv32;
     const uint32_t lows = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x05040100u);
     lo_min = __builtin_elementwise_min(lo_min, __builtin_bit_cast(u16x2, lows) + u16x2{0x8004u, 0x8004u});
     yw[i] = pack_bf16(y0, y1);
   }
-  const bool need = row_exact | (min((uint32_t)lo_min[0], (uint32_t)lo_min[1]) <= 8u);
-  if (need) {
+  const bool need = odd | (min((uint32_t)lo_min[0], (uint32_t)lo_min[1]) <= 8u);
+  if (__builtin_expect(need, 0)) {   // rare: keep the fast path's code contiguous
+    // Rare: recompute the products here instead of keeping the fast path's
+    // 16 intermediates alive across the branch (the empty asm hides that
+    // they are the same values, so the compiler does not hold them in
+    // registers for the whole phase).
+    u32x4 gr = g, hr = hpk;
+    float ir = inv32;
+    asm volatile("" : "+v"(gr), "+v"(hr), "+v"(ir));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (row_exact | near_bf16_midpoint(hg[e] * inv32)) {
-        const uint32_t b = bf16_from_f64((double)hg[e] * inv);
+      const float ge = (e & 1) ? bf16_hi(gr[e >> 1]) : bf16_lo(gr[e >> 1]);
+      const float he = (e & 1) ? bf16_hi(hr[e >> 1]) : bf16_lo(hr[e >> 1]);
+      const float hg = he * ge;
+      if (row_exact | __builtin_amdgcn_classf(hg, kInexactProduct) | near_bf16_midpoint(hg * ir)) {
+        const uint32_t b = bf16_from_f64((double)he * (double)ge * inv);
         const int sh = (e & 1) * 16;
         yw[e >> 1] = (yw[e >> 1] & ~(0xFFFFu << sh)) | (b << sh);
       }
@@ -161,7 +186,7 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
   qh[0] = cvt_fp8x2<true>(hi[2], hi[3], cvt_fp8x2<false>(hi[0], hi[1], 0u));
   qh[1] = cvt_fp8x2<true>(hi[6], hi[7], cvt_fp8x2<false>(hi[4], hi[5], 0u));
   const bool tiny = s < 0x1p-100f;
-  if (tiny | (qw[0] != qh[0]) | (qw[1] != qh[1])) {
+  if (__builtin_expect(tiny | (qw[0] != qh[0]) | (qw[1] != qh[1]), 0)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int sh = (e & 3) * 8;

@@ -21,10 +21,11 @@
 //  * sum of h^2 in fp64 (each square exact), DPP tree within the wave, then
 //    the waves' partial sums in wave order through LDS,
 //    inv = 1/sqrt(ss/N + eps) in fp64 with correctly rounded divide / sqrt.
-//  * y = (h*g) * inv: h*g is exact in fp32; the product is first taken in
-//    fp32 with fl32(inv) (within 2 ulp of the fp64 product); only when it
-//    lands within 4 ulp of a bf16 rounding midpoint is the element redone as
-//    fp64 (h*g)*inv rounded once to bf16.
+//  * y = (h*g) * inv: h*g is exact in fp32 while it stays in the normal
+//    range; the product is first taken in fp32 with fl32(inv) (within 2 ulp
+//    of the fp64 product); only when it lands within 4 ulp of a bf16
+//    rounding midpoint, or h*g is denormal or infinite, is the element redone
+//    as fp64 h*g*inv rounded once to bf16.
 //  * FP8 scale s = fl32(amax/448), correctly rounded; codes through the
 //    hardware convert of yb * r for two reciprocals r bracketing 1/s: where
 //    both brackets give the same code it is the code of yb/s (rounding is
@@ -158,6 +159,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   double ss = 0.0;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
+    if (j > 0 && j * T >= C) break;   // the rest of the chunks lie past the row end for the whole workgroup
     u32x4 hw = xv[j];
     if (j * T + tid >= C) hw = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -182,9 +184,10 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   const double denom = ss / (double)P.N + (double)P.eps;
   const double inv = denom > 0.0 ? 1.0 / __builtin_sqrt(denom) : 0.0;
   const float inv32 = (float)inv;
-  // rows whose inverse norm leaves the comfortable fp32 range take the exact
-  // path for every element
-  const bool row_exact = inv > 0x1p100 || (inv != 0.0 && inv < 0x1p-100);
+  // Rows whose inverse norm leaves the comfortable fp32 range take the exact
+  // path for every element: inv > 2^16, where an h * gamma that underflows to
+  // zero in fp32 could still have a nonzero bf16 result, and inv < 2^-100.
+  const bool row_exact = inv > 0x1p16 || (inv != 0.0 && inv < 0x1p-100);
 
   // ---- phase 2: normalize, bf16, group scale, codes -----------------------
   u32x4* ybrow = P.yb ? reinterpret_cast<u32x4*>(P.yb + m * P.ldb) : nullptr;
@@ -196,15 +199,13 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
     u32x4 g;
     if constexpr (kShort) g = gv[j];
     else g = grow[c];
-    float hg[8];
+    float hv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float h0 = kShort ? hf[kShort ? j : 0][2 * i] : bf16_lo(xv[j][i]);
-      const float h1 = kShort ? hf[kShort ? j : 0][2 * i + 1] : bf16_hi(xv[j][i]);
-      hg[2 * i] = h0 * bf16_lo(g[i]);
-      hg[2 * i + 1] = h1 * bf16_hi(g[i]);
+      hv[2 * i] = kShort ? hf[kShort ? j : 0][2 * i] : bf16_lo(xv[j][i]);
+      hv[2 * i + 1] = kShort ? hf[kShort ? j : 0][2 * i + 1] : bf16_hi(xv[j][i]);
     }
-    const u32x4 yw = norm_bf16x8(hg, inv32, inv, row_exact);
+    const u32x4 yw = norm_bf16x8(hv, xv[j], g, inv32, inv, row_exact);
     // All stores of a row go out after its reduction: keeping the residual
     // write next to the others measured 3% faster than writing it as soon as
     // it is formed.

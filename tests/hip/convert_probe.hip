@@ -13,11 +13,17 @@ using namespace rmsq;
 #define GRID_LOOP(i, n) \
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < (n); i += (int64_t)gridDim.x * blockDim.x)
 
-__global__ void k_norm_bf16(const float* hg, const double* inv, const uint8_t* row_exact, uint16_t* out, int64_t n) {
+__global__ void k_norm_bf16(const float* hv, const float* gv, const double* inv, const uint8_t* row_exact,
+                            uint16_t* out, int64_t n) {
   GRID_LOOP(k, n) {
     float h[8];
-    for (int e = 0; e < 8; ++e) h[e] = hg[8 * k + e];
-    const u32x4 w = norm_bf16x8(h, (float)inv[k], inv[k], row_exact[k] != 0);
+    u32x4 hp, g;
+    for (int e = 0; e < 8; ++e) h[e] = hv[8 * k + e];
+    for (int i = 0; i < 4; ++i) {   // h and gamma are bf16 values: their fp32 patterns' high halves
+      hp[i] = (__float_as_uint(hv[8 * k + 2 * i]) >> 16) | (__float_as_uint(hv[8 * k + 2 * i + 1]) & 0xFFFF0000u);
+      g[i] = (__float_as_uint(gv[8 * k + 2 * i]) >> 16) | (__float_as_uint(gv[8 * k + 2 * i + 1]) & 0xFFFF0000u);
+    }
+    const u32x4 w = norm_bf16x8(h, hp, g, (float)inv[k], inv[k], row_exact[k] != 0);
     for (int e = 0; e < 8; ++e) out[8 * k + e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
   }
 }
@@ -111,9 +117,10 @@ static int launch_status() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 #define GRID(n) dim3((unsigned)(((n) + 255) / 256 < 65536 ? ((n) + 255) / 256 : 65536)), dim3(256), 0, (hipStream_t)stream
 
 extern "C" {
-int probe_norm_bf16(const float* hg, const double* inv, const uint8_t* ex, uint16_t* out, int64_t n, void* stream) {
+int probe_norm_bf16(const float* h, const float* g, const double* inv, const uint8_t* ex, uint16_t* out, int64_t n,
+                    void* stream) {
   if (n <= 0) return 0;
-  hipLaunchKernelGGL(k_norm_bf16, GRID(n), hg, inv, ex, out, n);
+  hipLaunchKernelGGL(k_norm_bf16, GRID(n), h, g, inv, ex, out, n);
   return launch_status();
 }
 int probe_fp8_scale(const uint16_t* a, float* s, int64_t n, void* stream) {

@@ -146,9 +146,45 @@ def test_norm_bf16x8_matches_fp64_rounding(orc):
     inv[k[nz]] *= 1 + rng.choice([-1, 0, 1], nz.sum()) * 2.0 ** -52
     ex = (rng.random(n // 8) < 0.05).astype(np.uint8)
     out = torch.empty(n, dtype=torch.int16, device="cuda")
-    call_probe("probe_norm_bf16", dev(hg), dev(inv), dev(ex), out, n=n // 8)
+    call_probe("probe_norm_bf16", dev(h.astype(np.float32)), dev(g.astype(np.float32)), dev(inv), dev(ex), out,
+               n=n // 8)
     want = orc.bf16_from_double(hg.astype(np.float64) * np.repeat(inv, 8))
     assert np.array_equal(host(out).view(np.uint16), want)
+
+
+def test_norm_bf16x8_products_outside_the_fp32_normal_range(orc):
+    """h * gamma that is denormal, underflows to zero or overflows in fp32
+    (extreme but finite bf16 inputs) still gives bf16(h * gamma * inv) taken
+    in fp64, as the oracle computes it."""
+    say("norm_bf16x8 extreme products")
+    rng = np.random.default_rng(15)
+    n = 100_000 * 8
+    sig = lambda k: 1 + rng.integers(0, 128, k) / 128.0          # 8 significant bits
+    sgn = lambda k: rng.choice([-1.0, 1.0], k)
+    cases = []
+    # denormal products (2^-149 <= |hg| < 2^-126) with inv up to 2^16
+    e1 = rng.integers(-75, -63, n)
+    cases.append((sgn(n) * sig(n) * 2.0 ** e1, sig(n) * 2.0 ** (rng.integers(-148, -126, n) - e1),
+                  2.0 ** rng.uniform(0, 16, n // 8)))
+    # products below 2^-150 (flush to zero in fp32) with inv up to 2^16
+    e2 = rng.integers(-90, -75, n)
+    cases.append((sgn(n) * sig(n) * 2.0 ** e2, sig(n) * 2.0 ** (rng.integers(-170, -151, n) - e2),
+                  2.0 ** rng.uniform(0, 16, n // 8)))
+    # products beyond the fp32 range with inv small enough for a finite y
+    e3 = rng.integers(64, 120, n)
+    cases.append((sgn(n) * sig(n) * 2.0 ** e3, sig(n) * 2.0 ** (rng.integers(128, 140, n) - e3),
+                  2.0 ** rng.uniform(-30, -13, n // 8)))
+    for h, g, inv in cases:
+        h32, g32 = h.astype(np.float32), g.astype(np.float32)
+        assert np.array_equal(h32.astype(np.float64), h) and np.array_equal(g32.astype(np.float64), g)
+        assert np.array_equal(orc.bf16_to_double(orc.bf16_from_double(h)), h)      # bf16 values
+        ex = np.zeros(n // 8, np.uint8)
+        out = torch.empty(n, dtype=torch.int16, device="cuda")
+        call_probe("probe_norm_bf16", dev(h32), dev(g32), dev(inv), dev(ex), out, n=n // 8)
+        want = orc.bf16_from_double(h * g * np.repeat(inv, 8))
+        got = host(out).view(np.uint16)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"{bad.size} differ, first h={h[bad[0]]} g={g[bad[0]]} inv={inv[bad[0] // 8]}"
 
 
 def test_fp8_scale_every_amax():

@@ -277,6 +277,25 @@ def test_tiny_and_huge_rows_take_the_exact_path(orc):
             check(orc, [p])
 
 
+def test_gamma_products_outside_the_fp32_range(orc):
+    """Gamma columns so small that h * gamma is an fp32 denormal, or so large
+    that it overflows fp32, in rows whose norm keeps y finite: those elements
+    take the fp64 path and still match the oracle."""
+    say("edge: h * gamma outside the fp32 normal range")
+    N = 1024
+    g = inputs.gamma_vec(N, 9).view(np.uint16).copy()
+    gf = inputs.gamma_vec(N, 9).view(np.uint16)
+    small = inputs.to_bf16_bits(np.float32(2.0 ** -130) * (1 + np.arange(128, dtype=np.float32) / 128))
+    g[128:256] = small                                   # bf16 denormal gammas: h * g denormal in fp32
+    g[256:320] = inputs.to_bf16_bits(np.float32(2.0 ** 100) * np.ones(64, np.float32))
+    x = inputs.normal_rows(6, N, 16, False)
+    x[3:] *= np.float32(2.0 ** 30)                       # h * 2^100 overflows fp32; inv ~ 2^-30 keeps y finite
+    for fmt in (0, 1):
+        p = {"x": inputs.to_bf16_bits(x), "gamma": g, "eps": 1e-6, "fmt": fmt, "keep_bf16": True}
+        check(orc, [p])
+    assert not np.array_equal(g, gf)
+
+
 def tie_rows(M, N, seed):
     """Rows with gamma = 1, eps = 0 and sum(h^2) = 4N exactly, so inv = 1/2 and
     y = h/2 with no rounding. Every 32-block starts with +-3.5 (group amax

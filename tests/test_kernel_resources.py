@@ -1,0 +1,65 @@
+"""Register and scratch budget of the HIP kernels, read from the gfx950 code
+object metadata that hipcc emits for the library source (device-only
+assembly, compiled here on the CPU). Occupancy is what keeps enough bytes in
+flight for the HBM-bound launches, so a change that raises the register
+count of the hot variants, spills, or starts using scratch memory fails here
+before it reaches a GPU.
+
+Limits (512 VGPRs per SIMD lane slot, allocated in granules of 8):
+  * J = 1, 2 (the shapes of the 7168-wide rows): at most 64 VGPRs, 8 waves per SIMD;
+  * J = 3: at most 80 VGPRs, 6 waves per SIMD; J = 4: at most 96, 5 waves;
+  * J = 7, 8: at most 128 VGPRs, J = 14: at most 168 (4-wave workgroups);
+  * no kernel spills or uses private (scratch) memory.
+"""
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from fp4_quant_amd import build as B
+
+NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)EEEvNS_6LaunchE$")
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        flags = [f for f in B.HIP_FLAGS if f not in ("-shared", "-fPIC")]
+        subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", "-I", os.path.join(B.ROOT, "include"),
+                        "-I", B.CSRC, os.path.join(B.CSRC, "rmsq_abi.hip"), "-o", out],
+                       check=True, capture_output=True)
+        text = open(out).read()
+    meta = text[text.index("amdhsa.kernels:"):]
+    ks = {}
+    for block in re.split(r"\n  - ", meta)[1:]:
+        def field(k):
+            m = re.search(r"\." + k + r":\s+(\S+)", block)
+            return m.group(1) if m else None
+        ks[field("name")] = {k: int(field(k) or 0) for k in
+                             ("vgpr_count", "agpr_count", "sgpr_count", "vgpr_spill_count", "sgpr_spill_count",
+                              "private_segment_fixed_size", "group_segment_fixed_size")}
+    return ks
+
+
+def test_every_kernel_variant_is_present(kernels):
+    fused = [n for n in kernels if NAME.match(n or "")]
+    # 3 formats (FP8, MXFP4, norm only) x residual or not x (7 shapes + 4 packed-row shapes)
+    assert len(fused) == 3 * 2 * (7 + 4), sorted(fused)
+    assert sum(1 for n in kernels if "rmsq_group_quant_kernel" in (n or "")) == 2
+
+
+def test_no_spills_and_no_scratch(kernels):
+    for n, k in kernels.items():
+        assert k["vgpr_spill_count"] == 0 and k["sgpr_spill_count"] == 0, (n, k)
+        assert k["private_segment_fixed_size"] == 0, (n, k)
+
+
+@pytest.mark.parametrize("J,limit", [(1, 64), (2, 64), (3, 80), (4, 96), (7, 128), (8, 128), (14, 168)])
+def test_register_budget(kernels, J, limit):
+    for n, k in kernels.items():
+        m = NAME.match(n or "")
+        if m and int(m.group(2)) == J:
+            assert k["vgpr_count"] + k["agpr_count"] <= limit, (n, k)
