@@ -183,25 +183,27 @@ void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
   *W_out = rmsq::kMaxWaves;
 }
 
-template <int FMT, bool RES>
+// EXACT is used for J <= 4 only: the long per-lane shapes (very wide rows)
+// keep their bounds, which also keeps them within the register budget.
+template <int FMT, bool RES, bool EXACT>
 void launch_res(const rmsq::Launch& L, int J, int R, const dim3 grid, const dim3 block, hipStream_t stream) {
   if (R > 1) {   // one row per wave, R rows per workgroup (J <= 4 only)
     switch (J) {
-      case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, true>), grid, block, 0, stream, L); break;
-      case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, true>), grid, block, 0, stream, L); break;
-      case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, true>), grid, block, 0, stream, L); break;
-      default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, true>), grid, block, 0, stream, L); break;
+      case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, true, EXACT>), grid, block, 0, stream, L); break;
+      case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, true, EXACT>), grid, block, 0, stream, L); break;
+      case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, true, EXACT>), grid, block, 0, stream, L); break;
+      default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, true, EXACT>), grid, block, 0, stream, L); break;
     }
     return;
   }
   switch (J) {
-    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES, false>), grid, block, 0, stream, L); break;
-    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES, false>), grid, block, 0, stream, L); break;
-    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES, false>), grid, block, 0, stream, L); break;
-    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, false>), grid, block, 0, stream, L); break;
-    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, false>), grid, block, 0, stream, L); break;
-    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, false>), grid, block, 0, stream, L); break;
-    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, false>), grid, block, 0, stream, L); break;
+    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES, false, false>), grid, block, 0, stream, L); break;
+    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES, false, false>), grid, block, 0, stream, L); break;
+    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES, false, false>), grid, block, 0, stream, L); break;
+    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, false, EXACT>), grid, block, 0, stream, L); break;
+    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, false, EXACT>), grid, block, 0, stream, L); break;
+    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, false, EXACT>), grid, block, 0, stream, L); break;
+    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, false, EXACT>), grid, block, 0, stream, L); break;
   }
 }
 
@@ -212,10 +214,15 @@ template <int FMT>
 rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, int R, hipStream_t stream) {
   const dim3 grid(R > 1 ? (unsigned)((L.rows + R - 1) / R) : (unsigned)L.rows);
   const dim3 block((unsigned)(64 * (R > 1 ? R : W)));
-  if (L.p[0].r)
-    launch_res<FMT, true>(L, J, R, grid, block, stream);
-  else
-    launch_res<FMT, false>(L, J, R, grid, block, stream);
+  bool exact = true;   // every row exactly fills its J*64*W (or J*64, packed) lanes
+  for (int i = 0; i < L.count; ++i) exact &= (L.p[i].N >> 3) == J * 64 * (R > 1 ? 1 : W);
+  if (L.p[0].r) {
+    if (exact) launch_res<FMT, true, true>(L, J, R, grid, block, stream);
+    else launch_res<FMT, true, false>(L, J, R, grid, block, stream);
+  } else {
+    if (exact) launch_res<FMT, false, true>(L, J, R, grid, block, stream);
+    else launch_res<FMT, false, false>(L, J, R, grid, block, stream);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return RMSQ_OK;

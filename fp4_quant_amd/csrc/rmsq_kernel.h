@@ -87,7 +87,10 @@ __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t
 // WAVE_ROWS: rows short enough for one wave (J*64 chunks) are packed one per
 // wave, blockDim/64 consecutive rows per workgroup, with no LDS and no
 // barrier; otherwise the workgroup's waves share one row.
-template <int FMT, int J, bool RES, bool WAVE_ROWS>
+// EXACT: every row of the launch has exactly J*T chunks (T lanes per row),
+// so no lane needs a bound (the usual shapes: 7168 = 2 x 7 waves or 1 x 14,
+// 1536 = 3 x 1, 512 = 1 x 1).
+template <int FMT, int J, bool RES, bool WAVE_ROWS, bool EXACT>
 __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Launch L) {
   // Short per-lane rows (the usual shapes) keep h as fp32 and fetch gamma
   // together with x and r; long ones keep h packed and fetch gamma late, to
@@ -116,6 +119,8 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   const int T = WAVE_ROWS ? 64 : blockDim.x;
   const int tid = WAVE_ROWS ? (threadIdx.x & 63) : threadIdx.x;
   const int C = P.N >> 3;
+  // chunk index a lane loads: clamped to the row for a ragged launch
+  auto chunk = [C](int c) { return EXACT ? c : min(c, C - 1); };
 
   // ---- loads: x, gamma (short rows), then r, all issued before any use ---
   // (of the issue orders measured, this one was fastest on both the
@@ -129,17 +134,17 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   const u32x4* grow = reinterpret_cast<const u32x4*>(P.gamma);
   u32x4 xv[J], rv[RES ? J : 1], gv[kShort ? J : 1];
 #pragma unroll
-  for (int j = 0; j < J; ++j) xv[j] = __builtin_nontemporal_load(xrow + min(j * T + tid, C - 1));
+  for (int j = 0; j < J; ++j) xv[j] = __builtin_nontemporal_load(xrow + chunk(j * T + tid));
   if constexpr (kShort) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) gv[j] = grow[min(j * T + tid, C - 1)];
+    for (int j = 0; j < J; ++j) gv[j] = grow[chunk(j * T + tid)];
   }
   // keep the r loads in place: the scheduler may otherwise interleave them
   // with x's, or hoist x's unpacking (and the wait for x) above them
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (RES) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) rv[j] = __builtin_nontemporal_load(rrow + min(j * T + tid, C - 1));
+    for (int j = 0; j < J; ++j) rv[j] = __builtin_nontemporal_load(rrow + chunk(j * T + tid));
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -159,9 +164,9 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   double ss = 0.0;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    if (j > 0 && j * T >= C) break;   // the rest of the chunks lie past the row end for the whole workgroup
+    if (!EXACT && j > 0 && j * T >= C) break;   // the rest lie past the row end for the whole workgroup
     u32x4 hw = xv[j];
-    if (j * T + tid >= C) hw = u32x4{0u, 0u, 0u, 0u};
+    if (!EXACT && j * T + tid >= C) hw = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float a = bf16_lo(hw[i]), b = bf16_hi(hw[i]);
@@ -195,7 +200,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = j * T + tid;
-    if (c >= C) continue;
+    if (!EXACT && c >= C) continue;
     u32x4 g;
     if constexpr (kShort) g = gv[j];
     else g = grow[c];

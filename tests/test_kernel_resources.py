@@ -20,7 +20,7 @@ import pytest
 
 from fp4_quant_amd import build as B
 
-NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)EEEvNS_6LaunchE$")
+NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)ELb(\d)EEEvNS_6LaunchE$")
 
 
 @pytest.fixture(scope="module")
@@ -46,8 +46,9 @@ def kernels():
 
 def test_every_kernel_variant_is_present(kernels):
     fused = [n for n in kernels if NAME.match(n or "")]
-    # 3 formats (FP8, MXFP4, norm only) x residual or not x (7 shapes + 4 packed-row shapes)
-    assert len(fused) == 3 * 2 * (7 + 4), sorted(fused)
+    # 3 formats (FP8, MXFP4, norm only) x residual or not x (7 shapes + 4 packed-row shapes),
+    # the 4 short shapes and 4 packed-row shapes also for rows that exactly fill the launch
+    assert len(fused) == 3 * 2 * (7 + 4 + 4 + 4), sorted(fused)
     assert sum(1 for n in kernels if "rmsq_group_quant_kernel" in (n or "")) == 2
 
 
