@@ -230,6 +230,16 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def kernel_name(fmt, N, rows, residual):
+    """The fused kernel instance a single-problem launch uses (as rocprofv3
+    names it), with its waves per row."""
+    import fp4_quant_amd as fq
+    J, W = fq.rmsq_query_shape(N, rows)
+    exact = "true" if N // 8 == J * 64 * W else "false"
+    return (f"rmsq_fused_kernel<{fmt}, {J}, {'true' if residual else 'false'}, false, {exact}>"
+            f" ({W} waves per row)")
+
+
 def recorded_traffic(config):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
@@ -331,6 +341,9 @@ def main():
             configs[name] = {"us_per_launch": round(pl * 1e3, 2), "GBps": round(wk.bytes / (pl * 1e-3) / 1e9, 1),
                              "frac_of_peak": round(wk.bytes / (pl * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                              "Mtok_per_s": round(wk.rows / (pl * 1e-3) / 1e6, 2), "bytes": wk.bytes}
+            tr = recorded_traffic(name)
+            if tr is not None:
+                configs[name]["traffic"] = tr
             if wk.bytes < 64 << 20:       # launch-bound sizes: also replayed from a HIP graph
                 pg = time_workload_graph(wk, 100)
                 configs[name]["us_per_launch_graph"] = round(pg * 1e3, 2)
@@ -379,7 +392,7 @@ def main():
         "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": recorded_traffic(args.config),
-                     "kernel": "rmsq_fused_kernel<%d,%d> x %d waves" % ((fmt,) + fq.rmsq_query_shape(N, w.rows)),
+                     "kernel": kernel_name(fmt, N, w.rows, specs[0]["residual"]),
                      "bytes_per_launch": w.bytes,
                      "us_per_launch": round(step_ms * 1e3, 2)},
         "stream_ceilings_GBps": ceil,
