@@ -127,3 +127,41 @@ def test_graph_capture_and_replay():
         for a, c in zip(_snapshot(bufs), want):
             assert np.array_equal(a, c), f"replay {k}"
         _ = (x.float() * 2).sum().item()              # eager work between replays
+
+
+def test_graph_capture_of_a_mixed_set_two_launches(orc):
+    """A multi-problem set mixing problems with and without a residual is
+    enqueued as two launches; captured in a graph, every replay matches the
+    oracle."""
+    from tests.test_gpu_parity import run_oracle
+    say("HIP graph capture of a mixed multi-problem set")
+    pa = inputs.make_problem(96, 7168, seed_x=93, residual=True, outliers=True)
+    pb = inputs.make_problem(1100, 1536, seed_x=94, residual=False, outliers=False)
+    prob_a, bufs_a = _buffers(pa)
+    xb, gb = dev(pb["x"]), dev(pb["gamma"])
+    qb, sb, yb = fq.alloc_outputs(1100, 1536, 0, 0, True)
+    prob_b = fq.make_problem(xb, gb, pb["eps"], qb, sb, out_bf16=yb)
+    arr = fq.problem_array([prob_a, prob_b])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fq.rmsnorm_quant_group_multi(arr)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        fq.rmsnorm_quant_group_multi(arr)
+    wa = run_oracle(orc, dict(pa, fmt=0))
+    wb = run_oracle(orc, dict(pb, fmt=0))
+    for k in range(3):
+        for t in list(bufs_a[3:]) + [qb, sb, yb]:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ro, q, sc, ybo = (host(t) for t in bufs_a[3:])
+        assert np.array_equal(ro, wa["residual_out"]), k
+        assert np.array_equal(ybo, wa["bf16"]) and np.array_equal(q, wa["q"]), k
+        assert np.array_equal(sc.reshape(-1).view(np.uint32), wa["scale"].reshape(-1).view(np.uint32)), k
+        assert np.array_equal(host(yb), wb["bf16"]) and np.array_equal(host(qb), wb["q"]), k
+        assert np.array_equal(host(sb).reshape(-1).view(np.uint32), wb["scale"].reshape(-1).view(np.uint32)), k
+        _ = (xb.float() * 2).sum().item()              # eager work between replays
