@@ -59,6 +59,7 @@ class Workload:
         from fp4_quant_amd import inputs
         self.name, self.fmt, self.layout = name, fmt, layout
         self.bytes = sum(algorithmic_bytes(s["M"], s["N"], fmt, s["residual"], s["keep_bf16"]) for s in specs)
+        self.keep_bf16 = specs[0]["keep_bf16"]
         self.rows = sum(s["M"] for s in specs)
         nsets = max(2, min(512, -(-3 * MALL_BYTES // max(self.bytes, 1))))
         self.sets = []
@@ -255,26 +256,52 @@ def recorded_traffic(config):
     return None
 
 
+def _oracle_call(p, fmt, layout, keep):
+    import oracle
+    oracle.rmsnorm_quant_group(p["x"], p["gamma"], p["eps"], residual=p.get("residual"),
+                               group=128 if fmt == 0 else 32, fmt=fmt, scale_layout=layout, keep_bf16=keep)
+
+
 def cpu_baseline(w, budget_s):
-    """The CPU oracle as it stands on this host, over the workload's rows,
-    repeated until budget_s has passed (at least once)."""
+    """The CPU oracle as it stands on this host, over the workload's first
+    problem (its full rows), repeated until budget_s has passed (at least
+    once), with the OpenMP threads the host gives it; then once more on a
+    512-row sample with a single thread (in a child process, so the thread
+    count is set before the OpenMP runtime starts)."""
+    import statistics
     import oracle
     p = w.host[0]
     M, N = p["x"].shape
-    keep = True
-    t_total, reps = 0.0, 0
+    keep = w.keep_bf16
+    times = []
     while True:
         t0 = time.perf_counter()
-        oracle.rmsnorm_quant_group(p["x"], p["gamma"], p["eps"], residual=p.get("residual"),
-                                   group=128, fmt=0, keep_bf16=keep)
-        t_total += time.perf_counter() - t0
-        reps += 1
-        if t_total >= budget_s:
+        _oracle_call(p, w.fmt, w.layout, keep)
+        times.append(time.perf_counter() - t0)
+        if sum(times) >= budget_s:
             break
-    sec = t_total / reps
-    return {"value": round(w.bytes / sec / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "mtok_per_s": round(M / sec / 1e6, 4),
-            "sample": f"the full {M}x{N} workload, {reps} run(s), {sec:.3f} s each (median not taken: mean)"}
+    sec = statistics.median(times)
+    bytes_ = algorithmic_bytes(M, N, w.fmt, "residual" in p, keep)
+    out = {"value": round(bytes_ / sec / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+           "kind": "oracle", "mtok_per_s": round(M / sec / 1e6, 4),
+           "sample": f"the full {M}x{N} rows of the workload, {len(times)} run(s), median {sec:.3f} s"}
+    rows = min(M, 512)
+    code = ("import sys, time; sys.path.insert(0, %r)\n"
+            "from fp4_quant_amd import inputs\nimport bench\n"
+            "p = inputs.make_problem(%d, %d, seed_x=0, residual=%r, outliers=True)\n"
+            "ts = []\n"
+            "for _ in range(3):\n"
+            "    t0 = time.perf_counter(); bench._oracle_call(p, %d, %d, %r); ts.append(time.perf_counter() - t0)\n"
+            "print(sorted(ts)[1])\n") % (ROOT, rows, N, "residual" in p, w.fmt, w.layout, keep)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode == 0:
+        s1 = float(r.stdout.strip().splitlines()[-1])
+        b1 = algorithmic_bytes(rows, N, w.fmt, "residual" in p, keep)
+        out["single_thread"] = {"value": round(b1 / s1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "mtok_per_s": round(rows / s1 / 1e6, 4),
+                                "sample": f"{rows}x{N} rows, median of 3 runs, {s1:.3f} s"}
+    return out
 
 
 SPECS = {
