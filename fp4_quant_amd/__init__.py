@@ -57,7 +57,7 @@ class rmsq_problem(C.Structure):
 EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "add_rmsnorm",
            "dynamic_per_group_scaled_quant", "rmsq_device_supported",
            "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape",
-           "rmsq_query_shape", "rmsq_set_row_group", "rmsq_set_wave_rows")
+           "rmsq_query_shape", "rmsq_set_row_group", "rmsq_set_wave_rows", "rmsq_set_row_splits")
 
 _lib = None
 
@@ -93,6 +93,8 @@ def lib() -> C.CDLL:
         L.rmsq_set_row_group.argtypes = [i32]
         L.rmsq_set_wave_rows.restype = None
         L.rmsq_set_wave_rows.argtypes = [i32]
+        L.rmsq_set_row_splits.restype = None
+        L.rmsq_set_row_splits.argtypes = [i32]
         L.rmsq_query_shape.restype = i32
         L.rmsq_query_shape.argtypes = [i64, i64, C.POINTER(i32), C.POINTER(i32)]
         _lib = L
@@ -186,6 +188,10 @@ def rmsq_set_row_group(g: int = 0) -> None:
 
 def rmsq_set_wave_rows(R: int = 0) -> None:
     lib().rmsq_set_wave_rows(int(R))
+
+
+def rmsq_set_row_splits(S: int = 0) -> None:
+    lib().rmsq_set_row_splits(int(S))
 
 
 def rmsq_query_shape(N: int, rows: int):

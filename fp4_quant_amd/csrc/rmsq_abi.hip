@@ -3,6 +3,7 @@
 // include/rmsq.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -163,6 +164,7 @@ constexpr int kJs[] = {2, 3, 4, 1, 7, 8, 14};
 constexpr int kJsFewRows[] = {1, 2, 3, 4, 7, 8, 14};
 constexpr int64_t kComputeUnits = 256;
 constexpr int kWaveRowsPerBlock = 4;
+constexpr int kMaxSplits = 8;
 
 void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
   const bool few = rows <= kComputeUnits;
@@ -212,9 +214,9 @@ void launch_res(const rmsq::Launch& L, int J, int R, const dim3 grid, const dim3
 // workgroup, one per wave.
 template <int FMT>
 rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, int R, hipStream_t stream) {
-  const dim3 grid(R > 1 ? (unsigned)((L.rows + R - 1) / R) : (unsigned)L.rows);
+  const dim3 grid(R > 1 ? (unsigned)((L.rows + R - 1) / R) : (unsigned)L.rows * (unsigned)L.splits);
   const dim3 block((unsigned)(64 * (R > 1 ? R : W)));
-  bool exact = true;   // every row exactly fills its J*64*W (or J*64, packed) lanes
+  bool exact = L.splits == 1;   // every row exactly fills its J*64*W (or J*64, packed) lanes
   for (int i = 0; i < L.count; ++i) exact &= (L.p[i].N >> 3) == J * 64 * (R > 1 ? 1 : W);
   if (L.p[0].r) {
     if (exact) launch_res<FMT, true, true>(L, J, R, grid, block, stream);
@@ -230,7 +232,7 @@ rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, int R, hipStream_t s
 
 // Launch-shape override for measurement sweeps, set by rmsq_set_shape
 // (0, 0 = automatic choice).
-std::atomic<int> g_force_J{0}, g_force_W{0}, g_force_G{0}, g_force_R{0};
+std::atomic<int> g_force_J{0}, g_force_W{0}, g_force_G{0}, g_force_R{0}, g_force_S{0};
 
 bool compiled_J(int J) {
   for (int k : kJs)
@@ -322,6 +324,23 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
     int lgR = 0;
     while ((2 << lgR) <= R) ++lgR;
     L.row_group_log2 = R > 1 ? (lg > lgR ? lg - lgR : 0) : lg;   // groups of workgroups when packed
+    // Fewer rows than compute units: split each row over several workgroups
+    // (each recomputes the row's sum of squares, bit-identically, and does
+    // the normalize / quantize work for its share), so every CU works.
+    L.splits = 1;
+    if (R == 1) {
+      const int fS = g_force_S.load();
+      int S = 1;
+      if (fS > 0) S = fS;
+      else
+        while (S < kMaxSplits && rows * S * 2 <= kComputeUnits) S *= 2;
+      const int64_t q = mode == Mode::kNormOnly ? 1 : ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? 16 : 4;
+      int64_t Cmin = Cmax;
+      for (int i = 0; i < n; ++i) Cmin = std::min<int64_t>(Cmin, L.p[i].N / 8);
+      while (S > 1 && Cmin / q < S) S /= 2;   // at least one group per split
+      L.splits = S;
+      if (S > 1) L.row_group_log2 = 0;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const rmsq_status st = mode == Mode::kNormOnly               ? launch_fmt<2>(L, J, W, R, s)
                            : ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(L, J, W, R, s)
@@ -452,6 +471,8 @@ void rmsq_set_shape(int32_t J, int32_t W) {
 void rmsq_set_row_group(int32_t g) { g_force_G.store(g > 0 && g <= 64 ? g : 0); }
 
 void rmsq_set_wave_rows(int32_t R) { g_force_R.store(R > 0 && R <= rmsq::kMaxWaves ? R : 0); }
+
+void rmsq_set_row_splits(int32_t S) { g_force_S.store(S > 0 && S <= kMaxSplits ? S : 0); }
 
 int32_t rmsq_query_shape(int64_t N, int64_t rows, int32_t* J, int32_t* W) {
   if (N <= 0 || N % 8 || N > RMSQ_N_MAX || rows < 0 || !J || !W) return RMSQ_ERR_INVALID_ARG;

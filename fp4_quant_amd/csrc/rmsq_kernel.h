@@ -65,8 +65,10 @@ constexpr int max_waves(int J) { return J >= 7 ? 4 : kMaxWaves; }
 struct Launch {
   Problem p[kMaxProblems];
   int32_t count;
-  int32_t rows;           // grid size: one workgroup per row over all problems
+  int32_t rows;           // rows over all problems
   int32_t row_group_log2; // 2^k consecutive rows kept together on one XCD (0 = dispatch order)
+  int32_t splits;         // workgroups per row (>= 1): each computes the row's statistics
+                          // and normalizes / quantizes its own 1/splits of the row
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
@@ -87,8 +89,8 @@ __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t
 // WAVE_ROWS: rows short enough for one wave (J*64 chunks) are packed one per
 // wave, blockDim/64 consecutive rows per workgroup, with no LDS and no
 // barrier; otherwise the workgroup's waves share one row.
-// EXACT: every row of the launch has exactly J*T chunks (T lanes per row),
-// so no lane needs a bound (the usual shapes: 7168 = 2 x 7 waves or 1 x 14,
+// EXACT: every row of the launch has exactly J*T chunks (T lanes per row)
+// and is not split, so no lane needs a bound (the usual shapes: 7168 = 2 x 7 waves or 1 x 14,
 // 1536 = 3 x 1, 512 = 1 x 1).
 template <int FMT, int J, bool RES, bool WAVE_ROWS, bool EXACT>
 __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Launch L) {
@@ -101,13 +103,18 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   // Neighbouring row groups run on different XCDs at the same time. (Giving
   // each XCD one contiguous block of M/8 rows instead was measured 12%
   // slower on the prefill workload.)
-  int32_t row;
+  int32_t row, split = 0;
   if constexpr (WAVE_ROWS) {
     const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
     row = row_of_block((int32_t)blockIdx.x, (int32_t)gridDim.x, L.row_group_log2) * (int32_t)(blockDim.x >> 6) + wave;
     if (row >= L.rows) return;   // the whole wave leaves: nothing below synchronizes
   } else {
-    row = row_of_block((int32_t)blockIdx.x, L.rows, L.row_group_log2);
+    int32_t b = (int32_t)blockIdx.x;
+    if (L.splits > 1) {      // block = split * rows + row: a row's splits share an XCD when rows % 8 == 0
+      split = b / L.rows;
+      b -= split * L.rows;
+    }
+    row = row_of_block(b, L.rows, L.row_group_log2);
   }
   int pi = 0;
 #pragma unroll
@@ -121,6 +128,14 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   const int C = P.N >> 3;
   // chunk index a lane loads: clamped to the row for a ragged launch
   auto chunk = [C](int c) { return EXACT ? c : min(c, C - 1); };
+  // chunks this workgroup normalizes and stores: all of them, or with row
+  // splits a range whose ends fall on group boundaries (16 chunks FP8, 4 MXFP4)
+  int lo = 0, hi = C;
+  if (!WAVE_ROWS && L.splits > 1) {
+    constexpr int q = FMT == 0 ? 16 : FMT == 1 ? 4 : 1;
+    lo = split * (C / q) / L.splits * q;
+    hi = split + 1 == L.splits ? C : (split + 1) * (C / q) / L.splits * q;
+  }
 
   // ---- loads: x, gamma (short rows), then r, all issued before any use ---
   // (of the issue orders measured, this one was fastest on both the
@@ -200,7 +215,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = j * T + tid;
-    if (!EXACT && c >= C) continue;
+    if (!EXACT && (c < lo || c >= hi)) continue;
     u32x4 g;
     if constexpr (kShort) g = gv[j];
     else g = grow[c];

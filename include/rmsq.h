@@ -201,6 +201,14 @@ void rmsq_set_row_group(int32_t g);
  * depend on it. */
 void rmsq_set_wave_rows(int32_t R);
 
+/* Measurement hook: each row is split over S workgroups (S in 1..8; each
+ * computes the row's statistics and normalizes / quantizes its own share of
+ * the groups) for later calls in this process; 0 restores the automatic
+ * choice (the largest power of two S <= 8 with rows * S <= 256, one
+ * workgroup per compute unit, for launches of at most 128 rows; 1 above).
+ * Results do not depend on it. */
+void rmsq_set_row_splits(int32_t S);
+
 /* The launch shape the library picks (without an override) for rows of N
  * elements, the widest problem of a call, and `rows` rows in total: J chunks
  * of 8 elements per lane and W waves per workgroup (one workgroup per row).

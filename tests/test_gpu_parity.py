@@ -245,6 +245,43 @@ def test_rows_packed_one_per_wave(orc, R):
         fq.rmsq_set_row_group(0)
 
 
+@pytest.mark.parametrize("S", [2, 3, 4, 8])
+def test_rows_split_over_workgroups(orc, S):
+    """Each row split over S workgroups (every one recomputes the row's
+    statistics and handles its share of the groups): both formats, scale
+    layouts, residual or not, ragged widths whose groups do not divide
+    evenly, and two problems of different widths in one launch."""
+    try:
+        fq.rmsq_set_row_splits(S)
+        for k, (M, N, fmt, lay, res) in enumerate([(64, 7168, 0, 0, True), (5, 7168, 1, 1, True),
+                                                     (33, 1536, 0, 2, False), (7, 384, 1, 2, False),
+                                                     (3, 128, 0, 0, True), (9, 32768, 0, 0, True)]):
+            say(f"row splits S={S} M={M} N={N} fmt={fmt} layout={lay}")
+            p = inputs.make_problem(M, N, seed_x=700 + k, residual=res, outliers=True)
+            check(orc, [dict(p, fmt=fmt, scale_layout=lay, keep_bf16=(k % 2 == 0))])
+        a = inputs.make_problem(40, 1536, seed_x=710, residual=False, outliers=True)
+        b = inputs.make_problem(24, 512, seed_x=711, residual=False, outliers=True)
+        check(orc, [dict(a, fmt=0, scale_layout=2), dict(b, fmt=0, scale_layout=0, keep_bf16=True)])
+    finally:
+        fq.rmsq_set_row_splits(0)
+
+
+def test_automatic_row_splits_for_decode(orc):
+    """The decode workload (64 rows) takes the automatic split; its result is
+    the oracle's, and the same with splitting switched off."""
+    say("decode with automatic row splits")
+    p = dict(_cfg("decode"), keep_bf16=True)
+    check(orc, [p])
+    auto = run_gpu([p])[0]
+    try:
+        fq.rmsq_set_row_splits(1)
+        one = run_gpu([p])[0]
+    finally:
+        fq.rmsq_set_row_splits(0)
+    for k in auto:
+        assert np.array_equal(auto[k], one[k]), k
+
+
 # ------------------------------------------------------------ edge cases --
 def test_zero_rows_zero_groups_and_signed_zeros(orc):
     say("edge: zeros")
