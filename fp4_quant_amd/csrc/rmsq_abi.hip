@@ -327,8 +327,12 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
     // Fewer rows than compute units: split each row over several workgroups
     // (each recomputes the row's sum of squares, bit-identically, and does
     // the normalize / quantize work for its share), so every CU works.
+    // Not with an in-place residual: a split would read the residual row
+    // while another split of the same row overwrites it with h.
+    bool in_place = false;
+    for (int i = 0; i < n; ++i) in_place |= L.p[i].r != nullptr && L.p[i].r == L.p[i].h;
     L.splits = 1;
-    if (R == 1) {
+    if (R == 1 && !in_place) {
       const int fS = g_force_S.load();
       int S = 1;
       if (fS > 0) S = fS;

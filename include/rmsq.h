@@ -206,6 +206,7 @@ void rmsq_set_wave_rows(int32_t R);
  * the groups) for later calls in this process; 0 restores the automatic
  * choice (the largest power of two S <= 8 with rows * S <= 256, one
  * workgroup per compute unit, for launches of at most 128 rows; 1 above).
+ * Rows are never split when a problem's residual is updated in place.
  * Results do not depend on it. */
 void rmsq_set_row_splits(int32_t S);
 

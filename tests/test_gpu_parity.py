@@ -262,6 +262,9 @@ def test_rows_split_over_workgroups(orc, S):
         a = inputs.make_problem(40, 1536, seed_x=710, residual=False, outliers=True)
         b = inputs.make_problem(24, 512, seed_x=711, residual=False, outliers=True)
         check(orc, [dict(a, fmt=0, scale_layout=2), dict(b, fmt=0, scale_layout=0, keep_bf16=True)])
+        # an in-place residual is never split (the library keeps one workgroup per row)
+        c = inputs.make_problem(16, 7168, seed_x=712, residual=True, outliers=True)
+        check(orc, [dict(c, fmt=0, keep_bf16=True, inplace=True)])
     finally:
         fq.rmsq_set_row_splits(0)
 
