@@ -214,9 +214,11 @@ void launch_res(const rmsq::Launch& L, int J, int R, const dim3 grid, const dim3
 // workgroup, one per wave.
 template <int FMT>
 rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, int R, hipStream_t stream) {
-  const dim3 grid(R > 1 ? (unsigned)((L.rows + R - 1) / R) : (unsigned)L.rows * (unsigned)L.splits);
+  const unsigned padded = (unsigned)((L.rows + 7) / 8 * 8);   // row splits pad the rows to a multiple of 8
+  const dim3 grid(R > 1 ? (unsigned)((L.rows + R - 1) / R)
+                        : L.splits_log2 > 0 ? padded << L.splits_log2 : (unsigned)L.rows);
   const dim3 block((unsigned)(64 * (R > 1 ? R : W)));
-  bool exact = L.splits == 1;   // every row exactly fills its J*64*W (or J*64, packed) lanes
+  bool exact = L.splits_log2 == 0;   // every row exactly fills its J*64*W (or J*64, packed) lanes
   for (int i = 0; i < L.count; ++i) exact &= (L.p[i].N >> 3) == J * 64 * (R > 1 ? 1 : W);
   if (L.p[0].r) {
     if (exact) launch_res<FMT, true, true>(L, J, R, grid, block, stream);
@@ -283,7 +285,7 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
       d.ldb = p.ldb ? p.ldb : p.N;
       d.M = (int32_t)p.M;
       d.N = (int32_t)p.N;
-      d.row_begin = (int32_t)rows;
+      L.row_begin[n - 1] = (int32_t)rows;
       d.layout = p.scale_layout;
       d.eps = p.eps;
       rows += p.M;
@@ -331,18 +333,19 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
     // while another split of the same row overwrites it with h.
     bool in_place = false;
     for (int i = 0; i < n; ++i) in_place |= L.p[i].r != nullptr && L.p[i].r == L.p[i].h;
-    L.splits = 1;
+    L.splits_log2 = 0;
     if (R == 1 && !in_place) {
       const int fS = g_force_S.load();
       int S = 1;
-      if (fS > 0) S = fS;
+      if (fS > 0)
+        while (S * 2 <= fS) S *= 2;   // largest power of two <= fS
       else
         while (S < kMaxSplits && rows * S * 2 <= kComputeUnits) S *= 2;
       const int64_t q = mode == Mode::kNormOnly ? 1 : ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? 16 : 4;
       int64_t Cmin = Cmax;
       for (int i = 0; i < n; ++i) Cmin = std::min<int64_t>(Cmin, L.p[i].N / 8);
       while (S > 1 && Cmin / q < S) S /= 2;   // at least one group per split
-      L.splits = S;
+      while ((1 << L.splits_log2) < S) ++L.splits_log2;
       if (S > 1) L.row_group_log2 = 0;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -50,7 +50,6 @@ struct Problem {
   uint16_t* yb;           // bf16 side-output, or null
   int64_t ldx, ldr, ldb;  // row strides in elements
   int32_t M, N;
-  int32_t row_begin;      // first launch row of this problem
   int32_t layout;         // scale layout: 0 row-major, 1 32-row tiles (MXFP4), 2 column-major
   float eps;
 };
@@ -62,13 +61,17 @@ constexpr int kMaxWaves = 16;
 // not cut to 128 by a 1024-thread bound.
 constexpr int max_waves(int J) { return J >= 7 ? 4 : kMaxWaves; }
 
+// The launch-wide scalars come first, in one 32-byte block, so a wave reads
+// them with one scalar load and only the selected problem's fields depend on
+// it.
 struct Launch {
-  Problem p[kMaxProblems];
   int32_t count;
   int32_t rows;           // rows over all problems
   int32_t row_group_log2; // 2^k consecutive rows kept together on one XCD (0 = dispatch order)
-  int32_t splits;         // workgroups per row (>= 1): each computes the row's statistics
-                          // and normalizes / quantizes its own 1/splits of the row
+  int32_t splits_log2;    // 2^k workgroups per row: each computes the row's statistics
+                          // and normalizes / quantizes its own share of the row
+  int32_t row_begin[kMaxProblems];  // first launch row of each problem (increasing)
+  Problem p[kMaxProblems];
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
@@ -79,9 +82,10 @@ struct Launch {
 // written from a single L2 instead of being merged from several. The mapping
 // is a bijection on each block of 8*g rows; a ragged tail keeps dispatch order.
 __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t lg) {
-  if (lg == 0 || b >= (rows >> (lg + 3)) << (lg + 3)) return b;
   const int32_t x = b & 7, k = b >> 3;
-  return ((((k >> lg) << 3) + x) << lg) + (k & ((1 << lg) - 1));
+  const int32_t mapped = ((((k >> lg) << 3) + x) << lg) + (k & ((1 << lg) - 1));
+  // a select, not a branch: the launch scalars are then all needed up front
+  return (lg == 0) | (b >= (rows >> (lg + 3)) << (lg + 3)) ? b : mapped;
 }
 
 // RES: every problem of the launch has a residual (otherwise none has), so
@@ -103,26 +107,28 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   // Neighbouring row groups run on different XCDs at the same time. (Giving
   // each XCD one contiguous block of M/8 rows instead was measured 12%
   // slower on the prefill workload.)
+  const int32_t count = L.count, rows = L.rows, lg = L.row_group_log2, slg = L.splits_log2;
+  const int32_t rb1 = L.row_begin[1], rb2 = L.row_begin[2], rb3 = L.row_begin[3];
   int32_t row, split = 0;
   if constexpr (WAVE_ROWS) {
     const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
-    row = row_of_block((int32_t)blockIdx.x, (int32_t)gridDim.x, L.row_group_log2) * (int32_t)(blockDim.x >> 6) + wave;
-    if (row >= L.rows) return;   // the whole wave leaves: nothing below synchronizes
+    row = row_of_block((int32_t)blockIdx.x, (int32_t)gridDim.x, lg) * (int32_t)(blockDim.x >> 6) + wave;
+    if (row >= rows) return;   // the whole wave leaves: nothing below synchronizes
   } else {
-    int32_t b = (int32_t)blockIdx.x;
-    if (L.splits > 1) {      // block = split * rows + row: a row's splits share an XCD when rows % 8 == 0
-      split = b / L.rows;
-      b -= split * L.rows;
-    }
-    row = row_of_block(b, L.rows, L.row_group_log2);
+    // Row splits (slg > 0): blocks in runs of 8 rows x 2^slg splits, block =
+    // (row / 8) * 8 * 2^slg + split * 8 + row % 8, so a row's splits share an
+    // XCD (block % 8) and its L2 serves their repeated reads of the row. Rows
+    // are padded to a multiple of 8; padding blocks leave at once. Without
+    // splits the host may group rows per XCD (lg > 0); the two are exclusive.
+    const int32_t b = (int32_t)blockIdx.x;
+    split = slg > 0 ? (b >> 3) & ((1 << slg) - 1) : 0;
+    row = slg > 0 ? ((b >> (3 + slg)) << 3) | (b & 7) : row_of_block(b, rows, lg);
+    if (row >= rows) return;   // the whole workgroup leaves before any barrier
   }
-  int pi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxProblems; ++i)
-    if (i < L.count && row >= L.p[i].row_begin) pi = i;
+  // problems are consecutive ranges of rows (row_begin increasing)
+  const int pi = (count > 1 && row >= rb1) + (count > 2 && row >= rb2) + (count > 3 && row >= rb3);
   const Problem& P = L.p[pi];
-
-  const int64_t m = row - P.row_begin;
+  const int64_t m = row - L.row_begin[pi];
   const int T = WAVE_ROWS ? 64 : blockDim.x;
   const int tid = WAVE_ROWS ? (threadIdx.x & 63) : threadIdx.x;
   const int C = P.N >> 3;
@@ -131,10 +137,10 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   // chunks this workgroup normalizes and stores: all of them, or with row
   // splits a range whose ends fall on group boundaries (16 chunks FP8, 4 MXFP4)
   int lo = 0, hi = C;
-  if (!WAVE_ROWS && L.splits > 1) {
+  if (!WAVE_ROWS && slg > 0) {
     constexpr int q = FMT == 0 ? 16 : FMT == 1 ? 4 : 1;
-    lo = split * (C / q) / L.splits * q;
-    hi = split + 1 == L.splits ? C : (split + 1) * (C / q) / L.splits * q;
+    lo = ((split * (C / q)) >> slg) * q;
+    hi = split + 1 == (1 << slg) ? C : (((split + 1) * (C / q)) >> slg) * q;
   }
 
   // ---- loads: x, gamma (short rows), then r, all issued before any use ---

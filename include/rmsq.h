@@ -201,7 +201,8 @@ void rmsq_set_row_group(int32_t g);
  * depend on it. */
 void rmsq_set_wave_rows(int32_t R);
 
-/* Measurement hook: each row is split over S workgroups (S in 1..8; each
+/* Measurement hook: each row is split over S workgroups (S in 1..8, rounded
+ * down to a power of two; each
  * computes the row's statistics and normalizes / quantizes its own share of
  * the groups) for later calls in this process; 0 restores the automatic
  * choice (the largest power of two S <= 8 with rows * S <= 256, one

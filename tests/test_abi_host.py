@@ -184,6 +184,37 @@ def test_row_grouping_is_a_bijection():
             assert sorted(row_of_block(b, rows, g) for b in range(rows)) == list(range(rows)), (g, rows)
 
 
+def test_row_split_block_mapping_is_a_bijection():
+    """With 2^slg workgroups per row, block b -> (row, split) as the kernel
+    computes it covers every (row, split) of the padded rows exactly once,
+    keeps a row's splits on one XCD (b % 8), and the chunk ranges of a row's
+    splits partition the row on group boundaries."""
+    for slg in (1, 2, 3):
+        S = 1 << slg
+        for rows in (1, 7, 8, 9, 33, 64, 100, 128):
+            padded = (rows + 7) // 8 * 8
+            seen = {}
+            for b in range(padded * S):
+                split = (b >> 3) & (S - 1)
+                row = ((b >> (3 + slg)) << 3) | (b & 7)
+                assert (row, split) not in seen
+                seen[(row, split)] = b
+            assert set(seen) == {(r, k) for r in range(padded) for k in range(S)}
+            for r in range(rows):
+                assert len({seen[(r, k)] % 8 for k in range(S)}) == 1
+        for C, q in ((896, 16), (192, 16), (64, 16), (16, 16), (896, 4), (12, 4), (48, 1)):
+            if C // q < S:
+                continue
+            bounds = []
+            for k in range(S):
+                lo = ((k * (C // q)) >> slg) * q
+                hi = C if k + 1 == S else (((k + 1) * (C // q)) >> slg) * q
+                assert lo % q == 0 and hi % q == 0 or hi == C
+                bounds.append((lo, hi))
+            assert bounds[0][0] == 0 and bounds[-1][1] == C
+            assert all(bounds[k][1] == bounds[k + 1][0] and bounds[k][0] < bounds[k][1] for k in range(S - 1))
+
+
 def test_launch_shape_always_fits():
     """For every N the library accepts, the chosen shape covers the row with a
     legal workgroup (long per-lane rows use at most 4 waves)."""
