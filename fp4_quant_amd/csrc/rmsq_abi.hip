@@ -185,27 +185,32 @@ void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
   *W_out = rmsq::kMaxWaves;
 }
 
+// The fused kernel's arguments: the launch scalars (preloaded into SGPRs),
+// then the launch description.
+#define RMSQ_LAUNCH_ARGS(L) \
+  (L).count, (L).rows, (L).row_group_log2, (L).splits_log2, (L).row_begin[1], (L).row_begin[2], (L).row_begin[3], (L)
+
 // EXACT is used for J <= 4 only: the long per-lane shapes (very wide rows)
 // keep their bounds, which also keeps them within the register budget.
 template <int FMT, bool RES, bool EXACT>
 void launch_res(const rmsq::Launch& L, int J, int R, const dim3 grid, const dim3 block, hipStream_t stream) {
   if (R > 1) {   // one row per wave, R rows per workgroup (J <= 4 only)
     switch (J) {
-      case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, true, EXACT>), grid, block, 0, stream, L); break;
-      case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, true, EXACT>), grid, block, 0, stream, L); break;
-      case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, true, EXACT>), grid, block, 0, stream, L); break;
-      default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, true, EXACT>), grid, block, 0, stream, L); break;
+      case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, true, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, true, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, true, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, true, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
     }
     return;
   }
   switch (J) {
-    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES, false, false>), grid, block, 0, stream, L); break;
-    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES, false, false>), grid, block, 0, stream, L); break;
-    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES, false, false>), grid, block, 0, stream, L); break;
-    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, false, EXACT>), grid, block, 0, stream, L); break;
-    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, false, EXACT>), grid, block, 0, stream, L); break;
-    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, false, EXACT>), grid, block, 0, stream, L); break;
-    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, false, EXACT>), grid, block, 0, stream, L); break;
+    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES, false, false>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES, false, false>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES, false, false>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, false, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, false, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, false, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, false, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
   }
 }
 

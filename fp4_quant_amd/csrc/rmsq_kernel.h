@@ -61,9 +61,10 @@ constexpr int kMaxWaves = 16;
 // not cut to 128 by a 1024-thread bound.
 constexpr int max_waves(int J) { return J >= 7 ? 4 : kMaxWaves; }
 
-// The launch-wide scalars come first, in one 32-byte block, so a wave reads
-// them with one scalar load and only the selected problem's fields depend on
-// it.
+// Launch description. The scalars are also passed as the kernel's leading
+// int arguments, which the library is built to have preloaded into SGPRs at
+// wave launch (gfx950 kernel-argument preloading), so only the selected
+// problem's fields are read from the argument block.
 struct Launch {
   int32_t count;
   int32_t rows;           // rows over all problems
@@ -97,7 +98,9 @@ __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t
 // and is not split, so no lane needs a bound (the usual shapes: 7168 = 2 x 7 waves or 1 x 14,
 // 1536 = 3 x 1, 512 = 1 x 1).
 template <int FMT, int J, bool RES, bool WAVE_ROWS, bool EXACT>
-__global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Launch L) {
+__global__ void __launch_bounds__(64 * max_waves(J))
+rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t rb1, int32_t rb2, int32_t rb3,
+                  const Launch L) {   // the ints repeat L's scalars (count, rows, row_group_log2, splits_log2, row_begin[1..3])
   // Short per-lane rows (the usual shapes) keep h as fp32 and fetch gamma
   // together with x and r; long ones keep h packed and fetch gamma late, to
   // stay within the register budget.
@@ -107,8 +110,6 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   // Neighbouring row groups run on different XCDs at the same time. (Giving
   // each XCD one contiguous block of M/8 rows instead was measured 12%
   // slower on the prefill workload.)
-  const int32_t count = L.count, rows = L.rows, lg = L.row_group_log2, slg = L.splits_log2;
-  const int32_t rb1 = L.row_begin[1], rb2 = L.row_begin[2], rb3 = L.row_begin[3];
   int32_t row, split = 0;
   if constexpr (WAVE_ROWS) {
     const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
@@ -128,7 +129,7 @@ __global__ void __launch_bounds__(64 * max_waves(J)) rmsq_fused_kernel(const Lau
   // problems are consecutive ranges of rows (row_begin increasing)
   const int pi = (count > 1 && row >= rb1) + (count > 2 && row >= rb2) + (count > 3 && row >= rb3);
   const Problem& P = L.p[pi];
-  const int64_t m = row - L.row_begin[pi];
+  const int64_t m = row - (pi == 0 ? 0 : pi == 1 ? rb1 : pi == 2 ? rb2 : rb3);
   const int T = WAVE_ROWS ? 64 : blockDim.x;
   const int tid = WAVE_ROWS ? (threadIdx.x & 63) : threadIdx.x;
   const int C = P.N >> 3;

@@ -20,7 +20,7 @@ import pytest
 
 from fp4_quant_amd import build as B
 
-NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)ELb(\d)EEEvNS_6LaunchE$")
+NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)ELb(\d)EEEviiiiiiiNS_6LaunchE$")
 
 
 @pytest.fixture(scope="module")
@@ -41,6 +41,11 @@ def kernels():
         ks[field("name")] = {k: int(field(k) or 0) for k in
                              ("vgpr_count", "agpr_count", "sgpr_count", "vgpr_spill_count", "sgpr_spill_count",
                               "private_segment_fixed_size", "group_segment_fixed_size")}
+    # kernel descriptors (.amdhsa_kernel blocks) carry the preload length
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.S):
+        pl = re.search(r"\.amdhsa_user_sgpr_kernarg_preload_length (\d+)", m.group(2))
+        if m.group(1) in ks:
+            ks[m.group(1)]["kernarg_preload"] = int(pl.group(1)) if pl else 0
     return ks
 
 
@@ -50,6 +55,13 @@ def test_every_kernel_variant_is_present(kernels):
     # the 4 short shapes and 4 packed-row shapes also for rows that exactly fill the launch
     assert len(fused) == 3 * 2 * (7 + 4 + 4 + 4), sorted(fused)
     assert sum(1 for n in kernels if "rmsq_group_quant_kernel" in (n or "")) == 2
+
+
+def test_launch_scalars_are_preloaded(kernels):
+    """The fused kernels' seven leading int arguments are preloaded into
+    SGPRs (gfx950 kernel-argument preloading)."""
+    fused = [n for n in kernels if NAME.match(n or "")]
+    assert fused and all(kernels[n]["kernarg_preload"] == 7 for n in fused)
 
 
 def test_no_spills_and_no_scratch(kernels):
