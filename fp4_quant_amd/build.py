@@ -17,10 +17,10 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     # lane flags are combined with bitwise | on purpose: no short-circuit branches
     "-Wno-bitwise-instead-of-logical",
-    # the fused kernel's 7 leading int arguments arrive preloaded in SGPRs
+    # the fused kernel's 9 leading int arguments arrive preloaded in SGPRs
     # (the code object keeps a fallback that loads them when the firmware
     # does not preload)
-    "-mllvm", "-amdgpu-kernarg-preload-count=7",
+    "-mllvm", "-amdgpu-kernarg-preload-count=9",
 ]
 
 

@@ -187,8 +187,9 @@ void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
 
 // The fused kernel's arguments: the launch scalars (preloaded into SGPRs),
 // then the launch description.
-#define RMSQ_LAUNCH_ARGS(L) \
-  (L).count, (L).rows, (L).row_group_log2, (L).splits_log2, (L).row_begin[1], (L).row_begin[2], (L).row_begin[3], (L)
+#define RMSQ_LAUNCH_ARGS(L)                                                                                  \
+  (L).count, (L).rows, (L).row_group_log2, (L).splits_log2, (L).row_begin[1], (L).row_begin[2], (L).row_begin[3], \
+      (int32_t)block.x, (int32_t)grid.x, (L)
 
 // EXACT is used for J <= 4 only: the long per-lane shapes (very wide rows)
 // keep their bounds, which also keeps them within the register budget.

@@ -41,15 +41,18 @@
 namespace rmsq {
 
 struct Problem {
+  // what the loads need, first (one 48-byte run)
   const uint16_t* x;
-  const uint16_t* r;      // residual in, or null
-  uint16_t* h;            // residual out (null exactly when r is null)
   const uint16_t* gamma;
+  const uint16_t* r;      // residual in, or null
+  int64_t ldx, ldr;       // row strides in elements
+  int32_t N, M;
+  // the rest
+  uint16_t* h;            // residual out (null exactly when r is null)
   uint8_t* q;
   void* scale;
   uint16_t* yb;           // bf16 side-output, or null
-  int64_t ldx, ldr, ldb;  // row strides in elements
-  int32_t M, N;
+  int64_t ldb;
   int32_t layout;         // scale layout: 0 row-major, 1 32-row tiles (MXFP4), 2 column-major
   float eps;
 };
@@ -100,7 +103,9 @@ __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t
 template <int FMT, int J, bool RES, bool WAVE_ROWS, bool EXACT>
 __global__ void __launch_bounds__(64 * max_waves(J))
 rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t rb1, int32_t rb2, int32_t rb3,
-                  const Launch L) {   // the ints repeat L's scalars (count, rows, row_group_log2, splits_log2, row_begin[1..3])
+                  int32_t threads, int32_t blocks, const Launch L) {
+  // the ints repeat L's scalars (count, rows, row_group_log2, splits_log2,
+  // row_begin[1..3]) and the launch's blockDim.x and gridDim.x
   // Short per-lane rows (the usual shapes) keep h as fp32 and fetch gamma
   // together with x and r; long ones keep h packed and fetch gamma late, to
   // stay within the register budget.
@@ -113,7 +118,7 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   int32_t row, split = 0;
   if constexpr (WAVE_ROWS) {
     const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
-    row = row_of_block((int32_t)blockIdx.x, (int32_t)gridDim.x, lg) * (int32_t)(blockDim.x >> 6) + wave;
+    row = row_of_block((int32_t)blockIdx.x, blocks, lg) * (threads >> 6) + wave;
     if (row >= rows) return;   // the whole wave leaves: nothing below synchronizes
   } else {
     // Row splits (slg > 0): blocks in runs of 8 rows x 2^slg splits, block =
@@ -130,7 +135,7 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   const int pi = (count > 1 && row >= rb1) + (count > 2 && row >= rb2) + (count > 3 && row >= rb3);
   const Problem& P = L.p[pi];
   const int64_t m = row - (pi == 0 ? 0 : pi == 1 ? rb1 : pi == 2 ? rb2 : rb3);
-  const int T = WAVE_ROWS ? 64 : blockDim.x;
+  const int T = WAVE_ROWS ? 64 : threads;
   const int tid = WAVE_ROWS ? (threadIdx.x & 63) : threadIdx.x;
   const int C = P.N >> 3;
   // chunk index a lane loads: clamped to the row for a ragged launch

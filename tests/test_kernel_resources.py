@@ -20,7 +20,7 @@ import pytest
 
 from fp4_quant_amd import build as B
 
-NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)ELb(\d)EEEviiiiiiiNS_6LaunchE$")
+NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)ELb(\d)EEEviiiiiiiiiNS_6LaunchE$")
 
 
 @pytest.fixture(scope="module")
@@ -58,10 +58,10 @@ def test_every_kernel_variant_is_present(kernels):
 
 
 def test_launch_scalars_are_preloaded(kernels):
-    """The fused kernels' seven leading int arguments are preloaded into
+    """The fused kernels' nine leading int arguments are preloaded into
     SGPRs (gfx950 kernel-argument preloading)."""
     fused = [n for n in kernels if NAME.match(n or "")]
-    assert fused and all(kernels[n]["kernarg_preload"] == 7 for n in fused)
+    assert fused and all(kernels[n]["kernarg_preload"] == 9 for n in fused)
 
 
 def test_no_spills_and_no_scratch(kernels):
