@@ -54,6 +54,8 @@ def _bind(L):
     L.oracle_rmsnorm_quant_group.restype = C.c_int
     L.oracle_rmsnorm_quant_group.argtypes = [_p, _i64, _p, _i64, _p, C.c_float, _i64, _i64,
                                              _i32, _i32, _i32, _p, _p, _p, _p, _i64]
+    L.oracle_gemm_a16wfp4_prequant.restype = C.c_int
+    L.oracle_gemm_a16wfp4_prequant.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _i64]
     L.oracle_num_threads.restype = C.c_int
     L.oracle_num_threads.argtypes = []
     return L
@@ -173,6 +175,23 @@ class Oracle:
                                    M, N, _ptr(h), N, _ptr(yb), N)
         return h, yb
 
+    def gemm_a16wfp4_prequant(self, a, w, w_scale):
+        """A16WFP4 prequant GEMM: a [M, K] uint16 (bf16 bits, row stride may
+        exceed K), w [N, K/2] uint8 e2m1 codes, w_scale [N, K/32] uint8 e8m0.
+        Returns C [M, N] float64."""
+        M, K = a.shape
+        assert a.strides[1] == 2 and a.dtype == np.uint16
+        N = w.shape[0]
+        assert w.shape == (N, K // 2) and w_scale.shape == (N, K // 32)
+        w = np.ascontiguousarray(w, dtype=np.uint8)
+        w_scale = np.ascontiguousarray(w_scale, dtype=np.uint8)
+        out = np.zeros((M, N), np.float64)
+        rc = self._L.oracle_gemm_a16wfp4_prequant(_ptr(a), a.strides[0] // 2, _ptr(w), _ptr(w_scale), M, N, K,
+                                                  _ptr(out), N)
+        if rc != 0:
+            raise ValueError("oracle: arguments outside the defined operation")
+        return out
+
     def group_quant(self, yb, group=128, fmt=FMT_FP8, scale_layout=LAYOUT_ROW, scale_fill=0):
         """Stage 2 alone on bf16 rows: returns (q, scale)."""
         yb = np.ascontiguousarray(yb, dtype=np.uint16)
@@ -236,6 +255,10 @@ def rmsnorm_quant_group(*a, **k):
 
 def add_rmsnorm(*a, **k):
     return default().add_rmsnorm(*a, **k)
+
+
+def gemm_a16wfp4_prequant(*a, **k):
+    return default().gemm_a16wfp4_prequant(*a, **k)
 
 
 def group_quant(*a, **k):

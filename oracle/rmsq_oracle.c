@@ -388,6 +388,62 @@ int oracle_rmsnorm_quant_group(const uint16_t* x, int64_t ldx,
     return 0;
 }
 
+/*
+ * A16WFP4 "prequant" GEMM ([ATT], the AITER pull requests it lists: a GEMM of
+ * bf16 activations with FP4 weights that quantizes the activations inside
+ * the GEMM; [ATT, run notes]: the path used at concurrency 4). The pages name
+ * the kernel only; READING: the activation rows are quantized exactly as the
+ * MXFP4 group quantization above (1x32 groups along K, e8m0 scale from the
+ * group amax, e2m1 codes), the weights come as e2m1 codes [N, K/2] (element
+ * 2k of a row in the low nibble) with e8m0 scales [N, K/32], and
+ *   C[m][n] = sum_k (qa[m][k] * 2^(ea[m][k/32] - 127)) * (qw[n][k] * 2^(ew[n][k/32] - 127)),
+ * accumulated here in double in k order.
+ */
+static double e8m0_value(uint8_t byte)
+{
+    return ldexp(1.0, (int)byte - 127);
+}
+
+int oracle_gemm_a16wfp4_prequant(const uint16_t* a, int64_t lda,
+                                 const uint8_t* w, const uint8_t* w_scale,
+                                 int64_t M, int64_t N, int64_t K,
+                                 double* out, int64_t ldc)
+{
+    if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || lda < K || ldc < N)
+        return -1;
+    if (fegetround() != FE_TONEAREST)
+        return -1;
+#pragma omp parallel
+    {
+        uint8_t* qa = (uint8_t*)malloc((size_t)K / 2);
+        uint8_t* ea = (uint8_t*)malloc((size_t)K / 32);
+        double* da = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            /* the activation row's MXFP4 quantization, then its values */
+            group_quant_row(a + m * lda, 0, 1, K, 32, 1, 0, qa, ea);
+            for (int64_t k = 0; k < K; ++k) {
+                uint8_t code = (uint8_t)((qa[k / 2] >> (4 * (k % 2))) & 0xF);
+                da[k] = oracle_e2m1_decode(code) * e8m0_value(ea[k / 32]);
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                const uint8_t* wr = w + n * (K / 2);
+                const uint8_t* sr = w_scale + n * (K / 32);
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    uint8_t code = (uint8_t)((wr[k / 2] >> (4 * (k % 2))) & 0xF);
+                    acc += da[k] * (oracle_e2m1_decode(code) * e8m0_value(sr[k / 32]));
+                }
+                out[m * ldc + n] = acc;
+            }
+        }
+        free(da);
+        free(ea);
+        free(qa);
+    }
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

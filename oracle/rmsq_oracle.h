@@ -63,6 +63,17 @@ int oracle_rmsnorm_quant_group(const uint16_t* x, int64_t ldx,
                                uint16_t* residual_out,
                                uint16_t* out_bf16, int64_t ldb);
 
+/* A16WFP4 prequant GEMM: a [M, K] bf16 (row stride lda) quantized to MXFP4
+ * per 1x32 group along K as oracle_group_quant does, times the MXFP4 weights
+ * w [N, K/2] codes (element 2k in the low nibble) with e8m0 scales
+ * w_scale [N, K/32]: out[m*ldc + n] = sum over k of the dequantized products,
+ * in double. Returns 0, or -1 for arguments it does not define (K a positive
+ * multiple of 32). */
+int oracle_gemm_a16wfp4_prequant(const uint16_t* a, int64_t lda,
+                                 const uint8_t* w, const uint8_t* w_scale,
+                                 int64_t M, int64_t N, int64_t K,
+                                 double* out, int64_t ldc);
+
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

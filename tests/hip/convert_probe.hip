@@ -112,6 +112,27 @@ __global__ void k_cvt_fp8_bf16_scaled(const uint32_t* pairs, const float* scale,
   }
 }
 
+// One v_mfma_scale_f32_16x16x128_f8f6f4 with e2m1 A and B per wave, on raw
+// lane registers from the host: wave w reads a, b [w][lane][4 dwords], the
+// e8m0 scale registers sa, sb [w][lane] and writes d [w][lane][4]. One wave
+// per 64-thread block; the tests pin the operand and result layouts.
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+__global__ void k_mfma_scale_fp4(const uint32_t* a, const uint32_t* b, const uint32_t* sa, const uint32_t* sb, float* d,
+                                 int64_t waves) {
+  const int64_t w = blockIdx.x;
+  if (w >= waves) return;
+  const int l = threadIdx.x;
+  const int64_t o = (w * 64 + l) * 4;
+  v8i_t av = {(int)a[o], (int)a[o + 1], (int)a[o + 2], (int)a[o + 3], 0, 0, 0, 0};
+  v8i_t bv = {(int)b[o], (int)b[o + 1], (int)b[o + 2], (int)b[o + 3], 0, 0, 0, 0};
+  const v4f_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+  const v4f_t r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa[w * 64 + l], 0,
+                                                                 (int)sb[w * 64 + l]);
+  for (int i = 0; i < 4; ++i) d[o + i] = r[i];
+}
+
 static int launch_status() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 
 #define GRID(n) dim3((unsigned)(((n) + 255) / 256 < 65536 ? ((n) + 255) / 256 : 65536)), dim3(256), 0, (hipStream_t)stream
@@ -176,6 +197,12 @@ int probe_cvt_fp4_bf16_scaled(const uint32_t* pairs, const float* scale, uint8_t
 int probe_cvt_fp8_bf16_scaled(const uint32_t* pairs, const float* scale, uint16_t* out, int64_t n, void* stream) {
   if (n <= 0) return 0;
   hipLaunchKernelGGL(k_cvt_fp8_bf16_scaled, GRID(n), pairs, scale, out, n);
+  return launch_status();
+}
+int probe_mfma_scale_fp4(const uint32_t* a, const uint32_t* b, const uint32_t* sa, const uint32_t* sb, float* d,
+                         int64_t waves, void* stream) {
+  if (waves <= 0) return 0;
+  hipLaunchKernelGGL(k_mfma_scale_fp4, dim3((unsigned)waves), dim3(64), 0, (hipStream_t)stream, a, b, sa, sb, d, waves);
   return launch_status();
 }
 int probe_fp8_exact(const float* v, const float* s, uint8_t* out, int64_t n, void* stream) {

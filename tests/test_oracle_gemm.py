@@ -1,0 +1,105 @@
+"""Pins for the oracle's A16WFP4 prequant GEMM (CPU only).
+
+The expected values come from the definitions, not from the oracle: the e2m1
+grid and the e8m0 scale are written out here, numpy's matmul does the
+contraction, and the activation quantization is either avoided (inputs that
+MXFP4 represents exactly, so quantizing is the identity) or taken from the
+oracle's group quantization, which test_oracle_codecs and
+test_oracle_pipeline pin on their own.
+"""
+import numpy as np
+import pytest
+
+from fp4_quant_amd import inputs
+
+E2M1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6])
+
+
+def bf16_to_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def dequant_rows(codes, scales):
+    """[R, K/2] e2m1 codes (element 2k low nibble) and [R, K/32] e8m0 bytes -> [R, K] float64."""
+    lo, hi = codes & 0xF, codes >> 4
+    q = np.stack([E2M1[lo], E2M1[hi]], -1).reshape(codes.shape[0], -1)
+    return q * np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+
+
+def random_weights(N, K, seed):
+    rng = np.random.default_rng(seed)
+    w = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    ws = rng.integers(118, 134, (N, K // 32)).astype(np.uint8)
+    return w, ws
+
+
+def test_hand_example(orc):
+    # 32 ones then 32 twos: group scales 2^-2 and 2^-1, codes 4.0 -> exact; weights all 1.0
+    a = np.array([[0x3F80] * 32 + [0x4000] * 32], np.uint16)
+    w = np.full((2, 32), 0x22, np.uint8)
+    ws = np.full((2, 2), 127, np.uint8)
+    assert orc.gemm_a16wfp4_prequant(a, w, ws).tolist() == [[96.0, 96.0]]
+    ws[1, 1] = 128                                   # second weight row's second group scaled by 2
+    assert orc.gemm_a16wfp4_prequant(a, w, ws).tolist() == [[96.0, 32.0 + 128.0]]
+
+
+def test_lossless_activations_match_numpy_matmul(orc):
+    """Activations built from e2m1 codes times a power of two per 32-group,
+    with a largest code of 4 or 6 in every group, are exactly MXFP4 values
+    (the scale rule picks the same power of two), so the GEMM is
+    A @ dequant(W)^T, computed here by numpy."""
+    rng = np.random.default_rng(5)
+    M, N, K = 7, 9, 256
+    codes = rng.integers(0, 16, (M, K))
+    codes[:, ::32] = rng.choice([6, 7, 14, 15], (M, K // 32))   # the group max: 4 or 6 in magnitude
+    e = rng.integers(-20, 20, (M, K // 32))
+    A = E2M1[codes] * np.repeat(np.ldexp(1.0, e), 32, axis=1)
+    a = inputs.to_bf16_bits(A.astype(np.float32))
+    assert np.array_equal(bf16_to_f32(a).astype(np.float64), A)
+    w, ws = random_weights(N, K, 6)
+    want = A @ dequant_rows(w, ws).T
+    got = orc.gemm_a16wfp4_prequant(a, w, ws)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+def test_equals_its_own_quantization_times_the_weights(orc):
+    """On general bf16 rows the GEMM equals (the activations' MXFP4 group
+    quantization, dequantized) @ dequant(W)^T."""
+    p = inputs.make_problem(5, 512, seed_x=30, residual=False, outliers=True)
+    w, ws = random_weights(11, 512, 7)
+    qa, sa = orc.group_quant(p["x"], 32, 1, 0)
+    want = dequant_rows(qa, sa) @ dequant_rows(w, ws).T
+    got = orc.gemm_a16wfp4_prequant(p["x"], w, ws)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("k", [-7, 3])
+def test_power_of_two_scaling(orc, k):
+    """Scaling the activations by 2^k scales every output by 2^k exactly (the
+    group scales absorb it); raising every weight scale byte by k does too."""
+    p = inputs.make_problem(3, 256, seed_x=31, residual=False, outliers=True)
+    w, ws = random_weights(4, 256, 8)
+    base = orc.gemm_a16wfp4_prequant(p["x"], w, ws)
+    xs = inputs.to_bf16_bits(bf16_to_f32(p["x"]) * np.float32(2.0 ** k))
+    assert np.array_equal(orc.gemm_a16wfp4_prequant(xs, w, ws), base * 2.0 ** k)
+    assert np.array_equal(orc.gemm_a16wfp4_prequant(p["x"], w, (ws.astype(int) + k).astype(np.uint8)),
+                          base * 2.0 ** k)
+
+
+def test_strided_rows_and_zero_rows(orc):
+    p = inputs.make_problem(4, 256, seed_x=32, residual=False, outliers=False)
+    w, ws = random_weights(5, 256, 9)
+    wide = np.zeros((4, 384), np.uint16)
+    wide[:, :256] = p["x"]
+    wide[1, :256] = 0                                # an all-zero row: scale byte 127, codes 0
+    x = p["x"].copy()
+    x[1] = 0
+    got = orc.gemm_a16wfp4_prequant(wide[:, :256], w, ws)
+    assert np.array_equal(got, orc.gemm_a16wfp4_prequant(x, w, ws))
+    assert np.all(got[1] == 0)
+
+
+def test_rejects_undefined_shapes(orc):
+    a = np.zeros((2, 48), np.uint16)
+    with pytest.raises((ValueError, AssertionError)):
+        orc.gemm_a16wfp4_prequant(a, np.zeros((3, 24), np.uint8), np.zeros((3, 1), np.uint8))

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_codecs as TC
+from tests import test_oracle_gemm as TG
 from tests import test_oracle_pipeline as TP
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "rmsq_oracle.c")
@@ -46,6 +47,12 @@ MUTANTS = {
     "nibbles swapped": ("(uint8_t)(lo | (hi << 4))", "(uint8_t)(hi | (lo << 4))"),
     "tiled scale offset transposed": ("+ g * 32 + (m % 32);", "+ (m % 32) * groups_per_row + g;"),
     "column-major scales stored row-major": ("return g * M + m;", "return m * G + g;"),
+    "GEMM weight nibbles swapped": ("uint8_t code = (uint8_t)((wr[k / 2] >> (4 * (k % 2))) & 0xF);",
+                                    "uint8_t code = (uint8_t)((wr[k / 2] >> (4 * (1 - k % 2))) & 0xF);"),
+    "GEMM e8m0 bias 126": ("return ldexp(1.0, (int)byte - 127);", "return ldexp(1.0, (int)byte - 126);"),
+    "GEMM activation scale dropped": ("da[k] = oracle_e2m1_decode(code) * e8m0_value(ea[k / 32]);",
+                                      "da[k] = oracle_e2m1_decode(code);"),
+    "GEMM weight scale per 16": ("e8m0_value(sr[k / 32])", "e8m0_value(sr[(k / 16) % (K / 32)])"),
 }
 
 
@@ -66,6 +73,9 @@ def _pins():
     p += [functools.partial(TP.test_fp8_matches_exact_rational_reference, seed=0, residual=r) for r in (False, True)]
     p.append(functools.partial(TP.test_mxfp4_matches_exact_rational_reference, seed=0))
     p += [functools.partial(TC.test_e4m3fn_encode_every_bf16_by_brute_force, scale=s) for s in (1.0, 2.0 ** -7)]
+    p += [TG.test_hand_example, TG.test_lossless_activations_match_numpy_matmul,
+          TG.test_equals_its_own_quantization_times_the_weights]
+    p += [functools.partial(TG.test_power_of_two_scaling, k=k) for k in (-7, 3)]
     return p
 
 
