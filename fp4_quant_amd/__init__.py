@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(HERE, "librmsq.so")
 RMSQ_OK, RMSQ_ERR_INVALID_ARG, RMSQ_ERR_UNSUPPORTED, RMSQ_ERR_HIP = 0, 1, 2, 3
 FMT_FP8_E4M3FN, FMT_MXFP4_E2M1 = 0, 1
 SCALE_ROW_MAJOR, SCALE_TILED32, SCALE_COL_MAJOR = 0, 1, 2
+W_ROW_MAJOR, W_PRESHUFFLED = 0, 1
 MAX_PROBLEMS = 4
 N_MAX = 32768
 _FMT = {"fp8": FMT_FP8_E4M3FN, "mxfp4": FMT_MXFP4_E2M1}
@@ -57,7 +58,8 @@ class rmsq_problem(C.Structure):
 EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "add_rmsnorm",
            "dynamic_per_group_scaled_quant", "rmsq_device_supported",
            "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape",
-           "rmsq_query_shape", "rmsq_set_row_group", "rmsq_set_wave_rows", "rmsq_set_row_splits")
+           "rmsq_query_shape", "rmsq_set_row_group", "rmsq_set_wave_rows", "rmsq_set_row_splits",
+           "gemm_a16wfp4_prequant", "mxfp4_weight_preshuffle")
 
 _lib = None
 
@@ -97,6 +99,10 @@ def lib() -> C.CDLL:
         L.rmsq_set_row_splits.argtypes = [i32]
         L.rmsq_query_shape.restype = i32
         L.rmsq_query_shape.argtypes = [i64, i64, C.POINTER(i32), C.POINTER(i32)]
+        L.gemm_a16wfp4_prequant.restype = i32
+        L.gemm_a16wfp4_prequant.argtypes = [p, i64, p, p, i32, i64, i64, i64, p, i64, p]
+        L.mxfp4_weight_preshuffle.restype = i32
+        L.mxfp4_weight_preshuffle.argtypes = [p, p, i64, i64, p, p, p]
         _lib = L
     return _lib
 
@@ -168,6 +174,20 @@ def dynamic_per_group_scaled_quant(x, M, N, group, fmt, scale_layout, out_q, out
     _check(lib().dynamic_per_group_scaled_quant(_ptr(x), int(M), int(N), int(group), int(fmt),
                                                 int(scale_layout), _ptr(out_q), _ptr(out_scale),
                                                 _stream(stream, x.device if x is not None else None)))
+
+
+def gemm_a16wfp4_prequant(a, lda, w, w_scale, w_layout, M, N, K, out, ldc, stream=None) -> None:
+    """The A16WFP4 prequant GEMM (bf16 activations quantized to MXFP4 inside
+    the GEMM, MXFP4 weights, fp32 output), C argument order."""
+    _check(lib().gemm_a16wfp4_prequant(_ptr(a), int(lda), _ptr(w), _ptr(w_scale), int(w_layout), int(M), int(N),
+                                       int(K), _ptr(out), int(ldc),
+                                       _stream(stream, a.device if a is not None else None)))
+
+
+def mxfp4_weight_preshuffle(w, w_scale, N, K, w_out, w_scale_out, stream=None) -> None:
+    """Row-major MXFP4 weights to the preshuffled layout, C argument order."""
+    _check(lib().mxfp4_weight_preshuffle(_ptr(w), _ptr(w_scale), int(N), int(K), _ptr(w_out), _ptr(w_scale_out),
+                                         _stream(stream, w.device if w is not None else None)))
 
 
 def rmsq_device_supported(device: int = 0) -> bool:

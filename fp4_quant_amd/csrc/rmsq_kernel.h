@@ -89,7 +89,7 @@ __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t
   const int32_t x = b & 7, k = b >> 3;
   const int32_t mapped = ((((k >> lg) << 3) + x) << lg) + (k & ((1 << lg) - 1));
   // a select, not a branch: the launch scalars are then all needed up front
-  return (lg == 0) | (b >= (rows >> (lg + 3)) << (lg + 3)) ? b : mapped;
+  return ((lg == 0) | (b >= (rows >> (lg + 3)) << (lg + 3))) ? b : mapped;
 }
 
 // RES: every problem of the launch has a residual (otherwise none has), so

@@ -14,6 +14,13 @@ latents of 1536 and 512):
 * gamma ~ U(0.5, 1.5), seed ``seed_x + 2``.
 * every value rounded to bf16 by ``torch.Tensor.to(torch.bfloat16)``.
 
+The A16WFP4 GEMM (``make_gemm``) takes activations drawn as x above (seed
+``seed``, with the outlier channels) and random MXFP4 weights: code bytes
+uniform over 0..255 (two e2m1 codes each, seed ``seed + 1``) and e8m0 scale
+bytes uniform over 116..123 (seed ``seed + 2``), the scales of 1x32 groups of
+N(0, 0.02) weights. Its workload is the projection that follows the attention
+input norm of a 7168-wide model (1536 + 576 outputs) at a decode batch of 4.
+
 bf16 tensors are returned as numpy ``uint16`` bit patterns.
 """
 from __future__ import annotations
@@ -65,6 +72,23 @@ CONFIGS = {
 }
 # Two independent latent norms in one launch (MLA q and kv), no residual.
 MLA = [dict(M=4096, N=1536, seed_x=10), dict(M=4096, N=512, seed_x=20)]
+
+
+GEMM = dict(M=4, N=2112, K=7168)
+
+
+def fp4_weights(N: int, K: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP4 weights [N, K]: e2m1 code bytes [N, K/2] and e8m0 scale bytes [N, K/32]."""
+    w = np.random.default_rng(seed).integers(0, 256, (N, K // 2), dtype=np.uint8)
+    ws = np.random.default_rng(seed + 1).integers(116, 124, (N, K // 32)).astype(np.uint8)
+    return w, ws
+
+
+def make_gemm(M: int, N: int, K: int, seed: int = 40) -> dict:
+    """bf16 activations a [M, K] and MXFP4 weights (w, ws) for the GEMM."""
+    a = to_bf16_bits(normal_rows(M, K, seed, True))
+    w, ws = fp4_weights(N, K, seed + 1)
+    return {"a": a, "w": w, "ws": ws}
 
 
 def make_config(name: str, M: int | None = None) -> dict:

@@ -79,6 +79,21 @@ typedef int32_t rmsq_status;
 
 #define RMSQ_MAX_PROBLEMS 4
 #define RMSQ_N_MAX 32768
+#define RMSQ_GEMM_N_MAX (1 << 20)
+#define RMSQ_GEMM_K_MAX (1 << 20)
+
+/* Weight layouts of gemm_a16wfp4_prequant (this library's; the page names a
+ * preshuffled-weight GEMM without giving its layout).
+ * ROW_MAJOR: codes [N, K/2] (element 2j of a row in the low nibble of byte
+ *   j), scales [N, K/32].
+ * PRESHUFFLED: the operand order of the kernel's matrix-core steps. For
+ *   column tile t (rows 16t .. 16t+15), 128-wide K step s and lane l in
+ *   0..63, the 16 code bytes of row 16t + l%16, 32-group 4s + l/16 sit at
+ *   byte ((t * K/128 + s) * 64 + l) * 16, and that group's scale byte at
+ *   (t * K/128 + s) * 64 + l. Same sizes as ROW_MAJOR; made by
+ *   mxfp4_weight_preshuffle. */
+#define RMSQ_W_ROW_MAJOR 0
+#define RMSQ_W_PRESHUFFLED 1
 
 /*
  * Fused residual add + RMSNorm + per-group dynamic quantization of M rows of
@@ -165,6 +180,48 @@ rmsq_status add_rmsnorm(const void* x, const void* residual_in, const void* gamm
  */
 rmsq_status dynamic_per_group_scaled_quant(const void* x, int64_t M, int64_t N, int32_t group, int32_t fmt,
                                            int32_t scale_layout, void* out_q, void* out_scale, void* stream);
+
+/*
+ * gemm_a16wfp4_prequant: [ATT, required aiter changes] the A16WFP4 GEMM with
+ * the activation quantization inside the GEMM ("prequant"), which the page
+ * pairs with the norm fused into the all-reduce at concurrency 4 (small M).
+ *   out[m, n] = sum_k dq(a)[m, k] * dq(w)[n, k]
+ * where dq(a) is the MXFP4 group quantization (1x32 along K, e8m0 scale from
+ * the group amax, e2m1 codes rounded to nearest even, as
+ * rmsnorm_quant_group_multi computes it for RMSQ_FMT_MXFP4_E2M1) of each bf16
+ * row of `a`, dequantized, and dq(w) the dequantized weights. Products are
+ * exact in fp32 when they lie in its normal range, and accumulate in fp32 on
+ * the matrix cores in an order fixed for a given shape (so results repeat
+ * bit for bit).
+ *
+ *  a        [M, K] bf16, row stride lda elements (lda >= K, lda % 8 == 0),
+ *           16-byte aligned, read only; finite values.
+ *  w        e2m1 codes, N * K/2 bytes in layout w_layout, 16-byte aligned.
+ *  w_scale  e8m0 bytes (scale 2^(byte - 127)), N * K/32 bytes in layout
+ *           w_layout; byte 255 is not a number and gives unspecified results.
+ *  w_layout RMSQ_W_ROW_MAJOR or RMSQ_W_PRESHUFFLED (faster loads).
+ *  out      [M, N] fp32, row stride ldc >= N, 4-byte aligned, written, must
+ *           not overlap the inputs.
+ *  M >= 0 (0: nothing is launched), N a positive multiple of 16 up to
+ *  RMSQ_GEMM_N_MAX, K a positive multiple of 128 up to RMSQ_GEMM_K_MAX.
+ *  Tuned for small M (decode batches); any M up to 65535 * 64 is accepted.
+ * The caller owns every buffer. Bad sizes, strides, layout, alignment or
+ * overlap: RMSQ_ERR_INVALID_ARG, nothing launched. Asynchronous on `stream`.
+ */
+rmsq_status gemm_a16wfp4_prequant(const void* a, int64_t lda, const void* w, const void* w_scale, int32_t w_layout,
+                                  int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, void* stream);
+
+/*
+ * mxfp4_weight_preshuffle: [ATT, required aiter changes] the weight
+ * preshuffle that the page's preshuffled-weight GEMM relies on, here for
+ * MXFP4 weights: rearranges row-major codes `w` [N, K/2] and scales
+ * `w_scale` [N, K/32] into RMSQ_W_PRESHUFFLED order in `w_out` and
+ * `w_scale_out` (same sizes, caller-owned, must not overlap the inputs; w and
+ * w_out 16-byte aligned). A byte permutation, done once per weight matrix.
+ * N, K as for gemm_a16wfp4_prequant. Errors as there. Asynchronous.
+ */
+rmsq_status mxfp4_weight_preshuffle(const void* w, const void* w_scale, int64_t N, int64_t K, void* w_out,
+                                    void* w_scale_out, void* stream);
 
 /* 1 if HIP device `device` is a gfx950 (MI355X-class) GPU, else 0.
  * [ARQ, Motivation]: the single-kernel path is gated to gfx95x devices and

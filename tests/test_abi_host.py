@@ -252,3 +252,50 @@ def test_unfused_entry_points_validate():
     if not fq.rmsq_device_supported(0):
         assert L.add_rmsnorm(A, r, g, 1e-6, 4, 256, ro, yb, None) == fq.RMSQ_ERR_UNSUPPORTED
         assert L.dynamic_per_group_scaled_quant(A, 4, 256, 32, 1, 1, q, sc, None) == fq.RMSQ_ERR_UNSUPPORTED
+
+
+def test_gemm_validates():
+    L = fq.lib()
+    E = fq.RMSQ_ERR_INVALID_ARG
+    w, s, o = A + 100 * MB, A + 200 * MB, A + 300 * MB
+    R = fq.W_ROW_MAJOR
+
+    def g(a=A, lda=256, w=w, s=s, lay=R, M=4, N=32, K=256, o=o, ldc=32):
+        # gemm_a16wfp4_prequant(a, lda, w, w_scale, w_layout, M, N, K, out, ldc, stream)
+        return L.gemm_a16wfp4_prequant(a, lda, w, s, lay, M, N, K, o, ldc, None)
+
+    assert g(N=24, ldc=24) == E          # N % 16
+    assert g(K=200) == E                 # K % 128
+    assert g(M=-1) == E
+    assert g(lda=128) == E               # lda < K
+    assert g(lda=260) == E               # lda % 8
+    assert g(ldc=16) == E                # ldc < N
+    assert g(lay=2) == E                 # unknown weight layout
+    assert g(a=A + 2) == E               # a alignment
+    assert g(w=w + 8) == E               # w alignment
+    assert g(o=o + 2) == E               # out alignment
+    assert g(o=A + 64) == E              # out overlaps a
+    assert g(o=w + 1024) == E            # out overlaps w
+    assert g(o=s) == E                   # out overlaps the scales
+    assert g(a=None) == E                # NULL
+    assert g(lda=1 << 21, K=1 << 21) == E   # K beyond the limit
+    assert g(M=0) == fq.RMSQ_OK          # no-op
+    assert g(M=0, lay=fq.W_PRESHUFFLED) == fq.RMSQ_OK
+    assert g() in (fq.RMSQ_OK, fq.RMSQ_ERR_UNSUPPORTED)
+    if not fq.rmsq_device_supported(0):
+        assert g() == fq.RMSQ_ERR_UNSUPPORTED
+
+
+def test_preshuffle_validates():
+    L = fq.lib()
+    E = fq.RMSQ_ERR_INVALID_ARG
+    w, s, wo, so = A, A + 100 * MB, A + 200 * MB, A + 300 * MB
+    # mxfp4_weight_preshuffle(w, w_scale, N, K, w_out, w_scale_out, stream)
+    assert L.mxfp4_weight_preshuffle(w, s, 24, 256, wo, so, None) == E       # N % 16
+    assert L.mxfp4_weight_preshuffle(w, s, 32, 192, wo, so, None) == E       # K % 128
+    assert L.mxfp4_weight_preshuffle(w, s, 32, 256, w + 1024, so, None) == E  # output overlaps input
+    assert L.mxfp4_weight_preshuffle(w, s, 32, 256, wo, s + 8, None) == E    # scale output overlaps
+    assert L.mxfp4_weight_preshuffle(w, s, 32, 256, wo + 4, so, None) == E   # alignment
+    assert L.mxfp4_weight_preshuffle(None, s, 32, 256, wo, so, None) == E
+    if not fq.rmsq_device_supported(0):
+        assert L.mxfp4_weight_preshuffle(w, s, 32, 256, wo, so, None) == fq.RMSQ_ERR_UNSUPPORTED

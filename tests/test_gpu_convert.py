@@ -354,7 +354,7 @@ def test_fp4_codes8_every_value_amax_pair(orc):
 _E2M1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6])
 
 
-def _mfma_model(a, b, sa, sb):
+def _mfma_model(a, b, sa, sb, magnitude=False):
     """v_mfma_scale_f32_16x16x128_f8f6f4 with e2m1 A and B, as the GEMM uses
     it: lane l holds A row l % 16 and B column l % 16, K elements 32 * (l // 16)
     ... + 31 (element 8d + j in nibble j of dword d), with the e8m0 scale of
@@ -370,24 +370,34 @@ def _mfma_model(a, b, sa, sb):
                 for j in range(8):
                     A[i, 32 * kb + 8 * d + j] = _E2M1[(a[w, l, d] >> (4 * j)) & 15] * 2.0 ** (int(sa[w, l] & 255) - 127)
                     B[32 * kb + 8 * d + j, i] = _E2M1[(b[w, l, d] >> (4 * j)) & 15] * 2.0 ** (int(sb[w, l] & 255) - 127)
-        D = A @ B
+        D = np.abs(A) @ np.abs(B) if magnitude else A @ B
         for l in range(64):
             out[w, l] = D[4 * (l // 16):4 * (l // 16) + 4, l % 16]
     return out
 
 
-def test_hw_mfma_scale_fp4_layout():
+@pytest.mark.parametrize("lo,hi", [(126, 129), (112, 143)])
+def test_hw_mfma_scale_fp4_layout(lo, hi):
     """The operand, scale and result layout of the block-scaled FP4 MFMA that
-    the prequant GEMM is written against, on random codes and scales (the sums
-    are small enough to be exact in fp32)."""
-    say("raw v_mfma_scale_f32_16x16x128_f8f6f4 (e2m1 x e2m1)")
-    rng = np.random.default_rng(21)
+    the prequant GEMM is written against, on random codes and scale bytes in
+    lo..hi-1 (the other bytes of the scale registers random). With bytes 126..128
+    every product is a multiple of 2^-4 and every sum of 128 below 2^15, so
+    the result is exact; with the wide range the fp32 sum may round, within
+    128 * 2^-24 of the sum of |products|."""
+    say(f"raw v_mfma_scale_f32_16x16x128_f8f6f4 (e2m1 x e2m1), scale bytes {lo}..{hi - 1}")
+    rng = np.random.default_rng(21 + lo)
     W = 6
     a = rng.integers(0, 2 ** 32, (W, 64, 4), dtype=np.uint64).astype(np.uint32)
     b = rng.integers(0, 2 ** 32, (W, 64, 4), dtype=np.uint64).astype(np.uint32)
-    sa = rng.integers(122, 133, (W, 64)).astype(np.uint32) | (rng.integers(0, 256, (W, 64)).astype(np.uint32) << 8)
-    sb = rng.integers(122, 133, (W, 64)).astype(np.uint32) | (rng.integers(0, 256, (W, 64)).astype(np.uint32) << 16)
+    sa = rng.integers(lo, hi, (W, 64)).astype(np.uint32) | (rng.integers(0, 256, (W, 64)).astype(np.uint32) << 8)
+    sb = rng.integers(lo, hi, (W, 64)).astype(np.uint32) | (rng.integers(0, 256, (W, 64)).astype(np.uint32) << 16)
     d = torch.zeros(W * 64 * 4, dtype=torch.float32, device="cuda")
     call_probe("probe_mfma_scale_fp4", dev(a.view(np.int32)), dev(b.view(np.int32)), dev(sa.view(np.int32)),
                dev(sb.view(np.int32)), d, n=W)
-    assert np.array_equal(host(d).reshape(W, 64, 4), _mfma_model(a, b, sa, sb))
+    got = host(d).reshape(W, 64, 4).astype(np.float64)
+    want = _mfma_model(a, b, sa, sb)
+    if (lo, hi) == (126, 129):
+        assert np.array_equal(got, want)
+    else:
+        absum = _mfma_model(a, b, sa, sb, magnitude=True)
+        assert np.all(np.abs(got - want) <= 128 * 2.0 ** -24 * absum)

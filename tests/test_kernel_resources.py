@@ -76,3 +76,15 @@ def test_register_budget(kernels, J, limit):
         m = NAME.match(n or "")
         if m and int(m.group(2)) == J:
             assert k["vgpr_count"] + k["agpr_count"] <= limit, (n, k)
+
+
+def test_gemm_variants_fit_sixteen_waves(kernels):
+    """The GEMM launches up to 16 waves per workgroup (4 per SIMD), so each
+    variant must fit 128 registers (VGPRs + AGPRs) and the LDS of its
+    partial sums."""
+    gemm = {n: k for n, k in kernels.items() if "rmsq_gemm_a16wfp4_kernel" in (n or "")}
+    # (4 row-tile counts + the staged variant with 1 or 2 column tiles) x 2 weight layouts
+    assert len(gemm) == 12, sorted(gemm)
+    for n, k in gemm.items():
+        assert k["vgpr_count"] + k["agpr_count"] <= 128, (n, k)
+        assert k["group_segment_fixed_size"] <= 64 * 1024, (n, k)
