@@ -15,7 +15,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                 region (HIP events on the launch stream)
   cpu_baseline  the double-precision CPU oracle on the machine's host cores
   configs       the other workloads (decode, prefill at 512 rows, the two MLA
-                latent norms in one launch, MXFP4 in both scale layouts)
+                latent norms in one launch, MXFP4 in both scale layouts) and
+                the A16WFP4 prequant GEMM at a decode batch of 4 (bytes:
+                weight codes and scales, activations, fp32 output)
 """
 from __future__ import annotations
 
@@ -93,6 +95,50 @@ class Workload:
     def launch(self, i, stream=None):
         import fp4_quant_amd as fq
         fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0], stream or self.stream)
+
+
+def gemm_bytes(M, N, K):
+    """MXFP4 weight codes + e8m0 scales read, bf16 activations read, fp32 output written."""
+    return N * K // 2 + N * K // 32 + M * K * 2 + M * N * 4
+
+
+# The A16WFP4 prequant GEMM after the attention input norm of a 7168-wide
+# model (1536 + 576 outputs) at a decode batch of 4, preshuffled weights.
+GEMM_SPECS = {
+    "gemm_a16wfp4_decode": dict(M=4, N=2112, K=7168),
+}
+
+
+class GemmWorkload:
+    """Rotating sets of preshuffled weights (and activations, outputs) for the
+    A16WFP4 prequant GEMM, enough sets that no launch finds its weights in
+    the Infinity Cache."""
+
+    def __init__(self, name, M, N, K):
+        import torch
+        import fp4_quant_amd as fq
+        from fp4_quant_amd import inputs
+        self.name, self.M, self.N, self.K = name, M, N, K
+        self.rows = M
+        self.bytes = gemm_bytes(M, N, K)
+        g = inputs.make_gemm(M, N, K)
+        a = torch.from_numpy(g["a"].view("int16")).view(torch.bfloat16).cuda()
+        w, ws = torch.from_numpy(g["w"]).cuda(), torch.from_numpy(g["ws"]).cuda()
+        nsets = max(2, min(512, -(-3 * MALL_BYTES // self.bytes)))
+        self.sets = []
+        for _ in range(nsets):
+            sw, sws = torch.empty_like(w), torch.empty_like(ws)
+            fq.mxfp4_weight_preshuffle(w, ws, N, K, sw, sws)
+            out = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+            self.sets.append((a.clone(), sw, sws, out))
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def launch(self, i, stream=None):
+        import fp4_quant_amd as fq
+        a, w, ws, out = self.sets[i % len(self.sets)]
+        fq.gemm_a16wfp4_prequant(a, self.K, w, ws, fq.W_PRESHUFFLED, self.M, self.N, self.K, out, self.N,
+                                 stream or self.stream)
 
 
 class UnfusedWorkload(Workload):
@@ -220,14 +266,18 @@ def copy_probe(launches):
     torch.cuda.synchronize()
 
 
-def kernel_source_hash():
+FUSED_SOURCES = ("rmsq_abi.hip", "rmsq_device.h", "rmsq_kernel.h")
+GEMM_SOURCES = ("rmsq_abi.hip", "rmsq_device.h", "rmsq_gemm.h")
+
+
+def kernel_source_hash(files=FUSED_SOURCES):
+    """sha256 over the sources a kernel and its launch are built from."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "fp4_quant_amd", "csrc")
-    for fn in sorted(os.listdir(d)):
-        if fn.endswith((".h", ".hip")):
-            h.update(fn.encode())
-            h.update(open(os.path.join(d, fn), "rb").read())
+    for fn in sorted(files):
+        h.update(fn.encode())
+        h.update(open(os.path.join(d, fn), "rb").read())
     return h.hexdigest()
 
 
@@ -251,7 +301,8 @@ def recorded_traffic(config):
         line = line.strip()
         if line.startswith("{"):
             rec = json.loads(line)
-            if rec.get("kernel_source_sha256") == kernel_source_hash():
+            files = GEMM_SOURCES if config in GEMM_SPECS else FUSED_SOURCES
+            if rec.get("kernel_source_sha256") == kernel_source_hash(files):
                 return rec.get("hbm_bytes_per_launch")
     return None
 
@@ -322,7 +373,8 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed launches first; a few hundred let the clocks settle")
-    ap.add_argument("--config", default="prefill", choices=sorted(SPECS))
+    ap.add_argument("--config", default="prefill", choices=sorted(SPECS) + sorted(GEMM_SPECS),
+                    help="headline workload (a GEMM config only with --only-kernel)")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline budget (0 skips it)")
     ap.add_argument("--only-kernel", action="store_true",
@@ -344,6 +396,14 @@ def main():
         copy_probe(args.copy_probe)
         return
 
+    if args.config in GEMM_SPECS:
+        if not args.only_kernel:
+            print("bench.py: GEMM configs are headline workloads only with --only-kernel", file=sys.stderr)
+            sys.exit(2)
+        wg = GemmWorkload(args.config, **GEMM_SPECS[args.config])
+        pg = time_workload(wg, args.steps, args.warmup)
+        log(f"bench: {args.config}: {pg * 1e3:.2f} us per launch, {wg.bytes / (pg * 1e-3) / 1e9:.0f} GB/s")
+        return
     specs, fmt, layout = SPECS[args.config]
     log(f"bench: building workload {args.config}")
     w = Workload(args.config, specs, fmt, layout)
@@ -375,6 +435,23 @@ def main():
                 pg = time_workload_graph(wk, 100)
                 configs[name]["us_per_launch_graph"] = round(pg * 1e3, 2)
                 configs[name]["GBps_graph"] = round(wk.bytes / (pg * 1e-3) / 1e9, 1)
+            del wk
+            torch.cuda.empty_cache()
+        for name, g in GEMM_SPECS.items():
+            log(f"bench: workload {name}")
+            wk = GemmWorkload(name, **g)
+            pl = time_workload(wk, max(50, args.steps // 2), max(50, args.warmup))
+            pg = time_workload_graph(wk, 100)
+            gb = wk.bytes / (pl * 1e-3) / 1e9
+            configs[name] = {"M": g["M"], "N": g["N"], "K": g["K"], "weights": "preshuffled",
+                             "us_per_launch": round(pl * 1e3, 2), "GBps": round(gb, 1),
+                             "frac_of_peak": round(gb / HBM_PEAK_GBPS, 4), "bytes": wk.bytes,
+                             "us_per_launch_graph": round(pg * 1e3, 2),
+                             "GBps_graph": round(wk.bytes / (pg * 1e-3) / 1e9, 1),
+                             "TFLOPs": round(2 * g["M"] * g["N"] * g["K"] / (pl * 1e-3) / 1e12, 3)}
+            tr = recorded_traffic(name)
+            if tr is not None:
+                configs[name]["traffic"] = tr
             del wk
             torch.cuda.empty_cache()
     if not args.no_configs and args.config == "prefill":
