@@ -56,6 +56,8 @@ def _bind(L):
                                              _i32, _i32, _i32, _p, _p, _p, _p, _i64]
     L.oracle_gemm_a16wfp4_prequant.restype = C.c_int
     L.oracle_gemm_a16wfp4_prequant.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _i64]
+    L.oracle_gemm_a16w8_prequant.restype = C.c_int
+    L.oracle_gemm_a16w8_prequant.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _i64]
     L.oracle_num_threads.restype = C.c_int
     L.oracle_num_threads.argtypes = []
     return L
@@ -192,6 +194,23 @@ class Oracle:
             raise ValueError("oracle: arguments outside the defined operation")
         return out
 
+    def gemm_a16w8_prequant(self, a, w, w_scale):
+        """A16W8 prequant GEMM: a [M, K] uint16 (bf16 bits, row stride may
+        exceed K), w [N, K] uint8 e4m3fn codes, w_scale [ceil(N/128), K/128]
+        float32 block scales. Returns C [M, N] float64."""
+        M, K = a.shape
+        assert a.strides[1] == 2 and a.dtype == np.uint16
+        N = w.shape[0]
+        assert w.shape == (N, K) and w_scale.shape == (-(-N // 128), K // 128)
+        w = np.ascontiguousarray(w, dtype=np.uint8)
+        w_scale = np.ascontiguousarray(w_scale, dtype=np.float32)
+        out = np.zeros((M, N), np.float64)
+        rc = self._L.oracle_gemm_a16w8_prequant(_ptr(a), a.strides[0] // 2, _ptr(w), _ptr(w_scale), M, N, K,
+                                                _ptr(out), N)
+        if rc != 0:
+            raise ValueError("oracle: arguments outside the defined operation")
+        return out
+
     def group_quant(self, yb, group=128, fmt=FMT_FP8, scale_layout=LAYOUT_ROW, scale_fill=0):
         """Stage 2 alone on bf16 rows: returns (q, scale)."""
         yb = np.ascontiguousarray(yb, dtype=np.uint16)
@@ -259,6 +278,10 @@ def add_rmsnorm(*a, **k):
 
 def gemm_a16wfp4_prequant(*a, **k):
     return default().gemm_a16wfp4_prequant(*a, **k)
+
+
+def gemm_a16w8_prequant(*a, **k):
+    return default().gemm_a16w8_prequant(*a, **k)
 
 
 def group_quant(*a, **k):

@@ -444,6 +444,53 @@ int oracle_gemm_a16wfp4_prequant(const uint16_t* a, int64_t lda,
     return 0;
 }
 
+/*
+ * A16W8 prequant GEMM, the FP8 counterpart that [ATT] lists for its DS FP8
+ * runs (an a16w8 GEMM). READING: the activation rows are quantized exactly
+ * as the FP8 group quantization above (1x128 groups along K, fp32 scale
+ * amax/448, e4m3fn codes of the quotient); the weights come as e4m3fn codes
+ * [N, K] with fp32 scales per 128x128 block [ceil(N/128), K/128] (the block
+ * layout of the DeepSeek FP8 checkpoints those runs serve), and
+ *   C[m][n] = sum_k (qa[m][k] * sa[m][k/128]) * (qw[n][k] * sw[n/128][k/128]),
+ * accumulated here in double in k order.
+ */
+int oracle_gemm_a16w8_prequant(const uint16_t* a, int64_t lda,
+                               const uint8_t* w, const float* w_scale,
+                               int64_t M, int64_t N, int64_t K,
+                               double* out, int64_t ldc)
+{
+    if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || lda < K || ldc < N)
+        return -1;
+    if (fegetround() != FE_TONEAREST)
+        return -1;
+    const int64_t kb = K / 128;
+#pragma omp parallel
+    {
+        uint8_t* qa = (uint8_t*)malloc((size_t)K);
+        float* sa = (float*)malloc((size_t)kb * sizeof(float));
+        double* da = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            /* the activation row's FP8 quantization, then its values */
+            group_quant_row(a + m * lda, 0, 1, K, 128, 0, 0, qa, sa);
+            for (int64_t k = 0; k < K; ++k)
+                da[k] = oracle_e4m3fn_decode(qa[k]) * (double)sa[k / 128];
+            for (int64_t n = 0; n < N; ++n) {
+                const uint8_t* wr = w + n * K;
+                const float* sr = w_scale + (n / 128) * kb;
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc += da[k] * (oracle_e4m3fn_decode(wr[k]) * (double)sr[k / 128]);
+                out[m * ldc + n] = acc;
+            }
+        }
+        free(da);
+        free(sa);
+        free(qa);
+    }
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -74,6 +74,17 @@ int oracle_gemm_a16wfp4_prequant(const uint16_t* a, int64_t lda,
                                  int64_t M, int64_t N, int64_t K,
                                  double* out, int64_t ldc);
 
+/* A16W8 prequant GEMM: a [M, K] bf16 (row stride lda) quantized to FP8
+ * e4m3fn per 1x128 group along K as oracle_group_quant does, times the FP8
+ * weights w [N, K] e4m3fn codes with fp32 scales per 128x128 block
+ * w_scale [ceil(N/128), K/128]: out[m*ldc + n] = sum over k of the
+ * dequantized products, in double. Returns 0, or -1 for arguments it does not
+ * define (K a positive multiple of 128). */
+int oracle_gemm_a16w8_prequant(const uint16_t* a, int64_t lda,
+                               const uint8_t* w, const float* w_scale,
+                               int64_t M, int64_t N, int64_t K,
+                               double* out, int64_t ldc);
+
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

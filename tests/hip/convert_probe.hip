@@ -133,6 +133,25 @@ __global__ void k_mfma_scale_fp4(const uint32_t* a, const uint32_t* b, const uin
   for (int i = 0; i < 4; ++i) d[o + i] = r[i];
 }
 
+// The same instruction with e4m3fn A and B (cbsz = blgp = 0): wave w reads
+// a, b [w][lane][8 dwords] and the scale registers sa, sb [w][lane].
+__global__ void k_mfma_scale_fp8(const uint32_t* a, const uint32_t* b, const uint32_t* sa, const uint32_t* sb, float* d,
+                                 int64_t waves) {
+  const int64_t w = blockIdx.x;
+  if (w >= waves) return;
+  const int l = threadIdx.x;
+  const int64_t o = (w * 64 + l) * 8;
+  v8i_t av, bv;
+  for (int i = 0; i < 8; ++i) {
+    av[i] = (int)a[o + i];
+    bv[i] = (int)b[o + i];
+  }
+  const v4f_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+  const v4f_t r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, (int)sa[w * 64 + l], 0,
+                                                                 (int)sb[w * 64 + l]);
+  for (int i = 0; i < 4; ++i) d[(w * 64 + l) * 4 + i] = r[i];
+}
+
 static int launch_status() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 
 #define GRID(n) dim3((unsigned)(((n) + 255) / 256 < 65536 ? ((n) + 255) / 256 : 65536)), dim3(256), 0, (hipStream_t)stream
@@ -203,6 +222,12 @@ int probe_mfma_scale_fp4(const uint32_t* a, const uint32_t* b, const uint32_t* s
                          int64_t waves, void* stream) {
   if (waves <= 0) return 0;
   hipLaunchKernelGGL(k_mfma_scale_fp4, dim3((unsigned)waves), dim3(64), 0, (hipStream_t)stream, a, b, sa, sb, d, waves);
+  return launch_status();
+}
+int probe_mfma_scale_fp8(const uint32_t* a, const uint32_t* b, const uint32_t* sa, const uint32_t* sb, float* d,
+                         int64_t waves, void* stream) {
+  if (waves <= 0) return 0;
+  hipLaunchKernelGGL(k_mfma_scale_fp8, dim3((unsigned)waves), dim3(64), 0, (hipStream_t)stream, a, b, sa, sb, d, waves);
   return launch_status();
 }
 int probe_fp8_exact(const float* v, const float* s, uint8_t* out, int64_t n, void* stream) {

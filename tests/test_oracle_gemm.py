@@ -103,3 +103,86 @@ def test_rejects_undefined_shapes(orc):
     a = np.zeros((2, 48), np.uint16)
     with pytest.raises((ValueError, AssertionError)):
         orc.gemm_a16wfp4_prequant(a, np.zeros((3, 24), np.uint8), np.zeros((3, 1), np.uint8))
+
+
+# ------------------------------------------------------------------ A16W8 --
+def e4m3_values(codes):
+    """e4m3fn bytes -> float64 through torch's own float8_e4m3fn dtype."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def dequant_fp8_weights(w, ws):
+    """[N, K] e4m3fn codes with [ceil(N/128), K/128] fp32 block scales -> [N, K] float64."""
+    N, K = w.shape
+    s = np.repeat(np.repeat(ws.astype(np.float64), 128, axis=0)[:N], 128, axis=1)
+    return e4m3_values(w) * s
+
+
+def random_fp8_weights(N, K, seed):
+    rng = np.random.default_rng(seed)
+    w = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x7E                    # no NaN codes
+    ws = rng.uniform(2.0 ** -12, 2.0 ** -6, (-(-N // 128), K // 128)).astype(np.float32)
+    return w, ws
+
+
+def test_a16w8_hand_example(orc):
+    # 128 x 448 then 128 x 224: group scales 1 and 0.5 exactly, codes 448 -> exact; weights 1.0 (0x38)
+    a = np.array([[0x43E0] * 128 + [0x4360] * 128], np.uint16)
+    w = np.full((2, 256), 0x38, np.uint8)
+    ws = np.ones((1, 2), np.float32)
+    assert orc.gemm_a16w8_prequant(a, w, ws).tolist() == [[128 * 448.0 + 128 * 224.0] * 2]
+    ws[0, 1] = 4.0                                   # second K block of the weights scaled by 4
+    assert orc.gemm_a16w8_prequant(a, w, ws).tolist() == [[128 * 448.0 + 4 * 128 * 224.0] * 2]
+
+
+def test_a16w8_lossless_activations_match_numpy_matmul(orc):
+    """Activations built from e4m3fn values times a power of two per 128-group,
+    with +-448 in every group, are exactly FP8 values (the scale is that power
+    of two), so the GEMM is A @ dequant(W)^T, computed here by numpy. N = 200
+    spans two 128-row weight blocks, K = 384 three K blocks."""
+    rng = np.random.default_rng(15)
+    M, N, K = 6, 200, 384
+    codes = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E
+    codes[:, ::128] = rng.choice([0x7E, 0xFE], (M, K // 128))   # +-448 in every group
+    e = rng.integers(-20, 20, (M, K // 128))
+    A = e4m3_values(codes) * np.repeat(np.ldexp(1.0, e), 128, axis=1)
+    a = inputs.to_bf16_bits(A.astype(np.float32))
+    assert np.array_equal(bf16_to_f32(a).astype(np.float64), A)
+    w, ws = random_fp8_weights(N, K, 16)
+    want = A @ dequant_fp8_weights(w, ws).T
+    got = orc.gemm_a16w8_prequant(a, w, ws)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+def test_a16w8_equals_its_own_quantization_times_the_weights(orc):
+    """On general bf16 rows the GEMM equals (the activations' FP8 group
+    quantization, dequantized) @ dequant(W)^T."""
+    p = inputs.make_problem(5, 512, seed_x=33, residual=False, outliers=True)
+    w, ws = random_fp8_weights(136, 512, 17)
+    qa, sa = orc.group_quant(p["x"], 128, 0, 0)
+    da = e4m3_values(qa) * np.repeat(sa.reshape(5, -1).astype(np.float64), 128, axis=1)
+    want = da @ dequant_fp8_weights(w, ws).T
+    got = orc.gemm_a16w8_prequant(p["x"], w, ws)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("k", [-7, 3])
+def test_a16w8_power_of_two_scaling(orc, k):
+    """Scaling the activations by 2^k scales every output by 2^k exactly (the
+    fp32 group scales absorb it); scaling every weight block scale too."""
+    p = inputs.make_problem(3, 256, seed_x=34, residual=False, outliers=True)
+    w, ws = random_fp8_weights(20, 256, 18)
+    base = orc.gemm_a16w8_prequant(p["x"], w, ws)
+    xs = inputs.to_bf16_bits(bf16_to_f32(p["x"]) * np.float32(2.0 ** k))
+    assert np.array_equal(orc.gemm_a16w8_prequant(xs, w, ws), base * 2.0 ** k)
+    assert np.array_equal(orc.gemm_a16w8_prequant(p["x"], w, ws * np.float32(2.0 ** k)), base * 2.0 ** k)
+
+
+def test_a16w8_rejects_undefined_shapes(orc):
+    a = np.zeros((2, 192), np.uint16)
+    with pytest.raises((ValueError, AssertionError)):
+        orc.gemm_a16w8_prequant(a, np.zeros((3, 192), np.uint8), np.zeros((1, 1), np.float32))

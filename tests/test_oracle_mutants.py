@@ -53,6 +53,13 @@ MUTANTS = {
     "GEMM activation scale dropped": ("da[k] = oracle_e2m1_decode(code) * e8m0_value(ea[k / 32]);",
                                       "da[k] = oracle_e2m1_decode(code);"),
     "GEMM weight scale per 16": ("e8m0_value(sr[k / 32])", "e8m0_value(sr[(k / 16) % (K / 32)])"),
+    "A16W8 activation scale dropped": ("da[k] = oracle_e4m3fn_decode(qa[k]) * (double)sa[k / 128];",
+                                       "da[k] = oracle_e4m3fn_decode(qa[k]);"),
+    "A16W8 weight block rows of 64": ("const float* sr = w_scale + (n / 128) * kb;",
+                                      "const float* sr = w_scale + ((n / 64) % ((N + 127) / 128)) * kb;"),
+    "A16W8 weight scale per 64 columns": ("(double)sr[k / 128]);", "(double)sr[(k / 64) % kb]);"),
+    "A16W8 weight scale divides": ("acc += da[k] * (oracle_e4m3fn_decode(wr[k]) * (double)sr[k / 128]);",
+                                   "acc += da[k] * (oracle_e4m3fn_decode(wr[k]) / (double)sr[k / 128]);"),
 }
 
 
@@ -76,6 +83,8 @@ def _pins():
     p += [TG.test_hand_example, TG.test_lossless_activations_match_numpy_matmul,
           TG.test_equals_its_own_quantization_times_the_weights]
     p += [functools.partial(TG.test_power_of_two_scaling, k=k) for k in (-7, 3)]
+    p += [TG.test_a16w8_hand_example, TG.test_a16w8_lossless_activations_match_numpy_matmul,
+          TG.test_a16w8_equals_its_own_quantization_times_the_weights]
     return p
 
 
