@@ -97,15 +97,22 @@ class Workload:
         fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0], stream or self.stream)
 
 
-def gemm_bytes(M, N, K):
-    """MXFP4 weight codes + e8m0 scales read, bf16 activations read, fp32 output written."""
-    return N * K // 2 + N * K // 32 + M * K * 2 + M * N * 4
+def gemm_bytes(M, N, K, fmt=1):
+    """Weight codes + scales read (MXFP4: e8m0 per 1x32; FP8: fp32 per 128x128
+    block), bf16 activations read, fp32 output written."""
+    if fmt == 1:
+        w = N * K // 2 + N * K // 32
+    else:
+        w = N * K + -(-N // 128) * (K // 128) * 4
+    return w + M * K * 2 + M * N * 4
 
 
-# The A16WFP4 prequant GEMM after the attention input norm of a 7168-wide
-# model (1536 + 576 outputs) at a decode batch of 4, preshuffled weights.
+# The prequant GEMMs after the attention input norm of a 7168-wide model
+# (1536 + 576 outputs) at a decode batch of 4, preshuffled weights: MXFP4
+# weights (A16WFP4) and FP8 block-scaled weights (A16W8).
 GEMM_SPECS = {
-    "gemm_a16wfp4_decode": dict(M=4, N=2112, K=7168),
+    "gemm_a16wfp4_decode": dict(M=4, N=2112, K=7168, fmt=1),
+    "gemm_a16w8_decode": dict(M=4, N=2112, K=7168, fmt=0),
 }
 
 
@@ -114,21 +121,26 @@ class GemmWorkload:
     A16WFP4 prequant GEMM, enough sets that no launch finds its weights in
     the Infinity Cache."""
 
-    def __init__(self, name, M, N, K):
+    def __init__(self, name, M, N, K, fmt):
         import torch
         import fp4_quant_amd as fq
         from fp4_quant_amd import inputs
-        self.name, self.M, self.N, self.K = name, M, N, K
+        self.name, self.M, self.N, self.K, self.fmt = name, M, N, K, fmt
         self.rows = M
-        self.bytes = gemm_bytes(M, N, K)
-        g = inputs.make_gemm(M, N, K)
+        self.bytes = gemm_bytes(M, N, K, fmt)
+        g = inputs.make_gemm(M, N, K) if fmt == 1 else inputs.make_gemm8(M, N, K)
         a = torch.from_numpy(g["a"].view("int16")).view(torch.bfloat16).cuda()
         w, ws = torch.from_numpy(g["w"]).cuda(), torch.from_numpy(g["ws"]).cuda()
         nsets = max(2, min(512, -(-3 * MALL_BYTES // self.bytes)))
         self.sets = []
         for _ in range(nsets):
-            sw, sws = torch.empty_like(w), torch.empty_like(ws)
-            fq.mxfp4_weight_preshuffle(w, ws, N, K, sw, sws)
+            sw = torch.empty_like(w)
+            if fmt == 1:
+                sws = torch.empty_like(ws)
+                fq.mxfp4_weight_preshuffle(w, ws, N, K, sw, sws)
+            else:
+                sws = ws.clone()
+                fq.fp8_weight_preshuffle(w, N, K, sw)
             out = torch.zeros((M, N), dtype=torch.float32, device="cuda")
             self.sets.append((a.clone(), sw, sws, out))
         torch.cuda.synchronize()
@@ -137,8 +149,8 @@ class GemmWorkload:
     def launch(self, i, stream=None):
         import fp4_quant_amd as fq
         a, w, ws, out = self.sets[i % len(self.sets)]
-        fq.gemm_a16wfp4_prequant(a, self.K, w, ws, fq.W_PRESHUFFLED, self.M, self.N, self.K, out, self.N,
-                                 stream or self.stream)
+        f = fq.gemm_a16wfp4_prequant if self.fmt == 1 else fq.gemm_a16w8_prequant
+        f(a, self.K, w, ws, fq.W_PRESHUFFLED, self.M, self.N, self.K, out, self.N, stream or self.stream)
 
 
 class UnfusedWorkload(Workload):
@@ -443,7 +455,9 @@ def main():
             pl = time_workload(wk, max(50, args.steps // 2), max(50, args.warmup))
             pg = time_workload_graph(wk, 100)
             gb = wk.bytes / (pl * 1e-3) / 1e9
-            configs[name] = {"M": g["M"], "N": g["N"], "K": g["K"], "weights": "preshuffled",
+            configs[name] = {"M": g["M"], "N": g["N"], "K": g["K"],
+                             "weights": ("MXFP4" if g["fmt"] == 1 else "FP8 e4m3fn, 128x128 block scales") +
+                                        ", preshuffled",
                              "us_per_launch": round(pl * 1e3, 2), "GBps": round(gb, 1),
                              "frac_of_peak": round(gb / HBM_PEAK_GBPS, 4), "bytes": wk.bytes,
                              "us_per_launch_graph": round(pg * 1e3, 2),

@@ -59,7 +59,7 @@ EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "add_rmsnorm",
            "dynamic_per_group_scaled_quant", "rmsq_device_supported",
            "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape",
            "rmsq_query_shape", "rmsq_set_row_group", "rmsq_set_wave_rows", "rmsq_set_row_splits",
-           "gemm_a16wfp4_prequant", "mxfp4_weight_preshuffle")
+           "gemm_a16wfp4_prequant", "mxfp4_weight_preshuffle", "gemm_a16w8_prequant", "fp8_weight_preshuffle")
 
 _lib = None
 
@@ -103,6 +103,10 @@ def lib() -> C.CDLL:
         L.gemm_a16wfp4_prequant.argtypes = [p, i64, p, p, i32, i64, i64, i64, p, i64, p]
         L.mxfp4_weight_preshuffle.restype = i32
         L.mxfp4_weight_preshuffle.argtypes = [p, p, i64, i64, p, p, p]
+        L.gemm_a16w8_prequant.restype = i32
+        L.gemm_a16w8_prequant.argtypes = [p, i64, p, p, i32, i64, i64, i64, p, i64, p]
+        L.fp8_weight_preshuffle.restype = i32
+        L.fp8_weight_preshuffle.argtypes = [p, i64, i64, p, p]
         _lib = L
     return _lib
 
@@ -188,6 +192,21 @@ def mxfp4_weight_preshuffle(w, w_scale, N, K, w_out, w_scale_out, stream=None) -
     """Row-major MXFP4 weights to the preshuffled layout, C argument order."""
     _check(lib().mxfp4_weight_preshuffle(_ptr(w), _ptr(w_scale), int(N), int(K), _ptr(w_out), _ptr(w_scale_out),
                                          _stream(stream, w.device if w is not None else None)))
+
+
+def gemm_a16w8_prequant(a, lda, w, w_scale, w_layout, M, N, K, out, ldc, stream=None) -> None:
+    """The A16W8 prequant GEMM (bf16 activations quantized to FP8 per 1x128
+    group inside the GEMM, e4m3fn weights with fp32 128x128 block scales,
+    fp32 output), C argument order."""
+    _check(lib().gemm_a16w8_prequant(_ptr(a), int(lda), _ptr(w), _ptr(w_scale), int(w_layout), int(M), int(N),
+                                     int(K), _ptr(out), int(ldc),
+                                     _stream(stream, a.device if a is not None else None)))
+
+
+def fp8_weight_preshuffle(w, N, K, w_out, stream=None) -> None:
+    """Row-major e4m3fn weights to the A16W8 GEMM's preshuffled layout."""
+    _check(lib().fp8_weight_preshuffle(_ptr(w), int(N), int(K), _ptr(w_out),
+                                       _stream(stream, w.device if w is not None else None)))
 
 
 def rmsq_device_supported(device: int = 0) -> bool:

@@ -20,6 +20,10 @@ uniform over 0..255 (two e2m1 codes each, seed ``seed + 1``) and e8m0 scale
 bytes uniform over 116..123 (seed ``seed + 2``), the scales of 1x32 groups of
 N(0, 0.02) weights. Its workload is the projection that follows the attention
 input norm of a 7168-wide model (1536 + 576 outputs) at a decode batch of 4.
+The A16W8 GEMM (``make_gemm8``) takes the same activations and random FP8
+weights: e4m3fn code bytes uniform over the 254 non-NaN codes (seed
+``seed + 1``) and fp32 128x128 block scales uniform over [1e-4, 1e-3] (seed
+``seed + 2``), the range of amax/448 for blocks of N(0, 0.02) weights.
 
 bf16 tensors are returned as numpy ``uint16`` bit patterns.
 """
@@ -82,6 +86,21 @@ def fp4_weights(N: int, K: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
     w = np.random.default_rng(seed).integers(0, 256, (N, K // 2), dtype=np.uint8)
     ws = np.random.default_rng(seed + 1).integers(116, 124, (N, K // 32)).astype(np.uint8)
     return w, ws
+
+
+def fp8_block_weights(N: int, K: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """FP8 weights [N, K]: e4m3fn code bytes (no NaN codes) and fp32 block scales [ceil(N/128), K/128]."""
+    w = np.random.default_rng(seed).integers(0, 254, (N, K), dtype=np.uint8)
+    w = w + (w >= 0x7F)                           # skip 0x7F: the 254 codes 0..0x7E, 0x80..0xFE
+    ws = np.random.default_rng(seed + 1).uniform(1e-4, 1e-3, (-(-N // 128), K // 128)).astype(np.float32)
+    return w.astype(np.uint8), ws
+
+
+def make_gemm8(M: int, N: int, K: int, seed: int = 40) -> dict:
+    """bf16 activations a [M, K] and FP8 block-scaled weights (w, ws) for the A16W8 GEMM."""
+    a = to_bf16_bits(normal_rows(M, K, seed, True))
+    w, ws = fp8_block_weights(N, K, seed + 1)
+    return {"a": a, "w": w, "ws": ws}
 
 
 def make_gemm(M: int, N: int, K: int, seed: int = 40) -> dict:

@@ -223,6 +223,46 @@ rmsq_status gemm_a16wfp4_prequant(const void* a, int64_t lda, const void* w, con
 rmsq_status mxfp4_weight_preshuffle(const void* w, const void* w_scale, int64_t N, int64_t K, void* w_out,
                                     void* w_scale_out, void* stream);
 
+/*
+ * gemm_a16w8_prequant: [ATT, required aiter changes] the a16w8 GEMM of the
+ * page's DS FP8 runs, with the activation quantization inside the GEMM as in
+ * gemm_a16wfp4_prequant:
+ *   out[m, n] = sum_k dq(a)[m, k] * dq(w)[n, k]
+ * where dq(a) is the FP8 group quantization (1x128 along K, fp32 scale
+ * amax/448, e4m3fn codes rounded to nearest even, as
+ * rmsnorm_quant_group_multi computes it for RMSQ_FMT_FP8_E4M3FN) of each bf16
+ * row of `a`, dequantized, and dq(w)[n, k] = w[n, k] * w_scale[n/128, k/128].
+ * Each 128-wide K block's sum of code products comes from the matrix cores
+ * and is scaled by the two scales and accumulated in fp32, in an order fixed
+ * for a given shape.
+ *
+ *  a        [M, K] bf16, row stride lda elements (lda >= K, lda % 8 == 0),
+ *           16-byte aligned, read only; finite values.
+ *  w        e4m3fn codes, N * K bytes in layout w_layout (RMSQ_W_ROW_MAJOR:
+ *           [N, K]; RMSQ_W_PRESHUFFLED: made by fp8_weight_preshuffle),
+ *           16-byte aligned; no NaN codes (0x7F, 0xFF).
+ *  w_scale  fp32 [ceil(N/128), K/128] row-major block scales, finite,
+ *           4-byte aligned.
+ *  out      [M, N] fp32, row stride ldc >= N, 4-byte aligned, written, must
+ *           not overlap the inputs.
+ *  M, N, K, ownership, errors and the stream as for gemm_a16wfp4_prequant,
+ *  except that M may be at most 65535 * 32.
+ */
+rmsq_status gemm_a16w8_prequant(const void* a, int64_t lda, const void* w, const void* w_scale, int32_t w_layout,
+                                int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, void* stream);
+
+/*
+ * fp8_weight_preshuffle: [ATT, required aiter changes] the a16w8 GEMM's
+ * weight preshuffle: rearranges row-major e4m3fn codes `w` [N, K] into the
+ * operand order of gemm_a16w8_prequant in `w_out` (N * K bytes, caller-owned,
+ * must not overlap `w`; both 16-byte aligned). For column tile t (rows 16t ..
+ * 16t+15), 128-wide K step s, half h in {0, 1} and lane l in 0..63, the 16
+ * bytes at ((t * K/128 + s) * 2 + h) * 64 + l (in 16-byte units) are bytes
+ * 128s + 32(l/16) + 16h .. +15 of row 16t + l%16. The block scales keep their
+ * layout. N, K and errors as for gemm_a16wfp4_prequant. Asynchronous.
+ */
+rmsq_status fp8_weight_preshuffle(const void* w, int64_t N, int64_t K, void* w_out, void* stream);
+
 /* 1 if HIP device `device` is a gfx950 (MI355X-class) GPU, else 0.
  * [ARQ, Motivation]: the single-kernel path is gated to gfx95x devices and
  * callers fall back otherwise; this library's entry points return

@@ -299,3 +299,35 @@ def test_preshuffle_validates():
     assert L.mxfp4_weight_preshuffle(None, s, 32, 256, wo, so, None) == E
     if not fq.rmsq_device_supported(0):
         assert L.mxfp4_weight_preshuffle(w, s, 32, 256, wo, so, None) == fq.RMSQ_ERR_UNSUPPORTED
+
+
+def test_gemm8_validates():
+    L = fq.lib()
+    E = fq.RMSQ_ERR_INVALID_ARG
+    w, s, o = A + 100 * MB, A + 200 * MB, A + 300 * MB
+
+    def g(a=A, lda=256, w=w, s=s, lay=fq.W_ROW_MAJOR, M=4, N=32, K=256, o=o, ldc=32):
+        # gemm_a16w8_prequant(a, lda, w, w_scale, w_layout, M, N, K, out, ldc, stream)
+        return L.gemm_a16w8_prequant(a, lda, w, s, lay, M, N, K, o, ldc, None)
+
+    assert g(N=24, ldc=24) == E          # N % 16
+    assert g(K=192, lda=192) == E        # K % 128
+    assert g(M=-1) == E
+    assert g(M=65535 * 32 + 1) == E      # more row blocks than the grid holds
+    assert g(lda=128) == E
+    assert g(ldc=16) == E
+    assert g(lay=2) == E
+    assert g(s=s + 2) == E               # scale alignment
+    assert g(w=w + 8) == E
+    assert g(o=w + 4096) == E            # out overlaps w (N * K = 8192 bytes)
+    assert g(o=s + 4) == E               # out overlaps the block scales (1 x 2 floats)
+    assert g(a=None) == E
+    assert g(M=0) == fq.RMSQ_OK
+    if not fq.rmsq_device_supported(0):
+        assert g() == fq.RMSQ_ERR_UNSUPPORTED
+    # fp8_weight_preshuffle(w, N, K, w_out, stream)
+    assert L.fp8_weight_preshuffle(w, 24, 256, o, None) == E
+    assert L.fp8_weight_preshuffle(w, 32, 256, w + 4096, None) == E
+    assert L.fp8_weight_preshuffle(w, 32, 256, o + 8, None) == E
+    if not fq.rmsq_device_supported(0):
+        assert L.fp8_weight_preshuffle(w, 32, 256, o, None) == fq.RMSQ_ERR_UNSUPPORTED

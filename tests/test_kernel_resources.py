@@ -85,6 +85,10 @@ def test_gemm_variants_fit_sixteen_waves(kernels):
     gemm = {n: k for n, k in kernels.items() if "rmsq_gemm_a16wfp4_kernel" in (n or "")}
     # (4 row-tile counts + the staged variant with 1 or 2 column tiles) x 2 weight layouts
     assert len(gemm) == 12, sorted(gemm)
+    gemm8 = {n: k for n, k in kernels.items() if "rmsq_gemm_a16w8_kernel" in (n or "")}
+    # (1 or 2 row tiles + the staged variant) x 2 weight layouts
+    assert len(gemm8) == 6, sorted(gemm8)
+    gemm.update(gemm8)
     for n, k in gemm.items():
         assert k["vgpr_count"] + k["agpr_count"] <= 128, (n, k)
         assert k["group_segment_fixed_size"] <= 64 * 1024, (n, k)
