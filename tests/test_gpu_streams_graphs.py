@@ -165,3 +165,59 @@ def test_graph_capture_of_a_mixed_set_two_launches(orc):
         assert np.array_equal(host(yb), wb["bf16"]) and np.array_equal(host(qb), wb["q"]), k
         assert np.array_equal(host(sb).reshape(-1).view(np.uint32), wb["scale"].reshape(-1).view(np.uint32)), k
         _ = (xb.float() * 2).sum().item()              # eager work between replays
+
+
+@pytest.mark.parametrize("fmt", [1, 0])
+def test_graph_capture_of_the_prequant_gemms(fmt):
+    """Both prequant GEMMs (preshuffled weights, staged activations at M = 4
+    and per-wave activations at M = 20) captured in one HIP graph: each
+    replay, with new activations copied in and eager work between replays,
+    equals the eager result bit for bit."""
+    say(f"HIP graph capture of the prequant GEMM (fmt {fmt})")
+    N, K = 2112, 7168
+    mk = inputs.make_gemm if fmt == 1 else inputs.make_gemm8
+    call = fq.gemm_a16wfp4_prequant if fmt == 1 else fq.gemm_a16w8_prequant
+    g = mk(20, N, K, seed=95)
+    w, ws = dev(g["w"]), dev(g["ws"])
+    sw = torch.empty_like(w)
+    if fmt == 1:
+        sws = torch.empty_like(ws)
+        fq.mxfp4_weight_preshuffle(w, ws, N, K, sw, sws)
+    else:
+        sws = ws
+        fq.fp8_weight_preshuffle(w, N, K, sw)
+    a = dev(g["a"])
+    a_alt = dev(mk(20, N, K, seed=96)["a"])
+    a_in = a.clone()
+    outs = [torch.zeros((M, N), dtype=torch.float32, device="cuda") for M in (4, 20)]
+
+    def launch():
+        for o in outs:
+            M = o.shape[0]
+            call(a_in, K, sw, sws, fq.W_PRESHUFFLED, M, N, K, o, N)
+
+    def eager(src):
+        a_in.copy_(src)
+        launch()
+        torch.cuda.synchronize()
+        return [host(o).copy() for o in outs]
+
+    want = [eager(a), eager(a_alt)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        launch()
+    for k in range(6):
+        a_in.copy_(a if k % 2 == 0 else a_alt)
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip([host(o) for o in outs], want[k % 2]):
+            assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), f"replay {k}"
+        _ = (a_in.float() * 2).sum().item()
