@@ -278,8 +278,8 @@ def copy_probe(launches):
     torch.cuda.synchronize()
 
 
-FUSED_SOURCES = ("rmsq_abi.hip", "rmsq_device.h", "rmsq_kernel.h")
-GEMM_SOURCES = ("rmsq_abi.hip", "rmsq_device.h", "rmsq_gemm.h")
+FUSED_SOURCES = ("rmsq_abi.hip", "rmsq_abi_common.h", "rmsq_device.h", "rmsq_kernel.h")
+GEMM_SOURCES = ("rmsq_gemm_abi.hip", "rmsq_abi_common.h", "rmsq_device.h", "rmsq_gemm.h")
 
 
 def kernel_source_hash(files=FUSED_SOURCES):

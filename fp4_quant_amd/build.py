@@ -7,6 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librmsq.so")
+# translation units of the library: the fused kernels' ABI and the GEMMs' ABI
+SOURCES = ("rmsq_abi.hip", "rmsq_gemm_abi.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [
@@ -15,6 +17,8 @@ HIP_FLAGS = [
     # no packed fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
+    # only the C ABI of include/rmsq.h is exported
+    "-fvisibility=hidden",
     # lane flags are combined with bitwise | on purpose: no short-circuit branches
     "-Wno-bitwise-instead-of-logical",
     # the fused kernel's 9 leading int arguments arrive preloaded in SGPRs
@@ -26,7 +30,7 @@ HIP_FLAGS = [
 
 def build(verbose: bool = False, extra=()) -> str:
     cmd = [HIPCC, *HIP_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(CSRC, "rmsq_abi.hip"), "-o", LIB + ".tmp"]
+           *[os.path.join(CSRC, f) for f in SOURCES], "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

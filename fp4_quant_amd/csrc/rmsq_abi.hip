@@ -11,10 +11,10 @@
 #include <cstring>
 
 #include "rmsq.h"
-#include "rmsq_gemm.h"
+#include "rmsq_abi_common.h"
 #include "rmsq_kernel.h"
 
-namespace {
+namespace rmsq_abi {
 
 thread_local char g_err[512];
 
@@ -26,14 +26,45 @@ rmsq_status fail(rmsq_status s, const char* fmt, ...) {
   return s;
 }
 
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+rmsq_status check_overlaps(const Range* rs, int nr) {
+  for (int i = 0; i < nr; ++i) {
+    if (!rs[i].output) continue;
+    for (int k = 0; k < nr; ++k) {
+      if (k == i || (k < i && rs[k].output)) continue;
+      const Range &a = rs[i], &b = rs[k];
+      if (a.lo >= b.hi || b.lo >= a.hi) continue;
+      // in-place residual: residual_out is exactly residual_in of the same problem
+      if (a.problem == b.problem && a.kind == 2 && b.kind == 1 && a.lo == b.lo && a.hi == b.hi) continue;
+      return fail(RMSQ_ERR_INVALID_ARG, "output buffer %d of problem %d overlaps buffer %d of problem %d", a.kind,
+                  a.problem, b.kind, b.problem);
+    }
+  }
+  return RMSQ_OK;
+}
 
-struct Range {
-  uintptr_t lo, hi;  // [lo, hi)
-  bool output;
-  int problem;
-  int kind;          // 0 x, 1 residual_in, 2 residual_out, 3 gamma, 4 q, 5 scale, 6 bf16
-};
+namespace {
+// gfx950 check, cached per device.
+std::atomic<int8_t> g_arch_ok[64];
+}  // namespace
+
+bool device_is_gfx950(int dev) {
+  if (dev < 0) return false;
+  if (dev < 64) {
+    const int8_t c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c) return c > 0;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  return ok;
+}
+
+}  // namespace rmsq_abi
+
+namespace {
+
+using namespace rmsq_abi;
 
 size_t scale_bytes(int64_t M, int64_t N, int32_t group, int32_t fmt, int32_t layout) {
   if (M < 0 || N <= 0 || group <= 0 || N % group) return 0;
@@ -118,38 +149,6 @@ rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Mode mod
   return RMSQ_OK;
 }
 
-rmsq_status check_overlaps(const Range* rs, int nr) {
-  for (int i = 0; i < nr; ++i) {
-    if (!rs[i].output) continue;
-    for (int k = 0; k < nr; ++k) {
-      if (k == i || (k < i && rs[k].output)) continue;
-      const Range &a = rs[i], &b = rs[k];
-      if (a.lo >= b.hi || b.lo >= a.hi) continue;
-      // in-place residual: residual_out is exactly residual_in of the same problem
-      if (a.problem == b.problem && a.kind == 2 && b.kind == 1 && a.lo == b.lo && a.hi == b.hi) continue;
-      return fail(RMSQ_ERR_INVALID_ARG, "output buffer %d of problem %d overlaps buffer %d of problem %d", a.kind,
-                  a.problem, b.kind, b.problem);
-    }
-  }
-  return RMSQ_OK;
-}
-
-// gfx950 check, cached per device.
-std::atomic<int8_t> g_arch_ok[64];
-
-bool device_is_gfx950(int dev) {
-  if (dev < 0) return false;
-  if (dev < 64) {
-    const int8_t c = g_arch_ok[dev].load(std::memory_order_relaxed);
-    if (c) return c > 0;
-  }
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
-  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
-  return ok;
-}
-
 // Launch shape: chunk-steps per lane J (compiled set) and waves per row W.
 // Measured on MI355X: spreading a row over several waves with 2-4 chunks per
 // lane sustains the traffic far better than long per-lane rows (one wave per
@@ -163,7 +162,6 @@ bool device_is_gfx950(int dev) {
 // 6.3 us against 6.8 us for J 2 x 7; at 512 rows J 2 x 7 is faster again).
 constexpr int kJs[] = {2, 3, 4, 1, 7, 8, 14};
 constexpr int kJsFewRows[] = {1, 2, 3, 4, 7, 8, 14};
-constexpr int64_t kComputeUnits = 256;
 constexpr int kWaveRowsPerBlock = 4;
 constexpr int kMaxSplits = 8;
 
@@ -396,225 +394,6 @@ rmsq_status run_quant(const rmsq_problem& p, void* stream) {
   return RMSQ_OK;
 }
 
-// The A16WFP4 prequant GEMM: grid x = 16-column tiles of the output, y =
-// blocks of 64 rows; the row tiles per block (MT) follow M.
-template <bool SHUF>
-void launch_gemm(const rmsq::GemmArgs& G, int MT, int CT, bool staged, int waves, hipStream_t s) {
-  const dim3 grid((unsigned)(G.N / (16 * CT)),
-                  (unsigned)((G.M + rmsq::kGemmRowsPerBlock - 1) / rmsq::kGemmRowsPerBlock)),
-      block(64 * waves);
-  const size_t lds = rmsq::gemm_lds_bytes(staged, G.M, G.K, MT, CT, waves);
-  constexpr int SS = rmsq::kGemmStagedSteps;
-  if (staged && CT == 2) {
-    hipLaunchKernelGGL((rmsq::rmsq_gemm_a16wfp4_kernel<1, SS, SHUF, true, 2>), grid, block, lds, s, G);
-    return;
-  }
-  if (staged) {
-    hipLaunchKernelGGL((rmsq::rmsq_gemm_a16wfp4_kernel<1, SS, SHUF, true, 1>), grid, block, lds, s, G);
-    return;
-  }
-  switch (MT) {
-    case 1: hipLaunchKernelGGL((rmsq::rmsq_gemm_a16wfp4_kernel<1, 4, SHUF, false, 1>), grid, block, lds, s, G); break;
-    case 2: hipLaunchKernelGGL((rmsq::rmsq_gemm_a16wfp4_kernel<2, 2, SHUF, false, 1>), grid, block, lds, s, G); break;
-    case 3: hipLaunchKernelGGL((rmsq::rmsq_gemm_a16wfp4_kernel<3, 1, SHUF, false, 1>), grid, block, lds, s, G); break;
-    default: hipLaunchKernelGGL((rmsq::rmsq_gemm_a16wfp4_kernel<4, 1, SHUF, false, 1>), grid, block, lds, s, G); break;
-  }
-}
-
-rmsq_status check_gemm_weights(int64_t N, int64_t K) {
-  if (N <= 0 || K <= 0 || N % 16 || K % 128)
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: need N a positive multiple of 16 and K a positive multiple of 128 "
-                "(N=%lld K=%lld)", (long long)N, (long long)K);
-  if (K > RMSQ_GEMM_K_MAX || N > RMSQ_GEMM_N_MAX)
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: N=%lld K=%lld beyond the supported sizes", (long long)N, (long long)K);
-  return RMSQ_OK;
-}
-
-rmsq_status run_gemm(const void* a, int64_t lda, const void* w, const void* w_scale, int32_t w_layout, int64_t M,
-                     int64_t N, int64_t K, void* out, int64_t ldc, void* stream) {
-  g_err[0] = 0;
-  if (const rmsq_status st = check_gemm_weights(N, K); st != RMSQ_OK) return st;
-  if (M < 0 || (M + rmsq::kGemmRowsPerBlock - 1) / rmsq::kGemmRowsPerBlock > 65535)
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: M=%lld outside [0, 65535 * 64]", (long long)M);
-  if (w_layout != RMSQ_W_ROW_MAJOR && w_layout != RMSQ_W_PRESHUFFLED)
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: unknown weight layout %d", w_layout);
-  if (lda < K || lda % 8 || ldc < N)
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: need lda >= K with lda %% 8 == 0 and ldc >= N (lda=%lld ldc=%lld)",
-                (long long)lda, (long long)ldc);
-  if (M == 0) return RMSQ_OK;
-  if (!a || !w || !w_scale || !out) return fail(RMSQ_ERR_INVALID_ARG, "gemm: NULL buffer");
-  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 4))
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: a and w must be 16-byte aligned, out 4-byte aligned");
-  Range rs[4];
-  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pw = reinterpret_cast<uintptr_t>(w),
-                  ps = reinterpret_cast<uintptr_t>(w_scale), po = reinterpret_cast<uintptr_t>(out);
-  rs[0] = {pa, pa + (uintptr_t)(((M - 1) * lda + K) * 2), false, 0, 0};
-  rs[1] = {pw, pw + (uintptr_t)(N * (K / 2)), false, 0, 3};
-  rs[2] = {ps, ps + (uintptr_t)(N * (K / 32)), false, 0, 5};
-  rs[3] = {po, po + (uintptr_t)(((M - 1) * ldc + N) * 4), true, 0, 4};
-  if (const rmsq_status st = check_overlaps(rs, 4); st != RMSQ_OK) return st;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
-    return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");
-  rmsq::GemmArgs G;
-  G.a = static_cast<const uint16_t*>(a);
-  G.w = static_cast<const uint8_t*>(w);
-  G.ws = static_cast<const uint8_t*>(w_scale);
-  G.out = static_cast<float*>(out);
-  G.lda = lda;
-  G.ldc = ldc;
-  G.M = (int32_t)M;
-  G.N = (int32_t)N;
-  G.K = (int32_t)K;
-  // Row tiles per block and waves per workgroup. Staged activations (at most
-  // 4 rows): enough waves that each covers at most 4 steps and each thread
-  // at most 4 chunks of 8 elements. Otherwise SW steps per batch (registers:
-  // 16 per step and tile for the activations, 5 for the weights) and enough
-  // waves that each wave's K range is one batch, at most 16.
-  const int MT = M >= 64 ? 4 : (int)((M + 15) / 16);
-  const int steps = (int)(K / 128);
-  const int64_t chunks = M * (K / 8);
-  const int staged_waves =
-      (int)std::max<int64_t>((steps + rmsq::kGemmStagedSteps - 1) / rmsq::kGemmStagedSteps,
-                             (chunks + 64 * rmsq::kGemmStagedChunks - 1) / (64 * rmsq::kGemmStagedChunks));
-  const bool staged = M <= rmsq::kGemmStagedRows && staged_waves <= rmsq::kGemmMaxWaves;
-  const int SW = MT == 1 ? 4 : MT == 2 ? 2 : 1;
-  const int waves = staged ? staged_waves : std::min(rmsq::kGemmMaxWaves, std::max(1, (steps + SW - 1) / SW));
-  // Two column tiles per staged workgroup once there are at least 256 tiles:
-  // half as many workgroups each stage the activations for twice the weights.
-  const int CT = staged && (N / 16) % 2 == 0 && N / 16 >= kComputeUnits ? 2 : 1;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (w_layout == RMSQ_W_PRESHUFFLED)
-    launch_gemm<true>(G, MT, CT, staged, waves, s);
-  else
-    launch_gemm<false>(G, MT, CT, staged, waves, s);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return RMSQ_OK;
-}
-
-// The A16W8 prequant GEMM: the same grid as the A16WFP4 one, one column tile
-// per workgroup.
-template <bool SHUF>
-void launch_gemm8(const rmsq::Gemm8Args& G, int MT, bool staged, int waves, hipStream_t s) {
-  const dim3 grid((unsigned)(G.N / 16), (unsigned)((G.M + 16 * MT - 1) / (16 * MT))), block(64 * waves);
-  const size_t lds = rmsq::gemm8_lds_bytes(staged, G.M, G.K, MT, waves);
-  if (staged)
-    hipLaunchKernelGGL((rmsq::rmsq_gemm_a16w8_kernel<1, rmsq::kGemmStagedSteps, SHUF, true>), grid, block, lds, s, G);
-  else if (MT == 1)
-    hipLaunchKernelGGL((rmsq::rmsq_gemm_a16w8_kernel<1, 2, SHUF, false>), grid, block, lds, s, G);
-  else
-    hipLaunchKernelGGL((rmsq::rmsq_gemm_a16w8_kernel<2, 1, SHUF, false>), grid, block, lds, s, G);
-}
-
-rmsq_status run_gemm8(const void* a, int64_t lda, const void* w, const void* w_scale, int32_t w_layout, int64_t M,
-                      int64_t N, int64_t K, void* out, int64_t ldc, void* stream) {
-  g_err[0] = 0;
-  if (const rmsq_status st = check_gemm_weights(N, K); st != RMSQ_OK) return st;
-  if (M < 0 || (M + 16 * rmsq::kGemm8MaxTiles - 1) / (16 * rmsq::kGemm8MaxTiles) > 65535)
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: M=%lld outside [0, 65535 * 32]", (long long)M);
-  if (w_layout != RMSQ_W_ROW_MAJOR && w_layout != RMSQ_W_PRESHUFFLED)
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: unknown weight layout %d", w_layout);
-  if (lda < K || lda % 8 || ldc < N)
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: need lda >= K with lda %% 8 == 0 and ldc >= N (lda=%lld ldc=%lld)",
-                (long long)lda, (long long)ldc);
-  if (M == 0) return RMSQ_OK;
-  if (!a || !w || !w_scale || !out) return fail(RMSQ_ERR_INVALID_ARG, "gemm: NULL buffer");
-  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(w_scale, 4) || !aligned(out, 4))
-    return fail(RMSQ_ERR_INVALID_ARG, "gemm: a and w must be 16-byte aligned, w_scale and out 4-byte aligned");
-  Range rs[4];
-  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pw = reinterpret_cast<uintptr_t>(w),
-                  ps = reinterpret_cast<uintptr_t>(w_scale), po = reinterpret_cast<uintptr_t>(out);
-  rs[0] = {pa, pa + (uintptr_t)(((M - 1) * lda + K) * 2), false, 0, 0};
-  rs[1] = {pw, pw + (uintptr_t)(N * K), false, 0, 3};
-  rs[2] = {ps, ps + (uintptr_t)(((N + 127) / 128) * (K / 128) * 4), false, 0, 5};
-  rs[3] = {po, po + (uintptr_t)(((M - 1) * ldc + N) * 4), true, 0, 4};
-  if (const rmsq_status st = check_overlaps(rs, 4); st != RMSQ_OK) return st;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
-    return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");
-  rmsq::Gemm8Args G;
-  G.a = static_cast<const uint16_t*>(a);
-  G.w = static_cast<const uint8_t*>(w);
-  G.ws = static_cast<const float*>(w_scale);
-  G.out = static_cast<float*>(out);
-  G.lda = lda;
-  G.ldc = ldc;
-  G.M = (int32_t)M;
-  G.N = (int32_t)N;
-  G.K = (int32_t)K;
-  // as for the A16WFP4 GEMM, with 8 registers per step for the weights and
-  // 16 per step and tile for the activations, at most two row tiles
-  const int MT = M > 16 ? 2 : 1;
-  const int steps = (int)(K / 128);
-  const int64_t chunks = M * (K / 8);
-  const int staged_waves =
-      (int)std::max<int64_t>((steps + rmsq::kGemmStagedSteps - 1) / rmsq::kGemmStagedSteps,
-                             (chunks + 64 * rmsq::kGemmStagedChunks - 1) / (64 * rmsq::kGemmStagedChunks));
-  const bool staged = M <= rmsq::kGemmStagedRows && staged_waves <= rmsq::kGemmMaxWaves;
-  const int SW = MT == 1 ? 2 : 1;
-  const int waves = staged ? staged_waves : std::min(rmsq::kGemmMaxWaves, std::max(1, (steps + SW - 1) / SW));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (w_layout == RMSQ_W_PRESHUFFLED)
-    launch_gemm8<true>(G, MT, staged, waves, s);
-  else
-    launch_gemm8<false>(G, MT, staged, waves, s);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return RMSQ_OK;
-}
-
-rmsq_status run_preshuffle8(const void* w, int64_t N, int64_t K, void* w_out, void* stream) {
-  g_err[0] = 0;
-  if (const rmsq_status st = check_gemm_weights(N, K); st != RMSQ_OK) return st;
-  if (!w || !w_out) return fail(RMSQ_ERR_INVALID_ARG, "preshuffle: NULL buffer");
-  if (!aligned(w, 16) || !aligned(w_out, 16))
-    return fail(RMSQ_ERR_INVALID_ARG, "preshuffle: w and w_out must be 16-byte aligned");
-  Range rs[2];
-  const uintptr_t pw = reinterpret_cast<uintptr_t>(w), qw = reinterpret_cast<uintptr_t>(w_out);
-  rs[0] = {pw, pw + (uintptr_t)(N * K), false, 0, 3};
-  rs[1] = {qw, qw + (uintptr_t)(N * K), true, 0, 4};
-  if (const rmsq_status st = check_overlaps(rs, 2); st != RMSQ_OK) return st;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
-    return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");
-  const int64_t units = N * (K / 16);
-  const unsigned blocks = (unsigned)std::min<int64_t>((units + 255) / 256, 4096);
-  hipLaunchKernelGGL(rmsq::rmsq_fp8_preshuffle_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint8_t*>(w), static_cast<uint8_t*>(w_out), (int32_t)K, units);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return RMSQ_OK;
-}
-
-rmsq_status run_preshuffle(const void* w, const void* w_scale, int64_t N, int64_t K, void* w_out, void* w_scale_out,
-                           void* stream) {
-  g_err[0] = 0;
-  if (const rmsq_status st = check_gemm_weights(N, K); st != RMSQ_OK) return st;
-  if (!w || !w_scale || !w_out || !w_scale_out) return fail(RMSQ_ERR_INVALID_ARG, "preshuffle: NULL buffer");
-  if (!aligned(w, 16) || !aligned(w_out, 16))
-    return fail(RMSQ_ERR_INVALID_ARG, "preshuffle: w and w_out must be 16-byte aligned");
-  Range rs[4];
-  const uintptr_t pw = reinterpret_cast<uintptr_t>(w), ps = reinterpret_cast<uintptr_t>(w_scale),
-                  qw = reinterpret_cast<uintptr_t>(w_out), qs = reinterpret_cast<uintptr_t>(w_scale_out);
-  rs[0] = {pw, pw + (uintptr_t)(N * (K / 2)), false, 0, 3};
-  rs[1] = {ps, ps + (uintptr_t)(N * (K / 32)), false, 0, 5};
-  rs[2] = {qw, qw + (uintptr_t)(N * (K / 2)), true, 0, 4};
-  rs[3] = {qs, qs + (uintptr_t)(N * (K / 32)), true, 0, 5};
-  if (const rmsq_status st = check_overlaps(rs, 4); st != RMSQ_OK) return st;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
-    return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");
-  const int64_t units = N * (K / 32);
-  const unsigned blocks = (unsigned)std::min<int64_t>((units + 255) / 256, 4096);
-  hipLaunchKernelGGL(rmsq::rmsq_mxfp4_preshuffle_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(w_scale),
-                     static_cast<uint8_t*>(w_out), static_cast<uint8_t*>(w_scale_out), (int32_t)K, units);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return RMSQ_OK;
-}
-
 }  // namespace
 
 extern "C" {
@@ -672,25 +451,6 @@ rmsq_status dynamic_per_group_scaled_quant(const void* x, int64_t M, int64_t N, 
   p.out_q = out_q;
   p.out_scale = out_scale;
   return run_quant(p, stream);
-}
-
-rmsq_status gemm_a16wfp4_prequant(const void* a, int64_t lda, const void* w, const void* w_scale, int32_t w_layout,
-                                  int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, void* stream) {
-  return run_gemm(a, lda, w, w_scale, w_layout, M, N, K, out, ldc, stream);
-}
-
-rmsq_status mxfp4_weight_preshuffle(const void* w, const void* w_scale, int64_t N, int64_t K, void* w_out,
-                                    void* w_scale_out, void* stream) {
-  return run_preshuffle(w, w_scale, N, K, w_out, w_scale_out, stream);
-}
-
-rmsq_status gemm_a16w8_prequant(const void* a, int64_t lda, const void* w, const void* w_scale, int32_t w_layout,
-                                int64_t M, int64_t N, int64_t K, void* out, int64_t ldc, void* stream) {
-  return run_gemm8(a, lda, w, w_scale, w_layout, M, N, K, out, ldc, stream);
-}
-
-rmsq_status fp8_weight_preshuffle(const void* w, int64_t N, int64_t K, void* w_out, void* stream) {
-  return run_preshuffle8(w, N, K, w_out, stream);
 }
 
 int32_t rmsq_device_supported(int32_t device) {

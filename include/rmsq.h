@@ -49,6 +49,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility; these declarations are its
+ * exported interface. */
+#pragma GCC visibility push(default)
+
 typedef int32_t rmsq_status;
 #define RMSQ_OK 0
 #define RMSQ_ERR_INVALID_ARG 1 /* bad pointer, alignment, stride, shape or overlap */
@@ -313,6 +317,8 @@ void rmsq_set_row_splits(int32_t S);
  * of 8 elements per lane and W waves per workgroup (one workgroup per row).
  * RMSQ_ERR_INVALID_ARG for N outside (0, RMSQ_N_MAX] or not a multiple of 8. */
 rmsq_status rmsq_query_shape(int64_t N, int64_t rows, int32_t* J, int32_t* W);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

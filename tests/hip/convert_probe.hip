@@ -156,6 +156,8 @@ static int launch_status() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 
 #define GRID(n) dim3((unsigned)(((n) + 255) / 256 < 65536 ? ((n) + 255) / 256 : 65536)), dim3(256), 0, (hipStream_t)stream
 
+// exported: the library is built with hidden visibility
+#pragma GCC visibility push(default)
 extern "C" {
 int probe_norm_bf16(const float* h, const float* g, const double* inv, const uint8_t* ex, uint16_t* out, int64_t n,
                     void* stream) {
@@ -236,3 +238,4 @@ int probe_fp8_exact(const float* v, const float* s, uint8_t* out, int64_t n, voi
   return launch_status();
 }
 }
+#pragma GCC visibility pop

@@ -199,6 +199,8 @@ __global__ void k_empty(int* p) {
 
 static int st_rc() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 
+// exported: the library is built with hidden visibility
+#pragma GCC visibility push(default)
 extern "C" {
 // kind: 0 read, 1 write, 2 copy, 3 FP8 mix, 4 MXFP4 mix (nontemporal only); nt: nontemporal
 // hints; blocks/threads: launch shape.
@@ -275,3 +277,4 @@ int stream_probe_empty(int blocks, int threads, void* stream) {
   return st_rc();
 }
 }
+#pragma GCC visibility pop

@@ -331,3 +331,14 @@ def test_gemm8_validates():
     assert L.fp8_weight_preshuffle(w, 32, 256, o + 8, None) == E
     if not fq.rmsq_device_supported(0):
         assert L.fp8_weight_preshuffle(w, 32, 256, o, None) == fq.RMSQ_ERR_UNSUPPORTED
+
+
+def test_library_exports_only_the_declared_interface():
+    """Built with hidden visibility: the dynamic symbol table holds the C ABI
+    of include/rmsq.h and nothing else of the library's own code."""
+    import shutil
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", fq.LIB_PATH], capture_output=True, text=True, check=True)
+    text_syms = {l.split()[-1] for l in out.stdout.splitlines() if len(l.split()) == 3 and l.split()[1] == "T"}
+    assert text_syms == set(_declared_functions())

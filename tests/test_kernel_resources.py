@@ -25,16 +25,20 @@ NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)ELb
 
 @pytest.fixture(scope="module")
 def kernels():
+    text = ""
     with tempfile.TemporaryDirectory() as d:
-        out = os.path.join(d, "k.s")
-        flags = [f for f in B.HIP_FLAGS if f not in ("-shared", "-fPIC")]
-        subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", "-I", os.path.join(B.ROOT, "include"),
-                        "-I", B.CSRC, os.path.join(B.CSRC, "rmsq_abi.hip"), "-o", out],
-                       check=True, capture_output=True)
-        text = open(out).read()
-    meta = text[text.index("amdhsa.kernels:"):]
+        for src in B.SOURCES:
+            out = os.path.join(d, src + ".s")
+            flags = [f for f in B.HIP_FLAGS if f not in ("-shared", "-fPIC")]
+            subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", "-I", os.path.join(B.ROOT, "include"),
+                            "-I", B.CSRC, os.path.join(B.CSRC, src), "-o", out],
+                           check=True, capture_output=True)
+            text += open(out).read()
     ks = {}
-    for block in re.split(r"\n  - ", meta)[1:]:
+    blocks = []
+    for part in text.split("amdhsa.kernels:")[1:]:
+        blocks += re.split(r"\n  - ", part)[1:]
+    for block in blocks:
         def field(k):
             m = re.search(r"\." + k + r":\s+(\S+)", block)
             return m.group(1) if m else None
