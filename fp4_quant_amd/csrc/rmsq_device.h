@@ -155,10 +155,9 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
 // rounding is the correctly rounded one. Smaller amax uses the IEEE fp32
 // division (denormals kept).
 __device__ __forceinline__ float fp8_scale(uint32_t amax_bits) {
-  if (amax_bits == 0) return 1.0f;
   const float a = __uint_as_float(amax_bits << 16);
-  if (amax_bits >= 0x0D80u) return (float)((double)a * (1.0 / 448.0));
-  return a / 448.0f;
+  if (__builtin_expect(amax_bits < 0x0D80u, 0)) return amax_bits == 0 ? 1.0f : a / 448.0f;
+  return (float)((double)a * (1.0 / 448.0));
 }
 
 // e4m3fn codes of v[e] / s for 8 bf16 values v (as fp32) of one group, bytes
