@@ -277,3 +277,58 @@ def fused_rmsnorm_quant(x, gamma, eps=1e-6, residual=None, fmt="fp8", keep_bf16=
                      out_bf16=yb, fmt=f, scale_layout=lay)
     rmsnorm_quant_group_multi([p], stream)
     return ((yb, q, scale) if keep_bf16 else (q, scale)), res_out
+
+
+def preshuffle_weights(w, w_scale, fmt="mxfp4", stream=None):
+    """The prequant GEMM's faster weight layout, made once per weight matrix.
+
+    ``fmt="mxfp4"``: ``w`` [N, K/2] uint8 e2m1 codes and ``w_scale`` [N, K/32]
+    uint8 e8m0 bytes; returns both rearranged. ``fmt="fp8"``: ``w`` [N, K]
+    uint8 e4m3fn codes (``w_scale``, the [ceil(N/128), K/128] fp32 block
+    scales, keeps its layout and is returned as is)."""
+    import torch
+    N = w.shape[0]
+    if fmt == "mxfp4":
+        K = w.shape[1] * 2
+        sw, sws = torch.empty_like(w), torch.empty_like(w_scale)
+        mxfp4_weight_preshuffle(w, w_scale, N, K, sw, sws, stream)
+        return sw, sws
+    if fmt == "fp8":
+        K = w.shape[1]
+        sw = torch.empty_like(w)
+        fp8_weight_preshuffle(w, N, K, sw, stream)
+        return sw, w_scale
+    raise ValueError(f"unknown weight format {fmt!r}")
+
+
+def prequant_gemm(a, w, w_scale, fmt="mxfp4", preshuffled=False, out=None, stream=None):
+    """out = a @ w^T with the bf16 activations ``a`` [M, K] quantized inside the
+    GEMM: ``fmt="mxfp4"`` (1x32 MXFP4 groups; ``w`` [N, K/2] e2m1 codes,
+    ``w_scale`` [N, K/32] e8m0 bytes) or ``fmt="fp8"`` (1x128 FP8 groups;
+    ``w`` [N, K] e4m3fn codes, ``w_scale`` [ceil(N/128), K/128] fp32 block
+    scales). ``preshuffled``: the weights come from ``preshuffle_weights``.
+    Returns the fp32 [M, N] output (``out`` if given)."""
+    import torch
+    if a.dtype != torch.bfloat16 or a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be a 2-D bf16 tensor with unit column stride")
+    if w.dtype != torch.uint8 or not w.is_contiguous() or not w_scale.is_contiguous():
+        raise ValueError("w must be contiguous uint8 codes and w_scale contiguous")
+    M, K = a.shape
+    N = w.shape[0]
+    if fmt == "mxfp4":
+        if w.shape != (N, K // 2) or w_scale.dtype != torch.uint8 or w_scale.numel() != N * (K // 32):
+            raise ValueError("MXFP4 weights: w [N, K/2] uint8 and w_scale [N, K/32] uint8")
+        call = gemm_a16wfp4_prequant
+    elif fmt == "fp8":
+        if w.shape != (N, K) or w_scale.dtype != torch.float32 or w_scale.numel() != -(-N // 128) * (K // 128):
+            raise ValueError("FP8 weights: w [N, K] uint8 and w_scale [ceil(N/128), K/128] float32")
+        call = gemm_a16w8_prequant
+    else:
+        raise ValueError(f"unknown weight format {fmt!r}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    elif out.dtype != torch.float32 or out.shape != (M, N) or out.stride(1) != 1:
+        raise ValueError("out must be a float32 [M, N] tensor with unit column stride")
+    call(a, a.stride(0), w, w_scale, W_PRESHUFFLED if preshuffled else W_ROW_MAJOR, M, N, K, out, out.stride(0),
+         stream)
+    return out

@@ -375,3 +375,23 @@ def test_gemm8_layouts_agree_bit_for_bit(M):
     r0 = run_gemm8(g["a"], g["w"], g["ws"], layout=fq.W_ROW_MAJOR)
     r1 = run_gemm8(g["a"], g["w"], g["ws"], layout=fq.W_PRESHUFFLED)
     assert np.array_equal(r0.view(np.uint32), r1.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+def test_python_wrappers(orc, fmt):
+    """prequant_gemm / preshuffle_weights allocate, check and call the C ABI:
+    the same bits as the raw entry points, on a strided activation view."""
+    M, N, K = 4, 64, 512
+    g = (inputs.make_gemm if fmt == "mxfp4" else inputs.make_gemm8)(M, N, K, seed=190)
+    a_full = dev(np.concatenate([g["a"], np.zeros((M, 64), np.uint16)], axis=1))
+    a = a_full[:, :K]
+    w, ws = dev(g["w"]), dev(g["ws"])
+    r_plain = fq.prequant_gemm(a, w, ws, fmt=fmt)
+    sw, sws = fq.preshuffle_weights(w, ws, fmt=fmt)
+    r_shuf = fq.prequant_gemm(a, sw, sws, fmt=fmt, preshuffled=True)
+    torch.cuda.synchronize()
+    raw = (run_gemm if fmt == "mxfp4" else run_gemm8)(g["a"], g["w"], g["ws"])
+    assert np.array_equal(host(r_plain).view(np.uint32), raw.view(np.uint32))
+    assert np.array_equal(host(r_shuf).view(np.uint32), raw.view(np.uint32))
+    with pytest.raises(ValueError):
+        fq.prequant_gemm(a.float(), w, ws, fmt=fmt)
