@@ -29,12 +29,14 @@
 // bytes contiguous (codes) and 64 bytes (scales), so every weight load of a
 // wave reads 1 KiB of consecutive bytes.
 //
-// Activations: with at most 4 rows and one batch of steps per wave, the
-// workgroup first loads its rows with all lanes (consecutive 16-byte chunks,
-// issued before the weight loads so the two latencies overlap), quantizes
-// each 32-group once in lane quads, and keeps the codes in LDS, from where
-// each wave reads its operands. Otherwise each wave loads and quantizes the
-// 32-groups of its own operands (lanes of rows past M load nothing).
+// Activations: with at most 4 rows and one batch of steps per wave, a wave's
+// 64 activation groups are one per lane: every lane loads and quantizes one
+// (loads issued before the weight loads, so the two latencies overlap), and
+// the operand lanes fetch the codes with ds_bpermute; no workgroup barrier
+// precedes the matrix-core steps. Otherwise each wave loads and quantizes the
+// 32-groups of its own operands (lanes of rows past M read row M-1; their
+// results are not stored). All loads of a batch are unconditional: a load
+// under a branch would make the first use of any later load wait for it.
 #pragma once
 
 #include <algorithm>
@@ -57,9 +59,8 @@ struct GemmArgs {
 
 constexpr int kGemmMaxWaves = 16;
 constexpr int kGemmRowsPerBlock = 64;   // 4 tiles of 16 rows
-constexpr int kGemmStagedRows = 4;      // at most this many activation rows are staged in LDS
-constexpr int kGemmStagedChunks = 4;    // 8-element chunks per lane when staging
-constexpr int kGemmStagedSteps = 4;     // steps per wave when staging (one batch)
+constexpr int kGemmStagedRows = 4;      // at most this many rows take the small-M path
+constexpr int kGemmStagedSteps = 4;     // steps per wave on the small-M path (one batch)
 
 // MXFP4 quantization of one 32-element bf16 group held by one lane (16
 // packed dwords): the e8m0 byte and the 4 dwords of e2m1 codes.
@@ -73,20 +74,16 @@ __device__ __forceinline__ uint32_t mx_group32(const u32x4 v[4], u32x4* codes) {
   return byte;
 }
 
-// LDS bytes the kernel needs: the staged activation codes and scales, or the
-// waves' partial sums, whichever is larger (the partial sums reuse the
-// staging area after a barrier).
-inline size_t gemm_lds_bytes(bool staged, int rows, int K, int MT, int CT, int waves) {
-  const size_t stage = staged ? (size_t)(K / 32) * rows * 17 : 0;
-  const size_t part = (size_t)(waves - 1) * MT * CT * 64 * sizeof(v4f32);
-  return (std::max(stage, part) + 15) & ~(size_t)15;
+// LDS bytes the kernel needs: the waves' partial sums.
+inline size_t gemm_lds_bytes(int MT, int CT, int waves) {
+  return (size_t)(waves - 1) * MT * CT * 64 * sizeof(v4f32);
 }
 
 // MT row tiles of 16 rows and CT column tiles per workgroup, SW steps
-// loaded per batch, SHUF: preshuffled weights, STAGED: activations staged in
-// LDS (MT == 1, SW == kGemmStagedSteps, M <= kGemmStagedRows, M * K/8 <= 4
-// chunks per thread, every wave's steps in one batch); CT > 1 only when
-// staged, where a wave reuses each activation operand for CT tiles.
+// loaded per batch, SHUF: preshuffled weights, STAGED: the small-M path (MT ==
+// 1, SW == kGemmStagedSteps, M <= kGemmStagedRows, every wave's steps in one
+// batch); CT > 1 only there, where a wave reuses each activation operand for
+// CT tiles.
 template <int MT, int SW, bool SHUF, bool STAGED, int CT>
 __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16wfp4_kernel(const GemmArgs G) {
   static_assert(CT == 1 || STAGED, "several column tiles only with staged activations");
@@ -127,16 +124,19 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16wfp4_kernel(c
   for (int t = 0; t < MT * CT; ++t) acc[t] = v4f32{0.0f, 0.0f, 0.0f, 0.0f};
 
   if constexpr (STAGED) {
-    // rows 0 .. R-1 (a single row block), 8-element chunk c = r * K/8 + kc
+    // Small M: the wave's batch of SW = 4 steps needs at most 4 rows x 16
+    // activation groups, one per lane: lane L holds step i = L/16, row
+    // min(L/4 % 4, M-1), 32-element quarter L%4, loaded with all lanes and
+    // quantized in place; the operand lane of row r, quarter kb then fetches
+    // it from lane 16 i + 4 r + kb (ds_bpermute). No workgroup barrier
+    // precedes the matrix-core steps.
     const int R = G.M;
-    const int C8 = G.K >> 3, total = R * C8, T = blockDim.x;
-    u32x4 v[kGemmStagedChunks];
+    const int ai = lane >> 4, ar = min((lane >> 2) & 3, R - 1), aq = lane & 3;
+    const int ast = min(s_lo + ai, s_hi - 1);
+    const u32x4* ap = reinterpret_cast<const u32x4*>(G.a + (int64_t)ar * G.lda) + ast * 16 + aq * 4;
+    u32x4 av[4];
 #pragma unroll
-    for (int u = 0; u < kGemmStagedChunks; ++u) {
-      const int c = min((int)threadIdx.x + u * T, total - 1);
-      const int r = c / C8, kc = c - r * C8;
-      v[u] = reinterpret_cast<const u32x4*>(G.a + (int64_t)r * G.lda)[kc];
-    }
+    for (int j = 0; j < 4; ++j) av[j] = ap[j];
     __builtin_amdgcn_sched_barrier(0);
     u32x4 bw[CT][SW];
     uint32_t sb[CT][SW];
@@ -144,44 +144,26 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16wfp4_kernel(c
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int i = 0; i < SW; ++i) {
-        bw[ct][i] = u32x4{0u, 0u, 0u, 0u};
-        sb[ct][i] = 127u;
-        if (s_lo + i < s_hi) {
-          bw[ct][i] = wq[ct * wq_tile + (s_lo + i) * ws_step];
-          sb[ct][i] = wsc[ct * ws_tile + (s_lo + i) * ws_step];
-        }
+        const int st = min(s_lo + i, s_hi - 1);   // steps past the range re-read the last (unused)
+        bw[ct][i] = wq[ct * wq_tile + st * ws_step];
+        sb[ct][i] = wsc[ct * ws_tile + st * ws_step];
       }
     __builtin_amdgcn_sched_barrier(0);
-    // codes of group g of row r at LDS byte (g * R + r) * 16, its scale byte
-    // at NG * R * 16 + g * R + r; a lane quad holds the four chunks of a
-    // group (T is a multiple of 64 and K/8 of 16, so quads never straddle
-    // groups or rows, and every lane of a quad is in or out of range alike)
-    const int NG = G.K >> 5;
-    uint8_t* codes = lds;
-    uint8_t* scl = lds + NG * R * 16;
-#pragma unroll
-    for (int u = 0; u < kGemmStagedChunks; ++u) {
-      const int c = threadIdx.x + u * T;
-      const uint32_t byte = mx_scale_byte(max4(amax8(v[u])));
-      const uint32_t cw = fp4_codes8(v[u], byte);
-      if (c < total) {
-        const int r = c / C8, kc = c - r * C8, g = kc >> 2, d = kc & 3;
-        *reinterpret_cast<uint32_t*>(codes + (g * R + r) * 16 + d * 4) = cw;
-        if (d == 0) scl[g * R + r] = (uint8_t)byte;
-      }
-    }
-    __syncthreads();
+    u32x4 qa;
+    const uint32_t byte = mx_group32(av, &qa);
     const int r = lane & 15;
     const bool live = r < R;
 #pragma unroll
     for (int i = 0; i < SW; ++i) {
       if (s_lo + i >= s_hi) break;
-      const int g = (s_lo + i) * 4 + kb;
-      u32x4 q = u32x4{0u, 0u, 0u, 0u};
-      uint32_t sa = 127u;
-      if (live) {
-        q = *reinterpret_cast<const u32x4*>(codes + (g * R + r) * 16);
-        sa = scl[g * R + r];
+      const int src = (16 * i + 4 * min(r, 3) + kb) << 2;   // ds_bpermute byte address
+      u32x4 q;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) q[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)qa[d]);
+      uint32_t sa = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)byte);
+      if (!live) {
+        q = u32x4{0u, 0u, 0u, 0u};
+        sa = 127u;
       }
       const v8i32 aop = {(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
 #pragma unroll
@@ -191,38 +173,31 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16wfp4_kernel(c
                                                                    (int)sb[ct][i]);
       }
     }
-    __syncthreads();   // the partial sums below reuse the staging area
   } else {
-    // activation row of this lane in each tile; rows past M are not loaded
+    // activation row of this lane in each tile; lanes of rows past M read
+    // row M-1 (their results are not stored)
     const u32x4* arow[MT];
-    bool live[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int m = m0 + 16 * t + (lane & 15);
-      live[t] = m < G.M;
       arow[t] = reinterpret_cast<const u32x4*>(G.a + (int64_t)min(m, G.M - 1) * G.lda);
     }
     for (int s0 = s_lo; s0 < s_hi; s0 += SW) {
       u32x4 bw[SW];
       uint32_t sb[SW];
       u32x4 av[SW][MT][4];
+      // every load of the batch unconditionally (steps past the range re-read
+      // the last one and are not used), so no use waits on a partial batch
 #pragma unroll
       for (int i = 0; i < SW; ++i) {
-        const int kg = (s0 + i) * 4 + kb;   // 32-element group index along K
-        const bool in = s0 + i < s_hi;      // wave-uniform
-        bw[i] = u32x4{0u, 0u, 0u, 0u};
-        sb[i] = 127u;
-        if (in) {
-          bw[i] = wq[(s0 + i) * ws_step];
-          sb[i] = wsc[(s0 + i) * ws_step];
-        }
+        const int st = min(s0 + i, s_hi - 1);   // wave-uniform
+        const int kg = st * 4 + kb;             // 32-element group index along K
+        bw[i] = wq[st * ws_step];
+        sb[i] = wsc[st * ws_step];
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            av[i][t][j] = u32x4{0u, 0u, 0u, 0u};
-            if (in && live[t]) av[i][t][j] = arow[t][kg * 4 + j];   // 64 bytes = 32 bf16
-          }
+          for (int j = 0; j < 4; ++j) av[i][t][j] = arow[t][kg * 4 + j];   // 64 bytes = 32 bf16
       }
 #pragma unroll
       for (int i = 0; i < SW; ++i) {
@@ -306,12 +281,9 @@ struct Gemm8Args {
   int32_t M, N, K;
 };
 
-// LDS bytes of the A16W8 kernel: staged codes (128 B) and scales (4 B) per
-// row and K block, or the waves' partial sums.
-inline size_t gemm8_lds_bytes(bool staged, int rows, int K, int MT, int waves) {
-  const size_t stage = staged ? (size_t)(K / 128) * rows * (128 + 4) : 0;
-  const size_t part = (size_t)(waves - 1) * MT * 64 * sizeof(v4f32);
-  return (std::max(stage, part) + 15) & ~(size_t)15;
+// LDS bytes of the A16W8 kernel: the waves' partial sums.
+inline size_t gemm8_lds_bytes(int MT, int waves) {
+  return (size_t)(waves - 1) * MT * 64 * sizeof(v4f32);
 }
 
 __device__ __forceinline__ void unpack_bf16x8(const u32x4 w, float f[8]) {
@@ -338,8 +310,8 @@ __device__ __forceinline__ v8i32 fp8_codes32(const u32x4 v[4], float sc) {
 }
 
 // MT row tiles per workgroup, SW steps per batch, SHUF: preshuffled weights,
-// STAGED: activations staged in LDS (MT == 1, SW == kGemmStagedSteps,
-// M <= kGemmStagedRows, M * K/8 <= 4 chunks per thread, one batch per wave).
+// STAGED: the small-M path (MT == 1, SW == kGemmStagedSteps,
+// M <= kGemmStagedRows, one batch per wave).
 // Row blocks are 16 * MT rows (MT <= kGemm8MaxTiles: the activation
 // registers of more tiles would not fit beside the 32-byte operands).
 constexpr int kGemm8MaxTiles = 2;
@@ -378,106 +350,81 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16w8_kernel(con
   for (int t = 0; t < MT; ++t) acc[t] = v4f32{0.0f, 0.0f, 0.0f, 0.0f};
 
   if constexpr (STAGED) {
-    // rows 0 .. R-1 (a single row block), 8-element chunk c = r * K/8 + kc;
-    // a 16-lane DPP row holds one 128-group
+    // Small M: the wave's batch of SW = 4 steps needs at most 4 rows x 4
+    // groups of 128, each held by a lane quad: lane L holds step i = L/16,
+    // row min(L/4 % 4, M-1), quarter L%4 (32 elements), so the quad's DPP
+    // max gives the group amax; the operand lane of row r, quarter kb then
+    // fetches the codes from lane 16 i + 4 r + kb, and each result lane the
+    // scales of its four rows (ds_bpermute). No workgroup barrier precedes
+    // the matrix-core steps.
     const int R = G.M;
-    const int C8 = G.K >> 3, total = R * C8, T = blockDim.x;
-    u32x4 v[kGemmStagedChunks];
+    const int ai = lane >> 4, ar = min((lane >> 2) & 3, R - 1), aq = lane & 3;
+    const int ast = min(s_lo + ai, s_hi - 1);
+    const u32x4* ap = reinterpret_cast<const u32x4*>(G.a + (int64_t)ar * G.lda) + ast * 16 + aq * 4;
+    u32x4 av[4];
 #pragma unroll
-    for (int u = 0; u < kGemmStagedChunks; ++u) {
-      const int c = min((int)threadIdx.x + u * T, total - 1);
-      const int r = c / C8, kc = c - r * C8;
-      v[u] = reinterpret_cast<const u32x4*>(G.a + (int64_t)r * G.lda)[kc];
-    }
+    for (int j = 0; j < 4; ++j) av[j] = ap[j];
     __builtin_amdgcn_sched_barrier(0);
     u32x4 bw[SW][2];
     float sw[SW];
 #pragma unroll
     for (int i = 0; i < SW; ++i) {
-      bw[i][0] = bw[i][1] = u32x4{0u, 0u, 0u, 0u};
-      sw[i] = 0.0f;
-      if (s_lo + i < s_hi) {
-        bw[i][0] = wq[(s_lo + i) * wstep];
-        bw[i][1] = wq[(s_lo + i) * wstep + whalf];
-        sw[i] = wsrow[s_lo + i];
-      }
+      const int st = min(s_lo + i, s_hi - 1);   // steps past the range re-read the last (unused)
+      bw[i][0] = wq[st * wstep];
+      bw[i][1] = wq[st * wstep + whalf];
+      sw[i] = wsrow[st];
     }
     __builtin_amdgcn_sched_barrier(0);
-    // codes of group g of row r at LDS byte (g * R + r) * 128, its fp32 scale
-    // at byte NG * R * 128 + (g * R + r) * 4 (T is a multiple of 64 and K/8 of
-    // 16, so a 16-lane row never straddles groups and is in or out of range
-    // as a whole)
-    const int NG = G.K >> 7;
-    uint8_t* codes = lds;
-    float* scl = reinterpret_cast<float*>(lds + NG * R * 128);
-#pragma unroll
-    for (int u = 0; u < kGemmStagedChunks; ++u) {
-      const int c = threadIdx.x + u * T;
-      const float sc = fp8_scale(max16(amax8(v[u])));
-      float f[8];
-      unpack_bf16x8(v[u], f);
-      const u32x2 q = fp8_codes8(f, sc);
-      if (c < total) {
-        const int r = c / C8, kc = c - r * C8, g = kc >> 4, d = kc & 15;
-        *reinterpret_cast<u32x2*>(codes + (g * R + r) * 128 + d * 8) = q;
-        if (d == 0) scl[g * R + r] = sc;
-      }
-    }
-    __syncthreads();
+    const uint32_t am = max(max(amax8(av[0]), amax8(av[1])), max(amax8(av[2]), amax8(av[3])));
+    const float sc = fp8_scale(max4(am));
+    const v8i32 qa = fp8_codes32(av, sc);
     const int r = lane & 15;
     const bool live = r < R;
 #pragma unroll
     for (int i = 0; i < SW; ++i) {
       if (s_lo + i >= s_hi) break;
-      const int g = s_lo + i;
-      v8i32 aop = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (live) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(codes + (g * R + r) * 128 + kb * 32);
-        const u32x4 q0 = src[0], q1 = src[1];
-        aop = v8i32{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
-      }
+      const int src = (16 * i + 4 * min(r, 3) + kb) << 2;   // ds_bpermute byte address
+      v8i32 aop;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) aop[d] = __builtin_amdgcn_ds_bpermute(src, qa[d]);
+      if (!live) aop = v8i32{0, 0, 0, 0, 0, 0, 0, 0};
       const v8i32 bop = {(int)bw[i][0][0], (int)bw[i][0][1], (int)bw[i][0][2], (int)bw[i][0][3],
                          (int)bw[i][1][0], (int)bw[i][1][1], (int)bw[i][1][2], (int)bw[i][1][3]};
       const v4f32 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, v4f32{0.0f, 0.0f, 0.0f, 0.0f}, 0,
                                                                        0, 0, 127, 0, 127);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        // result row 4 kb + j: its scale sits in lane 16 i + 4 (4 kb + j) (rows past 3 give 0)
         const int row = 4 * kb + j;
-        const float ts = row < R ? scl[g * R + row] * sw[i] : 0.0f;
+        const float sa = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute((16 * i + 4 * min(row, 3)) << 2,
+                                                                               (int)__float_as_uint(sc)));
+        const float ts = row < R ? sa * sw[i] : 0.0f;
         acc[0][j] = __builtin_fmaf(d[j], ts, acc[0][j]);
       }
     }
-    __syncthreads();   // the partial sums below reuse the staging area
   } else {
+    // lanes of rows past M read row M-1 (their results are not stored)
     const u32x4* arow[MT];
-    bool live[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int m = m0 + 16 * t + (lane & 15);
-      live[t] = m < G.M;
       arow[t] = reinterpret_cast<const u32x4*>(G.a + (int64_t)min(m, G.M - 1) * G.lda);
     }
     for (int s0 = s_lo; s0 < s_hi; s0 += SW) {
       u32x4 bw[SW][2];
       float sw[SW];
       u32x4 av[SW][MT][4];
+      // unconditional loads, as in the A16WFP4 kernel
 #pragma unroll
       for (int i = 0; i < SW; ++i) {
-        const bool in = s0 + i < s_hi;      // wave-uniform
-        bw[i][0] = bw[i][1] = u32x4{0u, 0u, 0u, 0u};
-        sw[i] = 0.0f;
-        if (in) {
-          bw[i][0] = wq[(s0 + i) * wstep];
-          bw[i][1] = wq[(s0 + i) * wstep + whalf];
-          sw[i] = wsrow[s0 + i];
-        }
+        const int st = min(s0 + i, s_hi - 1);   // wave-uniform
+        bw[i][0] = wq[st * wstep];
+        bw[i][1] = wq[st * wstep + whalf];
+        sw[i] = wsrow[st];
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            av[i][t][j] = u32x4{0u, 0u, 0u, 0u};
-            if (in && live[t]) av[i][t][j] = arow[t][(s0 + i) * 16 + kb * 4 + j];   // 32 bf16
-          }
+          for (int j = 0; j < 4; ++j) av[i][t][j] = arow[t][st * 16 + kb * 4 + j];   // 32 bf16
       }
 #pragma unroll
       for (int i = 0; i < SW; ++i) {

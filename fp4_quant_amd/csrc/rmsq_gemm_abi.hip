@@ -20,7 +20,7 @@ void launch_gemm(const rmsq::GemmArgs& G, int MT, int CT, bool staged, int waves
   const dim3 grid((unsigned)(G.N / (16 * CT)),
                   (unsigned)((G.M + rmsq::kGemmRowsPerBlock - 1) / rmsq::kGemmRowsPerBlock)),
       block(64 * waves);
-  const size_t lds = rmsq::gemm_lds_bytes(staged, G.M, G.K, MT, CT, waves);
+  const size_t lds = rmsq::gemm_lds_bytes(MT, CT, waves);
   constexpr int SS = rmsq::kGemmStagedSteps;
   if (staged && CT == 2) {
     hipLaunchKernelGGL((rmsq::rmsq_gemm_a16wfp4_kernel<1, SS, SHUF, true, 2>), grid, block, lds, s, G);
@@ -83,17 +83,14 @@ rmsq_status run_gemm(const void* a, int64_t lda, const void* w, const void* w_sc
   G.M = (int32_t)M;
   G.N = (int32_t)N;
   G.K = (int32_t)K;
-  // Row tiles per block and waves per workgroup. Staged activations (at most
-  // 4 rows): enough waves that each covers at most 4 steps and each thread
-  // at most 4 chunks of 8 elements. Otherwise SW steps per batch (registers:
-  // 16 per step and tile for the activations, 5 for the weights) and enough
-  // waves that each wave's K range is one batch, at most 16.
+  // Row tiles per block and waves per workgroup. Small M (at most 4 rows):
+  // enough waves that each covers at most 4 steps, one batch. Otherwise SW
+  // steps per batch (registers: 16 per step and tile for the activations, 5
+  // for the weights) and enough waves that each wave's K range is one batch,
+  // at most 16.
   const int MT = M >= 64 ? 4 : (int)((M + 15) / 16);
   const int steps = (int)(K / 128);
-  const int64_t chunks = M * (K / 8);
-  const int staged_waves =
-      (int)std::max<int64_t>((steps + rmsq::kGemmStagedSteps - 1) / rmsq::kGemmStagedSteps,
-                             (chunks + 64 * rmsq::kGemmStagedChunks - 1) / (64 * rmsq::kGemmStagedChunks));
+  const int staged_waves = (steps + rmsq::kGemmStagedSteps - 1) / rmsq::kGemmStagedSteps;
   const bool staged = M <= rmsq::kGemmStagedRows && staged_waves <= rmsq::kGemmMaxWaves;
   const int SW = MT == 1 ? 4 : MT == 2 ? 2 : 1;
   const int waves = staged ? staged_waves : std::min(rmsq::kGemmMaxWaves, std::max(1, (steps + SW - 1) / SW));
@@ -115,7 +112,7 @@ rmsq_status run_gemm(const void* a, int64_t lda, const void* w, const void* w_sc
 template <bool SHUF>
 void launch_gemm8(const rmsq::Gemm8Args& G, int MT, bool staged, int waves, hipStream_t s) {
   const dim3 grid((unsigned)(G.N / 16), (unsigned)((G.M + 16 * MT - 1) / (16 * MT))), block(64 * waves);
-  const size_t lds = rmsq::gemm8_lds_bytes(staged, G.M, G.K, MT, waves);
+  const size_t lds = rmsq::gemm8_lds_bytes(MT, waves);
   if (staged)
     hipLaunchKernelGGL((rmsq::rmsq_gemm_a16w8_kernel<1, rmsq::kGemmStagedSteps, SHUF, true>), grid, block, lds, s, G);
   else if (MT == 1)
@@ -164,10 +161,7 @@ rmsq_status run_gemm8(const void* a, int64_t lda, const void* w, const void* w_s
   // 16 per step and tile for the activations, at most two row tiles
   const int MT = M > 16 ? 2 : 1;
   const int steps = (int)(K / 128);
-  const int64_t chunks = M * (K / 8);
-  const int staged_waves =
-      (int)std::max<int64_t>((steps + rmsq::kGemmStagedSteps - 1) / rmsq::kGemmStagedSteps,
-                             (chunks + 64 * rmsq::kGemmStagedChunks - 1) / (64 * rmsq::kGemmStagedChunks));
+  const int staged_waves = (steps + rmsq::kGemmStagedSteps - 1) / rmsq::kGemmStagedSteps;
   const bool staged = M <= rmsq::kGemmStagedRows && staged_waves <= rmsq::kGemmMaxWaves;
   const int SW = MT == 1 ? 2 : 1;
   const int waves = staged ? staged_waves : std::min(rmsq::kGemmMaxWaves, std::max(1, (steps + SW - 1) / SW));
