@@ -59,8 +59,8 @@ struct GemmArgs {
 
 constexpr int kGemmMaxWaves = 16;
 constexpr int kGemmRowsPerBlock = 64;   // 4 tiles of 16 rows
-constexpr int kGemmStagedRows = 4;      // at most this many rows take the small-M path
-constexpr int kGemmStagedSteps = 4;     // steps per wave on the small-M path (one batch)
+constexpr int kGemmSmallRows = 4;      // at most this many rows take the small-M path
+constexpr int kGemmSmallSteps = 4;     // steps per wave on the small-M path (one batch)
 
 // MXFP4 quantization of one 32-element bf16 group held by one lane (16
 // packed dwords): the e8m0 byte and the 4 dwords of e2m1 codes.
@@ -80,13 +80,13 @@ inline size_t gemm_lds_bytes(int MT, int CT, int waves) {
 }
 
 // MT row tiles of 16 rows and CT column tiles per workgroup, SW steps
-// loaded per batch, SHUF: preshuffled weights, STAGED: the small-M path (MT ==
-// 1, SW == kGemmStagedSteps, M <= kGemmStagedRows, every wave's steps in one
+// loaded per batch, SHUF: preshuffled weights, SMALLM: the small-M path (MT ==
+// 1, SW == kGemmSmallSteps, M <= kGemmSmallRows, every wave's steps in one
 // batch); CT > 1 only there, where a wave reuses each activation operand for
 // CT tiles.
-template <int MT, int SW, bool SHUF, bool STAGED, int CT>
+template <int MT, int SW, bool SHUF, bool SMALLM, int CT>
 __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16wfp4_kernel(const GemmArgs G) {
-  static_assert(CT == 1 || STAGED, "several column tiles only with staged activations");
+  static_assert(CT == 1 || SMALLM, "several column tiles only on the small-M path");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16wfp4_kernel(c
 #pragma unroll
   for (int t = 0; t < MT * CT; ++t) acc[t] = v4f32{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if constexpr (STAGED) {
+  if constexpr (SMALLM) {
     // Small M: the wave's batch of SW = 4 steps needs at most 4 rows x 16
     // activation groups, one per lane: lane L holds step i = L/16, row
     // min(L/4 % 4, M-1), 32-element quarter L%4, loaded with all lanes and
@@ -310,13 +310,13 @@ __device__ __forceinline__ v8i32 fp8_codes32(const u32x4 v[4], float sc) {
 }
 
 // MT row tiles per workgroup, SW steps per batch, SHUF: preshuffled weights,
-// STAGED: the small-M path (MT == 1, SW == kGemmStagedSteps,
-// M <= kGemmStagedRows, one batch per wave).
+// SMALLM: the small-M path (MT == 1, SW == kGemmSmallSteps,
+// M <= kGemmSmallRows, one batch per wave).
 // Row blocks are 16 * MT rows (MT <= kGemm8MaxTiles: the activation
 // registers of more tiles would not fit beside the 32-byte operands).
 constexpr int kGemm8MaxTiles = 2;
 
-template <int MT, int SW, bool SHUF, bool STAGED>
+template <int MT, int SW, bool SHUF, bool SMALLM>
 __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16w8_kernel(const Gemm8Args G) {
   static_assert(MT <= kGemm8MaxTiles, "at most two row tiles");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -349,7 +349,7 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16w8_kernel(con
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = v4f32{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if constexpr (STAGED) {
+  if constexpr (SMALLM) {
     // Small M: the wave's batch of SW = 4 steps needs at most 4 rows x 4
     // groups of 128, each held by a lane quad: lane L holds step i = L/16,
     // row min(L/4 % 4, M-1), quarter L%4 (32 elements), so the quad's DPP

@@ -16,17 +16,17 @@ using namespace rmsq_abi;
 // The A16WFP4 prequant GEMM: grid x = 16-column tiles of the output, y =
 // blocks of 64 rows; the row tiles per block (MT) follow M.
 template <bool SHUF>
-void launch_gemm(const rmsq::GemmArgs& G, int MT, int CT, bool staged, int waves, hipStream_t s) {
+void launch_gemm(const rmsq::GemmArgs& G, int MT, int CT, bool small_m, int waves, hipStream_t s) {
   const dim3 grid((unsigned)(G.N / (16 * CT)),
                   (unsigned)((G.M + rmsq::kGemmRowsPerBlock - 1) / rmsq::kGemmRowsPerBlock)),
       block(64 * waves);
   const size_t lds = rmsq::gemm_lds_bytes(MT, CT, waves);
-  constexpr int SS = rmsq::kGemmStagedSteps;
-  if (staged && CT == 2) {
+  constexpr int SS = rmsq::kGemmSmallSteps;
+  if (small_m && CT == 2) {
     hipLaunchKernelGGL((rmsq::rmsq_gemm_a16wfp4_kernel<1, SS, SHUF, true, 2>), grid, block, lds, s, G);
     return;
   }
-  if (staged) {
+  if (small_m) {
     hipLaunchKernelGGL((rmsq::rmsq_gemm_a16wfp4_kernel<1, SS, SHUF, true, 1>), grid, block, lds, s, G);
     return;
   }
@@ -90,18 +90,18 @@ rmsq_status run_gemm(const void* a, int64_t lda, const void* w, const void* w_sc
   // at most 16.
   const int MT = M >= 64 ? 4 : (int)((M + 15) / 16);
   const int steps = (int)(K / 128);
-  const int staged_waves = (steps + rmsq::kGemmStagedSteps - 1) / rmsq::kGemmStagedSteps;
-  const bool staged = M <= rmsq::kGemmStagedRows && staged_waves <= rmsq::kGemmMaxWaves;
+  const int small_waves = (steps + rmsq::kGemmSmallSteps - 1) / rmsq::kGemmSmallSteps;
+  const bool small_m = M <= rmsq::kGemmSmallRows && small_waves <= rmsq::kGemmMaxWaves;
   const int SW = MT == 1 ? 4 : MT == 2 ? 2 : 1;
-  const int waves = staged ? staged_waves : std::min(rmsq::kGemmMaxWaves, std::max(1, (steps + SW - 1) / SW));
-  // Two column tiles per staged workgroup once there are at least 256 tiles:
+  const int waves = small_m ? small_waves : std::min(rmsq::kGemmMaxWaves, std::max(1, (steps + SW - 1) / SW));
+  // Two column tiles per small-M workgroup once there are at least 256 tiles:
   // half as many workgroups each stage the activations for twice the weights.
-  const int CT = staged && (N / 16) % 2 == 0 && N / 16 >= kComputeUnits ? 2 : 1;
+  const int CT = small_m && (N / 16) % 2 == 0 && N / 16 >= kComputeUnits ? 2 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w_layout == RMSQ_W_PRESHUFFLED)
-    launch_gemm<true>(G, MT, CT, staged, waves, s);
+    launch_gemm<true>(G, MT, CT, small_m, waves, s);
   else
-    launch_gemm<false>(G, MT, CT, staged, waves, s);
+    launch_gemm<false>(G, MT, CT, small_m, waves, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return RMSQ_OK;
@@ -110,11 +110,11 @@ rmsq_status run_gemm(const void* a, int64_t lda, const void* w, const void* w_sc
 // The A16W8 prequant GEMM: the same grid as the A16WFP4 one, one column tile
 // per workgroup.
 template <bool SHUF>
-void launch_gemm8(const rmsq::Gemm8Args& G, int MT, bool staged, int waves, hipStream_t s) {
+void launch_gemm8(const rmsq::Gemm8Args& G, int MT, bool small_m, int waves, hipStream_t s) {
   const dim3 grid((unsigned)(G.N / 16), (unsigned)((G.M + 16 * MT - 1) / (16 * MT))), block(64 * waves);
   const size_t lds = rmsq::gemm8_lds_bytes(MT, waves);
-  if (staged)
-    hipLaunchKernelGGL((rmsq::rmsq_gemm_a16w8_kernel<1, rmsq::kGemmStagedSteps, SHUF, true>), grid, block, lds, s, G);
+  if (small_m)
+    hipLaunchKernelGGL((rmsq::rmsq_gemm_a16w8_kernel<1, rmsq::kGemmSmallSteps, SHUF, true>), grid, block, lds, s, G);
   else if (MT == 1)
     hipLaunchKernelGGL((rmsq::rmsq_gemm_a16w8_kernel<1, 2, SHUF, false>), grid, block, lds, s, G);
   else
@@ -161,15 +161,15 @@ rmsq_status run_gemm8(const void* a, int64_t lda, const void* w, const void* w_s
   // 16 per step and tile for the activations, at most two row tiles
   const int MT = M > 16 ? 2 : 1;
   const int steps = (int)(K / 128);
-  const int staged_waves = (steps + rmsq::kGemmStagedSteps - 1) / rmsq::kGemmStagedSteps;
-  const bool staged = M <= rmsq::kGemmStagedRows && staged_waves <= rmsq::kGemmMaxWaves;
+  const int small_waves = (steps + rmsq::kGemmSmallSteps - 1) / rmsq::kGemmSmallSteps;
+  const bool small_m = M <= rmsq::kGemmSmallRows && small_waves <= rmsq::kGemmMaxWaves;
   const int SW = MT == 1 ? 2 : 1;
-  const int waves = staged ? staged_waves : std::min(rmsq::kGemmMaxWaves, std::max(1, (steps + SW - 1) / SW));
+  const int waves = small_m ? small_waves : std::min(rmsq::kGemmMaxWaves, std::max(1, (steps + SW - 1) / SW));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w_layout == RMSQ_W_PRESHUFFLED)
-    launch_gemm8<true>(G, MT, staged, waves, s);
+    launch_gemm8<true>(G, MT, small_m, waves, s);
   else
-    launch_gemm8<false>(G, MT, staged, waves, s);
+    launch_gemm8<false>(G, MT, small_m, waves, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return RMSQ_OK;

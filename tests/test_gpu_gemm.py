@@ -91,10 +91,10 @@ def check(orc, a, w, ws, got):
 
 LAYOUTS = [fq.W_ROW_MAJOR, fq.W_PRESHUFFLED]
 
-# Shapes: the decode workload, activations staged in LDS (M <= 4, up to
-# K = 8192 with 16 waves) and not (K = 8320 needs a 17th wave; M > 4), one to
+# Shapes: the decode workload, the small-M path (M <= 4, up to K = 8192 with
+# 16 waves) and the per-wave path (K = 8320 needs a 17th wave; M > 4), one to
 # four row tiles, row blocks past 64, ragged M in every tile count, and two
-# column tiles per staged workgroup (N/16 >= 256 and even; 4112 is odd).
+# column tiles per small-M workgroup (N/16 >= 256 and even; 4112 is odd).
 SHAPES = [(4, 2112, 7168), (1, 16, 128), (3, 16, 128), (2, 48, 1152), (4, 48, 256), (4, 32, 8192),
           (4, 32, 8320), (5, 32, 256), (16, 64, 384), (17, 32, 1024), (33, 48, 512), (64, 32, 7168),
           (70, 16, 256), (130, 32, 640), (4, 256, 16384), (4, 4096, 256), (2, 4128, 384), (4, 4112, 256)]
@@ -173,7 +173,7 @@ def test_gemm_zero_rows_and_special_groups(orc):
     got = run_gemm(a, g["w"], ws)
     assert np.all(got[1] == 0)
     check(orc, a, g["w"], ws, got)
-    # the same groups in a staged (M <= 4) call
+    # the same groups on the small-M path (M <= 4)
     got = run_gemm(a[1:5], g["w"], ws, layout=fq.W_PRESHUFFLED)
     assert np.all(got[0] == 0)
     check(orc, a[1:5], g["w"], ws, got)
@@ -281,7 +281,7 @@ def check8(orc, a, w, ws, got):
     assert not bad.any(), f"{bad.sum()} outputs beyond the bound; worst excess {float((err - bound).max())}"
 
 
-# decode workload, staged (M <= 4) and not, one or two row tiles, several row
+# decode workload, the small-M path (M <= 4) and not, one or two row tiles, several row
 # blocks, weight block rows that end inside a tile row (N = 2112: 16.5 blocks)
 SHAPES8 = [(4, 2112, 7168), (1, 16, 128), (3, 32, 256), (4, 48, 8192), (4, 32, 8320), (5, 144, 384),
            (16, 64, 1024), (17, 32, 512), (33, 48, 256), (70, 16, 640), (4, 256, 16384)]

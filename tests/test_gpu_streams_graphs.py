@@ -169,7 +169,7 @@ def test_graph_capture_of_a_mixed_set_two_launches(orc):
 
 @pytest.mark.parametrize("fmt", [1, 0])
 def test_graph_capture_of_the_prequant_gemms(fmt):
-    """Both prequant GEMMs (preshuffled weights, staged activations at M = 4
+    """Both prequant GEMMs (preshuffled weights, the small-M path at M = 4
     and per-wave activations at M = 20) captured in one HIP graph: each
     replay, with new activations copied in and eager work between replays,
     equals the eager result bit for bit."""

@@ -87,10 +87,10 @@ def test_gemm_variants_fit_sixteen_waves(kernels):
     variant must fit 128 registers (VGPRs + AGPRs) and the LDS of its
     partial sums."""
     gemm = {n: k for n, k in kernels.items() if "rmsq_gemm_a16wfp4_kernel" in (n or "")}
-    # (4 row-tile counts + the staged variant with 1 or 2 column tiles) x 2 weight layouts
+    # (4 row-tile counts + the small-M variant with 1 or 2 column tiles) x 2 weight layouts
     assert len(gemm) == 12, sorted(gemm)
     gemm8 = {n: k for n, k in kernels.items() if "rmsq_gemm_a16w8_kernel" in (n or "")}
-    # (1 or 2 row tiles + the staged variant) x 2 weight layouts
+    # (1 or 2 row tiles + the small-M variant) x 2 weight layouts
     assert len(gemm8) == 6, sorted(gemm8)
     gemm.update(gemm8)
     for n, k in gemm.items():
