@@ -395,3 +395,26 @@ def test_python_wrappers(orc, fmt):
     assert np.array_equal(host(r_shuf).view(np.uint32), raw.view(np.uint32))
     with pytest.raises(ValueError):
         fq.prequant_gemm(a.float(), w, ws, fmt=fmt)
+
+
+def test_gemm_random_shape_sweep(orc):
+    """Seeded random shapes for both GEMMs and both weight layouts: M in
+    1..80, N a multiple of 16 up to 640, K a multiple of 128 up to 2560,
+    padded activation and output strides."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        fmt = "mxfp4" if case % 2 == 0 else "fp8"
+        M = int(rng.choice([1, 2, 3, 4, int(rng.integers(5, 81))]))
+        N = 16 * int(rng.integers(1, 41))
+        K = 128 * int(rng.integers(1, 21))
+        layout = LAYOUTS[(case // 2) % 2]
+        lda = K + 8 * int(rng.integers(0, 3))
+        ldc = N + int(rng.integers(0, 5))
+        if fmt == "mxfp4":
+            g = inputs.make_gemm(M, N, K, seed=300 + case)
+            got = run_gemm(g["a"], g["w"], g["ws"], lda=lda, ldc=ldc, layout=layout)
+            check(orc, g["a"], g["w"], g["ws"], got)
+        else:
+            g = inputs.make_gemm8(M, N, K, seed=300 + case)
+            got = run_gemm8(g["a"], g["w"], g["ws"], lda=lda, ldc=ldc, layout=layout)
+            check8(orc, g["a"], g["w"], g["ws"], got)
