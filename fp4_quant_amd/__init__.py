@@ -117,7 +117,13 @@ def _check(status: int) -> None:
 
 
 def _ptr(t):
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor (None for None). A host tensor is refused:
+    the kernels would dereference its address on the GPU."""
+    if t is None:
+        return None
+    if getattr(t, "is_cuda", True) is False:
+        raise ValueError("fp4_quant_amd: buffers must be GPU tensors (got a tensor on %s)" % t.device)
+    return t.data_ptr()
 
 
 def _stream(stream, device=None):

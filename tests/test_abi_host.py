@@ -342,3 +342,14 @@ def test_library_exports_only_the_declared_interface():
     out = subprocess.run(["nm", "-D", "--defined-only", fq.LIB_PATH], capture_output=True, text=True, check=True)
     text_syms = {l.split()[-1] for l in out.stdout.splitlines() if len(l.split()) == 3 and l.split()[1] == "T"}
     assert text_syms == set(_declared_functions())
+
+
+def test_binding_refuses_host_tensors():
+    """A CPU tensor never reaches the C ABI: its address would be dereferenced
+    on the GPU."""
+    import torch
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fq.dynamic_per_group_scaled_quant(x, 4, 256, 128, 0, 0, x, x, stream=0)
+    with pytest.raises(ValueError):
+        fq.gemm_a16wfp4_prequant(x, 256, x, x, fq.W_ROW_MAJOR, 4, 16, 256, x, 16, stream=0)
