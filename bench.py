@@ -154,23 +154,27 @@ class GemmWorkload:
 
 
 class UnfusedWorkload(Workload):
-    """The same prefill batch through the two kernels the fusion replaces:
-    add_rmsnorm writes the residual and the bf16 rows, then the standalone
-    per-group quant reads the bf16 rows back (two launches per step)."""
+    """The same batch through the two kernels the fusion replaces: add_rmsnorm
+    writes the residual and the bf16 rows, then the standalone per-group quant
+    reads the bf16 rows back (two launches per step). Without a bf16
+    side-output the rows go through an intermediate buffer of their own."""
 
     def __init__(self, name, specs, fmt, layout=0):
+        import torch
         super().__init__(name, specs, fmt, layout)
         s = specs[0]
         self.moved = self.bytes + s["M"] * s["N"] * 2 * (0 if s["keep_bf16"] else 1) + s["M"] * s["N"] * 2
+        self.mid = [keep[6] if keep[6] is not None else
+                    torch.empty((s["M"], s["N"]), dtype=torch.bfloat16, device="cuda") for _, keep in self.sets]
 
-    def launch(self, i):
+    def launch(self, i, stream=None):
         import fp4_quant_amd as fq
-        probs, keep = self.sets[i % len(self.sets)]
-        x, g, r, ro, q, sc, yb = keep[:7]
+        k = i % len(self.sets)
+        x, g, r, ro, q, sc = self.sets[k][1][:6]
+        yb, st = self.mid[k], stream or self.stream
         M, N = x.shape
-        fq.add_rmsnorm(x, r, g, 1e-6, M, N, ro, yb, self.stream)
-        fq.dynamic_per_group_scaled_quant(yb, M, N, 128 if self.fmt == 0 else 32, self.fmt, self.layout, q, sc,
-                                          self.stream)
+        fq.add_rmsnorm(x, r, g, 1e-6, M, N, ro, yb, st)
+        fq.dynamic_per_group_scaled_quant(yb, M, N, 128 if self.fmt == 0 else 32, self.fmt, self.layout, q, sc, st)
 
 
 def time_workload(w, steps, warmup):
@@ -468,17 +472,25 @@ def main():
                 configs[name]["traffic"] = tr
             del wk
             torch.cuda.empty_cache()
-    if not args.no_configs and args.config == "prefill":
-        log("bench: unfused pair on the prefill batch")
-        wu = UnfusedWorkload("unfused", specs, fmt, layout)
-        pu = time_workload(wu, max(50, args.steps // 2), max(50, args.warmup))
-        configs["prefill_unfused_pair"] = {
-            "us_per_step": round(pu * 1e3, 2), "launches_per_step": 2,
-            "fused_algorithmic_GBps": round(w.bytes / (pu * 1e-3) / 1e9, 1),
-            "bytes_moved": wu.moved, "moved_GBps": round(wu.moved / (pu * 1e-3) / 1e9, 1),
-            "fused_speedup": round(pu / step_ms, 3)}
-        del wu
-        torch.cuda.empty_cache()
+    if not args.no_configs:
+        for name in ("prefill", "decode"):
+            sp, f, lay = SPECS[name]
+            log(f"bench: unfused pair on the {name} batch")
+            wu = UnfusedWorkload("unfused_" + name, sp, f, lay)
+            pu = time_workload(wu, max(50, args.steps // 2), max(50, args.warmup))
+            fused = step_ms if name == args.config else configs[name]["us_per_launch"] * 1e-3
+            rec = {"us_per_step": round(pu * 1e3, 2), "launches_per_step": 2,
+                   "fused_algorithmic_GBps": round(wu.bytes / (pu * 1e-3) / 1e9, 1),
+                   "bytes_moved": wu.moved, "moved_GBps": round(wu.moved / (pu * 1e-3) / 1e9, 1),
+                   "fused_speedup": round(pu / fused, 3)}
+            if wu.bytes < 64 << 20:       # launch-bound sizes: also replayed from a HIP graph
+                pg = time_workload_graph(wu, 100)
+                rec["us_per_step_graph"] = round(pg * 1e3, 2)
+                if "us_per_launch_graph" in configs.get(name, {}):
+                    rec["fused_speedup_graph"] = round(pg * 1e3 / configs[name]["us_per_launch_graph"], 3)
+            configs[name + "_unfused_pair"] = rec
+            del wu
+            torch.cuda.empty_cache()
     ceil = ceilings()
     log(f"bench: stream ceilings (GB/s) {ceil}")
 
