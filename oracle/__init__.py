@@ -58,6 +58,10 @@ def _bind(L):
     L.oracle_gemm_a16wfp4_prequant.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _i64]
     L.oracle_gemm_a16w8_prequant.restype = C.c_int
     L.oracle_gemm_a16w8_prequant.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _i64]
+    for name in ("oracle_gemm_afp4wfp4", "oracle_gemm_a8w8_blockscale"):
+        f = getattr(L, name)
+        f.restype = C.c_int
+        f.argtypes = [_p, _p, _i32, _p, _p, _i64, _i64, _i64, _p, _i64]
     L.oracle_num_threads.restype = C.c_int
     L.oracle_num_threads.argtypes = []
     return L
@@ -211,6 +215,49 @@ class Oracle:
             raise ValueError("oracle: arguments outside the defined operation")
         return out
 
+    def gemm_afp4wfp4(self, a_q, a_scale, w, w_scale, scale_layout=LAYOUT_ROW):
+        """GEMM of MXFP4 activations as the group quantization writes them
+        (a_q [M, K/2] uint8 codes, a_scale its e8m0 scale array in
+        scale_layout) with MXFP4 weights w [N, K/2], w_scale [N, K/32].
+        Returns C [M, N] float64."""
+        a_q = np.ascontiguousarray(a_q, dtype=np.uint8)
+        M, K = a_q.shape[0], a_q.shape[1] * 2
+        N = w.shape[0]
+        assert w.shape == (N, K // 2) and w_scale.shape == (N, K // 32)
+        sshape, _ = _scale_shape(M, K, 32, FMT_MXFP4, scale_layout)
+        a_scale = np.ascontiguousarray(a_scale, dtype=np.uint8)
+        assert a_scale.size >= int(np.prod(sshape))
+        w = np.ascontiguousarray(w, dtype=np.uint8)
+        w_scale = np.ascontiguousarray(w_scale, dtype=np.uint8)
+        out = np.zeros((M, N), np.float64)
+        rc = self._L.oracle_gemm_afp4wfp4(_ptr(a_q), _ptr(a_scale), scale_layout, _ptr(w), _ptr(w_scale), M, N, K,
+                                          _ptr(out), N)
+        if rc != 0:
+            raise ValueError("oracle: arguments outside the defined operation")
+        return out
+
+    def gemm_a8w8_blockscale(self, a_q, a_scale, w, w_scale, scale_layout=LAYOUT_ROW):
+        """GEMM of FP8 activations as the group quantization writes them
+        (a_q [M, K] uint8 e4m3fn codes, a_scale its fp32 scale array in
+        scale_layout, row- or column-major) with FP8 weights w [N, K] and
+        fp32 block scales w_scale [ceil(N/128), K/128]. Returns C [M, N]
+        float64."""
+        a_q = np.ascontiguousarray(a_q, dtype=np.uint8)
+        M, K = a_q.shape
+        N = w.shape[0]
+        assert w.shape == (N, K) and w_scale.shape == (-(-N // 128), K // 128)
+        sshape, _ = _scale_shape(M, K, 128, FMT_FP8, scale_layout)
+        a_scale = np.ascontiguousarray(a_scale, dtype=np.float32)
+        assert a_scale.size >= int(np.prod(sshape))
+        w = np.ascontiguousarray(w, dtype=np.uint8)
+        w_scale = np.ascontiguousarray(w_scale, dtype=np.float32)
+        out = np.zeros((M, N), np.float64)
+        rc = self._L.oracle_gemm_a8w8_blockscale(_ptr(a_q), _ptr(a_scale), scale_layout, _ptr(w), _ptr(w_scale),
+                                                 M, N, K, _ptr(out), N)
+        if rc != 0:
+            raise ValueError("oracle: arguments outside the defined operation")
+        return out
+
     def group_quant(self, yb, group=128, fmt=FMT_FP8, scale_layout=LAYOUT_ROW, scale_fill=0):
         """Stage 2 alone on bf16 rows: returns (q, scale)."""
         yb = np.ascontiguousarray(yb, dtype=np.uint16)
@@ -282,6 +329,14 @@ def gemm_a16wfp4_prequant(*a, **k):
 
 def gemm_a16w8_prequant(*a, **k):
     return default().gemm_a16w8_prequant(*a, **k)
+
+
+def gemm_afp4wfp4(*a, **k):
+    return default().gemm_afp4wfp4(*a, **k)
+
+
+def gemm_a8w8_blockscale(*a, **k):
+    return default().gemm_a8w8_blockscale(*a, **k)
 
 
 def group_quant(*a, **k):

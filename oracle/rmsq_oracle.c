@@ -491,6 +491,84 @@ int oracle_gemm_a16w8_prequant(const uint16_t* a, int64_t lda,
     return 0;
 }
 
+/*
+ * The GEMMs that consume activations already quantized by the fused kernel:
+ * [ATT, run notes] pairs the fused RMSNorm + quant with a separate GEMM above
+ * concurrency 4, fed by gemm_afp4wfp4_preshuffle (MXFP4) and, for the FP8
+ * runs, the block-scaled a8w8 GEMMs it lists; [ATF, Technical Details]
+ * requires the quantized activations' scales to come in the layout the GEMM
+ * reads. READING: the activations are exactly what the group quantization
+ * above writes - codes [M, K/2] (MXFP4, element 2k in the low nibble) or
+ * [M, K] (FP8), rows dense - with their scales in any of its layouts
+ * (scale_offset), and the weights are as in the prequant GEMMs:
+ *   MXFP4: C[m][n] = sum_k (qa[m][k] 2^(ea[m][k/32] - 127)) (qw[n][k] 2^(ew[n][k/32] - 127))
+ *   FP8:   C[m][n] = sum_k (qa[m][k] sa[m][k/128]) (qw[n][k] sw[n/128][k/128])
+ * accumulated here in double in k order.
+ */
+int oracle_gemm_afp4wfp4(const uint8_t* a_q, const uint8_t* a_scale, int32_t a_layout,
+                         const uint8_t* w, const uint8_t* w_scale,
+                         int64_t M, int64_t N, int64_t K, double* out, int64_t ldc)
+{
+    if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || ldc < N || a_layout < 0 || a_layout > 2)
+        return -1;
+    const int64_t G = K / 32;
+#pragma omp parallel
+    {
+        double* av = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            /* the given activation row's values: code times its group's scale */
+            const uint8_t* arow = a_q + m * (K / 2);
+            for (int64_t k = 0; k < K; ++k) {
+                uint8_t c = (uint8_t)((arow[k / 2] >> (4 * (k % 2))) & 0xF);
+                av[k] = oracle_e2m1_decode(c) * e8m0_value(a_scale[scale_offset(m, k / 32, M, G, a_layout)]);
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                const uint8_t* wrow = w + n * (K / 2);
+                const uint8_t* erow = w_scale + n * G;
+                double sum = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    uint8_t c = (uint8_t)((wrow[k / 2] >> (4 * (k % 2))) & 0xF);
+                    sum += av[k] * (oracle_e2m1_decode(c) * e8m0_value(erow[k / 32]));
+                }
+                out[m * ldc + n] = sum;
+            }
+        }
+        free(av);
+    }
+    return 0;
+}
+
+int oracle_gemm_a8w8_blockscale(const uint8_t* a_q, const float* a_scale, int32_t a_layout,
+                                const uint8_t* w, const float* w_scale,
+                                int64_t M, int64_t N, int64_t K, double* out, int64_t ldc)
+{
+    if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldc < N || (a_layout != 0 && a_layout != 2))
+        return -1;
+    const int64_t blocks = K / 128;
+#pragma omp parallel
+    {
+        double* av = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            const uint8_t* arow = a_q + m * K;
+            for (int64_t k = 0; k < K; ++k)
+                av[k] = oracle_e4m3fn_decode(arow[k]) *
+                        (double)a_scale[scale_offset(m, k / 128, M, blocks, a_layout)];
+            for (int64_t n = 0; n < N; ++n) {
+                const uint8_t* wrow = w + n * K;
+                const float* brow = w_scale + (n / 128) * blocks;   /* the weight row's 128-row block */
+                double sum = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    sum += av[k] * (oracle_e4m3fn_decode(wrow[k]) * (double)brow[k / 128]);
+                out[m * ldc + n] = sum;
+            }
+        }
+        free(av);
+    }
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

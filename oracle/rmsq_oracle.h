@@ -85,6 +85,21 @@ int oracle_gemm_a16w8_prequant(const uint16_t* a, int64_t lda,
                                int64_t M, int64_t N, int64_t K,
                                double* out, int64_t ldc);
 
+/* GEMMs of activations already quantized by the group quantization above
+ * (codes with dense rows, scales in its layout a_layout) and the prequant
+ * GEMMs' weights, the dequantized products summed in double:
+ * MXFP4: a_q [M, K/2], a_scale e8m0 (layout 0, 1 or 2), w [N, K/2],
+ *        w_scale e8m0 [N, K/32];
+ * FP8:   a_q [M, K] e4m3fn, a_scale fp32 (layout 0 or 2), w [N, K] e4m3fn,
+ *        w_scale fp32 [ceil(N/128), K/128].
+ * Return 0, or -1 for arguments they do not define. */
+int oracle_gemm_afp4wfp4(const uint8_t* a_q, const uint8_t* a_scale, int32_t a_layout,
+                         const uint8_t* w, const uint8_t* w_scale,
+                         int64_t M, int64_t N, int64_t K, double* out, int64_t ldc);
+int oracle_gemm_a8w8_blockscale(const uint8_t* a_q, const float* a_scale, int32_t a_layout,
+                                const uint8_t* w, const float* w_scale,
+                                int64_t M, int64_t N, int64_t K, double* out, int64_t ldc);
+
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

@@ -1,4 +1,5 @@
-"""Pins for the oracle's A16WFP4 prequant GEMM (CPU only).
+"""Pins for the oracle's GEMMs (CPU only): the prequant GEMMs and the GEMMs of
+already quantized activations.
 
 The expected values come from the definitions, not from the oracle: the e2m1
 grid and the e8m0 scale are written out here, numpy's matmul does the
@@ -186,3 +187,103 @@ def test_a16w8_rejects_undefined_shapes(orc):
     a = np.zeros((2, 192), np.uint16)
     with pytest.raises((ValueError, AssertionError)):
         orc.gemm_a16w8_prequant(a, np.zeros((3, 192), np.uint8), np.zeros((1, 1), np.float32))
+
+
+# ------------------------------------------- GEMMs of quantized activations --
+def layout_scales(S, layout):
+    """A [M, G] scale matrix as the group quantization lays it out, built with
+    numpy reshapes: row-major as is; 32-row tiles (rows padded to a multiple
+    of 32, group-major inside a tile, the tile's 32 rows adjacent);
+    column-major [G, M]."""
+    if layout == 0:
+        return np.ascontiguousarray(S)
+    if layout == 2:
+        return np.ascontiguousarray(S.T)
+    M, G = S.shape
+    Mp = -(-M // 32) * 32
+    P = np.zeros((Mp, G), S.dtype)
+    P[:M] = S
+    return np.ascontiguousarray(P.reshape(Mp // 32, 32, G).transpose(0, 2, 1)).reshape(-1)
+
+
+def test_afp4wfp4_hand_example(orc):
+    # one row: 32 ones (scale byte 127) then 32 twos (codes 1.0, scale byte 128); weights all 1.0
+    a_q = np.full((1, 32), 0x22, np.uint8)
+    a_s = np.array([[127, 128]], np.uint8)
+    w = np.full((2, 32), 0x22, np.uint8)
+    ws = np.full((2, 2), 127, np.uint8)
+    assert orc.gemm_afp4wfp4(a_q, a_s, w, ws).tolist() == [[96.0, 96.0]]
+    ws[1, 0] = 126                                   # second weight row's first group halved
+    assert orc.gemm_afp4wfp4(a_q, a_s, w, ws).tolist() == [[96.0, 16.0 + 64.0]]
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2])
+def test_afp4wfp4_matches_numpy_dequant_matmul(orc, layout):
+    """Random activation codes and scale bytes, the scales in each layout: the
+    GEMM is dequant(A) @ dequant(W)^T, computed here by numpy. 37 rows: a
+    ragged last 32-row tile."""
+    rng = np.random.default_rng(41)
+    M, N, K = 37, 9, 256
+    a_q = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    S = rng.integers(110, 140, (M, K // 32)).astype(np.uint8)
+    w, ws = random_weights(N, K, 42)
+    want = dequant_rows(a_q, S) @ dequant_rows(w, ws).T
+    got = orc.gemm_afp4wfp4(a_q, layout_scales(S, layout), w, ws, scale_layout=layout)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2])
+def test_afp4wfp4_of_the_group_quant_is_the_prequant_gemm(orc, layout):
+    """Quantizing bf16 rows with the group quantization (in any scale layout)
+    and multiplying the result gives exactly the prequant GEMM of the rows."""
+    p = inputs.make_problem(35, 256, seed_x=43, residual=False, outliers=True)
+    w, ws = random_weights(7, 256, 44)
+    qa, sa = orc.group_quant(p["x"], 32, 1, layout)
+    assert np.array_equal(orc.gemm_afp4wfp4(qa, sa, w, ws, scale_layout=layout),
+                          orc.gemm_a16wfp4_prequant(p["x"], w, ws))
+
+
+def test_a8w8_hand_example(orc):
+    # one row of 256: codes 1.0 (0x38) with scales 2 and 0.25; weights 1.0, block scales 1 and 3
+    a_q = np.full((1, 256), 0x38, np.uint8)
+    a_s = np.array([[2.0, 0.25]], np.float32)
+    w = np.full((2, 256), 0x38, np.uint8)
+    ws = np.array([[1.0, 3.0]], np.float32)
+    assert orc.gemm_a8w8_blockscale(a_q, a_s, w, ws).tolist() == [[128 * 2.0 + 128 * 0.75] * 2]
+
+
+@pytest.mark.parametrize("layout", [0, 2])
+def test_a8w8_matches_numpy_dequant_matmul(orc, layout):
+    """Random e4m3fn activation codes and fp32 group scales (row- or
+    column-major): the GEMM is dequant(A) @ dequant(W)^T by numpy. N = 200
+    spans two 128-row weight blocks, K = 384 three K blocks."""
+    rng = np.random.default_rng(45)
+    M, N, K = 6, 200, 384
+    a_q = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    a_q[(a_q & 0x7F) == 0x7F] = 0x7E
+    S = rng.uniform(2.0 ** -10, 2.0 ** 3, (M, K // 128)).astype(np.float32)
+    w, ws = random_fp8_weights(N, K, 46)
+    A = e4m3_values(a_q) * np.repeat(S.astype(np.float64), 128, axis=1)
+    want = A @ dequant_fp8_weights(w, ws).T
+    got = orc.gemm_a8w8_blockscale(a_q, layout_scales(S, layout), w, ws, scale_layout=layout)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("layout", [0, 2])
+def test_a8w8_of_the_group_quant_is_the_prequant_gemm(orc, layout):
+    p = inputs.make_problem(5, 512, seed_x=47, residual=False, outliers=True)
+    w, ws = random_fp8_weights(136, 512, 48)
+    qa, sa = orc.group_quant(p["x"], 128, 0, layout)
+    assert np.array_equal(orc.gemm_a8w8_blockscale(qa, sa, w, ws, scale_layout=layout),
+                          orc.gemm_a16w8_prequant(p["x"], w, ws))
+
+
+def test_quantized_activation_gemms_reject_undefined_arguments(orc):
+    with pytest.raises((ValueError, AssertionError)):      # K not a multiple of 32
+        orc.gemm_afp4wfp4(np.zeros((2, 24), np.uint8), np.zeros((2, 1), np.uint8),
+                          np.zeros((3, 24), np.uint8), np.zeros((3, 1), np.uint8))
+    with pytest.raises(ValueError):                        # FP8 scales have no 32-row tiled layout
+        orc.gemm_a8w8_blockscale(np.zeros((2, 128), np.uint8), np.ones(64, np.float32), np.zeros((3, 128), np.uint8),
+                                 np.ones((1, 1), np.float32), scale_layout=1)
+    assert orc.gemm_afp4wfp4(np.zeros((0, 32), np.uint8), np.zeros((0, 2), np.uint8), np.zeros((3, 32), np.uint8),
+                             np.zeros((3, 2), np.uint8)).shape == (0, 3)

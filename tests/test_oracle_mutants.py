@@ -58,6 +58,14 @@ MUTANTS = {
     "A16W8 weight block rows of 64": ("const float* sr = w_scale + (n / 128) * kb;",
                                       "const float* sr = w_scale + ((n / 64) % ((N + 127) / 128)) * kb;"),
     "A16W8 weight scale per 64 columns": ("(double)sr[k / 128]);", "(double)sr[(k / 64) % kb]);"),
+    "AFP4 activation nibbles swapped": ("uint8_t c = (uint8_t)((arow[k / 2] >> (4 * (k % 2))) & 0xF);",
+                                        "uint8_t c = (uint8_t)((arow[k / 2] >> (4 * (1 - k % 2))) & 0xF);"),
+    "AFP4 activation scales always row-major": ("a_scale[scale_offset(m, k / 32, M, G, a_layout)]",
+                                                "a_scale[scale_offset(m, k / 32, M, G, 0)]"),
+    "A8W8 activation scale per 32 columns": ("scale_offset(m, k / 128, M, blocks, a_layout)",
+                                             "scale_offset(m, (k / 32) % blocks, M, blocks, a_layout)"),
+    "A8W8 weight block scale ignored": ("(oracle_e4m3fn_decode(wrow[k]) * (double)brow[k / 128]);",
+                                        "(oracle_e4m3fn_decode(wrow[k]) * 1.0);"),
     "A16W8 weight scale divides": ("acc += da[k] * (oracle_e4m3fn_decode(wr[k]) * (double)sr[k / 128]);",
                                    "acc += da[k] * (oracle_e4m3fn_decode(wr[k]) / (double)sr[k / 128]);"),
 }
@@ -85,6 +93,9 @@ def _pins():
     p += [functools.partial(TG.test_power_of_two_scaling, k=k) for k in (-7, 3)]
     p += [TG.test_a16w8_hand_example, TG.test_a16w8_lossless_activations_match_numpy_matmul,
           TG.test_a16w8_equals_its_own_quantization_times_the_weights]
+    p += [TG.test_afp4wfp4_hand_example, TG.test_a8w8_hand_example]
+    p += [functools.partial(TG.test_afp4wfp4_matches_numpy_dequant_matmul, layout=k) for k in (0, 1, 2)]
+    p += [functools.partial(TG.test_a8w8_matches_numpy_dequant_matmul, layout=k) for k in (0, 2)]
     return p
 
 
