@@ -59,7 +59,8 @@ EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "add_rmsnorm",
            "dynamic_per_group_scaled_quant", "rmsq_device_supported",
            "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape",
            "rmsq_query_shape", "rmsq_set_row_group", "rmsq_set_wave_rows", "rmsq_set_row_splits",
-           "gemm_a16wfp4_prequant", "mxfp4_weight_preshuffle", "gemm_a16w8_prequant", "fp8_weight_preshuffle")
+           "gemm_a16wfp4_prequant", "mxfp4_weight_preshuffle", "gemm_a16w8_prequant", "fp8_weight_preshuffle",
+           "gemm_afp4wfp4", "gemm_a8w8_blockscale")
 
 _lib = None
 
@@ -107,6 +108,10 @@ def lib() -> C.CDLL:
         L.gemm_a16w8_prequant.argtypes = [p, i64, p, p, i32, i64, i64, i64, p, i64, p]
         L.fp8_weight_preshuffle.restype = i32
         L.fp8_weight_preshuffle.argtypes = [p, i64, i64, p, p]
+        for name in ("gemm_afp4wfp4", "gemm_a8w8_blockscale"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [p, p, i32, p, p, i32, i64, i64, i64, p, i64, p]
         _lib = L
     return _lib
 
@@ -207,6 +212,25 @@ def gemm_a16w8_prequant(a, lda, w, w_scale, w_layout, M, N, K, out, ldc, stream=
     _check(lib().gemm_a16w8_prequant(_ptr(a), int(lda), _ptr(w), _ptr(w_scale), int(w_layout), int(M), int(N),
                                      int(K), _ptr(out), int(ldc),
                                      _stream(stream, a.device if a is not None else None)))
+
+
+def gemm_afp4wfp4(a_q, a_scale, a_scale_layout, w, w_scale, w_layout, M, N, K, out, ldc, stream=None) -> None:
+    """The GEMM of MXFP4 activations as the group quantization writes them
+    (codes and e8m0 scales in any of its layouts) with MXFP4 weights, fp32
+    output, C argument order."""
+    _check(lib().gemm_afp4wfp4(_ptr(a_q), _ptr(a_scale), int(a_scale_layout), _ptr(w), _ptr(w_scale), int(w_layout),
+                               int(M), int(N), int(K), _ptr(out), int(ldc),
+                               _stream(stream, a_q.device if a_q is not None else None)))
+
+
+def gemm_a8w8_blockscale(a_q, a_scale, a_scale_layout, w, w_scale, w_layout, M, N, K, out, ldc,
+                         stream=None) -> None:
+    """The GEMM of FP8 activations as the group quantization writes them
+    (e4m3fn codes, fp32 1x128 scales row- or column-major) with e4m3fn weights
+    and fp32 128x128 block scales, fp32 output, C argument order."""
+    _check(lib().gemm_a8w8_blockscale(_ptr(a_q), _ptr(a_scale), int(a_scale_layout), _ptr(w), _ptr(w_scale),
+                                      int(w_layout), int(M), int(N), int(K), _ptr(out), int(ldc),
+                                      _stream(stream, a_q.device if a_q is not None else None)))
 
 
 def fp8_weight_preshuffle(w, N, K, w_out, stream=None) -> None:
@@ -337,4 +361,44 @@ def prequant_gemm(a, w, w_scale, fmt="mxfp4", preshuffled=False, out=None, strea
         raise ValueError("out must be a float32 [M, N] tensor with unit column stride")
     call(a, a.stride(0), w, w_scale, W_PRESHUFFLED if preshuffled else W_ROW_MAJOR, M, N, K, out, out.stride(0),
          stream)
+    return out
+
+
+def quantized_gemm(a_q, a_scale, w, w_scale, fmt="mxfp4", scale_layout=SCALE_ROW_MAJOR, preshuffled=False, out=None,
+                   stream=None):
+    """out = dq(a) @ dq(w)^T for activations already quantized by
+    ``fused_rmsnorm_quant`` or the standalone group quantization:
+    ``fmt="mxfp4"``: ``a_q`` [M, K/2] uint8 codes, ``a_scale`` its e8m0 bytes in
+    ``scale_layout`` (row-major, 32-row tiled or column-major), weights as for
+    ``prequant_gemm``; ``fmt="fp8"``: ``a_q`` [M, K] uint8 e4m3fn codes,
+    ``a_scale`` its fp32 scales (row- or column-major). Returns the fp32
+    [M, N] output (``out`` if given)."""
+    import torch
+    if a_q.dtype != torch.uint8 or a_q.dim() != 2 or not a_q.is_contiguous() or not a_scale.is_contiguous():
+        raise ValueError("a_q must be contiguous 2-D uint8 codes and a_scale contiguous")
+    if w.dtype != torch.uint8 or not w.is_contiguous() or not w_scale.is_contiguous():
+        raise ValueError("w must be contiguous uint8 codes and w_scale contiguous")
+    M, N = a_q.shape[0], w.shape[0]
+    if fmt == "mxfp4":
+        K = a_q.shape[1] * 2
+        if w.shape != (N, K // 2) or w_scale.dtype != torch.uint8 or w_scale.numel() != N * (K // 32):
+            raise ValueError("MXFP4 weights: w [N, K/2] uint8 and w_scale [N, K/32] uint8")
+        if a_scale.dtype != torch.uint8 or a_scale.numel() < rmsq_scale_bytes(M, K, 32, FMT_MXFP4_E2M1, scale_layout):
+            raise ValueError("a_scale: the e8m0 scale bytes of a_q in scale_layout")
+        call = gemm_afp4wfp4
+    elif fmt == "fp8":
+        K = a_q.shape[1]
+        if w.shape != (N, K) or w_scale.dtype != torch.float32 or w_scale.numel() != -(-N // 128) * (K // 128):
+            raise ValueError("FP8 weights: w [N, K] uint8 and w_scale [ceil(N/128), K/128] float32")
+        if a_scale.dtype != torch.float32 or a_scale.numel() < M * (K // 128):
+            raise ValueError("a_scale: the fp32 scales of a_q in scale_layout")
+        call = gemm_a8w8_blockscale
+    else:
+        raise ValueError(f"unknown weight format {fmt!r}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_q.device)
+    elif out.dtype != torch.float32 or out.shape != (M, N) or out.stride(1) != 1:
+        raise ValueError("out must be a float32 [M, N] tensor with unit column stride")
+    call(a_q, a_scale, scale_layout, w, w_scale, W_PRESHUFFLED if preshuffled else W_ROW_MAJOR, M, N, K, out,
+         out.stride(0), stream)
     return out

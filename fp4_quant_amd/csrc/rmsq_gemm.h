@@ -1,18 +1,24 @@
-// rmsq_gemm.h - A16WFP4 "prequant" GEMM for gfx950: bf16 activations are
-// quantized to MXFP4 inside the GEMM and multiplied with MXFP4 weights on the
-// block-scaled matrix cores.
+// rmsq_gemm.h - block-scaled GEMMs for gfx950 around the group
+// quantization: MXFP4 and FP8 weights times activations that are either bf16
+// and quantized inside the GEMM ("prequant"), or already quantized by the
+// group quantization (codes plus scales in one of its layouts).
 //
-// Source, cited by title: [ATT] "[Triton] DS FP4/FP8 Triton fusion and GEMM
+// Sources, cited by title: [ATT] "[Triton] DS FP4/FP8 Triton fusion and GEMM
 // optimization" lists an A16WFP4 GEMM that quantizes its activations inside
 // the GEMM (with a preshuffled-weight GEMM beside it), used at concurrency 4
 // (small M), where the norm is fused with the all-reduce and the group
-// quantization moves into the GEMM.
+// quantization moves into the GEMM; above concurrency 4 the fused RMSNorm +
+// quant feeds a separate GEMM of the quantized activations
+// (gemm_afp4wfp4_preshuffle, and block-scaled a8w8 GEMMs for FP8), whose
+// activation scale layout the quantization must match ([ATF, Technical
+// Details]).
 //
+// MXFP4 (rmsq_gemm_fp4_kernel):
 // C[m, n] = sum_k qa[m, k] 2^(ea[m, k/32] - 127) * qw[n, k] 2^(ew[n, k/32] - 127)
 // with (qa, ea) the MXFP4 group quantization (1x32 along K) of the bf16 row
 // a[m, :] - the same rule and arithmetic as the fused kernel's MXFP4 path -
-// and (qw, ew) the given weights. Products accumulate in fp32 on the matrix
-// cores.
+// or given, and (qw, ew) the weights. Products accumulate in fp32 on the
+// matrix cores.
 //
 // Mapping (small M, where the weights dominate the traffic). A workgroup of
 // up to 16 waves owns 16 output columns (one tile) and up to 64 rows (MT
@@ -29,14 +35,16 @@
 // bytes contiguous (codes) and 64 bytes (scales), so every weight load of a
 // wave reads 1 KiB of consecutive bytes.
 //
-// Activations: with at most 4 rows and one batch of steps per wave, a wave's
-// 64 activation groups are one per lane: every lane loads and quantizes one
-// (loads issued before the weight loads, so the two latencies overlap), and
-// the operand lanes fetch the codes with ds_bpermute; no workgroup barrier
-// precedes the matrix-core steps. Otherwise each wave loads and quantizes the
-// 32-groups of its own operands (lanes of rows past M read row M-1; their
-// results are not stored). All loads of a batch are unconditional: a load
-// under a branch would make the first use of any later load wait for it.
+// bf16 activations: with at most 4 rows and one batch of steps per wave, a
+// wave's 64 activation groups are one per lane: every lane loads and
+// quantizes one (loads issued before the weight loads, so the two latencies
+// overlap), and the operand lanes fetch the codes with ds_bpermute; no
+// workgroup barrier precedes the matrix-core steps. Otherwise each wave loads
+// and quantizes the 32-groups of its own operands. Quantized activations: each
+// lane loads its operand's 16 code bytes and its group's scale byte. Lanes of
+// rows past M read row M-1; their results are not stored. All loads of a
+// batch are unconditional: a load under a branch would make the first use of
+// any later load wait for it.
 #pragma once
 
 #include <algorithm>
@@ -49,12 +57,15 @@ typedef int v8i32 __attribute__((ext_vector_type(8)));
 typedef float v4f32 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
-  const uint16_t* a;      // bf16 [M, K], row stride lda elements
+  const uint16_t* a;      // bf16 [M, K], row stride lda elements (prequant)
+  const uint8_t* aq;      // or e2m1 codes [M, K/2], dense rows (quantized activations)
+  const uint8_t* as;      //    and their e8m0 scales in layout a_layout
   const uint8_t* w;       // e2m1 codes, row-major [N, K/2] or preshuffled
   const uint8_t* ws;      // e8m0 scales, row-major [N, K/32] or preshuffled
   float* out;             // fp32 [M, N], row stride ldc elements
   int64_t lda, ldc;
   int32_t M, N, K;
+  int32_t a_layout;       // 0 row-major [M, G], 1 32-row tiles, 2 column-major [G, M]
 };
 
 constexpr int kGemmMaxWaves = 16;
@@ -74,19 +85,34 @@ __device__ __forceinline__ uint32_t mx_group32(const u32x4 v[4], u32x4* codes) {
   return byte;
 }
 
+// Scale (row m, group g) of quantized activations with G groups per row and
+// M rows, in the layouts the group quantization writes, sits at
+// row_part + g * g_stride: row-major [M, G] (m G, 1), 32-row tiles with the
+// tile's 32 rows adjacent per group ((m/32) 32 G + m%32, 32), column-major
+// [G, M] (m, M).
+struct ScaleWalk {
+  int64_t row_part, g_stride;
+};
+__device__ __forceinline__ ScaleWalk act_scale_walk(int layout, int64_t m, int64_t G, int64_t M) {
+  if (layout == 1) return ScaleWalk{(m >> 5) * 32 * G + (m & 31), 32};
+  if (layout == 2) return ScaleWalk{m, M};
+  return ScaleWalk{m * G, 1};
+}
+
 // LDS bytes the kernel needs: the waves' partial sums.
 inline size_t gemm_lds_bytes(int MT, int CT, int waves) {
   return (size_t)(waves - 1) * MT * CT * 64 * sizeof(v4f32);
 }
 
 // MT row tiles of 16 rows and CT column tiles per workgroup, SW steps
-// loaded per batch, SHUF: preshuffled weights, SMALLM: the small-M path (MT ==
-// 1, SW == kGemmSmallSteps, M <= kGemmSmallRows, every wave's steps in one
-// batch); CT > 1 only there, where a wave reuses each activation operand for
-// CT tiles.
-template <int MT, int SW, bool SHUF, bool SMALLM, int CT>
-__global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16wfp4_kernel(const GemmArgs G) {
+// loaded per batch, SHUF: preshuffled weights, SMALLM: the small-M path of
+// bf16 activations (MT == 1, SW == kGemmSmallSteps, M <= kGemmSmallRows,
+// every wave's steps in one batch); CT > 1 only there, where a wave reuses
+// each activation operand for CT tiles. AQ: the activations arrive quantized.
+template <int MT, int SW, bool SHUF, bool SMALLM, int CT, bool AQ>
+__global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const GemmArgs G) {
   static_assert(CT == 1 || SMALLM, "several column tiles only on the small-M path");
+  static_assert(!(AQ && SMALLM), "the small-M path quantizes bf16 activations");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -177,15 +203,26 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16wfp4_kernel(c
     // activation row of this lane in each tile; lanes of rows past M read
     // row M-1 (their results are not stored)
     const u32x4* arow[MT];
+    const uint8_t* asrow[MT];   // quantized activations: the row's scale bytes, group stride a_gs
+    int64_t a_gs = 1;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const int m = m0 + 16 * t + (lane & 15);
-      arow[t] = reinterpret_cast<const u32x4*>(G.a + (int64_t)min(m, G.M - 1) * G.lda);
+      const int64_t m = min(m0 + 16 * t + (lane & 15), G.M - 1);
+      if constexpr (AQ) {
+        arow[t] = reinterpret_cast<const u32x4*>(G.aq + m * (G.K >> 1));
+        const ScaleWalk sw = act_scale_walk(G.a_layout, m, G.K >> 5, G.M);
+        asrow[t] = G.as + sw.row_part;
+        a_gs = sw.g_stride;
+      } else {
+        arow[t] = reinterpret_cast<const u32x4*>(G.a + m * G.lda);
+      }
     }
+    constexpr int AV = AQ ? 1 : 4;   // 16-byte loads per operand: codes, or 32 bf16
     for (int s0 = s_lo; s0 < s_hi; s0 += SW) {
       u32x4 bw[SW];
       uint32_t sb[SW];
-      u32x4 av[SW][MT][4];
+      u32x4 av[SW][MT][AV];
+      uint32_t sab[SW][MT];
       // every load of the batch unconditionally (steps past the range re-read
       // the last one and are not used), so no use waits on a partial batch
 #pragma unroll
@@ -195,18 +232,38 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16wfp4_kernel(c
         bw[i] = wq[st * ws_step];
         sb[i] = wsc[st * ws_step];
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+        for (int t = 0; t < MT; ++t) {
+          if constexpr (AQ) {
+            av[i][t][0] = arow[t][kg];          // 16 bytes = 32 e2m1 codes
+            sab[i][t] = asrow[t][kg * a_gs];
+          } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) av[i][t][j] = arow[t][kg * 4 + j];   // 64 bytes = 32 bf16
+            for (int j = 0; j < 4; ++j) av[i][t][j] = arow[t][kg * 4 + j];   // 64 bytes = 32 bf16
+          }
+        }
       }
+      // the whole batch is in flight before any use (otherwise the scheduler
+      // trades it for registers, waiting for one step's data before the next
+      // step's loads)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < SW; ++i) {
-        if (s0 + i >= s_hi) break;
+        // A step past the wave's range (its loads re-read the last one) adds
+        // zero products instead of being skipped: with no branch here, the
+        // compiler cannot sink a later step's loads below an earlier step's use.
+        const bool live = s0 + i < s_hi;   // wave-uniform
         const v8i32 bop = {(int)bw[i][0], (int)bw[i][1], (int)bw[i][2], (int)bw[i][3], 0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           u32x4 q;
-          const uint32_t sa = mx_group32(av[i][t], &q);
+          uint32_t sa;
+          if constexpr (AQ) {
+            q = av[i][t][0];
+            sa = sab[i][t];
+          } else {
+            sa = mx_group32(av[i][t], &q);
+          }
+          if (!live) q = u32x4{0u, 0u, 0u, 0u};
           const v8i32 aop = {(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
           acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[t], 4, 4, 0, (int)sa, 0, (int)sb[i]);
         }
@@ -253,11 +310,13 @@ __global__ void __launch_bounds__(256) rmsq_mxfp4_preshuffle_kernel(const uint8_
   }
 }
 
-// ------------------------------------------------------------------ A16W8 --
-// The FP8 counterpart ([ATT] lists an a16w8 GEMM for its DS FP8 runs): bf16
-// activations quantized per 1x128 group along K to e4m3fn with fp32 scales
-// (the fused kernel's FP8 rule: s = amax/448, exact codes), e4m3fn weights
-// [N, K] with fp32 scales per 128x128 block [ceil(N/128), K/128]:
+// -------------------------------------------------------------------- FP8 --
+// The FP8 counterpart (rmsq_gemm_fp8_kernel; [ATT] lists an a16w8 GEMM and
+// block-scaled a8w8 GEMMs for its DS FP8 runs): activations quantized per
+// 1x128 group along K to e4m3fn with fp32 scales - inside the GEMM from bf16
+// by the fused kernel's FP8 rule (s = amax/448, exact codes), or given with
+// their scales row- or column-major - and e4m3fn weights [N, K] with fp32
+// scales per 128x128 block [ceil(N/128), K/128]:
 //   C[m, n] = sum over K blocks b of sa[m, b] sw[n/128, b] sum_{k in b} qa[m, k] qw[n, k].
 // One 128-wide K step is one scale block, so each step's
 // v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3fn operands, unit scales) yields
@@ -273,12 +332,15 @@ __global__ void __launch_bounds__(256) rmsq_mxfp4_preshuffle_kernel(const uint8_
 // load of a wave reads consecutive bytes.
 
 struct Gemm8Args {
-  const uint16_t* a;      // bf16 [M, K], row stride lda elements
+  const uint16_t* a;      // bf16 [M, K], row stride lda elements (prequant)
+  const uint8_t* aq;      // or e4m3fn codes [M, K], dense rows (quantized activations)
+  const float* as;        //    and their fp32 scales in layout a_layout
   const uint8_t* w;       // e4m3fn codes, row-major [N, K] or preshuffled
   const float* ws;        // fp32 block scales [ceil(N/128), K/128]
   float* out;             // fp32 [M, N], row stride ldc elements
   int64_t lda, ldc;
   int32_t M, N, K;
+  int32_t a_layout;       // 0 row-major [M, K/128], 2 column-major [K/128, M]
 };
 
 // LDS bytes of the A16W8 kernel: the waves' partial sums.
@@ -310,15 +372,17 @@ __device__ __forceinline__ v8i32 fp8_codes32(const u32x4 v[4], float sc) {
 }
 
 // MT row tiles per workgroup, SW steps per batch, SHUF: preshuffled weights,
-// SMALLM: the small-M path (MT == 1, SW == kGemmSmallSteps,
-// M <= kGemmSmallRows, one batch per wave).
+// SMALLM: the small-M path of bf16 activations (MT == 1, SW ==
+// kGemmSmallSteps, M <= kGemmSmallRows, one batch per wave), AQ: the
+// activations arrive quantized.
 // Row blocks are 16 * MT rows (MT <= kGemm8MaxTiles: the activation
 // registers of more tiles would not fit beside the 32-byte operands).
 constexpr int kGemm8MaxTiles = 2;
 
-template <int MT, int SW, bool SHUF, bool SMALLM>
-__global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16w8_kernel(const Gemm8Args G) {
+template <int MT, int SW, bool SHUF, bool SMALLM, bool AQ>
+__global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const Gemm8Args G) {
   static_assert(MT <= kGemm8MaxTiles, "at most two row tiles");
+  static_assert(!(AQ && SMALLM), "the small-M path quantizes bf16 activations");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -405,16 +469,27 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16w8_kernel(con
   } else {
     // lanes of rows past M read row M-1 (their results are not stored)
     const u32x4* arow[MT];
+    const float* asrow[MT];   // quantized activations: the row's scales, block stride a_gs
+    int64_t a_gs = 1;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const int m = m0 + 16 * t + (lane & 15);
-      arow[t] = reinterpret_cast<const u32x4*>(G.a + (int64_t)min(m, G.M - 1) * G.lda);
+      const int64_t m = min(m0 + 16 * t + (lane & 15), G.M - 1);
+      if constexpr (AQ) {
+        arow[t] = reinterpret_cast<const u32x4*>(G.aq + m * G.K);
+        const ScaleWalk sw = act_scale_walk(G.a_layout, m, G.K >> 7, G.M);
+        asrow[t] = G.as + sw.row_part;
+        a_gs = sw.g_stride;
+      } else {
+        arow[t] = reinterpret_cast<const u32x4*>(G.a + m * G.lda);
+      }
     }
+    constexpr int AV = AQ ? 2 : 4;   // 16-byte loads per operand: 32 codes, or 32 bf16
     for (int s0 = s_lo; s0 < s_hi; s0 += SW) {
       u32x4 bw[SW][2];
       float sw[SW];
-      u32x4 av[SW][MT][4];
-      // unconditional loads, as in the A16WFP4 kernel
+      u32x4 av[SW][MT][AV];
+      float sav[SW][MT];
+      // unconditional loads, as in the FP4 kernel
 #pragma unroll
       for (int i = 0; i < SW; ++i) {
         const int st = min(s0 + i, s_hi - 1);   // wave-uniform
@@ -422,23 +497,40 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_a16w8_kernel(con
         bw[i][1] = wq[st * wstep + whalf];
         sw[i] = wsrow[st];
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+        for (int t = 0; t < MT; ++t) {
+          if constexpr (AQ) {
+            av[i][t][0] = arow[t][st * 8 + kb * 2];       // 32 e4m3fn codes
+            av[i][t][1] = arow[t][st * 8 + kb * 2 + 1];
+            sav[i][t] = asrow[t][st * a_gs];
+          } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) av[i][t][j] = arow[t][st * 16 + kb * 4 + j];   // 32 bf16
+            for (int j = 0; j < 4; ++j) av[i][t][j] = arow[t][st * 16 + kb * 4 + j];   // 32 bf16
+          }
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight first, as in the FP4 kernel
 #pragma unroll
       for (int i = 0; i < SW; ++i) {
-        if (s0 + i >= s_hi) break;
+        const bool live = s0 + i < s_hi;   // a dead step adds zero products, as in the FP4 kernel
         const v8i32 bop = {(int)bw[i][0][0], (int)bw[i][0][1], (int)bw[i][0][2], (int)bw[i][0][3],
                            (int)bw[i][1][0], (int)bw[i][1][1], (int)bw[i][1][2], (int)bw[i][1][3]};
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          // the row's 128-group spans the four lanes l%16 + 16q
-          uint32_t am = max(max(amax8(av[i][t][0]), amax8(av[i][t][1])), max(amax8(av[i][t][2]), amax8(av[i][t][3])));
-          am = max(am, (uint32_t)__shfl_xor((int)am, 16));
-          am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-          const float sc = fp8_scale(am);
-          const v8i32 aop = fp8_codes32(av[i][t], sc);
+          float sc;
+          v8i32 aop;
+          if constexpr (AQ) {
+            sc = sav[i][t];
+            aop = v8i32{(int)av[i][t][0][0], (int)av[i][t][0][1], (int)av[i][t][0][2], (int)av[i][t][0][3],
+                        (int)av[i][t][1][0], (int)av[i][t][1][1], (int)av[i][t][1][2], (int)av[i][t][1][3]};
+          } else {
+            // the row's 128-group spans the four lanes l%16 + 16q
+            uint32_t am = max(max(amax8(av[i][t][0]), amax8(av[i][t][1])), max(amax8(av[i][t][2]), amax8(av[i][t][3])));
+            am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+            am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+            sc = fp8_scale(am);
+            aop = fp8_codes32(av[i][t], sc);
+          }
+          if (!live) aop = v8i32{0, 0, 0, 0, 0, 0, 0, 0};
           const v4f32 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, v4f32{0.0f, 0.0f, 0.0f, 0.0f}, 0,
                                                                            0, 0, 127, 0, 127);
 #pragma unroll

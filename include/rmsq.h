@@ -267,6 +267,57 @@ rmsq_status gemm_a16w8_prequant(const void* a, int64_t lda, const void* w, const
  */
 rmsq_status fp8_weight_preshuffle(const void* w, int64_t N, int64_t K, void* w_out, void* stream);
 
+/*
+ * gemm_afp4wfp4: [ATT, run notes] above concurrency 4 the fused RMSNorm +
+ * quant feeds a separate GEMM of the quantized activations with MXFP4
+ * weights (gemm_afp4wfp4_preshuffle there), and [ATF, Technical Details]
+ * requires the activation scales in the layout that GEMM reads. This one
+ * reads what rmsnorm_quant_group_multi and dynamic_per_group_scaled_quant
+ * write for RMSQ_FMT_MXFP4_E2M1, in any of their scale layouts:
+ *   out[m, n] = sum_k dq(a)[m, k] * dq(w)[n, k]
+ * with dq(a)[m, k] = e2m1(a_q[m, k]) * 2^(e - 127), e the scale byte of
+ * (row m, group k/32) in layout a_scale_layout, and dq(w) as for
+ * gemm_a16wfp4_prequant. Accumulation as there; gemm_afp4wfp4 of the group
+ * quantization of rows `a` equals gemm_a16wfp4_prequant of `a` bit for bit
+ * when the two run with the same launch shape, and agrees within fp32
+ * rounding otherwise.
+ *
+ *  a_q            [M, K/2] e2m1 codes, rows dense (K/2 bytes apart), element
+ *                 2j of a row in the low nibble of byte j; 16-byte aligned.
+ *  a_scale        e8m0 bytes, rmsq_scale_bytes(M, K, 32, RMSQ_FMT_MXFP4_E2M1,
+ *                 a_scale_layout) of them.
+ *  a_scale_layout RMSQ_SCALE_ROW_MAJOR, RMSQ_SCALE_TILED32 or
+ *                 RMSQ_SCALE_COL_MAJOR.
+ *  w, w_scale, w_layout, out, ldc, M, N, K, ownership, errors and the stream
+ *                 as for gemm_a16wfp4_prequant.
+ */
+rmsq_status gemm_afp4wfp4(const void* a_q, const void* a_scale, int32_t a_scale_layout, const void* w,
+                          const void* w_scale, int32_t w_layout, int64_t M, int64_t N, int64_t K, void* out,
+                          int64_t ldc, void* stream);
+
+/*
+ * gemm_a8w8_blockscale: the FP8 counterpart, [ATT]'s block-scaled a8w8 GEMMs
+ * and [FRQ, Motivation]'s (fp8, scale) hand-off to the block-FP8 linear: the
+ * activations as rmsnorm_quant_group_multi writes them for
+ * RMSQ_FMT_FP8_E4M3FN,
+ *   out[m, n] = sum_k (a_q[m, k] * s[m, k/128]) * dq(w)[n, k]
+ * with s[m, b] the fp32 scale of (row m, group b) in layout a_scale_layout
+ * and dq(w) as for gemm_a16w8_prequant. Each 128-wide K block's sum of code
+ * products comes from the matrix cores and is scaled and accumulated in
+ * fp32 as there; of the group quantization of rows `a` it equals
+ * gemm_a16w8_prequant of `a` within that accumulation's rounding.
+ *
+ *  a_q            [M, K] e4m3fn codes, rows dense, 16-byte aligned; no NaN
+ *                 codes.
+ *  a_scale        fp32, M * K/128 of them, finite, 4-byte aligned.
+ *  a_scale_layout RMSQ_SCALE_ROW_MAJOR or RMSQ_SCALE_COL_MAJOR.
+ *  w, w_scale, w_layout, out, ldc, M, N, K, ownership, errors and the stream
+ *                 as for gemm_a16w8_prequant.
+ */
+rmsq_status gemm_a8w8_blockscale(const void* a_q, const void* a_scale, int32_t a_scale_layout, const void* w,
+                                 const void* w_scale, int32_t w_layout, int64_t M, int64_t N, int64_t K, void* out,
+                                 int64_t ldc, void* stream);
+
 /* 1 if HIP device `device` is a gfx950 (MI355X-class) GPU, else 0.
  * [ARQ, Motivation]: the single-kernel path is gated to gfx95x devices and
  * callers fall back otherwise; this library's entry points return

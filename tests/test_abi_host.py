@@ -353,3 +353,40 @@ def test_binding_refuses_host_tensors():
         fq.dynamic_per_group_scaled_quant(x, 4, 256, 128, 0, 0, x, x, stream=0)
     with pytest.raises(ValueError):
         fq.gemm_a16wfp4_prequant(x, 256, x, x, fq.W_ROW_MAJOR, 4, 16, 256, x, 16, stream=0)
+
+
+@pytest.mark.parametrize("entry", ["gemm_afp4wfp4", "gemm_a8w8_blockscale"])
+def test_quantized_activation_gemms_validate(entry):
+    L = fq.lib()
+    E = fq.RMSQ_ERR_INVALID_ARG
+    fp8 = entry == "gemm_a8w8_blockscale"
+    q, sa, w, s, o = A, A + 50 * MB, A + 100 * MB, A + 200 * MB, A + 300 * MB
+    R = fq.W_ROW_MAJOR
+    f = getattr(L, entry)
+
+    def g(q=q, sa=sa, al=fq.SCALE_ROW_MAJOR, w=w, s=s, lay=R, M=4, N=32, K=256, o=o, ldc=32):
+        # entry(a_q, a_scale, a_scale_layout, w, w_scale, w_layout, M, N, K, out, ldc, stream)
+        return f(q, sa, al, w, s, lay, M, N, K, o, ldc, None)
+
+    assert g(N=24, ldc=24) == E          # N % 16
+    assert g(K=200) == E                 # K % 128
+    assert g(M=-1) == E
+    assert g(ldc=16) == E                # ldc < N
+    assert g(lay=2) == E                 # unknown weight layout
+    assert g(al=3) == E                  # unknown activation scale layout
+    assert (g(al=fq.SCALE_TILED32) == E) == fp8   # tiled scales: MXFP4 only
+    assert g(q=q + 8) == E               # a_q alignment
+    if fp8:
+        assert g(sa=sa + 2) == E         # fp32 scales alignment
+    assert g(w=w + 8) == E               # w alignment
+    assert g(o=o + 2) == E               # out alignment
+    assert g(o=q + 64) == E              # out overlaps the codes
+    assert g(o=sa) == E                  # out overlaps the activation scales
+    assert g(o=w + 1024) == E            # out overlaps w
+    assert g(q=None) == E                # NULL
+    assert g(sa=None) == E
+    assert g(M=0) == fq.RMSQ_OK          # no-op, pointers unused
+    assert g(M=0, q=None, sa=None) == fq.RMSQ_OK
+    assert g() in (fq.RMSQ_OK, fq.RMSQ_ERR_UNSUPPORTED)
+    if not fq.rmsq_device_supported(0):
+        assert g() == fq.RMSQ_ERR_UNSUPPORTED

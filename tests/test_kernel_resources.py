@@ -86,12 +86,13 @@ def test_gemm_variants_fit_sixteen_waves(kernels):
     """The GEMM launches up to 16 waves per workgroup (4 per SIMD), so each
     variant must fit 128 registers (VGPRs + AGPRs) and the LDS of its
     partial sums."""
-    gemm = {n: k for n, k in kernels.items() if "rmsq_gemm_a16wfp4_kernel" in (n or "")}
-    # (4 row-tile counts + the small-M variant with 1 or 2 column tiles) x 2 weight layouts
-    assert len(gemm) == 12, sorted(gemm)
-    gemm8 = {n: k for n, k in kernels.items() if "rmsq_gemm_a16w8_kernel" in (n or "")}
-    # (1 or 2 row tiles + the small-M variant) x 2 weight layouts
-    assert len(gemm8) == 6, sorted(gemm8)
+    gemm = {n: k for n, k in kernels.items() if "rmsq_gemm_fp4_kernel" in (n or "")}
+    # (4 row-tile counts + the small-M variant with 1 or 2 column tiles + 4 row-tile
+    # counts of quantized activations) x 2 weight layouts
+    assert len(gemm) == 20, sorted(gemm)
+    gemm8 = {n: k for n, k in kernels.items() if "rmsq_gemm_fp8_kernel" in (n or "")}
+    # (1 or 2 row tiles + the small-M variant + 1 or 2 row tiles of quantized activations) x 2 weight layouts
+    assert len(gemm8) == 10, sorted(gemm8)
     gemm.update(gemm8)
     for n, k in gemm.items():
         assert k["vgpr_count"] + k["agpr_count"] <= 128, (n, k)
