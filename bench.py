@@ -97,60 +97,130 @@ class Workload:
         fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0], stream or self.stream)
 
 
-def gemm_bytes(M, N, K, fmt=1):
+def gemm_bytes(M, N, K, fmt=1, aq=False):
     """Weight codes + scales read (MXFP4: e8m0 per 1x32; FP8: fp32 per 128x128
-    block), bf16 activations read, fp32 output written."""
+    block), activations read (bf16, or codes + scales when already
+    quantized), fp32 output written."""
     if fmt == 1:
         w = N * K // 2 + N * K // 32
+        a = M * (K // 2 + K // 32) if aq else M * K * 2
     else:
         w = N * K + -(-N // 128) * (K // 128) * 4
-    return w + M * K * 2 + M * N * 4
+        a = M * (K + K // 128 * 4) if aq else M * K * 2
+    return w + a + M * N * 4
 
 
-# The prequant GEMMs after the attention input norm of a 7168-wide model
-# (1536 + 576 outputs) at a decode batch of 4, preshuffled weights: MXFP4
-# weights (A16WFP4) and FP8 block-scaled weights (A16W8).
+# The GEMMs after the attention input norm of a 7168-wide model (1536 + 576
+# outputs) at a decode batch of 4, preshuffled weights: the prequant GEMMs
+# (bf16 activations quantized inside) with MXFP4 weights (A16WFP4) and FP8
+# block-scaled weights (A16W8), and the GEMMs of already quantized
+# activations (row-major scales) with the same weights.
 GEMM_SPECS = {
     "gemm_a16wfp4_decode": dict(M=4, N=2112, K=7168, fmt=1),
     "gemm_a16w8_decode": dict(M=4, N=2112, K=7168, fmt=0),
+    "gemm_afp4wfp4_decode": dict(M=4, N=2112, K=7168, fmt=1, aq=True),
+    "gemm_a8w8_decode": dict(M=4, N=2112, K=7168, fmt=0, aq=True),
 }
 
 
-class GemmWorkload:
-    """Rotating sets of preshuffled weights (and activations, outputs) for the
-    A16WFP4 prequant GEMM, enough sets that no launch finds its weights in
-    the Infinity Cache."""
+def _weight_sets(N, K, fmt, per_set_bytes, g):
+    """Preshuffled copies of the weights, enough that no launch finds its
+    weights in the Infinity Cache."""
+    import torch
+    import fp4_quant_amd as fq
+    w, ws = torch.from_numpy(g["w"]).cuda(), torch.from_numpy(g["ws"]).cuda()
+    sets = []
+    for _ in range(max(2, min(512, -(-3 * MALL_BYTES // per_set_bytes)))):
+        sw = torch.empty_like(w)
+        if fmt == 1:
+            sws = torch.empty_like(ws)
+            fq.mxfp4_weight_preshuffle(w, ws, N, K, sw, sws)
+        else:
+            sws = ws.clone()
+            fq.fp8_weight_preshuffle(w, N, K, sw)
+        sets.append((sw, sws))
+    return sets
 
-    def __init__(self, name, M, N, K, fmt):
+
+class GemmWorkload:
+    """Rotating sets of preshuffled weights (and activations, outputs) for one
+    GEMM, enough sets that no launch finds its weights in the Infinity Cache.
+    aq: the activations come quantized (made once, by the library's group
+    quantization, row-major scales)."""
+
+    def __init__(self, name, M, N, K, fmt, aq=False):
         import torch
         import fp4_quant_amd as fq
         from fp4_quant_amd import inputs
-        self.name, self.M, self.N, self.K, self.fmt = name, M, N, K, fmt
+        self.name, self.M, self.N, self.K, self.fmt, self.aq = name, M, N, K, fmt, aq
         self.rows = M
-        self.bytes = gemm_bytes(M, N, K, fmt)
+        self.bytes = gemm_bytes(M, N, K, fmt, aq)
         g = inputs.make_gemm(M, N, K) if fmt == 1 else inputs.make_gemm8(M, N, K)
         a = torch.from_numpy(g["a"].view("int16")).view(torch.bfloat16).cuda()
-        w, ws = torch.from_numpy(g["w"]).cuda(), torch.from_numpy(g["ws"]).cuda()
-        nsets = max(2, min(512, -(-3 * MALL_BYTES // self.bytes)))
-        self.sets = []
-        for _ in range(nsets):
-            sw = torch.empty_like(w)
-            if fmt == 1:
-                sws = torch.empty_like(ws)
-                fq.mxfp4_weight_preshuffle(w, ws, N, K, sw, sws)
-            else:
-                sws = ws.clone()
-                fq.fp8_weight_preshuffle(w, N, K, sw)
-            out = torch.zeros((M, N), dtype=torch.float32, device="cuda")
-            self.sets.append((a.clone(), sw, sws, out))
+        acts = (a,)
+        if aq:
+            q, sc, _ = fq.alloc_outputs(M, K, fmt)
+            fq.dynamic_per_group_scaled_quant(a, M, K, 32 if fmt == 1 else 128, fmt, 0, q, sc)
+            acts = (q, sc)
+        self.sets = [(tuple(t.clone() for t in acts), sw, sws, torch.zeros((M, N), dtype=torch.float32, device="cuda"))
+                     for sw, sws in _weight_sets(N, K, fmt, self.bytes, g)]
         torch.cuda.synchronize()
         self.stream = torch.cuda.current_stream().cuda_stream
 
     def launch(self, i, stream=None):
         import fp4_quant_amd as fq
-        a, w, ws, out = self.sets[i % len(self.sets)]
-        f = fq.gemm_a16wfp4_prequant if self.fmt == 1 else fq.gemm_a16w8_prequant
-        f(a, self.K, w, ws, fq.W_PRESHUFFLED, self.M, self.N, self.K, out, self.N, stream or self.stream)
+        acts, w, ws, out = self.sets[i % len(self.sets)]
+        st = stream or self.stream
+        if self.aq:
+            f = fq.gemm_afp4wfp4 if self.fmt == 1 else fq.gemm_a8w8_blockscale
+            f(acts[0], acts[1], 0, w, ws, fq.W_PRESHUFFLED, self.M, self.N, self.K, out, self.N, st)
+        else:
+            f = fq.gemm_a16wfp4_prequant if self.fmt == 1 else fq.gemm_a16w8_prequant
+            f(acts[0], self.K, w, ws, fq.W_PRESHUFFLED, self.M, self.N, self.K, out, self.N, st)
+
+
+class NormGemmPipeline:
+    """One step of the attention-input path on M token rows of 7168: residual
+    add + RMSNorm of the rows, then the 2112-output MXFP4-weight GEMM, in the
+    two orders the pages choose between by concurrency:
+    "quant_gemm": the fused norm + MXFP4 group quantization (codes + e8m0
+    scales, in 32-row tiles from 32 rows on, row-major below, the pages' rule),
+    then the GEMM of the quantized activations;
+    "prequant": the norm alone (bf16 rows), then the prequant GEMM that
+    quantizes inside. Weights rotate past the Infinity Cache."""
+
+    def __init__(self, M, policy, N=2112, K=7168):
+        import torch
+        import fp4_quant_amd as fq
+        from fp4_quant_amd import inputs
+        self.M, self.N, self.K, self.policy = M, N, K, policy
+        p = inputs.make_problem(M, K, seed_x=0, residual=True)
+        g = inputs.make_gemm(M, N, K)
+        b = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
+        self.x, self.r, self.gamma = b(p["x"]), b(p["residual"]), b(p["gamma"])
+        self.ro = torch.empty_like(self.r)
+        self.layout = fq.SCALE_TILED32 if M >= 32 else fq.SCALE_ROW_MAJOR
+        self.q, self.sc, _ = fq.alloc_outputs(M, K, fq.FMT_MXFP4_E2M1, self.layout)
+        self.yb = torch.empty_like(self.x)
+        self.probs = fq.problem_array([fq.make_problem(self.x, self.gamma, 1e-6, self.q, self.sc, residual_in=self.r,
+                                                       residual_out=self.ro, fmt=fq.FMT_MXFP4_E2M1,
+                                                       scale_layout=self.layout)])
+        self.sets = [(sw, sws, torch.zeros((M, N), dtype=torch.float32, device="cuda"))
+                     for sw, sws in _weight_sets(N, K, 1, gemm_bytes(M, N, K, 1), g)]
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def launch(self, i, stream=None):
+        import fp4_quant_amd as fq
+        w, ws, out = self.sets[i % len(self.sets)]
+        st = stream or self.stream
+        M, N, K = self.M, self.N, self.K
+        if self.policy == "quant_gemm":
+            fq.rmsnorm_quant_group_multi(self.probs, st)
+            fq.gemm_afp4wfp4(self.q, self.sc, self.layout, w, ws, fq.W_PRESHUFFLED, M, N, K, out, N, st)
+        else:
+            fq.add_rmsnorm(self.x, self.r, self.gamma, 1e-6, M, K, self.ro, self.yb, st)
+            fq.gemm_a16wfp4_prequant(self.yb, K, w, ws, fq.W_PRESHUFFLED, M, N, K, out, N, st)
 
 
 class UnfusedWorkload(Workload):
@@ -460,6 +530,8 @@ def main():
             pg = time_workload_graph(wk, 100)
             gb = wk.bytes / (pl * 1e-3) / 1e9
             configs[name] = {"M": g["M"], "N": g["N"], "K": g["K"],
+                             "activations": "quantized (codes + row-major scales)" if g.get("aq") else
+                                            "bf16, quantized inside the GEMM",
                              "weights": ("MXFP4" if g["fmt"] == 1 else "FP8 e4m3fn, 128x128 block scales") +
                                         ", preshuffled",
                              "us_per_launch": round(pl * 1e3, 2), "GBps": round(gb, 1),
@@ -473,6 +545,24 @@ def main():
             del wk
             torch.cuda.empty_cache()
     if not args.no_configs:
+        # the pages' choice by concurrency, on one GPU: fused norm + quant then
+        # the GEMM of quantized activations, against the norm then the
+        # prequant GEMM (µs per step from HIP graph replays, 2 launches each)
+        pol = {}
+        for M in (4, 16, 64, 256):
+            row = {}
+            for policy in ("quant_gemm", "prequant"):
+                log(f"bench: norm + GEMM, {policy}, M={M}")
+                wp = NormGemmPipeline(M, policy)
+                row[policy + "_us"] = round(time_workload_graph(wp, 100) * 1e3, 2)
+                del wp
+                torch.cuda.empty_cache()
+            row["faster"] = min(("quant_gemm", "prequant"), key=lambda k: row[k + "_us"])
+            pol[f"M={M}"] = row
+        configs["norm_gemm_policy"] = {"N": 2112, "K": 7168, "weights": "MXFP4, preshuffled",
+                                       "quant_gemm": "fused residual + RMSNorm + MXFP4 quant (32-row tiled scales "
+                                                     "from 32 rows, row-major below), then gemm_afp4wfp4",
+                                       "prequant": "add_rmsnorm (bf16), then gemm_a16wfp4_prequant", **pol}
         for name in ("prefill", "decode"):
             sp, f, lay = SPECS[name]
             log(f"bench: unfused pair on the {name} batch")

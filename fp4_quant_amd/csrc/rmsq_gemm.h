@@ -99,19 +99,51 @@ __device__ __forceinline__ ScaleWalk act_scale_walk(int layout, int64_t m, int64
   return ScaleWalk{m * G, 1};
 }
 
-// LDS bytes the kernel needs: the waves' partial sums.
+// LDS bytes the kernel needs: the waves' partial sums, NT = MT * CT tiles of
+// 16 x 16 fp32 per wave.
 inline size_t gemm_lds_bytes(int MT, int CT, int waves) {
-  return (size_t)(waves - 1) * MT * CT * 64 * sizeof(v4f32);
+  return (size_t)waves * MT * CT * 64 * sizeof(v4f32);
 }
 
-// MT row tiles of 16 rows and CT column tiles per workgroup, SW steps
-// loaded per batch, SHUF: preshuffled weights, SMALLM: the small-M path of
-// bf16 activations (MT == 1, SW == kGemmSmallSteps, M <= kGemmSmallRows,
-// every wave's steps in one batch); CT > 1 only there, where a wave reuses
-// each activation operand for CT tiles. AQ: the activations arrive quantized.
+// The epilogue of both GEMM kernels. Every wave writes its NT accumulator
+// tiles (lane l: column l%16, rows 4(l/16) .. +3) to LDS; after the barrier
+// each thread adds up one of the workgroup's NT * 256 outputs over the waves
+// in wave order (fixed for a shape, so results repeat bit for bit) and
+// stores it, 16 consecutive threads storing 16 consecutive columns of a row.
+// The loads of all waves' partials are issued together (waves past the
+// launch's count re-read the last one and add zero) instead of one LDS round
+// trip per wave. Tile t covers columns col0 + 16 (t % CT) and rows
+// m0 + 16 (t / CT).
+template <int NT, int CT>
+__device__ __forceinline__ void gemm_reduce_store(const v4f32 (&acc)[NT], uint8_t* lds, int wave, int waves, int lane,
+                                                  int col0, int m0, float* out, int64_t ldc, int M) {
+  v4f32* part = reinterpret_cast<v4f32*>(lds);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) part[(wave * NT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  const float* pf = reinterpret_cast<const float*>(lds);
+  constexpr int kOut = NT * 256;
+  for (int e = threadIdx.x; e < kOut; e += blockDim.x) {
+    const int c16 = e & 15, r = (e >> 4) & 3, q = (e >> 6) & 3, t = e >> 8;
+    const int idx = (t * 64 + q * 16 + c16) * 4 + r;   // float of (tile t, lane 16q + c16, row r) in one wave's part
+    float c = pf[idx];
+#pragma unroll
+    for (int w = 1; w < kGemmMaxWaves; ++w) {
+      const float p = pf[min(w, waves - 1) * kOut + idx];
+      c += w < waves ? p : 0.0f;
+    }
+    const int m = m0 + 16 * (t / CT) + 4 * q + r;
+    if (m < M) out[(int64_t)m * ldc + col0 + 16 * (t % CT) + c16] = c;
+  }
+}
+
+// MT row tiles of 16 rows and CT column tiles per workgroup (a wave reuses
+// each activation operand for CT tiles), SW steps loaded per batch, SHUF:
+// preshuffled weights, SMALLM: the small-M path of bf16 activations (MT ==
+// 1, SW == kGemmSmallSteps, M <= kGemmSmallRows, every wave's steps in one
+// batch). AQ: the activations arrive quantized.
 template <int MT, int SW, bool SHUF, bool SMALLM, int CT, bool AQ>
 __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const GemmArgs G) {
-  static_assert(CT == 1 || SMALLM, "several column tiles only on the small-M path");
   static_assert(!(AQ && SMALLM), "the small-M path quantizes bf16 activations");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
@@ -219,8 +251,8 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const
     }
     constexpr int AV = AQ ? 1 : 4;   // 16-byte loads per operand: codes, or 32 bf16
     for (int s0 = s_lo; s0 < s_hi; s0 += SW) {
-      u32x4 bw[SW];
-      uint32_t sb[SW];
+      u32x4 bw[SW][CT];
+      uint32_t sb[SW][CT];
       u32x4 av[SW][MT][AV];
       uint32_t sab[SW][MT];
       // every load of the batch unconditionally (steps past the range re-read
@@ -229,8 +261,11 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const
       for (int i = 0; i < SW; ++i) {
         const int st = min(s0 + i, s_hi - 1);   // wave-uniform
         const int kg = st * 4 + kb;             // 32-element group index along K
-        bw[i] = wq[st * ws_step];
-        sb[i] = wsc[st * ws_step];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          bw[i][ct] = wq[ct * wq_tile + st * ws_step];
+          sb[i][ct] = wsc[ct * ws_tile + st * ws_step];
+        }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           if constexpr (AQ) {
@@ -252,7 +287,6 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const
         // zero products instead of being skipped: with no branch here, the
         // compiler cannot sink a later step's loads below an earlier step's use.
         const bool live = s0 + i < s_hi;   // wave-uniform
-        const v8i32 bop = {(int)bw[i][0], (int)bw[i][1], (int)bw[i][2], (int)bw[i][3], 0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           u32x4 q;
@@ -265,32 +299,18 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const
           }
           if (!live) q = u32x4{0u, 0u, 0u, 0u};
           const v8i32 aop = {(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
-          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[t], 4, 4, 0, (int)sa, 0, (int)sb[i]);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const v8i32 bop = {(int)bw[i][ct][0], (int)bw[i][ct][1], (int)bw[i][ct][2], (int)bw[i][ct][3], 0, 0, 0, 0};
+            acc[t * CT + ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[t * CT + ct], 4, 4, 0,
+                                                                               (int)sa, 0, (int)sb[i][ct]);
+          }
         }
       }
     }
   }
 
-  // the waves' partial sums meet in LDS; wave 0 adds them in wave order
-  v4f32* part = reinterpret_cast<v4f32*>(lds);
-  if (wave > 0) {
-#pragma unroll
-    for (int t = 0; t < MT * CT; ++t) part[((wave - 1) * MT * CT + t) * 64 + lane] = acc[t];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int t = 0; t < MT * CT; ++t) {
-    v4f32 c = acc[t];
-    for (int w = 0; w < waves - 1; ++w) c += part[(w * MT * CT + t) * 64 + lane];
-    // result lane l: column 16 (tile + ct) + l%16, rows 16 (t / CT) + 4 (l/16) + r
-    const int col = n + 16 * (t % CT);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 16 * (t / CT) + 4 * (lane >> 4) + r;
-      if (m < G.M) G.out[(int64_t)m * G.ldc + col] = c[r];
-    }
-  }
+  gemm_reduce_store<MT * CT, CT>(acc, lds, wave, waves, lane, tile * 16, m0, G.out, G.ldc, G.M);
 }
 
 // Row-major MXFP4 weights to the preshuffled operand order: one thread per
@@ -343,9 +363,9 @@ struct Gemm8Args {
   int32_t a_layout;       // 0 row-major [M, K/128], 2 column-major [K/128, M]
 };
 
-// LDS bytes of the A16W8 kernel: the waves' partial sums.
+// LDS bytes of the FP8 kernel: the waves' partial sums.
 inline size_t gemm8_lds_bytes(int MT, int waves) {
-  return (size_t)(waves - 1) * MT * 64 * sizeof(v4f32);
+  return (size_t)waves * MT * 64 * sizeof(v4f32);
 }
 
 __device__ __forceinline__ void unpack_bf16x8(const u32x4 w, float f[8]) {
@@ -543,23 +563,7 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const
     }
   }
 
-  v4f32* part = reinterpret_cast<v4f32*>(lds);
-  if (wave > 0) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t) part[((wave - 1) * MT + t) * 64 + lane] = acc[t];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    v4f32 c = acc[t];
-    for (int w = 0; w < waves - 1; ++w) c += part[(w * MT + t) * 64 + lane];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 16 * t + 4 * (lane >> 4) + r;
-      if (m < G.M) G.out[(int64_t)m * G.ldc + n] = c[r];
-    }
-  }
+  gemm_reduce_store<MT, 1>(acc, lds, wave, waves, lane, tile * 16, m0, G.out, G.ldc, G.M);
 }
 
 // Row-major e4m3fn weights to the preshuffled order: 16-byte unit

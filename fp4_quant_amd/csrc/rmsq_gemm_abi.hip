@@ -13,8 +13,28 @@ namespace {
 
 using namespace rmsq_abi;
 
-// The MXFP4 GEMM: grid x = 16-column tiles of the output, y = blocks of 64
-// rows; the row tiles per block (MT) follow M.
+// Steps per batch of the quantized-activation MXFP4 kernel with MT row and
+// CT column tiles: registers per step are 5 per row tile (codes, scale) and
+// 5 per column tile (weights, scale), beside 4 * MT * CT accumulators, within
+// 128 per lane.
+constexpr int aq_fp4_steps(int MT, int CT) { return CT == 1 ? (MT <= 2 ? 4 : 2) : 2; }
+
+// Column tiles per workgroup of the quantized-activation MXFP4 kernel
+// (measured, N = 2112, K = 7168): one up to 64 rows, where the weight stream
+// wants the most workgroups; two above (then MT = 4), where each workgroup's
+// activation loads - the kernel is bound by vector L1 accesses there - serve
+// twice the columns (128 rows: 33 -> 18.7 us, 256 rows: 49 -> 34 us; 64
+// rows: 17.4 -> 18.6 us).
+int aq_fp4_col_tiles(int64_t M, int64_t N) { return M > 64 && (N / 16) % 2 == 0 ? 2 : 1; }
+
+template <bool SHUF, int MT, int CT>
+void launch_aq_fp4(const rmsq::GemmArgs& G, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<MT, aq_fp4_steps(MT, CT), SHUF, false, CT, true>), grid, block, lds,
+                     s, G);
+}
+
+// The MXFP4 GEMM: grid x = groups of CT 16-column tiles of the output, y =
+// blocks of 64 rows; the row tiles per block (MT) follow M.
 template <bool SHUF>
 void launch_gemm(const rmsq::GemmArgs& G, int MT, int CT, bool small_m, bool aq, int waves, hipStream_t s) {
   const dim3 grid((unsigned)(G.N / (16 * CT)),
@@ -22,12 +42,13 @@ void launch_gemm(const rmsq::GemmArgs& G, int MT, int CT, bool small_m, bool aq,
       block(64 * waves);
   const size_t lds = rmsq::gemm_lds_bytes(MT, CT, waves);
   constexpr int SS = rmsq::kGemmSmallSteps;
-  if (aq) {   // quantized activations: 5 registers per step and tile beside the weights' 5
-    switch (MT) {
-      case 1: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<1, 4, SHUF, false, 1, true>), grid, block, lds, s, G); break;
-      case 2: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<2, 4, SHUF, false, 1, true>), grid, block, lds, s, G); break;
-      case 3: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<3, 2, SHUF, false, 1, true>), grid, block, lds, s, G); break;
-      default: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<4, 2, SHUF, false, 1, true>), grid, block, lds, s, G); break;
+  if (aq) {
+    switch (CT == 2 ? 0 : MT) {   // two column tiles come with four row tiles (aq_fp4_col_tiles)
+      case 0: launch_aq_fp4<SHUF, 4, 2>(G, grid, block, lds, s); break;
+      case 1: launch_aq_fp4<SHUF, 1, 1>(G, grid, block, lds, s); break;
+      case 2: launch_aq_fp4<SHUF, 2, 1>(G, grid, block, lds, s); break;
+      case 3: launch_aq_fp4<SHUF, 3, 1>(G, grid, block, lds, s); break;
+      default: launch_aq_fp4<SHUF, 4, 1>(G, grid, block, lds, s); break;
     }
     return;
   }
@@ -46,10 +67,6 @@ void launch_gemm(const rmsq::GemmArgs& G, int MT, int CT, bool small_m, bool aq,
     default: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<4, 1, SHUF, false, 1, false>), grid, block, lds, s, G); break;
   }
 }
-
-// Steps per batch of the quantized-activation MXFP4 kernels for MT row tiles
-// (the instances launched above).
-int aq_fp4_steps(int MT) { return MT <= 2 ? 4 : 2; }
 
 rmsq_status check_gemm_weights(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N % 16 || K % 128)
@@ -151,11 +168,18 @@ rmsq_status run_gemm(const GemmActs& A, const void* w, const void* w_scale, int3
   const int steps = (int)(K / 128);
   const int small_waves = (steps + rmsq::kGemmSmallSteps - 1) / rmsq::kGemmSmallSteps;
   const bool small_m = !A.quantized && M <= rmsq::kGemmSmallRows && small_waves <= rmsq::kGemmMaxWaves;
-  const int SW = A.quantized ? aq_fp4_steps(MT) : MT == 1 ? 4 : MT == 2 ? 2 : 1;
-  const int waves = small_m ? small_waves : std::min(rmsq::kGemmMaxWaves, std::max(1, (steps + SW - 1) / SW));
-  // Two column tiles per small-M workgroup once there are at least 256 tiles:
-  // half as many workgroups each quantize the activations for twice the weights.
-  const int CT = small_m && (N / 16) % 2 == 0 && N / 16 >= kComputeUnits ? 2 : 1;
+  // Column tiles per workgroup: on the small-M path two once there are at
+  // least 256 tiles (half as many workgroups each quantize the activations
+  // for twice the weights); for quantized activations as aq_fp4_col_tiles
+  // chooses (N divisible).
+  int CT = small_m && (N / 16) % 2 == 0 && N / 16 >= kComputeUnits ? 2 : 1;
+  if (A.quantized) CT = MT == 4 ? aq_fp4_col_tiles(M, N) : 1;
+  const int SW = A.quantized ? aq_fp4_steps(MT, CT) : MT == 1 ? 4 : MT == 2 ? 2 : 1;
+  // the waves' partial sums (1 KiB per row and column tile of each wave)
+  // stay within 64 KiB of LDS
+  const int waves = std::min(64 / (MT * CT), small_m ? small_waves
+                                                         : std::min(rmsq::kGemmMaxWaves,
+                                                                    std::max(1, (steps + SW - 1) / SW)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w_layout == RMSQ_W_PRESHUFFLED)
     launch_gemm<true>(G, MT, CT, small_m, A.quantized, waves, s);

@@ -67,8 +67,10 @@ def _within(got, want, bound):
 
 # decode, one to four row tiles of 16 (MXFP4) / one or two (FP8), several row
 # blocks, a ragged last 32-row scale tile (37, 70, 130 rows), long K
+# (two column tiles per workgroup above 64 rows when N/16 is even: 130 x 32, 200 x 96)
 SHAPES = [(4, 2112, 7168), (1, 16, 128), (5, 32, 256), (16, 64, 384), (17, 32, 1024), (33, 48, 512),
-          (37, 32, 256), (64, 32, 7168), (70, 16, 256), (130, 32, 640), (4, 4096, 256), (4, 32, 8320)]
+          (37, 32, 256), (64, 32, 7168), (70, 16, 256), (130, 32, 640), (200, 96, 512), (4, 4096, 256),
+          (4, 32, 8320)]
 SHAPES8 = [(4, 2112, 7168), (1, 16, 128), (3, 32, 256), (5, 144, 384), (16, 64, 1024), (17, 32, 512),
            (33, 48, 256), (70, 16, 640), (4, 32, 8320)]
 

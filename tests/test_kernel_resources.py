@@ -88,8 +88,8 @@ def test_gemm_variants_fit_sixteen_waves(kernels):
     partial sums."""
     gemm = {n: k for n, k in kernels.items() if "rmsq_gemm_fp4_kernel" in (n or "")}
     # (4 row-tile counts + the small-M variant with 1 or 2 column tiles + 4 row-tile
-    # counts of quantized activations) x 2 weight layouts
-    assert len(gemm) == 20, sorted(gemm)
+    # counts of quantized activations + their 4 x 2 tile variant) x 2 weight layouts
+    assert len(gemm) == 22, sorted(gemm)
     gemm8 = {n: k for n, k in kernels.items() if "rmsq_gemm_fp8_kernel" in (n or "")}
     # (1 or 2 row tiles + the small-M variant + 1 or 2 row tiles of quantized activations) x 2 weight layouts
     assert len(gemm8) == 10, sorted(gemm8)
