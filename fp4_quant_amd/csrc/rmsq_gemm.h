@@ -99,6 +99,11 @@ __device__ __forceinline__ ScaleWalk act_scale_walk(int layout, int64_t m, int64
   return ScaleWalk{m * G, 1};
 }
 
+// Waves per workgroup with NT accumulator tiles per wave: at most 16, and
+// their partial sums (1 KiB per tile and wave) within 64 KiB of LDS. The
+// launch bound follows, so kernels with more tiles get more registers.
+constexpr int gemm_max_waves(int NT) { return 64 / NT < kGemmMaxWaves ? 64 / NT : kGemmMaxWaves; }
+
 // LDS bytes the kernel needs: the waves' partial sums, NT = MT * CT tiles of
 // 16 x 16 fp32 per wave.
 inline size_t gemm_lds_bytes(int MT, int CT, int waves) {
@@ -141,9 +146,10 @@ __device__ __forceinline__ void gemm_reduce_store(const v4f32 (&acc)[NT], uint8_
 // each activation operand for CT tiles), SW steps loaded per batch, SHUF:
 // preshuffled weights, SMALLM: the small-M path of bf16 activations (MT ==
 // 1, SW == kGemmSmallSteps, M <= kGemmSmallRows, every wave's steps in one
-// batch). AQ: the activations arrive quantized.
-template <int MT, int SW, bool SHUF, bool SMALLM, int CT, bool AQ>
-__global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const GemmArgs G) {
+// batch). AQ: the activations arrive quantized (1: each operand loaded
+// directly, 2: a pair of steps per load, redistributed; see below).
+template <int MT, int SW, bool SHUF, bool SMALLM, int CT, int AQ>
+__global__ void __launch_bounds__(64 * gemm_max_waves(MT * CT)) rmsq_gemm_fp4_kernel(const GemmArgs G) {
   static_assert(!(AQ && SMALLM), "the small-M path quantizes bf16 activations");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
@@ -236,25 +242,42 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const
     // row M-1 (their results are not stored)
     const u32x4* arow[MT];
     const uint8_t* asrow[MT];   // quantized activations: the row's scale bytes, group stride a_gs
+    const u32x4* arowq[MT];     // quantized activations loaded directly: the operand lane's code row
+    int crow[MT][2];            // quantized activations loaded by pairs: code rows 8j + lane/8 of the tile
     int64_t a_gs = 1;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int64_t m = min(m0 + 16 * t + (lane & 15), G.M - 1);
       if constexpr (AQ) {
-        arow[t] = reinterpret_cast<const u32x4*>(G.aq + m * (G.K >> 1));
         const ScaleWalk sw = act_scale_walk(G.a_layout, m, G.K >> 5, G.M);
         asrow[t] = G.as + sw.row_part;
         a_gs = sw.g_stride;
+        arowq[t] = reinterpret_cast<const u32x4*>(G.aq + m * (G.K >> 1));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) crow[t][j] = min(m0 + 16 * t + 8 * j + (lane >> 3), G.M - 1);
       } else {
         arow[t] = reinterpret_cast<const u32x4*>(G.a + m * G.lda);
       }
     }
-    constexpr int AV = AQ ? 1 : 4;   // 16-byte loads per operand: codes, or 32 bf16
+    // AQ == 2: quantized activation codes are loaded a pair of steps at a
+    // time: each load covers 8 rows x 128 consecutive bytes (lane L: row
+    // 8j + L/8, bytes 16 (L%8) .. +15 of the pair's run), one full cache line
+    // per row, where loading an operand directly (AQ == 1) reads 16 rows x 64
+    // bytes (16 half lines); the operand lanes then fetch their 16 bytes with
+    // ds_bpermute. From a few rows on the kernel is bound by vector L1
+    // accesses, and this halves the accesses for the codes; with one to four
+    // rows the direct loads hit the same lines anyway and skip the exchange.
+    // The pair's run starts at step pb (clamped so the run stays inside the
+    // row; dead steps read anything in it).
+    static_assert(AQ != 2 || SW % 2 == 0, "quantized activations load pairs of steps");
+    constexpr int AV = AQ ? 2 : 4;   // AQ 2: the pair's two loads (at step 2p); AQ 1: one; else 32 bf16
+    const int kq = G.K >> 5;          // 16-byte units of codes per row
     for (int s0 = s_lo; s0 < s_hi; s0 += SW) {
       u32x4 bw[SW][CT];
       uint32_t sb[SW][CT];
       u32x4 av[SW][MT][AV];
       uint32_t sab[SW][MT];
+      int pb[SW];
       // every load of the batch unconditionally (steps past the range re-read
       // the last one and are not used), so no use waits on a partial batch
 #pragma unroll
@@ -268,8 +291,17 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          if constexpr (AQ) {
-            av[i][t][0] = arow[t][kg];          // 16 bytes = 32 e2m1 codes
+          if constexpr (AQ == 1) {
+            av[i][t][0] = arowq[t][kg];          // 16 bytes = 32 e2m1 codes
+            sab[i][t] = asrow[t][kg * a_gs];
+          } else if constexpr (AQ == 2) {
+            if (i % 2 == 0) {
+              pb[i] = max(0, min(s0 + i, steps - 2));   // wave-uniform
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                av[i][t][j] = reinterpret_cast<const u32x4*>(G.aq)[(int64_t)crow[t][j] * kq +
+                                                                   min(pb[i] * 4 + (lane & 7), kq - 1)];
+            }
             sab[i][t] = asrow[t][kg * a_gs];
           } else {
 #pragma unroll
@@ -291,8 +323,21 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp4_kernel(const
         for (int t = 0; t < MT; ++t) {
           u32x4 q;
           uint32_t sa;
-          if constexpr (AQ) {
+          if constexpr (AQ == 1) {
             q = av[i][t][0];
+            sa = sab[i][t];
+          } else if constexpr (AQ == 2) {
+            // this step's 16 bytes for row r = lane%16, quarter kb: lane
+            // 8 (r%8) + 4 o + kb of the pair's load r/8, o the step's place in the run
+            const int i0 = i & ~1;
+            const int o = min(s0 + i - pb[i0], 1);
+            const int src = (((lane & 7) << 3) + o * 4 + kb) << 2;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const int lo = __builtin_amdgcn_ds_bpermute(src, (int)av[i0][t][0][d]);
+              const int hi = __builtin_amdgcn_ds_bpermute(src, (int)av[i0][t][1][d]);
+              q[d] = (uint32_t)((lane & 8) ? hi : lo);
+            }
             sa = sab[i][t];
           } else {
             sa = mx_group32(av[i][t], &q);

@@ -27,10 +27,10 @@ constexpr int aq_fp4_steps(int MT, int CT) { return CT == 1 ? (MT <= 2 ? 4 : 2) 
 // rows: 17.4 -> 18.6 us).
 int aq_fp4_col_tiles(int64_t M, int64_t N) { return M > 64 && (N / 16) % 2 == 0 ? 2 : 1; }
 
-template <bool SHUF, int MT, int CT>
+template <bool SHUF, int MT, int CT, int AQ = 2>
 void launch_aq_fp4(const rmsq::GemmArgs& G, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<MT, aq_fp4_steps(MT, CT), SHUF, false, CT, true>), grid, block, lds,
-                     s, G);
+  hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<MT, aq_fp4_steps(MT, CT), SHUF, false, CT, AQ>), grid, block, lds, s,
+                     G);
 }
 
 // The MXFP4 GEMM: grid x = groups of CT 16-column tiles of the output, y =
@@ -43,7 +43,10 @@ void launch_gemm(const rmsq::GemmArgs& G, int MT, int CT, bool small_m, bool aq,
   const size_t lds = rmsq::gemm_lds_bytes(MT, CT, waves);
   constexpr int SS = rmsq::kGemmSmallSteps;
   if (aq) {
-    switch (CT == 2 ? 0 : MT) {   // two column tiles come with four row tiles (aq_fp4_col_tiles)
+    // two column tiles come with four row tiles (aq_fp4_col_tiles); up to
+    // four rows the codes are loaded directly, else by pairs of steps
+    switch (CT == 2 ? 0 : G.M <= rmsq::kGemmSmallRows ? -1 : MT) {
+      case -1: launch_aq_fp4<SHUF, 1, 1, 1>(G, grid, block, lds, s); break;
       case 0: launch_aq_fp4<SHUF, 4, 2>(G, grid, block, lds, s); break;
       case 1: launch_aq_fp4<SHUF, 1, 1>(G, grid, block, lds, s); break;
       case 2: launch_aq_fp4<SHUF, 2, 1>(G, grid, block, lds, s); break;
@@ -53,18 +56,18 @@ void launch_gemm(const rmsq::GemmArgs& G, int MT, int CT, bool small_m, bool aq,
     return;
   }
   if (small_m && CT == 2) {
-    hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<1, SS, SHUF, true, 2, false>), grid, block, lds, s, G);
+    hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<1, SS, SHUF, true, 2, 0>), grid, block, lds, s, G);
     return;
   }
   if (small_m) {
-    hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<1, SS, SHUF, true, 1, false>), grid, block, lds, s, G);
+    hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<1, SS, SHUF, true, 1, 0>), grid, block, lds, s, G);
     return;
   }
   switch (MT) {
-    case 1: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<1, 4, SHUF, false, 1, false>), grid, block, lds, s, G); break;
-    case 2: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<2, 2, SHUF, false, 1, false>), grid, block, lds, s, G); break;
-    case 3: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<3, 1, SHUF, false, 1, false>), grid, block, lds, s, G); break;
-    default: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<4, 1, SHUF, false, 1, false>), grid, block, lds, s, G); break;
+    case 1: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<1, 4, SHUF, false, 1, 0>), grid, block, lds, s, G); break;
+    case 2: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<2, 2, SHUF, false, 1, 0>), grid, block, lds, s, G); break;
+    case 3: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<3, 1, SHUF, false, 1, 0>), grid, block, lds, s, G); break;
+    default: hipLaunchKernelGGL((rmsq::rmsq_gemm_fp4_kernel<4, 1, SHUF, false, 1, 0>), grid, block, lds, s, G); break;
   }
 }
 
@@ -177,7 +180,7 @@ rmsq_status run_gemm(const GemmActs& A, const void* w, const void* w_scale, int3
   const int SW = A.quantized ? aq_fp4_steps(MT, CT) : MT == 1 ? 4 : MT == 2 ? 2 : 1;
   // the waves' partial sums (1 KiB per row and column tile of each wave)
   // stay within 64 KiB of LDS
-  const int waves = std::min(64 / (MT * CT), small_m ? small_waves
+  const int waves = std::min(rmsq::gemm_max_waves(MT * CT), small_m ? small_waves
                                                          : std::min(rmsq::kGemmMaxWaves,
                                                                     std::max(1, (steps + SW - 1) / SW)));
   hipStream_t s = static_cast<hipStream_t>(stream);
