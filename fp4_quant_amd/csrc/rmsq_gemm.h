@@ -439,12 +439,13 @@ __device__ __forceinline__ v8i32 fp8_codes32(const u32x4 v[4], float sc) {
 // MT row tiles per workgroup, SW steps per batch, SHUF: preshuffled weights,
 // SMALLM: the small-M path of bf16 activations (MT == 1, SW ==
 // kGemmSmallSteps, M <= kGemmSmallRows, one batch per wave), AQ: the
-// activations arrive quantized.
+// activations arrive quantized (1: each operand loaded directly, 2: 8 rows x
+// 128 bytes per load, redistributed, as in the FP4 kernel).
 // Row blocks are 16 * MT rows (MT <= kGemm8MaxTiles: the activation
 // registers of more tiles would not fit beside the 32-byte operands).
 constexpr int kGemm8MaxTiles = 2;
 
-template <int MT, int SW, bool SHUF, bool SMALLM, bool AQ>
+template <int MT, int SW, bool SHUF, bool SMALLM, int AQ>
 __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const Gemm8Args G) {
   static_assert(MT <= kGemm8MaxTiles, "at most two row tiles");
   static_assert(!(AQ && SMALLM), "the small-M path quantizes bf16 activations");
@@ -535,11 +536,14 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const
     // lanes of rows past M read row M-1 (their results are not stored)
     const u32x4* arow[MT];
     const float* asrow[MT];   // quantized activations: the row's scales, block stride a_gs
+    int crow[MT][2];          // AQ == 2: code rows 8j + lane/8 of the tile
     int64_t a_gs = 1;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int64_t m = min(m0 + 16 * t + (lane & 15), G.M - 1);
-      if constexpr (AQ) {
+      if constexpr (AQ != 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) crow[t][j] = min(m0 + 16 * t + 8 * j + (lane >> 3), G.M - 1);
         arow[t] = reinterpret_cast<const u32x4*>(G.aq + m * G.K);
         const ScaleWalk sw = act_scale_walk(G.a_layout, m, G.K >> 7, G.M);
         asrow[t] = G.as + sw.row_part;
@@ -563,9 +567,15 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const
         sw[i] = wsrow[st];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          if constexpr (AQ) {
+          if constexpr (AQ == 1) {
             av[i][t][0] = arow[t][st * 8 + kb * 2];       // 32 e4m3fn codes
             av[i][t][1] = arow[t][st * 8 + kb * 2 + 1];
+            sav[i][t] = asrow[t][st * a_gs];
+          } else if constexpr (AQ == 2) {
+            // the step's 128 code bytes of rows 8j + lane/8: lane L holds bytes 16 (L%8) .. +15
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              av[i][t][j] = reinterpret_cast<const u32x4*>(G.aq)[(int64_t)crow[t][j] * (G.K >> 4) + st * 8 + (lane & 7)];
             sav[i][t] = asrow[t][st * a_gs];
           } else {
 #pragma unroll
@@ -583,10 +593,21 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const
         for (int t = 0; t < MT; ++t) {
           float sc;
           v8i32 aop;
-          if constexpr (AQ) {
+          if constexpr (AQ == 1) {
             sc = sav[i][t];
             aop = v8i32{(int)av[i][t][0][0], (int)av[i][t][0][1], (int)av[i][t][0][2], (int)av[i][t][0][3],
                         (int)av[i][t][1][0], (int)av[i][t][1][1], (int)av[i][t][1][2], (int)av[i][t][1][3]};
+          } else if constexpr (AQ == 2) {
+            // bytes 32 kb .. +31 of row r = lane%16: lanes 8 (r%8) + 2 kb and + 1 of load r/8
+            sc = sav[i][t];
+            const int src = (((lane & 7) << 3) + 2 * kb) << 2;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+              const int a = src + ((d >> 2) << 2);
+              const int lo = __builtin_amdgcn_ds_bpermute(a, (int)av[i][t][0][d & 3]);
+              const int hi = __builtin_amdgcn_ds_bpermute(a, (int)av[i][t][1][d & 3]);
+              aop[d] = (lane & 8) ? hi : lo;
+            }
           } else {
             // the row's 128-group spans the four lanes l%16 + 16q
             uint32_t am = max(max(amax8(av[i][t][0]), amax8(av[i][t][1])), max(amax8(av[i][t][2]), amax8(av[i][t][3])));

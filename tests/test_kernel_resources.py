@@ -93,8 +93,9 @@ def test_gemm_variants_fit_sixteen_waves(kernels):
     # variant and the one-tile variant loading operands directly) x 2 weight layouts
     assert len(gemm) == 24, sorted(gemm)
     gemm8 = {n: k for n, k in kernels.items() if "rmsq_gemm_fp8_kernel" in (n or "")}
-    # (1 or 2 row tiles + the small-M variant + 1 or 2 row tiles of quantized activations) x 2 weight layouts
-    assert len(gemm8) == 10, sorted(gemm8)
+    # (1 or 2 row tiles + the small-M variant; quantized activations: 1 or 2 row tiles
+    # loading 8 rows per load and the one-tile variant loading operands directly) x 2 weight layouts
+    assert len(gemm8) == 12, sorted(gemm8)
     gemm.update(gemm8)
     for n, k in gemm.items():
         # waves per workgroup: 16, or fewer when MT * CT accumulator tiles per wave
