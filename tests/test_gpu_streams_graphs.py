@@ -221,3 +221,70 @@ def test_graph_capture_of_the_prequant_gemms(fmt):
         for got, exp in zip([host(o) for o in outs], want[k % 2]):
             assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), f"replay {k}"
         _ = (a_in.float() * 2).sum().item()
+
+
+@pytest.mark.parametrize("fmt", [1, 0])
+def test_graph_capture_of_norm_quant_then_gemm(fmt):
+    """The fused residual + RMSNorm + group quant feeding the GEMM of its
+    quantized activations (32 rows: 32-row tiled MXFP4 scales, column-major
+    FP8 scales), captured in one HIP graph: every replay, with new inputs
+    copied in and eager work between replays, equals the eager result bit for
+    bit (output, residual, codes and scales)."""
+    say(f"HIP graph capture of norm + quant then GEMM (fmt {fmt})")
+    M, N, K = 32, 2112, 7168
+    lay = fq.SCALE_TILED32 if fmt == 1 else fq.SCALE_COL_MAJOR
+    g = inputs.make_gemm(M, N, K, seed=97) if fmt == 1 else inputs.make_gemm8(M, N, K, seed=97)
+    w, ws = dev(g["w"]), dev(g["ws"])
+    sw = torch.empty_like(w)
+    if fmt == 1:
+        sws = torch.empty_like(ws)
+        fq.mxfp4_weight_preshuffle(w, ws, N, K, sw, sws)
+    else:
+        sws = ws
+        fq.fp8_weight_preshuffle(w, N, K, sw)
+    srcs = [inputs.make_problem(M, K, seed_x=s, residual=True) for s in (98, 99)]
+    x, r = dev(srcs[0]["x"]), dev(srcs[0]["residual"])
+    gam = dev(srcs[0]["gamma"])
+    ro = torch.empty_like(r)
+    q, sc, _ = fq.alloc_outputs(M, K, fmt, lay)
+    out = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    probs = fq.problem_array([fq.make_problem(x, gam, 1e-6, q, sc, residual_in=r, residual_out=ro, fmt=fmt,
+                                              scale_layout=lay)])
+    gemm = fq.gemm_afp4wfp4 if fmt == 1 else fq.gemm_a8w8_blockscale
+
+    def launch(stream=None):
+        st = stream.cuda_stream if stream is not None else None
+        fq.rmsnorm_quant_group_multi(probs, st)
+        gemm(q, sc, lay, sw, sws, fq.W_PRESHUFFLED, M, N, K, out, N, st)
+
+    def load(k):
+        x.copy_(dev(srcs[k]["x"]))
+        r.copy_(dev(srcs[k]["residual"]))
+
+    def snap():
+        return [host(t).copy() for t in (out, ro, q, sc)]
+
+    want = []
+    for k in range(2):
+        load(k)
+        launch()
+        torch.cuda.synchronize()
+        want.append(snap())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        launch(s)
+    for k in range(6):
+        load(k % 2)
+        for t in (out, ro, q, sc):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip(snap(), want[k % 2]):
+            assert np.array_equal(got.view(np.uint8), exp.view(np.uint8)), f"replay {k}"
+        _ = (x.float() * 2).sum().item()
