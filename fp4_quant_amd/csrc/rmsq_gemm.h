@@ -41,8 +41,10 @@
 // overlap), and the operand lanes fetch the codes with ds_bpermute; no
 // workgroup barrier precedes the matrix-core steps. Otherwise each wave loads
 // and quantizes the 32-groups of its own operands. Quantized activations: each
-// lane loads its operand's 16 code bytes and its group's scale byte. Lanes of
-// rows past M read row M-1; their results are not stored. All loads of a
+// lane loads its group's scale byte, and the codes come either straight into
+// the operand lanes (up to 4 rows) or 8 rows x 128 bytes per load and then
+// across lanes (more rows; the kernel is bound by vector L1 accesses there).
+// Lanes of rows past M read row M-1; their results are not stored. All loads of a
 // batch are unconditional: a load under a branch would make the first use of
 // any later load wait for it.
 #pragma once
