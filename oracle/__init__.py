@@ -62,9 +62,6 @@ def _bind(L):
         f = getattr(L, name)
         f.restype = C.c_int
         f.argtypes = [_p, _p, _i32, _p, _p, _i64, _i64, _i64, _p, _i64]
-    L.oracle_rmsnorm_gemm_a16wfp4.restype = C.c_int
-    L.oracle_rmsnorm_gemm_a16wfp4.argtypes = [_p, _i64, _p, _i64, _p, C.c_float, _i64, _i64, _p, _p, _i64, _p, _i64,
-                                              _p]
     L.oracle_num_threads.restype = C.c_int
     L.oracle_num_threads.argtypes = []
     return L
@@ -261,25 +258,6 @@ class Oracle:
             raise ValueError("oracle: arguments outside the defined operation")
         return out
 
-    def rmsnorm_gemm_a16wfp4(self, x, gamma, eps, w, w_scale, residual=None):
-        """Residual add + RMSNorm of the bf16 rows x [M, K] (uint16 bits), then
-        the A16WFP4 prequant GEMM of the normalized rows with w [N, K/2],
-        w_scale [N, K/32]. Returns (C [M, N] float64, residual_out or None)."""
-        x = np.ascontiguousarray(x, dtype=np.uint16)
-        M, K = x.shape
-        N = w.shape[0]
-        assert w.shape == (N, K // 2) and w_scale.shape == (N, K // 32)
-        r = None if residual is None else np.ascontiguousarray(residual, dtype=np.uint16)
-        h = None if r is None else np.zeros((M, K), np.uint16)
-        out = np.zeros((M, N), np.float64)
-        rc = self._L.oracle_rmsnorm_gemm_a16wfp4(_ptr(x), K, _ptr(r), K, _ptr(np.ascontiguousarray(gamma)), float(eps),
-                                                 M, K, _ptr(np.ascontiguousarray(w, dtype=np.uint8)),
-                                                 _ptr(np.ascontiguousarray(w_scale, dtype=np.uint8)), N, _ptr(out), N,
-                                                 _ptr(h))
-        if rc != 0:
-            raise ValueError("oracle: arguments outside the defined operation")
-        return out, h
-
     def group_quant(self, yb, group=128, fmt=FMT_FP8, scale_layout=LAYOUT_ROW, scale_fill=0):
         """Stage 2 alone on bf16 rows: returns (q, scale)."""
         yb = np.ascontiguousarray(yb, dtype=np.uint16)
@@ -359,10 +337,6 @@ def gemm_afp4wfp4(*a, **k):
 
 def gemm_a8w8_blockscale(*a, **k):
     return default().gemm_a8w8_blockscale(*a, **k)
-
-
-def rmsnorm_gemm_a16wfp4(*a, **k):
-    return default().rmsnorm_gemm_a16wfp4(*a, **k)
 
 
 def group_quant(*a, **k):

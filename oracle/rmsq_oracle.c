@@ -569,27 +569,6 @@ int oracle_gemm_a8w8_blockscale(const uint8_t* a_q, const float* a_scale, int32_
     return 0;
 }
 
-/*
- * Residual add + RMSNorm then the A16WFP4 prequant GEMM, as one operation
- * (the concurrency-4 step of [ATT, run notes]: the norm, then the GEMM that
- * quantizes its activations). READING: the GEMM multiplies exactly the bf16
- * rows the norm produces (stage 1 above), K being the row length.
- */
-int oracle_rmsnorm_gemm_a16wfp4(const uint16_t* x, int64_t ldx,
-                                const uint16_t* residual, int64_t ldr,
-                                const uint16_t* gamma, float eps, int64_t M, int64_t K,
-                                const uint8_t* w, const uint8_t* w_scale, int64_t N,
-                                double* out, int64_t ldc, uint16_t* h_out)
-{
-    if (M < 0 || K <= 0 || K % 32 != 0)
-        return -1;
-    uint16_t* yb = (uint16_t*)malloc((size_t)(M > 0 ? M : 1) * (size_t)K * sizeof(uint16_t));
-    oracle_add_rmsnorm(x, ldx, residual, ldr, gamma, eps, M, K, h_out, ldr, yb, K);
-    const int rc = oracle_gemm_a16wfp4_prequant(yb, K, w, w_scale, M, N, K, out, ldc);
-    free(yb);
-    return rc;
-}
-
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -100,15 +100,6 @@ int oracle_gemm_a8w8_blockscale(const uint8_t* a_q, const float* a_scale, int32_
                                 const uint8_t* w, const float* w_scale,
                                 int64_t M, int64_t N, int64_t K, double* out, int64_t ldc);
 
-/* Residual add + RMSNorm (oracle_add_rmsnorm; residual and h_out may be
- * NULL, h_out has row stride ldr) then the A16WFP4 prequant GEMM of the bf16
- * normalized rows (K = row length). Returns as the prequant GEMM does. */
-int oracle_rmsnorm_gemm_a16wfp4(const uint16_t* x, int64_t ldx,
-                                const uint16_t* residual, int64_t ldr,
-                                const uint16_t* gamma, float eps, int64_t M, int64_t K,
-                                const uint8_t* w, const uint8_t* w_scale, int64_t N,
-                                double* out, int64_t ldc, uint16_t* h_out);
-
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

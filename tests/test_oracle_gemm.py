@@ -287,27 +287,3 @@ def test_quantized_activation_gemms_reject_undefined_arguments(orc):
                                  np.ones((1, 1), np.float32), scale_layout=1)
     assert orc.gemm_afp4wfp4(np.zeros((0, 32), np.uint8), np.zeros((0, 2), np.uint8), np.zeros((3, 32), np.uint8),
                              np.zeros((3, 2), np.uint8)).shape == (0, 3)
-
-
-# --------------------------------------------- norm + prequant GEMM, composed --
-def test_rmsnorm_gemm_is_the_norm_then_the_prequant_gemm(orc):
-    p = inputs.make_problem(3, 512, seed_x=60, residual=True, outliers=True)
-    w, ws = random_weights(24, 512, 61)
-    got, h = orc.rmsnorm_gemm_a16wfp4(p["x"], p["gamma"], p["eps"], w, ws, residual=p["residual"])
-    h_want, yb = orc.add_rmsnorm(p["x"], p["gamma"], p["eps"], residual=p["residual"])
-    assert np.array_equal(h, h_want)
-    assert np.array_equal(got, orc.gemm_a16wfp4_prequant(yb, w, ws))
-
-
-@pytest.mark.parametrize("k", [-9, 0, 5])
-def test_rmsnorm_gemm_of_constant_rows_is_the_gemm_of_gamma(orc, k):
-    """With eps = 0 a row of one repeated positive value c normalizes to gamma
-    exactly (h / sqrt(mean h^2) = 1), whatever c = 2^k * 1.5 is, so the
-    output is the prequant GEMM of gamma itself."""
-    K = 256
-    gamma = inputs.gamma_vec(K, 62)
-    x = np.full((2, K), inputs.to_bf16_bits(np.float32(1.5 * 2.0 ** k)), np.uint16)
-    w, ws = random_weights(8, K, 63)
-    got, _ = orc.rmsnorm_gemm_a16wfp4(x, gamma, 0.0, w, ws)
-    want = orc.gemm_a16wfp4_prequant(np.stack([gamma, gamma]), w, ws)
-    assert np.array_equal(got, want)
