@@ -246,6 +246,7 @@ __global__ void __launch_bounds__(64 * gemm_max_waves(MT * CT)) rmsq_gemm_fp4_ke
     const uint8_t* asrow[MT];   // quantized activations: the row's scale bytes, group stride a_gs
     const u32x4* arowq[MT];     // quantized activations loaded directly: the operand lane's code row
     int crow[MT][2];            // quantized activations loaded by pairs: code rows 8j + lane/8 of the tile
+    const uint16_t* ablk = AQ ? nullptr : G.a + (int64_t)m0 * G.lda;   // bf16 activations: the block's first row
     int64_t a_gs = 1;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -258,7 +259,7 @@ __global__ void __launch_bounds__(64 * gemm_max_waves(MT * CT)) rmsq_gemm_fp4_ke
 #pragma unroll
         for (int j = 0; j < 2; ++j) crow[t][j] = min(m0 + 16 * t + 8 * j + (lane >> 3), G.M - 1);
       } else {
-        arow[t] = reinterpret_cast<const u32x4*>(G.a + m * G.lda);
+        (void)m;   // bf16 rows: 4 rows x 256 bytes per load from ablk, addressed in the batch below
       }
     }
     // AQ == 2: quantized activation codes are loaded a pair of steps at a
@@ -307,7 +308,13 @@ __global__ void __launch_bounds__(64 * gemm_max_waves(MT * CT)) rmsq_gemm_fp4_ke
             sab[i][t] = asrow[t][kg * a_gs];
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) av[i][t][j] = arow[t][kg * 4 + j];   // 64 bytes = 32 bf16
+            for (int j = 0; j < 4; ++j) {
+              // 32-bit offsets from the row block's first row (at most 64 rows,
+              // lda <= 2^25), so each address is one register beside a scalar base
+              const uint32_t row = (uint32_t)(min(m0 + 16 * t + 4 * j + (lane >> 4), G.M - 1) - m0);
+              const uint32_t off = row * (uint32_t)G.lda + (uint32_t)(st * 128 + (lane & 15) * 8);
+              av[i][t][j] = *reinterpret_cast<const u32x4*>(ablk + off);
+            }
           }
         }
       }
@@ -342,7 +349,36 @@ __global__ void __launch_bounds__(64 * gemm_max_waves(MT * CT)) rmsq_gemm_fp4_ke
             }
             sa = sab[i][t];
           } else {
-            sa = mx_group32(av[i][t], &q);
+            // Each lane quantizes its 8 elements of each load (the lane quad
+            // of a 32-group shares the amax by DPP), then the operand lane of
+            // row r, quarter kb fetches its 4 code dwords and scale byte
+            // from lanes 16 (r%4) + 4 kb + d of load r/4.
+            uint32_t code[4], byte[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              byte[j] = mx_scale_byte(max4(amax8(av[i][t][j])));
+              code[j] = fp4_codes8(av[i][t][j], byte[j]);
+            }
+            const int src = (((lane & 3) << 4) + (kb << 2)) << 2;
+            const int jr = (lane >> 2) & 3;   // load of this operand lane's row
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              int v = 0;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int x = __builtin_amdgcn_ds_bpermute(src + (d << 2), (int)code[j]);
+                v = jr == j ? x : v;
+              }
+              q[d] = (uint32_t)v;
+            }
+            sa = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int x = __builtin_amdgcn_ds_bpermute(src, (int)byte[j]);
+              sa = jr == j ? (uint32_t)x : sa;
+            }
+            // one tile at a time: interleaving the tiles' exchanges needs more registers than 16 waves leave
+            __builtin_amdgcn_sched_barrier(0);
           }
           if (!live) q = u32x4{0u, 0u, 0u, 0u};
           const v8i32 aop = {(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};

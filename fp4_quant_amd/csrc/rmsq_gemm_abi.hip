@@ -105,8 +105,9 @@ struct GemmActs {
 
 rmsq_status check_gemm_acts(const GemmActs& A, int32_t fmt, int64_t M, int64_t K, Range* rs, int* nr) {
   if (!A.quantized) {
-    if (A.lda < K || A.lda % 8)
-      return fail(RMSQ_ERR_INVALID_ARG, "gemm: need lda >= K with lda %% 8 == 0 (lda=%lld)", (long long)A.lda);
+    if (A.lda < K || A.lda % 8 || A.lda > RMSQ_GEMM_LDA_MAX)
+      return fail(RMSQ_ERR_INVALID_ARG, "gemm: need K <= lda <= %d with lda %% 8 == 0 (lda=%lld)", RMSQ_GEMM_LDA_MAX,
+                  (long long)A.lda);
     if (M == 0) return RMSQ_OK;
     if (!A.a) return fail(RMSQ_ERR_INVALID_ARG, "gemm: NULL buffer");
     if (!aligned(A.a, 16)) return fail(RMSQ_ERR_INVALID_ARG, "gemm: a must be 16-byte aligned");

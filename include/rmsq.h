@@ -85,6 +85,7 @@ typedef int32_t rmsq_status;
 #define RMSQ_N_MAX 32768
 #define RMSQ_GEMM_N_MAX (1 << 20)
 #define RMSQ_GEMM_K_MAX (1 << 20)
+#define RMSQ_GEMM_LDA_MAX (1 << 25)   /* row stride of the prequant GEMMs' bf16 activations, elements */
 
 /* Weight layouts of gemm_a16wfp4_prequant (this library's; the page names a
  * preshuffled-weight GEMM without giving its layout).
@@ -198,8 +199,8 @@ rmsq_status dynamic_per_group_scaled_quant(const void* x, int64_t M, int64_t N, 
  * the matrix cores in an order fixed for a given shape (so results repeat
  * bit for bit).
  *
- *  a        [M, K] bf16, row stride lda elements (lda >= K, lda % 8 == 0),
- *           16-byte aligned, read only; finite values.
+ *  a        [M, K] bf16, row stride lda elements (K <= lda <= RMSQ_GEMM_LDA_MAX,
+ *           lda % 8 == 0), 16-byte aligned, read only; finite values.
  *  w        e2m1 codes, N * K/2 bytes in layout w_layout, 16-byte aligned.
  *  w_scale  e8m0 bytes (scale 2^(byte - 127)), N * K/32 bytes in layout
  *           w_layout; byte 255 is not a number and gives unspecified results.
@@ -240,8 +241,8 @@ rmsq_status mxfp4_weight_preshuffle(const void* w, const void* w_scale, int64_t 
  * and is scaled by the two scales and accumulated in fp32, in an order fixed
  * for a given shape.
  *
- *  a        [M, K] bf16, row stride lda elements (lda >= K, lda % 8 == 0),
- *           16-byte aligned, read only; finite values.
+ *  a        [M, K] bf16, row stride lda elements (K <= lda <= RMSQ_GEMM_LDA_MAX,
+ *           lda % 8 == 0), 16-byte aligned, read only; finite values.
  *  w        e4m3fn codes, N * K bytes in layout w_layout (RMSQ_W_ROW_MAJOR:
  *           [N, K]; RMSQ_W_PRESHUFFLED: made by fp8_weight_preshuffle),
  *           16-byte aligned; no NaN codes (0x7F, 0xFF).

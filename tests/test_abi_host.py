@@ -269,6 +269,7 @@ def test_gemm_validates():
     assert g(M=-1) == E
     assert g(lda=128) == E               # lda < K
     assert g(lda=260) == E               # lda % 8
+    assert g(lda=(1 << 25) + 8) == E     # lda beyond RMSQ_GEMM_LDA_MAX
     assert g(ldc=16) == E                # ldc < N
     assert g(lay=2) == E                 # unknown weight layout
     assert g(a=A + 2) == E               # a alignment
