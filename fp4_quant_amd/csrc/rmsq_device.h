@@ -167,9 +167,23 @@ __device__ __forceinline__ float fp8_scale(uint32_t amax_bits) {
 // and the nearest-even products v*r_lo and v*r_hi bracket v/s. Rounding to
 // e4m3fn is monotone, so where both brackets give the same code that code is
 // the rounding of v/s (also across the e4m3fn subnormal range); four codes
-// are compared at once as a packed dword. Elsewhere - quotients within a few
-// ulp of a rounding midpoint, exact ties - and in groups whose scale is too
-// small for a normal reciprocal, the exact path decides.
+// are compared at once as a packed dword. Where they differ - quotients
+// within a few ulp of a rounding midpoint, exact ties - the two codes are
+// neighbours (the brackets are 8 fp32 ulp apart, e4m3fn codes at least 2^-4
+// relative), and v/s is compared with the boundary B between them: B has few
+// significant bits (1.ffff1 x 2^E in the normal range, (k + 1/2) 2^-9 in the
+// subnormal one: min(4, E + 10) fraction bits at its exponent E), and |x_hi|
+// exceeds it by less than the next such bit, so clearing |x_hi|'s lower
+// fraction bits gives B exactly; fma(B, s, -|v|) rounds once, so its sign is
+// that of B s - |v| and it is zero only at an exact tie (for s >= 2^-100 the
+// difference is a multiple of 2^-140, representable), which takes the code
+// with the even mantissa. With bf16 inputs this is not rare - exact ties come
+// with every group whose amax mantissa is a multiple of 7 - so it is one
+// straight block over the 8 elements, no per-element branch (STRAIGHT; the
+// long-row kernels, short of registers, decide each such element on the
+// double-precision path instead, under its own branch). Groups whose scale
+// is too small for a normal reciprocal take the double-precision path.
+template <bool STRAIGHT = true>
 __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
   const uint32_t rb = __float_as_uint(__builtin_amdgcn_rcpf(s));
   const float r_lo = __uint_as_float(rb - 4u), r_hi = __uint_as_float(rb + 4u);
@@ -185,14 +199,30 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
   qh[0] = cvt_fp8x2<true>(hi[2], hi[3], cvt_fp8x2<false>(hi[0], hi[1], 0u));
   qh[1] = cvt_fp8x2<true>(hi[6], hi[7], cvt_fp8x2<false>(hi[4], hi[5], 0u));
   const bool tiny = s < 0x1p-100f;
-  if (__builtin_expect(tiny | (qw[0] != qh[0]) | (qw[1] != qh[1]), 0)) {
+  if (!STRAIGHT || __builtin_expect(tiny, 0)) {
+    if (__builtin_expect(tiny | (qw[0] != qh[0]) | (qw[1] != qh[1]), 0)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 3) * 8;
+        if (tiny | ((((qw[e >> 2] ^ qh[e >> 2]) >> sh) & 0xFFu) != 0u)) {
+          const uint32_t b = fp8_exact(v[e], s);
+          qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
+        }
+      }
+    }
+  } else if (__builtin_expect((qw[0] != qh[0]) | (qw[1] != qh[1]), 0)) {
+    // one straight block for all 8 elements: where the brackets' codes c_lo,
+    // c_hi differ (neighbours), decide against the boundary between them
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int sh = (e & 3) * 8;
-      if (tiny | ((((qw[e >> 2] ^ qh[e >> 2]) >> sh) & 0xFFu) != 0u)) {
-        const uint32_t b = fp8_exact(v[e], s);
-        qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
-      }
+      const uint32_t c_lo = (qw[e >> 2] >> sh) & 0xFFu, c_hi = (qh[e >> 2] >> sh) & 0xFFu;
+      const uint32_t xb = __float_as_uint(hi[e]) & 0x7FFFFFFFu;
+      const int keep = max(0, min(4, (int)(xb >> 23) - 117));
+      const float B = __uint_as_float(xb & ~((1u << (23 - keep)) - 1u));
+      const float t = __builtin_fmaf(B, s, -__builtin_fabsf(v[e]));
+      const uint32_t b = (c_lo == c_hi) ? c_lo : t < 0.0f ? c_hi : t > 0.0f ? c_lo : ((c_lo & 1u) ? c_hi : c_lo);
+      qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
     }
   }
   return qw;

@@ -312,14 +312,18 @@ def test_rcp_within_one_ulp_for_every_scale():
         assert abs(Fraction(rv) - exact) <= Fraction(uv) - Fraction(rv), sv
 
 
-def test_fp8_codes8_every_value_amax_pair(orc):
-    say(f"fp8_codes8 exhaustive pairs (stride {STRIDE})")
+@pytest.mark.parametrize("probe", ["probe_fp8_codes", "probe_fp8_codes_per_element"])
+def test_fp8_codes8_every_value_amax_pair(orc, probe):
+    """Both forms of the exact fallback: one straight block per 8 elements
+    (the short-row kernels and the GEMMs) and per-element fp64 decisions
+    (the long-row kernels)."""
+    say(f"fp8_codes8 exhaustive pairs (stride {STRIDE}, {probe})")
     total = 0
     for amaxes, owner, v in _pair_batches():
         s = (_f32(amaxes.astype(np.uint16)) / np.float32(448.0))[owner]
         vf = _f32(v)
         out = torch.empty(v.size, dtype=torch.uint8, device="cuda")
-        call_probe("probe_fp8_codes", dev(vf), dev(s), out, n=v.size // 8)
+        call_probe(probe, dev(vf), dev(s), out, n=v.size // 8)
         q = vf.astype(np.float64) / np.repeat(s.astype(np.float64), 8)
         want = np.empty(v.size, np.uint8)
         _threaded(orc.e4m3fn_encode, q, want)
