@@ -178,12 +178,29 @@ __device__ __forceinline__ float fp8_scale(uint32_t amax_bits) {
 // that of B s - |v| and it is zero only at an exact tie (for s >= 2^-100 the
 // difference is a multiple of 2^-140, representable), which takes the code
 // with the even mantissa. With bf16 inputs this is not rare - exact ties come
-// with every group whose amax mantissa is a multiple of 7 - so it is one
-// straight block over the 8 elements, no per-element branch (STRAIGHT; the
-// long-row kernels, short of registers, decide each such element on the
-// double-precision path instead, under its own branch). Groups whose scale
-// is too small for a normal reciprocal take the double-precision path.
-template <bool STRAIGHT = true>
+// with every group whose amax mantissa is a multiple of 7 - so it must not
+// cost a branch per element. MODE picks the form (each measured best where
+// it is used): kFp8Straight, one straight block over the 8 elements (the
+// fused kernel's short rows); kFp8Rounds, one differing element per lane per
+// round, the wave looping while any lane has one left (the GEMMs, where each
+// lane encodes 32 elements); kFp8PerElement, each differing element on the
+// double-precision path under its own branch (the long-row kernels, short of
+// registers). Groups whose scale is too small for a normal reciprocal take
+// the double-precision path.
+enum Fp8Fix { kFp8PerElement = 0, kFp8Straight = 1, kFp8Rounds = 2 };
+
+// The rounding boundary between the neighbouring codes of x_hi's bracket and
+// the decision against it: 1 when v/s lies above the boundary or on it with
+// c_lo odd (then the code is c_lo + 1), else 0.
+__device__ __forceinline__ uint32_t fp8_round_up(float v, float x_hi, float s, uint32_t c_lo) {
+  const uint32_t xb = __float_as_uint(x_hi) & 0x7FFFFFFFu;
+  const int keep = max(0, min(4, (int)(xb >> 23) - 117));
+  const float B = __uint_as_float(xb & ~((1u << (23 - keep)) - 1u));
+  const float t = __builtin_fmaf(B, s, -__builtin_fabsf(v));
+  return (uint32_t)(t < 0.0f) | ((uint32_t)(t == 0.0f) & (c_lo & 1u));
+}
+
+template <int MODE = kFp8Straight>
 __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
   const uint32_t rb = __float_as_uint(__builtin_amdgcn_rcpf(s));
   const float r_lo = __uint_as_float(rb - 4u), r_hi = __uint_as_float(rb + 4u);
@@ -199,7 +216,7 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
   qh[0] = cvt_fp8x2<true>(hi[2], hi[3], cvt_fp8x2<false>(hi[0], hi[1], 0u));
   qh[1] = cvt_fp8x2<true>(hi[6], hi[7], cvt_fp8x2<false>(hi[4], hi[5], 0u));
   const bool tiny = s < 0x1p-100f;
-  if (!STRAIGHT || __builtin_expect(tiny, 0)) {
+  if (MODE == kFp8PerElement || __builtin_expect(tiny, 0)) {
     if (__builtin_expect(tiny | (qw[0] != qh[0]) | (qw[1] != qh[1]), 0)) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -211,18 +228,35 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
       }
     }
   } else if (__builtin_expect((qw[0] != qh[0]) | (qw[1] != qh[1]), 0)) {
-    // one straight block for all 8 elements: where the brackets' codes c_lo,
-    // c_hi differ (neighbours), decide against the boundary between them
+    // c_hi = c_lo + 1 where the codes differ (neighbours of one sign, no carry)
+    if constexpr (MODE == kFp8Straight) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 3) * 8;
-      const uint32_t c_lo = (qw[e >> 2] >> sh) & 0xFFu, c_hi = (qh[e >> 2] >> sh) & 0xFFu;
-      const uint32_t xb = __float_as_uint(hi[e]) & 0x7FFFFFFFu;
-      const int keep = max(0, min(4, (int)(xb >> 23) - 117));
-      const float B = __uint_as_float(xb & ~((1u << (23 - keep)) - 1u));
-      const float t = __builtin_fmaf(B, s, -__builtin_fabsf(v[e]));
-      const uint32_t b = (c_lo == c_hi) ? c_lo : t < 0.0f ? c_hi : t > 0.0f ? c_lo : ((c_lo & 1u) ? c_hi : c_lo);
-      qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 3) * 8;
+        const uint32_t c_lo = (qw[e >> 2] >> sh) & 0xFFu, c_hi = (qh[e >> 2] >> sh) & 0xFFu;
+        qw[e >> 2] += ((c_lo != c_hi) ? fp8_round_up(v[e], hi[e], s, c_lo) : 0u) << sh;
+      }
+    } else {
+      uint32_t dm = 0;   // elements whose bracket codes differ
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        dm |= (uint32_t)((((qw[e >> 2] ^ qh[e >> 2]) >> ((e & 3) * 8)) & 0xFFu) != 0u) << e;
+      while (__any(dm != 0u)) {   // at most 8 rounds: each clears a bit of every lane that has one
+        if (dm != 0u) {
+          const int e = __builtin_ctz(dm);
+          dm &= dm - 1u;
+          float ve = v[0], he = hi[0];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) {
+            ve = e == k ? v[k] : ve;
+            he = e == k ? hi[k] : he;
+          }
+          const int sh = (e & 3) * 8;
+          const uint32_t up = fp8_round_up(ve, he, s, ((e < 4 ? qw[0] : qw[1]) >> sh) & 0xFFu);
+          if (e < 4) qw[0] += up << sh;
+          else qw[1] += up << sh;
+        }
+      }
     }
   }
   return qw;

@@ -467,7 +467,7 @@ __device__ __forceinline__ v8i32 fp8_codes32(const u32x4 v[4], float sc) {
   for (int i = 0; i < 4; ++i) {
     float f[8];
     unpack_bf16x8(v[i], f);
-    const u32x2 c = fp8_codes8(f, sc);
+    const u32x2 c = fp8_codes8<kFp8Rounds>(f, sc);
     q[2 * i] = (int)c[0];
     q[2 * i + 1] = (int)c[1];
   }

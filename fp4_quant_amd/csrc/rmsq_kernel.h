@@ -256,7 +256,7 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
         v[2 * i + 1] = bf16_hi(yw[i]);
       }
       const float sc = fp8_scale(max16(am));
-      const u32x2 qw = fp8_codes8<kShort>(v, sc);
+      const u32x2 qw = fp8_codes8<kShort ? kFp8Straight : kFp8PerElement>(v, sc);
       u32x2* qrow = reinterpret_cast<u32x2*>(P.q + m * (int64_t)P.N);
       __builtin_nontemporal_store(qw, qrow + c);
       if ((tid & 15) == 0) {

@@ -312,11 +312,11 @@ def test_rcp_within_one_ulp_for_every_scale():
         assert abs(Fraction(rv) - exact) <= Fraction(uv) - Fraction(rv), sv
 
 
-@pytest.mark.parametrize("probe", ["probe_fp8_codes", "probe_fp8_codes_per_element"])
+@pytest.mark.parametrize("probe", ["probe_fp8_codes", "probe_fp8_codes_per_element", "probe_fp8_codes_rounds"])
 def test_fp8_codes8_every_value_amax_pair(orc, probe):
-    """Both forms of the exact fallback: one straight block per 8 elements
-    (the short-row kernels and the GEMMs) and per-element fp64 decisions
-    (the long-row kernels)."""
+    """Every form of the exact fallback: one straight block per 8 elements
+    (the short-row kernels), per-element fp64 decisions (the long-row
+    kernels) and one element per round (the GEMMs)."""
     say(f"fp8_codes8 exhaustive pairs (stride {STRIDE}, {probe})")
     total = 0
     for amaxes, owner, v in _pair_batches():
