@@ -156,17 +156,18 @@ rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Mode mod
 // pays the per-wave fixed cost of the norm (reduction, fp64 inverse square
 // root) too often. Rule: the first J of 2, 3, 4, 1 whose W stays <= 8 with
 // at most 20% idle lanes (7168 -> J 2 x 7 waves, 1536 -> J 3 x 1 wave);
-// then relax the wave limit, then take anything that fits. With no more
-// rows than compute units each row has a CU to itself and only its latency
-// counts: there the most waves win (J 1 x 14 waves for 64 rows of 7168:
-// 6.3 us against 6.8 us for J 2 x 7; at 512 rows J 2 x 7 is faster again).
+// then relax the wave limit, then take anything that fits. With at most two
+// rows per compute unit each row's latency counts most: there the most waves
+// win (J 1 x 14 waves for 64 rows of 7168: 6.3 us against 6.8 us for J 2 x 7;
+// 512 rows 8.42 against 8.63 us; from 768 rows J 2 x 7 is faster again:
+// 10.9 against 12.4 us).
 constexpr int kJs[] = {2, 3, 4, 1, 7, 8, 14};
 constexpr int kJsFewRows[] = {1, 2, 3, 4, 7, 8, 14};
 constexpr int kWaveRowsPerBlock = 4;
 constexpr int kMaxSplits = 8;
 
 void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
-  const bool few = rows <= kComputeUnits;
+  const bool few = rows <= 2 * kComputeUnits;
   for (int pass = 0; pass < 3; ++pass) {
     for (int k = 0; k < 7; ++k) {
       const int J = few ? kJsFewRows[k] : kJs[k];

@@ -225,8 +225,9 @@ def test_launch_shape_always_fits():
             assert J in (1, 2, 3, 4, 7, 8, 14) and 1 <= W <= (4 if J >= 7 else 16), (N, rows, J, W)
             assert J * W * 64 >= C_, (N, rows, J, W)
     assert fq.rmsq_query_shape(7168, 8192) == (2, 7)
-    assert fq.rmsq_query_shape(7168, 512) == (2, 7)
-    assert fq.rmsq_query_shape(7168, 64) == (1, 14)     # one row per CU: most waves
+    assert fq.rmsq_query_shape(7168, 768) == (2, 7)
+    assert fq.rmsq_query_shape(7168, 512) == (1, 14)    # at most two rows per CU: most waves
+    assert fq.rmsq_query_shape(7168, 64) == (1, 14)
     assert fq.rmsq_query_shape(1536, 8192) == (3, 1)
     with pytest.raises(fq.RmsqError):
         fq.rmsq_query_shape(32776, 1)
