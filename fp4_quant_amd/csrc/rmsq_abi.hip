@@ -215,23 +215,36 @@ void launch_res(const rmsq::Launch& L, int J, int R, const dim3 grid, const dim3
   }
 }
 
-// One launch of up to four problems; they either all have a residual or
-// none has (the caller splits a mixed set). R > 1: W is 1 and R rows share a
-// workgroup, one per wave.
+// One launch of up to four problems with the shape chosen for it; they
+// either all have a residual or none has (the caller splits a mixed set).
+// R > 1: W is 1 and R rows share a workgroup, one per wave.
+struct Plan {
+  rmsq::Launch L;
+  int J, W, R;
+  dim3 grid, block;
+};
+
+// The launch's grid: one workgroup per row (R > 1: per R rows; with row
+// splits, per split of a row, the rows padded to a multiple of 8).
+void plan_grid(Plan& P) {
+  const rmsq::Launch& L = P.L;
+  const int64_t padded = (L.rows + 7) / 8 * 8;
+  const int64_t blocks = P.R > 1 ? (L.rows + P.R - 1) / P.R : L.splits_log2 > 0 ? padded << L.splits_log2 : L.rows;
+  P.grid = dim3((unsigned)blocks);
+  P.block = dim3((unsigned)(64 * (P.R > 1 ? P.R : P.W)));
+}
+
 template <int FMT>
-rmsq_status launch_fmt(const rmsq::Launch& L, int J, int W, int R, hipStream_t stream) {
-  const unsigned padded = (unsigned)((L.rows + 7) / 8 * 8);   // row splits pad the rows to a multiple of 8
-  const dim3 grid(R > 1 ? (unsigned)((L.rows + R - 1) / R)
-                        : L.splits_log2 > 0 ? padded << L.splits_log2 : (unsigned)L.rows);
-  const dim3 block((unsigned)(64 * (R > 1 ? R : W)));
+rmsq_status launch_fmt(const Plan& P, hipStream_t stream) {
+  const rmsq::Launch& L = P.L;
   bool exact = L.splits_log2 == 0;   // every row exactly fills its J*64*W (or J*64, packed) lanes
-  for (int i = 0; i < L.count; ++i) exact &= (L.p[i].N >> 3) == J * 64 * (R > 1 ? 1 : W);
+  for (int i = 0; i < L.count; ++i) exact &= (L.p[i].N >> 3) == P.J * 64 * (P.R > 1 ? 1 : P.W);
   if (L.p[0].r) {
-    if (exact) launch_res<FMT, true, true>(L, J, R, grid, block, stream);
-    else launch_res<FMT, true, false>(L, J, R, grid, block, stream);
+    if (exact) launch_res<FMT, true, true>(L, P.J, P.R, P.grid, P.block, stream);
+    else launch_res<FMT, true, false>(L, P.J, P.R, P.grid, P.block, stream);
   } else {
-    if (exact) launch_res<FMT, false, true>(L, J, R, grid, block, stream);
-    else launch_res<FMT, false, false>(L, J, R, grid, block, stream);
+    if (exact) launch_res<FMT, false, true>(L, P.J, P.R, P.grid, P.block, stream);
+    else launch_res<FMT, false, false>(L, P.J, P.R, P.grid, P.block, stream);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -261,18 +274,15 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
   }
   if (const rmsq_status s = check_overlaps(rs, nr); s != RMSQ_OK) return s;
 
-  bool any = false;
-  for (int i = 0; i < count; ++i) any |= ps[i].M > 0;
-  if (!any) return RMSQ_OK;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
-    return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");
-
   // One launch for the problems with a residual and one for those without
-  // (a set that mixes the two takes two launches, in that order).
+  // (a set that mixes the two takes two launches, in that order). Both are
+  // planned and checked before either is enqueued.
+  Plan plans[2];
+  int np = 0;
   for (int with_res = 1; with_res >= 0; --with_res) {
-    rmsq::Launch L;
-    std::memset(&L, 0, sizeof L);
+    Plan& P = plans[np];
+    P = Plan{};
+    rmsq::Launch& L = P.L;
     int64_t rows = 0, Cmax = 0;
     int n = 0;
     for (int i = 0; i < count; ++i) {
@@ -354,10 +364,25 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
       while ((1 << L.splits_log2) < S) ++L.splits_log2;
       if (S > 1) L.row_group_log2 = 0;
     }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const rmsq_status st = mode == Mode::kNormOnly               ? launch_fmt<2>(L, J, W, R, s)
-                           : ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(L, J, W, R, s)
-                                                                : launch_fmt<1>(L, J, W, R, s);
+    P.J = J;
+    P.W = W;
+    P.R = R;
+    plan_grid(P);
+    // the dispatch counts work-items per dimension in 32 bits
+    if ((uint64_t)P.grid.x * P.block.x > UINT32_MAX)
+      return fail(RMSQ_ERR_UNSUPPORTED, "%lld rows of %lld elements need %llu work-items in one launch, beyond 2^32",
+                  (long long)rows, (long long)Cmax * 8, (unsigned long long)P.grid.x * P.block.x);
+    ++np;
+  }
+  if (np == 0) return RMSQ_OK;   // every problem has M == 0
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
+    return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int k = 0; k < np; ++k) {
+    const rmsq_status st = mode == Mode::kNormOnly               ? launch_fmt<2>(plans[k], s)
+                           : ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? launch_fmt<0>(plans[k], s)
+                                                                : launch_fmt<1>(plans[k], s);
     if (st != RMSQ_OK) return st;
   }
   return RMSQ_OK;
@@ -372,6 +397,11 @@ rmsq_status run_quant(const rmsq_problem& p, void* stream) {
   if (const rmsq_status st = check_problem(p, 0, p.fmt, Mode::kQuantOnly, rs, &nr); st != RMSQ_OK) return st;
   if (const rmsq_status st = check_overlaps(rs, nr); st != RMSQ_OK) return st;
   if (p.M == 0) return RMSQ_OK;
+  // one workgroup of 128 work-items per row (and per 1024 elements of it);
+  // the dispatch counts work-items per dimension in 32 bits
+  if (p.M > (int64_t)(UINT32_MAX / 128))
+    return fail(RMSQ_ERR_UNSUPPORTED, "quant: M = %lld rows need more than 2^32 work-items in one launch",
+                (long long)p.M);
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
     return fail(RMSQ_ERR_UNSUPPORTED, "current HIP device is not a gfx950 GPU");

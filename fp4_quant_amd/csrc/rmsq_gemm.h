@@ -240,9 +240,8 @@ __global__ void __launch_bounds__(64 * gemm_max_waves(MT * CT)) rmsq_gemm_fp4_ke
       }
     }
   } else {
-    // activation row of this lane in each tile; lanes of rows past M read
+    // activation rows of this lane in each tile; lanes of rows past M read
     // row M-1 (their results are not stored)
-    const u32x4* arow[MT];
     const uint8_t* asrow[MT];   // quantized activations: the row's scale bytes, group stride a_gs
     const u32x4* arowq[MT];     // quantized activations loaded directly: the operand lane's code row
     int crow[MT][2];            // quantized activations loaded by pairs: code rows 8j + lane/8 of the tile

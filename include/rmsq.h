@@ -35,6 +35,12 @@
  *    residual_out may be the very same buffer as residual_in (in place).
  *  - Validation happens before any HIP call; a status other than RMSQ_OK
  *    means nothing was enqueued. M == 0 is a no-op returning RMSQ_OK.
+ *  - Size limit: the hardware dispatch counts a launch's work-items in 32
+ *    bits, and a row takes 64 to 1024 of them (64 per wave of its launch
+ *    shape; the quantization alone, 128 per row), so a call whose rows would
+ *    need more than 2^32 work-items in one launch (e.g. more than 67M rows of
+ *    512 elements, 4.1M rows of any width always fit) returns
+ *    RMSQ_ERR_UNSUPPORTED; split such a batch into several calls.
  *  - Non-finite inputs are outside the contract (no fault, undefined values).
  *  - Thread safety: calls are re-entrant; calls on different streams may run
  *    concurrently.

@@ -127,6 +127,36 @@ def test_m_zero_is_a_noop_without_device():
     assert _call(M=0, r=None, ro=A + 400 * MB) == fq.RMSQ_OK     # empty tensors have NULL data
 
 
+TB = 1 << 40
+
+
+def test_launch_beyond_the_work_item_limit_is_refused_before_any_hip_call():
+    """One launch covers at most 2^32 work-items per grid dimension: 70M rows
+    of 512 (one 64-lane wave per row) exceed it, 60M rows do not. Buffers are
+    fake addresses 1 TiB apart; the refusal comes before the device check."""
+    big = dict(x=A, g=A + TB, q=A + 2 * TB, s=A + 3 * TB, N=512)
+    assert _call(M=70_000_000, **big) == fq.RMSQ_ERR_UNSUPPORTED
+    assert b"2^32" in fq.lib().rmsq_last_error()
+    # a set that mixes a residual problem with such a one: neither launch is made
+    small = dict(x=A + 4 * TB, ldx=0, residual_in=A + 5 * TB, residual_out=A + 6 * TB, ldr=0, gamma=A + TB,
+                 eps=1e-6, M=4, N=512, group=128, fmt=0, scale_layout=0, out_q=A + 7 * TB, out_scale=A + 8 * TB,
+                 out_bf16=None, ldb=0)
+    huge = dict(small, x=A, residual_in=None, residual_out=None, M=70_000_000, out_q=A + 2 * TB,
+                out_scale=A + 3 * TB)
+    assert _multi(probs=[small, huge]) == fq.RMSQ_ERR_UNSUPPORTED
+    assert b"2^32" in fq.lib().rmsq_last_error()
+    L = fq.lib()
+    assert L.dynamic_per_group_scaled_quant(A, 40_000_000, 128, 128, 0, 0, A + 2 * TB, A + 3 * TB,
+                                            None) == fq.RMSQ_ERR_UNSUPPORTED
+    assert b"2^32" in L.rmsq_last_error()
+    if not fq.rmsq_device_supported(0):   # within the limit: only the missing device stops it
+        assert _call(M=60_000_000, **big) == fq.RMSQ_ERR_UNSUPPORTED
+        assert b"gfx950" in fq.lib().rmsq_last_error()
+        assert L.dynamic_per_group_scaled_quant(A, 30_000_000, 128, 128, 0, 0, A + 2 * TB, A + 3 * TB,
+                                                None) == fq.RMSQ_ERR_UNSUPPORTED
+        assert b"gfx950" in L.rmsq_last_error()
+
+
 def test_valid_call_without_a_gfx950_device_is_unsupported():
     if fq.rmsq_device_supported(0):
         pytest.skip("a gfx950 device is present")
