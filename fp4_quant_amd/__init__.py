@@ -149,12 +149,44 @@ def rmsnorm_quant_group(x, residual_in, gamma, eps, M, N, group, fmt, out_q, out
 
 
 def _ld(t):
-    return 0 if t is None else int(t.stride(0))
+    """Row stride in elements for the library (0 = N: absent, or one row,
+    whose stride is never applied)."""
+    return 0 if t is None or t.shape[0] <= 1 else int(t.stride(0))
+
+
+def _check_rows(t, M, N, name):
+    """t: [M, N] bf16 rows with unit column stride and rows that do not
+    overlap (row stride >= N; the library also needs it a multiple of 8)."""
+    import torch
+    if M == 0:   # nothing is read or written (empty tensors may come in any shape)
+        return
+    if (t.dtype != torch.bfloat16 or t.dim() != 2 or tuple(t.shape) != (M, N) or (N > 1 and t.stride(1) != 1)
+            or (M > 1 and t.stride(0) < N)):
+        raise ValueError(f"{name} must be a [{M}, {N}] bf16 tensor with unit column stride and row stride >= N "
+                         f"(got {tuple(t.shape)} {t.dtype}, strides {tuple(t.stride())})")
 
 
 def make_problem(x, gamma, eps, out_q, out_scale, *, residual_in=None, residual_out=None,
                  out_bf16=None, fmt=FMT_FP8_E4M3FN, scale_layout=SCALE_ROW_MAJOR) -> rmsq_problem:
+    """One problem for ``rmsnorm_quant_group_multi``. The bf16 tensors are
+    checked for dtype and shape here (the library checks strides, alignment,
+    overlaps and the formats); residual_in and residual_out share one row
+    stride, which the library applies to both."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, N]")
     M, N = x.shape
+    _check_rows(x, M, N, "x")
+    if M and (gamma.dtype != torch.bfloat16 or gamma.numel() != N or not gamma.is_contiguous()):
+        raise ValueError(f"gamma must be {N} contiguous bf16 values")
+    if residual_in is not None:
+        _check_rows(residual_in, M, N, "residual_in")
+    if residual_out is not None:
+        _check_rows(residual_out, M, N, "residual_out")
+        if residual_in is not None and M > 1 and residual_out.stride(0) != residual_in.stride(0):
+            raise ValueError("residual_out must have the row stride of residual_in")
+    if out_bf16 is not None:
+        _check_rows(out_bf16, M, N, "out_bf16")
     return rmsq_problem(x=_ptr(x), ldx=_ld(x), residual_in=_ptr(residual_in),
                         residual_out=_ptr(residual_out), ldr=_ld(residual_in), gamma=_ptr(gamma),
                         eps=float(eps), M=M, N=N, group=_GROUP.get(fmt, 0), fmt=fmt,
@@ -302,7 +334,9 @@ def fused_rmsnorm_quant(x, gamma, eps=1e-6, residual=None, fmt="fp8", keep_bf16=
     q, scale, yb = alloc_outputs(M, N, f, lay, keep_bf16, x.device)
     res_out = None
     if residual is not None:
-        res_out = residual if inplace_residual else torch.empty_like(residual)
+        # the library writes residual_out with residual's row stride
+        res_out = residual if inplace_residual else torch.empty_strided(
+            residual.shape, residual.stride(), dtype=residual.dtype, device=residual.device)
     p = make_problem(x, gamma, eps, q, scale, residual_in=residual, residual_out=res_out,
                      out_bf16=yb, fmt=f, scale_layout=lay)
     rmsnorm_quant_group_multi([p], stream)
@@ -359,8 +393,9 @@ def prequant_gemm(a, w, w_scale, fmt="mxfp4", preshuffled=False, out=None, strea
         out = torch.empty((M, N), dtype=torch.float32, device=a.device)
     elif out.dtype != torch.float32 or out.shape != (M, N) or out.stride(1) != 1:
         raise ValueError("out must be a float32 [M, N] tensor with unit column stride")
-    call(a, a.stride(0), w, w_scale, W_PRESHUFFLED if preshuffled else W_ROW_MAJOR, M, N, K, out, out.stride(0),
-         stream)
+    # strides of a single row are never applied: pass the dense ones
+    call(a, a.stride(0) if M > 1 else K, w, w_scale, W_PRESHUFFLED if preshuffled else W_ROW_MAJOR, M, N, K, out,
+         out.stride(0) if M > 1 else N, stream)
     return out
 
 
@@ -400,5 +435,5 @@ def quantized_gemm(a_q, a_scale, w, w_scale, fmt="mxfp4", scale_layout=SCALE_ROW
     elif out.dtype != torch.float32 or out.shape != (M, N) or out.stride(1) != 1:
         raise ValueError("out must be a float32 [M, N] tensor with unit column stride")
     call(a_q, a_scale, scale_layout, w, w_scale, W_PRESHUFFLED if preshuffled else W_ROW_MAJOR, M, N, K, out,
-         out.stride(0), stream)
+         out.stride(0) if M > 1 else N, stream)
     return out

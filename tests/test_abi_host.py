@@ -422,3 +422,34 @@ def test_quantized_activation_gemms_validate(entry):
     assert g() in (fq.RMSQ_OK, fq.RMSQ_ERR_UNSUPPORTED)
     if not fq.rmsq_device_supported(0):
         assert g() == fq.RMSQ_ERR_UNSUPPORTED
+
+
+def test_make_problem_checks_the_tensors_before_taking_addresses():
+    """The binding's problem builder refuses tensors that the library would
+    misread (wrong dtype or shape, a row stride below N such as an expanded
+    residual, a residual output with another row stride) before it takes any
+    address; CPU tensors reach these checks first, so this runs without a GPU."""
+    import torch
+    M, N = 4, 256
+    x = torch.zeros((M, N), dtype=torch.bfloat16)
+    g = torch.ones(N, dtype=torch.bfloat16)
+    q = torch.zeros((M, N), dtype=torch.uint8)
+    s = torch.zeros((M, N // 128), dtype=torch.float32)
+    bad = [
+        dict(x=x.float()),
+        dict(x=x.t().contiguous().t()),                                   # column stride M
+        dict(gamma=g[:128]),
+        dict(residual_in=torch.zeros(N, dtype=torch.bfloat16).expand(M, N),
+             residual_out=torch.zeros((M, N), dtype=torch.bfloat16)),      # row stride 0
+        dict(residual_in=torch.zeros((M, N + 64), dtype=torch.bfloat16)[:, :N],
+             residual_out=torch.zeros((M, N), dtype=torch.bfloat16)),      # row strides differ
+        dict(out_bf16=torch.zeros((M, N), dtype=torch.float16)),
+    ]
+    for kw in bad:
+        args = dict(x=x, gamma=g)
+        args.update(kw)
+        xx, gg = args.pop("x"), args.pop("gamma")
+        with pytest.raises(ValueError):
+            fq.make_problem(xx, gg, 1e-6, q, s, **args)
+    with pytest.raises(ValueError, match="GPU tensors"):    # a well-formed problem on the host
+        fq.make_problem(x, g, 1e-6, q, s)

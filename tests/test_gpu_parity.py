@@ -428,4 +428,25 @@ def test_fused_convenience_wrapper_tuples():
     torch.cuda.synchronize()
     assert q4.shape == (64, 3584) and s4.numel() == 64 * 224
     with pytest.raises(fq.RmsqError):
-        fq.fused_rmsnorm_quant(x[:, :100], g, 1e-6)
+        fq.fused_rmsnorm_quant(x[:, :100], g[:100], 1e-6)   # N = 100: no whole FP8 group
+
+
+def test_fused_convenience_wrapper_padded_residual():
+    """A residual that is a view with padded rows: the residual output is
+    allocated with the same row stride (the library writes it with that
+    stride) and equals the contiguous call's, and the padding stays as it was."""
+    say("wrapper, padded residual rows")
+    p = _cfg("decode")
+    x, r, g = dev(p["x"]), dev(p["residual"]), dev(p["gamma"])
+    big = torch.full((64, 7168 + 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    big[:, :7168] = r
+    rv = big[:, :7168]
+    (q, s), res = fq.fused_rmsnorm_quant(x, g, 1e-6, residual=r)
+    (qv, sv), resv = fq.fused_rmsnorm_quant(x, g, 1e-6, residual=rv)
+    torch.cuda.synchronize()
+    assert resv.stride() == rv.stride()
+    assert torch.equal(q, qv) and torch.equal(s, sv) and torch.equal(res, resv)
+    (qi, si), resi = fq.fused_rmsnorm_quant(x, g, 1e-6, residual=rv, inplace_residual=True)
+    torch.cuda.synchronize()
+    assert resi.data_ptr() == rv.data_ptr() and torch.equal(resi, res) and torch.equal(qi, q)
+    assert torch.all(big[:, 7168:] == 7.0)
