@@ -75,18 +75,6 @@ constexpr int kGemmRowsPerBlock = 64;   // 4 tiles of 16 rows
 constexpr int kGemmSmallRows = 4;      // at most this many rows take the small-M path
 constexpr int kGemmSmallSteps = 4;     // steps per wave on the small-M path (one batch)
 
-// MXFP4 quantization of one 32-element bf16 group held by one lane (16
-// packed dwords): the e8m0 byte and the 4 dwords of e2m1 codes.
-__device__ __forceinline__ uint32_t mx_group32(const u32x4 v[4], u32x4* codes) {
-  const uint32_t am = max(max(amax8(v[0]), amax8(v[1])), max(amax8(v[2]), amax8(v[3])));
-  const uint32_t byte = mx_scale_byte(am);
-  (*codes)[0] = fp4_codes8(v[0], byte);
-  (*codes)[1] = fp4_codes8(v[1], byte);
-  (*codes)[2] = fp4_codes8(v[2], byte);
-  (*codes)[3] = fp4_codes8(v[3], byte);
-  return byte;
-}
-
 // Scale (row m, group g) of quantized activations with G groups per row and
 // M rows, in the layouts the group quantization writes, sits at
 // row_part + g * g_stride: row-major [M, G] (m G, 1), 32-row tiles with the
@@ -191,18 +179,19 @@ __global__ void __launch_bounds__(64 * gemm_max_waves(MT * CT)) rmsq_gemm_fp4_ke
 
   if constexpr (SMALLM) {
     // Small M: the wave's batch of SW = 4 steps needs at most 4 rows x 16
-    // activation groups, one per lane: lane L holds step i = L/16, row
-    // min(L/4 % 4, M-1), 32-element quarter L%4, loaded with all lanes and
-    // quantized in place; the operand lane of row r, quarter kb then fetches
-    // it from lane 16 i + 4 r + kb (ds_bpermute). No workgroup barrier
-    // precedes the matrix-core steps.
+    // activation groups of 32. Step i is one load of 4 rows x 256
+    // consecutive bytes (lane L: row min(L/16, M-1), elements 8 (L%16) ..
+    // +7 of the step), so each load reads whole cache lines; a lane quad then
+    // holds one group (its amax by DPP), each lane encodes its 8 elements, and
+    // the operand lane of row r, quarter kb fetches the 4 code dwords and the
+    // scale byte from lanes 16 r + 4 kb + d (ds_bpermute). With each lane
+    // reading 64 bytes of one group instead, every load touched four times
+    // the cache lines. No workgroup barrier precedes the matrix-core steps.
     const int R = G.M;
-    const int ai = lane >> 4, ar = min((lane >> 2) & 3, R - 1), aq = lane & 3;
-    const int ast = min(s_lo + ai, s_hi - 1);
-    const u32x4* ap = reinterpret_cast<const u32x4*>(G.a + (int64_t)ar * G.lda) + ast * 16 + aq * 4;
-    u32x4 av[4];
+    const u32x4* ap = reinterpret_cast<const u32x4*>(G.a + (int64_t)min(lane >> 4, R - 1) * G.lda) + (lane & 15);
+    u32x4 av[SW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) av[j] = ap[j];
+    for (int i = 0; i < SW; ++i) av[i] = ap[min(s_lo + i, s_hi - 1) * 16];   // past the range: re-read (unused)
     __builtin_amdgcn_sched_barrier(0);
     u32x4 bw[CT][SW];
     uint32_t sb[CT][SW];
@@ -215,17 +204,17 @@ __global__ void __launch_bounds__(64 * gemm_max_waves(MT * CT)) rmsq_gemm_fp4_ke
         sb[ct][i] = wsc[ct * ws_tile + st * ws_step];
       }
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 qa;
-    const uint32_t byte = mx_group32(av, &qa);
     const int r = lane & 15;
     const bool live = r < R;
+    const int src = (16 * min(r, 3) + 4 * kb) << 2;   // ds_bpermute byte address of the group's first lane
 #pragma unroll
     for (int i = 0; i < SW; ++i) {
       if (s_lo + i >= s_hi) break;
-      const int src = (16 * i + 4 * min(r, 3) + kb) << 2;   // ds_bpermute byte address
+      const uint32_t byte = mx_scale_byte(max4(amax8(av[i])));
+      const uint32_t code = fp4_codes8(av[i], byte);
       u32x4 q;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) q[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)qa[d]);
+      for (int d = 0; d < 4; ++d) q[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src + (d << 2), (int)code);
       uint32_t sa = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)byte);
       if (!live) {
         q = u32x4{0u, 0u, 0u, 0u};
@@ -518,19 +507,18 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const
 
   if constexpr (SMALLM) {
     // Small M: the wave's batch of SW = 4 steps needs at most 4 rows x 4
-    // groups of 128, each held by a lane quad: lane L holds step i = L/16,
-    // row min(L/4 % 4, M-1), quarter L%4 (32 elements), so the quad's DPP
-    // max gives the group amax; the operand lane of row r, quarter kb then
-    // fetches the codes from lane 16 i + 4 r + kb, and each result lane the
+    // groups of 128. Step i is one load of 4 rows x 256 consecutive bytes
+    // (lane L: row min(L/16, M-1), elements 8 (L%16) .. +7 of the step), so
+    // each 16-lane DPP row holds one group (amax by DPP) and each lane
+    // encodes its 8 elements; the operand lane of row r, quarter kb fetches
+    // its 8 code dwords from lanes 16 r + 4 kb + d, and each result lane the
     // scales of its four rows (ds_bpermute). No workgroup barrier precedes
     // the matrix-core steps.
     const int R = G.M;
-    const int ai = lane >> 4, ar = min((lane >> 2) & 3, R - 1), aq = lane & 3;
-    const int ast = min(s_lo + ai, s_hi - 1);
-    const u32x4* ap = reinterpret_cast<const u32x4*>(G.a + (int64_t)ar * G.lda) + ast * 16 + aq * 4;
-    u32x4 av[4];
+    const u32x4* ap = reinterpret_cast<const u32x4*>(G.a + (int64_t)min(lane >> 4, R - 1) * G.lda) + (lane & 15);
+    u32x4 av[SW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) av[j] = ap[j];
+    for (int i = 0; i < SW; ++i) av[i] = ap[min(s_lo + i, s_hi - 1) * 16];   // past the range: re-read (unused)
     __builtin_amdgcn_sched_barrier(0);
     u32x4 bw[SW][2];
     float sw[SW];
@@ -542,18 +530,22 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const
       sw[i] = wsrow[st];
     }
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t am = max(max(amax8(av[0]), amax8(av[1])), max(amax8(av[2]), amax8(av[3])));
-    const float sc = fp8_scale(max4(am));
-    const v8i32 qa = fp8_codes32(av, sc);
     const int r = lane & 15;
     const bool live = r < R;
+    const int src = (16 * min(r, 3) + 4 * kb) << 2;   // ds_bpermute byte address of the quarter's first lane
 #pragma unroll
     for (int i = 0; i < SW; ++i) {
       if (s_lo + i >= s_hi) break;
-      const int src = (16 * i + 4 * min(r, 3) + kb) << 2;   // ds_bpermute byte address
+      const float sc = fp8_scale(max16(amax8(av[i])));
+      float f[8];
+      unpack_bf16x8(av[i], f);
+      const u32x2 c = fp8_codes8<kFp8Rounds>(f, sc);
       v8i32 aop;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) aop[d] = __builtin_amdgcn_ds_bpermute(src, qa[d]);
+      for (int d = 0; d < 4; ++d) {
+        aop[2 * d] = __builtin_amdgcn_ds_bpermute(src + (d << 2), (int)c[0]);
+        aop[2 * d + 1] = __builtin_amdgcn_ds_bpermute(src + (d << 2), (int)c[1]);
+      }
       if (!live) aop = v8i32{0, 0, 0, 0, 0, 0, 0, 0};
       const v8i32 bop = {(int)bw[i][0][0], (int)bw[i][0][1], (int)bw[i][0][2], (int)bw[i][0][3],
                          (int)bw[i][1][0], (int)bw[i][1][1], (int)bw[i][1][2], (int)bw[i][1][3]};
@@ -561,9 +553,9 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const
                                                                        0, 0, 127, 0, 127);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // result row 4 kb + j: its scale sits in lane 16 i + 4 (4 kb + j) (rows past 3 give 0)
+        // result row 4 kb + j: its scale sits in every lane 16 (4 kb + j) + x (rows past 3 give 0)
         const int row = 4 * kb + j;
-        const float sa = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute((16 * i + 4 * min(row, 3)) << 2,
+        const float sa = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute((16 * min(row, 3)) << 2,
                                                                                (int)__float_as_uint(sc)));
         const float ts = row < R ? sa * sw[i] : 0.0f;
         acc[0][j] = __builtin_fmaf(d[j], ts, acc[0][j]);
