@@ -13,7 +13,7 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   roofline      the fused kernel against the 8 TB/s HBM peak: algorithmic
                 bytes per launch over the average launch time of the timed
                 region (HIP events on the launch stream)
-  cpu_baseline  the double-precision CPU oracle on the machine's host cores
+  cpu_baseline  the double-precision CPU oracle on the host's cores
   configs       the other workloads (decode, prefill at 512 rows, the two MLA
                 latent norms in one launch, MXFP4 in both scale layouts) and
                 the A16WFP4 prequant GEMM at a decode batch of 4 (bytes:
@@ -276,7 +276,7 @@ def _stream_probe():
 
 
 def ceilings(reps=30):
-    """Achievable HBM bandwidth on this machine from the no-arithmetic stream
+    """Achievable HBM bandwidth of this GPU from the no-arithmetic stream
     probes (tests/hip/stream_probe.hip), nontemporal loads and stores like the
     fused kernel, three rotating buffer sets so nothing is served from the
     Infinity Cache: a plain copy, and streams with the fused kernels' exact

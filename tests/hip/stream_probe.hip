@@ -1,6 +1,6 @@
 // stream_probe.hip - test-only bandwidth probes: plain streams (read, write,
 // copy) and the fused kernel's exact traffic pattern with no arithmetic, to
-// measure the achievable HBM ceiling on the box. Grid-stride loops, bounds
+// measure the achievable HBM ceiling of the GPU. Grid-stride loops, bounds
 // checked; n16 counts 16-byte elements.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
