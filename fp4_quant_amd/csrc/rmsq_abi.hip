@@ -163,7 +163,7 @@ rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Mode mod
 // 10.9 against 12.4 us).
 constexpr int kJs[] = {2, 3, 4, 1, 7, 8, 14};
 constexpr int kJsFewRows[] = {1, 2, 3, 4, 7, 8, 14};
-constexpr int kWaveRowsPerBlock = 4;
+constexpr int kWaveRowsPerBlock = 8;
 constexpr int kMaxSplits = 8;
 
 void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {

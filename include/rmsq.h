@@ -356,7 +356,7 @@ void rmsq_set_row_group(int32_t g);
 /* Measurement hook: rows that one wave covers (a shape with W = 1) are packed
  * R per workgroup, one per wave, for later calls in this process: R in
  * 2..16, or 1 for one row per workgroup; 0 restores the automatic choice
- * (R = 4 once a launch has at least 1024 rows, else 1). Results do not
+ * (R = 8 once a launch has at least 1024 rows, else 1). Results do not
  * depend on it. */
 void rmsq_set_wave_rows(int32_t R);
 
