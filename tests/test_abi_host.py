@@ -149,7 +149,13 @@ def test_launch_beyond_the_work_item_limit_is_refused_before_any_hip_call():
     assert L.dynamic_per_group_scaled_quant(A, 40_000_000, 128, 128, 0, 0, A + 2 * TB, A + 3 * TB,
                                             None) == fq.RMSQ_ERR_UNSUPPORTED
     assert b"2^32" in L.rmsq_last_error()
+    # the widest rows (32768: 16 waves, 1024 work-items each): 2^22 - 1 rows fit, 2^22 do not
+    wide = dict(big, N=32768)
+    assert _call(M=1 << 22, **wide) == fq.RMSQ_ERR_UNSUPPORTED
+    assert b"2^32" in fq.lib().rmsq_last_error()
     if not fq.rmsq_device_supported(0):   # within the limit: only the missing device stops it
+        assert _call(M=(1 << 22) - 1, **wide) == fq.RMSQ_ERR_UNSUPPORTED
+        assert b"gfx950" in fq.lib().rmsq_last_error()
         assert _call(M=60_000_000, **big) == fq.RMSQ_ERR_UNSUPPORTED
         assert b"gfx950" in fq.lib().rmsq_last_error()
         assert L.dynamic_per_group_scaled_quant(A, 30_000_000, 128, 128, 0, 0, A + 2 * TB, A + 3 * TB,
