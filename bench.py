@@ -12,12 +12,20 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                 read, residual, codes, scales and bf16 written; gamma excluded)
   roofline      the fused kernel against the 8 TB/s HBM peak: algorithmic
                 bytes per launch over the average launch time of the timed
-                region (HIP events on the launch stream)
-  cpu_baseline  the double-precision CPU oracle on the host's cores
+                region (HIP events on the launch stream), with the achievable
+                ceiling of the same traffic measured by no-arithmetic probes
+  cpu_baseline  the double-precision CPU oracle on the host's cores, timed
+                on preallocated outputs
   configs       the other workloads (decode, prefill at 512 rows, the two MLA
-                latent norms in one launch, MXFP4 in both scale layouts) and
-                the A16WFP4 prequant GEMM at a decode batch of 4 (bytes:
-                weight codes and scales, activations, fp32 output)
+                latent norms in one launch, MXFP4 in both scale layouts, ...),
+                each as the median of several timed windows, with the floor of
+                its own launch plan (the kernel's memory skeleton without
+                arithmetic), and the GEMMs at a decode batch of 4
+  parity        the first rows of every timed workload's outputs against the
+                oracle, read back after the timing
+  inputs_sha256 sha256 of every generated input array
+  git_sha, source_sha256, gpu_state (clocks, power, temperatures before and
+                after the timed region), host (CPU model, cores)
 """
 from __future__ import annotations
 
@@ -89,12 +97,74 @@ class Workload:
                                              out_bf16=yb, fmt=fmt, scale_layout=layout))
             self.sets.append((fq.problem_array(probs), keep))
         self.host = host
+        self.specs = specs
+        self.sha = [{k: inputs.sha256(v) for k, v in p.items() if hasattr(v, "dtype")} for p in host]
         # launches go to torch's current stream, whose handle is taken once
         self.stream = torch.cuda.current_stream().cuda_stream
 
     def launch(self, i, stream=None):
         import fp4_quant_amd as fq
         fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0], stream or self.stream)
+
+    def plan(self):
+        import fp4_quant_amd as fq
+        return fq.rmsq_plan_launch(self.sets[0][0])
+
+    def capture(self, rows=512):
+        """The first `rows` rows of each problem's outputs in buffer set 0, on
+        the host (every launch on a set writes the same bytes), for the parity
+        check against the oracle."""
+        import torch
+        torch.cuda.synchronize()
+        keep = self.sets[0][1]
+        out = []
+        for k, s in enumerate(self.specs):
+            x, g, r, ro, q, sc, yb = keep[7 * k:7 * k + 7]
+            n = min(rows, s["M"])
+            G = s["N"] // (128 if self.fmt == 0 else 32)
+            if self.layout == 1:
+                scale = sc[:-(-n // 32) * 32 * G]
+            elif self.layout == 2:
+                scale = sc[:, :n]
+            else:
+                scale = sc[:n]
+            d = {"rows": n, "q": q[:n].cpu().numpy(), "scale": scale.contiguous().cpu().numpy()}
+            if ro is not None:
+                d["residual_out"] = ro[:n].contiguous().view(torch.int16).cpu().numpy().view("uint16")
+            if yb is not None:
+                d["bf16"] = yb[:n].contiguous().view(torch.int16).cpu().numpy().view("uint16")
+            out.append(d)
+        return out
+
+
+class FloorWorkload:
+    """The floor of a workload's own launch plan: the library plans the call
+    (rmsq_plan_launch, host arithmetic only) and the probe library launches
+    the fused kernel's memory skeleton for exactly that plan - same grid,
+    mapping, loads, barrier and stores, no arithmetic - on the workload's
+    buffers (tests/hip/stream_probe.hip, k_plan_floor). Overwrites the
+    workload's outputs with bit mixes: run it after the outputs were read."""
+
+    def __init__(self, w):
+        import ctypes as C
+        import fp4_quant_amd as fq
+        self.w = w
+        plan = fq.rmsq_launch_plan()
+        arr = w.sets[0][0]
+        if fq.lib().rmsq_plan_launch(arr, len(arr), None, C.byref(plan)) != 0:
+            raise RuntimeError(fq.lib().rmsq_last_error().decode())
+        self.infos = [plan.launch[k] for k in range(plan.launches)]
+        self.L = _stream_probe()
+        self.L.stream_probe_plan_floor.restype = C.c_int
+        self.L.stream_probe_plan_floor.argtypes = [C.POINTER(fq.rmsq_problem), C.c_int32,
+                                                   C.POINTER(fq.rmsq_launch_info), C.c_void_p]
+        self.stream = w.stream
+        self.C = C
+
+    def launch(self, i, stream=None):
+        arr = self.w.sets[i % len(self.w.sets)][0]
+        for info in self.infos:
+            assert self.L.stream_probe_plan_floor(arr, len(arr), self.C.byref(info), stream or self.stream) == 0
 
 
 def gemm_bytes(M, N, K, fmt=1, aq=False):
@@ -156,6 +226,7 @@ class GemmWorkload:
         self.rows = M
         self.bytes = gemm_bytes(M, N, K, fmt, aq)
         g = inputs.make_gemm(M, N, K) if fmt == 1 else inputs.make_gemm8(M, N, K)
+        self.host = g
         a = torch.from_numpy(g["a"].view("int16")).view(torch.bfloat16).cuda()
         acts = (a,)
         if aq:
@@ -247,24 +318,34 @@ class UnfusedWorkload(Workload):
         fq.dynamic_per_group_scaled_quant(yb, M, N, 128 if self.fmt == 0 else 32, self.fmt, self.layout, q, sc, st)
 
 
-def time_workload(w, steps, warmup):
-    """Warm up, then time `steps` back-to-back launches between two HIP events
-    recorded on the launch stream (torch's current stream, which the binding
-    passes to the library). Returns the average milliseconds per launch; each
-    step is exactly one launch, so this is both the step time and the
+def time_workload(w, steps, warmup, windows=1):
+    """Warm up, then time `windows` windows of `steps` back-to-back launches,
+    each between two HIP events recorded on the launch stream (torch's
+    current stream, which the binding passes to the library). Returns the
+    average milliseconds per launch of each window (a list when windows > 1);
+    each step is exactly one launch, so this is both the step time and the
     kernel's average duration (rocprofv3's kernel trace of the same command
     reports the same average)."""
     import torch
     for i in range(warmup):
         w.launch(i)
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        w.launch(i)
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    out = []
+    for _ in range(windows):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            w.launch(i)
+        t1.record()
+        torch.cuda.synchronize()
+        out.append(t0.elapsed_time(t1) / steps)
+    return out if windows > 1 else out[0]
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
 def _stream_probe():
@@ -275,35 +356,57 @@ def _stream_probe():
     return L
 
 
-def ceilings(reps=30):
+def ceilings(reps=30, windows=3):
     """Achievable HBM bandwidth of this GPU from the no-arithmetic stream
     probes (tests/hip/stream_probe.hip), nontemporal loads and stores like the
     fused kernel, three rotating buffer sets so nothing is served from the
     Infinity Cache: a plain copy, and streams with the fused kernels' exact
     traffic mixes per 8 elements: FP8 with bf16 side-output (read 2 x 16 B,
-    write 2 x 16 B + 8 B) and MXFP4 (read 2 x 16 B, write 16 B + 4 B)."""
+    write 2 x 16 B + 8 B) and MXFP4 (read 2 x 16 B, write 16 B + 4 B). The FP8
+    mix is also run row-mapped like the kernel (7 waves x 2 chunks per row,
+    one barrier) and persistent (512 workgroups looping over the rows). Each
+    figure is the median of `windows` windows of `reps` launches."""
+    import ctypes as Cc
     import torch
     L = _stream_probe()
+    L.stream_probe_rows.restype = Cc.c_int
+    L.stream_probe_rows.argtypes = [Cc.c_void_p] * 5 + [Cc.c_int32] * 6 + [Cc.c_void_p]
     st = torch.cuda.current_stream().cuda_stream
-    n16 = 8192 * 7168 // 8
+    M, N = 8192, 7168
+    n16 = M * N // 8
     sets = [[torch.ones(n16 * 16, dtype=torch.uint8, device="cuda") for _ in range(4)] +
             [torch.zeros(n16 * 8, dtype=torch.uint8, device="cuda")] for _ in range(3)]
-    out = {}
-    for kind, name, nbytes in ((2, "copy", 2 * n16 * 16), (3, "fused_mix", 4 * n16 * 16 + n16 * 8),
-                               (4, "fused_mix_mxfp4", 3 * n16 * 16 + n16 * 4)):
+
+    def flat(kind):
         def go(i):
             S = sets[i % 3]
             assert L.stream_probe(kind, 1, *[t.data_ptr() for t in S], n16, 16384, 256, st) == 0
-        for i in range(50):
+        return go
+
+    def rows(persist):
+        def go(i):
+            S = sets[i % 3]
+            assert L.stream_probe_rows(*[t.data_ptr() for t in S], M, N // 8, 2, 7, 1, persist, st) == 0
+        return go
+
+    out = {}
+    mix = 4 * n16 * 16 + n16 * 8
+    for name, go, nbytes in (("copy", flat(2), 2 * n16 * 16), ("fused_mix", flat(3), mix),
+                             ("fused_mix_rows", rows(0), mix), ("fused_mix_persistent", rows(512), mix),
+                             ("fused_mix_mxfp4", flat(4), 3 * n16 * 16 + n16 * 4)):
+        for i in range(100):
             go(i)
         torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for i in range(reps):
-            go(i)
-        t1.record()
-        torch.cuda.synchronize()
-        out[name] = round(nbytes / (t0.elapsed_time(t1) / reps * 1e-3) / 1e9, 1)
+        ts = []
+        for _ in range(windows):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for i in range(reps):
+                go(i)
+            t1.record()
+            torch.cuda.synchronize()
+            ts.append(t0.elapsed_time(t1) / reps)
+        out[name] = round(nbytes / (median(ts) * 1e-3) / 1e9, 1)
     del sets
     torch.cuda.empty_cache()
     return out
@@ -393,52 +496,187 @@ def recorded_traffic(config):
     return None
 
 
-def _oracle_call(p, fmt, layout, keep):
+# ------------------------------------------------------------ identity --
+def source_sha256():
+    """sha256 over every source the library, its binding and this benchmark
+    are built from (C ABI header, HIP sources, Python), in name order."""
+    import hashlib
+    h = hashlib.sha256()
+    files = [os.path.join("include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))]
+    files += [os.path.join("fp4_quant_amd", "csrc", f)
+              for f in sorted(os.listdir(os.path.join(ROOT, "fp4_quant_amd", "csrc")))]
+    files += [os.path.join("fp4_quant_amd", f) for f in ("__init__.py", "inputs.py", "build.py")] + ["bench.py"]
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def git_identity():
+    """(sha, where it came from): the checkout's HEAD when git can read it,
+    else the HEAD recorded when the library was built (build_info.json)."""
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=20)
+        if r.returncode == 0 and r.stdout.strip():
+            d = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=20)
+            return r.stdout.strip(), "checkout" + (" (modified)" if d.stdout.strip() else "")
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        info = json.load(open(os.path.join(ROOT, "fp4_quant_amd", "build_info.json")))
+        return info.get("git_sha"), "build" + (" (modified)" if info.get("git_modified") else "")
+    except (OSError, ValueError):
+        return None, "unavailable"
+
+
+def host_info():
+    """CPU model and core counts of this host."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except OSError:
+        usable = None
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def gpu_state():
+    """Clocks, power and temperatures of device 0 from sysfs (read-only
+    files of its PCI device): the DPM level tables with the current level
+    marked '*', the power cap and current power, the clock and temperature
+    sensors. Missing files are left out."""
+    import glob
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+    d = f"/sys/bus/pci/devices/{bdf}"
+    out = {"pci": bdf}
+
+    def rd(path):
+        try:
+            return open(path).read().strip()
+        except OSError:
+            return None
+
+    for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk", "power_dpm_force_performance_level"):
+        v = rd(os.path.join(d, name))
+        if v is not None:
+            cur = [l for l in v.splitlines() if l.rstrip().endswith("*")]
+            out[name] = cur[0].rstrip(" *") if cur else v.replace("\n", "; ")
+    for hw in sorted(glob.glob(os.path.join(d, "hwmon", "hwmon*"))):
+        for f in sorted(os.listdir(hw)):
+            if f.endswith(("_input", "_average", "_cap", "_label")) and f.startswith(("power", "freq", "temp")):
+                v = rd(os.path.join(hw, f))
+                if v is not None:
+                    out[f] = v
+    if len(out) == 1:   # no sysfs view: ask the SMI tool once
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower", "--json"],
+                               capture_output=True, text=True, timeout=30)
+            out["rocm_smi"] = json.loads(r.stdout) if r.returncode == 0 else None
+        except (OSError, subprocess.SubprocessError, ValueError):
+            out["rocm_smi"] = None
+    return out
+
+
+# ------------------------------------------------------------ CPU leg --
+def _oracle_call(p, fmt, layout, keep, out=None, rows=None):
     import oracle
-    oracle.rmsnorm_quant_group(p["x"], p["gamma"], p["eps"], residual=p.get("residual"),
-                               group=128 if fmt == 0 else 32, fmt=fmt, scale_layout=layout, keep_bf16=keep)
+    x = p["x"] if rows is None else p["x"][:rows]
+    r = p.get("residual")
+    if r is not None and rows is not None:
+        r = r[:rows]
+    return oracle.rmsnorm_quant_group(x, p["gamma"], p["eps"], residual=r, group=128 if fmt == 0 else 32, fmt=fmt,
+                                      scale_layout=layout, keep_bf16=keep, out=out)
+
+
+def _oracle_out(p, fmt, layout, keep, rows):
+    import oracle
+    N = p["x"].shape[1]
+    return oracle.alloc_outputs(rows, N, 128 if fmt == 0 else 32, fmt, layout, "residual" in p, keep)
 
 
 def cpu_baseline(w, budget_s):
     """The CPU oracle as it stands on this host, over the workload's first
-    problem (its full rows), repeated until budget_s has passed (at least
-    once), with the OpenMP threads the host gives it; then once more on a
-    512-row sample with a single thread (in a child process, so the thread
-    count is set before the OpenMP runtime starts)."""
-    import statistics
+    problem (its full rows): the outputs are allocated and written once
+    before timing, so each timed call is the oracle's own work (its OpenMP
+    loop over rows, with the threads the host gives it), repeated until
+    budget_s has passed (at least three times); then a single-thread run on a
+    512-row sample (in a child process, so the thread count is set before the
+    OpenMP runtime starts), median of 5, also on preallocated outputs."""
     import oracle
     p = w.host[0]
     M, N = p["x"].shape
     keep = w.keep_bf16
+    out = _oracle_out(p, w.fmt, w.layout, keep, M)
+    _oracle_call(p, w.fmt, w.layout, keep, out)          # first call: code and data paged in
     times = []
-    while True:
+    while len(times) < 3 or sum(times) < budget_s:
         t0 = time.perf_counter()
-        _oracle_call(p, w.fmt, w.layout, keep)
+        _oracle_call(p, w.fmt, w.layout, keep, out)
         times.append(time.perf_counter() - t0)
-        if sum(times) >= budget_s:
-            break
-    sec = statistics.median(times)
+    sec = median(times)
     bytes_ = algorithmic_bytes(M, N, w.fmt, "residual" in p, keep)
-    out = {"value": round(bytes_ / sec / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+    res = {"value": round(bytes_ / sec / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
            "kind": "oracle", "mtok_per_s": round(M / sec / 1e6, 4),
-           "sample": f"the full {M}x{N} rows of the workload, {len(times)} run(s), median {sec:.3f} s"}
+           "sample": f"the full {M}x{N} rows of the workload, outputs preallocated, {len(times)} run(s) in "
+                     f"{sum(times):.1f} s, median {sec * 1e3:.2f} ms", **host_info()}
     rows = min(M, 512)
     code = ("import sys, time; sys.path.insert(0, %r)\n"
             "from fp4_quant_amd import inputs\nimport bench\n"
             "p = inputs.make_problem(%d, %d, seed_x=0, residual=%r, outliers=True)\n"
+            "out = bench._oracle_out(p, %d, %d, %r, %d)\n"
+            "bench._oracle_call(p, %d, %d, %r, out)\n"
             "ts = []\n"
-            "for _ in range(3):\n"
-            "    t0 = time.perf_counter(); bench._oracle_call(p, %d, %d, %r); ts.append(time.perf_counter() - t0)\n"
-            "print(sorted(ts)[1])\n") % (ROOT, rows, N, "residual" in p, w.fmt, w.layout, keep)
+            "for _ in range(5):\n"
+            "    t0 = time.perf_counter(); bench._oracle_call(p, %d, %d, %r, out); ts.append(time.perf_counter() - t0)\n"
+            "print(sorted(ts)[2])\n") % (ROOT, rows, N, "residual" in p, w.fmt, w.layout, keep, rows,
+                                         w.fmt, w.layout, keep, w.fmt, w.layout, keep)
     env = dict(os.environ, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
     if r.returncode == 0:
         s1 = float(r.stdout.strip().splitlines()[-1])
         b1 = algorithmic_bytes(rows, N, w.fmt, "residual" in p, keep)
-        out["single_thread"] = {"value": round(b1 / s1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+        res["single_thread"] = {"value": round(b1 / s1 / 1e9, 3), "unit": "GB/s", "cores": 1,
                                 "mtok_per_s": round(rows / s1 / 1e6, 4),
-                                "sample": f"{rows}x{N} rows, median of 3 runs, {s1:.3f} s"}
-    return out
+                                "sample": f"{rows}x{N} rows, outputs preallocated, median of 5 runs, "
+                                          f"{s1 * 1e3:.2f} ms"}
+        res["speedup_over_one_thread"] = round(res["value"] / res["single_thread"]["value"], 2)
+    return res
+
+
+def parity_summary(captured, rows=512):
+    """The GPU's outputs for the first rows of each timed workload (read back
+    after its timing, `captured`: name -> (workload, per-problem outputs))
+    against the oracle on the same input rows: bf16 rows, residual and scales
+    bit for bit, and the fraction of identical codes."""
+    import numpy as np
+    rep, ok = {}, True
+    for name, (w, got) in captured.items():
+        probs = []
+        for p, g in zip(w.host, got):
+            n = g["rows"]
+            want = _oracle_call(p, w.fmt, w.layout, w.keep_bf16, rows=n)
+            d = {"rows": n}
+            for k in ("residual_out", "bf16"):
+                if k in g:
+                    d[k + "_bit_exact"] = bool(np.array_equal(g[k], want[k]))
+                    ok &= d[k + "_bit_exact"]
+            ws = want["scale"]
+            d["scales_bit_exact"] = bool(np.array_equal(g["scale"].view(np.uint8), ws.view(np.uint8)))
+            d["codes_identical_frac"] = float(np.mean(g["q"] == want["q"]))
+            ok &= d["scales_bit_exact"] and d["codes_identical_frac"] == 1.0
+            probs.append(d)
+        rep[name] = probs
+    return {"rows_per_problem": rows, "all_bit_exact": ok, "workloads": rep}
 
 
 SPECS = {
@@ -451,6 +689,40 @@ SPECS = {
     "mxfp4_tiled32": ([dict(M=16384, N=7168, residual=True, keep_bf16=False)], 1, 1),
     "prefill_colscales": ([dict(M=8192, N=7168, residual=True, keep_bf16=True)], 0, 2),
 }
+SHORT = ("decode", "prefill512", "mla")
+
+
+def measure_config(name, args, captured, hashes):
+    """One fused workload: median of 5 windows after a long warm-up, its
+    plan, the floor of that plan, HIP-graph replay for the short ones."""
+    import torch
+    sp, f, lay = SPECS[name]
+    wk = Workload(name, sp, f, lay)
+    hashes[name] = wk.sha if len(wk.sha) > 1 else wk.sha[0]
+    steps, warm = max(50, args.steps // 2), max(300, args.warmup)
+    ws = time_workload(wk, steps, warm, windows=5)
+    pl = median(ws)
+    captured[name] = (wk, wk.capture())
+    gb = wk.bytes / (pl * 1e-3) / 1e9
+    rec = {"us_per_launch": round(pl * 1e3, 2), "us_windows": [round(t * 1e3, 2) for t in ws],
+           "GBps": round(gb, 1), "frac_of_peak": round(gb / HBM_PEAK_GBPS, 4),
+           "Mtok_per_s": round(wk.rows / (pl * 1e-3) / 1e6, 2), "bytes": wk.bytes,
+           "plan": [{k: l[k] for k in ("chunks_per_lane", "waves_per_row", "rows_per_workgroup", "row_splits",
+                                       "workgroups", "threads_per_workgroup")} for l in wk.plan()]}
+    tr = recorded_traffic(name)
+    if tr is not None:
+        rec["traffic"] = tr
+    if wk.bytes < 64 << 20:       # launch-bound sizes: also replayed from a HIP graph
+        pg = time_workload_graph(wk, 100)
+        rec["us_per_launch_graph"] = round(pg * 1e3, 2)
+        rec["GBps_graph"] = round(wk.bytes / (pg * 1e-3) / 1e9, 1)
+    fl = median(time_workload(FloorWorkload(wk), steps, warm, windows=5))
+    rec["floor_us"] = round(fl * 1e3, 2)
+    rec["floor_GBps"] = round(wk.bytes / (fl * 1e-3) / 1e9, 1)
+    rec["kernel_over_floor"] = round(pl / fl, 3)
+    del wk
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -458,13 +730,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed launches first; a few hundred let the clocks settle")
+                    help="untimed launches right before the timed window")
     ap.add_argument("--config", default="prefill", choices=sorted(SPECS) + sorted(GEMM_SPECS),
                     help="headline workload (a GEMM config only with --only-kernel)")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline budget (0 skips it)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline budget (0 skips the CPU leg)")
     ap.add_argument("--only-kernel", action="store_true",
                     help="launch only the headline workload (for profiler runs)")
+    ap.add_argument("--floor", action="store_true",
+                    help="with --only-kernel: launch the floor probe of the workload's plan instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="LAUNCHES",
                     help="only launch a 1 GiB nontemporal copy LAUNCHES times (counter calibration)")
     args = ap.parse_args()
@@ -491,42 +765,28 @@ def main():
         log(f"bench: {args.config}: {pg * 1e3:.2f} us per launch, {wg.bytes / (pg * 1e-3) / 1e9:.0f} GB/s")
         return
     specs, fmt, layout = SPECS[args.config]
-    log(f"bench: building workload {args.config}")
-    w = Workload(args.config, specs, fmt, layout)
-    log(f"bench: {len(w.sets)} rotating buffer sets, {w.bytes / 1e6:.1f} MB per step")
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    step_ms = time_workload(w, args.steps, args.warmup)
-    wall = time.perf_counter() - t_wall
-    gbps = w.bytes / (step_ms * 1e-3) / 1e9
-    log(f"bench: {args.config}: {step_ms * 1e3:.2f} us per launch, {gbps:.0f} GB/s")
     if args.only_kernel:
+        log(f"bench: building workload {args.config}")
+        w = Workload(args.config, specs, fmt, layout)
+        ms = time_workload(FloorWorkload(w) if args.floor else w, args.steps, args.warmup)
+        log(f"bench: {args.config}{' floor' if args.floor else ''}: {ms * 1e3:.2f} us per launch, "
+            f"{w.bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
         return
 
-    configs = {}
+    state = {"start": gpu_state()}
+    configs, captured, hashes = {}, {}, {}
     if not args.no_configs:
-        for name, (sp, f, lay) in SPECS.items():
+        for name in SPECS:
             if name == args.config:
                 continue
             log(f"bench: workload {name}")
-            wk = Workload(name, sp, f, lay)
-            pl = time_workload(wk, max(50, args.steps // 2), max(50, args.warmup))
-            configs[name] = {"us_per_launch": round(pl * 1e3, 2), "GBps": round(wk.bytes / (pl * 1e-3) / 1e9, 1),
-                             "frac_of_peak": round(wk.bytes / (pl * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                             "Mtok_per_s": round(wk.rows / (pl * 1e-3) / 1e6, 2), "bytes": wk.bytes}
-            tr = recorded_traffic(name)
-            if tr is not None:
-                configs[name]["traffic"] = tr
-            if wk.bytes < 64 << 20:       # launch-bound sizes: also replayed from a HIP graph
-                pg = time_workload_graph(wk, 100)
-                configs[name]["us_per_launch_graph"] = round(pg * 1e3, 2)
-                configs[name]["GBps_graph"] = round(wk.bytes / (pg * 1e-3) / 1e9, 1)
-            del wk
-            torch.cuda.empty_cache()
+            configs[name] = measure_config(name, args, captured, hashes)
         for name, g in GEMM_SPECS.items():
             log(f"bench: workload {name}")
             wk = GemmWorkload(name, **g)
-            pl = time_workload(wk, max(50, args.steps // 2), max(50, args.warmup))
+            hashes[name] = {k: inputs_sha(v) for k, v in wk.host.items()}
+            ws = time_workload(wk, max(50, args.steps // 2), max(300, args.warmup), windows=5)
+            pl = median(ws)
             pg = time_workload_graph(wk, 100)
             gb = wk.bytes / (pl * 1e-3) / 1e9
             configs[name] = {"M": g["M"], "N": g["N"], "K": g["K"],
@@ -534,8 +794,8 @@ def main():
                                             "bf16, quantized inside the GEMM",
                              "weights": ("MXFP4" if g["fmt"] == 1 else "FP8 e4m3fn, 128x128 block scales") +
                                         ", preshuffled",
-                             "us_per_launch": round(pl * 1e3, 2), "GBps": round(gb, 1),
-                             "frac_of_peak": round(gb / HBM_PEAK_GBPS, 4), "bytes": wk.bytes,
+                             "us_per_launch": round(pl * 1e3, 2), "us_windows": [round(t * 1e3, 2) for t in ws],
+                             "GBps": round(gb, 1), "frac_of_peak": round(gb / HBM_PEAK_GBPS, 4), "bytes": wk.bytes,
                              "us_per_launch_graph": round(pg * 1e3, 2),
                              "GBps_graph": round(wk.bytes / (pg * 1e-3) / 1e9, 1),
                              "TFLOPs": round(2 * g["M"] * g["N"] * g["K"] / (pl * 1e-3) / 1e12, 3)}
@@ -544,10 +804,9 @@ def main():
                 configs[name]["traffic"] = tr
             del wk
             torch.cuda.empty_cache()
-    if not args.no_configs:
         # the pages' choice by concurrency, on one GPU: fused norm + quant then
         # the GEMM of quantized activations, against the norm then the
-        # prequant GEMM (µs per step from HIP graph replays, 2 launches each)
+        # prequant GEMM (us per step from HIP graph replays, 2 launches each)
         pol = {}
         for M in (4, 16, 64, 256):
             row = {}
@@ -567,12 +826,12 @@ def main():
             sp, f, lay = SPECS[name]
             log(f"bench: unfused pair on the {name} batch")
             wu = UnfusedWorkload("unfused_" + name, sp, f, lay)
-            pu = time_workload(wu, max(50, args.steps // 2), max(50, args.warmup))
-            fused = step_ms if name == args.config else configs[name]["us_per_launch"] * 1e-3
+            pu = median(time_workload(wu, max(50, args.steps // 2), max(300, args.warmup), windows=3))
             rec = {"us_per_step": round(pu * 1e3, 2), "launches_per_step": 2,
                    "fused_algorithmic_GBps": round(wu.bytes / (pu * 1e-3) / 1e9, 1),
-                   "bytes_moved": wu.moved, "moved_GBps": round(wu.moved / (pu * 1e-3) / 1e9, 1),
-                   "fused_speedup": round(pu / fused, 3)}
+                   "bytes_moved": wu.moved, "moved_GBps": round(wu.moved / (pu * 1e-3) / 1e9, 1)}
+            if name in configs:
+                rec["fused_speedup"] = round(pu * 1e3 / configs[name]["us_per_launch"], 3)
             if wu.bytes < 64 << 20:       # launch-bound sizes: also replayed from a HIP graph
                 pg = time_workload_graph(wu, 100)
                 rec["us_per_step_graph"] = round(pg * 1e3, 2)
@@ -584,12 +843,45 @@ def main():
     ceil = ceilings()
     log(f"bench: stream ceilings (GB/s) {ceil}")
 
-    cpu = None
+    # The headline: W warm-up launches, then exactly K timed launches (the
+    # GPU has been busy with the table above, so its clocks have settled);
+    # four more windows of K launches follow for their spread.
+    log(f"bench: building workload {args.config}")
+    w = Workload(args.config, specs, fmt, layout)
+    hashes[args.config] = w.sha if len(w.sha) > 1 else w.sha[0]
+    log(f"bench: {len(w.sets)} rotating buffer sets, {w.bytes / 1e6:.1f} MB per step")
+    torch.cuda.synchronize()
+    state["before_timed"] = gpu_state()
+    t_wall = time.perf_counter()
+    step_ms = time_workload(w, args.steps, args.warmup)
+    wall = time.perf_counter() - t_wall
+    state["after_timed"] = gpu_state()
+    extra = time_workload(w, args.steps, 0, windows=4)
+    captured[args.config] = (w, w.capture())
+    gbps = w.bytes / (step_ms * 1e-3) / 1e9
+    log(f"bench: {args.config}: {step_ms * 1e3:.2f} us per launch, {gbps:.0f} GB/s")
+    fl = median(time_workload(FloorWorkload(w), max(50, args.steps), max(300, args.warmup), windows=5))
+
+    cpu, parity = None, None
     if args.cpu_seconds > 0:
         log("bench: CPU oracle baseline")
         cpu = cpu_baseline(w, args.cpu_seconds)
+        log("bench: parity of the timed workloads' first rows against the oracle")
+        parity = parity_summary(captured)
+        log(f"bench: parity all bit-exact: {parity['all_bit_exact']}")
 
     M, N = specs[0]["M"], specs[0]["N"]
+    mix = "fused_mix" if fmt == 0 else "fused_mix_mxfp4"
+    probes = {k: v for k, v in ceil.items() if k.startswith(mix) and (fmt == 1) == k.endswith("mxfp4")}
+    probes["plan_floor"] = round(w.bytes / (fl * 1e-3) / 1e9, 1)
+    best = max(probes, key=probes.get)
+    if "mxfp4_row" in configs:
+        c = configs["mxfp4_row"]
+        mxp = {"flat": ceil["fused_mix_mxfp4"], "plan_floor": c["floor_GBps"]}
+        c["achievable"] = {"probes_GBps": mxp, "best": max(mxp, key=mxp.get),
+                           "frac_of_best": round(c["GBps"] / max(mxp.values()), 4),
+                           "frac_of_peak": c["frac_of_peak"]}
+    git_sha, git_from = git_identity()
     out = {
         "metric": "achieved HBM GB/s (% of MI355X peak) and Mtokens/s at N=7168, group=128",
         "value": round(gbps, 1),
@@ -614,16 +906,28 @@ def main():
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": recorded_traffic(args.config),
                      "kernel": kernel_name(fmt, N, w.rows, specs[0]["residual"]),
                      "bytes_per_launch": w.bytes,
-                     "us_per_launch": round(step_ms * 1e3, 2)},
+                     "us_per_launch": round(step_ms * 1e3, 2),
+                     "us_windows_after": [round(t * 1e3, 2) for t in extra],
+                     "achievable": {"probes_GBps": probes, "best": best, "GBps": probes[best],
+                                    "frac_of_peak": round(probes[best] / HBM_PEAK_GBPS, 4),
+                                    "frac_of_achievable": round(gbps / probes[best], 4)}},
         "stream_ceilings_GBps": ceil,
-        "frac_of_mix_ceiling": round(gbps / ceil["fused_mix"], 4) if args.config == "prefill" else None,
-        "mxfp4_frac_of_mix_ceiling": (round(configs["mxfp4_row"]["GBps"] / ceil["fused_mix_mxfp4"], 4)
-                                      if "mxfp4_row" in configs else None),
         "cpu_baseline": cpu,
+        "parity": parity,
         "configs": configs,
+        "inputs_sha256": hashes,
+        "git_sha": git_sha,
+        "git_sha_from": git_from,
+        "source_sha256": source_sha256(),
+        "gpu_state": state,
         "timed_wall_s": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
+
+
+def inputs_sha(a):
+    from fp4_quant_amd import inputs
+    return inputs.sha256(a)
 
 
 if __name__ == "__main__":

@@ -55,10 +55,25 @@ class rmsq_problem(C.Structure):
                 ("ldb", C.c_int64)]
 
 
-EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "add_rmsnorm",
-           "dynamic_per_group_scaled_quant", "rmsq_device_supported",
-           "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_set_shape",
-           "rmsq_query_shape", "rmsq_set_row_group", "rmsq_set_wave_rows", "rmsq_set_row_splits",
+class rmsq_launch_hint(C.Structure):
+    _fields_ = [("chunks_per_lane", C.c_int32), ("waves_per_row", C.c_int32), ("row_group", C.c_int32),
+                ("rows_per_workgroup", C.c_int32), ("row_splits", C.c_int32)]
+
+
+class rmsq_launch_info(C.Structure):
+    _fields_ = [("problems", C.c_int32), ("rows", C.c_int32), ("chunks_per_lane", C.c_int32),
+                ("waves_per_row", C.c_int32), ("rows_per_workgroup", C.c_int32), ("row_splits", C.c_int32),
+                ("row_group", C.c_int32), ("threads_per_workgroup", C.c_int32), ("workgroups", C.c_int64),
+                ("residual", C.c_int32), ("reserved", C.c_int32)]
+
+
+class rmsq_launch_plan(C.Structure):
+    _fields_ = [("launches", C.c_int32), ("reserved", C.c_int32), ("launch", rmsq_launch_info * 2)]
+
+
+EXPORTS = ("rmsnorm_quant_group", "rmsnorm_quant_group_multi", "rmsnorm_quant_group_multi_ex", "rmsq_plan_launch",
+           "add_rmsnorm", "dynamic_per_group_scaled_quant", "rmsq_device_supported",
+           "rmsq_scale_bytes", "rmsq_status_string", "rmsq_last_error", "rmsq_query_shape",
            "gemm_a16wfp4_prequant", "mxfp4_weight_preshuffle", "gemm_a16w8_prequant", "fp8_weight_preshuffle",
            "gemm_afp4wfp4", "gemm_a8w8_blockscale")
 
@@ -90,14 +105,11 @@ def lib() -> C.CDLL:
         L.rmsq_status_string.argtypes = [i32]
         L.rmsq_last_error.restype = C.c_char_p
         L.rmsq_last_error.argtypes = []
-        L.rmsq_set_shape.restype = None
-        L.rmsq_set_shape.argtypes = [i32, i32]
-        L.rmsq_set_row_group.restype = None
-        L.rmsq_set_row_group.argtypes = [i32]
-        L.rmsq_set_wave_rows.restype = None
-        L.rmsq_set_wave_rows.argtypes = [i32]
-        L.rmsq_set_row_splits.restype = None
-        L.rmsq_set_row_splits.argtypes = [i32]
+        L.rmsnorm_quant_group_multi_ex.restype = i32
+        L.rmsnorm_quant_group_multi_ex.argtypes = [C.POINTER(rmsq_problem), i32, C.POINTER(rmsq_launch_hint), p]
+        L.rmsq_plan_launch.restype = i32
+        L.rmsq_plan_launch.argtypes = [C.POINTER(rmsq_problem), i32, C.POINTER(rmsq_launch_hint),
+                                       C.POINTER(rmsq_launch_plan)]
         L.rmsq_query_shape.restype = i32
         L.rmsq_query_shape.argtypes = [i64, i64, C.POINTER(i32), C.POINTER(i32)]
         L.gemm_a16wfp4_prequant.restype = i32
@@ -166,12 +178,38 @@ def _check_rows(t, M, N, name):
                          f"(got {tuple(t.shape)} {t.dtype}, strides {tuple(t.stride())})")
 
 
+def _check_quant_outputs(out_q, out_scale, M, N, fmt, scale_layout):
+    """out_q: M*N (FP8) or M*N/2 (MXFP4) dense uint8 code bytes; out_scale:
+    dense float32 (FP8) or uint8 (MXFP4) scales holding at least the bytes the
+    layout needs. The C ABI takes bare pointers and cannot see a buffer's
+    size, so a short one is refused here, before any address is taken."""
+    import torch
+    if M == 0:
+        return
+    if fmt not in _GROUP:
+        return   # the library reports the unknown format
+    group = _GROUP[fmt]
+    if N % group:
+        return   # the library reports the shape
+    want_q = M * N if fmt == FMT_FP8_E4M3FN else M * N // 2
+    if out_q is None or out_q.dtype != torch.uint8 or out_q.numel() != want_q or not out_q.is_contiguous():
+        raise ValueError(f"out_q must be {want_q} contiguous uint8 code bytes"
+                         + ("" if out_q is None else f" (got {out_q.numel()} {out_q.dtype})"))
+    dt = torch.float32 if fmt == FMT_FP8_E4M3FN else torch.uint8
+    need = rmsq_scale_bytes(M, N, group, fmt, scale_layout)
+    if out_scale is None or out_scale.dtype != dt or not out_scale.is_contiguous() or (
+            need and out_scale.numel() * out_scale.element_size() < need):
+        raise ValueError(f"out_scale must be contiguous {dt} holding at least {need} bytes for scale layout "
+                         f"{scale_layout}" + ("" if out_scale is None else
+                                              f" (got {out_scale.numel()} {out_scale.dtype})"))
+
+
 def make_problem(x, gamma, eps, out_q, out_scale, *, residual_in=None, residual_out=None,
                  out_bf16=None, fmt=FMT_FP8_E4M3FN, scale_layout=SCALE_ROW_MAJOR) -> rmsq_problem:
-    """One problem for ``rmsnorm_quant_group_multi``. The bf16 tensors are
-    checked for dtype and shape here (the library checks strides, alignment,
-    overlaps and the formats); residual_in and residual_out share one row
-    stride, which the library applies to both."""
+    """One problem for ``rmsnorm_quant_group_multi``. The tensors are checked
+    here for dtype, shape, size and device (the library checks strides,
+    alignment, overlaps and the formats); residual_in and residual_out share
+    one row stride, which the library applies to both."""
     import torch
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, N]")
@@ -187,6 +225,12 @@ def make_problem(x, gamma, eps, out_q, out_scale, *, residual_in=None, residual_
             raise ValueError("residual_out must have the row stride of residual_in")
     if out_bf16 is not None:
         _check_rows(out_bf16, M, N, "out_bf16")
+    _check_quant_outputs(out_q, out_scale, M, N, fmt, scale_layout)
+    if M:
+        for name, t in (("gamma", gamma), ("residual_in", residual_in), ("residual_out", residual_out),
+                        ("out_bf16", out_bf16), ("out_q", out_q), ("out_scale", out_scale)):
+            if t is not None and t.device != x.device:
+                raise ValueError(f"{name} is on {t.device}, x on {x.device}")
     return rmsq_problem(x=_ptr(x), ldx=_ld(x), residual_in=_ptr(residual_in),
                         residual_out=_ptr(residual_out), ldr=_ld(residual_in), gamma=_ptr(gamma),
                         eps=float(eps), M=M, N=N, group=_GROUP.get(fmt, 0), fmt=fmt,
@@ -200,13 +244,32 @@ def problem_array(problems):
     return (rmsq_problem * len(problems))(*problems)
 
 
-def rmsnorm_quant_group_multi(problems, stream=None) -> None:
+def launch_hint(J=0, W=0, row_group=0, rows_per_workgroup=0, row_splits=0) -> rmsq_launch_hint:
+    """A per-call launch hint (0 = the library's choice for that field)."""
+    return rmsq_launch_hint(int(J), int(W), int(row_group), int(rows_per_workgroup), int(row_splits))
+
+
+def rmsnorm_quant_group_multi(problems, stream=None, hint=None) -> None:
     """Up to four independent problems (``rmsq_problem`` structs from
     ``make_problem``, or an array from ``problem_array``) in one kernel
     launch. ``stream``: a torch stream, a raw hipStream_t handle, or None for
-    torch's current stream."""
+    torch's current stream. ``hint``: an optional ``launch_hint`` for this
+    call only (``rmsnorm_quant_group_multi_ex``)."""
     arr = problems if isinstance(problems, C.Array) else problem_array(problems)
-    _check(lib().rmsnorm_quant_group_multi(arr, len(arr), _stream(stream)))
+    if hint is None:
+        _check(lib().rmsnorm_quant_group_multi(arr, len(arr), _stream(stream)))
+    else:
+        _check(lib().rmsnorm_quant_group_multi_ex(arr, len(arr), C.byref(hint), _stream(stream)))
+
+
+def rmsq_plan_launch(problems, hint=None):
+    """The launches the library would make for these problems (and hint),
+    as a list of dicts, without launching anything (no GPU needed)."""
+    arr = problems if isinstance(problems, C.Array) else problem_array(problems)
+    plan = rmsq_launch_plan()
+    _check(lib().rmsq_plan_launch(arr, len(arr), C.byref(hint) if hint is not None else None, C.byref(plan)))
+    return [{f: getattr(plan.launch[k], f) for f, _ in rmsq_launch_info._fields_ if f != "reserved"}
+            for k in range(plan.launches)]
 
 
 def add_rmsnorm(x, residual_in, gamma, eps, M, N, residual_out, out_bf16, stream=None) -> None:
@@ -277,22 +340,6 @@ def rmsq_device_supported(device: int = 0) -> bool:
 
 def rmsq_scale_bytes(M, N, group, fmt, scale_layout=SCALE_ROW_MAJOR) -> int:
     return int(lib().rmsq_scale_bytes(int(M), int(N), int(group), int(fmt), int(scale_layout)))
-
-
-def rmsq_set_shape(J: int = 0, W: int = 0) -> None:
-    lib().rmsq_set_shape(int(J), int(W))
-
-
-def rmsq_set_row_group(g: int = 0) -> None:
-    lib().rmsq_set_row_group(int(g))
-
-
-def rmsq_set_wave_rows(R: int = 0) -> None:
-    lib().rmsq_set_wave_rows(int(R))
-
-
-def rmsq_set_row_splits(S: int = 0) -> None:
-    lib().rmsq_set_row_splits(int(S))
 
 
 def rmsq_query_shape(N: int, rows: int):

@@ -41,7 +41,27 @@ def build(verbose: bool = False, extra=()) -> str:
     if verbose and msgs.strip():
         print(msgs)
     os.replace(LIB + ".tmp", LIB)
+    write_build_info()
     return LIB
+
+
+def write_build_info() -> None:
+    """Record the checkout's HEAD next to the library (build_info.json, not
+    versioned), so a copy of the tree without its git metadata can still name
+    the commit it was built from."""
+    import json
+    info = {"git_sha": None, "git_modified": None}
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=20)
+        if r.returncode == 0:
+            info["git_sha"] = r.stdout.strip()
+            d = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=20)
+            info["git_modified"] = bool(d.stdout.strip())
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(os.path.join(HERE, "build_info.json"), "w") as f:
+        json.dump(info, f)
 
 
 if __name__ == "__main__":

@@ -251,21 +251,44 @@ rmsq_status launch_fmt(const Plan& P, hipStream_t stream) {
   return RMSQ_OK;
 }
 
-// Launch-shape override for measurement sweeps, set by rmsq_set_shape
-// (0, 0 = automatic choice).
-std::atomic<int> g_force_J{0}, g_force_W{0}, g_force_G{0}, g_force_R{0}, g_force_S{0};
-
 bool compiled_J(int J) {
   for (int k : kJs)
     if (k == J) return true;
   return false;
 }
 
-rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) {
+// The optional per-call launch hint, checked before anything is planned.
+rmsq_status check_hint(const rmsq_launch_hint* h) {
+  if (!h) return RMSQ_OK;
+  if ((h->chunks_per_lane == 0) != (h->waves_per_row == 0))
+    return fail(RMSQ_ERR_INVALID_ARG, "hint: chunks_per_lane and waves_per_row are set together (or both 0)");
+  if (h->chunks_per_lane != 0 &&
+      (!compiled_J(h->chunks_per_lane) || h->waves_per_row < 1 || h->waves_per_row > rmsq::max_waves(h->chunks_per_lane)))
+    return fail(RMSQ_ERR_INVALID_ARG, "hint: no launch shape of %d chunks per lane x %d waves", h->chunks_per_lane,
+                h->waves_per_row);
+  if (h->row_group < 0 || h->row_group > 64)
+    return fail(RMSQ_ERR_INVALID_ARG, "hint: row_group %d outside 0..64", h->row_group);
+  if (h->rows_per_workgroup < 0 || h->rows_per_workgroup > rmsq::kMaxWaves)
+    return fail(RMSQ_ERR_INVALID_ARG, "hint: rows_per_workgroup %d outside 0..%d", h->rows_per_workgroup,
+                rmsq::kMaxWaves);
+  if (h->row_splits < 0 || h->row_splits > kMaxSplits)
+    return fail(RMSQ_ERR_INVALID_ARG, "hint: row_splits %d outside 0..%d", h->row_splits, kMaxSplits);
+  return RMSQ_OK;
+}
+
+// Validate the problems and plan their launches (one for the problems with
+// a residual, one for those without; a set that mixes the two takes two
+// launches, in that order). Everything here is host arithmetic on the
+// arguments: no HIP call, no state outside *plans.
+rmsq_status plan(const rmsq_problem* ps, int32_t count, Mode mode, const rmsq_launch_hint* hint, Plan plans[2],
+                 int* np_out) {
   g_err[0] = 0;
+  *np_out = 0;
   if (!ps) return fail(RMSQ_ERR_INVALID_ARG, "problems is NULL");
   if (count < 1 || count > RMSQ_MAX_PROBLEMS)
     return fail(RMSQ_ERR_INVALID_ARG, "count = %d outside 1..%d", count, RMSQ_MAX_PROBLEMS);
+  if (const rmsq_status s = check_hint(hint); s != RMSQ_OK) return s;
+  const rmsq_launch_hint h = hint ? *hint : rmsq_launch_hint{0, 0, 0, 0, 0};
   Range rs[RMSQ_MAX_PROBLEMS * 7];
   int nr = 0;
   for (int i = 0; i < count; ++i) {
@@ -274,10 +297,6 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
   }
   if (const rmsq_status s = check_overlaps(rs, nr); s != RMSQ_OK) return s;
 
-  // One launch for the problems with a residual and one for those without
-  // (a set that mixes the two takes two launches, in that order). Both are
-  // planned and checked before either is enqueued.
-  Plan plans[2];
   int np = 0;
   for (int with_res = 1; with_res >= 0; --with_res) {
     Plan& P = plans[np];
@@ -314,10 +333,12 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
 
     int J, W;
     pick_shape(Cmax, rows, &J, &W);
-    const int fJ = g_force_J.load(), fW = g_force_W.load();
-    if (compiled_J(fJ) && fW > 0 && fW <= rmsq::max_waves(fJ) && (int64_t)fJ * fW * 64 >= Cmax) {
-      J = fJ;
-      W = fW;
+    if (h.chunks_per_lane != 0) {
+      if ((int64_t)h.chunks_per_lane * h.waves_per_row * 64 < Cmax)
+        return fail(RMSQ_ERR_INVALID_ARG, "hint: %d chunks per lane x %d waves do not cover rows of %lld elements",
+                    h.chunks_per_lane, h.waves_per_row, (long long)Cmax * 8);
+      J = h.chunks_per_lane;
+      W = h.waves_per_row;
     }
     // Row grouping per XCD (measured): 16 rows when a problem writes tiled or
     // column-major scales (neighbouring rows' scales share lines there; half a
@@ -326,19 +347,16 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
     bool grouped = false;
     for (int i = 0; i < n; ++i) grouped |= L.p[i].layout != RMSQ_SCALE_ROW_MAJOR;
     int lg = grouped ? 4 : 0;
-    if (const int fG = g_force_G.load(); fG > 0) {
+    if (h.row_group > 0) {
       lg = 0;
-      while ((2 << lg) <= fG) ++lg;   // largest power of two <= fG
+      while ((2 << lg) <= h.row_group) ++lg;   // largest power of two <= the hint
     }
     // Rows that fit one wave are packed several per workgroup once there are
     // enough of them to fill the machine (a CU holds only so many
     // workgroups, so one-wave workgroups leave wave slots empty).
     int R = 1;
-    if (W == 1 && J <= 4) {
-      const int fR = g_force_R.load();
-      R = fR > 0 ? fR : (rows >= 4 * kComputeUnits ? kWaveRowsPerBlock : 1);
-      if (R > rmsq::kMaxWaves) R = rmsq::kMaxWaves;
-    }
+    if (W == 1 && J <= 4) R = h.rows_per_workgroup > 0 ? h.rows_per_workgroup
+                                                       : (rows >= 4 * kComputeUnits ? kWaveRowsPerBlock : 1);
     int lgR = 0;
     while ((2 << lgR) <= R) ++lgR;
     L.row_group_log2 = R > 1 ? (lg > lgR ? lg - lgR : 0) : lg;   // groups of workgroups when packed
@@ -351,10 +369,9 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
     for (int i = 0; i < n; ++i) in_place |= L.p[i].r != nullptr && L.p[i].r == L.p[i].h;
     L.splits_log2 = 0;
     if (R == 1 && !in_place) {
-      const int fS = g_force_S.load();
       int S = 1;
-      if (fS > 0)
-        while (S * 2 <= fS) S *= 2;   // largest power of two <= fS
+      if (h.row_splits > 0)
+        while (S * 2 <= h.row_splits) S *= 2;   // largest power of two <= the hint
       else
         while (S < kMaxSplits && rows * S * 2 <= kComputeUnits) S *= 2;
       const int64_t q = mode == Mode::kNormOnly ? 1 : ps[0].fmt == RMSQ_FMT_FP8_E4M3FN ? 16 : 4;
@@ -374,6 +391,14 @@ rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, void* stream) 
                   (long long)rows, (long long)Cmax * 8, (unsigned long long)P.grid.x * P.block.x);
     ++np;
   }
+  *np_out = np;
+  return RMSQ_OK;
+}
+
+rmsq_status run(const rmsq_problem* ps, int32_t count, Mode mode, const rmsq_launch_hint* hint, void* stream) {
+  Plan plans[2];
+  int np = 0;
+  if (const rmsq_status s = plan(ps, count, mode, hint, plans, &np); s != RMSQ_OK) return s;
   if (np == 0) return RMSQ_OK;   // every problem has M == 0
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
@@ -447,11 +472,41 @@ rmsq_status rmsnorm_quant_group(const void* x, const void* residual_in, const vo
   p.out_q = out_q;
   p.out_scale = out_scale;
   p.out_bf16 = out_bf16_or_null;
-  return run(&p, 1, Mode::kFused, stream);
+  return run(&p, 1, Mode::kFused, nullptr, stream);
 }
 
 rmsq_status rmsnorm_quant_group_multi(const rmsq_problem* problems, int32_t count, void* stream) {
-  return run(problems, count, Mode::kFused, stream);
+  return run(problems, count, Mode::kFused, nullptr, stream);
+}
+
+rmsq_status rmsnorm_quant_group_multi_ex(const rmsq_problem* problems, int32_t count, const rmsq_launch_hint* hint,
+                                         void* stream) {
+  return run(problems, count, Mode::kFused, hint, stream);
+}
+
+rmsq_status rmsq_plan_launch(const rmsq_problem* problems, int32_t count, const rmsq_launch_hint* hint,
+                             rmsq_launch_plan* out) {
+  if (!out) return fail(RMSQ_ERR_INVALID_ARG, "plan output is NULL");
+  std::memset(out, 0, sizeof *out);
+  Plan plans[2];
+  int np = 0;
+  if (const rmsq_status s = plan(problems, count, Mode::kFused, hint, plans, &np); s != RMSQ_OK) return s;
+  out->launches = np;
+  for (int k = 0; k < np; ++k) {
+    const Plan& P = plans[k];
+    rmsq_launch_info& d = out->launch[k];
+    d.problems = P.L.count;
+    d.rows = P.L.rows;
+    d.chunks_per_lane = P.J;
+    d.waves_per_row = P.W;
+    d.rows_per_workgroup = P.R;
+    d.row_splits = 1 << P.L.splits_log2;
+    d.row_group = 1 << P.L.row_group_log2;
+    d.workgroups = (int64_t)P.grid.x;
+    d.threads_per_workgroup = (int32_t)P.block.x;
+    d.residual = P.L.p[0].r != nullptr;
+  }
+  return RMSQ_OK;
 }
 
 rmsq_status add_rmsnorm(const void* x, const void* residual_in, const void* gamma, float eps, int64_t M, int64_t N,
@@ -466,7 +521,7 @@ rmsq_status add_rmsnorm(const void* x, const void* residual_in, const void* gamm
   p.M = M;
   p.N = N;
   p.out_bf16 = out_bf16;
-  return run(&p, 1, Mode::kNormOnly, stream);
+  return run(&p, 1, Mode::kNormOnly, nullptr, stream);
 }
 
 rmsq_status dynamic_per_group_scaled_quant(const void* x, int64_t M, int64_t N, int32_t group, int32_t fmt,
@@ -505,17 +560,6 @@ const char* rmsq_status_string(rmsq_status s) {
 }
 
 const char* rmsq_last_error(void) { return g_err; }
-
-void rmsq_set_shape(int32_t J, int32_t W) {
-  g_force_J.store(J);
-  g_force_W.store(W);
-}
-
-void rmsq_set_row_group(int32_t g) { g_force_G.store(g > 0 && g <= 64 ? g : 0); }
-
-void rmsq_set_wave_rows(int32_t R) { g_force_R.store(R > 0 && R <= rmsq::kMaxWaves ? R : 0); }
-
-void rmsq_set_row_splits(int32_t S) { g_force_S.store(S > 0 && S <= kMaxSplits ? S : 0); }
 
 int32_t rmsq_query_shape(int64_t N, int64_t rows, int32_t* J, int32_t* W) {
   if (N <= 0 || N % 8 || N > RMSQ_N_MAX || rows < 0 || !J || !W) return RMSQ_ERR_INVALID_ARG;

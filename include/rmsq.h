@@ -23,9 +23,11 @@
  *
  * Conventions shared by every entry point:
  *  - Data pointers are DEVICE pointers owned by the caller. The library
- *    allocates no device memory, keeps no per-call state, and never
- *    synchronizes the host: work is enqueued on `stream` (a hipStream_t;
- *    NULL is the default stream) and the call returns.
+ *    allocates no device memory and never synchronizes the host: work is
+ *    enqueued on `stream` (a hipStream_t; NULL is the default stream) and
+ *    the call returns. The only state it keeps between calls is a cached
+ *    per-device answer to "is this a gfx950"; a call's launch plan depends on
+ *    its own arguments only (see rmsq_launch_hint).
  *  - bf16 tensors are row-major with a row stride (ld, in elements) that is a
  *    multiple of 8 and >= N; bf16 pointers are 16-byte aligned. Codes and
  *    scales are dense: codes [M, N] bytes (FP8) or [M, N/2] (MXFP4); scales
@@ -42,8 +44,9 @@
  *    512 elements, 4.1M rows of any width always fit) returns
  *    RMSQ_ERR_UNSUPPORTED; split such a batch into several calls.
  *  - Non-finite inputs are outside the contract (no fault, undefined values).
- *  - Thread safety: calls are re-entrant; calls on different streams may run
- *    concurrently.
+ *  - Thread safety: calls are re-entrant and may come from any number of
+ *    host threads at once; calls on different streams may run concurrently.
+ *    The message of rmsq_last_error is kept per thread.
  */
 #ifndef RMSQ_H
 #define RMSQ_H
@@ -167,6 +170,76 @@ typedef struct rmsq_problem {
  * host during the call and may be freed when it returns.
  */
 rmsq_status rmsnorm_quant_group_multi(const rmsq_problem* problems, int32_t count, void* stream);
+
+/*
+ * Optional per-call launch hint for rmsnorm_quant_group_multi_ex and
+ * rmsq_plan_launch, for measurement sweeps and callers that tune their own
+ * shapes. A zero field leaves that choice to the library. Results never
+ * depend on the launch plan (every plan computes the same bytes); only the
+ * speed does. The hint applies to the one call it is passed to: the library
+ * keeps no launch state between calls.
+ *  chunks_per_lane, waves_per_row  J 16-byte chunks per lane (1, 2, 3, 4, 7,
+ *        8 or 14) and W waves per row (1..16; 1..4 when J >= 7), set
+ *        together; J*W*64 chunks must cover the widest row of the launch.
+ *  row_group  consecutive rows kept on one XCD (1..64, rounded down to a
+ *        power of two; 1 = plain dispatch order). Automatic: 16 when a
+ *        problem writes tiled or column-major scales, else 1.
+ *  rows_per_workgroup  rows packed one per wave per workgroup when a row fits
+ *        one wave (1..16). Automatic: 8 once a launch has at least 1024 rows,
+ *        else 1. Not used when rows span several waves.
+ *  row_splits  workgroups sharing each row (1..8, rounded down to a power of
+ *        two; each computes the row's statistics and normalizes / quantizes
+ *        its own share of the groups). Automatic: the largest power of two
+ *        S <= 8 with rows * S <= 256 for launches of at most 128 rows, else 1.
+ *        Rows are never split when a problem's residual is updated in place,
+ *        when rows are packed per workgroup, or below one group per split.
+ * A field outside its range, or a J x W that does not cover a row, gives
+ * RMSQ_ERR_INVALID_ARG (nothing is launched).
+ */
+typedef struct rmsq_launch_hint {
+    int32_t chunks_per_lane;
+    int32_t waves_per_row;
+    int32_t row_group;
+    int32_t rows_per_workgroup;
+    int32_t row_splits;
+} rmsq_launch_hint;
+
+/* rmsnorm_quant_group_multi with an optional launch hint (NULL: the
+ * library's own plan, exactly as rmsnorm_quant_group_multi). Same contract,
+ * errors and stream semantics. */
+rmsq_status rmsnorm_quant_group_multi_ex(const rmsq_problem* problems, int32_t count, const rmsq_launch_hint* hint,
+                                         void* stream);
+
+/* One planned launch of the fused kernel. */
+typedef struct rmsq_launch_info {
+    int32_t problems;               /* problems in this launch                  */
+    int32_t rows;                   /* rows over those problems                 */
+    int32_t chunks_per_lane;        /* J                                        */
+    int32_t waves_per_row;          /* W                                        */
+    int32_t rows_per_workgroup;     /* R (1: one row, or a share of one, per workgroup) */
+    int32_t row_splits;             /* S workgroups per row                     */
+    int32_t row_group;              /* consecutive rows kept on one XCD         */
+    int32_t threads_per_workgroup;
+    int64_t workgroups;
+    int32_t residual;               /* 1 if this launch's problems have a residual */
+    int32_t reserved;
+} rmsq_launch_info;
+
+typedef struct rmsq_launch_plan {
+    int32_t launches;               /* 0 (every M is 0), 1, or 2 (a set mixing problems with and
+                                       without a residual: those with one first) */
+    int32_t reserved;
+    rmsq_launch_info launch[2];
+} rmsq_launch_plan;
+
+/* The launches rmsnorm_quant_group_multi_ex would make for these arguments,
+ * written to *plan, without launching anything and without any HIP call
+ * (host arithmetic only, so it runs without a GPU and from any thread).
+ * Validates exactly as the launching call does and returns its status; on
+ * an error *plan is zeroed. The problems' pointers are checked (alignment,
+ * overlap) but never dereferenced. */
+rmsq_status rmsq_plan_launch(const rmsq_problem* problems, int32_t count, const rmsq_launch_hint* hint,
+                             rmsq_launch_plan* plan);
 
 /*
  * The two kernels the fused call replaces, for callers that need them apart
@@ -340,37 +413,7 @@ const char* rmsq_status_string(rmsq_status s);
 /* Message of the last validation or HIP error on the calling thread, or "". */
 const char* rmsq_last_error(void);
 
-/* Measurement hook: force the launch shape of later calls in this process:
- * J 16-byte chunks per lane (one of 1, 2, 3, 4, 7, 8, 14) and W waves (1..16)
- * per row. Shapes that cannot cover a row, and (0, 0), restore the automatic
- * choice. Results do not depend on the shape. */
-void rmsq_set_shape(int32_t J, int32_t W);
-
-/* Measurement hook: force the number of consecutive rows kept together on one
- * XCD (1..64, rounded down to a power of two; 1 = plain dispatch order) for
- * later calls in this process;
- * 0 restores the automatic choice (16 when a problem uses a tiled or
- * column-major scale layout, else 1). Results do not depend on it. */
-void rmsq_set_row_group(int32_t g);
-
-/* Measurement hook: rows that one wave covers (a shape with W = 1) are packed
- * R per workgroup, one per wave, for later calls in this process: R in
- * 2..16, or 1 for one row per workgroup; 0 restores the automatic choice
- * (R = 8 once a launch has at least 1024 rows, else 1). Results do not
- * depend on it. */
-void rmsq_set_wave_rows(int32_t R);
-
-/* Measurement hook: each row is split over S workgroups (S in 1..8, rounded
- * down to a power of two; each
- * computes the row's statistics and normalizes / quantizes its own share of
- * the groups) for later calls in this process; 0 restores the automatic
- * choice (the largest power of two S <= 8 with rows * S <= 256, one
- * workgroup per compute unit, for launches of at most 128 rows; 1 above).
- * Rows are never split when a problem's residual is updated in place.
- * Results do not depend on it. */
-void rmsq_set_row_splits(int32_t S);
-
-/* The launch shape the library picks (without an override) for rows of N
+/* The launch shape the library picks (without a hint) for rows of N
  * elements, the widest problem of a call, and `rows` rows in total: J chunks
  * of 8 elements per lane and W waves per workgroup (one workgroup per row).
  * RMSQ_ERR_INVALID_ARG for N outside (0, RMSQ_N_MAX] or not a multiple of 8. */

@@ -12,7 +12,7 @@ LIB = os.path.join(HERE, "libconvert_probe.so")
 def build(verbose: bool = False) -> str:
     sys.path.insert(0, ROOT)
     from fp4_quant_amd.build import HIPCC, HIP_FLAGS, CSRC
-    cmd = [HIPCC, *HIP_FLAGS, "-I", CSRC, os.path.join(HERE, "convert_probe.hip"),
+    cmd = [HIPCC, *HIP_FLAGS, "-I", CSRC, "-I", os.path.join(ROOT, "include"), os.path.join(HERE, "convert_probe.hip"),
            os.path.join(HERE, "stream_probe.hip"), "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rmsq.h"
+#include "rmsq_kernel.h"
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -193,6 +196,91 @@ __global__ void __launch_bounds__(1024) k_rows_pol(const u32x4* x, const u32x4* 
   }
 }
 
+// The fused kernel's memory skeleton for one launch plan, with no arithmetic:
+// the same grid, row / split / packed-wave mapping, loads (x, gamma, r, in the
+// same order, 16 bytes per lane), one cross-wave exchange through LDS with the
+// workgroup barrier, and the same stores (h, bf16 rows, codes, one scale per
+// group) - the values stored are bit mixes of the inputs. Its time is the
+// floor of a launch of that plan: what is left when the statistics, the
+// normalization and the quantization cost nothing.
+template <int FMT, int J, bool RES, bool WAVE_ROWS>
+__global__ void __launch_bounds__(64 * rmsq::max_waves(J))
+k_plan_floor(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t rb1, int32_t rb2, int32_t rb3,
+             int32_t threads, int32_t blocks, const rmsq::Launch L) {
+  __shared__ uint32_t red[rmsq::kMaxWaves];
+  int32_t row, split = 0;
+  if constexpr (WAVE_ROWS) {
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+    row = rmsq::row_of_block((int32_t)blockIdx.x, blocks, lg) * (threads >> 6) + wave;
+    if (row >= rows) return;
+  } else {
+    const int32_t b = (int32_t)blockIdx.x;
+    split = slg > 0 ? (b >> 3) & ((1 << slg) - 1) : 0;
+    row = slg > 0 ? ((b >> (3 + slg)) << 3) | (b & 7) : rmsq::row_of_block(b, rows, lg);
+    if (row >= rows) return;
+  }
+  const int pi = (count > 1 && row >= rb1) + (count > 2 && row >= rb2) + (count > 3 && row >= rb3);
+  const rmsq::Problem& P = L.p[pi];
+  const int64_t m = row - (pi == 0 ? 0 : pi == 1 ? rb1 : pi == 2 ? rb2 : rb3);
+  const int T = WAVE_ROWS ? 64 : threads;
+  const int tid = WAVE_ROWS ? (threadIdx.x & 63) : threadIdx.x;
+  const int C = P.N >> 3;
+  int lo = 0, hi = C;
+  if (!WAVE_ROWS && slg > 0) {
+    constexpr int q = FMT == 0 ? 16 : 4;
+    lo = ((split * (C / q)) >> slg) * q;
+    hi = split + 1 == (1 << slg) ? C : (((split + 1) * (C / q)) >> slg) * q;
+  }
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(P.x + m * P.ldx);
+  const u32x4* rrow = RES ? reinterpret_cast<const u32x4*>(P.r + m * P.ldr) : nullptr;
+  const u32x4* grow = reinterpret_cast<const u32x4*>(P.gamma);
+  u32x4 xv[J], rv[RES ? J : 1], gv[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) xv[j] = __builtin_nontemporal_load(xrow + min(j * T + tid, C - 1));
+#pragma unroll
+  for (int j = 0; j < J; ++j) gv[j] = grow[min(j * T + tid, C - 1)];
+  if constexpr (RES) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) rv[j] = __builtin_nontemporal_load(rrow + min(j * T + tid, C - 1));
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (RES) xv[j] += rv[j];
+    acc ^= xv[j][0] ^ xv[j][3];
+  }
+  const int nw = T >> 6;
+  if (!WAVE_ROWS && nw > 1) {
+    if ((tid & 63) == 0) red[tid >> 6] = acc;
+    __syncthreads();
+    acc = red[(tid >> 6) ^ 1];
+  }
+  u32x4* ybrow = P.yb ? reinterpret_cast<u32x4*>(P.yb + m * P.ldb) : nullptr;
+  u32x4* hrow = RES ? reinterpret_cast<u32x4*>(P.h + m * P.ldr) : nullptr;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = j * T + tid;
+    if (c < lo || c >= hi) continue;
+    if constexpr (RES) __builtin_nontemporal_store(xv[j], hrow + c);
+    const u32x4 y = xv[j] ^ gv[j];
+    if (ybrow) __builtin_nontemporal_store(y, ybrow + c);
+    if constexpr (FMT == 0) {
+      __builtin_nontemporal_store(u32x2{y[0] ^ y[1], y[2] ^ acc}, reinterpret_cast<u32x2*>(P.q + m * (int64_t)P.N) + c);
+      if ((tid & 15) == 0)
+        reinterpret_cast<uint32_t*>(P.scale)[P.layout == 2 ? (c >> 4) * P.M + m : m * (P.N >> 7) + (c >> 4)] = y[3];
+    } else {
+      __builtin_nontemporal_store(y[0] ^ y[1] ^ acc, reinterpret_cast<uint32_t*>(P.q + m * (int64_t)(P.N >> 1)) + c);
+      if ((tid & 3) == 0) {
+        const int64_t gcount = P.N >> 5, gi = c >> 2;
+        const int64_t off = P.layout == 0   ? m * gcount + gi
+                            : P.layout == 1 ? (m >> 5) * (32 * gcount) + gi * 32 + (m & 31)
+                                            : gi * P.M + m;
+        reinterpret_cast<uint8_t*>(P.scale)[off] = (uint8_t)y[3];
+      }
+    }
+  }
+}
+
 __global__ void k_empty(int* p) {
   if (p && threadIdx.x == 1024) p[0] = 0;   // never true: blocks are at most 1024 threads
 }
@@ -270,6 +358,65 @@ int stream_probe_policy(int lp, int sp, const void* x, const void* r, void* h, v
 }
 #undef POL_ROW
 #undef POL_CASE
+// The memory skeleton of one planned launch of the fused kernel (k_plan_floor):
+// `problems` as for rmsnorm_quant_group_multi (already validated by the
+// library's planner, which produced `info` for exactly these problems: the
+// launch's problems are those with M > 0 whose residual presence matches
+// info->residual, in order). FP8 or MXFP4 as the problems' fmt; J in 1..4.
+int stream_probe_plan_floor(const rmsq_problem* ps, int32_t count, const rmsq_launch_info* info, void* stream) {
+  if (!ps || !info || count < 1 || count > 4 || info->chunks_per_lane < 1 || info->chunks_per_lane > 4) return 1;
+  rmsq::Launch L{};
+  int n = 0;
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) {
+    const rmsq_problem& p = ps[i];
+    if (p.M == 0 || (p.residual_in != nullptr) != (info->residual != 0)) continue;
+    rmsq::Problem& d = L.p[n++];
+    d.x = static_cast<const uint16_t*>(p.x);
+    d.r = static_cast<const uint16_t*>(p.residual_in);
+    d.h = static_cast<uint16_t*>(p.residual_out);
+    d.gamma = static_cast<const uint16_t*>(p.gamma);
+    d.q = static_cast<uint8_t*>(p.out_q);
+    d.scale = p.out_scale;
+    d.yb = static_cast<uint16_t*>(p.out_bf16);
+    d.ldx = p.ldx ? p.ldx : p.N;
+    d.ldr = p.ldr ? p.ldr : p.N;
+    d.ldb = p.ldb ? p.ldb : p.N;
+    d.M = (int32_t)p.M;
+    d.N = (int32_t)p.N;
+    d.layout = p.scale_layout;
+    L.row_begin[n - 1] = (int32_t)rows;
+    rows += p.M;
+  }
+  if (n != info->problems || rows != info->rows) return 1;
+  L.count = n;
+  L.rows = (int32_t)rows;
+  int lg = 0, slg = 0;
+  while ((1 << lg) < info->row_group) ++lg;
+  while ((1 << slg) < info->row_splits) ++slg;
+  L.row_group_log2 = lg;
+  L.splits_log2 = slg;
+  const dim3 g((unsigned)info->workgroups), t((unsigned)info->threads_per_workgroup);
+  const bool packed = info->rows_per_workgroup > 1, res = info->residual != 0, fp4 = ps[0].fmt == 1;
+  hipStream_t s = (hipStream_t)stream;
+#define FLOOR_ARGS L.count, L.rows, L.row_group_log2, L.splits_log2, L.row_begin[1], L.row_begin[2], L.row_begin[3], \
+                   (int32_t)t.x, (int32_t)g.x, L
+#define FLOOR_J(F, JJ, R)                                                                           \
+  if (info->chunks_per_lane == JJ) {                                                                \
+    if (packed) hipLaunchKernelGGL((k_plan_floor<F, JJ, R, true>), g, t, 0, s, FLOOR_ARGS);         \
+    else hipLaunchKernelGGL((k_plan_floor<F, JJ, R, false>), g, t, 0, s, FLOOR_ARGS);               \
+    return st_rc();                                                                                 \
+  }
+#define FLOOR_F(F, R) FLOOR_J(F, 1, R) FLOOR_J(F, 2, R) FLOOR_J(F, 3, R) FLOOR_J(F, 4, R)
+  if (!fp4 && res) { FLOOR_F(0, true) }
+  if (!fp4 && !res) { FLOOR_F(0, false) }
+  if (fp4 && res) { FLOOR_F(1, true) }
+  if (fp4 && !res) { FLOOR_F(1, false) }
+#undef FLOOR_F
+#undef FLOOR_J
+#undef FLOOR_ARGS
+  return 1;
+}
 // An empty kernel: the launch-overhead floor of back-to-back launches.
 int stream_probe_empty(int blocks, int threads, void* stream) {
   if (blocks <= 0 || threads <= 0 || threads > 1024) return 1;

@@ -1,7 +1,10 @@
 """Host-side tests of the C ABI: the library loads, exports every symbol the
 header declares, and validates arguments before touching the GPU. Pointers
 here are fake addresses that are never dereferenced: validation needs only
-their values."""
+their values. A call that passed validation by mistake would enqueue a kernel
+on those addresses, so where a gfx950 GPU is present the whole module is
+skipped: these tests are for the CPU build, where such a regression shows up
+as a failed assertion (the missing device stops the call)."""
 import ctypes as C
 import os
 import re
@@ -12,6 +15,8 @@ import pytest
 import fp4_quant_amd as fq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(fq.rmsq_device_supported(0), reason="fake device addresses: CPU build only")
 
 A = 0x7F0000000000          # fake, 256-byte aligned device addresses
 MB = 1 << 20
@@ -36,18 +41,20 @@ def test_library_exports_every_declared_symbol():
     assert set(fq.EXPORTS) <= set(names)
 
 
-def test_struct_layout_matches_header(tmp_path):
-    """The ctypes mirror of rmsq_problem has the C compiler's layout."""
-    fields = [f for f, _ in fq.rmsq_problem._fields_]
+@pytest.mark.parametrize("struct", ["rmsq_problem", "rmsq_launch_hint", "rmsq_launch_info", "rmsq_launch_plan"])
+def test_struct_layout_matches_header(tmp_path, struct):
+    """The ctypes mirrors of the header's structs have the C compiler's layout."""
+    cls = getattr(fq, struct)
+    fields = [f for f, _ in cls._fields_]
     src = tmp_path / "layout.c"
-    body = "".join(f'printf("%zu\\n", offsetof(rmsq_problem, {f}));' for f in fields)
+    body = "".join(f'printf("%zu\\n", offsetof({struct}, {f}));' for f in fields)
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "rmsq.h"\n'
-                   f'int main(void){{printf("%zu\\n", sizeof(rmsq_problem));{body}return 0;}}\n')
+                   f'int main(void){{printf("%zu\\n", sizeof({struct}));{body}return 0;}}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
-    assert got[0] == C.sizeof(fq.rmsq_problem)
-    assert got[1:] == [getattr(fq.rmsq_problem, f).offset for f in fields]
+    assert got[0] == C.sizeof(cls)
+    assert got[1:] == [getattr(cls, f).offset for f in fields]
 
 
 def test_status_strings():
@@ -198,13 +205,6 @@ def test_multi_count_and_shared_fmt():
     # two problems whose outputs collide
     p3 = dict(p, x=A + 600 * MB)
     assert _multi(probs=[p, p3]) == fq.RMSQ_ERR_INVALID_ARG
-
-
-def test_set_shape_is_callable():
-    fq.rmsq_set_shape(14, 1)
-    fq.rmsq_set_shape(0, 0)
-    fq.rmsq_set_row_group(32)
-    fq.rmsq_set_row_group(0)
 
 
 def test_row_grouping_is_a_bijection():
@@ -459,3 +459,36 @@ def test_make_problem_checks_the_tensors_before_taking_addresses():
             fq.make_problem(xx, gg, 1e-6, q, s, **args)
     with pytest.raises(ValueError, match="GPU tensors"):    # a well-formed problem on the host
         fq.make_problem(x, g, 1e-6, q, s)
+
+
+def test_make_problem_checks_the_output_buffers():
+    """Codes and scales reach the C ABI as bare pointers, so their sizes are
+    checked in the binding: a short, mistyped or non-contiguous code or scale
+    buffer is refused before any address is taken (CPU tensors reach these
+    checks first, so this runs without a GPU)."""
+    import torch
+    M, N = 33, 256
+    x = torch.zeros((M, N), dtype=torch.bfloat16)
+    g = torch.ones(N, dtype=torch.bfloat16)
+    u8, f32 = torch.uint8, torch.float32
+    ok = {0: (torch.zeros((M, N), dtype=u8), torch.zeros((M, N // 128), dtype=f32)),
+          1: (torch.zeros((M, N // 2), dtype=u8), torch.zeros(64 * (N // 32), dtype=u8))}   # tiled: 64 rows
+    bad = [
+        (0, 0, torch.zeros((M, N - 8), dtype=u8), ok[0][1]),                 # codes short
+        (0, 0, torch.zeros((M, N), dtype=torch.int8), ok[0][1]),             # codes mistyped
+        (0, 0, torch.zeros((N, M), dtype=u8).t(), ok[0][1]),                 # codes not dense
+        (0, 0, None, ok[0][1]),
+        (0, 0, ok[0][0], torch.zeros((M, 1), dtype=f32)),                    # scales short
+        (0, 0, ok[0][0], torch.zeros((M, 2), dtype=u8)),                     # FP8 scales are fp32
+        (0, 2, ok[0][0], torch.zeros((2, M), dtype=f32)[:, :M - 1]),         # column-major, short
+        (1, 0, torch.zeros((M, N), dtype=u8), ok[1][1]),                     # MXFP4 codes are N/2 per row
+        (1, 1, ok[1][0], torch.zeros(M * (N // 32), dtype=u8)),              # tiled needs 64 rows here
+        (1, 0, ok[1][0], torch.zeros(M * (N // 32), dtype=f32)),             # MXFP4 scales are bytes
+        (1, 0, ok[1][0], None),
+    ]
+    for fmt, lay, q, s in bad:
+        with pytest.raises(ValueError, match="out_q|out_scale"):
+            fq.make_problem(x, g, 1e-6, q, s, fmt=fmt, scale_layout=lay)
+    for fmt, lay in ((0, 0), (0, 2), (1, 0), (1, 1), (1, 2)):   # the right sizes pass on to the device check
+        with pytest.raises(ValueError, match="GPU tensors"):
+            fq.make_problem(x, g, 1e-6, *ok[fmt], fmt=fmt, scale_layout=lay)

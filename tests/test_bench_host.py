@@ -57,3 +57,45 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def _fake_capture(w, rows):
+    """What Workload.capture returns, made from the oracle's own outputs."""
+    got = []
+    for p in w.host:
+        o = bench._oracle_call(p, w.fmt, w.layout, w.keep_bf16, rows=rows)
+        d = {"rows": rows, "q": o["q"].copy(), "scale": o["scale"].copy()}
+        for k in ("residual_out", "bf16"):
+            if k in o:
+                d[k] = o[k].copy()
+        got.append(d)
+    return got
+
+
+def test_parity_summary_reports_exact_and_detects_a_flipped_byte():
+    import types
+    from fp4_quant_amd import inputs
+    for fmt, lay, keep in ((0, 0, True), (1, 1, False), (0, 2, False)):
+        w = types.SimpleNamespace(host=[inputs.make_problem(40, 512, seed_x=5, residual=True)], fmt=fmt,
+                                  layout=lay, keep_bf16=keep)
+        cap = _fake_capture(w, 40)
+        rep = bench.parity_summary({"w": (w, cap)})
+        assert rep["all_bit_exact"], rep
+        cap[0]["q"][3, 7] ^= 1
+        rep = bench.parity_summary({"w": (w, cap)})
+        assert not rep["all_bit_exact"]
+        assert rep["workloads"]["w"][0]["codes_identical_frac"] < 1.0
+        cap = _fake_capture(w, 40)
+        cap[0]["residual_out"][0, 0] ^= 1
+        assert not bench.parity_summary({"w": (w, cap)})["all_bit_exact"]
+
+
+def test_identity_fields():
+    a, b = bench.source_sha256(), bench.source_sha256()
+    assert a == b and len(a) == 64
+    sha, where = bench.git_identity()
+    assert where.startswith(("checkout", "build", "unavailable"))
+    assert sha is None or len(sha) == 40
+    h = bench.host_info()
+    assert h["logical_cpus"] >= 1
+    assert bench.median([3, 1, 2]) == 2 and bench.median([4, 1, 2, 3]) == 2.5

@@ -43,7 +43,7 @@ def _strided_dev(a, ld):
     return dev(full)[:, :N]
 
 
-def run_gpu(problems, single_entry=False):
+def run_gpu(problems, single_entry=False, hint=None):
     """problems: dicts with numpy x, gamma, eps and optional residual,
     fmt, scale_layout, keep_bf16, inplace, ldx, ldr, ldb. Returns a list of
     dicts of numpy outputs, after checking every guard band."""
@@ -79,7 +79,7 @@ def run_gpu(problems, single_entry=False):
             structs.append(fq.make_problem(x, g, p["eps"], o["q"].t, o["scale"].t, residual_in=r,
                                            residual_out=ro, out_bf16=yb, fmt=fmt, scale_layout=lay))
     if not single_entry:
-        fq.rmsnorm_quant_group_multi(structs)
+        fq.rmsnorm_quant_group_multi(structs, hint=hint)
     torch.cuda.synchronize()
     res = []
     for o, ro, yb, r, p in outs:
@@ -115,8 +115,8 @@ def run_oracle(orc, p):
                                    keep_bf16=True, scale_fill=SENT if fmt == 1 else 0)
 
 
-def check(orc, problems, single_entry=False, strict=True):
-    got = run_gpu(problems, single_entry)
+def check(orc, problems, single_entry=False, strict=True, hint=None):
+    got = run_gpu(problems, single_entry, hint)
     reps = []
     for g, p in zip(got, problems):
         want = run_oracle(orc, p)
@@ -206,21 +206,18 @@ def test_every_launch_shape_gives_the_same_result(orc, N):
     p.update(fmt=0, keep_bf16=True)
     want = None
     C = N // 8
-    try:
-        for J in (1, 2, 3, 4, 7, 8, 14):
-            for W in range(1, 17):
-                if J * W * 64 < C or (J >= 7 and W > 4) or (J * (W - 1) * 64 >= C and W > 1):
-                    continue
-                say(f"shape J={J} W={W} N={N}")
-                fq.rmsq_set_shape(J, W)
-                check(orc, [p])
-                got = run_gpu([p])[0]
-                if want is None:
-                    want = got
-                for k in got:
-                    assert np.array_equal(got[k], want[k]), (J, W, k)
-    finally:
-        fq.rmsq_set_shape(0, 0)
+    for J in (1, 2, 3, 4, 7, 8, 14):
+        for W in range(1, 17):
+            if J * W * 64 < C or (J >= 7 and W > 4) or (J * (W - 1) * 64 >= C and W > 1):
+                continue
+            say(f"shape J={J} W={W} N={N}")
+            h = fq.launch_hint(J, W)
+            check(orc, [p], hint=h)
+            got = run_gpu([p], hint=h)[0]
+            if want is None:
+                want = got
+            for k in got:
+                assert np.array_equal(got[k], want[k]), (J, W, k)
 
 
 @pytest.mark.parametrize("R", [2, 3, 4, 8, 16])
@@ -228,21 +225,17 @@ def test_rows_packed_one_per_wave(orc, R):
     """Short rows packed R per workgroup (one per wave): ragged row counts,
     both formats, every scale layout, with and without residual, two problems
     of different widths, and forced XCD row grouping."""
-    try:
-        fq.rmsq_set_wave_rows(R)
-        for k, (M, N, fmt, lay, res) in enumerate([(1030, 1536, 0, 0, False), (37, 512, 1, 1, True),
-                                                     (257, 2048, 0, 2, True), (65, 256, 1, 2, False)]):
-            say(f"packed rows R={R} M={M} N={N} fmt={fmt} layout={lay}")
-            p = inputs.make_problem(M, N, seed_x=600 + k, residual=res, outliers=True)
-            check(orc, [dict(p, fmt=fmt, scale_layout=lay, keep_bf16=(k % 2 == 0))])
-        a = inputs.make_problem(515, 1536, seed_x=610, residual=False, outliers=True)
-        b = inputs.make_problem(299, 512, seed_x=611, residual=False, outliers=True)
-        for g in (0, 16, 64):
-            fq.rmsq_set_row_group(g)
-            check(orc, [dict(a, fmt=0, scale_layout=2), dict(b, fmt=0, scale_layout=0, keep_bf16=True)])
-    finally:
-        fq.rmsq_set_wave_rows(0)
-        fq.rmsq_set_row_group(0)
+    for k, (M, N, fmt, lay, res) in enumerate([(1030, 1536, 0, 0, False), (37, 512, 1, 1, True),
+                                                 (257, 2048, 0, 2, True), (65, 256, 1, 2, False)]):
+        say(f"packed rows R={R} M={M} N={N} fmt={fmt} layout={lay}")
+        p = inputs.make_problem(M, N, seed_x=600 + k, residual=res, outliers=True)
+        check(orc, [dict(p, fmt=fmt, scale_layout=lay, keep_bf16=(k % 2 == 0))],
+              hint=fq.launch_hint(rows_per_workgroup=R))
+    a = inputs.make_problem(515, 1536, seed_x=610, residual=False, outliers=True)
+    b = inputs.make_problem(299, 512, seed_x=611, residual=False, outliers=True)
+    for g in (0, 16, 64):
+        check(orc, [dict(a, fmt=0, scale_layout=2), dict(b, fmt=0, scale_layout=0, keep_bf16=True)],
+              hint=fq.launch_hint(rows_per_workgroup=R, row_group=g))
 
 
 @pytest.mark.parametrize("S", [2, 4, 8])
@@ -251,22 +244,19 @@ def test_rows_split_over_workgroups(orc, S):
     statistics and handles its share of the groups): both formats, scale
     layouts, residual or not, ragged widths whose groups do not divide
     evenly, and two problems of different widths in one launch."""
-    try:
-        fq.rmsq_set_row_splits(S)
-        for k, (M, N, fmt, lay, res) in enumerate([(64, 7168, 0, 0, True), (5, 7168, 1, 1, True),
-                                                     (33, 1536, 0, 2, False), (7, 384, 1, 2, False),
-                                                     (3, 128, 0, 0, True), (9, 32768, 0, 0, True)]):
-            say(f"row splits S={S} M={M} N={N} fmt={fmt} layout={lay}")
-            p = inputs.make_problem(M, N, seed_x=700 + k, residual=res, outliers=True)
-            check(orc, [dict(p, fmt=fmt, scale_layout=lay, keep_bf16=(k % 2 == 0))])
-        a = inputs.make_problem(40, 1536, seed_x=710, residual=False, outliers=True)
-        b = inputs.make_problem(24, 512, seed_x=711, residual=False, outliers=True)
-        check(orc, [dict(a, fmt=0, scale_layout=2), dict(b, fmt=0, scale_layout=0, keep_bf16=True)])
-        # an in-place residual is never split (the library keeps one workgroup per row)
-        c = inputs.make_problem(16, 7168, seed_x=712, residual=True, outliers=True)
-        check(orc, [dict(c, fmt=0, keep_bf16=True, inplace=True)])
-    finally:
-        fq.rmsq_set_row_splits(0)
+    h = fq.launch_hint(row_splits=S)
+    for k, (M, N, fmt, lay, res) in enumerate([(64, 7168, 0, 0, True), (5, 7168, 1, 1, True),
+                                                 (33, 1536, 0, 2, False), (7, 384, 1, 2, False),
+                                                 (3, 128, 0, 0, True), (9, 32768, 0, 0, True)]):
+        say(f"row splits S={S} M={M} N={N} fmt={fmt} layout={lay}")
+        p = inputs.make_problem(M, N, seed_x=700 + k, residual=res, outliers=True)
+        check(orc, [dict(p, fmt=fmt, scale_layout=lay, keep_bf16=(k % 2 == 0))], hint=h)
+    a = inputs.make_problem(40, 1536, seed_x=710, residual=False, outliers=True)
+    b = inputs.make_problem(24, 512, seed_x=711, residual=False, outliers=True)
+    check(orc, [dict(a, fmt=0, scale_layout=2), dict(b, fmt=0, scale_layout=0, keep_bf16=True)], hint=h)
+    # an in-place residual is never split (the library keeps one workgroup per row)
+    c = inputs.make_problem(16, 7168, seed_x=712, residual=True, outliers=True)
+    check(orc, [dict(c, fmt=0, keep_bf16=True, inplace=True)], hint=h)
 
 
 def test_automatic_row_splits_for_decode(orc):
@@ -276,11 +266,7 @@ def test_automatic_row_splits_for_decode(orc):
     p = dict(_cfg("decode"), keep_bf16=True)
     check(orc, [p])
     auto = run_gpu([p])[0]
-    try:
-        fq.rmsq_set_row_splits(1)
-        one = run_gpu([p])[0]
-    finally:
-        fq.rmsq_set_row_splits(0)
+    one = run_gpu([p], hint=fq.launch_hint(row_splits=1))[0]
     for k in auto:
         assert np.array_equal(auto[k], one[k]), k
 
