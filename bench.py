@@ -350,6 +350,8 @@ def median(v):
 
 def _stream_probe():
     import ctypes as C
+    import fp4_quant_amd
+    fp4_quant_amd.lib()   # torch first, so the probes share its HIP runtime
     L = C.CDLL(os.path.join(ROOT, "tests", "hip", "libconvert_probe.so"))
     L.stream_probe.restype = C.c_int
     L.stream_probe.argtypes = [C.c_int, C.c_int] + [C.c_void_p] * 5 + [C.c_int64, C.c_int, C.c_int, C.c_void_p]

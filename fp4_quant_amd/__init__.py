@@ -64,7 +64,7 @@ class rmsq_launch_info(C.Structure):
     _fields_ = [("problems", C.c_int32), ("rows", C.c_int32), ("chunks_per_lane", C.c_int32),
                 ("waves_per_row", C.c_int32), ("rows_per_workgroup", C.c_int32), ("row_splits", C.c_int32),
                 ("row_group", C.c_int32), ("threads_per_workgroup", C.c_int32), ("workgroups", C.c_int64),
-                ("residual", C.c_int32), ("reserved", C.c_int32)]
+                ("residual", C.c_int32), ("tail", C.c_int32)]
 
 
 class rmsq_launch_plan(C.Structure):
@@ -87,6 +87,12 @@ def lib() -> C.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
                                "(the HIP library is required; there is no CPU fallback)")
+        # The library must call the same HIP runtime as the torch whose
+        # streams and memory it is given. torch ships its own runtime and
+        # loads it into the process-wide symbol scope, so with torch loaded
+        # first the library's HIP calls bind to it; loaded before torch, they
+        # would bind to the system runtime, a second runtime on the same GPU.
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         p, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
         L.rmsnorm_quant_group.restype = i32
@@ -268,7 +274,7 @@ def rmsq_plan_launch(problems, hint=None):
     arr = problems if isinstance(problems, C.Array) else problem_array(problems)
     plan = rmsq_launch_plan()
     _check(lib().rmsq_plan_launch(arr, len(arr), C.byref(hint) if hint is not None else None, C.byref(plan)))
-    return [{f: getattr(plan.launch[k], f) for f, _ in rmsq_launch_info._fields_ if f != "reserved"}
+    return [{f: getattr(plan.launch[k], f) for f, _ in rmsq_launch_info._fields_}
             for k in range(plan.launches)]
 
 

@@ -191,27 +191,30 @@ void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
   (L).count, (L).rows, (L).row_group_log2, (L).splits_log2, (L).row_begin[1], (L).row_begin[2], (L).row_begin[3], \
       (int32_t)block.x, (int32_t)grid.x, (L)
 
-// EXACT is used for J <= 4 only: the long per-lane shapes (very wide rows)
-// keep their bounds, which also keeps them within the register budget.
-template <int FMT, bool RES, bool EXACT>
+// The exact and uniform tails are used for J <= 4 only: the long per-lane
+// shapes (very wide rows) keep their bounds, which also keeps them within the
+// register budget; the uniform tail is compiled for packed rows only.
+template <int FMT, bool RES, int TAIL>
 void launch_res(const rmsq::Launch& L, int J, int R, const dim3 grid, const dim3 block, hipStream_t stream) {
+  constexpr int kPackedTail = TAIL;
+  constexpr int kRowTail = TAIL == rmsq::kUniform ? rmsq::kRagged : TAIL;
   if (R > 1) {   // one row per wave, R rows per workgroup (J <= 4 only)
     switch (J) {
-      case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, true, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-      case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, true, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-      case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, true, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-      default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, true, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, true, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, true, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, true, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, true, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
     }
     return;
   }
   switch (J) {
-    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES, false, false>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES, false, false>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES, false, false>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, false, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, false, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, false, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, false, EXACT>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES, false, rmsq::kRagged>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES, false, rmsq::kRagged>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES, false, rmsq::kRagged>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, false, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, false, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, false, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, false, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
   }
 }
 
@@ -234,17 +237,36 @@ void plan_grid(Plan& P) {
   P.block = dim3((unsigned)(64 * (P.R > 1 ? P.R : P.W)));
 }
 
+// How the launch's rows end (rmsq::Tail): every row exactly fills its
+// J*64*W lanes (J*64 when packed) - exact; packed rows that are all a whole
+// number of 64-lane steps - uniform; otherwise ragged. Row splits are ragged.
+int launch_tail(const Plan& P) {
+  const rmsq::Launch& L = P.L;
+  if (L.splits_log2 != 0 || P.J > 4) return rmsq::kRagged;
+  const int64_t T = 64 * (P.R > 1 ? 1 : P.W);
+  bool exact = true, uniform = P.R > 1;
+  for (int i = 0; i < L.count; ++i) {
+    const int64_t C = L.p[i].N >> 3;
+    exact &= C == P.J * T;
+    uniform &= C % T == 0 && C <= P.J * T;
+  }
+  return exact ? rmsq::kExact : uniform ? rmsq::kUniform : rmsq::kRagged;
+}
+
 template <int FMT>
 rmsq_status launch_fmt(const Plan& P, hipStream_t stream) {
   const rmsq::Launch& L = P.L;
-  bool exact = L.splits_log2 == 0;   // every row exactly fills its J*64*W (or J*64, packed) lanes
-  for (int i = 0; i < L.count; ++i) exact &= (L.p[i].N >> 3) == P.J * 64 * (P.R > 1 ? 1 : P.W);
-  if (L.p[0].r) {
-    if (exact) launch_res<FMT, true, true>(L, P.J, P.R, P.grid, P.block, stream);
-    else launch_res<FMT, true, false>(L, P.J, P.R, P.grid, P.block, stream);
+  const int tail = launch_tail(P);
+  const bool res = L.p[0].r != nullptr;
+  if (tail == rmsq::kExact) {
+    if (res) launch_res<FMT, true, rmsq::kExact>(L, P.J, P.R, P.grid, P.block, stream);
+    else launch_res<FMT, false, rmsq::kExact>(L, P.J, P.R, P.grid, P.block, stream);
+  } else if (tail == rmsq::kUniform) {
+    if (res) launch_res<FMT, true, rmsq::kUniform>(L, P.J, P.R, P.grid, P.block, stream);
+    else launch_res<FMT, false, rmsq::kUniform>(L, P.J, P.R, P.grid, P.block, stream);
   } else {
-    if (exact) launch_res<FMT, false, true>(L, P.J, P.R, P.grid, P.block, stream);
-    else launch_res<FMT, false, false>(L, P.J, P.R, P.grid, P.block, stream);
+    if (res) launch_res<FMT, true, rmsq::kRagged>(L, P.J, P.R, P.grid, P.block, stream);
+    else launch_res<FMT, false, rmsq::kRagged>(L, P.J, P.R, P.grid, P.block, stream);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -505,6 +527,7 @@ rmsq_status rmsq_plan_launch(const rmsq_problem* problems, int32_t count, const 
     d.workgroups = (int64_t)P.grid.x;
     d.threads_per_workgroup = (int32_t)P.block.x;
     d.residual = P.L.p[0].r != nullptr;
+    d.tail = launch_tail(P);
   }
   return RMSQ_OK;
 }

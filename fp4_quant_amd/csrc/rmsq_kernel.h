@@ -63,6 +63,15 @@ constexpr int kMaxWaves = 16;
 // they are launched with at most 4 waves per row so the register budget is
 // not cut to 128 by a 1024-thread bound.
 constexpr int max_waves(int J) { return J >= 7 ? 4 : kMaxWaves; }
+// Rows of 3 chunks per lane packed one per wave (the 1536-wide MLA latent
+// rows) are launched 8 rows per workgroup; held to 64 VGPRs, 8 waves fit on
+// each SIMD, so four such workgroups per compute unit and a 4096 + 4096-row
+// launch is resident at once (at 72 VGPRs only three fit and a third of the
+// grid waits for a second round).
+#ifndef RMSQ_AB_P3_CAP
+#define RMSQ_AB_P3_CAP 8
+#endif
+constexpr int min_waves_per_simd(int J, bool wave_rows) { return wave_rows && J == 3 ? RMSQ_AB_P3_CAP : 1; }
 
 // Launch description. The scalars are also passed as the kernel's leading
 // int arguments, which the library is built to have preloaded into SGPRs at
@@ -97,11 +106,21 @@ __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t
 // WAVE_ROWS: rows short enough for one wave (J*64 chunks) are packed one per
 // wave, blockDim/64 consecutive rows per workgroup, with no LDS and no
 // barrier; otherwise the workgroup's waves share one row.
-// EXACT: every row of the launch has exactly J*T chunks (T lanes per row)
-// and is not split, so no lane needs a bound (the usual shapes: 7168 = 2 x 7 waves or 1 x 14,
-// 1536 = 3 x 1, 512 = 1 x 1).
-template <int FMT, int J, bool RES, bool WAVE_ROWS, bool EXACT>
-__global__ void __launch_bounds__(64 * max_waves(J))
+// TAIL: how the rows of the launch end (T lanes per row, no row splits
+// except with kRagged):
+//   kExact    every row has exactly J*T chunks, so no lane needs a bound (the
+//             usual shapes: 7168 = 2 x 7 waves or 1 x 14, 1536 = 3 x 1,
+//             512 = 1 x 1);
+//   kUniform  every row has a whole number of chunk steps (a multiple of T
+//             chunks, at most J*T): steps past a row's end are skipped by the
+//             whole wave, with a scalar test, and their loads re-read the last
+//             step (packed rows only: the MLA latents, 1536 and 512 wide, in
+//             one launch);
+//   kRagged   anything else: lanes past the row end clamp their chunk index.
+enum Tail { kRagged = 0, kExact = 1, kUniform = 2 };
+
+template <int FMT, int J, bool RES, bool WAVE_ROWS, int TAIL>
+__global__ void __launch_bounds__(64 * max_waves(J), min_waves_per_simd(J, WAVE_ROWS))
 rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t rb1, int32_t rb2, int32_t rb3,
                   int32_t threads, int32_t blocks, const Launch L) {
   // the ints repeat L's scalars (count, rows, row_group_log2, splits_log2,
@@ -110,6 +129,15 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // together with x and r; long ones keep h packed and fetch gamma late, to
   // stay within the register budget.
   constexpr bool kShort = J <= 4;
+#ifndef RMSQ_AB_P3_KEEP_H
+#define RMSQ_AB_P3_KEEP_H 0
+#endif
+#ifndef RMSQ_AB_P3_EARLY_G
+#define RMSQ_AB_P3_EARLY_G 1
+#endif
+  constexpr bool kP3 = WAVE_ROWS && J == 3;
+  constexpr bool kKeepH = kShort && (kP3 ? RMSQ_AB_P3_KEEP_H : true);
+  constexpr bool kEarlyG = kShort && (kP3 ? RMSQ_AB_P3_EARLY_G : true);
   __shared__ double red[kMaxWaves];
 
   // Neighbouring row groups run on different XCDs at the same time. (Giving
@@ -138,8 +166,18 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   const int T = WAVE_ROWS ? 64 : threads;
   const int tid = WAVE_ROWS ? (threadIdx.x & 63) : threadIdx.x;
   const int C = P.N >> 3;
-  // chunk index a lane loads: clamped to the row for a ragged launch
-  auto chunk = [C](int c) { return EXACT ? c : min(c, C - 1); };
+  // what a lane loads at step j: row pointer + load(j), clamped to the row's
+  // last step (kUniform: a wave-uniform offset, so the lane offset tid is
+  // shared by every step) or to its last chunk (kRagged)
+  const int jl = TAIL == kUniform ? C / T - 1 : 0;
+  auto load = [C, T, tid, jl](const u32x4* row, int j) {
+    if constexpr (TAIL == kUniform) return (row + min(j, jl) * T)[tid];
+    return row[TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1)];
+  };
+  auto load_nt = [C, T, tid, jl](const u32x4* row, int j) {
+    if constexpr (TAIL == kUniform) return __builtin_nontemporal_load(row + min(j, jl) * T + tid);
+    return __builtin_nontemporal_load(row + (TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1)));
+  };
   // chunks this workgroup normalizes and stores: all of them, or with row
   // splits a range whose ends fall on group boundaries (16 chunks FP8, 4 MXFP4)
   int lo = 0, hi = C;
@@ -159,19 +197,19 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   const u32x4* xrow = reinterpret_cast<const u32x4*>(P.x + m * P.ldx);
   const u32x4* rrow = RES ? reinterpret_cast<const u32x4*>(P.r + m * P.ldr) : nullptr;
   const u32x4* grow = reinterpret_cast<const u32x4*>(P.gamma);
-  u32x4 xv[J], rv[RES ? J : 1], gv[kShort ? J : 1];
+  u32x4 xv[J], rv[RES ? J : 1], gv[kEarlyG ? J : 1];
 #pragma unroll
-  for (int j = 0; j < J; ++j) xv[j] = __builtin_nontemporal_load(xrow + chunk(j * T + tid));
-  if constexpr (kShort) {
+  for (int j = 0; j < J; ++j) xv[j] = load_nt(xrow, j);
+  if constexpr (kEarlyG) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) gv[j] = grow[chunk(j * T + tid)];
+    for (int j = 0; j < J; ++j) gv[j] = load(grow, j);
   }
   // keep the r loads in place: the scheduler may otherwise interleave them
   // with x's, or hoist x's unpacking (and the wait for x) above them
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (RES) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) rv[j] = __builtin_nontemporal_load(rrow + chunk(j * T + tid));
+    for (int j = 0; j < J; ++j) rv[j] = load_nt(rrow, j);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -187,17 +225,17 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
     }
   }
   // xv now holds h (packed bf16); sum of squares over the live chunks
-  float hf[kShort ? J : 1][8];
+  float hf[kKeepH ? J : 1][8];
   double ss = 0.0;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    if (!EXACT && j > 0 && j * T >= C) break;   // the rest lie past the row end for the whole workgroup
+    if (TAIL != kExact && j > 0 && j * T >= C) break;   // the rest lie past the row end for the whole workgroup
     u32x4 hw = xv[j];
-    if (!EXACT && j * T + tid >= C) hw = u32x4{0u, 0u, 0u, 0u};
+    if (TAIL == kRagged && j * T + tid >= C) hw = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float a = bf16_lo(hw[i]), b = bf16_hi(hw[i]);
-      if constexpr (kShort) {
+      if constexpr (kKeepH) {
         hf[j][2 * i] = a;
         hf[j][2 * i + 1] = b;
       }
@@ -227,15 +265,16 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = j * T + tid;
-    if (!EXACT && (c < lo || c >= hi)) continue;
+    if (TAIL == kUniform && j * T >= C) continue;   // a whole step past the row end (wave-uniform)
+    if (TAIL == kRagged && (c < lo || c >= hi)) continue;
     u32x4 g;
-    if constexpr (kShort) g = gv[j];
+    if constexpr (kEarlyG) g = gv[j];
     else g = grow[c];
     float hv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      hv[2 * i] = kShort ? hf[kShort ? j : 0][2 * i] : bf16_lo(xv[j][i]);
-      hv[2 * i + 1] = kShort ? hf[kShort ? j : 0][2 * i + 1] : bf16_hi(xv[j][i]);
+      hv[2 * i] = kKeepH ? hf[kKeepH ? j : 0][2 * i] : bf16_lo(xv[j][i]);
+      hv[2 * i + 1] = kKeepH ? hf[kKeepH ? j : 0][2 * i + 1] : bf16_hi(xv[j][i]);
     }
     const u32x4 yw = norm_bf16x8(hv, xv[j], g, inv32, inv, row_exact);
     // All stores of a row go out after its reduction: keeping the residual

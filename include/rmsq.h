@@ -222,7 +222,9 @@ typedef struct rmsq_launch_info {
     int32_t threads_per_workgroup;
     int64_t workgroups;
     int32_t residual;               /* 1 if this launch's problems have a residual */
-    int32_t reserved;
+    int32_t tail;                   /* how its rows end: 1 every row fills the launch shape exactly,
+                                       2 rows one wave each, all whole 64-lane steps (steps past a row's
+                                       end skipped by the wave), 0 otherwise (lanes past the end bounded) */
 } rmsq_launch_info;
 
 typedef struct rmsq_launch_plan {

@@ -22,6 +22,8 @@ def say(msg: str) -> None:
 def probe():
     global _probe
     if _probe is None:
+        import fp4_quant_amd
+        fp4_quant_amd.lib()   # torch first, so the probes share its HIP runtime
         if not os.path.exists(PROBE_PATH):
             raise RuntimeError(f"{PROBE_PATH} is not built: run __graft_entry__.build()")
         L = C.CDLL(PROBE_PATH)

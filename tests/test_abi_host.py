@@ -492,3 +492,17 @@ def test_make_problem_checks_the_output_buffers():
     for fmt, lay in ((0, 0), (0, 2), (1, 0), (1, 1), (1, 2)):   # the right sizes pass on to the device check
         with pytest.raises(ValueError, match="GPU tensors"):
             fq.make_problem(x, g, 1e-6, *ok[fmt], fmt=fmt, scale_layout=lay)
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """Loaded through the binding, even before anything imported torch, the
+    library's HIP calls resolve to the runtime torch loaded (the one that owns
+    the streams and memory it is given), not to a second copy."""
+    code = "import fp4_quant_amd as fq; fq.lib()"
+    env = dict(os.environ, LD_DEBUG="bindings")
+    r = subprocess.run([__import__("sys").executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stderr.splitlines() if "librmsq.so" in l and "`hipLaunchKernel'" in l]
+    assert lines, "no binding of hipLaunchKernel seen"
+    assert all("torch/lib/libamdhip64" in l for l in lines), lines

@@ -7,7 +7,9 @@ before it reaches a GPU.
 
 Limits (512 VGPRs per SIMD lane slot, allocated in granules of 8):
   * J = 1, 2 (the shapes of the 7168-wide rows): at most 64 VGPRs, 8 waves per SIMD;
-  * J = 3: at most 80 VGPRs, 6 waves per SIMD; J = 4: at most 96, 5 waves;
+  * J = 3: at most 80 VGPRs, 6 waves per SIMD, and at most 64 (8 waves) for
+    rows packed one per wave (the MLA latents: the whole launch resident at
+    once); J = 4: at most 96, 5 waves;
   * J = 7, 8: at most 128 VGPRs, J = 14: at most 168 (4-wave workgroups);
   * no kernel spills or uses private (scratch) memory.
 """
@@ -20,7 +22,7 @@ import pytest
 
 from fp4_quant_amd import build as B
 
-NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)ELb(\d)EEEviiiiiiiiiNS_6LaunchE$")
+NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)ELi(\d)EEEviiiiiiiiiNS_6LaunchE$")
 
 
 @pytest.fixture(scope="module")
@@ -56,8 +58,9 @@ def kernels():
 def test_every_kernel_variant_is_present(kernels):
     fused = [n for n in kernels if NAME.match(n or "")]
     # 3 formats (FP8, MXFP4, norm only) x residual or not x (7 shapes + 4 packed-row shapes),
-    # the 4 short shapes and 4 packed-row shapes also for rows that exactly fill the launch
-    assert len(fused) == 3 * 2 * (7 + 4 + 4 + 4), sorted(fused)
+    # the 4 short shapes and 4 packed-row shapes also for rows that exactly fill the launch,
+    # and the 4 packed-row shapes for rows of whole 64-lane steps (uniform tail)
+    assert len(fused) == 3 * 2 * (7 + 4 + 4 + 4 + 4), sorted(fused)
     assert sum(1 for n in kernels if "rmsq_group_quant_kernel" in (n or "")) == 2
 
 
@@ -79,7 +82,8 @@ def test_register_budget(kernels, J, limit):
     for n, k in kernels.items():
         m = NAME.match(n or "")
         if m and int(m.group(2)) == J:
-            assert k["vgpr_count"] + k["agpr_count"] <= limit, (n, k)
+            lim = 64 if J == 3 and m.group(4) == "1" else limit
+            assert k["vgpr_count"] + k["agpr_count"] <= lim, (n, k)
 
 
 def test_gemm_variants_fit_sixteen_waves(kernels):

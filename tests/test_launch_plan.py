@@ -41,6 +41,10 @@ def test_default_plans_of_the_workloads():
     assert len(mla) == 1 and mla[0]["problems"] == 2 and mla[0]["rows"] == 8192
     assert (mla[0]["chunks_per_lane"], mla[0]["waves_per_row"], mla[0]["rows_per_workgroup"]) == (3, 1, 8)
     assert mla[0]["workgroups"] == 1024
+    assert mla[0]["tail"] == 2                       # whole 64-lane steps: the wave skips the rest
+    assert pre[0]["tail"] == 1 and dec["tail"] == 0  # exact rows; split rows are bounded per lane
+    assert plan([prob(M=4096, N=1536, residual=False)])[0]["tail"] == 1
+    assert plan([prob(0, M=4096, N=1536, residual=False), prob(1, M=4096, N=640, residual=False)])[0]["tail"] == 0
     mx = plan([prob(M=16384, fmt=1, layout=1)])[0]
     assert (mx["chunks_per_lane"], mx["waves_per_row"], mx["row_group"]) == (2, 7, 16)
 
