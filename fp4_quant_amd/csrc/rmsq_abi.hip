@@ -345,6 +345,7 @@ rmsq_status plan(const rmsq_problem* ps, int32_t count, Mode mode, const rmsq_la
       L.row_begin[n - 1] = (int32_t)rows;
       d.layout = p.scale_layout;
       d.eps = p.eps;
+      d.rn = 1.0 / (double)p.N;
       rows += p.M;
       if (p.N / 8 > Cmax) Cmax = p.N / 8;
     }

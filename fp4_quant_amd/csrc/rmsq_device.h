@@ -18,6 +18,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// A value the caller never reads, for the operands an instruction requires
+// but overwrites: the bits of a packed convert's destination that its next
+// convert replaces, and the "old" value of a DPP move whose every lane
+// receives a source lane. Left undefined, it costs no register initialization.
+__device__ __forceinline__ uint32_t any_u32() { return __builtin_nondeterministic_value(0u); }
+
 // bf16 halves of a packed dword, widened to fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -75,7 +81,7 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_bf16(uint32_t pair, uint32_t byte,
 // the exact quotient would.
 __device__ __forceinline__ uint32_t fp8_exact(float v, float s) {
   float t = f64_to_f32_odd((double)v / (double)s);
-  return cvt_fp8x2<false>(t, t, 0u) & 0xFFu;
+  return cvt_fp8x2<false>(t, t, any_u32()) & 0xFFu;
 }
 
 // ------------------------------------------------------- element blocks --
@@ -160,48 +166,34 @@ __device__ __forceinline__ float fp8_scale(uint32_t amax_bits) {
   return (float)((double)a * (1.0 / 448.0));
 }
 
-// e4m3fn codes of v[e] / s for 8 bf16 values v (as fp32) of one group, bytes
-// in element order. rs = v_rcp_f32(s) is within 1 ulp of 1/s for every scale
-// this kernel produces (s = fl32(amax/448) for a bf16 amax >= 2^-100; checked
-// exhaustively on the GPU), so r_lo = rs - 4 ulp < 1/s < rs + 4 ulp = r_hi,
-// and the nearest-even products v*r_lo and v*r_hi bracket v/s. Rounding to
-// e4m3fn is monotone, so where both brackets give the same code that code is
-// the rounding of v/s (also across the e4m3fn subnormal range); four codes
-// are compared at once as a packed dword. Where they differ - quotients
-// within a few ulp of a rounding midpoint, exact ties - the two codes are
-// neighbours (the brackets are 8 fp32 ulp apart, e4m3fn codes at least 2^-4
-// relative), and v/s is compared with the boundary B between them: B has few
-// significant bits (1.ffff1 x 2^E in the normal range, (k + 1/2) 2^-9 in the
-// subnormal one: min(4, E + 10) fraction bits at its exponent E), and |x_hi|
-// exceeds it by less than the next such bit, so clearing |x_hi|'s lower
-// fraction bits gives B exactly; fma(B, s, -|v|) rounds once, so its sign is
-// that of B s - |v| and it is zero only at an exact tie (for s >= 2^-100 the
-// difference is a multiple of 2^-140, representable), which takes the code
-// with the even mantissa. With bf16 inputs this is not rare - exact ties come
-// with every group whose amax mantissa is a multiple of 7 - so it must not
-// cost a branch per element. MODE picks the form (each measured best where
-// it is used): kFp8Straight, one straight block over the 8 elements (the
-// fused kernel's short rows); kFp8Rounds, one differing element per lane per
-// round, the wave looping while any lane has one left (the GEMMs, where each
-// lane encodes 32 elements); kFp8PerElement, each differing element on the
-// double-precision path under its own branch (the long-row kernels, short of
-// registers). Groups whose scale is too small for a normal reciprocal take
-// the double-precision path.
-enum Fp8Fix { kFp8PerElement = 0, kFp8Straight = 1, kFp8Rounds = 2 };
-
-// The rounding boundary between the neighbouring codes of x_hi's bracket and
-// the decision against it: 1 when v/s lies above the boundary or on it with
-// c_lo odd (then the code is c_lo + 1), else 0.
-__device__ __forceinline__ uint32_t fp8_round_up(float v, float x_hi, float s, uint32_t c_lo) {
-  const uint32_t xb = __float_as_uint(x_hi) & 0x7FFFFFFFu;
-  const int keep = max(0, min(4, (int)(xb >> 23) - 117));
-  const float B = __uint_as_float(xb & ~((1u << (23 - keep)) - 1u));
-  const float t = __builtin_fmaf(B, s, -__builtin_fabsf(v));
-  return (uint32_t)(t < 0.0f) | ((uint32_t)(t == 0.0f) & (c_lo & 1u));
-}
-
-template <int MODE = kFp8Straight>
-__device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
+// e4m3fn codes of v[e] / s for 8 bf16 values v (as fp32) of one group with
+// maximum magnitude amax and scale s = fp8_scale(amax) = fl32(amax / 448),
+// bytes in element order.
+//
+// Bracket: rs = v_rcp_f32(s) is within 1 ulp of 1/s for every scale this
+// library forms (checked exhaustively on the GPU), so r_lo = rs - 4 ulp <
+// 1/s < rs + 4 ulp = r_hi and the nearest-even products v*r_lo and v*r_hi
+// bracket v/s within 2^-20. Rounding to e4m3fn is monotone, so where both
+// give the same code that code is the rounding of v/s (also across the
+// e4m3fn subnormal range). Four codes are compared at once as a dword.
+//
+// Where they differ, v/s lies within 2^-20 of a rounding midpoint B. v/s is
+// R * amax / (448 s) with R = 448 v / amax and |amax / (448 s) - 1| <= 2^-24,
+// and for bf16 v and amax, R is either exactly a midpoint or at least 2^-12
+// (relative) away from every one (checked for every (v, amax) pair on the
+// CPU): so R = B exactly, and v/s = B * amax / (448 s) sits above B when
+// 448 s < amax, below it when 448 s > amax, and on it - a tie, which takes
+// the even code - when 448 s = amax (amax's mantissa a multiple of 7). The
+// sign of fma(s, 448, -amax) is that of the exact difference (a nonzero
+// difference is at least 2^-123, no underflow to zero), so one fma per group
+// decides every undecided element of it. The two codes are then neighbours of
+// one sign, c_hi = c_lo + 1 in each differing byte, so qh - qw has 0x01 in
+// exactly those bytes (no borrows), and the result is qw plus those ones where
+// the upper code is taken: all of them when 448 s < amax, the bytes with odd
+// c_lo on a tie, none otherwise. Branch-free, two bitwise ops and two adds
+// per four elements. Groups whose scale is below 2^-100 (no normal
+// reciprocal) take the double-precision path element by element.
+__device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s, float amax) {
   const uint32_t rb = __float_as_uint(__builtin_amdgcn_rcpf(s));
   const float r_lo = __uint_as_float(rb - 4u), r_hi = __uint_as_float(rb + 4u);
   float lo[8], hi[8];
@@ -211,54 +203,24 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s) {
     hi[e] = v[e] * r_hi;
   }
   u32x2 qw, qh;
-  qw[0] = cvt_fp8x2<true>(lo[2], lo[3], cvt_fp8x2<false>(lo[0], lo[1], 0u));
-  qw[1] = cvt_fp8x2<true>(lo[6], lo[7], cvt_fp8x2<false>(lo[4], lo[5], 0u));
-  qh[0] = cvt_fp8x2<true>(hi[2], hi[3], cvt_fp8x2<false>(hi[0], hi[1], 0u));
-  qh[1] = cvt_fp8x2<true>(hi[6], hi[7], cvt_fp8x2<false>(hi[4], hi[5], 0u));
-  const bool tiny = s < 0x1p-100f;
-  if (MODE == kFp8PerElement || __builtin_expect(tiny, 0)) {
-    if (__builtin_expect(tiny | (qw[0] != qh[0]) | (qw[1] != qh[1]), 0)) {
+  qw[0] = cvt_fp8x2<true>(lo[2], lo[3], cvt_fp8x2<false>(lo[0], lo[1], any_u32()));
+  qw[1] = cvt_fp8x2<true>(lo[6], lo[7], cvt_fp8x2<false>(lo[4], lo[5], any_u32()));
+  qh[0] = cvt_fp8x2<true>(hi[2], hi[3], cvt_fp8x2<false>(hi[0], hi[1], any_u32()));
+  qh[1] = cvt_fp8x2<true>(hi[6], hi[7], cvt_fp8x2<false>(hi[4], hi[5], any_u32()));
+  if (__builtin_expect(s < 0x1p-100f, 0)) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 3) * 8;
-        if (tiny | ((((qw[e >> 2] ^ qh[e >> 2]) >> sh) & 0xFFu) != 0u)) {
-          const uint32_t b = fp8_exact(v[e], s);
-          qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
-        }
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 3) * 8;
+      const uint32_t b = fp8_exact(v[e], s);
+      qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
     }
-  } else if (__builtin_expect((qw[0] != qh[0]) | (qw[1] != qh[1]), 0)) {
-    // c_hi = c_lo + 1 where the codes differ (neighbours of one sign, no carry)
-    if constexpr (MODE == kFp8Straight) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 3) * 8;
-        const uint32_t c_lo = (qw[e >> 2] >> sh) & 0xFFu, c_hi = (qh[e >> 2] >> sh) & 0xFFu;
-        qw[e >> 2] += ((c_lo != c_hi) ? fp8_round_up(v[e], hi[e], s, c_lo) : 0u) << sh;
-      }
-    } else {
-      uint32_t dm = 0;   // elements whose bracket codes differ
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        dm |= (uint32_t)((((qw[e >> 2] ^ qh[e >> 2]) >> ((e & 3) * 8)) & 0xFFu) != 0u) << e;
-      while (__any(dm != 0u)) {   // at most 8 rounds: each clears a bit of every lane that has one
-        if (dm != 0u) {
-          const int e = __builtin_ctz(dm);
-          dm &= dm - 1u;
-          float ve = v[0], he = hi[0];
-#pragma unroll
-          for (int k = 1; k < 8; ++k) {
-            ve = e == k ? v[k] : ve;
-            he = e == k ? hi[k] : he;
-          }
-          const int sh = (e & 3) * 8;
-          const uint32_t up = fp8_round_up(ve, he, s, ((e < 4 ? qw[0] : qw[1]) >> sh) & 0xFFu);
-          if (e < 4) qw[0] += up << sh;
-          else qw[1] += up << sh;
-        }
-      }
-    }
+    return qw;
   }
+  const float t = __builtin_fmaf(s, 448.0f, -amax);
+  const uint32_t up = t < 0.0f ? 0xFFFFFFFFu : 0u;    // v/s above the midpoint: the upper code
+  const uint32_t tie = t == 0.0f ? 0xFFFFFFFFu : 0u;  // on it: the even one
+#pragma unroll
+  for (int k = 0; k < 2; ++k) qw[k] += (qh[k] - qw[k]) & (up | (tie & qw[k]));
   return qw;
 }
 
@@ -275,7 +237,7 @@ __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
 // (the division by a power of two is exact), packed two per byte with the
 // even element in the low nibble.
 __device__ __forceinline__ uint32_t fp4_codes8(const u32x4 yw, uint32_t byte) {
-  uint32_t w = cvt_fp4x2_bf16<0>(yw[0], byte, 0u);
+  uint32_t w = cvt_fp4x2_bf16<0>(yw[0], byte, any_u32());
   w = cvt_fp4x2_bf16<1>(yw[1], byte, w);
   w = cvt_fp4x2_bf16<2>(yw[2], byte, w);
   w = cvt_fp4x2_bf16<3>(yw[3], byte, w);
@@ -286,14 +248,14 @@ __device__ __forceinline__ uint32_t fp4_codes8(const u32x4 yw, uint32_t byte) {
 // Rotate within each row of 16 lanes (DPP row_ror).
 template <int N>
 __device__ __forceinline__ uint32_t row_ror(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)any_u32(), (int)v, 0x120 + N, 0xF, 0xF, false);
 }
 // Swap within quads: lane i reads lane i^1 (quad_perm [1,0,3,2]) or i^2 ([2,3,0,1]).
 __device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)any_u32(), (int)v, 0xB1, 0xF, 0xF, false);
 }
 __device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)any_u32(), (int)v, 0x4E, 0xF, 0xF, false);
 }
 
 // max over the 16 lanes of a DPP row; every lane of the row gets the result.
@@ -314,8 +276,8 @@ __device__ __forceinline__ uint32_t max4(uint32_t v) {
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)any_u32(), (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)any_u32(), (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 

@@ -447,15 +447,16 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4 w, float f[8]) {
   }
 }
 
-// e4m3fn codes of 32 bf16 values (16 dwords) under scale sc: 8 dwords, element
-// order.
-__device__ __forceinline__ v8i32 fp8_codes32(const u32x4 v[4], float sc) {
+// e4m3fn codes of 32 bf16 values (16 dwords) of a group with maximum
+// magnitude amax (bf16 bits) and scale sc = fp8_scale(amax): 8 dwords,
+// element order.
+__device__ __forceinline__ v8i32 fp8_codes32(const u32x4 v[4], float sc, uint32_t amax) {
   v8i32 q;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float f[8];
     unpack_bf16x8(v[i], f);
-    const u32x2 c = fp8_codes8<kFp8Rounds>(f, sc);
+    const u32x2 c = fp8_codes8(f, sc, __uint_as_float(amax << 16));
     q[2 * i] = (int)c[0];
     q[2 * i + 1] = (int)c[1];
   }
@@ -536,10 +537,11 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const
 #pragma unroll
     for (int i = 0; i < SW; ++i) {
       if (s_lo + i >= s_hi) break;
-      const float sc = fp8_scale(max16(amax8(av[i])));
+      const uint32_t am = max16(amax8(av[i]));
+      const float sc = fp8_scale(am);
       float f[8];
       unpack_bf16x8(av[i], f);
-      const u32x2 c = fp8_codes8<kFp8Rounds>(f, sc);
+      const u32x2 c = fp8_codes8(f, sc, __uint_as_float(am << 16));
       v8i32 aop;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -643,7 +645,7 @@ __global__ void __launch_bounds__(64 * kGemmMaxWaves) rmsq_gemm_fp8_kernel(const
             am = max(am, (uint32_t)__shfl_xor((int)am, 16));
             am = max(am, (uint32_t)__shfl_xor((int)am, 32));
             sc = fp8_scale(am);
-            aop = fp8_codes32(av[i][t], sc);
+            aop = fp8_codes32(av[i][t], sc, am);
           }
           if (!live) aop = v8i32{0, 0, 0, 0, 0, 0, 0, 0};
           const v4f32 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, v4f32{0.0f, 0.0f, 0.0f, 0.0f}, 0,

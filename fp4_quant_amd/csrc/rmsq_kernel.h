@@ -55,6 +55,7 @@ struct Problem {
   int64_t ldb;
   int32_t layout;         // scale layout: 0 row-major, 1 32-row tiles (MXFP4), 2 column-major
   float eps;
+  double rn;              // 1/N rounded to nearest (host division)
 };
 
 constexpr int kMaxProblems = 4;
@@ -68,10 +69,7 @@ constexpr int max_waves(int J) { return J >= 7 ? 4 : kMaxWaves; }
 // each SIMD, so four such workgroups per compute unit and a 4096 + 4096-row
 // launch is resident at once (at 72 VGPRs only three fit and a third of the
 // grid waits for a second round).
-#ifndef RMSQ_AB_P3_CAP
-#define RMSQ_AB_P3_CAP 8
-#endif
-constexpr int min_waves_per_simd(int J, bool wave_rows) { return wave_rows && J == 3 ? RMSQ_AB_P3_CAP : 1; }
+constexpr int min_waves_per_simd(int J, bool wave_rows) { return wave_rows && J == 3 ? 8 : 1; }
 
 // Launch description. The scalars are also passed as the kernel's leading
 // int arguments, which the library is built to have preloaded into SGPRs at
@@ -129,15 +127,9 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // together with x and r; long ones keep h packed and fetch gamma late, to
   // stay within the register budget.
   constexpr bool kShort = J <= 4;
-#ifndef RMSQ_AB_P3_KEEP_H
-#define RMSQ_AB_P3_KEEP_H 0
-#endif
-#ifndef RMSQ_AB_P3_EARLY_G
-#define RMSQ_AB_P3_EARLY_G 1
-#endif
-  constexpr bool kP3 = WAVE_ROWS && J == 3;
-  constexpr bool kKeepH = kShort && (kP3 ? RMSQ_AB_P3_KEEP_H : true);
-  constexpr bool kEarlyG = kShort && (kP3 ? RMSQ_AB_P3_EARLY_G : true);
+  // Packed rows of 3 chunks per lane (held to 64 VGPRs) unpack h again in
+  // phase 2 rather than keep 24 fp32 copies across the reduction.
+  constexpr bool kKeepH = kShort && !(WAVE_ROWS && J == 3);
   __shared__ double red[kMaxWaves];
 
   // Neighbouring row groups run on different XCDs at the same time. (Giving
@@ -170,11 +162,11 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // last step (kUniform: a wave-uniform offset, so the lane offset tid is
   // shared by every step) or to its last chunk (kRagged)
   const int jl = TAIL == kUniform ? C / T - 1 : 0;
-  auto load = [C, T, tid, jl](const u32x4* row, int j) {
+  auto load = [&](const u32x4* row, int j) {
     if constexpr (TAIL == kUniform) return (row + min(j, jl) * T)[tid];
     return row[TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1)];
   };
-  auto load_nt = [C, T, tid, jl](const u32x4* row, int j) {
+  auto load_nt = [&](const u32x4* row, int j) {
     if constexpr (TAIL == kUniform) return __builtin_nontemporal_load(row + min(j, jl) * T + tid);
     return __builtin_nontemporal_load(row + (TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1)));
   };
@@ -197,10 +189,10 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   const u32x4* xrow = reinterpret_cast<const u32x4*>(P.x + m * P.ldx);
   const u32x4* rrow = RES ? reinterpret_cast<const u32x4*>(P.r + m * P.ldr) : nullptr;
   const u32x4* grow = reinterpret_cast<const u32x4*>(P.gamma);
-  u32x4 xv[J], rv[RES ? J : 1], gv[kEarlyG ? J : 1];
+  u32x4 xv[J], rv[RES ? J : 1], gv[kShort ? J : 1];
 #pragma unroll
   for (int j = 0; j < J; ++j) xv[j] = load_nt(xrow, j);
-  if constexpr (kEarlyG) {
+  if constexpr (kShort) {
 #pragma unroll
     for (int j = 0; j < J; ++j) gv[j] = load(grow, j);
   }
@@ -212,6 +204,20 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
     for (int j = 0; j < J; ++j) rv[j] = load_nt(rrow, j);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // Every other field of the problem record this row needs, read now: their
+  // scalar loads then overlap the row's vector loads instead of stalling the
+  // statistics and the stores later (each late scalar load costs a memory
+  // round trip on the row's critical path, which is what bounds the short
+  // launches).
+  const float eps = P.eps;
+  const double rn = P.rn;
+  const int32_t layout = P.layout, M = P.M;
+  uint16_t* const hbase = RES ? P.h : nullptr;
+  uint16_t* const ybase = P.yb;
+  uint8_t* const qbase = FMT == 2 ? nullptr : P.q;
+  void* const sbase = FMT == 2 ? nullptr : P.scale;
+  const int64_t ldb = P.ldb;
+  asm volatile("" ::"s"(eps), "s"(rn), "s"(layout), "s"(M), "s"(hbase), "s"(ybase), "s"(qbase), "s"(sbase), "s"(ldb));
 
   // ---- phase 1: h = x + r (stored after the reduction, with the other outputs)
   if constexpr (RES) {
@@ -251,7 +257,14 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
     ss = 0.0;
     for (int w = 0; w < nw; ++w) ss += red[w];
   }
-  const double denom = ss / (double)P.N + (double)P.eps;
+  // ss / N, correctly rounded, from the correctly rounded reciprocal rn: the
+  // product q0 is within an ulp of the quotient, its residual ss - q0 * N is
+  // exact in one fma, and one more fma with rn rounds the corrected quotient
+  // to nearest (Markstein's quotient refinement).
+  const double nd = (double)P.N;
+  const double q0 = ss * rn;
+  const double ms = __builtin_fma(__builtin_fma(-q0, nd, ss), rn, q0);
+  const double denom = ms + (double)eps;
   const double inv = denom > 0.0 ? 1.0 / __builtin_sqrt(denom) : 0.0;
   const float inv32 = (float)inv;
   // Rows whose inverse norm leaves the comfortable fp32 range take the exact
@@ -260,15 +273,15 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   const bool row_exact = inv > 0x1p16 || (inv != 0.0 && inv < 0x1p-100);
 
   // ---- phase 2: normalize, bf16, group scale, codes -----------------------
-  u32x4* ybrow = P.yb ? reinterpret_cast<u32x4*>(P.yb + m * P.ldb) : nullptr;
-  u32x4* hrow = RES ? reinterpret_cast<u32x4*>(P.h + m * P.ldr) : nullptr;
+  u32x4* ybrow = ybase ? reinterpret_cast<u32x4*>(ybase + m * ldb) : nullptr;
+  u32x4* hrow = RES ? reinterpret_cast<u32x4*>(hbase + m * P.ldr) : nullptr;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = j * T + tid;
     if (TAIL == kUniform && j * T >= C) continue;   // a whole step past the row end (wave-uniform)
     if (TAIL == kRagged && (c < lo || c >= hi)) continue;
     u32x4 g;
-    if constexpr (kEarlyG) g = gv[j];
+    if constexpr (kShort) g = gv[j];
     else g = grow[c];
     float hv[8];
 #pragma unroll
@@ -294,26 +307,27 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
         v[2 * i] = bf16_lo(yw[i]);
         v[2 * i + 1] = bf16_hi(yw[i]);
       }
-      const float sc = fp8_scale(max16(am));
-      const u32x2 qw = fp8_codes8<kShort ? kFp8Straight : kFp8PerElement>(v, sc);
-      u32x2* qrow = reinterpret_cast<u32x2*>(P.q + m * (int64_t)P.N);
+      const uint32_t gam = max16(am);
+      const float sc = fp8_scale(gam);
+      const u32x2 qw = fp8_codes8(v, sc, __uint_as_float(gam << 16));
+      u32x2* qrow = reinterpret_cast<u32x2*>(qbase + m * (int64_t)P.N);
       __builtin_nontemporal_store(qw, qrow + c);
       if ((tid & 15) == 0) {
         const int64_t g = c >> 4;
-        reinterpret_cast<float*>(P.scale)[P.layout == 2 ? g * P.M + m : m * (P.N >> 7) + g] = sc;
+        reinterpret_cast<float*>(sbase)[layout == 2 ? g * M + m : m * (P.N >> 7) + g] = sc;
       }
     } else if constexpr (FMT == 1) {
       // MXFP4 e2m1, group 32 = one lane quad
       const uint32_t byte = mx_scale_byte(max4(am));
       const uint32_t w = fp4_codes8(yw, byte);
-      uint32_t* qrow = reinterpret_cast<uint32_t*>(P.q + m * (int64_t)(P.N >> 1));
+      uint32_t* qrow = reinterpret_cast<uint32_t*>(qbase + m * (int64_t)(P.N >> 1));
       __builtin_nontemporal_store(w, qrow + c);
       if ((tid & 3) == 0) {
         const int64_t gcount = P.N >> 5, gi = c >> 2;
-        const int64_t off = P.layout == 0   ? m * gcount + gi
-                            : P.layout == 1 ? (m >> 5) * (32 * gcount) + gi * 32 + (m & 31)
-                                            : gi * P.M + m;
-        reinterpret_cast<uint8_t*>(P.scale)[off] = (uint8_t)byte;
+        const int64_t off = layout == 0   ? m * gcount + gi
+                            : layout == 1 ? (m >> 5) * (32 * gcount) + gi * 32 + (m & 31)
+                                          : gi * M + m;
+        reinterpret_cast<uint8_t*>(sbase)[off] = (uint8_t)byte;
       }
     }
   }
@@ -350,8 +364,9 @@ __global__ void __launch_bounds__(256) rmsq_group_quant_kernel(const QuantArgs A
       v[2 * i] = bf16_lo(yw[i]);
       v[2 * i + 1] = bf16_hi(yw[i]);
     }
-    const float sc = fp8_scale(max16(am));
-    const u32x2 qw = fp8_codes8(v, sc);
+    const uint32_t gam = max16(am);
+    const float sc = fp8_scale(gam);
+    const u32x2 qw = fp8_codes8(v, sc, __uint_as_float(gam << 16));
     __builtin_nontemporal_store(qw, reinterpret_cast<u32x2*>(A.q + m * (int64_t)A.N) + c);
     if ((threadIdx.x & 15) == 0) {
       const int64_t g = c >> 4;

@@ -30,8 +30,7 @@ def probe():
         for name in ("probe_norm_bf16", "probe_fp8_scale", "probe_fp8_codes", "probe_mx_byte",
                      "probe_fp4_codes", "probe_cvt_bf16", "probe_cvt_fp8", "probe_cvt_fp4",
                      "probe_f64_to_bf16", "probe_fp8_exact", "probe_rcp", "probe_cvt_fp4_bf16_scaled",
-                     "probe_cvt_fp8_bf16_scaled", "probe_mfma_scale_fp4", "probe_mfma_scale_fp8",
-                     "probe_fp8_codes_per_element", "probe_fp8_codes_rounds"):
+                     "probe_cvt_fp8_bf16_scaled", "probe_mfma_scale_fp4", "probe_mfma_scale_fp8"):
             f = getattr(L, name)
             f.restype = C.c_int
         _probe = L

@@ -32,12 +32,14 @@ __global__ void k_fp8_scale(const uint16_t* amax, float* s, int64_t n) {
   GRID_LOOP(i, n) s[i] = fp8_scale(amax[i]);
 }
 
-template <int MODE>
-__global__ void k_fp8_codes(const float* v, const float* s, uint8_t* out, int64_t n) {
+// codes of 8 values of a group with maximum magnitude amax[k] (bf16 bits),
+// under the scale the kernels form for it
+__global__ void k_fp8_codes(const float* v, const uint16_t* amax, uint8_t* out, int64_t n) {
   GRID_LOOP(k, n) {
     float x[8];
     for (int e = 0; e < 8; ++e) x[e] = v[8 * k + e];
-    const u32x2 q = fp8_codes8<MODE>(x, s[k]);
+    const uint32_t a = amax[k];
+    const u32x2 q = fp8_codes8(x, fp8_scale(a), __uint_as_float(a << 16));
     for (int e = 0; e < 8; ++e) out[8 * k + e] = (uint8_t)(q[e >> 2] >> ((e & 3) * 8));
   }
 }
@@ -171,19 +173,9 @@ int probe_fp8_scale(const uint16_t* a, float* s, int64_t n, void* stream) {
   hipLaunchKernelGGL(k_fp8_scale, GRID(n), a, s, n);
   return launch_status();
 }
-int probe_fp8_codes(const float* v, const float* s, uint8_t* out, int64_t n, void* stream) {
+int probe_fp8_codes(const float* v, const uint16_t* amax, uint8_t* out, int64_t n, void* stream) {
   if (n <= 0) return 0;
-  hipLaunchKernelGGL(k_fp8_codes<kFp8Straight>, GRID(n), v, s, out, n);
-  return launch_status();
-}
-int probe_fp8_codes_per_element(const float* v, const float* s, uint8_t* out, int64_t n, void* stream) {
-  if (n <= 0) return 0;
-  hipLaunchKernelGGL(k_fp8_codes<kFp8PerElement>, GRID(n), v, s, out, n);
-  return launch_status();
-}
-int probe_fp8_codes_rounds(const float* v, const float* s, uint8_t* out, int64_t n, void* stream) {
-  if (n <= 0) return 0;
-  hipLaunchKernelGGL(k_fp8_codes<kFp8Rounds>, GRID(n), v, s, out, n);
+  hipLaunchKernelGGL(k_fp8_codes, GRID(n), v, amax, out, n);
   return launch_status();
 }
 int probe_mx_byte(const uint16_t* a, uint8_t* out, int64_t n, void* stream) {
