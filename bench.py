@@ -612,8 +612,9 @@ def cpu_baseline(w, budget_s):
     before timing, so each timed call is the oracle's own work (its OpenMP
     loop over rows, with the threads the host gives it), repeated until
     budget_s has passed (at least three times); then a single-thread run on a
-    512-row sample (in a child process, so the thread count is set before the
-    OpenMP runtime starts), median of 5, also on preallocated outputs."""
+    512-row sample (in a child process, with the oracle's thread count set
+    through the OpenMP runtime: a host may fix OMP_NUM_THREADS for every
+    process it starts), median of 5, also on preallocated outputs."""
     import oracle
     p = w.host[0]
     M, N = p["x"].shape
@@ -633,19 +634,22 @@ def cpu_baseline(w, budget_s):
                      f"{sum(times):.1f} s, median {sec * 1e3:.2f} ms", **host_info()}
     rows = min(M, 512)
     code = ("import sys, time; sys.path.insert(0, %r)\n"
-            "from fp4_quant_amd import inputs\nimport bench\n"
+            "from fp4_quant_amd import inputs\nimport bench, oracle\n"
+            "oracle.set_num_threads(1)\n"
             "p = inputs.make_problem(%d, %d, seed_x=0, residual=%r, outliers=True)\n"
             "out = bench._oracle_out(p, %d, %d, %r, %d)\n"
             "bench._oracle_call(p, %d, %d, %r, out)\n"
             "ts = []\n"
             "for _ in range(5):\n"
             "    t0 = time.perf_counter(); bench._oracle_call(p, %d, %d, %r, out); ts.append(time.perf_counter() - t0)\n"
-            "print(sorted(ts)[2])\n") % (ROOT, rows, N, "residual" in p, w.fmt, w.layout, keep, rows,
-                                         w.fmt, w.layout, keep, w.fmt, w.layout, keep)
+            "print(oracle.num_threads(), sorted(ts)[2])\n") % (ROOT, rows, N, "residual" in p, w.fmt, w.layout, keep,
+                                                               rows, w.fmt, w.layout, keep, w.fmt, w.layout, keep)
     env = dict(os.environ, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
     if r.returncode == 0:
-        s1 = float(r.stdout.strip().splitlines()[-1])
+        nt1, s1 = r.stdout.strip().splitlines()[-1].split()
+        s1 = float(s1)
+        assert int(nt1) == 1, f"the single-thread oracle leg ran {nt1} threads"
         b1 = algorithmic_bytes(rows, N, w.fmt, "residual" in p, keep)
         res["single_thread"] = {"value": round(b1 / s1 / 1e9, 3), "unit": "GB/s", "cores": 1,
                                 "mtok_per_s": round(rows / s1 / 1e6, 4),

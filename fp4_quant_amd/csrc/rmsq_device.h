@@ -202,11 +202,14 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s, float ama
     lo[e] = v[e] * r_lo;
     hi[e] = v[e] * r_hi;
   }
+  // The first convert of each dword writes its low half; the high half it
+  // keeps is replaced by the second, so the register it starts from is any
+  // value that dies here (one of its own operands): no initialization.
   u32x2 qw, qh;
-  qw[0] = cvt_fp8x2<true>(lo[2], lo[3], cvt_fp8x2<false>(lo[0], lo[1], any_u32()));
-  qw[1] = cvt_fp8x2<true>(lo[6], lo[7], cvt_fp8x2<false>(lo[4], lo[5], any_u32()));
-  qh[0] = cvt_fp8x2<true>(hi[2], hi[3], cvt_fp8x2<false>(hi[0], hi[1], any_u32()));
-  qh[1] = cvt_fp8x2<true>(hi[6], hi[7], cvt_fp8x2<false>(hi[4], hi[5], any_u32()));
+  qw[0] = cvt_fp8x2<true>(lo[2], lo[3], cvt_fp8x2<false>(lo[0], lo[1], __float_as_uint(lo[1])));
+  qw[1] = cvt_fp8x2<true>(lo[6], lo[7], cvt_fp8x2<false>(lo[4], lo[5], __float_as_uint(lo[5])));
+  qh[0] = cvt_fp8x2<true>(hi[2], hi[3], cvt_fp8x2<false>(hi[0], hi[1], __float_as_uint(hi[1])));
+  qh[1] = cvt_fp8x2<true>(hi[6], hi[7], cvt_fp8x2<false>(hi[4], hi[5], __float_as_uint(hi[5])));
   if (__builtin_expect(s < 0x1p-100f, 0)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

@@ -64,6 +64,8 @@ def _bind(L):
         f.argtypes = [_p, _p, _i32, _p, _p, _i64, _i64, _i64, _p, _i64]
     L.oracle_num_threads.restype = C.c_int
     L.oracle_num_threads.argtypes = []
+    L.oracle_set_num_threads.restype = None
+    L.oracle_set_num_threads.argtypes = [C.c_int]
     return L
 
 
@@ -101,6 +103,9 @@ class Oracle:
 
     def num_threads(self) -> int:
         return self._L.oracle_num_threads()
+
+    def set_num_threads(self, n: int) -> None:
+        self._L.oracle_set_num_threads(int(n))
 
     # ------------------------------------------------------------- codecs --
     def bf16_from_double(self, v) -> np.ndarray:
@@ -311,6 +316,10 @@ def lib():
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    default().set_num_threads(n)
 
 
 def bf16_from_double(v):

@@ -569,6 +569,18 @@ int oracle_gemm_a8w8_blockscale(const uint8_t* a_q, const float* a_scale, int32_
     return 0;
 }
 
+/* Threads the oracle's parallel loops use from now on (n >= 1): the
+ * process environment may fix OMP_NUM_THREADS for every child process, so
+ * the thread count is set through the runtime instead. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

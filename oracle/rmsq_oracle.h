@@ -101,6 +101,7 @@ int oracle_gemm_a8w8_blockscale(const uint8_t* a_q, const float* a_scale, int32_
                                 int64_t M, int64_t N, int64_t K, double* out, int64_t ldc);
 
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
