@@ -63,11 +63,11 @@ def algorithmic_bytes(M, N, fmt, residual, keep_bf16):
 class Workload:
     """Rotating sets of device buffers for one or more problems launched together."""
 
-    def __init__(self, name, specs, fmt, layout=0):
+    def __init__(self, name, specs, fmt, layout=0, hint=None):
         import torch
         import fp4_quant_amd as fq
         from fp4_quant_amd import inputs
-        self.name, self.fmt, self.layout = name, fmt, layout
+        self.name, self.fmt, self.layout, self.hint = name, fmt, layout, hint
         self.bytes = sum(algorithmic_bytes(s["M"], s["N"], fmt, s["residual"], s["keep_bf16"]) for s in specs)
         self.keep_bf16 = specs[0]["keep_bf16"]
         self.rows = sum(s["M"] for s in specs)
@@ -104,11 +104,11 @@ class Workload:
 
     def launch(self, i, stream=None):
         import fp4_quant_amd as fq
-        fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0], stream or self.stream)
+        fq.rmsnorm_quant_group_multi(self.sets[i % len(self.sets)][0], stream or self.stream, hint=self.hint)
 
     def plan(self):
         import fp4_quant_amd as fq
-        return fq.rmsq_plan_launch(self.sets[0][0])
+        return fq.rmsq_plan_launch(self.sets[0][0], self.hint)
 
     def capture(self, rows=512):
         """The first `rows` rows of each problem's outputs in buffer set 0, on
@@ -151,7 +151,8 @@ class FloorWorkload:
         self.w = w
         plan = fq.rmsq_launch_plan()
         arr = w.sets[0][0]
-        if fq.lib().rmsq_plan_launch(arr, len(arr), None, C.byref(plan)) != 0:
+        hint = C.byref(w.hint) if getattr(w, "hint", None) is not None else None
+        if fq.lib().rmsq_plan_launch(arr, len(arr), hint, C.byref(plan)) != 0:
             raise RuntimeError(fq.lib().rmsq_last_error().decode())
         self.infos = [plan.launch[k] for k in range(plan.launches)]
         self.L = _stream_probe()
@@ -713,7 +714,7 @@ def measure_config(name, args, captured, hashes):
     rec = {"us_per_launch": round(pl * 1e3, 2), "us_windows": [round(t * 1e3, 2) for t in ws],
            "GBps": round(gb, 1), "frac_of_peak": round(gb / HBM_PEAK_GBPS, 4),
            "Mtok_per_s": round(wk.rows / (pl * 1e-3) / 1e6, 2), "bytes": wk.bytes,
-           "plan": [{k: l[k] for k in ("chunks_per_lane", "waves_per_row", "rows_per_workgroup", "row_splits",
+           "plan": [{k: l[k] for k in ("chunks_per_lane", "waves_per_row", "waves_per_workgroup", "row_splits",
                                        "workgroups", "threads_per_workgroup")} for l in wk.plan()]}
     tr = recorded_traffic(name)
     if tr is not None:

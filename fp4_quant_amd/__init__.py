@@ -57,14 +57,14 @@ class rmsq_problem(C.Structure):
 
 class rmsq_launch_hint(C.Structure):
     _fields_ = [("chunks_per_lane", C.c_int32), ("waves_per_row", C.c_int32), ("row_group", C.c_int32),
-                ("rows_per_workgroup", C.c_int32), ("row_splits", C.c_int32)]
+                ("waves_per_workgroup", C.c_int32), ("row_splits", C.c_int32), ("lanes_per_row", C.c_int32)]
 
 
 class rmsq_launch_info(C.Structure):
     _fields_ = [("problems", C.c_int32), ("rows", C.c_int32), ("chunks_per_lane", C.c_int32),
-                ("waves_per_row", C.c_int32), ("rows_per_workgroup", C.c_int32), ("row_splits", C.c_int32),
+                ("waves_per_row", C.c_int32), ("waves_per_workgroup", C.c_int32), ("row_splits", C.c_int32),
                 ("row_group", C.c_int32), ("threads_per_workgroup", C.c_int32), ("workgroups", C.c_int64),
-                ("residual", C.c_int32), ("tail", C.c_int32)]
+                ("residual", C.c_int32), ("tail", C.c_int32), ("lanes_per_row", C.c_int32 * 4)]
 
 
 class rmsq_launch_plan(C.Structure):
@@ -250,9 +250,10 @@ def problem_array(problems):
     return (rmsq_problem * len(problems))(*problems)
 
 
-def launch_hint(J=0, W=0, row_group=0, rows_per_workgroup=0, row_splits=0) -> rmsq_launch_hint:
+def launch_hint(J=0, W=0, row_group=0, waves_per_workgroup=0, row_splits=0, lanes_per_row=0) -> rmsq_launch_hint:
     """A per-call launch hint (0 = the library's choice for that field)."""
-    return rmsq_launch_hint(int(J), int(W), int(row_group), int(rows_per_workgroup), int(row_splits))
+    return rmsq_launch_hint(int(J), int(W), int(row_group), int(waves_per_workgroup), int(row_splits),
+                            int(lanes_per_row))
 
 
 def rmsnorm_quant_group_multi(problems, stream=None, hint=None) -> None:
@@ -274,8 +275,12 @@ def rmsq_plan_launch(problems, hint=None):
     arr = problems if isinstance(problems, C.Array) else problem_array(problems)
     plan = rmsq_launch_plan()
     _check(lib().rmsq_plan_launch(arr, len(arr), C.byref(hint) if hint is not None else None, C.byref(plan)))
-    return [{f: getattr(plan.launch[k], f) for f, _ in rmsq_launch_info._fields_}
-            for k in range(plan.launches)]
+    out = []
+    for k in range(plan.launches):
+        d = {f: getattr(plan.launch[k], f) for f, _ in rmsq_launch_info._fields_}
+        d["lanes_per_row"] = list(d["lanes_per_row"])[:d["problems"]]
+        out.append(d)
+    return out
 
 
 def add_rmsnorm(x, residual_in, gamma, eps, M, N, residual_out, out_bf16, stream=None) -> None:

@@ -160,13 +160,19 @@ rmsq_status check_problem(const rmsq_problem& p, int idx, int32_t fmt0, Mode mod
 // rows per compute unit each row's latency counts most: there the most waves
 // win (J 1 x 14 waves for 64 rows of 7168: 6.3 us against 6.8 us for J 2 x 7;
 // 512 rows 8.42 against 8.63 us; from 768 rows J 2 x 7 is faster again:
-// 10.9 against 12.4 us).
+// 10.9 against 12.4 us). Rows of at most 64 chunks take one chunk per lane:
+// packed, they then share a wave 16, 32 or 64 lanes each.
 constexpr int kJs[] = {2, 3, 4, 1, 7, 8, 14};
 constexpr int kJsFewRows[] = {1, 2, 3, 4, 7, 8, 14};
 constexpr int kWaveRowsPerBlock = 8;
 constexpr int kMaxSplits = 8;
 
 void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
+  if (C <= 64) {
+    *J_out = 1;
+    *W_out = 1;
+    return;
+  }
   const bool few = rows <= 2 * kComputeUnits;
   for (int pass = 0; pass < 3; ++pass) {
     for (int k = 0; k < 7; ++k) {
@@ -193,41 +199,54 @@ void pick_shape(int64_t C, int64_t rows, int* J_out, int* W_out) {
 
 // The exact and uniform tails are used for J <= 4 only: the long per-lane
 // shapes (very wide rows) keep their bounds, which also keeps them within the
-// register budget; the uniform tail is compiled for packed rows only.
+// register budget; the uniform tail is compiled for rows packed one per wave
+// only (with one chunk per lane it coincides with the exact one).
 template <int FMT, bool RES, int TAIL>
-void launch_res(const rmsq::Launch& L, int J, int R, const dim3 grid, const dim3 block, hipStream_t stream) {
+void launch_res(const rmsq::Launch& L, int J, int pack, const dim3 grid, const dim3 block, hipStream_t stream) {
+  using rmsq::rmsq_fused_kernel;
   constexpr int kPackedTail = TAIL;
   constexpr int kRowTail = TAIL == rmsq::kUniform ? rmsq::kRagged : TAIL;
-  if (R > 1) {   // one row per wave, R rows per workgroup (J <= 4 only)
+  if (pack == rmsq::kPackLanes) {   // one chunk per lane, 16 to 64 lanes per row
+    hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 1, RES, rmsq::kPackLanes, kRowTail>), grid, block, 0, stream,
+                       RMSQ_LAUNCH_ARGS(L));
+    return;
+  }
+  if (pack == rmsq::kPackWave) {   // one row per wave (J <= 4 only)
+    constexpr int P = rmsq::kPackWave;
     switch (J) {
-      case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, true, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-      case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, true, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-      case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, true, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-      default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, true, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      case 4: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 4, RES, P, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      case 3: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 3, RES, P, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      case 2: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 2, RES, P, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+      default: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 1, RES, P, kPackedTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
     }
     return;
   }
+  constexpr int N = rmsq::kPackNone;
   switch (J) {
-    case 14: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 14, RES, false, rmsq::kRagged>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 8: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 8, RES, false, rmsq::kRagged>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 7: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 7, RES, false, rmsq::kRagged>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 4: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 4, RES, false, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 3: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 3, RES, false, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    case 2: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 2, RES, false, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
-    default: hipLaunchKernelGGL((rmsq::rmsq_fused_kernel<FMT, 1, RES, false, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 14: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 14, RES, N, rmsq::kRagged>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 8: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 8, RES, N, rmsq::kRagged>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 7: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 7, RES, N, rmsq::kRagged>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 4: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 4, RES, N, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 3: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 3, RES, N, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    case 2: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 2, RES, N, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
+    default: hipLaunchKernelGGL((rmsq_fused_kernel<FMT, 1, RES, N, kRowTail>), grid, block, 0, stream, RMSQ_LAUNCH_ARGS(L)); break;
   }
 }
 
 // One launch of up to four problems with the shape chosen for it; they
 // either all have a residual or none has (the caller splits a mixed set).
-// R > 1: W is 1 and R rows share a workgroup, one per wave.
+// R > 1: packed rows, W is 1 and a workgroup has R waves, each holding one
+// row (pack = kPackWave) or, with one chunk per lane, one row per
+// 2^lanes_log2 lanes (kPackLanes; L.rows then counts waves).
 struct Plan {
   rmsq::Launch L;
   int J, W, R;
+  int pack;       // rmsq::Pack
+  int64_t rows;   // rows over the launch's problems
   dim3 grid, block;
 };
 
-// The launch's grid: one workgroup per row (R > 1: per R rows; with row
+// The launch's grid: one workgroup per row (R > 1: per R waves; with row
 // splits, per split of a row, the rows padded to a multiple of 8).
 void plan_grid(Plan& P) {
   const rmsq::Launch& L = P.L;
@@ -237,18 +256,23 @@ void plan_grid(Plan& P) {
   P.block = dim3((unsigned)(64 * (P.R > 1 ? P.R : P.W)));
 }
 
-// How the launch's rows end (rmsq::Tail): every row exactly fills its
-// J*64*W lanes (J*64 when packed) - exact; packed rows that are all a whole
-// number of 64-lane steps - uniform; otherwise ragged. Row splits are ragged.
+// Lanes holding one row of problem i: 64 x W, or packed 2^lanes_log2.
+int64_t row_lanes(const Plan& P, int i) { return P.R > 1 ? int64_t{1} << P.L.p[i].lanes_log2 : 64 * P.W; }
+
+
+// How the launch's rows end (rmsq::Tail): every row exactly fills its J x T
+// lanes (T lanes per row) - exact; packed rows that are all a whole number of
+// T-lane steps - uniform; otherwise ragged. Packed launches whose last wave
+// of a problem is partly empty, and row splits, are ragged.
 int launch_tail(const Plan& P) {
   const rmsq::Launch& L = P.L;
   if (L.splits_log2 != 0 || P.J > 4) return rmsq::kRagged;
-  const int64_t T = 64 * (P.R > 1 ? 1 : P.W);
   bool exact = true, uniform = P.R > 1;
   for (int i = 0; i < L.count; ++i) {
-    const int64_t C = L.p[i].N >> 3;
-    exact &= C == P.J * T;
-    uniform &= C % T == 0 && C <= P.J * T;
+    const int64_t C = L.p[i].N >> 3, T = row_lanes(P, i);
+    const bool full = P.pack != rmsq::kPackLanes || L.p[i].M % (64 / T) == 0;
+    exact &= C == P.J * T && full;
+    uniform &= C % T == 0 && C <= P.J * T && full;
   }
   return exact ? rmsq::kExact : uniform ? rmsq::kUniform : rmsq::kRagged;
 }
@@ -259,14 +283,14 @@ rmsq_status launch_fmt(const Plan& P, hipStream_t stream) {
   const int tail = launch_tail(P);
   const bool res = L.p[0].r != nullptr;
   if (tail == rmsq::kExact) {
-    if (res) launch_res<FMT, true, rmsq::kExact>(L, P.J, P.R, P.grid, P.block, stream);
-    else launch_res<FMT, false, rmsq::kExact>(L, P.J, P.R, P.grid, P.block, stream);
+    if (res) launch_res<FMT, true, rmsq::kExact>(L, P.J, P.pack, P.grid, P.block, stream);
+    else launch_res<FMT, false, rmsq::kExact>(L, P.J, P.pack, P.grid, P.block, stream);
   } else if (tail == rmsq::kUniform) {
-    if (res) launch_res<FMT, true, rmsq::kUniform>(L, P.J, P.R, P.grid, P.block, stream);
-    else launch_res<FMT, false, rmsq::kUniform>(L, P.J, P.R, P.grid, P.block, stream);
+    if (res) launch_res<FMT, true, rmsq::kUniform>(L, P.J, P.pack, P.grid, P.block, stream);
+    else launch_res<FMT, false, rmsq::kUniform>(L, P.J, P.pack, P.grid, P.block, stream);
   } else {
-    if (res) launch_res<FMT, true, rmsq::kRagged>(L, P.J, P.R, P.grid, P.block, stream);
-    else launch_res<FMT, false, rmsq::kRagged>(L, P.J, P.R, P.grid, P.block, stream);
+    if (res) launch_res<FMT, true, rmsq::kRagged>(L, P.J, P.pack, P.grid, P.block, stream);
+    else launch_res<FMT, false, rmsq::kRagged>(L, P.J, P.pack, P.grid, P.block, stream);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RMSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -290,11 +314,13 @@ rmsq_status check_hint(const rmsq_launch_hint* h) {
                 h->waves_per_row);
   if (h->row_group < 0 || h->row_group > 64)
     return fail(RMSQ_ERR_INVALID_ARG, "hint: row_group %d outside 0..64", h->row_group);
-  if (h->rows_per_workgroup < 0 || h->rows_per_workgroup > rmsq::kMaxWaves)
-    return fail(RMSQ_ERR_INVALID_ARG, "hint: rows_per_workgroup %d outside 0..%d", h->rows_per_workgroup,
+  if (h->waves_per_workgroup < 0 || h->waves_per_workgroup > rmsq::kMaxWaves)
+    return fail(RMSQ_ERR_INVALID_ARG, "hint: waves_per_workgroup %d outside 0..%d", h->waves_per_workgroup,
                 rmsq::kMaxWaves);
   if (h->row_splits < 0 || h->row_splits > kMaxSplits)
     return fail(RMSQ_ERR_INVALID_ARG, "hint: row_splits %d outside 0..%d", h->row_splits, kMaxSplits);
+  if (h->lanes_per_row != 0 && h->lanes_per_row != 16 && h->lanes_per_row != 32 && h->lanes_per_row != 64)
+    return fail(RMSQ_ERR_INVALID_ARG, "hint: lanes_per_row %d is not 0, 16, 32 or 64", h->lanes_per_row);
   return RMSQ_OK;
 }
 
@@ -310,7 +336,7 @@ rmsq_status plan(const rmsq_problem* ps, int32_t count, Mode mode, const rmsq_la
   if (count < 1 || count > RMSQ_MAX_PROBLEMS)
     return fail(RMSQ_ERR_INVALID_ARG, "count = %d outside 1..%d", count, RMSQ_MAX_PROBLEMS);
   if (const rmsq_status s = check_hint(hint); s != RMSQ_OK) return s;
-  const rmsq_launch_hint h = hint ? *hint : rmsq_launch_hint{0, 0, 0, 0, 0};
+  const rmsq_launch_hint h = hint ? *hint : rmsq_launch_hint{0, 0, 0, 0, 0, 0};
   Range rs[RMSQ_MAX_PROBLEMS * 7];
   int nr = 0;
   for (int i = 0; i < count; ++i) {
@@ -378,7 +404,7 @@ rmsq_status plan(const rmsq_problem* ps, int32_t count, Mode mode, const rmsq_la
     // enough of them to fill the machine (a CU holds only so many
     // workgroups, so one-wave workgroups leave wave slots empty).
     int R = 1;
-    if (W == 1 && J <= 4) R = h.rows_per_workgroup > 0 ? h.rows_per_workgroup
+    if (W == 1 && J <= 4) R = h.waves_per_workgroup > 0 ? h.waves_per_workgroup
                                                        : (rows >= 4 * kComputeUnits ? kWaveRowsPerBlock : 1);
     int lgR = 0;
     while ((2 << lgR) <= R) ++lgR;
@@ -403,6 +429,48 @@ rmsq_status plan(const rmsq_problem* ps, int32_t count, Mode mode, const rmsq_la
       while (S > 1 && Cmin / q < S) S /= 2;   // at least one group per split
       while ((1 << L.splits_log2) < S) ++L.splits_log2;
       if (S > 1) L.row_group_log2 = 0;
+    }
+    // Packed rows of one chunk per lane: each problem's rows take 2^k lanes
+    // (16, 32 or 64), the fewest that hold the row unless the hint fixes
+    // them, so a wave holds 2^(6-k) rows and their statistics share one
+    // instruction sequence (128-wide rows: four per wave). Measured against
+    // one row per wave (16384 rows, MI355X): 5.3 against 9.0 us for rows of
+    // 128, 8.0 against 12.7 us for rows of 256 with a residual. The launch
+    // then counts waves: problem i fills waves row_begin[i] ... (its last one
+    // possibly part empty). Wider rows, and more chunks per lane, keep one
+    // row per wave.
+    P.rows = rows;
+    P.pack = R > 1 ? rmsq::kPackWave : rmsq::kPackNone;
+    for (int i = 0; i < n; ++i) L.p[i].lanes_log2 = 6;
+    if (h.lanes_per_row > 0 && h.lanes_per_row < 64 && R > 1 && J != 1)
+      return fail(RMSQ_ERR_INVALID_ARG, "hint: %d lanes per row needs one chunk per lane (the launch has %d)",
+                  h.lanes_per_row, J);
+    if (R > 1 && J == 1) {
+      bool lanes = false;
+      for (int i = 0; i < n; ++i) {
+        rmsq::Problem& d = L.p[i];
+        const int64_t C = d.N / 8;
+        int lt = 4;
+        if (h.lanes_per_row > 0) {
+          while ((1 << lt) < h.lanes_per_row) ++lt;
+          if (C > int64_t{1} << lt)
+            return fail(RMSQ_ERR_INVALID_ARG, "hint: %d lanes per row do not hold rows of %lld elements",
+                        h.lanes_per_row, (long long)C * 8);
+        } else {
+          while (lt < 6 && C > int64_t{1} << lt) ++lt;
+        }
+        d.lanes_log2 = lt;
+        lanes |= lt < 6;
+      }
+      if (lanes) {
+        P.pack = rmsq::kPackLanes;
+        int64_t waves = 0;
+        for (int i = 0; i < n; ++i) {
+          L.row_begin[i] = (int32_t)waves;
+          waves += (L.p[i].M + (64 >> L.p[i].lanes_log2) - 1) >> (6 - L.p[i].lanes_log2);
+        }
+        L.rows = (int32_t)waves;
+      }
     }
     P.J = J;
     P.W = W;
@@ -519,16 +587,17 @@ rmsq_status rmsq_plan_launch(const rmsq_problem* problems, int32_t count, const 
     const Plan& P = plans[k];
     rmsq_launch_info& d = out->launch[k];
     d.problems = P.L.count;
-    d.rows = P.L.rows;
+    d.rows = (int32_t)P.rows;
     d.chunks_per_lane = P.J;
     d.waves_per_row = P.W;
-    d.rows_per_workgroup = P.R;
+    d.waves_per_workgroup = P.R;
     d.row_splits = 1 << P.L.splits_log2;
     d.row_group = 1 << P.L.row_group_log2;
     d.workgroups = (int64_t)P.grid.x;
     d.threads_per_workgroup = (int32_t)P.block.x;
     d.residual = P.L.p[0].r != nullptr;
     d.tail = launch_tail(P);
+    for (int i = 0; i < P.L.count; ++i) d.lanes_per_row[i] = (int32_t)row_lanes(P, i);
   }
   return RMSQ_OK;
 }

@@ -276,32 +276,58 @@ __device__ __forceinline__ uint32_t max4(uint32_t v) {
   return v;
 }
 
+// DPP row rotation of a double (both halves): lane i of each 16-lane row
+// reads lane (i + N) mod 16 of that row. Every lane must be active; with
+// bound_ctrl and all rows and banks enabled every lane is written, so no old
+// value is needed (and none is copied in).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)any_u32(), (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)any_u32(), (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ double readlane_f64(double v, int lane) {
+// v + (the same lane of the neighbouring 16-lane row): rows 0 and 1 both get
+// r0 + r1, rows 2 and 3 both get r2 + r3 (v_permlane16_swap exchanges the odd
+// rows of its first operand with the even rows of its second; with both
+// operands v the two results hold r0 r0 r2 r2 and r1 r1 r3 r3).
+__device__ __forceinline__ double add_rows16(double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
+         __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
 }
 
-// Sum over the 64 lanes of a (fully active) wave in a fixed order: DPP
-// rotations within each 16-lane row (addition is commutative, so every lane of
-// a row ends with the same value), then the four row sums in a fixed tree.
-// The result is wave-uniform.
-__device__ __forceinline__ double wave_sum(double v) {
+// v + (the same lane of the other 32-lane half): v_permlane32_swap exchanges
+// rows 2-3 of its first operand with rows 0-1 of its second, so with both
+// operands v the results hold r0 r1 r0 r1 and r2 r3 r2 r3.
+__device__ __forceinline__ double add_halves32(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
+         __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
+}
+
+// Sum over each aligned group of 2^lt lanes (lt = 4, 5 or 6) of a fully
+// active wave, in a fixed order: DPP rotations within each 16-lane row
+// (addition is commutative, so every lane of a row ends with the same value),
+// then rows 0+1 and 2+3, then the two pairs. Every lane gets its group's sum,
+// bit-identical across the group.
+__device__ __forceinline__ double lanes_sum(double v, int lt) {
   v += dpp_f64<0x128>(v);
   v += dpp_f64<0x124>(v);
   v += dpp_f64<0x122>(v);
   v += dpp_f64<0x121>(v);
-  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+  if (lt >= 5) v = add_rows16(v);
+  if (lt >= 6) v = add_halves32(v);
+  return v;
 }
+
+// Sum over the 64 lanes of a wave: (r0 + r1) + (r2 + r3) of the row sums.
+__device__ __forceinline__ double wave_sum(double v) { return lanes_sum(v, 6); }
 
 // Largest |value| of eight packed bf16 (four dwords), as a bf16 magnitude
 // pattern: integer max of (bits & 0x7FFF) orders bf16 magnitudes exactly.

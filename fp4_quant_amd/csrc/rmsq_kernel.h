@@ -10,6 +10,9 @@
 //
 // Mapping. One workgroup per token row, 64*W threads (W waves, runtime),
 // each lane owning J chunks of 8 bf16 (16 bytes): chunk c = j*64*W + lane.
+// Short rows are packed instead, several waves per workgroup: one row per
+// wave (chunk c = j*64 + lane), or rows of at most 32 chunks one per group of
+// 16 or 32 lanes (one chunk per lane).
 // All of a row's loads are issued before any arithmetic; the row then stays
 // in registers across the one reduction, and every output is stored once.
 // Loads and stores are 16-byte and coalesced across the wave. A 128-element
@@ -56,6 +59,7 @@ struct Problem {
   int32_t layout;         // scale layout: 0 row-major, 1 32-row tiles (MXFP4), 2 column-major
   float eps;
   double rn;              // 1/N rounded to nearest (host division)
+  int32_t lanes_log2;     // rows packed by lanes: 2^k lanes per row (k = 4, 5 or 6)
 };
 
 constexpr int kMaxProblems = 4;
@@ -64,26 +68,26 @@ constexpr int kMaxWaves = 16;
 // they are launched with at most 4 waves per row so the register budget is
 // not cut to 128 by a 1024-thread bound.
 constexpr int max_waves(int J) { return J >= 7 ? 4 : kMaxWaves; }
-// Rows of 3 chunks per lane packed one per wave (the 1536-wide MLA latent
-// rows) are launched 8 rows per workgroup; held to 64 VGPRs, 8 waves fit on
-// each SIMD, so four such workgroups per compute unit and a 4096 + 4096-row
-// launch is resident at once (at 72 VGPRs only three fit and a third of the
-// grid waits for a second round).
-constexpr int min_waves_per_simd(int J, bool wave_rows) { return wave_rows && J == 3 ? 8 : 1; }
-
 // Launch description. The scalars are also passed as the kernel's leading
 // int arguments, which the library is built to have preloaded into SGPRs at
 // wave launch (gfx950 kernel-argument preloading), so only the selected
 // problem's fields are read from the argument block.
 struct Launch {
   int32_t count;
-  int32_t rows;           // rows over all problems
-  int32_t row_group_log2; // 2^k consecutive rows kept together on one XCD (0 = dispatch order)
+  int32_t rows;           // launch units over all problems: rows, or waves with packed rows
+  int32_t row_group_log2; // 2^k consecutive rows (packed: workgroups) kept together on one
+                          // XCD (0 = dispatch order)
   int32_t splits_log2;    // 2^k workgroups per row: each computes the row's statistics
                           // and normalizes / quantizes its own share of the row
-  int32_t row_begin[kMaxProblems];  // first launch row of each problem (increasing)
+  int32_t row_begin[kMaxProblems];  // first launch unit of each problem (increasing)
   Problem p[kMaxProblems];
 };
+
+// Rows packed by lanes: problem p fills the launch waves from row_begin[p]
+// on, 2^(6-lt) rows per wave with lt = its lanes_log2. Lane l of the
+// problem's wave u works on row (u << (6 - lt)) + (l >> lt), as lane
+// l & (2^lt - 1) of that row.
+__device__ __forceinline__ int32_t packed_row(int32_t u, int lt, int lane) { return (u << (6 - lt)) + (lane >> lt); }
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
 // L2. With g = 2^lg > 1, every run of g consecutive rows is processed on one
@@ -101,24 +105,45 @@ __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t
 
 // RES: every problem of the launch has a residual (otherwise none has), so
 // the loads of x, r and gamma form one straight block with no branch.
-// WAVE_ROWS: rows short enough for one wave (J*64 chunks) are packed one per
-// wave, blockDim/64 consecutive rows per workgroup, with no LDS and no
-// barrier; otherwise the workgroup's waves share one row.
+// PACK: how rows map to lanes.
+//   kPackNone   the workgroup's waves share one row (LDS for the reduction);
+//   kPackWave   rows short enough for one wave (J*64 chunks) are packed one
+//               per wave, blockDim/64 consecutive rows per workgroup, with no
+//               LDS and no barrier;
+//   kPackLanes  (J = 1) likewise, but one row per group of T = 16, 32 or 64
+//               lanes, per problem: rows of 128 or 256 elements fill a wave
+//               4 or 2 at a time instead of leaving 48 or 32 lanes idle (the
+//               row index is then per lane, which costs the one-per-wave
+//               layout a few percent, so it stays separate).
 // TAIL: how the rows of the launch end (T lanes per row, no row splits
 // except with kRagged):
-//   kExact    every row has exactly J*T chunks, so no lane needs a bound (the
-//             usual shapes: 7168 = 2 x 7 waves or 1 x 14, 1536 = 3 x 1,
-//             512 = 1 x 1);
+//   kExact    every row has exactly J*T chunks and every lane group of a
+//             packed launch has a row, so no lane needs a bound (the usual
+//             shapes: 7168 = 2 x 7 waves or 1 x 14, 1536 = 3 x 1, 512 = 1 x 1);
 //   kUniform  every row has a whole number of chunk steps (a multiple of T
-//             chunks, at most J*T): steps past a row's end are skipped by the
-//             whole wave, with a scalar test, and their loads re-read the last
-//             step (packed rows only: the MLA latents, 1536 and 512 wide, in
-//             one launch);
-//   kRagged   anything else: lanes past the row end clamp their chunk index.
+//             chunks, at most J*T) and every lane group has a row: steps past
+//             a row's end are skipped by the whole wave, with a scalar test,
+//             and their loads re-read the last step (rows packed one per wave
+//             only: the MLA latents, 1536 and 512 wide, in one launch);
+//   kRagged   anything else: lanes past the row end clamp their chunk index,
+//             and lane groups past a problem's last row reload that row and
+//             store nothing.
 enum Tail { kRagged = 0, kExact = 1, kUniform = 2 };
+enum Pack { kPackNone = 0, kPackWave = 1, kPackLanes = 2 };
 
-template <int FMT, int J, bool RES, bool WAVE_ROWS, int TAIL>
-__global__ void __launch_bounds__(64 * max_waves(J), min_waves_per_simd(J, WAVE_ROWS))
+// Packed rows of 3 chunks per lane (the 1536-wide MLA latent rows), and of 4
+// when quantized without a residual and bounded (the MLA latents in 4-chunk
+// steps), are launched 8 waves per workgroup; held to
+// 64 VGPRs, 8 waves fit on each SIMD, so four such workgroups per compute
+// unit and a 4096 + 4096-row launch is resident at once (at 72 VGPRs only
+// three fit and a third of the grid waits for a second round). The other
+// 4-chunk variants do not fit that budget without spilling.
+constexpr int min_waves_per_simd(int FMT, int J, bool packed, bool res, int tail) {
+  return packed && (J == 3 || (J == 4 && !res && FMT != 2 && tail != kExact)) ? 8 : 1;
+}
+
+template <int FMT, int J, bool RES, int PACK, int TAIL>
+__global__ void __launch_bounds__(64 * max_waves(J), min_waves_per_simd(FMT, J, PACK != kPackNone, RES, TAIL))
 rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t rb1, int32_t rb2, int32_t rb3,
                   int32_t threads, int32_t blocks, const Launch L) {
   // the ints repeat L's scalars (count, rows, row_group_log2, splits_log2,
@@ -127,16 +152,18 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // together with x and r; long ones keep h packed and fetch gamma late, to
   // stay within the register budget.
   constexpr bool kShort = J <= 4;
-  // Packed rows of 3 chunks per lane (held to 64 VGPRs) unpack h again in
-  // phase 2 rather than keep 24 fp32 copies across the reduction.
-  constexpr bool kKeepH = kShort && !(WAVE_ROWS && J == 3);
+  // Packed rows of 3 or 4 chunks per lane (held to 64 VGPRs) unpack h again
+  // in phase 2 rather than keep 24 or 32 fp32 copies across the reduction.
+  constexpr bool kPacked = PACK != kPackNone;
+  static_assert(PACK != kPackLanes || J == 1, "rows packed by lanes take one chunk per lane");
+  constexpr bool kKeepH = kShort && !(kPacked && J >= 3);
   __shared__ double red[kMaxWaves];
 
   // Neighbouring row groups run on different XCDs at the same time. (Giving
   // each XCD one contiguous block of M/8 rows instead was measured 12%
   // slower on the prefill workload.)
-  int32_t row, split = 0;
-  if constexpr (WAVE_ROWS) {
+  int32_t row, split = 0;   // the launch unit: a row, or with packed rows a wave
+  if constexpr (kPacked) {
     const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
     row = row_of_block((int32_t)blockIdx.x, blocks, lg) * (threads >> 6) + wave;
     if (row >= rows) return;   // the whole wave leaves: nothing below synchronizes
@@ -151,12 +178,20 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
     row = slg > 0 ? ((b >> (3 + slg)) << 3) | (b & 7) : row_of_block(b, rows, lg);
     if (row >= rows) return;   // the whole workgroup leaves before any barrier
   }
-  // problems are consecutive ranges of rows (row_begin increasing)
+  // problems are consecutive ranges of launch units (row_begin increasing)
   const int pi = (count > 1 && row >= rb1) + (count > 2 && row >= rb2) + (count > 3 && row >= rb3);
   const Problem& P = L.p[pi];
-  const int64_t m = row - (pi == 0 ? 0 : pi == 1 ? rb1 : pi == 2 ? rb2 : rb3);
-  const int T = WAVE_ROWS ? 64 : threads;
-  const int tid = WAVE_ROWS ? (threadIdx.x & 63) : threadIdx.x;
+  const int32_t u = row - (pi == 0 ? 0 : pi == 1 ? rb1 : pi == 2 ? rb2 : rb3);
+  const int lt = PACK == kPackLanes ? P.lanes_log2 : 6;
+  const int T = PACK == kPackLanes ? 1 << lt : kPacked ? 64 : threads;
+  const int tid = kPacked ? (int)(threadIdx.x & (T - 1)) : (int)threadIdx.x;
+  int64_t m = u;
+  bool live = true;   // packed by lanes: this lane group has a row of the problem
+  if constexpr (PACK == kPackLanes) {
+    const int32_t r = packed_row(u, lt, threadIdx.x & 63);
+    live = r < P.M;
+    m = live ? r : P.M - 1;
+  }
   const int C = P.N >> 3;
   // what a lane loads at step j: row pointer + load(j), clamped to the row's
   // last step (kUniform: a wave-uniform offset, so the lane offset tid is
@@ -172,8 +207,8 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   };
   // chunks this workgroup normalizes and stores: all of them, or with row
   // splits a range whose ends fall on group boundaries (16 chunks FP8, 4 MXFP4)
-  int lo = 0, hi = C;
-  if (!WAVE_ROWS && slg > 0) {
+  int lo = 0, hi = live ? C : 0;
+  if (!kPacked && slg > 0) {
     constexpr int q = FMT == 0 ? 16 : FMT == 1 ? 4 : 1;
     lo = ((split * (C / q)) >> slg) * q;
     hi = split + 1 == (1 << slg) ? C : (((split + 1) * (C / q)) >> slg) * q;
@@ -249,9 +284,9 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
       ss = __builtin_fma((double)b, (double)b, ss);
     }
   }
-  ss = wave_sum(ss);
+  ss = PACK == kPackLanes ? lanes_sum(ss, lt) : wave_sum(ss);
   const int nw = T >> 6;
-  if (!WAVE_ROWS && nw > 1) {
+  if (!kPacked && nw > 1) {
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     ss = 0.0;

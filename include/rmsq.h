@@ -184,24 +184,33 @@ rmsq_status rmsnorm_quant_group_multi(const rmsq_problem* problems, int32_t coun
  *  row_group  consecutive rows kept on one XCD (1..64, rounded down to a
  *        power of two; 1 = plain dispatch order). Automatic: 16 when a
  *        problem writes tiled or column-major scales, else 1.
- *  rows_per_workgroup  rows packed one per wave per workgroup when a row fits
- *        one wave (1..16). Automatic: 8 once a launch has at least 1024 rows,
- *        else 1. Not used when rows span several waves.
+ *  waves_per_workgroup  packed rows: waves per workgroup when a row fits one
+ *        wave (1..16; 1 = no packing: one row per workgroup). Automatic: 8
+ *        once a launch has at least 1024 rows, else 1. Not used when rows
+ *        span several waves.
+ *  lanes_per_row  packed rows of one chunk per lane (J = 1, rows of at most
+ *        512 elements): lanes per row for every problem of the launch (16, 32
+ *        or 64; a wave then holds 4, 2 or 1 rows, whose statistics share one
+ *        instruction sequence). Automatic, per problem: the fewest that hold
+ *        the row (128-wide rows 16 lanes each). Below 64 with J > 1 it is
+ *        refused; ignored when rows are not packed.
  *  row_splits  workgroups sharing each row (1..8, rounded down to a power of
  *        two; each computes the row's statistics and normalizes / quantizes
  *        its own share of the groups). Automatic: the largest power of two
  *        S <= 8 with rows * S <= 256 for launches of at most 128 rows, else 1.
  *        Rows are never split when a problem's residual is updated in place,
  *        when rows are packed per workgroup, or below one group per split.
- * A field outside its range, or a J x W that does not cover a row, gives
- * RMSQ_ERR_INVALID_ARG (nothing is launched).
+ * A field outside its range, or a J x W (packed by lanes: lanes_per_row)
+ * that does not cover a row, gives RMSQ_ERR_INVALID_ARG (nothing is
+ * launched).
  */
 typedef struct rmsq_launch_hint {
     int32_t chunks_per_lane;
     int32_t waves_per_row;
     int32_t row_group;
-    int32_t rows_per_workgroup;
+    int32_t waves_per_workgroup;
     int32_t row_splits;
+    int32_t lanes_per_row;
 } rmsq_launch_hint;
 
 /* rmsnorm_quant_group_multi with an optional launch hint (NULL: the
@@ -216,7 +225,8 @@ typedef struct rmsq_launch_info {
     int32_t rows;                   /* rows over those problems                 */
     int32_t chunks_per_lane;        /* J                                        */
     int32_t waves_per_row;          /* W                                        */
-    int32_t rows_per_workgroup;     /* R (1: one row, or a share of one, per workgroup) */
+    int32_t waves_per_workgroup;    /* R > 1: packed rows, R waves per workgroup (1: one row,
+                                       or a share of one, per workgroup) */
     int32_t row_splits;             /* S workgroups per row                     */
     int32_t row_group;              /* consecutive rows kept on one XCD         */
     int32_t threads_per_workgroup;
@@ -225,6 +235,8 @@ typedef struct rmsq_launch_info {
     int32_t tail;                   /* how its rows end: 1 every row fills the launch shape exactly,
                                        2 rows one wave each, all whole 64-lane steps (steps past a row's
                                        end skipped by the wave), 0 otherwise (lanes past the end bounded) */
+    int32_t lanes_per_row[4];       /* lanes holding one row of each of its problems: 64 x W; packed
+                                       64, or 16, 32 or 64 when packed by lanes (J = 1) */
 } rmsq_launch_info;
 
 typedef struct rmsq_launch_plan {

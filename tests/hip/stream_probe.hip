@@ -203,10 +203,11 @@ __global__ void __launch_bounds__(1024) k_rows_pol(const u32x4* x, const u32x4* 
 // group) - the values stored are bit mixes of the inputs. Its time is the
 // floor of a launch of that plan: what is left when the statistics, the
 // normalization and the quantization cost nothing.
-template <int FMT, int J, bool RES, bool WAVE_ROWS>
+template <int FMT, int J, bool RES, int PACK>
 __global__ void __launch_bounds__(64 * rmsq::max_waves(J))
 k_plan_floor(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t rb1, int32_t rb2, int32_t rb3,
              int32_t threads, int32_t blocks, const rmsq::Launch L) {
+  constexpr bool WAVE_ROWS = PACK != rmsq::kPackNone;
   __shared__ uint32_t red[rmsq::kMaxWaves];
   int32_t row, split = 0;
   if constexpr (WAVE_ROWS) {
@@ -221,11 +222,19 @@ k_plan_floor(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t rb1, 
   }
   const int pi = (count > 1 && row >= rb1) + (count > 2 && row >= rb2) + (count > 3 && row >= rb3);
   const rmsq::Problem& P = L.p[pi];
-  const int64_t m = row - (pi == 0 ? 0 : pi == 1 ? rb1 : pi == 2 ? rb2 : rb3);
-  const int T = WAVE_ROWS ? 64 : threads;
-  const int tid = WAVE_ROWS ? (threadIdx.x & 63) : threadIdx.x;
+  const int32_t u = row - (pi == 0 ? 0 : pi == 1 ? rb1 : pi == 2 ? rb2 : rb3);
+  const int lt = PACK == rmsq::kPackLanes ? P.lanes_log2 : 6;
+  const int T = PACK == rmsq::kPackLanes ? 1 << lt : WAVE_ROWS ? 64 : threads;
+  const int tid = WAVE_ROWS ? (int)(threadIdx.x & (T - 1)) : (int)threadIdx.x;
+  int64_t m = u;
+  bool live = true;
+  if constexpr (PACK == rmsq::kPackLanes) {
+    const int32_t r = rmsq::packed_row(u, lt, threadIdx.x & 63);
+    live = r < P.M;
+    m = live ? r : P.M - 1;
+  }
   const int C = P.N >> 3;
-  int lo = 0, hi = C;
+  int lo = 0, hi = live ? C : 0;
   if (!WAVE_ROWS && slg > 0) {
     constexpr int q = FMT == 0 ? 16 : 4;
     lo = ((split * (C / q)) >> slg) * q;
@@ -385,27 +394,47 @@ int stream_probe_plan_floor(const rmsq_problem* ps, int32_t count, const rmsq_la
     d.M = (int32_t)p.M;
     d.N = (int32_t)p.N;
     d.layout = p.scale_layout;
+    d.lanes_log2 = 6;
     L.row_begin[n - 1] = (int32_t)rows;
     rows += p.M;
   }
   if (n != info->problems || rows != info->rows) return 1;
   L.count = n;
   L.rows = (int32_t)rows;
+  bool lanes = false;   // rows packed by lanes: the launch counts waves
+  if (info->waves_per_workgroup > 1) {
+    for (int i = 0; i < n; ++i) {
+      const int32_t T = info->lanes_per_row[i];
+      if (T != 16 && T != 32 && T != 64) return 1;
+      L.p[i].lanes_log2 = T == 16 ? 4 : T == 32 ? 5 : 6;
+      lanes |= T < 64;
+    }
+  }
+  if (lanes) {
+    if (info->chunks_per_lane != 1) return 1;
+    int64_t waves = 0;
+    for (int i = 0; i < n; ++i) {
+      L.row_begin[i] = (int32_t)waves;
+      waves += (L.p[i].M + (64 >> L.p[i].lanes_log2) - 1) >> (6 - L.p[i].lanes_log2);
+    }
+    L.rows = (int32_t)waves;
+  }
   int lg = 0, slg = 0;
   while ((1 << lg) < info->row_group) ++lg;
   while ((1 << slg) < info->row_splits) ++slg;
   L.row_group_log2 = lg;
   L.splits_log2 = slg;
   const dim3 g((unsigned)info->workgroups), t((unsigned)info->threads_per_workgroup);
-  const bool packed = info->rows_per_workgroup > 1, res = info->residual != 0, fp4 = ps[0].fmt == 1;
+  const bool packed = info->waves_per_workgroup > 1, res = info->residual != 0, fp4 = ps[0].fmt == 1;
   hipStream_t s = (hipStream_t)stream;
 #define FLOOR_ARGS L.count, L.rows, L.row_group_log2, L.splits_log2, L.row_begin[1], L.row_begin[2], L.row_begin[3], \
                    (int32_t)t.x, (int32_t)g.x, L
-#define FLOOR_J(F, JJ, R)                                                                           \
-  if (info->chunks_per_lane == JJ) {                                                                \
-    if (packed) hipLaunchKernelGGL((k_plan_floor<F, JJ, R, true>), g, t, 0, s, FLOOR_ARGS);         \
-    else hipLaunchKernelGGL((k_plan_floor<F, JJ, R, false>), g, t, 0, s, FLOOR_ARGS);               \
-    return st_rc();                                                                                 \
+#define FLOOR_J(F, JJ, R)                                                                             \
+  if (info->chunks_per_lane == JJ) {                                                                  \
+    if (JJ == 1 && lanes) hipLaunchKernelGGL((k_plan_floor<F, 1, R, rmsq::kPackLanes>), g, t, 0, s, FLOOR_ARGS); \
+    else if (packed) hipLaunchKernelGGL((k_plan_floor<F, JJ, R, rmsq::kPackWave>), g, t, 0, s, FLOOR_ARGS);      \
+    else hipLaunchKernelGGL((k_plan_floor<F, JJ, R, rmsq::kPackNone>), g, t, 0, s, FLOOR_ARGS);                  \
+    return st_rc();                                                                                   \
   }
 #define FLOOR_F(F, R) FLOOR_J(F, 1, R) FLOOR_J(F, 2, R) FLOOR_J(F, 3, R) FLOOR_J(F, 4, R)
   if (!fp4 && res) { FLOOR_F(0, true) }

@@ -177,6 +177,9 @@ def test_mla_two_problems_one_launch_from_one_projection_buffer(orc):
     probs = [{"x": pq["x"], "gamma": pq["gamma"], "eps": 1e-6, "ldx": 2112},
              {"x": pk["x"], "gamma": pk["gamma"], "eps": 1e-6, "ldx": 2112}]
     check(orc, probs)
+    # in 4-chunk steps (the kv rows then use one of four)
+    say("workload mla hint J=4")
+    check(orc, probs, hint=fq.launch_hint(4, 1))
 
 
 def test_single_entry_point(orc):
@@ -230,12 +233,52 @@ def test_rows_packed_one_per_wave(orc, R):
         say(f"packed rows R={R} M={M} N={N} fmt={fmt} layout={lay}")
         p = inputs.make_problem(M, N, seed_x=600 + k, residual=res, outliers=True)
         check(orc, [dict(p, fmt=fmt, scale_layout=lay, keep_bf16=(k % 2 == 0))],
-              hint=fq.launch_hint(rows_per_workgroup=R))
+              hint=fq.launch_hint(waves_per_workgroup=R))
     a = inputs.make_problem(515, 1536, seed_x=610, residual=False, outliers=True)
     b = inputs.make_problem(299, 512, seed_x=611, residual=False, outliers=True)
     for g in (0, 16, 64):
         check(orc, [dict(a, fmt=0, scale_layout=2), dict(b, fmt=0, scale_layout=0, keep_bf16=True)],
-              hint=fq.launch_hint(rows_per_workgroup=R, row_group=g))
+              hint=fq.launch_hint(waves_per_workgroup=R, row_group=g))
+
+
+@pytest.mark.parametrize("R", [2, 8])
+def test_rows_packed_by_lanes(orc, R):
+    """Rows of at most 256 elements packed 16 or 32 lanes each (4 or 2 rows
+    per wave, one chunk per lane): row counts that leave a problem's last
+    wave part empty, rows narrower than their lanes, both formats, every
+    scale layout (the tiled MXFP4 layout with the rows of one tile spread
+    over several waves), residual or not, and problems of different widths
+    and lanes in one launch."""
+    for k, (M, N, fmt, lay, res, T) in enumerate([
+            (37, 128, 0, 0, True, 16), (65, 256, 1, 1, False, 32), (130, 128, 0, 2, True, 32),
+            (33, 192, 1, 0, False, 32), (70, 64, 1, 2, False, 16), (41, 256, 0, 0, True, 32)]):
+        say(f"packed by lanes R={R} M={M} N={N} fmt={fmt} layout={lay} lanes={T}")
+        p = inputs.make_problem(M, N, seed_x=620 + k, residual=res, outliers=True)
+        check(orc, [dict(p, fmt=fmt, scale_layout=lay, keep_bf16=(k % 2 == 0))],
+              hint=fq.launch_hint(waves_per_workgroup=R, lanes_per_row=T))
+    a = inputs.make_problem(515, 512, seed_x=630, residual=False, outliers=True)
+    b = inputs.make_problem(299, 256, seed_x=631, residual=False, outliers=True)
+    c = inputs.make_problem(45, 128, seed_x=632, residual=False, outliers=True)
+    say(f"packed by lanes R={R} three widths (64 / 32 / 16 lanes)")
+    check(orc, [dict(a, fmt=0, scale_layout=2), dict(b, fmt=0, scale_layout=0, keep_bf16=True),
+                dict(c, fmt=0, scale_layout=0)], hint=fq.launch_hint(waves_per_workgroup=R))
+
+
+def test_every_lane_count_gives_the_same_result(orc):
+    """The same 128-wide rows packed 64, 32 or 16 lanes each give identical
+    outputs (one chunk per lane; the statistics' summation tree is the same)."""
+    p = inputs.make_problem(44, 128, seed_x=640, residual=True, outliers=True)
+    p.update(fmt=0, keep_bf16=True)
+    want = None
+    for T in (64, 32, 16):
+        say(f"lanes T={T}")
+        h = fq.launch_hint(waves_per_workgroup=4, lanes_per_row=T)
+        check(orc, [p], hint=h)
+        got = run_gpu([p], hint=h)[0]
+        if want is None:
+            want = got
+        for k in got:
+            assert np.array_equal(got[k], want[k]), (T, k)
 
 
 @pytest.mark.parametrize("S", [2, 4, 8])

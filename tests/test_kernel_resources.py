@@ -8,8 +8,10 @@ before it reaches a GPU.
 Limits (512 VGPRs per SIMD lane slot, allocated in granules of 8):
   * J = 1, 2 (the shapes of the 7168-wide rows): at most 64 VGPRs, 8 waves per SIMD;
   * J = 3: at most 80 VGPRs, 6 waves per SIMD, and at most 64 (8 waves) for
-    rows packed one per wave (the MLA latents: the whole launch resident at
-    once); J = 4: at most 96, 5 waves;
+    packed rows (the MLA latents: the whole launch resident at once); J = 4:
+    at most 96, 5 waves, and 64 for packed rows quantized without a residual
+    whose rows end inside the launch shape (the MLA latents with the 512-wide
+    rows 16 lanes each);
   * J = 7, 8: at most 128 VGPRs, J = 14: at most 168 (4-wave workgroups);
   * no kernel spills or uses private (scratch) memory.
 """
@@ -22,7 +24,7 @@ import pytest
 
 from fp4_quant_amd import build as B
 
-NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELb(\d)ELi(\d)EEEviiiiiiiiiNS_6LaunchE$")
+NAME = re.compile(r"^_ZN4rmsq17rmsq_fused_kernelILi(\d)ELi(\d+)ELb(\d)ELi(\d)ELi(\d)EEEviiiiiiiiiNS_6LaunchE$")
 
 
 @pytest.fixture(scope="module")
@@ -59,8 +61,10 @@ def test_every_kernel_variant_is_present(kernels):
     fused = [n for n in kernels if NAME.match(n or "")]
     # 3 formats (FP8, MXFP4, norm only) x residual or not x (7 shapes + 4 packed-row shapes),
     # the 4 short shapes and 4 packed-row shapes also for rows that exactly fill the launch,
-    # and the 4 packed-row shapes for rows of whole 64-lane steps (uniform tail)
-    assert len(fused) == 3 * 2 * (7 + 4 + 4 + 4 + 4), sorted(fused)
+    # the 4 packed-row shapes for rows of whole 64-lane steps (uniform tail), and rows
+    # packed by lanes (one chunk per lane), bounded or exact
+    assert len(fused) == 3 * 2 * (7 + 4 + 4 + 4 + 4 + 2), sorted(fused)
+    assert sum(1 for n in fused if NAME.match(n).group(4) == "2") == 3 * 2 * 2
     assert sum(1 for n in kernels if "rmsq_group_quant_kernel" in (n or "")) == 2
 
 
@@ -82,7 +86,9 @@ def test_register_budget(kernels, J, limit):
     for n, k in kernels.items():
         m = NAME.match(n or "")
         if m and int(m.group(2)) == J:
-            lim = 64 if J == 3 and m.group(4) == "1" else limit
+            packed = m.group(4) != "0"
+            capped = packed and (J == 3 or (J == 4 and m.group(1) != "2" and m.group(3) == "0" and m.group(5) != "1"))
+            lim = 64 if capped else limit
             assert k["vgpr_count"] + k["agpr_count"] <= lim, (n, k)
 
 

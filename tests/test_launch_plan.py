@@ -39,7 +39,8 @@ def test_default_plans_of_the_workloads():
     assert dec["workgroups"] == 64 * 4
     mla = plan([prob(0, M=4096, N=1536, residual=False), prob(1, M=4096, N=512, residual=False)])
     assert len(mla) == 1 and mla[0]["problems"] == 2 and mla[0]["rows"] == 8192
-    assert (mla[0]["chunks_per_lane"], mla[0]["waves_per_row"], mla[0]["rows_per_workgroup"]) == (3, 1, 8)
+    assert (mla[0]["chunks_per_lane"], mla[0]["waves_per_row"], mla[0]["waves_per_workgroup"]) == (3, 1, 8)
+    assert mla[0]["lanes_per_row"] == [64, 64]       # one row per wave
     assert mla[0]["workgroups"] == 1024
     assert mla[0]["tail"] == 2                       # whole 64-lane steps: the wave skips the rest
     assert pre[0]["tail"] == 1 and dec["tail"] == 0  # exact rows; split rows are bounded per lane
@@ -71,9 +72,13 @@ def test_hint_fields_take_effect():
     assert plan([prob(M=8192, layout=2)], fq.launch_hint(row_group=32))[0]["row_group"] == 32
     assert plan([prob(M=8192, layout=2)])[0]["row_group"] == 16
     one = [prob(M=2048, N=1536, residual=False)]
-    assert plan(one)[0]["rows_per_workgroup"] == 8
-    l = plan(one, fq.launch_hint(rows_per_workgroup=3))[0]
-    assert l["rows_per_workgroup"] == 3 and l["workgroups"] == -(-2048 // 3) and l["threads_per_workgroup"] == 192
+    assert plan(one)[0]["waves_per_workgroup"] == 8
+    l = plan(one, fq.launch_hint(waves_per_workgroup=3))[0]
+    assert l["waves_per_workgroup"] == 3 and l["workgroups"] == -(-2048 // 3) and l["threads_per_workgroup"] == 192
+    mla = [prob(0, M=4096, N=1536, residual=False), prob(1, M=4096, N=512, residual=False)]
+    l = plan(mla, fq.launch_hint(4, 1))[0]
+    assert l["lanes_per_row"] == [64, 64] and l["workgroups"] == 1024 and l["tail"] == 2
+    assert plan(mla, fq.launch_hint(lanes_per_row=64)) == plan(mla)
     # the default plan is what no hint and an all-zero hint give
     assert plan(p) == plan(p, fq.launch_hint())
 
@@ -81,8 +86,9 @@ def test_hint_fields_take_effect():
 @pytest.mark.parametrize("hint", [
     fq.launch_hint(2, 0), fq.launch_hint(0, 7), fq.launch_hint(5, 7), fq.launch_hint(7, 5),
     fq.launch_hint(1, 17), fq.launch_hint(1, 7),            # 1 x 7 waves cannot cover 7168
-    fq.launch_hint(row_group=-1), fq.launch_hint(row_group=65), fq.launch_hint(rows_per_workgroup=17),
-    fq.launch_hint(row_splits=9), fq.launch_hint(row_splits=-2)])
+    fq.launch_hint(row_group=-1), fq.launch_hint(row_group=65), fq.launch_hint(waves_per_workgroup=17),
+    fq.launch_hint(row_splits=9), fq.launch_hint(row_splits=-2), fq.launch_hint(lanes_per_row=8),
+    fq.launch_hint(lanes_per_row=48), fq.launch_hint(lanes_per_row=128)])
 def test_bad_hints_are_refused(hint):
     arr = (fq.rmsq_problem * 1)(fq.rmsq_problem(**prob()))
     out = fq.rmsq_launch_plan()
@@ -91,6 +97,36 @@ def test_bad_hints_are_refused(hint):
     assert out.launches == 0
     # the launching entry point refuses the same hint before any HIP call
     assert fq.lib().rmsnorm_quant_group_multi_ex(arr, 1, C.byref(hint), None) == fq.RMSQ_ERR_INVALID_ARG
+
+
+def test_packed_lanes_per_row():
+    """Packed rows of one chunk per lane take the fewest lanes (16, 32, 64)
+    that hold the row; a wave then holds 64 / lanes rows, and a problem whose
+    row count is not a multiple of that leaves its last wave part empty
+    (ragged tail). Rows of more chunks per lane keep one row per wave."""
+    for N, lanes in ((128, 16), (256, 32), (512, 64), (1024, 64)):
+        l = plan([prob(M=4096, N=N, residual=False)])[0]
+        assert l["waves_per_workgroup"] == 8 and l["lanes_per_row"] == [lanes], N
+        waves = 4096 * lanes // 64
+        assert l["workgroups"] == waves // 8 and l["tail"] == 1, N
+    l = plan([prob(M=4096, N=2048, residual=False)])[0]          # two waves per row: not packed
+    assert (l["waves_per_row"], l["waves_per_workgroup"], l["lanes_per_row"]) == (2, 1, [128])
+    l = plan([prob(M=4099, N=128, residual=False)])[0]          # 1025 waves, the last one 3/4 empty
+    assert l["workgroups"] == -(-1025 // 8) and l["tail"] == 0
+    l = plan([prob(M=4096, N=128, residual=False)], fq.launch_hint(lanes_per_row=32))[0]
+    assert l["lanes_per_row"] == [32] and l["workgroups"] == 2048 // 8 and l["tail"] == 0   # half of each row's lanes idle
+    mixed = plan([prob(0, M=515, N=512, residual=False), prob(1, M=299, N=256, residual=False),
+                  prob(2, M=45, N=128, residual=False)], fq.launch_hint(waves_per_workgroup=8))[0]
+    assert mixed["lanes_per_row"] == [64, 32, 16] and mixed["tail"] == 0
+    assert mixed["workgroups"] == -(-(515 + 150 + 12) // 8)
+    # fewer than 64 lanes per row need rows of one chunk per lane, and must hold the row
+    for N, lanes in ((1536, 32), (512, 32), (256, 16)):
+        arr = (fq.rmsq_problem * 1)(fq.rmsq_problem(**prob(M=4096, N=N, residual=False)))
+        out = fq.rmsq_launch_plan()
+        h = fq.launch_hint(lanes_per_row=lanes)
+        assert fq.lib().rmsq_plan_launch(arr, 1, C.byref(h), C.byref(out)) == fq.RMSQ_ERR_INVALID_ARG, N
+    # unpacked launches report the lanes of their whole row
+    assert plan([prob(M=8192)])[0]["lanes_per_row"] == [7 * 64]
 
 
 def test_plan_validates_like_the_call():
