@@ -87,8 +87,10 @@ __device__ __forceinline__ uint32_t fp8_exact(float v, float s) {
 // ------------------------------------------------------- element blocks --
 // The per-chunk arithmetic of the fused kernel, on 8 consecutive elements.
 
+// Low 16 bits of an fp32 within 2 of 0x8000: at most 2 ulps from a bf16
+// rounding midpoint of its binade.
 __device__ __forceinline__ bool near_bf16_midpoint(float y) {
-  return ((__float_as_uint(y) & 0xFFFFu) - 0x7FFCu) <= 8u;
+  return ((__float_as_uint(y) & 0xFFFFu) - 0x7FFEu) <= 4u;
 }
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
@@ -101,17 +103,21 @@ constexpr int kInexactProduct = 0x001 | 0x002 | 0x004 | 0x010 | 0x080 | 0x200;
 // bf16(h * g * inv) for 8 elements: h bf16 values (as fp32, and packed two
 // per dword in hpk), g the 8 bf16 gammas packed two per dword, inv the fp64
 // inverse norm and inv32 = fl32(inv). hg = h * g is exact in fp32 unless it
-// leaves the normal range; then y = hg * inv32 is within 2 ulp of the fp64
-// product h * g * inv, so its bf16 rounding is final unless y lies within 4
-// ulp of a bf16 midpoint. Those elements, elements whose hg is denormal or
-// infinite, and every element of a row_exact row are redone in fp64 from h
+// leaves the normal range; then fl32(inv) and the product each round once,
+// so y = hg * inv32 is within 2^-23 (1 + 2^-25) |y| of h * g * inv, under
+// 2 (1 + 2^-22) ulps of y's binade: a y at least 3 ulps from a bf16 midpoint
+// rounds as the exact product does, and as the fp64 product (within 2^-53 of
+// it). Its bf16 rounding is therefore final unless y lies within 2 ulps of a
+// midpoint (errors of about 1.5 ulps occur). Those elements, elements whose
+// hg is denormal or infinite, and every element of a row_exact row are
+// redone in fp64 from h
 // and g (their product is exact there) with a single rounding. (A product
 // that underflows to zero is harmless here: the caller flags rows with
 // inv > 2^16, and below that a zero hg keeps the sign of a true result that
 // rounds to zero in bf16 anyway.) The window test runs on packed 16-bit
 // lanes: the low halves of two products side by side (v_perm_b32), plus
-// 0x8004 modulo 2^16, fall in [0, 8] exactly for the products whose low 16
-// bits lie in [0x7FFC, 0x8004]; the minimum over the 8 elements decides
+// 0x8002 modulo 2^16, fall in [0, 4] exactly for the products whose low 16
+// bits lie in [0x7FFE, 0x8002]; the minimum over the 8 elements decides
 // whether any of them needs the fp64 path.
 __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, const u32x4 g, float inv32,
                                              double inv, bool row_exact) {
@@ -124,10 +130,10 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
     odd |= __builtin_amdgcn_classf(hg0, kInexactProduct) | __builtin_amdgcn_classf(hg1, kInexactProduct);
     const float y0 = hg0 * inv32, y1 = hg1 * inv32;
     const uint32_t lows = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x05040100u);
-    lo_min = __builtin_elementwise_min(lo_min, __builtin_bit_cast(u16x2, lows) + u16x2{0x8004u, 0x8004u});
+    lo_min = __builtin_elementwise_min(lo_min, __builtin_bit_cast(u16x2, lows) + u16x2{0x8002u, 0x8002u});
     yw[i] = pack_bf16(y0, y1);
   }
-  const bool need = odd | (min((uint32_t)lo_min[0], (uint32_t)lo_min[1]) <= 8u);
+  const bool need = odd | (min((uint32_t)lo_min[0], (uint32_t)lo_min[1]) <= 4u);
   if (__builtin_expect(need, 0)) {   // rare: keep the fast path's code contiguous
     // Rare: recompute the products here instead of keeping the fast path's
     // 16 intermediates alive across the branch (the empty asm hides that

@@ -26,7 +26,7 @@
 //    inv = 1/sqrt(ss/N + eps) in fp64 with correctly rounded divide / sqrt.
 //  * y = (h*g) * inv: h*g is exact in fp32 while it stays in the normal
 //    range; the product is first taken in fp32 with fl32(inv) (within 2 ulp
-//    of the fp64 product); only when it lands within 4 ulp of a bf16
+//    of the fp64 product); only when it lands within 2 ulp of a bf16
 //    rounding midpoint, or h*g is denormal or infinite, is the element redone
 //    as fp64 h*g*inv rounded once to bf16.
 //  * FP8 scale s = fl32(amax/448), correctly rounded; codes through the
