@@ -192,44 +192,49 @@ __device__ __forceinline__ float fp8_scale(uint32_t amax_bits) {
 // the even code - when 448 s = amax (amax's mantissa a multiple of 7). The
 // sign of fma(s, 448, -amax) is that of the exact difference (a nonzero
 // difference is at least 2^-123, no underflow to zero), so one fma per group
-// decides every undecided element of it. The two codes are then neighbours of
-// one sign, c_hi = c_lo + 1 in each differing byte, so qh - qw has 0x01 in
-// exactly those bytes (no borrows), and the result is qw plus those ones where
-// the upper code is taken: all of them when 448 s < amax, the bytes with odd
-// c_lo on a tie, none otherwise. Branch-free, two bitwise ops and two adds
-// per four elements. Groups whose scale is below 2^-100 (no normal
-// reciprocal) take the double-precision path element by element.
+// decides every element of it: off a midpoint both brackets agree, and on
+// one the upper bracket gives the upper code and the lower the lower. So a
+// group with 448 s < amax takes the codes of v*r_hi, one with 448 s > amax
+// those of v*r_lo - one product and half a convert per element - and only a
+// group with an exact scale (448 s = amax, about one in seven) needs both:
+// the two codes are then neighbours of one sign where they differ, c_hi =
+// c_lo + 1 in each differing byte, so qh - qw has 0x01 in exactly those
+// bytes (no borrows), and adding it where c_lo is odd gives the even code.
+// Groups whose scale is below 2^-100 (no normal reciprocal) take the
+// double-precision path element by element.
 __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s, float amax) {
-  const uint32_t rb = __float_as_uint(__builtin_amdgcn_rcpf(s));
-  const float r_lo = __uint_as_float(rb - 4u), r_hi = __uint_as_float(rb + 4u);
-  float lo[8], hi[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    lo[e] = v[e] * r_lo;
-    hi[e] = v[e] * r_hi;
-  }
-  // The first convert of each dword writes its low half; the high half it
-  // keeps is replaced by the second, so the register it starts from is any
-  // value that dies here (one of its own operands): no initialization.
-  u32x2 qw, qh;
-  qw[0] = cvt_fp8x2<true>(lo[2], lo[3], cvt_fp8x2<false>(lo[0], lo[1], __float_as_uint(lo[1])));
-  qw[1] = cvt_fp8x2<true>(lo[6], lo[7], cvt_fp8x2<false>(lo[4], lo[5], __float_as_uint(lo[5])));
-  qh[0] = cvt_fp8x2<true>(hi[2], hi[3], cvt_fp8x2<false>(hi[0], hi[1], __float_as_uint(hi[1])));
-  qh[1] = cvt_fp8x2<true>(hi[6], hi[7], cvt_fp8x2<false>(hi[4], hi[5], __float_as_uint(hi[5])));
+  u32x2 qw;
   if (__builtin_expect(s < 0x1p-100f, 0)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int sh = (e & 3) * 8;
       const uint32_t b = fp8_exact(v[e], s);
-      qw[e >> 2] = (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh);
+      qw[e >> 2] = e & 3 ? (qw[e >> 2] & ~(0xFFu << sh)) | (b << sh) : b;
     }
     return qw;
   }
+  const uint32_t rb = __float_as_uint(__builtin_amdgcn_rcpf(s));
+  const float r_lo = __uint_as_float(rb - 4u), r_hi = __uint_as_float(rb + 4u);
   const float t = __builtin_fmaf(s, 448.0f, -amax);
-  const uint32_t up = t < 0.0f ? 0xFFFFFFFFu : 0u;    // v/s above the midpoint: the upper code
-  const uint32_t tie = t == 0.0f ? 0xFFFFFFFFu : 0u;  // on it: the even one
+  const float r = t < 0.0f ? r_hi : r_lo;
+  float p[8];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) qw[k] += (qh[k] - qw[k]) & (up | (tie & qw[k]));
+  for (int e = 0; e < 8; ++e) p[e] = v[e] * r;
+  // The first convert of each dword writes its low half; the high half it
+  // keeps is replaced by the second, so the register it starts from is any
+  // value that dies here (one of its own operands): no initialization.
+  qw[0] = cvt_fp8x2<true>(p[2], p[3], cvt_fp8x2<false>(p[0], p[1], __float_as_uint(p[1])));
+  qw[1] = cvt_fp8x2<true>(p[6], p[7], cvt_fp8x2<false>(p[4], p[5], __float_as_uint(p[5])));
+  if (t == 0.0f) {   // exact scale: ties take the even code
+    float h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = v[e] * r_hi;
+    u32x2 qh;
+    qh[0] = cvt_fp8x2<true>(h[2], h[3], cvt_fp8x2<false>(h[0], h[1], __float_as_uint(h[1])));
+    qh[1] = cvt_fp8x2<true>(h[6], h[7], cvt_fp8x2<false>(h[4], h[5], __float_as_uint(h[5])));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) qw[k] += (qh[k] - qw[k]) & qw[k];
+  }
   return qw;
 }
 
