@@ -95,6 +95,15 @@ __device__ __forceinline__ bool near_bf16_midpoint(float y) {
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
+// Largest |value| of eight packed bf16 (four dwords), as a bf16 magnitude
+// pattern: integer max of (bits & 0x7FFF) orders bf16 magnitudes exactly.
+__device__ __forceinline__ uint32_t amax8(u32x4 w) {
+  const u16x2 a = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, w[1] & 0x7FFF7FFFu);
+  const u16x2 c = __builtin_bit_cast(u16x2, w[2] & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2, w[3] & 0x7FFF7FFFu);
+  const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max((uint32_t)m[0], (uint32_t)m[1]);
+}
+
 // Classes of an fp32 product h * gamma that is not exact or not finite:
 // NaN, +-infinity, +-denormal (v_cmp_class_f32 mask). A normal product of two
 // bf16 (8 significant bits each) is exact in fp32.
@@ -119,11 +128,18 @@ constexpr int kInexactProduct = 0x001 | 0x002 | 0x004 | 0x010 | 0x080 | 0x200;
 // 0x8002 modulo 2^16, fall in [0, 4] exactly for the products whose low 16
 // bits lie in [0x7FFE, 0x8002]; the minimum over the 8 elements decides
 // whether any of them needs the fp64 path.
+//
+// am: the largest |result| as a bf16 magnitude pattern (what amax8 gives for
+// the returned words). Rounding to nearest is monotone and symmetric, so on
+// the fast path it is the bf16 of the largest |y| (one v_max3_f32 with
+// absolute-value operands per pair, one convert); the fp64 path takes it from
+// the final words.
 __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, const u32x4 g, float inv32,
-                                             double inv, bool row_exact) {
+                                             double inv, bool row_exact, uint32_t& am) {
   u32x4 yw;
   u16x2 lo_min = {0xFFFFu, 0xFFFFu};
   bool odd = row_exact;
+  float ymax;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float hg0 = h[2 * i] * bf16_lo(g[i]), hg1 = h[2 * i + 1] * bf16_hi(g[i]);
@@ -131,8 +147,11 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
     const float y0 = hg0 * inv32, y1 = hg1 * inv32;
     const uint32_t lows = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x05040100u);
     lo_min = __builtin_elementwise_min(lo_min, __builtin_bit_cast(u16x2, lows) + u16x2{0x8002u, 0x8002u});
+    ymax = i == 0 ? __builtin_fmaxf(__builtin_fabsf(y0), __builtin_fabsf(y1))
+                  : __builtin_fmaxf(__builtin_fmaxf(ymax, __builtin_fabsf(y0)), __builtin_fabsf(y1));
     yw[i] = pack_bf16(y0, y1);
   }
+  am = pack_bf16(ymax, 0.0f);
   const bool need = odd | (min((uint32_t)lo_min[0], (uint32_t)lo_min[1]) <= 4u);
   if (__builtin_expect(need, 0)) {   // rare: keep the fast path's code contiguous
     // Rare: recompute the products here instead of keeping the fast path's
@@ -153,6 +172,7 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
         yw[e >> 1] = (yw[e >> 1] & ~(0xFFFFu << sh)) | (b << sh);
       }
     }
+    am = amax8(yw);
   }
   return yw;
 }
@@ -339,14 +359,5 @@ __device__ __forceinline__ double lanes_sum(double v, int lt) {
 
 // Sum over the 64 lanes of a wave: (r0 + r1) + (r2 + r3) of the row sums.
 __device__ __forceinline__ double wave_sum(double v) { return lanes_sum(v, 6); }
-
-// Largest |value| of eight packed bf16 (four dwords), as a bf16 magnitude
-// pattern: integer max of (bits & 0x7FFF) orders bf16 magnitudes exactly.
-__device__ __forceinline__ uint32_t amax8(u32x4 w) {
-  const u16x2 a = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, w[1] & 0x7FFF7FFFu);
-  const u16x2 c = __builtin_bit_cast(u16x2, w[2] & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2, w[3] & 0x7FFF7FFFu);
-  const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
-  return max((uint32_t)m[0], (uint32_t)m[1]);
-}
 
 }  // namespace rmsq

@@ -324,7 +324,8 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
       hv[2 * i] = kKeepH ? hf[kKeepH ? j : 0][2 * i] : bf16_lo(xv[j][i]);
       hv[2 * i + 1] = kKeepH ? hf[kKeepH ? j : 0][2 * i + 1] : bf16_hi(xv[j][i]);
     }
-    const u32x4 yw = norm_bf16x8(hv, xv[j], g, inv32, inv, row_exact);
+    uint32_t am;
+    const u32x4 yw = norm_bf16x8(hv, xv[j], g, inv32, inv, row_exact, am);
     // All stores of a row go out after its reduction: keeping the residual
     // write next to the others measured 3% faster than writing it as soon as
     // it is formed.
@@ -332,7 +333,6 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
     if (ybrow) __builtin_nontemporal_store(yw, ybrow + c);
 
     if constexpr (FMT == 2) continue;   // norm only: no quantization
-    const uint32_t am = amax8(yw);
 
     if constexpr (FMT == 0) {
       // FP8 e4m3fn, group 128 = one 16-lane DPP row

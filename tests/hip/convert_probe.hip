@@ -14,7 +14,7 @@ using namespace rmsq;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < (n); i += (int64_t)gridDim.x * blockDim.x)
 
 __global__ void k_norm_bf16(const float* hv, const float* gv, const double* inv, const uint8_t* row_exact,
-                            uint16_t* out, int64_t n) {
+                            uint16_t* out, uint16_t* am_out, int64_t n) {
   GRID_LOOP(k, n) {
     float h[8];
     u32x4 hp, g;
@@ -23,8 +23,10 @@ __global__ void k_norm_bf16(const float* hv, const float* gv, const double* inv,
       hp[i] = (__float_as_uint(hv[8 * k + 2 * i]) >> 16) | (__float_as_uint(hv[8 * k + 2 * i + 1]) & 0xFFFF0000u);
       g[i] = (__float_as_uint(gv[8 * k + 2 * i]) >> 16) | (__float_as_uint(gv[8 * k + 2 * i + 1]) & 0xFFFF0000u);
     }
-    const u32x4 w = norm_bf16x8(h, hp, g, (float)inv[k], inv[k], row_exact[k] != 0);
+    uint32_t am;
+    const u32x4 w = norm_bf16x8(h, hp, g, (float)inv[k], inv[k], row_exact[k] != 0, am);
     for (int e = 0; e < 8; ++e) out[8 * k + e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+    am_out[k] = (uint16_t)am;
   }
 }
 
@@ -162,10 +164,10 @@ static int launch_status() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 // exported: the library is built with hidden visibility
 #pragma GCC visibility push(default)
 extern "C" {
-int probe_norm_bf16(const float* h, const float* g, const double* inv, const uint8_t* ex, uint16_t* out, int64_t n,
-                    void* stream) {
+int probe_norm_bf16(const float* h, const float* g, const double* inv, const uint8_t* ex, uint16_t* out,
+                    uint16_t* am, int64_t n, void* stream) {
   if (n <= 0) return 0;
-  hipLaunchKernelGGL(k_norm_bf16, GRID(n), h, g, inv, ex, out, n);
+  hipLaunchKernelGGL(k_norm_bf16, GRID(n), h, g, inv, ex, out, am, n);
   return launch_status();
 }
 int probe_fp8_scale(const uint16_t* a, float* s, int64_t n, void* stream) {

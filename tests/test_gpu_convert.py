@@ -146,10 +146,13 @@ def test_norm_bf16x8_matches_fp64_rounding(orc):
     inv[k[nz]] *= 1 + rng.choice([-1, 0, 1], nz.sum()) * 2.0 ** -52
     ex = (rng.random(n // 8) < 0.05).astype(np.uint8)
     out = torch.empty(n, dtype=torch.int16, device="cuda")
-    call_probe("probe_norm_bf16", dev(h.astype(np.float32)), dev(g.astype(np.float32)), dev(inv), dev(ex), out,
+    am = torch.empty(n // 8, dtype=torch.int16, device="cuda")
+    call_probe("probe_norm_bf16", dev(h.astype(np.float32)), dev(g.astype(np.float32)), dev(inv), dev(ex), out, am,
                n=n // 8)
     want = orc.bf16_from_double(hg.astype(np.float64) * np.repeat(inv, 8))
     assert np.array_equal(host(out).view(np.uint16), want)
+    # the group maximum it returns: the largest bf16 magnitude of the 8 results
+    assert np.array_equal(host(am).view(np.uint16), (want & 0x7FFF).reshape(-1, 8).max(axis=1))
 
 
 def test_norm_bf16x8_products_outside_the_fp32_normal_range(orc):
@@ -180,11 +183,13 @@ def test_norm_bf16x8_products_outside_the_fp32_normal_range(orc):
         assert np.array_equal(orc.bf16_to_double(orc.bf16_from_double(h)), h)      # bf16 values
         ex = np.zeros(n // 8, np.uint8)
         out = torch.empty(n, dtype=torch.int16, device="cuda")
-        call_probe("probe_norm_bf16", dev(h32), dev(g32), dev(inv), dev(ex), out, n=n // 8)
+        am = torch.empty(n // 8, dtype=torch.int16, device="cuda")
+        call_probe("probe_norm_bf16", dev(h32), dev(g32), dev(inv), dev(ex), out, am, n=n // 8)
         want = orc.bf16_from_double(h * g * np.repeat(inv, 8))
         got = host(out).view(np.uint16)
         bad = np.flatnonzero(got != want)
         assert bad.size == 0, f"{bad.size} differ, first h={h[bad[0]]} g={g[bad[0]]} inv={inv[bad[0] // 8]}"
+        assert np.array_equal(host(am).view(np.uint16), (want & 0x7FFF).reshape(-1, 8).max(axis=1))
 
 
 def test_fp8_scale_every_amax():
