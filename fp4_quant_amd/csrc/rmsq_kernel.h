@@ -181,6 +181,17 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // problems are consecutive ranges of launch units (row_begin increasing)
   const int pi = (count > 1 && row >= rb1) + (count > 2 && row >= rb2) + (count > 3 && row >= rb3);
   const Problem& P = L.p[pi];
+  // The record's fields that the loads need, read together before anything
+  // branches on them: one scalar round trip. (The row-split bounds below use
+  // N; read where first used, the compiler fetched N alone, waited, and only
+  // then fetched the pointers and strides - a second round trip on the
+  // critical path of the short launches.)
+  const uint16_t* const px = P.x;
+  const uint16_t* const pg = P.gamma;
+  const uint16_t* const pr = RES ? P.r : nullptr;
+  const int64_t ldx = P.ldx, ldr = RES ? P.ldr : 0;
+  const int32_t N = P.N, M = P.M;
+  asm volatile("" ::"s"(px), "s"(pg), "s"(pr), "s"(ldx), "s"(ldr), "s"(N), "s"(M));
   const int32_t u = row - (pi == 0 ? 0 : pi == 1 ? rb1 : pi == 2 ? rb2 : rb3);
   const int lt = PACK == kPackLanes ? P.lanes_log2 : 6;
   const int T = PACK == kPackLanes ? 1 << lt : kPacked ? 64 : threads;
@@ -189,10 +200,10 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   bool live = true;   // packed by lanes: this lane group has a row of the problem
   if constexpr (PACK == kPackLanes) {
     const int32_t r = packed_row(u, lt, threadIdx.x & 63);
-    live = r < P.M;
-    m = live ? r : P.M - 1;
+    live = r < M;
+    m = live ? r : M - 1;
   }
-  const int C = P.N >> 3;
+  const int C = N >> 3;
   // what a lane loads at step j: row pointer + load(j), clamped to the row's
   // last step (kUniform: a wave-uniform offset, so the lane offset tid is
   // shared by every step) or to its last chunk (kRagged)
@@ -205,15 +216,6 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
     if constexpr (TAIL == kUniform) return __builtin_nontemporal_load(row + min(j, jl) * T + tid);
     return __builtin_nontemporal_load(row + (TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1)));
   };
-  // chunks this workgroup normalizes and stores: all of them, or with row
-  // splits a range whose ends fall on group boundaries (16 chunks FP8, 4 MXFP4)
-  int lo = 0, hi = live ? C : 0;
-  if (!kPacked && slg > 0) {
-    constexpr int q = FMT == 0 ? 16 : FMT == 1 ? 4 : 1;
-    lo = ((split * (C / q)) >> slg) * q;
-    hi = split + 1 == (1 << slg) ? C : (((split + 1) * (C / q)) >> slg) * q;
-  }
-
   // ---- loads: x, gamma (short rows), then r, all issued before any use ---
   // (of the issue orders measured, this one was fastest on both the
   // bandwidth-bound and the latency-bound shapes)
@@ -221,9 +223,9 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // past the row end re-read the last chunk (the address of a live lane of
   // the same instruction, so no extra traffic) and their h is zeroed before
   // the sum of squares; their stores are skipped.
-  const u32x4* xrow = reinterpret_cast<const u32x4*>(P.x + m * P.ldx);
-  const u32x4* rrow = RES ? reinterpret_cast<const u32x4*>(P.r + m * P.ldr) : nullptr;
-  const u32x4* grow = reinterpret_cast<const u32x4*>(P.gamma);
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(px + m * ldx);
+  const u32x4* rrow = RES ? reinterpret_cast<const u32x4*>(pr + m * ldr) : nullptr;
+  const u32x4* grow = reinterpret_cast<const u32x4*>(pg);
   u32x4 xv[J], rv[RES ? J : 1], gv[kShort ? J : 1];
 #pragma unroll
   for (int j = 0; j < J; ++j) xv[j] = load_nt(xrow, j);
@@ -239,6 +241,15 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
     for (int j = 0; j < J; ++j) rv[j] = load_nt(rrow, j);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // chunks this workgroup normalizes and stores: all of them, or with row
+  // splits a range whose ends fall on group boundaries (16 chunks FP8, 4 MXFP4)
+  int lo = 0, hi = live ? C : 0;
+  if (!kPacked && slg > 0) {
+    constexpr int q = FMT == 0 ? 16 : FMT == 1 ? 4 : 1;
+    lo = ((split * (C / q)) >> slg) * q;
+    hi = split + 1 == (1 << slg) ? C : (((split + 1) * (C / q)) >> slg) * q;
+  }
+
   // Every other field of the problem record this row needs, read now: their
   // scalar loads then overlap the row's vector loads instead of stalling the
   // statistics and the stores later (each late scalar load costs a memory
@@ -246,7 +257,7 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // launches).
   const float eps = P.eps;
   const double rn = P.rn;
-  const int32_t layout = P.layout, M = P.M;
+  const int32_t layout = P.layout;
   uint16_t* const hbase = RES ? P.h : nullptr;
   uint16_t* const ybase = P.yb;
   uint8_t* const qbase = FMT == 2 ? nullptr : P.q;
@@ -296,7 +307,7 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // product q0 is within an ulp of the quotient, its residual ss - q0 * N is
   // exact in one fma, and one more fma with rn rounds the corrected quotient
   // to nearest (Markstein's quotient refinement).
-  const double nd = (double)P.N;
+  const double nd = (double)N;
   const double q0 = ss * rn;
   const double ms = __builtin_fma(__builtin_fma(-q0, nd, ss), rn, q0);
   const double denom = ms + (double)eps;
@@ -309,7 +320,7 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
 
   // ---- phase 2: normalize, bf16, group scale, codes -----------------------
   u32x4* ybrow = ybase ? reinterpret_cast<u32x4*>(ybase + m * ldb) : nullptr;
-  u32x4* hrow = RES ? reinterpret_cast<u32x4*>(hbase + m * P.ldr) : nullptr;
+  u32x4* hrow = RES ? reinterpret_cast<u32x4*>(hbase + m * ldr) : nullptr;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = j * T + tid;
@@ -345,20 +356,20 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
       const uint32_t gam = max16(am);
       const float sc = fp8_scale(gam);
       const u32x2 qw = fp8_codes8(v, sc, __uint_as_float(gam << 16));
-      u32x2* qrow = reinterpret_cast<u32x2*>(qbase + m * (int64_t)P.N);
+      u32x2* qrow = reinterpret_cast<u32x2*>(qbase + m * (int64_t)N);
       __builtin_nontemporal_store(qw, qrow + c);
       if ((tid & 15) == 0) {
         const int64_t g = c >> 4;
-        reinterpret_cast<float*>(sbase)[layout == 2 ? g * M + m : m * (P.N >> 7) + g] = sc;
+        reinterpret_cast<float*>(sbase)[layout == 2 ? g * M + m : m * (N >> 7) + g] = sc;
       }
     } else if constexpr (FMT == 1) {
       // MXFP4 e2m1, group 32 = one lane quad
       const uint32_t byte = mx_scale_byte(max4(am));
       const uint32_t w = fp4_codes8(yw, byte);
-      uint32_t* qrow = reinterpret_cast<uint32_t*>(qbase + m * (int64_t)(P.N >> 1));
+      uint32_t* qrow = reinterpret_cast<uint32_t*>(qbase + m * (int64_t)(N >> 1));
       __builtin_nontemporal_store(w, qrow + c);
       if ((tid & 3) == 0) {
-        const int64_t gcount = P.N >> 5, gi = c >> 2;
+        const int64_t gcount = N >> 5, gi = c >> 2;
         const int64_t off = layout == 0   ? m * gcount + gi
                             : layout == 1 ? (m >> 5) * (32 * gcount) + gi * 32 + (m & 31)
                                           : gi * M + m;
