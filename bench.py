@@ -60,6 +60,14 @@ def algorithmic_bytes(M, N, fmt, residual, keep_bf16):
     return b
 
 
+def host_inputs(specs):
+    """The seeded synthetic inputs of a workload's problems, on the host (what
+    Workload uploads, and what its inputs_sha256 hashes)."""
+    from fp4_quant_amd import inputs
+    return [inputs.make_problem(s["M"], s["N"], seed_x=s.get("seed", 0), residual=s["residual"],
+                                outliers=s.get("outliers", True)) for s in specs]
+
+
 class Workload:
     """Rotating sets of device buffers for one or more problems launched together."""
 
@@ -74,10 +82,7 @@ class Workload:
         nsets = max(2, min(512, -(-3 * MALL_BYTES // max(self.bytes, 1))))
         self.sets = []
         host = []
-        for s in specs:
-            p = inputs.make_problem(s["M"], s["N"], seed_x=s.get("seed", 0), residual=s["residual"],
-                                    outliers=s.get("outliers", True))
-            host.append(p)
+        host.extend(host_inputs(specs))
         for k in range(nsets):
             probs, keep = [], []
             for s, p in zip(specs, host):
