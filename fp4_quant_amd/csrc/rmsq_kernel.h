@@ -152,10 +152,10 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // together with x and r; long ones keep h packed and fetch gamma late, to
   // stay within the register budget.
   constexpr bool kShort = J <= 4;
-  // Packed rows of 3 or 4 chunks per lane (held to 64 VGPRs) unpack h again
-  // in phase 2 rather than keep 24 or 32 fp32 copies across the reduction.
   constexpr bool kPacked = PACK != kPackNone;
   static_assert(PACK != kPackLanes || J == 1, "rows packed by lanes take one chunk per lane");
+  // Packed rows of 3 or 4 chunks per lane (held to 64 VGPRs) unpack h again
+  // in phase 2 rather than keep 24 or 32 fp32 copies across the reduction.
   constexpr bool kKeepH = kShort && !(kPacked && J >= 3);
   __shared__ double red[kMaxWaves];
 
@@ -298,10 +298,22 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   ss = PACK == kPackLanes ? lanes_sum(ss, lt) : wave_sum(ss);
   const int nw = T >> 6;
   if (!kPacked && nw > 1) {
+    // The waves' sums in a fixed pairwise tree over all 16 slots, four adds
+    // deep (one dependent chain of nw adds was on the critical path of the
+    // short launches); the slots past the last wave hold zero, which adds
+    // exactly.
     if ((tid & 63) == 0) red[tid >> 6] = ss;
+    if (tid >= nw && tid < kMaxWaves) red[tid] = 0.0;
     __syncthreads();
-    ss = 0.0;
-    for (int w = 0; w < nw; ++w) ss += red[w];
+    double t[kMaxWaves / 2];
+#pragma unroll
+    for (int k = 0; k < kMaxWaves / 2; ++k) t[k] = red[2 * k] + red[2 * k + 1];
+#pragma unroll
+    for (int n = kMaxWaves / 4; n >= 1; n /= 2) {
+#pragma unroll
+      for (int k = 0; k < n; ++k) t[k] = t[2 * k] + t[2 * k + 1];
+    }
+    ss = t[0];
   }
   // ss / N, correctly rounded, from the correctly rounded reciprocal rn: the
   // product q0 is within an ulp of the quotient, its residual ss - q0 * N is
