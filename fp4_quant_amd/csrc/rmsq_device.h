@@ -178,18 +178,22 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
 }
 
 // FP8 scale of a group from its amax (a bf16 magnitude pattern): amax / 448
-// rounded once to fp32, 1.0 for an all-zero group. For amax >= 2^-100 the
-// quotient is a normal fp32 and is formed as fl32(amax * fl64(1/448)): amax
-// has 8 significant bits, so amax/448 = (A/7) 2^k, whose bits past any
-// rounding position repeat with period 3 and never come within 2^-27
-// (relative) of an fp32 midpoint unless 7 divides A and the quotient is
-// exact; the fp64 product is within 2^-52 of the quotient, so its fp32
-// rounding is the correctly rounded one. Smaller amax uses the IEEE fp32
-// division (denormals kept).
+// rounded once to fp32, 1.0 for an all-zero group. For amax >= 2^-100 it is
+// formed in fp32 by one division refinement step: q0 = fl32(amax * c) with
+// c = fl32(1/448) is within an ulp of the quotient, the residual
+// amax - 448 q0 is exact in one fma, and q0 + residual * c rounded once (a
+// second fma) is the correctly rounded amax / 448 - for every bf16 amax in
+// that range, checked exhaustively (a CPU test, and the GPU probe of this
+// function). (amax has 8 significant bits, so amax/448 = (A/7) 2^k, whose
+// bits past any rounding position repeat with period 3 and never come within
+// 2^-27 (relative) of an fp32 midpoint unless 7 divides A and the quotient is
+// exact.) Smaller amax uses the IEEE fp32 division (denormals kept).
 __device__ __forceinline__ float fp8_scale(uint32_t amax_bits) {
   const float a = __uint_as_float(amax_bits << 16);
   if (__builtin_expect(amax_bits < 0x0D80u, 0)) return amax_bits == 0 ? 1.0f : a / 448.0f;
-  return (float)((double)a * (1.0 / 448.0));
+  constexpr float c = 1.0f / 448.0f;
+  const float q0 = a * c;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 448.0f, a), c, q0);
 }
 
 // e4m3fn codes of v[e] / s for 8 bf16 values v (as fp32) of one group with
