@@ -483,8 +483,8 @@ def kernel_name(fmt, N, rows, residual):
     names it), with its waves per row."""
     import fp4_quant_amd as fq
     J, W = fq.rmsq_query_shape(N, rows)
-    exact = "true" if N // 8 == J * 64 * W else "false"
-    return (f"rmsq_fused_kernel<{fmt}, {J}, {'true' if residual else 'false'}, false, {exact}>"
+    tail = 1 if N // 8 == J * 64 * W else 0     # rmsq::Tail: exact, else ragged
+    return (f"rmsq_fused_kernel<{fmt}, {J}, {'true' if residual else 'false'}, 0, {tail}>"
             f" ({W} waves per row)")
 
 
@@ -596,14 +596,15 @@ def gpu_state():
 
 
 # ------------------------------------------------------------ CPU leg --
-def _oracle_call(p, fmt, layout, keep, out=None, rows=None):
+def _oracle_call(p, fmt, layout, keep, out=None, rows=None, orc=None):
     import oracle
+    orc = orc or oracle.default()
     x = p["x"] if rows is None else p["x"][:rows]
     r = p.get("residual")
     if r is not None and rows is not None:
         r = r[:rows]
-    return oracle.rmsnorm_quant_group(x, p["gamma"], p["eps"], residual=r, group=128 if fmt == 0 else 32, fmt=fmt,
-                                      scale_layout=layout, keep_bf16=keep, out=out)
+    return orc.rmsnorm_quant_group(x, p["gamma"], p["eps"], residual=r, group=128 if fmt == 0 else 32, fmt=fmt,
+                                   scale_layout=layout, keep_bf16=keep, out=out)
 
 
 def _oracle_out(p, fmt, layout, keep, rows):
@@ -618,9 +619,10 @@ def cpu_baseline(w, budget_s):
     before timing, so each timed call is the oracle's own work (its OpenMP
     loop over rows, with the threads the host gives it), repeated until
     budget_s has passed (at least three times); then a single-thread run on a
-    512-row sample (in a child process, with the oracle's thread count set
-    through the OpenMP runtime: a host may fix OMP_NUM_THREADS for every
-    process it starts), median of 5, also on preallocated outputs."""
+    512-row sample with the same source built without OpenMP (oracle.serial():
+    a host's OpenMP runtime may keep its own thread count whatever the
+    process asks for), median of 5, also on preallocated outputs, in a child
+    process."""
     import oracle
     p = w.host[0]
     M, N = p["x"].shape
@@ -641,14 +643,14 @@ def cpu_baseline(w, budget_s):
     rows = min(M, 512)
     code = ("import sys, time; sys.path.insert(0, %r)\n"
             "from fp4_quant_amd import inputs\nimport bench, oracle\n"
-            "oracle.set_num_threads(1)\n"
+            "orc = oracle.serial()\n"
             "p = inputs.make_problem(%d, %d, seed_x=0, residual=%r, outliers=True)\n"
             "out = bench._oracle_out(p, %d, %d, %r, %d)\n"
-            "bench._oracle_call(p, %d, %d, %r, out)\n"
+            "bench._oracle_call(p, %d, %d, %r, out, orc=orc)\n"
             "ts = []\n"
             "for _ in range(5):\n"
-            "    t0 = time.perf_counter(); bench._oracle_call(p, %d, %d, %r, out); ts.append(time.perf_counter() - t0)\n"
-            "print(oracle.num_threads(), sorted(ts)[2])\n") % (ROOT, rows, N, "residual" in p, w.fmt, w.layout, keep,
+            "    t0 = time.perf_counter(); bench._oracle_call(p, %d, %d, %r, out, orc=orc); ts.append(time.perf_counter() - t0)\n"
+            "print(orc.num_threads(), sorted(ts)[2])\n") % (ROOT, rows, N, "residual" in p, w.fmt, w.layout, keep,
                                                                rows, w.fmt, w.layout, keep, w.fmt, w.layout, keep)
     env = dict(os.environ, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)

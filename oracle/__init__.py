@@ -309,6 +309,21 @@ def default() -> Oracle:
     return _default
 
 
+_serial = None
+
+
+def serial() -> Oracle:
+    """The same oracle built without OpenMP: one thread, whatever the host's
+    OpenMP runtime is told (for a single-core timing)."""
+    global _serial
+    if _serial is None:
+        from . import build as _b
+        if not os.path.exists(_b.LIB_SERIAL):
+            _b.build()
+        _serial = Oracle(_b.LIB_SERIAL)
+    return _serial
+
+
 # Module-level API: the default build.
 def lib():
     return default().lib()

@@ -99,3 +99,20 @@ def test_identity_fields():
     h = bench.host_info()
     assert h["logical_cpus"] >= 1
     assert bench.median([3, 1, 2]) == 2 and bench.median([4, 1, 2, 3]) == 2.5
+
+
+def test_serial_oracle_is_one_thread_and_equal():
+    """The single-thread CPU leg times the oracle built without OpenMP
+    (oracle.serial()): one thread whatever the host's OpenMP runtime imposes,
+    and the same outputs as the OpenMP build."""
+    import numpy as np
+    import oracle
+    from fp4_quant_amd import inputs
+    assert oracle.serial().num_threads() == 1
+    p = inputs.make_problem(37, 1024, seed_x=5, residual=True, outliers=True)
+    for fmt, layout in ((0, 0), (1, 1)):
+        a = bench._oracle_out(p, fmt, layout, True, 37)
+        b = bench._oracle_out(p, fmt, layout, True, 37)
+        bench._oracle_call(p, fmt, layout, True, a)
+        bench._oracle_call(p, fmt, layout, True, b, orc=oracle.serial())
+        assert a.keys() == b.keys() and all(np.array_equal(a[k], b[k]) for k in a)
