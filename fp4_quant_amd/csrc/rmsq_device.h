@@ -104,6 +104,41 @@ __device__ __forceinline__ uint32_t amax8(u32x4 w) {
   return max((uint32_t)m[0], (uint32_t)m[1]);
 }
 
+// The inverse norm inv = 1 / sqrt(d), d = ss/N + eps, as the definition forms
+// it in fp64: a correctly rounded square root, then a correctly rounded
+// division (0 when d is 0, and for an infinite d). About 30 fp64
+// instructions, two of them transcendental; the kernels need it only where
+// an element is redone in fp64.
+__device__ __forceinline__ double inv_norm64(double d) { return d > 0.0 ? 1.0 / __builtin_sqrt(d) : 0.0; }
+
+// What every element needs from the inverse norm: inv32 = fl32(inv) and
+// whether the row takes the exact path for all its elements (inv > 2^16,
+// where an h * gamma that underflows to zero in fp32 could still have a
+// nonzero bf16 result, or inv < 2^-100), without forming inv itself.
+//
+// z = 1/sqrt(d) is refined from v_rsq_f64 by two Newton steps
+// z' = z + (z/2)(1 - (d z) z), each taking a relative error e to at most
+// 1.5 e^2 plus 1.5 units of fp64 rounding (2^-53): from any start within
+// 2^-14 (v_rsq_f64 is far closer) to within 2^-27, then within 2^-52.4.
+// inv rounds twice, so it is within 2^-52 (1 + 2^-52) of 1/sqrt(d), and
+// |z - inv| < 2^-51 z. Rounding to nearest is monotone, so fl32(z) = fl32(inv)
+// unless an fp32 rounding midpoint lies within 2^-51 z of z: in z's binade
+// [2^k, 2^k+1) the midpoints are where the 29 mantissa bits below fp32
+// precision read 2^28, and one unit of those bits is at least 2^-53 z, so
+// that can only happen when they lie within 4 of 2^28. Within 32 of it
+// (about one row in 10^7) and for d outside (0, inf), inv is formed in full.
+// The row test on z is widened by 2^-48 (relative) so that it also holds
+// for inv.
+__device__ __forceinline__ float inv_norm32(double d, bool& row_exact) {
+  double z = __builtin_amdgcn_rsq(d);
+  z = __builtin_fma(0.5 * z, __builtin_fma(-(d * z), z, 1.0), z);
+  z = __builtin_fma(0.5 * z, __builtin_fma(-(d * z), z, 1.0), z);
+  const uint32_t t = (uint32_t)__double_as_longlong(z) & 0x1FFFFFFFu;
+  if (__builtin_expect((t - (0x10000000u - 32u) <= 64u) | !(d > 0.0 && d < __builtin_inf()), 0)) z = inv_norm64(d);
+  row_exact = z > 0x1.ffffffffffffcp15 || (z != 0.0 && z < 0x1.0000000000010p-100);
+  return (float)z;
+}
+
 // Classes of an fp32 product h * gamma that is not exact or not finite:
 // NaN, +-infinity, +-denormal (v_cmp_class_f32 mask). A normal product of two
 // bf16 (8 significant bits each) is exact in fp32.
@@ -111,7 +146,8 @@ constexpr int kInexactProduct = 0x001 | 0x002 | 0x004 | 0x010 | 0x080 | 0x200;
 
 // bf16(h * g * inv) for 8 elements: h bf16 values (as fp32, and packed two
 // per dword in hpk), g the 8 bf16 gammas packed two per dword, inv the fp64
-// inverse norm and inv32 = fl32(inv). hg = h * g is exact in fp32 unless it
+// inverse norm (returned by inv64(), which only the rare fp64 path calls) and
+// inv32 = fl32(inv). hg = h * g is exact in fp32 unless it
 // leaves the normal range; then fl32(inv) and the product each round once,
 // so y = hg * inv32 is within 2^-23 (1 + 2^-25) |y| of h * g * inv, under
 // 2 (1 + 2^-22) ulps of y's binade: a y at least 3 ulps from a bf16 midpoint
@@ -134,16 +170,21 @@ constexpr int kInexactProduct = 0x001 | 0x002 | 0x004 | 0x010 | 0x080 | 0x200;
 // the fast path it is the bf16 of the largest |y| (one v_max3_f32 with
 // absolute-value operands per pair, one convert); the fp64 path takes it from
 // the final words.
+template <class Inv64>
 __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, const u32x4 g, float inv32,
-                                             double inv, bool row_exact, uint32_t& am) {
+                                             Inv64 inv64, bool row_exact, uint32_t& am) {
   u32x4 yw;
   u16x2 lo_min = {0xFFFFu, 0xFFFFu};
   bool odd = row_exact;
   float ymax;
+  // the class mask as a scalar operand (a literal would be rematerialized in
+  // a vector register for every call)
+  int cls = kInexactProduct;
+  asm("" : "+s"(cls));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float hg0 = h[2 * i] * bf16_lo(g[i]), hg1 = h[2 * i + 1] * bf16_hi(g[i]);
-    odd |= __builtin_amdgcn_classf(hg0, kInexactProduct) | __builtin_amdgcn_classf(hg1, kInexactProduct);
+    odd |= __builtin_amdgcn_classf(hg0, cls) | __builtin_amdgcn_classf(hg1, cls);
     const float y0 = hg0 * inv32, y1 = hg1 * inv32;
     const uint32_t lows = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x05040100u);
     lo_min = __builtin_elementwise_min(lo_min, __builtin_bit_cast(u16x2, lows) + u16x2{0x8002u, 0x8002u});
@@ -158,9 +199,10 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
     // 16 intermediates alive across the branch (the empty asm hides that
     // they are the same values, so the compiler does not hold them in
     // registers for the whole phase).
+    double inv = inv64();
     u32x4 gr = g, hr = hpk;
     float ir = inv32;
-    asm volatile("" : "+v"(gr), "+v"(hr), "+v"(ir));
+    asm volatile("" : "+v"(gr), "+v"(hr), "+v"(ir), "+v"(inv));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float ge = (e & 1) ? bf16_hi(gr[e >> 1]) : bf16_lo(gr[e >> 1]);

@@ -22,8 +22,11 @@
 // Numerics (results equal the double-precision definition bit for bit):
 //  * h = bf16(x + r): the fp32 sum rounds to the same bf16 as the exact sum.
 //  * sum of h^2 in fp64 (each square exact), DPP tree within the wave, then
-//    the waves' partial sums in wave order through LDS,
-//    inv = 1/sqrt(ss/N + eps) in fp64 with correctly rounded divide / sqrt.
+//    the waves' partial sums in a fixed pairwise tree through LDS,
+//    inv = 1/sqrt(ss/N + eps) in fp64 with correctly rounded divide / sqrt;
+//    fl32(inv) comes from a Newton-refined reciprocal square root that is
+//    close enough to decide it, and inv itself is formed only where an
+//    element is redone in fp64.
 //  * y = (h*g) * inv: h*g is exact in fp32 while it stays in the normal
 //    range; the product is first taken in fp32 with fl32(inv) (within 2 ulp
 //    of the fp64 product); only when it lands within 2 ulp of a bf16
@@ -204,18 +207,32 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
     m = live ? r : M - 1;
   }
   const int C = N >> 3;
-  // what a lane loads at step j: row pointer + load(j), clamped to the row's
-  // last step (kUniform: a wave-uniform offset, so the lane offset tid is
-  // shared by every step) or to its last chunk (kRagged)
+  // What a lane loads at step j: the row's chunk j*T + tid, clamped to the
+  // row's last step (kUniform: a wave-uniform offset, so the lane offset tid
+  // is shared by every step) or to its last chunk (kRagged). Rows packed one
+  // per wave address it as a 32-bit byte offset from the wave-uniform row
+  // pointer, so the loads take the scalar-base form
+  // (SGPR base + 32-bit VGPR offset) with no 64-bit vector address add per
+  // load (the empty asm keeps the uniform part whole: left alone, the
+  // compiler shares row + lane offset between the loads and adds each step's
+  // offset to it in vector registers). Rows over several waves keep plain
+  // indexing, which measured 0.15% faster on the bandwidth-bound shapes.
   const int jl = TAIL == kUniform ? C / T - 1 : 0;
-  auto load = [&](const u32x4* row, int j) {
-    if constexpr (TAIL == kUniform) return (row + min(j, jl) * T)[tid];
-    return row[TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1)];
+  using gchar = const __attribute__((address_space(1))) char;
+  using gu32x4 = const __attribute__((address_space(1))) u32x4;
+  auto at = [&](const u32x4* row, int j) -> gu32x4* {
+    if constexpr (PACK == kPackWave) {
+      gchar* b = (gchar*)row;
+      if constexpr (TAIL == kUniform) b += (int64_t)min(j, jl) * T * 16;
+      asm("" : "+s"(b));
+      const int c = TAIL == kUniform ? tid : TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1);
+      return (gu32x4*)(b + (uint32_t)(c * 16));
+    }
+    if constexpr (TAIL == kUniform) return (gu32x4*)(row + min(j, jl) * T + tid);
+    return (gu32x4*)(row + (TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1)));
   };
-  auto load_nt = [&](const u32x4* row, int j) {
-    if constexpr (TAIL == kUniform) return __builtin_nontemporal_load(row + min(j, jl) * T + tid);
-    return __builtin_nontemporal_load(row + (TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1)));
-  };
+  auto load = [&](const u32x4* row, int j) { return *at(row, j); };
+  auto load_nt = [&](const u32x4* row, int j) { return __builtin_nontemporal_load(at(row, j)); };
   // ---- loads: x, gamma (short rows), then r, all issued before any use ---
   // (of the issue orders measured, this one was fastest on both the
   // bandwidth-bound and the latency-bound shapes)
@@ -229,12 +246,14 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   u32x4 xv[J], rv[RES ? J : 1], gv[kShort ? J : 1];
 #pragma unroll
   for (int j = 0; j < J; ++j) xv[j] = load_nt(xrow, j);
+  if constexpr (PACK == kPackWave) __builtin_amdgcn_sched_barrier(0);
   if constexpr (kShort) {
 #pragma unroll
     for (int j = 0; j < J; ++j) gv[j] = load(grow, j);
   }
-  // keep the r loads in place: the scheduler may otherwise interleave them
-  // with x's, or hoist x's unpacking (and the wait for x) above them
+  // keep the loads in this order: the scheduler may otherwise interleave
+  // gamma's or r's with x's, or hoist x's unpacking (and the wait for x)
+  // above them
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (RES) {
 #pragma unroll
@@ -323,12 +342,18 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   const double q0 = ss * rn;
   const double ms = __builtin_fma(__builtin_fma(-q0, nd, ss), rn, q0);
   const double denom = ms + (double)eps;
-  const double inv = denom > 0.0 ? 1.0 / __builtin_sqrt(denom) : 0.0;
-  const float inv32 = (float)inv;
-  // Rows whose inverse norm leaves the comfortable fp32 range take the exact
-  // path for every element: inv > 2^16, where an h * gamma that underflows to
-  // zero in fp32 could still have a nonzero bf16 result, and inv < 2^-100.
-  const bool row_exact = inv > 0x1p16 || (inv != 0.0 && inv < 0x1p-100);
+  // fl32 of the inverse norm; the fp64 value itself is formed only where an
+  // element is redone in fp64. Rows whose inverse norm leaves the
+  // comfortable fp32 range take the exact path for every element.
+  bool row_exact;
+  const float inv32 = inv_norm32(denom, row_exact);
+  // (The empty asm keeps the compiler from hoisting the loop-invariant fp64
+  // inverse out of the rare block that calls this.)
+  const auto inv64 = [denom] {
+    double d = denom;
+    asm volatile("" : "+v"(d));
+    return inv_norm64(d);
+  };
 
   // ---- phase 2: normalize, bf16, group scale, codes -----------------------
   u32x4* ybrow = ybase ? reinterpret_cast<u32x4*>(ybase + m * ldb) : nullptr;
@@ -348,7 +373,7 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
       hv[2 * i + 1] = kKeepH ? hf[kKeepH ? j : 0][2 * i + 1] : bf16_hi(xv[j][i]);
     }
     uint32_t am;
-    const u32x4 yw = norm_bf16x8(hv, xv[j], g, inv32, inv, row_exact, am);
+    const u32x4 yw = norm_bf16x8(hv, xv[j], g, inv32, inv64, row_exact, am);
     // All stores of a row go out after its reduction: keeping the residual
     // write next to the others measured 3% faster than writing it as soon as
     // it is formed.

@@ -24,9 +24,18 @@ __global__ void k_norm_bf16(const float* hv, const float* gv, const double* inv,
       g[i] = (__float_as_uint(gv[8 * k + 2 * i]) >> 16) | (__float_as_uint(gv[8 * k + 2 * i + 1]) & 0xFFFF0000u);
     }
     uint32_t am;
-    const u32x4 w = norm_bf16x8(h, hp, g, (float)inv[k], inv[k], row_exact[k] != 0, am);
+    const u32x4 w = norm_bf16x8(h, hp, g, (float)inv[k], [&] { return inv[k]; }, row_exact[k] != 0, am);
     for (int e = 0; e < 8; ++e) out[8 * k + e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
     am_out[k] = (uint16_t)am;
+  }
+}
+
+// the fused kernels' fl32 of the inverse norm of d, and their row test
+__global__ void k_inv_norm(const double* d, float* inv32, uint8_t* row_exact, int64_t n) {
+  GRID_LOOP(i, n) {
+    bool ex;
+    inv32[i] = inv_norm32(d[i], ex);
+    row_exact[i] = ex;
   }
 }
 
@@ -169,6 +178,10 @@ int probe_norm_bf16(const float* h, const float* g, const double* inv, const uin
   if (n <= 0) return 0;
   hipLaunchKernelGGL(k_norm_bf16, GRID(n), h, g, inv, ex, out, am, n);
   return launch_status();
+}
+int probe_inv_norm(const double* d, float* inv32, uint8_t* ex, int64_t n, void* stream) {
+  hipLaunchKernelGGL(k_inv_norm, GRID(n), d, inv32, ex, n);
+  return (int)hipGetLastError();
 }
 int probe_fp8_scale(const uint16_t* a, float* s, int64_t n, void* stream) {
   if (n <= 0) return 0;

@@ -192,6 +192,38 @@ def test_norm_bf16x8_products_outside_the_fp32_normal_range(orc):
         assert np.array_equal(host(am).view(np.uint16), (want & 0x7FFF).reshape(-1, 8).max(axis=1))
 
 
+def test_inverse_norm_fp32_and_row_test():
+    """inv_norm32 (hardware v_rsq_f64, two Newton steps, a margin check with a
+    fallback to the full fp64 formula) gives fl32 of inv = fl64(1 / fl64(sqrt(d)))
+    and flags every row with inv > 2^16 or inv < 2^-100: random d over the
+    range the kernels form, d aimed so that inv lies within a few hundred fp64
+    ulps of an fp32 rounding midpoint, d around the row thresholds, and the
+    ends (d = 0 and d = inf give inv = 0)."""
+    say("inv_norm32")
+    rng = np.random.default_rng(21)
+    n = 1_000_000
+    d_rand = np.ldexp(1.0 + rng.random(n), rng.integers(-280, 271, n))
+    e = rng.integers(-120, 120, n)
+    mid = np.ldexp(1.0 + (rng.integers(0, 2 ** 23, n) + 0.5) * 2.0 ** -23, e)
+    d_aim = (1.0 / (mid * mid)) * (1.0 + rng.integers(-400, 401, n) * 2.0 ** -53)
+    j = np.arange(-3000, 3001)
+    d_thr = np.concatenate([1.0 / (t * (1.0 + j * 2.0 ** -53)) ** 2 for t in (2.0 ** 16, 2.0 ** -100)])
+    d = np.concatenate([d_rand, d_aim, d_thr, [0.0, np.inf, 2.0 ** -149, 1.0, 0.25, 4.0]])
+    inv32 = torch.empty(d.size, dtype=torch.float32, device="cuda")
+    ex = torch.empty(d.size, dtype=torch.uint8, device="cuda")
+    call_probe("probe_inv_norm", dev(d), inv32, ex, n=d.size)
+    with np.errstate(divide="ignore"):
+        inv = np.where(d > 0, 1.0 / np.sqrt(d), 0.0)
+    got = host(inv32)
+    bad = np.flatnonzero(got.view(np.uint32) != inv.astype(np.float32).view(np.uint32))
+    assert bad.size == 0, f"{bad.size} differ, first d={d[bad[0]]!r} inv={inv[bad[0]]!r} got={got[bad[0]]!r}"
+    flag = host(ex).astype(bool)
+    must = (inv > 2.0 ** 16) | ((inv != 0) & (inv < 2.0 ** -100))
+    must_not = (inv <= 2.0 ** 16 * (1 - 2.0 ** -47)) & ((inv == 0) | (inv >= 2.0 ** -100 * (1 + 2.0 ** -47)))
+    assert np.all(flag[must]) and not np.any(flag[must_not])
+    assert must.sum() > 1000 and must_not.sum() > 1000
+
+
 def test_fp8_scale_every_amax():
     say("fp8_scale")
     out = torch.empty(MAG16.size, dtype=torch.float32, device="cuda")
