@@ -264,8 +264,9 @@ __device__ __forceinline__ float fp8_scale(uint32_t amax_bits) {
 // those of v*r_lo - one product and half a convert per element - and only a
 // group with an exact scale (448 s = amax, about one in seven) needs both:
 // the two codes are then neighbours of one sign where they differ, c_hi =
-// c_lo + 1 in each differing byte, so qh - qw has 0x01 in exactly those
-// bytes (no borrows), and adding it where c_lo is odd gives the even code.
+// c_lo + 1 in each differing byte, and the even one of the pair is
+// (c_lo + c_hi + (c_lo & 1)) / 2 in every byte (where they agree too), one
+// v_lerp_u8 per four codes.
 // Groups whose scale is below 2^-100 (no normal reciprocal) take the
 // double-precision path element by element.
 __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s, float amax) {
@@ -280,9 +281,8 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s, float ama
     return qw;
   }
   const uint32_t rb = __float_as_uint(__builtin_amdgcn_rcpf(s));
-  const float r_lo = __uint_as_float(rb - 4u), r_hi = __uint_as_float(rb + 4u);
   const float t = __builtin_fmaf(s, 448.0f, -amax);
-  const float r = t < 0.0f ? r_hi : r_lo;
+  const float r = __uint_as_float(rb + (t < 0.0f ? 4u : -4u));   // r_hi or r_lo
   float p[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) p[e] = v[e] * r;
@@ -292,6 +292,7 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s, float ama
   qw[0] = cvt_fp8x2<true>(p[2], p[3], cvt_fp8x2<false>(p[0], p[1], __float_as_uint(p[1])));
   qw[1] = cvt_fp8x2<true>(p[6], p[7], cvt_fp8x2<false>(p[4], p[5], __float_as_uint(p[5])));
   if (t == 0.0f) {   // exact scale: ties take the even code
+    const float r_hi = __uint_as_float(rb + 4u);
     float h[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = v[e] * r_hi;
@@ -299,7 +300,7 @@ __device__ __forceinline__ u32x2 fp8_codes8(const float v[8], float s, float ama
     qh[0] = cvt_fp8x2<true>(h[2], h[3], cvt_fp8x2<false>(h[0], h[1], __float_as_uint(h[1])));
     qh[1] = cvt_fp8x2<true>(h[6], h[7], cvt_fp8x2<false>(h[4], h[5], __float_as_uint(h[5])));
 #pragma unroll
-    for (int k = 0; k < 2; ++k) qw[k] += (qh[k] - qw[k]) & qw[k];
+    for (int k = 0; k < 2; ++k) qw[k] = __builtin_amdgcn_lerp(qw[k], qh[k], qw[k]);
   }
   return qw;
 }
