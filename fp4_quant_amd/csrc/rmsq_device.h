@@ -104,6 +104,14 @@ __device__ __forceinline__ uint32_t amax8(u32x4 w) {
   return max((uint32_t)m[0], (uint32_t)m[1]);
 }
 
+// A raw buffer resource over `bytes` bytes at p (untyped 32-bit data
+// format, no stride): a buffer load whose lane offset is at or past `bytes`
+// returns zeros and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+constexpr int kBufNontemporal = 2;   // cache-policy operand of the buffer loads: nt
+
 // The inverse norm inv = 1 / sqrt(d), d = ss/N + eps, as the definition forms
 // it in fp64: a correctly rounded square root, then a correctly rounded
 // division (0 when d is 0, and for an infinite d). About 30 fp64

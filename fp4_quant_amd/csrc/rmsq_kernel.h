@@ -210,29 +210,28 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // What a lane loads at step j: the row's chunk j*T + tid, clamped to the
   // row's last step (kUniform: a wave-uniform offset, so the lane offset tid
   // is shared by every step) or to its last chunk (kRagged). Rows packed one
-  // per wave address it as a 32-bit byte offset from the wave-uniform row
-  // pointer, so the loads take the scalar-base form
-  // (SGPR base + 32-bit VGPR offset) with no 64-bit vector address add per
-  // load (the empty asm keeps the uniform part whole: left alone, the
-  // compiler shares row + lane offset between the loads and adds each step's
-  // offset to it in vector registers). Rows over several waves keep plain
-  // indexing, which measured 0.15% faster on the bandwidth-bound shapes.
+  // per wave read through buffer resources over the row instead: a chunk
+  // past the row's end (a whole step of a shorter row in a kUniform launch,
+  // the tail lanes of a ragged one) then reads zeros and touches no memory,
+  // where the clamped form re-read a kilobyte per step from the caches, and
+  // the loads take the row as a scalar base with one shared lane offset.
+  // Rows over several waves keep plain indexing, which measured 0.15% faster
+  // on the bandwidth-bound shapes than a scalar-base form.
   const int jl = TAIL == kUniform ? C / T - 1 : 0;
-  using gchar = const __attribute__((address_space(1))) char;
-  using gu32x4 = const __attribute__((address_space(1))) u32x4;
-  auto at = [&](const u32x4* row, int j) -> gu32x4* {
-    if constexpr (PACK == kPackWave) {
-      gchar* b = (gchar*)row;
-      if constexpr (TAIL == kUniform) b += (int64_t)min(j, jl) * T * 16;
-      asm("" : "+s"(b));
-      const int c = TAIL == kUniform ? tid : TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1);
-      return (gu32x4*)(b + (uint32_t)(c * 16));
-    }
-    if constexpr (TAIL == kUniform) return (gu32x4*)(row + min(j, jl) * T + tid);
-    return (gu32x4*)(row + (TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1)));
+  auto at = [&](const u32x4* row, int j) {
+    if constexpr (TAIL == kUniform) return row + min(j, jl) * T + tid;
+    return row + (TAIL == kExact ? j * T + tid : min(j * T + tid, C - 1));
   };
   auto load = [&](const u32x4* row, int j) { return *at(row, j); };
   auto load_nt = [&](const u32x4* row, int j) { return __builtin_nontemporal_load(at(row, j)); };
+  // (each step has its own resource, starting at the step and ending at the
+  // row's end, so that the range check rests on the lane offset alone)
+  auto load_buf = [&](const void* row, int j, auto policy) {
+    const int done = j * T * 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(reinterpret_cast<const char*>(row) + done, C * 16 > done ? C * 16 - done : 0);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, 0, decltype(policy)::value));
+  };
   // ---- loads: x, gamma (short rows), then r, all issued before any use ---
   // (of the issue orders measured, this one was fastest on both the
   // bandwidth-bound and the latency-bound shapes)
@@ -244,20 +243,32 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   const u32x4* rrow = RES ? reinterpret_cast<const u32x4*>(pr + m * ldr) : nullptr;
   const u32x4* grow = reinterpret_cast<const u32x4*>(pg);
   u32x4 xv[J], rv[RES ? J : 1], gv[kShort ? J : 1];
+  if constexpr (PACK == kPackWave) {
 #pragma unroll
-  for (int j = 0; j < J; ++j) xv[j] = load_nt(xrow, j);
-  if constexpr (PACK == kPackWave) __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kShort) {
+    for (int j = 0; j < J; ++j) xv[j] = load_buf(xrow, j, std::integral_constant<int, kBufNontemporal>{});
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < J; ++j) gv[j] = load(grow, j);
+    for (int j = 0; j < J; ++j) gv[j] = load_buf(grow, j, std::integral_constant<int, 0>{});
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) xv[j] = load_nt(xrow, j);
+    if constexpr (kShort) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) gv[j] = load(grow, j);
+    }
   }
   // keep the loads in this order: the scheduler may otherwise interleave
   // gamma's or r's with x's, or hoist x's unpacking (and the wait for x)
   // above them
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (RES) {
+    if constexpr (PACK == kPackWave) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) rv[j] = load_nt(rrow, j);
+      for (int j = 0; j < J; ++j) rv[j] = load_buf(rrow, j, std::integral_constant<int, kBufNontemporal>{});
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) rv[j] = load_nt(rrow, j);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   // chunks this workgroup normalizes and stores: all of them, or with row

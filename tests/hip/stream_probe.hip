@@ -244,13 +244,32 @@ k_plan_floor(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t rb1, 
   const u32x4* rrow = RES ? reinterpret_cast<const u32x4*>(P.r + m * P.ldr) : nullptr;
   const u32x4* grow = reinterpret_cast<const u32x4*>(P.gamma);
   u32x4 xv[J], rv[RES ? J : 1], gv[J];
+  if constexpr (PACK == rmsq::kPackWave) {
+    // as the kernel: one buffer resource per step, from the step to the
+    // row's end (steps and lanes past it read zeros, no memory)
+    auto ld = [&](const u32x4* row, int j, auto policy) {
+      const int done = j * T * 16;
+      const __amdgpu_buffer_rsrc_t rs =
+          rmsq::buffer_rsrc(reinterpret_cast<const char*>(row) + done, C * 16 > done ? C * 16 - done : 0);
+      return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, 0, decltype(policy)::value));
+    };
 #pragma unroll
-  for (int j = 0; j < J; ++j) xv[j] = __builtin_nontemporal_load(xrow + min(j * T + tid, C - 1));
+    for (int j = 0; j < J; ++j) xv[j] = ld(xrow, j, std::integral_constant<int, rmsq::kBufNontemporal>{});
 #pragma unroll
-  for (int j = 0; j < J; ++j) gv[j] = grow[min(j * T + tid, C - 1)];
-  if constexpr (RES) {
+    for (int j = 0; j < J; ++j) gv[j] = ld(grow, j, std::integral_constant<int, 0>{});
+    if constexpr (RES) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) rv[j] = __builtin_nontemporal_load(rrow + min(j * T + tid, C - 1));
+      for (int j = 0; j < J; ++j) rv[j] = ld(rrow, j, std::integral_constant<int, rmsq::kBufNontemporal>{});
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) xv[j] = __builtin_nontemporal_load(xrow + min(j * T + tid, C - 1));
+#pragma unroll
+    for (int j = 0; j < J; ++j) gv[j] = grow[min(j * T + tid, C - 1)];
+    if constexpr (RES) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) rv[j] = __builtin_nontemporal_load(rrow + min(j * T + tid, C - 1));
+    }
   }
   uint32_t acc = 0;
 #pragma unroll
