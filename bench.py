@@ -24,8 +24,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   parity        the first rows of every timed workload's outputs against the
                 oracle, read back after the timing
   inputs_sha256 sha256 of every generated input array
-  git_sha, source_sha256, gpu_state (clocks, power, temperatures before and
-                after the timed region), host (CPU model, cores)
+  git_sha, source_sha256, gpu_state (clocks, power, temperatures at the
+                start, after a half-second spin-up that lifts the clocks off
+                idle before anything is timed, and before and after the timed
+                region), host (CPU model, cores)
 """
 from __future__ import annotations
 
@@ -324,18 +326,27 @@ class UnfusedWorkload(Workload):
         fq.dynamic_per_group_scaled_quant(yb, M, N, 128 if self.fmt == 0 else 32, self.fmt, self.layout, q, sc, st)
 
 
-def time_workload(w, steps, warmup, windows=1):
-    """Warm up, then time `windows` windows of `steps` back-to-back launches,
-    each between two HIP events recorded on the launch stream (torch's
-    current stream, which the binding passes to the library). Returns the
-    average milliseconds per launch of each window (a list when windows > 1);
-    each step is exactly one launch, so this is both the step time and the
-    kernel's average duration (rocprofv3's kernel trace of the same command
-    reports the same average)."""
+def time_workload(w, steps, warmup, windows=1, min_warm_s=0.05):
+    """Warm up (`warmup` launches, continued until at least `min_warm_s` of
+    launching has passed: the GPU idles while a workload's inputs are
+    built, and a few hundred microsecond-launches leave its clock still
+    ramping through the first windows), then time `windows` windows of
+    `steps` back-to-back launches, each between two HIP events recorded on
+    the launch stream (torch's current stream, which the binding passes to
+    the library). Returns the average milliseconds per launch of each window
+    (a list when windows > 1); each step is exactly one launch, so this is
+    both the step time and the kernel's average duration (rocprofv3's kernel
+    trace of the same command reports the same average)."""
     import torch
     for i in range(warmup):
         w.launch(i)
     torch.cuda.synchronize()
+    t_end, i = time.time() + min_warm_s, warmup
+    while time.time() < t_end:
+        for _ in range(50):
+            w.launch(i)
+            i += 1
+        torch.cuda.synchronize()
     out = []
     for _ in range(windows):
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -346,6 +357,23 @@ def time_workload(w, steps, warmup, windows=1):
         torch.cuda.synchronize()
         out.append(t0.elapsed_time(t1) / steps)
     return out if windows > 1 else out[0]
+
+
+def spin_up_clocks(seconds=0.5):
+    """Keep the GPU busy for a moment (256 MB copies) before the first timed
+    window: from idle it starts at a low engine clock, and the first workload
+    timed would otherwise measure the clock's ramp (a decode window read
+    8.75 us at the start of a run and 6.34 us a few windows later)."""
+    import torch
+    a = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(8):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
 
 
 def median(v):
@@ -775,19 +803,21 @@ def main():
             print("bench.py: GEMM configs are headline workloads only with --only-kernel", file=sys.stderr)
             sys.exit(2)
         wg = GemmWorkload(args.config, **GEMM_SPECS[args.config])
-        pg = time_workload(wg, args.steps, args.warmup)
+        pg = time_workload(wg, args.steps, args.warmup, min_warm_s=0)
         log(f"bench: {args.config}: {pg * 1e3:.2f} us per launch, {wg.bytes / (pg * 1e-3) / 1e9:.0f} GB/s")
         return
     specs, fmt, layout = SPECS[args.config]
     if args.only_kernel:
         log(f"bench: building workload {args.config}")
         w = Workload(args.config, specs, fmt, layout)
-        ms = time_workload(FloorWorkload(w) if args.floor else w, args.steps, args.warmup)
+        ms = time_workload(FloorWorkload(w) if args.floor else w, args.steps, args.warmup, min_warm_s=0)
         log(f"bench: {args.config}{' floor' if args.floor else ''}: {ms * 1e3:.2f} us per launch, "
             f"{w.bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
         return
 
     state = {"start": gpu_state()}
+    spin_up_clocks()
+    state["after_spin_up"] = gpu_state()
     configs, captured, hashes = {}, {}, {}
     if not args.no_configs:
         for name in SPECS:
@@ -867,10 +897,10 @@ def main():
     torch.cuda.synchronize()
     state["before_timed"] = gpu_state()
     t_wall = time.perf_counter()
-    step_ms = time_workload(w, args.steps, args.warmup)
+    step_ms = time_workload(w, args.steps, args.warmup, min_warm_s=0)   # exactly W warm-up steps, then K
     wall = time.perf_counter() - t_wall
     state["after_timed"] = gpu_state()
-    extra = time_workload(w, args.steps, 0, windows=4)
+    extra = time_workload(w, args.steps, 0, windows=4, min_warm_s=0)
     captured[args.config] = (w, w.capture())
     gbps = w.bytes / (step_ms * 1e-3) / 1e9
     log(f"bench: {args.config}: {step_ms * 1e3:.2f} us per launch, {gbps:.0f} GB/s")
