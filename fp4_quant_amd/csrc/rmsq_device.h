@@ -136,15 +136,19 @@ __device__ __forceinline__ double inv_norm64(double d) { return d > 0.0 ? 1.0 / 
 // that can only happen when they lie within 4 of 2^28. Within 32 of it
 // (about one row in 10^7) and for d outside (0, inf), inv is formed in full.
 // The row test on z is widened by 2^-48 (relative) so that it also holds
-// for inv.
-__device__ __forceinline__ float inv_norm32(double d, bool& row_exact) {
+// for inv. inv_lo = fl32(z - inv32) is returned too: inv32 + inv_lo is then
+// within 2^-51 z + 2^-48 z of inv, which the fp64 path uses to decide most
+// elements in fp32.
+__device__ __forceinline__ float inv_norm32(double d, bool& row_exact, float& inv_lo) {
   double z = __builtin_amdgcn_rsq(d);
   z = __builtin_fma(0.5 * z, __builtin_fma(-(d * z), z, 1.0), z);
   z = __builtin_fma(0.5 * z, __builtin_fma(-(d * z), z, 1.0), z);
   const uint32_t t = (uint32_t)__double_as_longlong(z) & 0x1FFFFFFFu;
   if (__builtin_expect((t - (0x10000000u - 32u) <= 64u) | !(d > 0.0 && d < __builtin_inf()), 0)) z = inv_norm64(d);
   row_exact = z > 0x1.ffffffffffffcp15 || (z != 0.0 && z < 0x1.0000000000010p-100);
-  return (float)z;
+  const float inv32 = (float)z;
+  inv_lo = (float)(z - (double)inv32);
+  return inv32;
 }
 
 // Classes of an fp32 product h * gamma that is not exact or not finite:
@@ -154,8 +158,8 @@ constexpr int kInexactProduct = 0x001 | 0x002 | 0x004 | 0x010 | 0x080 | 0x200;
 
 // bf16(h * g * inv) for 8 elements: h bf16 values (as fp32, and packed two
 // per dword in hpk), g the 8 bf16 gammas packed two per dword, inv the fp64
-// inverse norm (returned by inv64(), which only the rare fp64 path calls) and
-// inv32 = fl32(inv). hg = h * g is exact in fp32 unless it
+// inverse norm (returned by inv64(), which only the rare fp64 path calls),
+// inv32 = fl32(inv) and inv_lo with inv32 + inv_lo within 2^-47.8 inv of inv. hg = h * g is exact in fp32 unless it
 // leaves the normal range; then fl32(inv) and the product each round once,
 // so y = hg * inv32 is within 2^-23 (1 + 2^-25) |y| of h * g * inv, under
 // 2 (1 + 2^-22) ulps of y's binade: a y at least 3 ulps from a bf16 midpoint
@@ -178,9 +182,9 @@ constexpr int kInexactProduct = 0x001 | 0x002 | 0x004 | 0x010 | 0x080 | 0x200;
 // the fast path it is the bf16 of the largest |y| (one v_max3_f32 with
 // absolute-value operands per pair, one convert); the fp64 path takes it from
 // the final words.
-template <class Inv64>
+template <bool SPLIT = true, class Inv64>
 __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, const u32x4 g, float inv32,
-                                             Inv64 inv64, bool row_exact, uint32_t& am) {
+                                             float inv_lo, Inv64 inv64, bool row_exact, uint32_t& am) {
   u32x4 yw;
   u16x2 lo_min = {0xFFFFu, 0xFFFFu};
   bool odd = row_exact;
@@ -207,19 +211,68 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
     // 16 intermediates alive across the branch (the empty asm hides that
     // they are the same values, so the compiler does not hold them in
     // registers for the whole phase).
-    double inv = inv64();
-    u32x4 gr = g, hr = hpk;
-    float ir = inv32;
-    asm volatile("" : "+v"(gr), "+v"(hr), "+v"(ir), "+v"(inv));
+    //
+    // An element taken for its midpoint window alone (h*g normal, the row
+    // not flagged, 2^-100 <= |y| < 2^127) is decided in fp32 first (SPLIT):
+    // with M the bf16 midpoint next to y = fl32(hg inv32) (the same upper 16
+    // bits, low half 0x8000), D = (y - M) + (t1 + t2), t1 = fma(hg, inv32, -y)
+    // the product's exact residual and t2 = hg inv_lo, equals hg inv - M to
+    // within 2^-45.9 |y| before its own last rounding, which keeps its sign
+    // (inv32 + inv_lo within 2^-47.8 inv of inv; t2 and t1 + t2 round once,
+    // to within 2^-48 |y| and 2^-47 |y|; y - M and t1 are exact), and the
+    // definition's fp64 Y lies within 2^-53 |y| of hg inv. So where
+    // |D| > 2^-45 |M| (|M| within 2^-7 of |y|) the
+    // sign of D says on which side of M Y lies: the upper bf16 (away from
+    // zero) when D has y's sign, the lower otherwise. The rest - ties, near
+    // ties, flagged rows and products, extreme magnitudes - are redone in
+    // fp64 from h and g (their product is exact there) with a single rounding
+    // of h g inv, and only then is inv formed (about 30 dependent fp64
+    // instructions that the waves entering this block, the last to finish a
+    // launch, would otherwise all wait for). SPLIT false: inv formed at once,
+    // for launches whose register budget does not take the larger block.
+    if constexpr (SPLIT) {
+      u32x4 gr = g, hr = hpk;
+      float ir = inv32, il = inv_lo;
+      asm volatile("" : "+v"(gr), "+v"(hr), "+v"(ir), "+v"(il));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float ge = (e & 1) ? bf16_hi(gr[e >> 1]) : bf16_lo(gr[e >> 1]);
-      const float he = (e & 1) ? bf16_hi(hr[e >> 1]) : bf16_lo(hr[e >> 1]);
-      const float hg = he * ge;
-      if (row_exact | __builtin_amdgcn_classf(hg, kInexactProduct) | near_bf16_midpoint(hg * ir)) {
-        const uint32_t b = bf16_from_f64((double)he * (double)ge * inv);
-        const int sh = (e & 1) * 16;
-        yw[e >> 1] = (yw[e >> 1] & ~(0xFFFFu << sh)) | (b << sh);
+      for (int e = 0; e < 8; ++e) {
+        const float ge = (e & 1) ? bf16_hi(gr[e >> 1]) : bf16_lo(gr[e >> 1]);
+        const float he = (e & 1) ? bf16_hi(hr[e >> 1]) : bf16_lo(hr[e >> 1]);
+        const float hg = he * ge;
+        const float y = hg * ir;
+        const bool odd_e = row_exact | __builtin_amdgcn_classf(hg, kInexactProduct);
+        if (odd_e | near_bf16_midpoint(y)) {
+          uint32_t b;
+          bool done = false;
+          const float ay = __builtin_fabsf(y);
+          if (!odd_e && ay >= 0x1p-100f && ay < 0x1p127f) {
+            const float M = __uint_as_float((__float_as_uint(y) & 0xFFFF0000u) | 0x8000u);
+            const float D = (y - M) + (__builtin_fmaf(hg, ir, -y) + hg * il);
+            if (__builtin_fabsf(D) > 0x1p-45f * __builtin_fabsf(M)) {
+              b = (__float_as_uint(y) >> 16) + ((__float_as_uint(D) ^ __float_as_uint(y)) >> 31 ? 0u : 1u);
+              done = true;
+            }
+          }
+          if (!done) b = bf16_from_f64((double)he * (double)ge * inv64());
+          const int sh = (e & 1) * 16;
+          yw[e >> 1] = (yw[e >> 1] & ~(0xFFFFu << sh)) | (b << sh);
+        }
+      }
+    } else {
+      double inv = inv64();
+      u32x4 gr = g, hr = hpk;
+      float ir = inv32;
+      asm volatile("" : "+v"(gr), "+v"(hr), "+v"(ir), "+v"(inv));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ge = (e & 1) ? bf16_hi(gr[e >> 1]) : bf16_lo(gr[e >> 1]);
+        const float he = (e & 1) ? bf16_hi(hr[e >> 1]) : bf16_lo(hr[e >> 1]);
+        const float hg = he * ge;
+        if (row_exact | __builtin_amdgcn_classf(hg, kInexactProduct) | near_bf16_midpoint(hg * ir)) {
+          const uint32_t b = bf16_from_f64((double)he * (double)ge * inv);
+          const int sh = (e & 1) * 16;
+          yw[e >> 1] = (yw[e >> 1] & ~(0xFFFFu << sh)) | (b << sh);
+        }
       }
     }
     am = amax8(yw);

@@ -160,6 +160,11 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // Packed rows of 3 or 4 chunks per lane (held to 64 VGPRs) unpack h again
   // in phase 2 rather than keep 24 or 32 fp32 copies across the reduction.
   constexpr bool kKeepH = kShort && !(kPacked && J >= 3);
+  // The fp64 path decides midpoint-window elements in fp32 first, except
+  // where the larger rare block would not fit: packed rows of 3 chunks with
+  // exact tails (held to 64 VGPRs) and long per-lane rows (whose unrolled
+  // steps it would push past the unroller's limit, into scratch memory).
+  constexpr bool kSplitExact = kShort && !(kPacked && J == 3 && TAIL == kExact);
   __shared__ double red[kMaxWaves];
 
   // Neighbouring row groups run on different XCDs at the same time. (Giving
@@ -357,7 +362,8 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // element is redone in fp64. Rows whose inverse norm leaves the
   // comfortable fp32 range take the exact path for every element.
   bool row_exact;
-  const float inv32 = inv_norm32(denom, row_exact);
+  float inv_lo;
+  const float inv32 = inv_norm32(denom, row_exact, inv_lo);
   // (The empty asm keeps the compiler from hoisting the loop-invariant fp64
   // inverse out of the rare block that calls this.)
   const auto inv64 = [denom] {
@@ -384,7 +390,7 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
       hv[2 * i + 1] = kKeepH ? hf[kKeepH ? j : 0][2 * i + 1] : bf16_hi(xv[j][i]);
     }
     uint32_t am;
-    const u32x4 yw = norm_bf16x8(hv, xv[j], g, inv32, inv64, row_exact, am);
+    const u32x4 yw = norm_bf16x8<kSplitExact>(hv, xv[j], g, inv32, inv_lo, inv64, row_exact, am);
     // All stores of a row go out after its reduction: keeping the residual
     // write next to the others measured 3% faster than writing it as soon as
     // it is formed.
