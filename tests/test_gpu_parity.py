@@ -401,6 +401,51 @@ def test_tie_heavy_rows_exact_codes(orc):
     check(orc, [{"x": x, "gamma": g, "eps": 0.0, "fmt": 1, "keep_bf16": True}])
 
 
+def bf16_tie_rows(M, N, seed):
+    """Rows whose normalized values sit exactly on bf16 rounding midpoints
+    with gamma = 1.5 and eps = 0: sum(h^2) = 4N exactly, so inv = 1/2, and
+    about a quarter of each row are values h in [2, 4) whose product 1.5 h
+    needs one bit more than bf16 holds (the ninth significant bit set, or the
+    two dropped bits 10): y = 0.75 h is then a tie. The rest are +-2 and
+    smaller powers of two that make the squares add up."""
+    rng = np.random.default_rng(seed)
+    mant = np.arange(128, 256)
+    p = 3 * mant
+    tie = ((p < 512) & (p % 2 == 1)) | ((p >= 512) & (p % 4 == 2))
+    vals = mant[tie] / 64.0                      # 8 significant bits, in [2, 4)
+    rows = []
+    for m in range(M):
+        h = np.zeros(N, np.float64)
+        k = N // 4
+        h[:k] = rng.choice(vals, k) * rng.choice([-1, 1], k)
+        R = 4.0 * N - float((h ** 2).sum())
+        free = list(range(k, N))
+        rng.shuffle(free)
+        for v in (2.0, 1.0, 0.5, 0.25, 0.125, 0.0625, 0.03125, 0.015625):
+            while R >= v * v and free:
+                h[free.pop()] = v * rng.choice([-1, 1])
+                R -= v * v
+        assert R == 0 and (h ** 2).sum() == 4.0 * N, R
+        rows.append(rng.permutation(h))
+    return inputs.to_bf16_bits(np.array(rows, np.float32))
+
+
+def test_bf16_ties_and_near_ties_through_the_kernel(orc):
+    """Exact bf16 ties of the normalized value (eps = 0: inv = 1/2 exactly)
+    take the even bf16 and the codes derived from it; with eps = 2^-30 the
+    same products lie about 2^-34 below their midpoints (inv a hair under
+    1/2, fl32(inv) still 1/2), which the rare path decides in fp32 from
+    inv_lo. Both against the oracle, FP8 and MXFP4, with the bf16 output,
+    in one-row-per-wave and row-spanning launches."""
+    say("edge: bf16 ties through the kernel")
+    for N, M in ((1024, 64), (7168, 8)):
+        x = bf16_tie_rows(M, N, 21 + N)
+        g = inputs.to_bf16_bits(np.full(N, 1.5, np.float32))
+        for eps in (0.0, 2.0 ** -30):
+            for fmt in (0, 1):
+                check(orc, [{"x": x, "gamma": g, "eps": eps, "fmt": fmt, "keep_bf16": True}])
+
+
 def test_strides_inplace_and_tiles(orc):
     say("edge: strides, in place, tiles")
     p = inputs.make_problem(33, 7168, seed_x=31, residual=True, outliers=True)
