@@ -30,8 +30,10 @@
 //  * y = (h*g) * inv: h*g is exact in fp32 while it stays in the normal
 //    range; the product is first taken in fp32 with fl32(inv) (within 2 ulp
 //    of the fp64 product); only when it lands within 2 ulp of a bf16
-//    rounding midpoint, or h*g is denormal or infinite, is the element redone
-//    as fp64 h*g*inv rounded once to bf16.
+//    rounding midpoint, or h*g is denormal or infinite, is the element redone:
+//    a midpoint case is decided in fp32 from the sign of y - midpoint
+//    corrected by the product's exact residual and inv's low part, and ties,
+//    near ties and the rest are redone as fp64 h*g*inv rounded once to bf16.
 //  * FP8 scale s = fl32(amax/448), correctly rounded; codes through the
 //    hardware convert of yb * r for two reciprocals r bracketing 1/s: where
 //    both brackets give the same code it is the code of yb/s (rounding is
