@@ -187,6 +187,7 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
                                              float inv_lo, Inv64 inv64, bool row_exact, uint32_t& am) {
   u32x4 yw;
   u16x2 lo_min = {0xFFFFu, 0xFFFFu};
+  u16x2 tw[4];   // per pair: (low 16 bits + 0x8002) mod 2^16, at most 4 in the window
   bool odd = row_exact;
   float ymax;
   // the class mask as a scalar operand (a literal would be rematerialized in
@@ -199,7 +200,8 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
     odd |= __builtin_amdgcn_classf(hg0, cls) | __builtin_amdgcn_classf(hg1, cls);
     const float y0 = hg0 * inv32, y1 = hg1 * inv32;
     const uint32_t lows = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x05040100u);
-    lo_min = __builtin_elementwise_min(lo_min, __builtin_bit_cast(u16x2, lows) + u16x2{0x8002u, 0x8002u});
+    tw[i] = __builtin_bit_cast(u16x2, lows) + u16x2{0x8002u, 0x8002u};
+    lo_min = __builtin_elementwise_min(lo_min, tw[i]);
     ymax = i == 0 ? __builtin_fmaxf(__builtin_fabsf(y0), __builtin_fabsf(y1))
                   : __builtin_fmaxf(__builtin_fmaxf(ymax, __builtin_fabsf(y0)), __builtin_fabsf(y1));
     yw[i] = pack_bf16(y0, y1);
@@ -212,8 +214,8 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
     // they are the same values, so the compiler does not hold them in
     // registers for the whole phase).
     //
-    // An element taken for its midpoint window alone (h*g normal, the row
-    // not flagged, 2^-100 <= |y| < 2^127) is decided in fp32 first (SPLIT):
+    // In a wave with no flagged row or product, an element taken for its
+    // midpoint window (2^-100 <= |y| < 2^127) is decided in fp32 first (SPLIT):
     // with M the bf16 midpoint next to y = fl32(hg inv32) (the same upper 16
     // bits, low half 0x8000), D = (y - M) + (t1 + t2), t1 = fma(hg, inv32, -y)
     // the product's exact residual and t2 = hg inv_lo, equals hg inv - M to
@@ -224,28 +226,33 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
     // |D| > 2^-45 |M| (|M| within 2^-7 of |y|) the
     // sign of D says on which side of M Y lies: the upper bf16 (away from
     // zero) when D has y's sign, the lower otherwise. The rest - ties, near
-    // ties, flagged rows and products, extreme magnitudes - are redone in
-    // fp64 from h and g (their product is exact there) with a single rounding
-    // of h g inv, and only then is inv formed (about 30 dependent fp64
-    // instructions that the waves entering this block, the last to finish a
-    // launch, would otherwise all wait for). SPLIT false: inv formed at once,
-    // for launches whose register budget does not take the larger block.
-    if constexpr (SPLIT) {
+    // ties, extreme magnitudes - are redone in fp64 from h and g (their
+    // product is exact there) with a single rounding of h g inv, and only then
+    // is inv formed (about 30 dependent fp64 instructions that the waves
+    // entering this block, the last to finish a launch, would otherwise all
+    // wait for). Waves with a flagged lane, and launches whose register
+    // budget does not take the larger block (SPLIT false), take the direct
+    // block: inv formed at once, every element needing it redone in fp64.
+    if (SPLIT && !__builtin_amdgcn_ballot_w64(odd)) {
+      // No lane has a flagged product or row: only window elements, read off
+      // the fast path's test values, so that a section costs one compare
+      // (the waves entering this block finish last, and its length is what
+      // the short launches wait for). A flagged lane anywhere in the wave
+      // takes the direct block below.
       u32x4 gr = g, hr = hpk;
       float ir = inv32, il = inv_lo;
       asm volatile("" : "+v"(gr), "+v"(hr), "+v"(ir), "+v"(il));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float ge = (e & 1) ? bf16_hi(gr[e >> 1]) : bf16_lo(gr[e >> 1]);
-        const float he = (e & 1) ? bf16_hi(hr[e >> 1]) : bf16_lo(hr[e >> 1]);
-        const float hg = he * ge;
-        const float y = hg * ir;
-        const bool odd_e = row_exact | __builtin_amdgcn_classf(hg, kInexactProduct);
-        if (odd_e | near_bf16_midpoint(y)) {
+        if ((uint32_t)tw[e >> 1][e & 1] <= 4u) {
+          const float ge = (e & 1) ? bf16_hi(gr[e >> 1]) : bf16_lo(gr[e >> 1]);
+          const float he = (e & 1) ? bf16_hi(hr[e >> 1]) : bf16_lo(hr[e >> 1]);
+          const float hg = he * ge;
+          const float y = hg * ir;
           uint32_t b;
           bool done = false;
           const float ay = __builtin_fabsf(y);
-          if (!odd_e && ay >= 0x1p-100f && ay < 0x1p127f) {
+          if (ay >= 0x1p-100f && ay < 0x1p127f) {
             const float M = __uint_as_float((__float_as_uint(y) & 0xFFFF0000u) | 0x8000u);
             const float D = (y - M) + (__builtin_fmaf(hg, ir, -y) + hg * il);
             if (__builtin_fabsf(D) > 0x1p-45f * __builtin_fabsf(M)) {

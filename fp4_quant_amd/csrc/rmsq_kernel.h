@@ -128,11 +128,12 @@ __device__ __forceinline__ int32_t row_of_block(int32_t b, int32_t rows, int32_t
 //   kUniform  every row has a whole number of chunk steps (a multiple of T
 //             chunks, at most J*T) and every lane group has a row: steps past
 //             a row's end are skipped by the whole wave, with a scalar test,
-//             and their loads re-read the last step (rows packed one per wave
-//             only: the MLA latents, 1536 and 512 wide, in one launch);
-//   kRagged   anything else: lanes past the row end clamp their chunk index,
-//             and lane groups past a problem's last row reload that row and
-//             store nothing.
+//             and their loads read zeros through the row's buffer resources
+//             without touching memory (rows packed one per wave only: the MLA
+//             latents, 1536 and 512 wide, in one launch);
+//   kRagged   anything else: lanes past the row end clamp their chunk index
+//             (read zeros, packed one per wave), and lane groups past a
+//             problem's last row reload that row and store nothing.
 enum Tail { kRagged = 0, kExact = 1, kUniform = 2 };
 enum Pack { kPackNone = 0, kPackWave = 1, kPackLanes = 2 };
 
@@ -162,11 +163,14 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // Packed rows of 3 or 4 chunks per lane (held to 64 VGPRs) unpack h again
   // in phase 2 rather than keep 24 or 32 fp32 copies across the reduction.
   constexpr bool kKeepH = kShort && !(kPacked && J >= 3);
-  // The fp64 path decides midpoint-window elements in fp32 first, except
-  // where the larger rare block would not fit: packed rows of 3 chunks with
-  // exact tails (held to 64 VGPRs) and long per-lane rows (whose unrolled
-  // steps it would push past the unroller's limit, into scratch memory).
-  constexpr bool kSplitExact = kShort && !(kPacked && J == 3 && TAIL == kExact);
+  // The fp64 path decides midpoint-window elements in fp32 first where its
+  // latency bounds the launch: one chunk per lane (decode, short prefills,
+  // rows packed by lanes) and rows packed one per wave up to 3 chunks (the
+  // MLA latents), except 3 chunks with exact tails (held to 64 VGPRs, where
+  // the larger block spills). Rows over several waves with more chunks are
+  // bandwidth-bound; there the larger block cost the prefill batch 3% (it
+  // moves the memory-bound code around the branch) and gains nothing.
+  constexpr bool kSplitExact = J == 1 || (kPacked && J <= 3 && !(J == 3 && TAIL == kExact));
   __shared__ double red[kMaxWaves];
 
   // Neighbouring row groups run on different XCDs at the same time. (Giving
@@ -244,8 +248,9 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   // bandwidth-bound and the latency-bound shapes)
   // A ragged row clamps its chunk index instead of guarding the loads: lanes
   // past the row end re-read the last chunk (the address of a live lane of
-  // the same instruction, so no extra traffic) and their h is zeroed before
-  // the sum of squares; their stores are skipped.
+  // the same instruction, so no extra traffic; rows packed one per wave read
+  // zeros there instead) and their h is zeroed before the sum of squares;
+  // their stores are skipped.
   const u32x4* xrow = reinterpret_cast<const u32x4*>(px + m * ldx);
   const u32x4* rrow = RES ? reinterpret_cast<const u32x4*>(pr + m * ldr) : nullptr;
   const u32x4* grow = reinterpret_cast<const u32x4*>(pg);
