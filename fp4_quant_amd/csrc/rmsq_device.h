@@ -88,9 +88,19 @@ __device__ __forceinline__ uint32_t fp8_exact(float v, float s) {
 // The per-chunk arithmetic of the fused kernel, on 8 consecutive elements.
 
 // Low 16 bits of an fp32 within 2 of 0x8000: at most 2 ulps from a bf16
-// rounding midpoint of its binade.
+// rounding midpoint of its binade. It contains both windows a row can have
+// (below), so the direct fp64 block redoes every element the fast path left
+// undecided without keeping the row's window at hand.
 __device__ __forceinline__ bool near_bf16_midpoint(float y) {
   return ((__float_as_uint(y) & 0xFFFFu) - 0x7FFEu) <= 4u;
+}
+
+// The window of a row, from the sign of inv_lo (inv - inv32 rounded): low
+// halves {0x7FFF, 0x8000} when inv32 <= inv, {0x8000, 0x8001} when inv32 > inv.
+// Returned as the pair offset that maps the window to {0, 1}: (low 16 bits +
+// offset) mod 2^16 <= 1, two 16-bit lanes per dword.
+__device__ __forceinline__ uint32_t bf16_window_offset(float inv_lo) {
+  return 0x80018001u - (__float_as_uint(inv_lo) >> 31) * 0x00010001u;
 }
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
@@ -159,23 +169,26 @@ constexpr int kInexactProduct = 0x001 | 0x002 | 0x004 | 0x010 | 0x080 | 0x200;
 // bf16(h * g * inv) for 8 elements: h bf16 values (as fp32, and packed two
 // per dword in hpk), g the 8 bf16 gammas packed two per dword, inv the fp64
 // inverse norm (returned by inv64(), which only the rare fp64 path calls),
-// inv32 = fl32(inv) and inv_lo with inv32 + inv_lo within 2^-47.8 inv of inv. hg = h * g is exact in fp32 unless it
-// leaves the normal range; then fl32(inv) and the product each round once,
-// so y = hg * inv32 is within 2^-23 (1 + 2^-25) |y| of h * g * inv, under
-// 2 (1 + 2^-22) ulps of y's binade: a y at least 3 ulps from a bf16 midpoint
-// rounds as the exact product does, and as the fp64 product (within 2^-53 of
-// it). Its bf16 rounding is therefore final unless y lies within 2 ulps of a
-// midpoint (errors of about 1.5 ulps occur). Those elements, elements whose
-// hg is denormal or infinite, and every element of a row_exact row are
-// redone in fp64 from h
-// and g (their product is exact there) with a single rounding. (A product
-// that underflows to zero is harmless here: the caller flags rows with
-// inv > 2^16, and below that a zero hg keeps the sign of a true result that
-// rounds to zero in bf16 anyway.) The window test runs on packed 16-bit
-// lanes: the low halves of two products side by side (v_perm_b32), plus
-// 0x8002 modulo 2^16, fall in [0, 4] exactly for the products whose low 16
-// bits lie in [0x7FFE, 0x8002]; the minimum over the 8 elements decides
-// whether any of them needs the fp64 path.
+// inv32 = fl32(inv) and inv_lo with inv32 + inv_lo within 2^-47.8 inv of inv,
+// off the row's window offset (bf16_window_offset(inv_lo)). hg = h * g is
+// exact in fp32 unless it leaves the normal range. With a = hg * inv32 and
+// inv = inv32 (1 + e), |e| <= 2^-24, the exact product is a + a e, where
+// |a e| is under one ulp of y's binade (|a| < 2^24 ulps), and y = fl32(a) is
+// within half an ulp of a: |hg inv| - |y| lies in [-1/2, 3/2) ulps when
+// e >= 0 and in (-3/2, 1/2] when e <= 0. A y whose low 16 bits are below
+// 0x7FFF or above 0x8000 (e >= 0), or below 0x8000 or above 0x8001 (e <= 0),
+// therefore rounds to bf16 as the exact product does, and as the fp64 product
+// (within 2^-53 of it). The sign of inv_lo picks the window; where it differs
+// from that of e, |e| < 2^-50 and either window holds. Elements in the
+// window, elements whose hg is denormal or infinite, and every element of a
+// row_exact row are redone from h and g (their product is exact there) with a
+// single rounding. (A product that underflows to zero is harmless here: the
+// caller flags rows with inv > 2^16, and below that a zero hg keeps the sign
+// of a true result that rounds to zero in bf16 anyway.) The window test runs
+// on packed 16-bit lanes: the low halves of two products side by side
+// (v_perm_b32), plus off modulo 2^16, fall in [0, 1] exactly for the window's
+// two values; the minimum over the 8 elements decides whether any of them
+// needs the rare path.
 //
 // am: the largest |result| as a bf16 magnitude pattern (what amax8 gives for
 // the returned words). Rounding to nearest is monotone and symmetric, so on
@@ -184,10 +197,11 @@ constexpr int kInexactProduct = 0x001 | 0x002 | 0x004 | 0x010 | 0x080 | 0x200;
 // the final words.
 template <bool SPLIT = true, class Inv64>
 __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, const u32x4 g, float inv32,
-                                             float inv_lo, Inv64 inv64, bool row_exact, uint32_t& am) {
+                                             float inv_lo, uint32_t off, Inv64 inv64, bool row_exact,
+                                             uint32_t& am) {
   u32x4 yw;
   u16x2 lo_min = {0xFFFFu, 0xFFFFu};
-  u16x2 tw[4];   // per pair: (low 16 bits + 0x8002) mod 2^16, at most 4 in the window
+  u16x2 tw[4];   // per pair: (low 16 bits + off) mod 2^16, at most 1 in the window
   bool odd = row_exact;
   float ymax;
   // the class mask as a scalar operand (a literal would be rematerialized in
@@ -200,14 +214,14 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
     odd |= __builtin_amdgcn_classf(hg0, cls) | __builtin_amdgcn_classf(hg1, cls);
     const float y0 = hg0 * inv32, y1 = hg1 * inv32;
     const uint32_t lows = __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x05040100u);
-    tw[i] = __builtin_bit_cast(u16x2, lows) + u16x2{0x8002u, 0x8002u};
+    tw[i] = __builtin_bit_cast(u16x2, lows) + __builtin_bit_cast(u16x2, off);
     lo_min = __builtin_elementwise_min(lo_min, tw[i]);
     ymax = i == 0 ? __builtin_fmaxf(__builtin_fabsf(y0), __builtin_fabsf(y1))
                   : __builtin_fmaxf(__builtin_fmaxf(ymax, __builtin_fabsf(y0)), __builtin_fabsf(y1));
     yw[i] = pack_bf16(y0, y1);
   }
   am = pack_bf16(ymax, 0.0f);
-  const bool need = odd | (min((uint32_t)lo_min[0], (uint32_t)lo_min[1]) <= 4u);
+  const bool need = odd | (min((uint32_t)lo_min[0], (uint32_t)lo_min[1]) <= 1u);
   if (__builtin_expect(need, 0)) {   // rare: keep the fast path's code contiguous
     // Rare: recompute the products here instead of keeping the fast path's
     // 16 intermediates alive across the branch (the empty asm hides that
@@ -244,7 +258,7 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
       asm volatile("" : "+v"(gr), "+v"(hr), "+v"(ir), "+v"(il));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if ((uint32_t)tw[e >> 1][e & 1] <= 4u) {
+        if ((uint32_t)tw[e >> 1][e & 1] <= 1u) {
           const float ge = (e & 1) ? bf16_hi(gr[e >> 1]) : bf16_lo(gr[e >> 1]);
           const float he = (e & 1) ? bf16_hi(hr[e >> 1]) : bf16_lo(hr[e >> 1]);
           const float hg = he * ge;

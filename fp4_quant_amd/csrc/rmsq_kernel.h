@@ -371,6 +371,9 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
   bool row_exact;
   float inv_lo;
   const float inv32 = inv_norm32(denom, row_exact, inv_lo);
+  // one row per wave or per workgroup: the window offset is wave-uniform
+  const uint32_t win = PACK == kPackLanes ? bf16_window_offset(inv_lo)
+                                          : __builtin_amdgcn_readfirstlane(bf16_window_offset(inv_lo));
   // (The empty asm keeps the compiler from hoisting the loop-invariant fp64
   // inverse out of the rare block that calls this.)
   const auto inv64 = [denom] {
@@ -397,7 +400,7 @@ rmsq_fused_kernel(int32_t count, int32_t rows, int32_t lg, int32_t slg, int32_t 
       hv[2 * i + 1] = kKeepH ? hf[kKeepH ? j : 0][2 * i + 1] : bf16_hi(xv[j][i]);
     }
     uint32_t am;
-    const u32x4 yw = norm_bf16x8<kSplitExact>(hv, xv[j], g, inv32, inv_lo, inv64, row_exact, am);
+    const u32x4 yw = norm_bf16x8<kSplitExact>(hv, xv[j], g, inv32, inv_lo, win, inv64, row_exact, am);
     // All stores of a row go out after its reduction: keeping the residual
     // write next to the others measured 3% faster than writing it as soon as
     // it is formed.

@@ -24,7 +24,8 @@ __global__ void k_norm_bf16(const float* hv, const float* gv, const double* inv,
       g[i] = (__float_as_uint(gv[8 * k + 2 * i]) >> 16) | (__float_as_uint(gv[8 * k + 2 * i + 1]) & 0xFFFF0000u);
     }
     uint32_t am;
-    const u32x4 w = norm_bf16x8(h, hp, g, (float)inv[k], (float)(inv[k] - (double)(float)inv[k]), [&] { return inv[k]; },
+    const float lo = (float)(inv[k] - (double)(float)inv[k]);
+    const u32x4 w = norm_bf16x8(h, hp, g, (float)inv[k], lo, bf16_window_offset(lo), [&] { return inv[k]; },
                                 row_exact[k] != 0, am);
     for (int e = 0; e < 8; ++e) out[8 * k + e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
     am_out[k] = (uint16_t)am;

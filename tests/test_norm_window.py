@@ -1,23 +1,31 @@
 """The fused kernel rounds y = h * gamma * inv to bf16 from the fp32 product
-y32 = fl32(fl32(h * gamma) * fl32(inv)) and redoes the element in double
-only when the low 16 bits of y32 lie within 2 of the bf16 rounding midpoint
-0x8000. The bound behind that window: h * gamma is exact in fp32 (two 8-bit
-significands), fl32(inv) and the final product each round once, so
-|y32 - h*gamma*inv| <= 2^-23 (1 + 2^-25) |y|, under 2 (1 + 2^-22) ulps of
-y32's binade; an y32 at least 3 ulps from a midpoint therefore rounds to the
-same bf16 as the exact product, and as the double-precision product the
-definition rounds (which is within 2^-53 of it). Inside the window the fp32
-product does round the wrong way now and then; the errors seen reach about
-1.5 ulps, and the window is kept at the proven bound.
+y32 = fl32(fl32(h * gamma) * inv32), inv32 = fl32(inv), and redoes the element
+only when the low 16 bits of y32 fall in a window of two values that each row
+picks from the sign of inv_lo = fl32(z - inv32) (z the refined reciprocal
+square root, within 2^-51 z of inv): {0x7FFF, 0x8000} when inv_lo >= 0,
+{0x8000, 0x8001} when inv_lo < 0.
+
+The bound behind that window: h * gamma is exact in fp32 (two 8-bit
+significands). With a = hg * inv32 and eps = (inv - inv32) / inv32
+(|eps| <= 2^-24), the exact product is a (1 + eps), and |a| eps is under one
+ulp of y32's binade (|a| < 2^24 ulps); y32 = fl32(a) is within half an ulp
+of a. So |hg inv| - |y32| lies in [-1/2, 3/2) ulps when eps >= 0 and in
+(-3/2, 1/2] when eps <= 0: a y32 below 0x7FFF or above 0x8000 (eps >= 0), or
+below 0x8000 or above 0x8001 (eps <= 0), rounds to the same bf16 as the
+exact product, and as the double product the definition rounds (within
+2^-53 of it). Where inv_lo has the other sign than eps, |eps| < 2^-50 and
+either window holds.
 
 This CPU test checks that with the same IEEE binary32 / binary64 operations:
-random bf16 pairs with products in the normal range, and double inverse norms
+random bf16 pairs with products in the normal range; double inverse norms
 chosen to put the exact product within a few fp32 ulps of a bf16 midpoint
 (every mantissa, the top of the binade oversampled, where an ulp is smallest
-relative to the value), plus random inverse norms. Every sample outside the
-window must round like the double product, and enough samples must fall just
-outside it (3 or 4 ulps from the midpoint) for the check to mean something."""
-import os
+relative to the value); random inverse norms; and inverse norms within a few
+fp64 ulps of an fp32 value (eps near zero, where z may put inv_lo on the
+other side). Every sample outside its row's window must round like the double
+product; the signed error must stay in the interval for its sign of eps and
+come near its far end; and both window values must catch products that round
+the other way, so that neither can be dropped."""
 import subprocess
 
 SRC = r"""
@@ -53,57 +61,82 @@ static float rnd_bf16(int elo, int span) {
 }
 
 int main(void) {
-  long n = 0, bad = 0, in_window = 0, just_outside = 0, caught = 0, caught2 = 0;
-  double max_err = 0;   /* largest |y32 - h*g*inv| seen, in ulps of y32's binade */
+  long n = 0, bad = 0, in_window = 0, just_outside = 0, caught_mid = 0, caught_side = 0, flipped = 0;
+  long n_pos = 0, n_neg = 0;
+  /* signed error (|exact| - |y32|) in ulps of y32's binade, by the sign of eps */
+  double pos_min = 9, pos_max = -9, neg_min = 9, neg_max = -9;
   for (long k = 0; k < 6000000; ++k) {
     const float h = rnd_bf16(-20, 40), g = rnd_bf16(-8, 16);
     const float hg = h * g;                               /* exact: normal range */
     double inv;
-    if (k % 4 == 0) {                                     /* random inverse norm */
+    const int kind = (int)(k % 8);
+    if (kind == 0) {                                      /* random inverse norm */
       inv = ldexp(1.0 + (double)(rnd() >> 11) * 0x1p-53, (int)(rnd() % 40) - 20);
     } else {                                              /* aim at a bf16 midpoint */
-      const uint32_t m = (k % 4 == 1) ? 0x7Fu : (uint32_t)(rnd() & 0x7F);
+      const uint32_t m = (kind == 1) ? 0x7Fu : (uint32_t)(rnd() & 0x7F);
       const int e = (int)(rnd() % 40) - 20;
       const double mid = ldexp(1.0 + ((double)m + 0.5) / 128.0, e);   /* 1.m + half a bf16 ulp */
       inv = mid / fabs((double)hg);
-      /* move the product by up to +-6 fp32 ulps of its binade */
       const double ulp32 = ldexp(1.0, e - 23);
-      inv += ((double)(int64_t)(rnd() % 24001) - 12000.0) / 2000.0 * ulp32 / fabs((double)hg);
+      if (kind == 7) {
+        /* eps near zero: an fp32 inverse norm, moved by a few fp64 ulps */
+        inv = (double)(float)inv * (1.0 + ((double)(int64_t)(rnd() % 9) - 4.0) * 0x1p-53);
+      } else {
+        /* move the product by up to +-6 fp32 ulps of its binade */
+        inv += ((double)(int64_t)(rnd() % 24001) - 12000.0) / 2000.0 * ulp32 / fabs((double)hg);
+      }
     }
+    /* the kernel's z: within 3 units of 2^-53 (relative) of inv */
+    const double z = inv * (1.0 + ((double)(int64_t)(rnd() % 7) - 3.0) * 0x1p-53);
     const float inv32 = (float)inv;
+    const float inv_lo = (float)(z - (double)inv32);
+    const int neg = signbit(inv_lo) != 0;
+    if ((inv < (double)inv32) != neg && inv != (double)inv32) ++flipped;
+    const uint32_t wlo = neg ? 0x8000u : 0x7FFFu;         /* the row's window {wlo, wlo + 1} */
+
     const float y32 = hg * inv32;
     const double yo = (double)hg * inv;
-    const int d = (int)(bits_f(y32) & 0xFFFFu) - 0x8000;
+    const uint32_t L = bits_f(y32) & 0xFFFFu;
     ++n;
-    {   /* the exact product to 64 bits (long double), against the bound */
+    {   /* the exact product to 64 bits (long double), signed in magnitude */
       int ey;
       frexpf(y32, &ey);
       const long double ex = (long double)hg * (long double)inv;
-      const double err = (double)fabsl(((long double)y32 - ex) / ldexpl(1.0L, ey - 24));
-      if (err > max_err) max_err = err;
+      const double err = (double)((fabsl(ex) - fabsl((long double)y32)) / ldexpl(1.0L, ey - 24));
+      if (inv >= (double)inv32) {
+        ++n_pos;
+        if (err < pos_min) pos_min = err;
+        if (err > pos_max) pos_max = err;
+      } else {
+        ++n_neg;
+        if (err < neg_min) neg_min = err;
+        if (err > neg_max) neg_max = err;
+      }
     }
-    if (d >= -2 && d <= 2) {                              /* the kernel takes the exact path */
+    const int differs = bf16_of_float(y32) != bf16_of_double(yo);
+    if (L == wlo || L == wlo + 1) {                       /* the kernel takes the exact path */
       ++in_window;
-      if (bf16_of_float(y32) != bf16_of_double(yo)) {
-        if (d == 2 || d == -2) ++caught2;
-        else ++caught;
+      if (differs) {
+        if (L == 0x8000u) ++caught_mid;
+        else ++caught_side;
       }
       continue;
     }
-    if (d == 3 || d == 4 || d == -3 || d == -4) ++just_outside;
-    if (bf16_of_float(y32) != bf16_of_double(yo)) {
-      if (bad < 5) printf("h=%a g=%a inv=%a y32=%a d=%d\n", h, g, inv, y32, d);
+    if (L == wlo - 1 || L == wlo + 2) ++just_outside;
+    if (differs) {
+      if (bad < 5) printf("h=%a g=%a inv=%a y32=%a L=%x window=%x\n", h, g, inv, y32, L, wlo);
       ++bad;
     }
   }
-  printf("checked %ld mismatches %ld window %ld just_outside %ld caught %ld caught_at_2 %ld max_err_ulps %.6f\n", n,
-         bad, in_window, just_outside, caught, caught2, max_err);
+  printf("checked %ld mismatches %ld window %ld just_outside %ld caught_mid %ld caught_side %ld flipped %ld "
+         "n_pos %ld n_neg %ld pos_min %.6f pos_max %.6f neg_min %.6f neg_max %.6f\n", n, bad, in_window,
+         just_outside, caught_mid, caught_side, flipped, n_pos, n_neg, pos_min, pos_max, neg_min, neg_max);
   return bad != 0;
 }
 """
 
 
-def test_norm_midpoint_window_of_two_ulps(tmp_path):
+def test_norm_midpoint_window_per_row(tmp_path):
     src = tmp_path / "window.c"
     exe = tmp_path / "window"
     src.write_text(SRC)
@@ -112,11 +145,17 @@ def test_norm_midpoint_window_of_two_ulps(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     print(out.stdout)
     assert out.returncode == 0, out.stdout
-    fields = dict(zip(out.stdout.split()[0::2], out.stdout.split()[1::2]))
-    assert int(fields["mismatches"]) == 0
-    assert int(fields["window"]) > 100_000
-    assert int(fields["just_outside"]) > 100_000
-    # the window is needed: inside it the fp32 product does round the wrong way
-    assert int(fields["caught"]) > 0
-    # and the error stays within the bound the window is derived from
-    assert 1.0 < float(fields["max_err_ulps"]) <= 2.0 * (1 + 2 ** -22)
+    f = dict(zip(out.stdout.split()[0::2], out.stdout.split()[1::2]))
+    assert int(f["mismatches"]) == 0
+    assert int(f["window"]) > 50_000 and int(f["just_outside"]) > 50_000
+    assert int(f["n_pos"]) > 1_000_000 and int(f["n_neg"]) > 1_000_000
+    # the rows whose inv_lo sign differs from that of eps are exercised
+    assert int(f["flipped"]) > 1000
+    # both window values are needed: each catches products that round the other way
+    assert int(f["caught_mid"]) > 0 and int(f["caught_side"]) > 0
+    # the signed error stays in the interval the window is derived from, and
+    # comes near its far end (so the window cannot shift toward the midpoint)
+    tiny = 2.0 ** -20
+    assert -0.5 - tiny <= float(f["pos_min"]) and float(f["pos_max"]) < 1.5
+    assert -1.5 < float(f["neg_min"]) and float(f["neg_max"]) <= 0.5 + tiny
+    assert float(f["pos_max"]) > 1.3 and float(f["neg_min"]) < -1.3
