@@ -244,9 +244,10 @@ __device__ __forceinline__ u32x4 norm_bf16x8(const float h[8], const u32x4 hpk, 
     // product is exact there) with a single rounding of h g inv, and only then
     // is inv formed (about 30 dependent fp64 instructions that the waves
     // entering this block, the last to finish a launch, would otherwise all
-    // wait for). Waves with a flagged lane, and launches whose register
-    // budget does not take the larger block (SPLIT false), take the direct
-    // block: inv formed at once, every element needing it redone in fp64.
+    // wait for). Waves with a flagged lane, and kernels that keep the
+    // smaller code (SPLIT false: where the larger block would spill, or on
+    // bandwidth-bound rows, where it gains nothing), take the direct block:
+    // inv formed at once, every element needing it redone in fp64.
     if (SPLIT && !__builtin_amdgcn_ballot_w64(odd)) {
       // No lane has a flagged product or row: only window elements, read off
       // the fast path's test values, so that a section costs one compare

@@ -28,17 +28,21 @@
 //    close enough to decide it, and inv itself is formed only where an
 //    element is redone in fp64.
 //  * y = (h*g) * inv: h*g is exact in fp32 while it stays in the normal
-//    range; the product is first taken in fp32 with fl32(inv) (within 2 ulp
-//    of the fp64 product); only when it lands within 2 ulp of a bf16
-//    rounding midpoint, or h*g is denormal or infinite, is the element redone:
-//    a midpoint case is decided in fp32 from the sign of y - midpoint
-//    corrected by the product's exact residual and inv's low part, and ties,
-//    near ties and the rest are redone as fp64 h*g*inv rounded once to bf16.
+//    range; the product is first taken in fp32 with fl32(inv), whose error
+//    against the fp64 product lies within half an ulp on one side and 1.5 on
+//    the other (the side of inv - fl32(inv)); only when its low half is the
+//    bf16 rounding midpoint or that side's neighbour of it (two values per
+//    row), or h*g is denormal or infinite, is the element redone: a midpoint
+//    case is decided in fp32 from the sign of y - midpoint corrected by the
+//    product's exact residual and inv's low part, and ties, near ties and the
+//    rest are redone as fp64 h*g*inv rounded once to bf16.
 //  * FP8 scale s = fl32(amax/448), correctly rounded; codes through the
-//    hardware convert of yb * r for two reciprocals r bracketing 1/s: where
-//    both brackets give the same code it is the code of yb/s (rounding is
-//    monotone); elsewhere, and in groups with a tiny scale, the exact path
-//    rounds the double quotient.
+//    hardware convert of yb * r, with r the reciprocal of s rounded up or
+//    down: the sign of fma(s, 448, -amax) says on which side of every
+//    rounding midpoint yb/s lies (for bf16 yb and amax, 448 yb / amax is a
+//    midpoint exactly or far from one), so one bracket gives the codes of
+//    yb/s; a group whose scale is exact takes the even code of the two
+//    brackets, and groups with a tiny scale round the double quotient.
 //  * MXFP4 scale byte from the bf16 exponent of amax; codes through the
 //    hardware scaled convert straight from the packed bf16 (exact division
 //    by 2^e, then e2m1 rounding).
