@@ -446,6 +446,97 @@ def test_bf16_ties_and_near_ties_through_the_kernel(orc):
                 check(orc, [{"x": x, "gamma": g, "eps": eps, "fmt": fmt, "keep_bf16": True}])
 
 
+def _inv_like_the_definition(ss, N, eps32):
+    """fl64(1 / fl64(sqrt(fl64(ss / N) + eps))) for an exact fp64 ss."""
+    d = np.float64(ss) / np.float64(N) + np.float64(np.float32(eps32))
+    return np.float64(1.0) / np.sqrt(d)
+
+
+def side_crossing_row(N, sign, seed):
+    """One row (bf16 bits), gamma = 1 and an fp32 eps such that the row's
+    values +-h0 normalize to y = h0 * inv just past a bf16 rounding midpoint
+    M0, while the fp32 product with fl32(inv) lands on the side value of the
+    row's window and rounds the other way: inv lies 0.30 to 0.48 of an fp32
+    ulp from the fp32 grid, past M0 / h0 on the side the window covers (above
+    it with fl32(inv) below, sign = +1; below it with fl32(inv) above,
+    sign = -1). An eighth of the row holds +-h0, the rest powers of two that
+    make the sum of squares exact; eps places inv. Returns x, gamma, eps,
+    h0 and M0."""
+    rng = np.random.default_rng(seed)
+    mids = (2 * np.arange(128) + 257) / 256.0                 # bf16 midpoints in (1, 2)
+    for _ in range(20000):
+        h0 = rng.integers(128, 256) / 128.0
+        M0 = float(rng.choice(mids))
+        q = M0 / h0
+        if not 0.6 <= q < 2.0:
+            continue
+        lo = np.float32(q)
+        if np.float64(lo) > q:
+            lo = np.nextafter(lo, np.float32(0))
+        ulp = np.float64(np.nextafter(lo, np.float32(4))) - np.float64(lo)
+        frac = (q - np.float64(lo)) / ulp
+        if not (0.30 <= frac <= 0.48 if sign > 0 else 0.52 <= frac <= 0.70):
+            continue
+        k = N // 8
+        h = np.zeros(N)
+        h[:k] = h0 * rng.choice([-1.0, 1.0], k)
+        target = 1.0 / (q * (1.0 + sign * 2.0 ** -30)) ** 2
+        ss = np.floor((N * target - N * 2.0 ** -12) * 2.0 ** 16) / 2.0 ** 16
+        R = ss - k * h0 * h0
+        free = list(range(k, N))
+        for v in (2.0, 1.0, 0.5, 0.25, 0.125, 0.0625, 0.03125, 0.015625, 0.0078125, 0.00390625):
+            while R >= v * v and free:
+                h[free.pop()] = v * rng.choice([-1.0, 1.0])
+                R -= v * v
+        if R != 0 or float((h * h).sum()) != ss:
+            continue
+        eps0 = np.float32(target - ss / N)
+        for t in sorted(range(-3000, 3001), key=abs):
+            eps = np.float32(eps0 + np.float32(t) * (np.nextafter(eps0, np.float32(1)) - eps0))
+            if eps < 0:
+                continue
+            inv = _inv_like_the_definition(ss, N, eps)
+            Y = np.float64(h0) * inv
+            y32 = np.float32(h0) * np.float32(inv)
+            L = int(np.array(y32, np.float32).view(np.uint32)) & 0xFFFF
+            if sign > 0 and Y > M0 and y32 < M0 and L == 0x7FFF:
+                break
+            if sign < 0 and Y < M0 and y32 > M0 and L == 0x8001:
+                break
+        else:
+            continue
+        x = inputs.to_bf16_bits(rng.permutation(h).astype(np.float32))
+        return x, inputs.to_bf16_bits(np.ones(N, np.float32)), float(eps), h0, M0
+    raise AssertionError("no side-crossing row found")
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+@pytest.mark.parametrize("N, M", [(512, 1), (512, 1024), (1024, 1), (1024, 1024), (7168, 1), (7168, 64)])
+def test_window_side_values_through_the_kernel(orc, N, M, sign):
+    """The midpoint window's side value (0x7FFF in rows with fl32(inv) <= inv,
+    0x8001 in the others) must be redone: rows built so that the fp32 product
+    of the values +-h0 lands there while the definition's value lies past
+    the midpoint on the other side. Checked on the host first (the rows do
+    cross), then the kernel against the oracle in every launch shape these
+    sizes take (rows over one or several waves, rows packed one per wave,
+    rows split over workgroups; the split and the direct rare paths)."""
+    say(f"edge: window side values N={N} M={M} sign={sign}")
+    x, g, eps, h0, M0 = side_crossing_row(N, sign, 100 + N + (sign > 0))
+    xr = np.repeat(x[None, :], M, axis=0)
+    want = run_oracle(orc, {"x": xr[:1], "gamma": g, "eps": eps, "fmt": 0})
+    yb = want["bf16"].reshape(1, -1).view(np.uint16)[0]
+    hv = (x.astype(np.uint32) << 16).view(np.float32)
+    inv = _inv_like_the_definition(float((hv.astype(np.float64) ** 2).sum()), N, eps)
+    y32 = (hv * np.float32(inv)).astype(np.float32)
+    b32 = ((y32.view(np.uint32) + 0x7FFF + ((y32.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16)
+    sel = np.abs(hv) == np.float32(h0)
+    L = y32.view(np.uint32)[sel] & 0xFFFF
+    assert sel.sum() == N // 8 and np.all(L == (0x7FFF if sign > 0 else 0x8001))
+    assert np.all(b32[sel] != yb[sel])          # the fp32 product alone would round the wrong way
+    for fmt in (0, 1):
+        check(orc, [{"x": xr, "gamma": g, "eps": eps, "fmt": fmt, "keep_bf16": True}])
+
+
 def test_strides_inplace_and_tiles(orc):
     say("edge: strides, in place, tiles")
     p = inputs.make_problem(33, 7168, seed_x=31, residual=True, outliers=True)
