@@ -537,6 +537,22 @@ def test_window_side_values_through_the_kernel(orc, N, M, sign):
         check(orc, [{"x": xr, "gamma": g, "eps": eps, "fmt": fmt, "keep_bf16": True}])
 
 
+def test_window_side_values_mla_launch(orc):
+    """The side-value rows in the MLA launch shape: 1536-wide rows (fl32(inv)
+    below inv) and 512-wide rows (fl32(inv) above inv) as two problems of one
+    call, 1024 rows each (rows packed one per wave, steps past the shorter
+    rows skipped), and the 1536-wide rows alone (three chunks per lane, exact
+    tails)."""
+    say("edge: window side values, MLA launch")
+    xa, ga, ea, _, _ = side_crossing_row(1536, 1, 301)
+    xb, gb, eb, _, _ = side_crossing_row(512, -1, 302)
+    pa = {"x": np.repeat(xa[None, :], 1024, axis=0), "gamma": ga, "eps": ea, "fmt": 0, "keep_bf16": True}
+    pb = {"x": np.repeat(xb[None, :], 1024, axis=0), "gamma": gb, "eps": eb, "fmt": 0, "keep_bf16": True}
+    check(orc, [pa, pb])
+    check(orc, [pa])
+    check(orc, [dict(pa, fmt=1), dict(pb, fmt=1)])
+
+
 def test_strides_inplace_and_tiles(orc):
     say("edge: strides, in place, tiles")
     p = inputs.make_problem(33, 7168, seed_x=31, residual=True, outliers=True)
