@@ -49,6 +49,21 @@ def test_add_rmsnorm_matches_oracle_stage(orc, name):
         assert np.array_equal(h, wh)
 
 
+@pytest.mark.parametrize("sign", [1, -1])
+@pytest.mark.parametrize("N, M", [(512, 1), (512, 1024), (7168, 1), (7168, 64)])
+def test_add_rmsnorm_window_side_values(orc, N, M, sign):
+    """The norm alone on rows whose fp32 products land on the midpoint
+    window's side value and round the other way (built as in the fused
+    parity tests): the bf16 output still equals the oracle's."""
+    from tests.test_gpu_parity import side_crossing_row
+    say(f"add_rmsnorm window side values N={N} M={M} sign={sign}")
+    x, g, eps, _, _ = side_crossing_row(N, sign, 500 + N + (sign > 0))
+    p = {"x": np.repeat(x[None, :], M, axis=0), "gamma": g, "eps": eps}
+    _, yb = _norm_gpu(p)
+    _, wyb = orc.add_rmsnorm(p["x"], g, eps)
+    assert np.array_equal(yb, wyb)
+
+
 @pytest.mark.parametrize("fmt,layout", [(0, 0), (1, 0), (1, 1), (0, 2), (1, 2)])
 def test_group_quant_matches_oracle_stage(orc, fmt, layout):
     say(f"dynamic_per_group_scaled_quant fmt {fmt} layout {layout}")
