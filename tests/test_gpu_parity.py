@@ -511,7 +511,8 @@ def side_crossing_row(N, sign, seed):
 
 
 @pytest.mark.parametrize("sign", [1, -1])
-@pytest.mark.parametrize("N, M", [(512, 1), (512, 1024), (1024, 1), (1024, 1024), (7168, 1), (7168, 64)])
+@pytest.mark.parametrize("N, M", [(128, 1024), (256, 1024), (512, 1), (512, 1024), (1024, 1), (1024, 1024),
+                                  (7168, 1), (7168, 64)])
 def test_window_side_values_through_the_kernel(orc, N, M, sign):
     """The midpoint window's side value (0x7FFF in rows with fl32(inv) <= inv,
     0x8001 in the others) must be redone: rows built so that the fp32 product
@@ -519,7 +520,8 @@ def test_window_side_values_through_the_kernel(orc, N, M, sign):
     the midpoint on the other side. Checked on the host first (the rows do
     cross), then the kernel against the oracle in every launch shape these
     sizes take (rows over one or several waves, rows packed one per wave,
-    rows split over workgroups; the split and the direct rare paths)."""
+    rows split over workgroups, rows packed 16 or 32 lanes each with a window
+    per lane; the split and the direct rare paths)."""
     say(f"edge: window side values N={N} M={M} sign={sign}")
     x, g, eps, h0, M0 = side_crossing_row(N, sign, 100 + N + (sign > 0))
     xr = np.repeat(x[None, :], M, axis=0)
